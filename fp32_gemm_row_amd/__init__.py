@@ -1,0 +1,181 @@
+"""Python binding of the MI355X row-major FP32 GEMM library (libfp32_gemm_row.so).
+
+Argument marshalling only: every step of the product runs in the library's HIP
+kernels (C ABI in include/fp32_gemm_row.h). torch provides device memory and
+streams. If the built library is missing, importing the functions raises: there
+is no fallback.
+
+    solve(A, B, C, M, N, K, stream=None)   C[M,K] = A[M,N] x B[N,K]
+
+A, B, C are float32 CUDA (HIP) tensors, contiguous, with at least M*N, N*K and
+M*K elements (raw device addresses as ints are accepted too). `stream` is a
+torch.cuda.Stream, a raw hipStream_t int, or None for torch's current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp32_gemm_row.so")
+
+# Status codes and path / tile values (mirroring include/fp32_gemm_row.h).
+OK = 0
+ERR_NULL_POINTER = -1
+ERR_BAD_DIMS = -2
+ERR_MISALIGNED = -3
+ERR_ALIAS = -4
+ERR_BAD_PATH = -5
+ERR_DEVICE = -6
+ERR_LAUNCH = -7
+
+PATH_AUTO = 0
+PATH_MFMA_VEC = 1
+PATH_MFMA_SCALAR = 2
+PATH_GEMV_VEC = 3
+PATH_GEMV_SCALAR = 4
+PATH_NAMES = {
+    PATH_MFMA_VEC: "mfma_vec",
+    PATH_MFMA_SCALAR: "mfma_scalar",
+    PATH_GEMV_VEC: "gemv_vec",
+    PATH_GEMV_SCALAR: "gemv_scalar",
+}
+
+TILE_AUTO = 0
+TILE_256 = 256
+TILE_128 = 128
+TILE_64 = 64
+
+# Every symbol the header declares.
+EXPORTS = (
+    "solve",
+    "fgr_solve_default",
+    "fgr_solve_path",
+    "fgr_select_path",
+    "fgr_select_tile",
+    "fgr_status_string",
+    "fgr_version",
+)
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{message} (status {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle of the HIP library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m fp32_gemm_row_amd.build` "
+            "(there is no CPU fallback)"
+        )
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.solve.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+    lib.solve.restype = ci
+    lib.fgr_solve_default.argtypes = [vp, vp, vp, ci, ci, ci]
+    lib.fgr_solve_default.restype = ci
+    lib.fgr_solve_path.argtypes = [vp, vp, vp, ci, ci, ci, vp, ci, ci]
+    lib.fgr_solve_path.restype = ci
+    lib.fgr_select_path.argtypes = [vp, vp, vp, ci, ci, ci]
+    lib.fgr_select_path.restype = ci
+    lib.fgr_select_tile.argtypes = [ci, ci, ci]
+    lib.fgr_select_tile.restype = ci
+    lib.fgr_status_string.argtypes = [ci]
+    lib.fgr_status_string.restype = ctypes.c_char_p
+    lib.fgr_version.argtypes = []
+    lib.fgr_version.restype = ci
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().fgr_status_string(int(code)).decode()
+
+
+def _address(x, need: int, name: str) -> int:
+    """Device address of a float32 GPU tensor (checked) or a raw int address."""
+    if isinstance(x, int):
+        return x
+    import torch
+
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor or an int address")
+    if x.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {x.dtype}")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU, got {x.device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if x.numel() < need:
+        raise ValueError(f"{name} has {x.numel()} elements, needs {need}")
+    return x.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(code: int) -> None:
+    if code != OK:
+        raise GemmError(code, status_string(code))
+
+
+def _dims(M, N, K):
+    M, N, K = int(M), int(N), int(K)
+    if M < 1 or N < 1 or K < 1:
+        # let the library report it with its own code
+        return M, N, K, 0, 0, 0
+    return M, N, K, M * N, N * K, M * K
+
+
+def solve(A, B, C, M: int, N: int, K: int, stream=None) -> None:
+    """C[M,K] = A[M,N] x B[N,K] (row-major FP32) on `stream`; asynchronous."""
+    lib = load_library()
+    M, N, K, na, nb, nc = _dims(M, N, K)
+    a = _address(A, na, "A")
+    b = _address(B, nb, "B")
+    c = _address(C, nc, "C")
+    _check(lib.solve(a, b, c, M, N, K, _stream_handle(stream)))
+
+
+def solve_path(A, B, C, M: int, N: int, K: int, path: int, tile: int = TILE_AUTO, stream=None) -> None:
+    """solve() with the kernel path and output tile forced."""
+    lib = load_library()
+    M, N, K, na, nb, nc = _dims(M, N, K)
+    a = _address(A, na, "A")
+    b = _address(B, nb, "B")
+    c = _address(C, nc, "C")
+    _check(lib.fgr_solve_path(a, b, c, M, N, K, _stream_handle(stream), int(path), int(tile)))
+
+
+def select_path(A, B, C, M: int, N: int, K: int) -> int:
+    """The FGR path solve() would take (host-only decision; negative = error code)."""
+    lib = load_library()
+    a = A if isinstance(A, int) else A.data_ptr()
+    b = B if isinstance(B, int) else B.data_ptr()
+    c = C if isinstance(C, int) else C.data_ptr()
+    return int(lib.fgr_select_path(a, b, c, int(M), int(N), int(K)))
+
+
+def select_tile(M: int, K: int, num_cus: int = 0) -> int:
+    return int(load_library().fgr_select_tile(int(M), int(K), int(num_cus)))
+
+
+def version() -> int:
+    return int(load_library().fgr_version())

@@ -1,0 +1,252 @@
+// FP32 matrix-core (MFMA) GEMM for gfx950: C[M,K] = A[M,N] x B[N,K], row-major.
+//
+// The tiling follows the shared-memory / register-tiling line of "LeetGPU |
+// 02_Matrix_Multiplication" (sections "V1: Original 16 x 16 Shared-Memory
+// Tiling", "V1: Two-Dimensional Thread Tiling", "V2: Vectorized float4
+// Transfers", "V3: Register Prefetch and Double-Buffered Shared Memory") and
+// the T x T tile argument of "分块计算与矩阵乘法" (section 2), re-designed for CDNA4:
+//
+//  * one workgroup owns a BM x BN tile of C and the whole reduction over N
+//    (outputs are independent; no cross-workgroup reduction);
+//  * the reduction advances in chunks of BK: each chunk of A (BM x BK) and of
+//    B (BK x BN) is fetched with 128-bit loads (32-bit loads when rows are not
+//    16-byte aligned) into registers, written to one of two LDS buffers, and
+//    consumed by v_mfma_f32_32x32x2_f32 from the other buffer - one barrier
+//    per chunk (the register-prefetch double buffer of the V3 section);
+//  * each wave owns a (BM/WM) x (BN/WN) sub-tile held in FP32 accumulators,
+//    32 x 32 per MFMA block; an MFMA step contracts two reduction indices,
+//    one per half-wave;
+//  * out-of-range rows, columns and reduction indices are zero-filled in LDS
+//    and never loaded (the zero-padding rule of the study notes, section 4,
+//    and of the tutorial, section 2); stores are guarded by row < M, col < K.
+//
+// Operand layouts of v_mfma_f32_32x32x2_f32 (wave64, checked on the device):
+//   A operand: lane l holds A[i = l % 32][kk = l / 32]
+//   B operand: lane l holds B[kk = l / 32][j = l % 32]
+//   D (16 floats per lane): element r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l % 32]
+//
+// Reduction order: any permutation of the reduction index applied to both
+// operands leaves the product unchanged. Lane half g of an MFMA step (t, h)
+// takes reduction index n = 8h + 4g + t inside the chunk, so that a lane reads
+// its four A values n = 8h+4g .. 8h+4g+3 with one 128-bit LDS read and feeds
+// them to four consecutive MFMAs, while B is read as one 32-bit value per lane
+// per step (32 consecutive columns per half-wave, conflict-free).
+//
+// LDS layout: A chunk row-major with a row pitch of BK+4 floats (80 bytes for
+// BK = 16): eight consecutive rows read at the same column land in eight
+// disjoint groups of four banks, so the 128-bit fragment reads are
+// conflict-free. B chunk row-major with pitch BN.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgr {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// Workgroups are dispatched round-robin over the XCDs (id % 8). Renumber them
+// so that consecutive logical ids run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+  const int xcd = wg % kNumXcd;
+  const int local = wg / kNumXcd;
+  const int per = nwg / kNumXcd;
+  const int rem = nwg % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+// Grouped order (the program-id regrouping of the Triton section of the
+// LeetGPU write-up): walk `group` tile-rows at a time, row index fastest, so
+// that neighbouring logical ids share rows of A and columns of B.
+__device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles_n, int group,
+                                             int& tm, int& tn) {
+  const int per_group = group * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * group;
+  const int rows_left = tiles_m - first_m;
+  const int gsz = rows_left < group ? rows_left : group;
+  const int in = logical - g * per_group;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+struct MfmaTile {
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int kWaveM = BM / WM;  // rows of C per wave
+  static constexpr int kWaveN = BN / WN;  // columns of C per wave
+  static constexpr int kRB = kWaveM / 32;  // 32x32 MFMA blocks per wave, down
+  static constexpr int kCB = kWaveN / 32;  // and across
+  static constexpr int kLdA = BK + 4;      // padded A pitch in LDS (floats)
+  static constexpr int kLdB = BN;          // B pitch in LDS (floats)
+  static constexpr int kAQuads = BK / 4;   // float4 per A chunk row
+  static constexpr int kBQuads = BN / 4;   // float4 per B chunk row
+  static constexpr int kAPerThread = BM * BK / 4 / kThreads;
+  static constexpr int kBPerThread = BK * BN / 4 / kThreads;
+  static constexpr int kLdsFloats = 2 * (BM * kLdA + BK * kLdB);
+
+  static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be a multiple of 32x32");
+  static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+  static_assert(BM * BK / 4 % kThreads == 0, "A chunk must split evenly over threads");
+  static_assert(BK * BN / 4 % kThreads == 0, "B chunk must split evenly over threads");
+  static_assert(kThreads % kAQuads == 0 && kThreads % kBQuads == 0,
+                "a thread must keep the same column quad in every load slot");
+  static_assert(kLdsFloats * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+};
+
+// Load one float4 slot, zero-filling every element outside the matrix.
+// VEC: the four elements are either all inside or all outside (rows are
+// 16-byte aligned and the extent is a multiple of 4) and one 128-bit load is
+// used. Otherwise each element is checked and loaded on its own.
+template <bool VEC>
+__device__ __forceinline__ float4 load_quad(const float* __restrict__ p, bool row_ok, int col, int ncols) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (VEC) {
+    if (row_ok && col < ncols) v = *reinterpret_cast<const float4*>(p);
+  } else if (row_ok) {
+    if (col + 0 < ncols) v.x = p[0];
+    if (col + 1 < ncols) v.y = p[1];
+    if (col + 2 < ncols) v.z = p[2];
+    if (col + 3 < ncols) v.w = p[3];
+  }
+  return v;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
+    const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
+    int K, int tiles_m, int tiles_n, int group) {
+  using T = MfmaTile<BM, BN, BK, WM, WN, VEC>;
+  __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
+  float* const As0 = lds;
+  float* const Bs0 = lds + 2 * BM * T::kLdA;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int li = lane & 31;  // row (A operand) / column (B operand, D) inside a 32x32 block
+  const int lg = lane >> 5;  // half-wave: which of the two reduction indices of a step
+
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group, tm, tn);
+  const int m0 = tm * BM;
+  const int k0 = tn * BN;
+
+  // Per-thread load slots. A: slot f covers row f / kAQuads, float4 f % kAQuads
+  // of the chunk; B: row f / kBQuads, float4 f % kBQuads.
+  const float* a_ptr[T::kAPerThread];
+  bool a_row_ok[T::kAPerThread];
+  int a_lds[T::kAPerThread];
+  int a_col[T::kAPerThread];
+#pragma unroll
+  for (int i = 0; i < T::kAPerThread; ++i) {
+    const int f = tid + i * T::kThreads;
+    const int r = f / T::kAQuads;
+    const int q = f % T::kAQuads;
+    a_row_ok[i] = (m0 + r) < M;
+    a_col[i] = 4 * q;
+    a_ptr[i] = A + (int64_t)(a_row_ok[i] ? m0 + r : 0) * N + 4 * q;
+    a_lds[i] = r * T::kLdA + 4 * q;
+  }
+  const float* b_ptr[T::kBPerThread];
+  int b_row[T::kBPerThread];
+  int b_lds[T::kBPerThread];
+  const int b_col = k0 + 4 * (tid % T::kBQuads);
+#pragma unroll
+  for (int i = 0; i < T::kBPerThread; ++i) {
+    const int f = tid + i * T::kThreads;
+    const int r = f / T::kBQuads;
+    b_row[i] = r;
+    b_ptr[i] = B + (int64_t)r * K + b_col;
+    b_lds[i] = r * T::kLdB + 4 * (f % T::kBQuads);
+  }
+
+  float4 ra[T::kAPerThread];
+  float4 rb[T::kBPerThread];
+
+  auto load_chunk = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < T::kAPerThread; ++i)
+      ra[i] = load_quad<VEC>(a_ptr[i] + n0, a_row_ok[i], n0 + a_col[i], N);
+#pragma unroll
+    for (int i = 0; i < T::kBPerThread; ++i) {
+      const int n = n0 + b_row[i];
+      rb[i] = load_quad<VEC>(b_ptr[i] + (int64_t)n0 * K, n < N, b_col, K);
+    }
+  };
+  auto store_chunk = [&](int buf) {
+    float* As = As0 + buf * BM * T::kLdA;
+    float* Bs = Bs0 + buf * BK * T::kLdB;
+#pragma unroll
+    for (int i = 0; i < T::kAPerThread; ++i) *reinterpret_cast<float4*>(As + a_lds[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < T::kBPerThread; ++i) *reinterpret_cast<float4*>(Bs + b_lds[i]) = rb[i];
+  };
+
+  f32x16 acc[T::kRB][T::kCB];
+#pragma unroll
+  for (int i = 0; i < T::kRB; ++i)
+#pragma unroll
+    for (int j = 0; j < T::kCB; ++j) acc[i][j] = f32x16{};
+
+  const int a_frag = (wm * T::kWaveM + li) * T::kLdA + 4 * lg;
+  const int b_frag = 4 * lg * T::kLdB + wn * T::kWaveN + li;
+
+  const int nchunks = (N + BK - 1) / BK;
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunks;
+    if (more) load_chunk((c + 1) * BK);
+
+    const float* As = As0 + buf * BM * T::kLdA;
+    const float* Bs = Bs0 + buf * BK * T::kLdB;
+#pragma unroll
+    for (int h = 0; h < BK / 8; ++h) {
+      float4 a[T::kRB];
+      float b[T::kCB][4];
+#pragma unroll
+      for (int i = 0; i < T::kRB; ++i)
+        a[i] = *reinterpret_cast<const float4*>(As + a_frag + i * 32 * T::kLdA + 8 * h);
+#pragma unroll
+      for (int j = 0; j < T::kCB; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[j][t] = Bs[b_frag + (8 * h + t) * T::kLdB + j * 32];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < T::kRB; ++i)
+#pragma unroll
+          for (int j = 0; j < T::kCB; ++j) {
+            const float av = t == 0 ? a[i].x : t == 1 ? a[i].y : t == 2 ? a[i].z : a[i].w;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[j][t], acc[i][j], 0, 0, 0);
+          }
+    }
+
+    if (more) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: element r of lane l in block (i, j) is row 8*(r/4) + 4*lg + r%4,
+  // column li of that block. Each half-wave stores 32 consecutive floats.
+#pragma unroll
+  for (int i = 0; i < T::kRB; ++i)
+#pragma unroll
+    for (int j = 0; j < T::kCB; ++j) {
+      const int col = k0 + wn * T::kWaveN + j * 32 + li;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        if (row < M && col < K) C[(int64_t)row * K + col] = acc[i][j][r];
+      }
+    }
+}
+
+}  // namespace fgr

@@ -1,0 +1,206 @@
+// C-ABI entry points of the row-major FP32 GEMM library (declared, with the
+// full contract, in include/fp32_gemm_row.h): argument checks, path and tile
+// selection, and the launches. Every step of the product runs in the kernels
+// of gemm_mfma.hpp and gemv.hpp; this file only decides and enqueues.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "fp32_gemm_row.h"
+#include "gemm_mfma.hpp"
+#include "gemv.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCus = 256;  // MI355X
+constexpr int kTileGroup = 4;     // tile-rows per group in the workgroup order
+
+struct DeviceInfo {
+  bool probed = false;
+  bool ok = false;
+  int cus = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+// Current device, checked once: it must be a gfx950 (the FP32 MFMA layouts and
+// the LDS budget used here are gfx950's).
+int current_device(int* cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FGR_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.probed) {
+    hipDeviceProp_t p;
+    d.probed = true;
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess && std::strncmp(p.gcnArchName, "gfx950", 6) == 0) {
+      d.ok = true;
+      d.cus = p.multiProcessorCount;
+    }
+  }
+  if (!d.ok) return FGR_ERR_DEVICE;
+  *cus = d.cus;
+  return FGR_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* p, int64_t pn, const void* q, int64_t qn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)pn * 4;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + (uintptr_t)qn * 4;
+  return a0 < b1 && b0 < a1;
+}
+
+int check_args(const float* A, const float* B, const float* C, int M, int N, int K) {
+  if (!A || !B || !C) return FGR_ERR_NULL_POINTER;
+  if (M < 1 || N < 1 || K < 1) return FGR_ERR_BAD_DIMS;
+  if (!aligned(A, 4) || !aligned(B, 4) || !aligned(C, 4)) return FGR_ERR_MISALIGNED;
+  const int64_t mn = (int64_t)M * N, nk = (int64_t)N * K, mk = (int64_t)M * K;
+  if (overlaps(C, mk, A, mn) || overlaps(C, mk, B, nk)) return FGR_ERR_ALIAS;
+  return FGR_OK;
+}
+
+bool mfma_vec_ok(const float* A, const float* B, const float* C, int N, int K) {
+  return N % 4 == 0 && K % 4 == 0 && aligned(A, 16) && aligned(B, 16) && aligned(C, 16);
+}
+
+bool gemv_vec_ok(const float* B, int K) { return K % 4 == 0 && aligned(B, 16); }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int select_path(const float* A, const float* B, const float* C, int M, int N, int K) {
+  if (M == 1) return gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR;
+  return mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
+}
+
+int select_tile(int M, int K, int cus) {
+  if (cus <= 0) cus = kDefaultCus;
+  if (cdiv(M, 256) * cdiv(K, 256) >= cus) return FGR_TILE_256;
+  if (cdiv(M, 128) * cdiv(K, 128) >= cus) return FGR_TILE_128;
+  return FGR_TILE_64;
+}
+
+int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStream_t stream) {
+  if (blocks < 1 || blocks > INT_MAX) return FGR_ERR_BAD_DIMS;
+  const hipError_t e =
+      hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
+  return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  int tiles_m = (int)cdiv(M, BM);
+  int tiles_n = (int)cdiv(K, BN);
+  int group = kTileGroup;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_kernel<BM, BN, BK, WM, WN, VEC>),
+                (int64_t)tiles_m * tiles_n, WM * WN * 64, args, s);
+}
+
+template <bool VEC>
+int launch_mfma_tile(int tile, const float* A, const float* B, float* C, int M, int N, int K,
+                     hipStream_t s) {
+  switch (tile) {
+    case FGR_TILE_256: return launch_mfma<256, 256, 16, 2, 2, VEC>(A, B, C, M, N, K, s);
+    case FGR_TILE_128: return launch_mfma<128, 128, 16, 2, 2, VEC>(A, B, C, M, N, K, s);
+    case FGR_TILE_64: return launch_mfma<64, 64, 16, 2, 2, VEC>(A, B, C, M, N, K, s);
+    default: return FGR_ERR_BAD_PATH;
+  }
+}
+
+template <int VW>
+int launch_gemv(const float* A, const float* B, float* C, int N, int K, hipStream_t s) {
+  constexpr int NT = 256;
+  void* args[] = {&A, &B, &C, &N, &K};
+  return launch(reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, NT, 8>),
+                cdiv(K, fgr::kGemvCols), NT, args, s);
+}
+
+int run(const float* A, const float* B, float* C, int M, int N, int K, void* stream, int path,
+        int tile) {
+  int rc = check_args(A, B, C, M, N, K);
+  if (rc != FGR_OK) return rc;
+  const int chosen = select_path(A, B, C, M, N, K);
+  if (path == FGR_PATH_AUTO) path = chosen;
+  switch (path) {
+    case FGR_PATH_MFMA_VEC:
+      if (!mfma_vec_ok(A, B, C, N, K)) return FGR_ERR_BAD_PATH;
+      break;
+    case FGR_PATH_MFMA_SCALAR: break;
+    case FGR_PATH_GEMV_VEC:
+      if (M != 1 || !gemv_vec_ok(B, K)) return FGR_ERR_BAD_PATH;
+      break;
+    case FGR_PATH_GEMV_SCALAR:
+      if (M != 1) return FGR_ERR_BAD_PATH;
+      break;
+    default: return FGR_ERR_BAD_PATH;
+  }
+  if (tile != FGR_TILE_AUTO && tile != FGR_TILE_256 && tile != FGR_TILE_128 && tile != FGR_TILE_64)
+    return FGR_ERR_BAD_PATH;
+
+  int cus = 0;
+  rc = current_device(&cus);
+  if (rc != FGR_OK) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (tile == FGR_TILE_AUTO) tile = select_tile(M, K, cus);
+
+  switch (path) {
+    case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
+    case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
+    case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, N, K, s);
+    case FGR_PATH_GEMV_SCALAR: return launch_gemv<1>(A, B, C, N, K, s);
+  }
+  return FGR_ERR_BAD_PATH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int solve(const float* A, const float* B, float* C, int M, int N, int K, void* stream) {
+  return run(A, B, C, M, N, K, stream, FGR_PATH_AUTO, FGR_TILE_AUTO);
+}
+
+int fgr_solve_default(const float* A, const float* B, float* C, int M, int N, int K) {
+  return run(A, B, C, M, N, K, nullptr, FGR_PATH_AUTO, FGR_TILE_AUTO);
+}
+
+int fgr_solve_path(const float* A, const float* B, float* C, int M, int N, int K, void* stream,
+                   int path, int tile) {
+  return run(A, B, C, M, N, K, stream, path, tile);
+}
+
+int fgr_select_path(const float* A, const float* B, const float* C, int M, int N, int K) {
+  const int rc = check_args(A, B, C, M, N, K);
+  if (rc != FGR_OK) return rc;
+  return select_path(A, B, C, M, N, K);
+}
+
+int fgr_select_tile(int M, int K, int num_cus) {
+  if (M < 1 || K < 1) return FGR_ERR_BAD_DIMS;
+  return select_tile(M, K, num_cus);
+}
+
+const char* fgr_status_string(int status) {
+  switch (status) {
+    case FGR_OK: return "ok";
+    case FGR_ERR_NULL_POINTER: return "null pointer argument";
+    case FGR_ERR_BAD_DIMS: return "M, N and K must be >= 1";
+    case FGR_ERR_MISALIGNED: return "pointer not 4-byte aligned";
+    case FGR_ERR_ALIAS: return "C overlaps A or B";
+    case FGR_ERR_BAD_PATH: return "forced path or tile cannot run these arguments";
+    case FGR_ERR_DEVICE: return "no gfx950 HIP device is current";
+    case FGR_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fgr_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+/*
+ * fp32_gemm_row.h - C ABI of the MI355X (gfx950) row-major FP32 GEMM library.
+ *
+ * Operation (the LeetGPU problem of "LeetGPU | 02_Matrix_Multiplication",
+ * sections "Problem Description" and "Implementation Requirements", and the
+ * CUDA "Approach" there; restated in section 1 of "CUDA 学习笔记 Matrix
+ * Multiplication：LeetGPU FP32 矩阵乘法，从逐元素到分块复用"):
+ *
+ *     C[m,k] = sum over n = 0 .. N-1 of A[m,n] * B[n,k]
+ *
+ * A is M x N, B is N x K, C is M x K, all dense row-major FP32 with leading
+ * dimensions exactly N, K and K: A[m,n] = A[m*N+n], B[n,k] = B[n*K+k],
+ * C[m,k] = C[m*K+k]. N is the reduction length. (The tutorial
+ * "分块计算与矩阵乘法" swaps the letters for the same product.)
+ *
+ * Arithmetic is IEEE FP32 throughout (FP32 matrix-core or vector FMA, FP32
+ * accumulation, no reduced-precision inputs). The summation order over n is
+ * unspecified, so results may differ from a sequential sum in the last bits;
+ * where every partial sum is exactly representable (e.g. small integers) the
+ * result is exact. The result is |C - exact| <= 1e-5 * sum_n |A[m,n]||B[n,k]|
+ * + 1e-6 per element on the tested workloads.
+ *
+ * Memory and ownership
+ *   A, B and C are DEVICE pointers owned by the caller. The library never
+ *   allocates, frees or synchronises; it keeps no workspace and no state
+ *   besides a per-device cache of device properties. C is overwritten
+ *   (every one of its M*K elements is written once; its prior contents,
+ *   even NaN, are ignored - the write-back rule of the CUDA study notes,
+ *   section 3, and "the result must be stored in C" of the LeetGPU
+ *   requirements). A and B are only read and may alias each other; C must
+ *   not overlap A or B.
+ *
+ * Streams
+ *   `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *   is enqueued on it and the call returns without waiting for it. The
+ *   LeetGPU form below uses the null stream.
+ *
+ * Alignment and paths
+ *   Any 4-byte-aligned pointers are accepted. When N % 4 == 0, K % 4 == 0
+ *   and A, B, C are 16-byte aligned the 128-bit load path is used; otherwise
+ *   a path with 32-bit loads (the role of the scalar fallback of the LeetGPU
+ *   write-up, section "V2: Vectorized float4 Transfers"). M == 1 takes the
+ *   bandwidth-bound matrix-vector path.
+ *
+ * Errors
+ *   Every entry point returns 0 (FGR_OK) on success or a negative FGR_ERR_*
+ *   code. Argument errors are detected on the host before any HIP call, and
+ *   nothing is enqueued then. FGR_ERR_LAUNCH reports a HIP error right after
+ *   the launch (from hipGetLastError); errors raised later, while the kernel
+ *   runs, surface at the caller's next synchronisation.
+ *
+ * Limits
+ *   The problem statement guarantees 1 <= M, N, K <= 8192 (LeetGPU
+ *   "Constraints"); that is the tested range. Larger values are accepted:
+ *   index and size arithmetic is 64-bit. Values < 1 are rejected.
+ */
+#ifndef FP32_GEMM_ROW_H
+#define FP32_GEMM_ROW_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FGR_OK 0
+#define FGR_ERR_NULL_POINTER (-1) /* A, B or C is NULL */
+#define FGR_ERR_BAD_DIMS (-2)     /* M, N or K < 1 */
+#define FGR_ERR_MISALIGNED (-3)   /* a pointer is not 4-byte aligned */
+#define FGR_ERR_ALIAS (-4)        /* C overlaps A or B */
+#define FGR_ERR_BAD_PATH (-5)     /* forced path/tile cannot run this shape */
+#define FGR_ERR_DEVICE (-6)       /* no HIP device, or the current one is not gfx950 */
+#define FGR_ERR_LAUNCH (-7)       /* HIP reported an error at launch */
+
+/* Paths (fgr_select_path / fgr_solve_path). */
+#define FGR_PATH_AUTO 0
+#define FGR_PATH_MFMA_VEC 1    /* FP32 MFMA, 128-bit loads; needs N%4 == K%4 == 0 and 16-B aligned pointers */
+#define FGR_PATH_MFMA_SCALAR 2 /* FP32 MFMA, 32-bit loads; any shape and 4-B alignment */
+#define FGR_PATH_GEMV_VEC 3    /* matrix-vector (M == 1), 128-bit loads of B; needs K%4 == 0 and 16-B aligned B, C */
+#define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector (M == 1), 32-bit loads */
+
+/* Output tile of the MFMA paths (rows x columns of C per workgroup). */
+#define FGR_TILE_AUTO 0
+#define FGR_TILE_256 256
+#define FGR_TILE_128 128
+#define FGR_TILE_64 64
+
+/*
+ * solve - C = A x B on `stream`.
+ *   A      device pointer, M*N floats, row-major (read only)
+ *   B      device pointer, N*K floats, row-major (read only)
+ *   C      device pointer, M*K floats, row-major (overwritten)
+ *   M,N,K  dimensions, each >= 1; N is the reduction length
+ *   stream hipStream_t as void*, NULL for the null stream
+ * Returns FGR_OK or an FGR_ERR_* code (see above). Asynchronous.
+ * The LeetGPU signature (section "Problem Description", and every "Solution"
+ * of the write-up) is solve(A, B, C, M, N, K) returning void; this form adds
+ * the stream and a status.
+ */
+int solve(const float *A, const float *B, float *C, int M, int N, int K, void *stream);
+
+/*
+ * fgr_solve_default - the six-argument LeetGPU form: solve(A, B, C, M, N, K, NULL).
+ */
+int fgr_solve_default(const float *A, const float *B, float *C, int M, int N, int K);
+
+/*
+ * fgr_solve_path - solve() with the path and output tile forced (for tests and
+ * benchmarks; the controlled comparisons of the LeetGPU write-up, section
+ * "Controlled Comparison", build each variant separately). path is an
+ * FGR_PATH_* value, tile an FGR_TILE_* value (ignored by the GEMV paths).
+ * Returns FGR_ERR_BAD_PATH if that path or tile cannot handle these arguments
+ * (e.g. a VEC path with N % 4 != 0, a GEMV path with M != 1, an unknown value).
+ */
+int fgr_solve_path(const float *A, const float *B, float *C, int M, int N, int K, void *stream,
+                   int path, int tile);
+
+/*
+ * fgr_select_path - the FGR_PATH_* value solve() would take for these
+ * arguments, or a negative FGR_ERR_* code for invalid arguments. Host only:
+ * makes no HIP call.
+ */
+int fgr_select_path(const float *A, const float *B, const float *C, int M, int N, int K);
+
+/*
+ * fgr_select_tile - the FGR_TILE_* output tile solve() would use on the MFMA
+ * paths for an M x K output on a device with `num_cus` compute units (<= 0:
+ * the 256 of MI355X). Host only.
+ */
+int fgr_select_tile(int M, int K, int num_cus);
+
+/* fgr_status_string - a static, human-readable name for a status code. */
+const char *fgr_status_string(int status);
+
+/* fgr_version - library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fgr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP32_GEMM_ROW_H */

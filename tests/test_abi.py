@@ -1,0 +1,149 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_row_amd as fgr
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fp32_gemm_row.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def declared_macros():
+    text = open(HEADER, encoding="utf-8").read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+FGR_(\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fgr.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fgr.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_python_constants_match_header():
+    macros = declared_macros()
+    for key, value in macros.items():
+        if key.startswith("ERR_") or key == "OK":
+            assert getattr(fgr, key) == value, key
+        elif key.startswith("PATH_") or key.startswith("TILE_"):
+            assert getattr(fgr, key) == value, key
+
+
+def test_version_and_status_strings(lib):
+    assert fgr.version() == 100
+    assert fgr.status_string(fgr.OK) == "ok"
+    for code in range(-7, 0):
+        s = fgr.status_string(code)
+        assert s and s != "unknown status"
+    assert fgr.status_string(12345) == "unknown status"
+
+
+# Fake, well-separated, 256-byte aligned "device" addresses: validation runs on
+# the host before any HIP call, so they are never dereferenced.
+A0, B0, C0 = 0x10000000, 0x20000000, 0x30000000
+
+
+def call(lib, a, b, c, M, N, K, path=0, tile=0):
+    return lib.fgr_solve_path(a, b, c, M, N, K, None, path, tile)
+
+
+def test_null_pointers_rejected(lib):
+    assert call(lib, 0, B0, C0, 2, 2, 2) == fgr.ERR_NULL_POINTER
+    assert call(lib, A0, 0, C0, 2, 2, 2) == fgr.ERR_NULL_POINTER
+    assert call(lib, A0, B0, 0, 2, 2, 2) == fgr.ERR_NULL_POINTER
+    assert lib.solve(A0, B0, 0, 2, 2, 2, None) == fgr.ERR_NULL_POINTER
+    assert lib.fgr_solve_default(0, B0, C0, 2, 2, 2) == fgr.ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("dims", [(0, 1, 1), (1, 0, 1), (1, 1, 0), (-1, 4, 4), (4, 4, -8)])
+def test_bad_dims_rejected(lib, dims):
+    assert call(lib, A0, B0, C0, *dims) == fgr.ERR_BAD_DIMS
+    assert lib.solve(A0, B0, C0, *dims, None) == fgr.ERR_BAD_DIMS
+
+
+def test_misaligned_pointers_rejected(lib):
+    assert call(lib, A0 + 2, B0, C0, 4, 4, 4) == fgr.ERR_MISALIGNED
+    assert call(lib, A0, B0 + 1, C0, 4, 4, 4) == fgr.ERR_MISALIGNED
+    assert call(lib, A0, B0, C0 + 3, 4, 4, 4) == fgr.ERR_MISALIGNED
+
+
+def test_overlap_of_output_rejected(lib):
+    M = N = K = 16
+    # C starts inside A
+    assert call(lib, A0, B0, A0 + 4 * (M * N - 1), M, N, K) == fgr.ERR_ALIAS
+    # C ends inside B
+    assert call(lib, A0, B0, B0 - 4 * (M * K - 1), M, N, K) == fgr.ERR_ALIAS
+    # A and B may alias each other
+    assert fgr.select_path(A0, A0, C0, M, N, K) == fgr.PATH_MFMA_VEC
+    # adjacent, not overlapping
+    assert fgr.select_path(A0, B0, A0 + 4 * M * N, M, N, K) == fgr.PATH_MFMA_VEC
+
+
+def test_forced_path_rejections(lib):
+    # vec path needs N % 4 == 0, K % 4 == 0 and 16-byte aligned pointers
+    assert call(lib, A0, B0, C0, 8, 6, 8, fgr.PATH_MFMA_VEC) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 8, 8, 6, fgr.PATH_MFMA_VEC) == fgr.ERR_BAD_PATH
+    assert call(lib, A0 + 4, B0, C0, 8, 8, 8, fgr.PATH_MFMA_VEC) == fgr.ERR_BAD_PATH
+    # matrix-vector paths need M == 1
+    assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_SCALAR) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 1, 8, 6, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
+    # unknown path or tile values
+    assert call(lib, A0, B0, C0, 8, 8, 8, 99) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 8, 8, 8, fgr.PATH_MFMA_VEC, 100) == fgr.ERR_BAD_PATH
+
+
+def test_path_selection_rules():
+    sp = fgr.select_path
+    assert sp(A0, B0, C0, 8192, 6144, 4096) == fgr.PATH_MFMA_VEC
+    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0 + 4, B0, C0, 8, 8, 8) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0, B0, C0 + 8, 8, 8, 8) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0, B0, C0, 1, 8192, 8192) == fgr.PATH_GEMV_VEC
+    assert sp(A0, B0, C0, 1, 3, 1) == fgr.PATH_GEMV_SCALAR
+    assert sp(A0, B0 + 4, C0, 1, 8, 8) == fgr.PATH_GEMV_SCALAR
+    assert sp(0, B0, C0, 1, 8, 8) == fgr.ERR_NULL_POINTER
+
+
+def test_tile_selection():
+    st = fgr.select_tile
+    assert st(8192, 4096, 256) == 256  # 512 tiles of 256x256
+    assert st(4096, 4096, 256) == 256  # 256 tiles
+    assert st(2048, 2048, 256) == 128  # 64 big tiles, 256 of 128x128
+    assert st(1023, 1027, 256) == 64
+    assert st(256, 256, 256) == 64
+    assert st(0, 4, 256) == fgr.ERR_BAD_DIMS
+    assert st(8192, 4096, 0) == 256  # default CU count
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fgr.solve(a, a, a, 2, 2, 2)
+    with pytest.raises(TypeError):
+        fgr.solve(a.double(), a, a, 2, 2, 2)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(fgr, "_lib", None)
+    with pytest.raises(ImportError):
+        fgr.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,282 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Bars (per element):
+  * exactly-summing inputs (the tutorial's eighths, small integers, the
+    worked examples): bit-exact, C_gpu == C_oracle;
+  * other inputs: finite and |C_gpu - C| <= 1e-5 * S + 1e-6 with
+    S = sum_n |A[m,n]||B[n,k]|, both from the fp64 oracle.
+C is prefilled with NaN before every call, so an element the kernels never
+write fails the finiteness check.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import GOLDEN_FILES, load_golden
+
+torch = pytest.importorskip("torch")
+import fp32_gemm_row_amd as fgr  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ALL_TILES = [fgr.TILE_256, fgr.TILE_128, fgr.TILE_64]
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_gemm(A, B, path=fgr.PATH_AUTO, tile=fgr.TILE_AUTO, offsets=(0, 0, 0), stream=None):
+    """Run the library on A, B (numpy float32); return C as numpy float32.
+
+    offsets shift each operand by that many floats inside a larger buffer, to
+    hand the library pointers that are 4-byte but not 16-byte aligned."""
+    M, N = A.shape
+    K = B.shape[1]
+    oa, ob, oc = offsets
+    ba = torch.empty(M * N + oa, dtype=torch.float32, device=DEV)
+    bb = torch.empty(N * K + ob, dtype=torch.float32, device=DEV)
+    bc = torch.full((M * K + oc,), float("nan"), dtype=torch.float32, device=DEV)
+    da, db, dc = ba[oa:], bb[ob:], bc[oc:]
+    da.copy_(torch.from_numpy(np.ascontiguousarray(A, dtype=np.float32).ravel()))
+    db.copy_(torch.from_numpy(np.ascontiguousarray(B, dtype=np.float32).ravel()))
+    torch.cuda.synchronize()
+    if path == fgr.PATH_AUTO and tile == fgr.TILE_AUTO:
+        fgr.solve(da, db, dc, M, N, K, stream=stream)
+    else:
+        fgr.solve_path(da, db, dc, M, N, K, path, tile, stream=stream)
+    torch.cuda.synchronize()
+    return dc.cpu().numpy().reshape(M, K)
+
+
+def assert_exact(C, Cref, label):
+    C64 = C.astype(np.float64)
+    bad = ~(C64 == Cref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        detail = ", ".join(f"[{i},{j}] gpu={C[i, j]!r} ref={Cref[i, j]!r}" for i, j in idx)
+        pytest.fail(f"{label}: {int(bad.sum())} of {bad.size} elements differ: {detail}")
+
+
+def assert_within_tolerance(C, Cref, S, label):
+    C64 = C.astype(np.float64)
+    finite = np.isfinite(C64)
+    if not finite.all():
+        idx = np.argwhere(~finite)[:5]
+        pytest.fail(f"{label}: {int((~finite).sum())} non-finite outputs, first at {idx.tolist()}")
+    err = np.abs(C64 - Cref)
+    tol = oracle.tolerance(S)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / tol), err.shape)
+        pytest.fail(
+            f"{label}: {int(bad.sum())} elements beyond 1e-5*S+1e-6; worst at {tuple(int(x) for x in i)} "
+            f"err={err[i]:.3e} tol={tol[i]:.3e}"
+        )
+
+
+def paths_for(M, N, K):
+    """(path, tile) pairs able to run an (M, N, K) product from aligned buffers."""
+    out = []
+    for tile in ALL_TILES:
+        out.append((fgr.PATH_MFMA_SCALAR, tile))
+        if N % 4 == 0 and K % 4 == 0:
+            out.append((fgr.PATH_MFMA_VEC, tile))
+    if M == 1:
+        out.append((fgr.PATH_GEMV_SCALAR, 0))
+        if K % 4 == 0:
+            out.append((fgr.PATH_GEMV_VEC, 0))
+    return out
+
+
+# ------------------------------------------------------------ worked examples
+
+
+@pytest.mark.parametrize("name", GOLDEN_FILES)
+def test_worked_examples_every_path(name):
+    M, N, K, A, B, C_expected = load_golden(name)
+    say(f"worked example {name} M={M} N={N} K={K}")
+    assert_exact(gpu_gemm(A, B), C_expected, f"{name} auto")
+    for path, tile in paths_for(M, N, K):
+        assert_exact(gpu_gemm(A, B, path, tile), C_expected, f"{name} path={path} tile={tile}")
+
+
+# ------------------------------------------------- exact shapes, every path
+
+EXACT_SHAPES = [
+    (1, 1, 1), (2, 2, 2), (1, 3, 1), (2, 3, 2), (3, 5, 4), (17, 19, 23), (17, 19, 31),
+    (129, 96, 132), (256, 96, 256), (255, 257, 129), (257, 129, 193), (512, 512, 512),
+    (2, 64, 64), (5, 64, 60), (8, 64, 64),
+    (70, 1, 70), (70, 15, 70), (70, 16, 70), (70, 17, 70),
+    (70, 70, 1), (70, 70, 3), (70, 70, 4), (70, 70, 5),
+    (1, 8, 4), (1, 1000, 999), (1, 4097, 1028), (1, 17, 33),
+    (513, 600, 515), (300, 2050, 260),
+]
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_eighths_bit_exact_every_path(shape):
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "eighths")
+    Cref, _ = oracle.gemm(A, B)
+    say(f"eighths {shape} auto")
+    assert_exact(gpu_gemm(A, B), Cref, f"eighths {shape} auto")
+    for path, tile in paths_for(M, N, K):
+        say(f"eighths {shape} path={fgr.PATH_NAMES[path]} tile={tile}")
+        assert_exact(gpu_gemm(A, B, path, tile), Cref, f"eighths {shape} path={path} tile={tile}")
+
+
+@pytest.mark.parametrize("shape", [(64, 64, 64), (129, 96, 132), (33, 20, 45), (1, 64, 64), (1, 13, 7)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_misaligned_pointers_take_scalar_path(shape):
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "eighths")
+    Cref, _ = oracle.gemm(A, B)
+    for offs in [(1, 0, 0), (0, 1, 0), (0, 0, 1), (3, 2, 1)]:
+        say(f"misaligned {shape} offsets={offs}")
+        assert_exact(gpu_gemm(A, B, offsets=offs), Cref, f"misaligned {shape} {offs}")
+
+
+def test_vec_path_refuses_misaligned_pointer():
+    A, B = synth.make_inputs(8, 8, 8, "eighths")
+    ba = torch.zeros(65, device=DEV)
+    b = torch.from_numpy(B.ravel()).to(DEV)
+    c = torch.zeros(64, device=DEV)
+    with pytest.raises(fgr.GemmError) as e:
+        fgr.solve_path(ba[1:], b, c, 8, 8, 8, fgr.PATH_MFMA_VEC)
+    assert e.value.code == fgr.ERR_BAD_PATH
+
+
+# ----------------------------------------------------- the five workloads
+
+
+def test_cube256_integer_bit_exact():
+    w = synth.WORKLOADS["cube256_int"]
+    A, B = synth.workload_inputs(w)
+    Cref, _ = oracle.gemm(A, B)
+    assert_exact(gpu_gemm(A, B), Cref, "cube256 integer auto")
+    for tile in ALL_TILES:
+        assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_VEC, tile), Cref, f"cube256 integer tile={tile}")
+
+
+@pytest.mark.parametrize("name", ["cube256", "ragged1023"])
+def test_small_workloads_full_compare(name):
+    w = synth.WORKLOADS[name]
+    A, B = synth.workload_inputs(w)
+    Cref, S = oracle.gemm(A, B)
+    say(f"{name} auto path={fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, w.M, w.N, w.K)]}")
+    assert_within_tolerance(gpu_gemm(A, B), Cref, S, f"{name} auto")
+    for path, tile in paths_for(w.M, w.N, w.K):
+        say(f"{name} path={fgr.PATH_NAMES[path]} tile={tile}")
+        assert_within_tolerance(gpu_gemm(A, B, path, tile), Cref, S, f"{name} path={path} tile={tile}")
+
+
+def sample_positions(M, K, tile, rng, extra=2048):
+    """Corners of every tile (the ragged tail included) plus random positions."""
+    rows, cols = [], []
+    for m0 in range(0, M, tile):
+        for k0 in range(0, K, tile):
+            m1 = min(m0 + tile, M) - 1
+            k1 = min(k0 + tile, K) - 1
+            for (r, c) in ((m0, k0), (m0, k1), (m1, k0), (m1, k1)):
+                rows.append(r)
+                cols.append(c)
+    rows.extend(rng.integers(0, M, size=extra).tolist())
+    cols.extend(rng.integers(0, K, size=extra).tolist())
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["cube4096", "leetgpu8192"])
+def test_large_workloads_sampled(name):
+    w = synth.WORKLOADS[name]
+    say(f"{name}: generating inputs")
+    A, B = synth.workload_inputs(w)
+    say(f"{name}: GPU run (auto path, tile {fgr.select_tile(w.M, w.K)})")
+    C = gpu_gemm(A, B)
+    assert np.isfinite(C).all(), f"{name}: non-finite outputs"
+    rng = np.random.default_rng(w.seed)
+    rows, cols = sample_positions(w.M, w.K, fgr.select_tile(w.M, w.K), rng)
+    say(f"{name}: oracle at {rows.size} positions")
+    Cref, S = oracle.gemm_at(A, B, rows, cols)
+    assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{name} sampled")
+
+
+def test_gemv_workload_full_compare():
+    w = synth.WORKLOADS["gemv8192"]
+    A, B = synth.workload_inputs(w)
+    Cref, S = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, w.M, w.N, w.K) == fgr.PATH_GEMV_VEC
+    assert_within_tolerance(gpu_gemm(A, B), Cref, S, "gemv8192 auto")
+    assert_within_tolerance(gpu_gemm(A, B, fgr.PATH_GEMV_SCALAR), Cref, S, "gemv8192 scalar")
+
+
+# ------------------------------------------------------------- properties
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = synth.WORKLOADS["ragged1023"]
+    A, B = synth.workload_inputs(w)
+    first = gpu_gemm(A, B)
+    for _ in range(4):
+        assert np.array_equal(gpu_gemm(A, B), first, equal_nan=True)
+
+
+def test_identity_and_one_hot():
+    rng = np.random.default_rng(0)
+    B = rng.uniform(-1, 1, size=(300, 260)).astype(np.float32)
+    assert_exact(gpu_gemm(np.eye(300, dtype=np.float32), B), B.astype(np.float64), "I x B")
+    A = np.zeros((70, 300), dtype=np.float32)
+    A[13, 299] = 1.0
+    A[69, 0] = 1.0
+    exp = np.zeros((70, 260))
+    exp[13] = B[299]
+    exp[69] = B[0]
+    assert_exact(gpu_gemm(A, B), exp, "one-hot rows")
+
+
+def test_single_product_reduction_is_exact():
+    # N = 1: C[m,k] = a * b, one product (the padding adds exact zeros)
+    rng = np.random.default_rng(1)
+    a = rng.uniform(-1, 1, size=(130, 1)).astype(np.float32)
+    b = rng.uniform(-1, 1, size=(1, 140)).astype(np.float32)
+    exp = (a * b).astype(np.float64)  # float32 product, correctly rounded
+    for path, tile in paths_for(130, 1, 140):
+        assert_exact(gpu_gemm(a, b, path, tile), exp, f"N=1 path={path} tile={tile}")
+
+
+def test_nan_in_a_row_poisons_only_that_row():
+    A, B = synth.make_inputs(64, 64, 64, "eighths")
+    A = A.copy()
+    A[5, 7] = np.nan
+    C = gpu_gemm(A, B)
+    assert np.isnan(C[5]).all()
+    mask = np.ones(64, dtype=bool)
+    mask[5] = False
+    Cref, _ = oracle.gemm(A[mask], B)
+    assert_exact(C[mask], Cref, "rows without NaN")
+
+
+def test_runs_on_a_side_stream():
+    A, B = synth.make_inputs(257, 129, 193, "eighths")
+    Cref, _ = oracle.gemm(A, B)
+    s = torch.cuda.Stream()
+    assert_exact(gpu_gemm(A, B, stream=s), Cref, "side stream")
+
+
+def test_six_argument_form_uses_null_stream():
+    A, B = synth.make_inputs(33, 40, 36, "eighths")
+    Cref, _ = oracle.gemm(A, B)
+    da = torch.from_numpy(A.ravel()).to(DEV)
+    db = torch.from_numpy(B.ravel()).to(DEV)
+    dc = torch.full((33 * 36,), float("nan"), device=DEV)
+    torch.cuda.synchronize()
+    lib = fgr.load_library()
+    assert lib.fgr_solve_default(da.data_ptr(), db.data_ptr(), dc.data_ptr(), 33, 40, 36) == 0
+    torch.cuda.synchronize()
+    assert_exact(dc.cpu().numpy().reshape(33, 36), Cref, "six-argument form")
