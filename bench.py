@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the row-major FP32 GEMM C[M,K] = A[M,N] x B[N,K] on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+One step is one call of the library's solve() on the workload's inputs,
+which are already resident in HBM when the timed region starts. W untimed
+steps, then exactly K steps between two device synchronisations on the host
+clock. Prints ONE JSON line:
+
+  value        whole-job throughput over the K steps (TFLOP/s = 2MNK / time;
+               GB/s of algorithmic bytes for the matrix-vector workload)
+  roofline     the kernel's average launch duration from HIP events recorded
+               around each launch on the stream it runs on, its algorithmic
+               FLOP (or bytes) per launch over that duration, against the
+               MI355X peak; `traffic` = HBM bytes per launch from rocprofv3
+               FETCH_SIZE / WRITE_SIZE counters (profiles/), or null if the
+               kernel sources changed since those counters were taken
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+               (leading rows of A), on this host's cores
+
+Workloads (seeded synthetic inputs, synth/): leetgpu8192 (default, the
+LeetGPU timed shape M=8192, N=6144, K=4096, normal entries / sqrt(N)),
+cube4096, ragged1023, cube256, gemv8192.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X: 256 CU x 256 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+METRIC = "FP32 GEMM TFLOP/s at M=8192,N=6144,K=4096; % of MI355X FP32 MFMA peak"
+KERNEL_SOURCES = ["gemm_mfma.hpp", "gemv.hpp", "solve.hip"]
+COPY_BYTES = 512 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp32_gemm_row_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from profiles/<workload>_traffic.md, if current."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    src = re.search(r"kernel-source-sha256:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm-bytes-per-launch:\s*([0-9]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return int(val.group(1))
+
+
+def cpu_baseline(w, A, B, target_s: float):
+    """Time the oracle on the first R rows of A (R sized for about target_s)."""
+    import oracle
+
+    threads = oracle.max_threads()
+    rows = 8
+    t0 = time.perf_counter()
+    oracle.gemm(A[:rows], B, threads=threads)
+    t_probe = time.perf_counter() - t0
+    rows_fit = int(rows * target_s / max(t_probe, 1e-6))
+    R = max(rows, min(w.M, rows_fit))
+    t0 = time.perf_counter()
+    oracle.gemm(A[:R], B, threads=threads)
+    elapsed = time.perf_counter() - t0
+    flops = 2.0 * R * w.N * w.K
+    if w.M == 1:
+        value = 4.0 * (R * w.N + w.N * w.K + R * w.K) / elapsed / 1e9
+        unit = "GB/s"
+    else:
+        value = flops / elapsed / 1e12
+        unit = "TFLOP/s"
+    return {
+        "value": round(value, 6),
+        "unit": unit,
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{R - 1} of A against all of B ({R}x{w.N}x{w.K}, fp64 with |a||b| sums), {elapsed:.2f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="leetgpu8192")
+    ap.add_argument("--path", type=int, default=0, help="force an FGR path (0 = auto)")
+    ap.add_argument("--tile", type=int, default=0, help="force an MFMA output tile (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, run a plain 512 MiB device copy three times "
+                         "(the known-size reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(
+            "bench.py measures one GPU only: the library has no multi-GPU path "
+            "(sharding output rows across GPUs is a design note, not built). Use --gpus 1.",
+            file=sys.stderr,
+        )
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import fp32_gemm_row_amd as fgr
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (no CPU fallback)", file=sys.stderr)
+        return 2
+    fgr.load_library()
+
+    w = synth.WORKLOADS[args.workload]
+    A, B = synth.workload_inputs(w)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A.ravel()).to(dev)
+    dB = torch.from_numpy(B.ravel()).to(dev)
+    dC = torch.empty(w.M * w.K, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    path = args.path or fgr.select_path(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), w.M, w.N, w.K)
+    tile = args.tile or (fgr.select_tile(w.M, w.K) if path in (fgr.PATH_MFMA_VEC, fgr.PATH_MFMA_SCALAR) else 0)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fgr.solve_path(dA, dB, dC, w.M, w.N, w.K, path, tile, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    gemv = w.M == 1
+    if gemv:
+        value = w.algorithmic_bytes * args.steps / wall / 1e9
+        unit = "GB/s"
+        achieved = w.algorithmic_bytes / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        metric = "FP32 GEMV-shaped GEMM GB/s at M=1,N=8192,K=8192; % of MI355X HBM peak"
+    else:
+        value = w.flops * args.steps / wall / 1e12
+        unit = "TFLOP/s"
+        achieved = w.flops / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        metric = METRIC if args.workload == "leetgpu8192" else f"FP32 GEMM TFLOP/s at M={w.M},N={w.N},K={w.K}"
+    roof["frac"] = round(achieved / roof["peak"], 4)
+    roof["traffic"] = recorded_traffic(args.workload)
+    roof["launch_ms"] = {
+        "mean": round(avg_launch_s * 1e3, 4),
+        "min": round(min(launch_ms), 4),
+        "max": round(max(launch_ms), 4),
+    }
+
+    out = {
+        "metric": metric,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "M": w.M,
+            "N": w.N,
+            "K": w.K,
+            "values": {"normal": "N(0,1)/sqrt(N)", "uniform": "U[-1,1)", "integer": "{-4..4}"}.get(w.dist, w.dist),
+            "seed": w.seed,
+            "path": fgr.PATH_NAMES.get(path, str(path)),
+            "tile": tile,
+        },
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = COPY_BYTES
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -72,8 +72,14 @@ __device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles
   tn = in / gsz;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC>
-struct MfmaTile {
+// Compile-time shape of one kernel instance.
+//   BM x BN   output tile of a workgroup;  BK  reduction chunk per LDS stage
+//   WM x WN   waves per workgroup (each owns a (BM/WM) x (BN/WN) sub-tile)
+//   MINB      workgroups per CU the register budget must allow
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MINB_ = 1>
+struct MfmaConfig {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int kMinBlocks = MINB_;
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kWaveM = BM / WM;  // rows of C per wave
   static constexpr int kWaveN = BN / WN;  // columns of C per wave
@@ -88,7 +94,7 @@ struct MfmaTile {
   static constexpr int kLdsFloats = 2 * (BM * kLdA + BK * kLdB);
 
   static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be a multiple of 32x32");
-  static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+  static_assert(BK % 16 == 0, "BK must be a multiple of 16 (an even number of half-steps)");
   static_assert(BM * BK / 4 % kThreads == 0, "A chunk must split evenly over threads");
   static_assert(BK * BN / 4 % kThreads == 0, "B chunk must split evenly over threads");
   static_assert(kThreads % kAQuads == 0 && kThreads % kBQuads == 0,
@@ -114,11 +120,11 @@ __device__ __forceinline__ float4 load_quad(const float* __restrict__ p, bool ro
   return v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
+template <class T, bool VEC>
+__global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
     int K, int tiles_m, int tiles_n, int group) {
-  using T = MfmaTile<BM, BN, BK, WM, WN, VEC>;
+  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, WN = T::WN;
   __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
   float* const As0 = lds;
   float* const Bs0 = lds + 2 * BM * T::kLdA;
@@ -165,17 +171,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
     b_lds[i] = r * T::kLdB + 4 * (f % T::kBQuads);
   }
 
+  // Interior tiles whose reduction chunk lies wholly inside N load without guards.
+  const bool interior = VEC && (m0 + BM <= M) && (k0 + BN <= K);
+
   float4 ra[T::kAPerThread];
   float4 rb[T::kBPerThread];
 
   auto load_chunk = [&](int n0) {
+    if (interior && n0 + BK <= N) {
 #pragma unroll
-    for (int i = 0; i < T::kAPerThread; ++i)
-      ra[i] = load_quad<VEC>(a_ptr[i] + n0, a_row_ok[i], n0 + a_col[i], N);
+      for (int i = 0; i < T::kAPerThread; ++i) ra[i] = *reinterpret_cast<const float4*>(a_ptr[i] + n0);
 #pragma unroll
-    for (int i = 0; i < T::kBPerThread; ++i) {
-      const int n = n0 + b_row[i];
-      rb[i] = load_quad<VEC>(b_ptr[i] + (int64_t)n0 * K, n < N, b_col, K);
+      for (int i = 0; i < T::kBPerThread; ++i)
+        rb[i] = *reinterpret_cast<const float4*>(b_ptr[i] + (int64_t)n0 * K);
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::kAPerThread; ++i)
+        ra[i] = load_quad<VEC>(a_ptr[i] + n0, a_row_ok[i], n0 + a_col[i], N);
+#pragma unroll
+      for (int i = 0; i < T::kBPerThread; ++i) {
+        const int n = n0 + b_row[i];
+        rb[i] = load_quad<VEC>(b_ptr[i] + (int64_t)n0 * K, n < N, b_col, K);
+      }
     }
   };
   auto store_chunk = [&](int buf) {
@@ -187,51 +204,88 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
     for (int i = 0; i < T::kBPerThread; ++i) *reinterpret_cast<float4*>(Bs + b_lds[i]) = rb[i];
   };
 
+  // MFMA operands of one half-step (8 reduction indices): per 32-row block a
+  // float4 of A (indices 4*lg .. 4*lg+3), per 32-column block four B values.
+  struct Frag {
+    float4 a[T::kRB];
+    float b[T::kCB][4];
+  };
+  const int a_frag = (wm * T::kWaveM + li) * T::kLdA + 4 * lg;
+  const int b_frag = 4 * lg * T::kLdB + wn * T::kWaveN + li;
+  auto read_frag = [&](Frag& f, int buf, int h) {
+    const float* As = As0 + buf * BM * T::kLdA + a_frag + 8 * h;
+    const float* Bs = Bs0 + buf * BK * T::kLdB + b_frag + 8 * h * T::kLdB;
+#pragma unroll
+    for (int i = 0; i < T::kRB; ++i) f.a[i] = *reinterpret_cast<const float4*>(As + i * 32 * T::kLdA);
+#pragma unroll
+    for (int j = 0; j < T::kCB; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f.b[j][t] = Bs[t * T::kLdB + j * 32];
+    // keep these reads ahead of the MFMAs that follow (they feed the next
+    // half-step, so their latency hides under the current one)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   f32x16 acc[T::kRB][T::kCB];
 #pragma unroll
   for (int i = 0; i < T::kRB; ++i)
 #pragma unroll
     for (int j = 0; j < T::kCB; ++j) acc[i][j] = f32x16{};
 
-  const int a_frag = (wm * T::kWaveM + li) * T::kLdA + 4 * lg;
-  const int b_frag = 4 * lg * T::kLdB + wn * T::kWaveN + li;
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < T::kRB; ++i)
+#pragma unroll
+        for (int j = 0; j < T::kCB; ++j) {
+          const float av = t == 0 ? f.a[i].x : t == 1 ? f.a[i].y : t == 2 ? f.a[i].z : f.a[i].w;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, f.b[j][t], acc[i][j], 0, 0, 0);
+        }
+    // nothing from the code that follows (LDS writes, the barrier, the next
+    // reads) may be hoisted into this run of MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
+  // Software pipeline. Chunk c is consumed from LDS buffer c % 2 in H = BK/8
+  // half-steps; the operands of half-step h + 1 are read from LDS while the
+  // MFMAs of half-step h run (two register sets, f[0] and f[1]). Chunk c + 1
+  // is fetched from global memory at the top of iteration c, written to the
+  // other LDS buffer before the last half-step, and one barrier then both
+  // publishes it and releases buffer c % 2 (all its reads were issued before
+  // this barrier); the first operands of chunk c + 1 are read while the last
+  // half-step of chunk c computes.
+  constexpr int H = BK / 8;
   const int nchunks = (N + BK - 1) / BK;
+  Frag f[2];
   load_chunk(0);
   store_chunk(0);
   __syncthreads();
+  read_frag(f[0], 0, 0);
 
-  for (int c = 0; c < nchunks; ++c) {
+  // Steady state: every chunk but the last. (The last is peeled off so that the
+  // loop body has no data-dependent branch around its barrier.)
+  for (int c = 0; c + 1 < nchunks; ++c) {
     const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) load_chunk((c + 1) * BK);
-
-    const float* As = As0 + buf * BM * T::kLdA;
-    const float* Bs = Bs0 + buf * BK * T::kLdB;
+    load_chunk((c + 1) * BK);
 #pragma unroll
-    for (int h = 0; h < BK / 8; ++h) {
-      float4 a[T::kRB];
-      float b[T::kCB][4];
-#pragma unroll
-      for (int i = 0; i < T::kRB; ++i)
-        a[i] = *reinterpret_cast<const float4*>(As + a_frag + i * 32 * T::kLdA + 8 * h);
-#pragma unroll
-      for (int j = 0; j < T::kCB; ++j)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[j][t] = Bs[b_frag + (8 * h + t) * T::kLdB + j * 32];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < T::kRB; ++i)
-#pragma unroll
-          for (int j = 0; j < T::kCB; ++j) {
-            const float av = t == 0 ? a[i].x : t == 1 ? a[i].y : t == 2 ? a[i].z : a[i].w;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[j][t], acc[i][j], 0, 0, 0);
-          }
+    for (int h = 0; h + 1 < H; ++h) {
+      read_frag(f[(h + 1) & 1], buf, h + 1);
+      mma(f[h & 1]);
     }
-
-    if (more) store_chunk(buf ^ 1);
+    store_chunk(buf ^ 1);
     __syncthreads();
+    read_frag(f[H & 1], buf ^ 1, 0);
+    mma(f[(H - 1) & 1]);
+  }
+  {
+    const int buf = (nchunks - 1) & 1;
+#pragma unroll
+    for (int h = 0; h + 1 < H; ++h) {
+      read_frag(f[(h + 1) & 1], buf, h + 1);
+      mma(f[h & 1]);
+    }
+    mma(f[(H - 1) & 1]);
   }
 
   // Epilogue: element r of lane l in block (i, j) is row 8*(r/4) + 4*lg + r%4,

@@ -93,23 +93,27 @@ int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStre
   return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+template <class Cfg, bool VEC>
 int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
-  int tiles_m = (int)cdiv(M, BM);
-  int tiles_n = (int)cdiv(K, BN);
+  int tiles_m = (int)cdiv(M, Cfg::BM);
+  int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
-  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_kernel<BM, BN, BK, WM, WN, VEC>),
-                (int64_t)tiles_m * tiles_n, WM * WN * 64, args, s);
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_kernel<Cfg, VEC>),
+                (int64_t)tiles_m * tiles_n, Cfg::kThreads, args, s);
 }
+
+using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
+using Tile128 = fgr::MfmaConfig<128, 128, 16, 2, 2>;
+using Tile64 = fgr::MfmaConfig<64, 64, 16, 2, 2>;
 
 template <bool VEC>
 int launch_mfma_tile(int tile, const float* A, const float* B, float* C, int M, int N, int K,
                      hipStream_t s) {
   switch (tile) {
-    case FGR_TILE_256: return launch_mfma<256, 256, 16, 2, 2, VEC>(A, B, C, M, N, K, s);
-    case FGR_TILE_128: return launch_mfma<128, 128, 16, 2, 2, VEC>(A, B, C, M, N, K, s);
-    case FGR_TILE_64: return launch_mfma<64, 64, 16, 2, 2, VEC>(A, B, C, M, N, K, s);
+    case FGR_TILE_256: return launch_mfma<Tile256, VEC>(A, B, C, M, N, K, s);
+    case FGR_TILE_128: return launch_mfma<Tile128, VEC>(A, B, C, M, N, K, s);
+    case FGR_TILE_64: return launch_mfma<Tile64, VEC>(A, B, C, M, N, K, s);
     default: return FGR_ERR_BAD_PATH;
   }
 }
