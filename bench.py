@@ -66,20 +66,115 @@ def recorded_traffic(workload: str):
     return int(val.group(1))
 
 
+def _csv_rows(path):
+    import csv
+
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(directory, suffix):
+    for root, _, files in os.walk(directory):
+        for name in files:
+            if name.endswith(suffix):
+                return os.path.join(root, name)
+    raise FileNotFoundError(f"no *{suffix} under {directory}")
+
+
+def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_path, warmup=5):
+    """Write the rocprofv3 summary of one workload's dominant kernel.
+
+    trace_dir: a --kernel-trace --stats run; fetch_dir / write_dir: --pmc
+    FETCH_SIZE / WRITE_SIZE runs of bench.py --calibrate-copy. Each counter
+    is scaled by (known bytes of the plain 512 MiB device copy) / (what the
+    same counter reads for that copy)."""
+    stats = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
+    stats.sort(key=lambda r: float(r["TotalDurationNs"]), reverse=True)
+    top = stats[0]
+    # the dispatches of the timed steps: drop the warm-up launches
+    trace = [r for r in _csv_rows(_find(trace_dir, "kernel_trace.csv")) if r["Kernel_Name"] == top["Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    timed = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace[warmup:]]
+    timed_avg = sum(timed) / len(timed)
+
+    def per_dispatch(directory, counter):
+        rows = _csv_rows(_find(directory, "counter_collection.csv"))
+        kern = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and r["Kernel_Name"] == top["Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+        if not kern or not copy:
+            raise ValueError(f"{counter}: kernel or copy dispatches missing in {directory}")
+        k_kib = sum(kern) / len(kern)
+        c_kib = sum(copy) / len(copy)
+        factor = COPY_BYTES / (c_kib * 1024.0)
+        return k_kib, c_kib, factor
+
+    f_k, f_c, f_fac = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_k, w_c, w_fac = per_dispatch(write_dir, "WRITE_SIZE")
+    fetch_bytes = f_k * 1024.0 * f_fac
+    write_bytes = w_k * 1024.0 * w_fac
+    total = int(round(fetch_bytes + write_bytes))
+
+    import synth
+
+    w = synth.WORKLOADS[workload]
+    lines = [
+        f"# rocprofv3 summary: {top['Name']} on {workload} (M={w.M}, N={w.N}, K={w.K})",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):",
+        "",
+        *[f"    {c}" for c in commands],
+        "",
+        "## Kernel trace (--kernel-trace --stats)",
+        "",
+        "| kernel | calls | average ns | min ns | max ns |",
+        "|---|---|---|---|---|",
+        *[f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |" for r in stats],
+        "",
+        f"Timed dispatches (the {len(timed)} after the {warmup} warm-up launches): average "
+        f"{timed_avg:.0f} ns, min {min(timed)} ns, max {max(timed)} ns.",
+        "",
+        f"FLOP per launch 2MNK = {w.flops}: {w.flops / timed_avg / 1e3:.2f} TFLOP/s at the timed average. "
+        f"Algorithmic bytes 4(MN+NK+MK) = {w.algorithmic_bytes}: {w.algorithmic_bytes / timed_avg:.1f} GB/s.",
+        f"timed-average-ns: {timed_avg:.0f}",
+        "",
+        "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE, KiB per dispatch)",
+        "",
+        "| counter | kernel KiB/dispatch | 512 MiB copy KiB/dispatch | scale (copy bytes / counter bytes) | kernel bytes |",
+        "|---|---|---|---|---|",
+        f"| FETCH_SIZE | {f_k:.1f} | {f_c:.1f} | {f_fac:.4f} | {fetch_bytes:.0f} |",
+        f"| WRITE_SIZE | {w_k:.1f} | {w_c:.1f} | {w_fac:.4f} | {write_bytes:.0f} |",
+        "",
+        f"hbm-bytes-per-launch: {total}",
+        f"ratio to algorithmic bytes: {total / w.algorithmic_bytes:.2f}",
+        f"kernel-source-sha256: {kernel_source_hash()}",
+        "",
+    ]
+    with open(out_path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    return out_path
+
+
 def cpu_baseline(w, A, B, target_s: float):
     """Time the oracle on the first R rows of A (R sized for about target_s)."""
     import oracle
 
     threads = oracle.max_threads()
-    rows = 8
-    t0 = time.perf_counter()
-    oracle.gemm(A[:rows], B, threads=threads)
-    t_probe = time.perf_counter() - t0
-    rows_fit = int(rows * target_s / max(t_probe, 1e-6))
-    R = max(rows, min(w.M, rows_fit))
-    t0 = time.perf_counter()
-    oracle.gemm(A[:R], B, threads=threads)
-    elapsed = time.perf_counter() - t0
+    rows = min(8, w.M)
+    while True:  # probe until a timing is long enough to extrapolate from
+        t0 = time.perf_counter()
+        oracle.gemm(A[:rows], B, threads=threads)
+        probe = time.perf_counter() - t0
+        if probe >= 0.5 or rows >= w.M:
+            break
+        rows = min(w.M, rows * 4)
+    R = max(rows, min(w.M, int(rows * target_s / max(probe, 1e-6))))
+    elapsed = probe
+    if R > rows:
+        t0 = time.perf_counter()
+        oracle.gemm(A[:R], B, threads=threads)
+        elapsed = time.perf_counter() - t0
     flops = 2.0 * R * w.N * w.K
     if w.M == 1:
         value = 4.0 * (R * w.N + w.N * w.K + R * w.K) / elapsed / 1e9
@@ -109,7 +204,16 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run a plain 512 MiB device copy three times "
                          "(the known-size reference for HBM byte counters)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/<workload>_traffic.md from three rocprofv3 output folders and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="(with --summarize) a command that produced the folders, recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize:
+        out = os.path.join(ROOT, "profiles", f"{args.workload}_traffic.md")
+        print(summarize_profiles(args.workload, *args.summarize, args.command, out, args.warmup))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(
