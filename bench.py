@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X: 256 CU x 256 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 METRIC = "FP32 GEMM TFLOP/s at M=8192,N=6144,K=4096; % of MI355X FP32 MFMA peak"
-KERNEL_SOURCES = ["gemm_mfma.hpp", "gemv.hpp", "solve.hip"]
+KERNEL_SOURCES = ["gemm_mfma.hpp", "gemm_mfma_dma.hpp", "gemv.hpp", "solve.hip"]
 COPY_BYTES = 512 << 20
 
 
@@ -199,6 +199,9 @@ def main() -> int:
     ap.add_argument("--workload", default="leetgpu8192")
     ap.add_argument("--path", type=int, default=0, help="force an FGR path (0 = auto)")
     ap.add_argument("--tile", type=int, default=0, help="force an MFMA output tile (0 = auto)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="cycle through this many copies of B (0 = 4 for the matrix-vector workload, "
+                         "whose 256 MiB B would otherwise partly stay in the 256 MB last-level cache; 1 otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -240,19 +243,22 @@ def main() -> int:
     A, B = synth.workload_inputs(w)
     dev = torch.device("cuda:0")
     dA = torch.from_numpy(A.ravel()).to(dev)
-    dB = torch.from_numpy(B.ravel()).to(dev)
+    copies = args.rotate or (4 if w.M == 1 else 1)
+    dBs = [torch.from_numpy(B.ravel()).to(dev) for _ in range(copies)]
+    dB = dBs[0]
     dC = torch.empty(w.M * w.K, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     path = args.path or fgr.select_path(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), w.M, w.N, w.K)
-    tile = args.tile or (fgr.select_tile(w.M, w.K) if path in (fgr.PATH_MFMA_VEC, fgr.PATH_MFMA_SCALAR) else 0)
+    tile = args.tile or (fgr.select_tile(w.M, w.K)
+                         if path in (fgr.PATH_MFMA_VEC, fgr.PATH_MFMA_SCALAR, fgr.PATH_MFMA_DMA) else 0)
     stream = torch.cuda.current_stream()
 
-    def step():
-        fgr.solve_path(dA, dB, dC, w.M, w.N, w.K, path, tile, stream=stream)
+    def step(i):
+        fgr.solve_path(dA, dBs[i % copies], dC, w.M, w.N, w.K, path, tile, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -260,7 +266,7 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        step()
+        step(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -311,6 +317,7 @@ def main() -> int:
             "seed": w.seed,
             "path": fgr.PATH_NAMES.get(path, str(path)),
             "tile": tile,
+            "b_copies": copies,
         },
         "roofline": roof,
         "cpu_baseline": None,

@@ -35,7 +35,9 @@ PATH_MFMA_VEC = 1
 PATH_MFMA_SCALAR = 2
 PATH_GEMV_VEC = 3
 PATH_GEMV_SCALAR = 4
+PATH_MFMA_DMA = 5
 PATH_NAMES = {
+    PATH_MFMA_DMA: "mfma_dma",
     PATH_MFMA_VEC: "mfma_vec",
     PATH_MFMA_SCALAR: "mfma_scalar",
     PATH_GEMV_VEC: "gemv_vec",

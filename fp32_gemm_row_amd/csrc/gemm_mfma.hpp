@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fgr {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -102,22 +104,80 @@ struct MfmaConfig {
   static_assert(kLdsFloats * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
-// Load one float4 slot, zero-filling every element outside the matrix.
-// VEC: the four elements are either all inside or all outside (rows are
-// 16-byte aligned and the extent is a multiple of 4) and one 128-bit load is
-// used. Otherwise each element is checked and loaded on its own.
+// One float4 slot of a chunk, loaded branch-free: an element outside the
+// matrix reads a harmless in-bounds address instead (`safe`, the matrix base)
+// and its bit in `ok` is cleared; mask_quad() then replaces it by zero when
+// the slot is written to LDS, so padding never carries real data. VEC: the
+// four elements are all inside or all outside (rows 16-byte aligned, extent a
+// multiple of 4) and one 128-bit load is used; otherwise each element is
+// checked and loaded on its own.
 template <bool VEC>
-__device__ __forceinline__ float4 load_quad(const float* __restrict__ p, bool row_ok, int col, int ncols) {
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+__device__ __forceinline__ float4 load_quad(const float* __restrict__ p, const float* __restrict__ safe,
+                                            bool row_ok, int col, int ncols, unsigned& ok) {
   if (VEC) {
-    if (row_ok && col < ncols) v = *reinterpret_cast<const float4*>(p);
-  } else if (row_ok) {
-    if (col + 0 < ncols) v.x = p[0];
-    if (col + 1 < ncols) v.y = p[1];
-    if (col + 2 < ncols) v.z = p[2];
-    if (col + 3 < ncols) v.w = p[3];
+    const bool in = row_ok && col < ncols;
+    ok = in ? 0xfu : 0u;
+    return *reinterpret_cast<const float4*>(in ? p : safe);
+  } else {
+    float e[4];
+    ok = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = row_ok && col + i < ncols;
+      ok |= in ? 1u << i : 0u;
+      e[i] = *(in ? p + i : safe);
+    }
+    return make_float4(e[0], e[1], e[2], e[3]);
   }
-  return v;
+}
+
+__device__ __forceinline__ float4 mask_quad(float4 v, unsigned ok) {
+  return make_float4(ok & 1u ? v.x : 0.f, ok & 2u ? v.y : 0.f, ok & 4u ? v.z : 0.f, ok & 8u ? v.w : 0.f);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
+template <int MASK, int PER, int N>
+__device__ __forceinline__ void sched_pairs() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(MASK, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, PER, 0);
+    sched_pairs<MASK, PER, N - 1>();
+  }
+}
+
+// Interleave the memory instructions of a half-step with its MFMAS MFMAs:
+// each LDS read (NR), global load (NV) or LDS write (NW) is followed by a few
+// MFMAs, so the wave never issues a burst of memory instructions while the
+// matrix core idles.
+template <int MFMAS, int NV, int NW, int NR>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int others = NV + NW + NR;
+  constexpr int per = others ? MFMAS / (others + 1) : MFMAS;
+  sched_pairs<kSchedDsRead, per, NR>();
+  sched_pairs<kSchedVmemRead, per, NV>();
+  sched_pairs<kSchedDsWrite, per, NW>();
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, MFMAS - per * others, 0);
+}
+
+// Number of load slots s in [0, slots) with s * steps / slots == h.
+constexpr int slots_in_step(int h, int steps, int slots) {
+  int n = 0;
+  for (int s = 0; s < slots; ++s)
+    if (s * steps / slots == h) ++n;
+  return n;
 }
 
 template <class T, bool VEC>
@@ -125,6 +185,7 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
     int K, int tiles_m, int tiles_n, int group) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, WN = T::WN;
+  constexpr int H = BK / 8;  // half-steps per chunk
   __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
   float* const As0 = lds;
   float* const Bs0 = lds + 2 * BM * T::kLdA;
@@ -171,37 +232,25 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
     b_lds[i] = r * T::kLdB + 4 * (f % T::kBQuads);
   }
 
-  // Interior tiles whose reduction chunk lies wholly inside N load without guards.
-  const bool interior = VEC && (m0 + BM <= M) && (k0 + BN <= K);
-
-  float4 ra[T::kAPerThread];
-  float4 rb[T::kBPerThread];
-
-  auto load_chunk = [&](int n0) {
-    if (interior && n0 + BK <= N) {
-#pragma unroll
-      for (int i = 0; i < T::kAPerThread; ++i) ra[i] = *reinterpret_cast<const float4*>(a_ptr[i] + n0);
-#pragma unroll
-      for (int i = 0; i < T::kBPerThread; ++i)
-        rb[i] = *reinterpret_cast<const float4*>(b_ptr[i] + (int64_t)n0 * K);
-    } else {
-#pragma unroll
-      for (int i = 0; i < T::kAPerThread; ++i)
-        ra[i] = load_quad<VEC>(a_ptr[i] + n0, a_row_ok[i], n0 + a_col[i], N);
-#pragma unroll
-      for (int i = 0; i < T::kBPerThread; ++i) {
-        const int n = n0 + b_row[i];
-        rb[i] = load_quad<VEC>(b_ptr[i] + (int64_t)n0 * K, n < N, b_col, K);
-      }
+  // Registers staging the next chunk: slots 0 .. kAPerThread-1 are A's, the
+  // rest B's.
+  constexpr int kSlots = T::kAPerThread + T::kBPerThread;
+  float4 stage[kSlots];
+  unsigned stage_ok[kSlots];
+  auto load_slot = [&](int s, int n0) {
+    if (s < T::kAPerThread)
+      stage[s] = load_quad<VEC>(a_ptr[s] + n0, A, a_row_ok[s], n0 + a_col[s], N, stage_ok[s]);
+    else {
+      const int i = s - T::kAPerThread;
+      stage[s] = load_quad<VEC>(b_ptr[i] + (int64_t)n0 * K, B, n0 + b_row[i] < N, b_col, K, stage_ok[s]);
     }
   };
-  auto store_chunk = [&](int buf) {
-    float* As = As0 + buf * BM * T::kLdA;
-    float* Bs = Bs0 + buf * BK * T::kLdB;
-#pragma unroll
-    for (int i = 0; i < T::kAPerThread; ++i) *reinterpret_cast<float4*>(As + a_lds[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < T::kBPerThread; ++i) *reinterpret_cast<float4*>(Bs + b_lds[i]) = rb[i];
+  auto store_slot = [&](int s, int buf) {
+    const float4 v = mask_quad(stage[s], stage_ok[s]);
+    if (s < T::kAPerThread)
+      *reinterpret_cast<float4*>(As0 + buf * BM * T::kLdA + a_lds[s]) = v;
+    else
+      *reinterpret_cast<float4*>(Bs0 + buf * BK * T::kLdB + b_lds[s - T::kAPerThread]) = v;
   };
 
   // MFMA operands of one half-step (8 reduction indices): per 32-row block a
@@ -221,9 +270,6 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
     for (int j = 0; j < T::kCB; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t) f.b[j][t] = Bs[t * T::kLdB + j * 32];
-    // keep these reads ahead of the MFMAs that follow (they feed the next
-    // half-step, so their latency hides under the current one)
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   f32x16 acc[T::kRB][T::kCB];
@@ -242,24 +288,30 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
           const float av = t == 0 ? f.a[i].x : t == 1 ? f.a[i].y : t == 2 ? f.a[i].z : f.a[i].w;
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, f.b[j][t], acc[i][j], 0, 0, 0);
         }
-    // nothing from the code that follows (LDS writes, the barrier, the next
-    // reads) may be hoisted into this run of MFMAs
-    __builtin_amdgcn_sched_barrier(0);
   };
+
+  constexpr int kMfmas = T::kRB * T::kCB * 4;  // per wave and half-step
+  constexpr int kReads = T::kRB + 2 * T::kCB;  // b128 A reads, paired 32-bit B reads
+  constexpr int kLoadInsts = VEC ? 1 : 4;      // global loads per slot
 
   // Software pipeline. Chunk c is consumed from LDS buffer c % 2 in H = BK/8
   // half-steps; the operands of half-step h + 1 are read from LDS while the
   // MFMAs of half-step h run (two register sets, f[0] and f[1]). Chunk c + 1
-  // is fetched from global memory at the top of iteration c, written to the
-  // other LDS buffer before the last half-step, and one barrier then both
-  // publishes it and releases buffer c % 2 (all its reads were issued before
-  // this barrier); the first operands of chunk c + 1 are read while the last
-  // half-step of chunk c computes.
-  constexpr int H = BK / 8;
+  // is fetched into registers during the first H - 2 half-steps of chunk c and
+  // written to the other LDS buffer during half-step H - 2 (with H = 2: all
+  // loads at the top of half-step 0, all writes after it). One barrier before
+  // the last half-step then both publishes chunk c + 1 and releases buffer
+  // c % 2 (all its reads were issued and completed before it); the first
+  // operands of chunk c + 1 are read while the last half-step of chunk c
+  // computes. The LDS writes into buffer (c + 1) % 2 are safe because the
+  // barrier of chunk c - 1 released it.
+  constexpr int kLoadSteps = H >= 3 ? H - 2 : 0;
   const int nchunks = (N + BK - 1) / BK;
   Frag f[2];
-  load_chunk(0);
-  store_chunk(0);
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) load_slot(s, 0);
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) store_slot(s, 0);
   __syncthreads();
   read_frag(f[0], 0, 0);
 
@@ -267,24 +319,46 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
   // loop body has no data-dependent branch around its barrier.)
   for (int c = 0; c + 1 < nchunks; ++c) {
     const int buf = c & 1;
-    load_chunk((c + 1) * BK);
+    const int n1 = (c + 1) * BK;
+    if (kLoadSteps == 0) {
 #pragma unroll
-    for (int h = 0; h + 1 < H; ++h) {
+      for (int s = 0; s < kSlots; ++s) load_slot(s, n1);
+    }
+    static_for<0, H - 1>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      constexpr int n_slots = kLoadSteps > 0 ? slots_in_step(h, kLoadSteps, kSlots) : 0;
+      constexpr bool writes = kLoadSteps > 0 && h == H - 2;
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s)
+        if (kLoadSteps > 0 && s * kLoadSteps / kSlots == h) load_slot(s, n1);
+      if (writes) {
+#pragma unroll
+        for (int s = 0; s < kSlots; ++s) store_slot(s, buf ^ 1);
+      }
       read_frag(f[(h + 1) & 1], buf, h + 1);
       mma(f[h & 1]);
+      sched_interleave<kMfmas, n_slots * kLoadInsts, writes ? kSlots : 0, kReads>();
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (kLoadSteps == 0) {
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) store_slot(s, buf ^ 1);
     }
-    store_chunk(buf ^ 1);
     __syncthreads();
     read_frag(f[H & 1], buf ^ 1, 0);
     mma(f[(H - 1) & 1]);
+    sched_interleave<kMfmas, 0, 0, kReads>();
+    __builtin_amdgcn_sched_barrier(0);
   }
   {
     const int buf = (nchunks - 1) & 1;
-#pragma unroll
-    for (int h = 0; h + 1 < H; ++h) {
+    static_for<0, H - 1>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
       read_frag(f[(h + 1) & 1], buf, h + 1);
       mma(f[h & 1]);
-    }
+      sched_interleave<kMfmas, 0, 0, kReads>();
+      __builtin_amdgcn_sched_barrier(0);
+    });
     mma(f[(H - 1) & 1]);
   }
 

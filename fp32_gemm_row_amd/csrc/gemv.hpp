@@ -9,11 +9,13 @@
 // segment of every row of B - and the whole reduction for them. Its threads
 // split the rows of B: LPR lanes cover the 32 columns of one row (8 lanes x
 // float4 on the 128-bit path, 32 lanes x float on the 32-bit path) and the
-// RPI = threads / LPR row groups walk rows r, r + RPI, r + 2 RPI, ...; the
-// reduction loop is unrolled so that each lane keeps several independent
-// loads in flight. A is staged through LDS in chunks and read from there.
-// The RPI partial sums of every column are then added in LDS. No atomics and
-// no workspace: the result is deterministic.
+// RPI = NT / LPR row groups walk rows r, r + RPI, r + 2 RPI, ...; the loop is
+// unrolled so that each lane keeps UNROLL independent loads in flight (with
+// NT = 1024 and UNROLL = 8 a workgroup has 1024 rows = 128 KiB of B in
+// flight). A is staged through LDS in chunks of up to 8192 elements. The row
+// groups' partial sums are first added across the lanes of each wave (lanes
+// that share columns differ by multiples of LPR), then across waves in LDS.
+// No atomics and no workspace: the result is deterministic.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,7 +24,7 @@
 namespace fgr {
 
 constexpr int kGemvCols = 32;       // output columns per workgroup
-constexpr int kGemvAChunk = 2048;   // elements of A staged in LDS at a time
+constexpr int kGemvAChunk = 8192;   // elements of A staged in LDS at a time
 
 template <int VW, int NT, int UNROLL>
 __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
@@ -30,13 +32,16 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
                                                   float* __restrict__ C, int N, int K) {
   constexpr int LPR = kGemvCols / VW;  // lanes per row segment
   constexpr int RPI = NT / LPR;        // rows in flight per workgroup step
+  constexpr int WAVES = NT / 64;
   static_assert(VW == 1 || VW == 4, "vector width");
-  static_assert(NT % LPR == 0, "threads must cover whole row segments");
+  static_assert(NT % 64 == 0 && 64 % LPR == 0, "waves must hold whole row segments");
 
   __shared__ float a_s[kGemvAChunk];
-  __shared__ float part[RPI][kGemvCols + 1];
+  __shared__ float part[WAVES][kGemvCols];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int cl = tid % LPR;  // column lane
   const int rl = tid / LPR;  // row group
   const int col = blockIdx.x * kGemvCols + cl * VW;
@@ -69,13 +74,21 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
     }
   }
 
+  // lanes cl, cl + LPR, cl + 2 LPR, ... of a wave hold the same columns
 #pragma unroll
-  for (int e = 0; e < VW; ++e) part[rl][cl * VW + e] = acc[e];
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < VW; ++e) part[wave][cl * VW + e] = acc[e];
+  }
   __syncthreads();
   if (tid < kGemvCols) {
     const int c = blockIdx.x * kGemvCols + tid;
     float s = 0.f;
-    for (int r = 0; r < RPI; ++r) s += part[r][tid];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += part[w][tid];
     if (c < K) C[c] = s;
   }
 }

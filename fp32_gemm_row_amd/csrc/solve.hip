@@ -11,6 +11,7 @@
 
 #include "fp32_gemm_row.h"
 #include "gemm_mfma.hpp"
+#include "gemm_mfma_dma.hpp"
 #include "gemv.hpp"
 
 namespace {
@@ -72,18 +73,24 @@ bool mfma_vec_ok(const float* A, const float* B, const float* C, int N, int K) {
 
 bool gemv_vec_ok(const float* B, int K) { return K % 4 == 0 && aligned(B, 16); }
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-int select_path(const float* A, const float* B, const float* C, int M, int N, int K) {
-  if (M == 1) return gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR;
-  return mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
+// Whole 256 x 256 tiles and an even number of 32-deep chunks: no padding.
+bool mfma_dma_ok(const float* A, const float* B, const float* C, int M, int N, int K) {
+  return mfma_vec_ok(A, B, C, N, K) && M % 256 == 0 && K % 256 == 0 && N % 64 == 0;
 }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int select_tile(int M, int K, int cus) {
   if (cus <= 0) cus = kDefaultCus;
   if (cdiv(M, 256) * cdiv(K, 256) >= cus) return FGR_TILE_256;
   if (cdiv(M, 128) * cdiv(K, 128) >= cus) return FGR_TILE_128;
   return FGR_TILE_64;
+}
+
+int select_path(const float* A, const float* B, const float* C, int M, int N, int K, int cus) {
+  if (M == 1) return gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR;
+  if (mfma_dma_ok(A, B, C, M, N, K) && select_tile(M, K, cus) == FGR_TILE_256) return FGR_PATH_MFMA_DMA;
+  return mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
 }
 
 int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStream_t stream) {
@@ -104,6 +111,16 @@ int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, h
 }
 
 using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
+using TileDma = fgr::DmaConfig<256, 256, 32, 2, 4>;
+
+int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  int tiles_m = M / TileDma::BM;
+  int tiles_n = K / TileDma::BN;
+  int group = kTileGroup;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDma>),
+                (int64_t)tiles_m * tiles_n, TileDma::kThreads, args, s);
+}
 using Tile128 = fgr::MfmaConfig<128, 128, 16, 2, 2>;
 using Tile64 = fgr::MfmaConfig<64, 64, 16, 2, 2>;
 
@@ -120,7 +137,7 @@ int launch_mfma_tile(int tile, const float* A, const float* B, float* C, int M, 
 
 template <int VW>
 int launch_gemv(const float* A, const float* B, float* C, int N, int K, hipStream_t s) {
-  constexpr int NT = 256;
+  constexpr int NT = 1024;  // 16 waves: 1024 rows of B in flight per workgroup
   void* args[] = {&A, &B, &C, &N, &K};
   return launch(reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, NT, 8>),
                 cdiv(K, fgr::kGemvCols), NT, args, s);
@@ -130,11 +147,14 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
         int tile) {
   int rc = check_args(A, B, C, M, N, K);
   if (rc != FGR_OK) return rc;
-  const int chosen = select_path(A, B, C, M, N, K);
-  if (path == FGR_PATH_AUTO) path = chosen;
   switch (path) {
+    case FGR_PATH_AUTO: break;
     case FGR_PATH_MFMA_VEC:
       if (!mfma_vec_ok(A, B, C, N, K)) return FGR_ERR_BAD_PATH;
+      break;
+    case FGR_PATH_MFMA_DMA:
+      if (!mfma_dma_ok(A, B, C, M, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256))
+        return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SCALAR: break;
     case FGR_PATH_GEMV_VEC:
@@ -152,9 +172,15 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   rc = current_device(&cus);
   if (rc != FGR_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (path == FGR_PATH_AUTO) {
+    path = select_path(A, B, C, M, N, K, cus);
+    // a forced smaller tile keeps the register-staged kernel
+    if (path == FGR_PATH_MFMA_DMA && tile != FGR_TILE_AUTO && tile != FGR_TILE_256) path = FGR_PATH_MFMA_VEC;
+  }
   if (tile == FGR_TILE_AUTO) tile = select_tile(M, K, cus);
 
   switch (path) {
+    case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, N, K, s);
@@ -183,7 +209,7 @@ int fgr_solve_path(const float* A, const float* B, float* C, int M, int N, int K
 int fgr_select_path(const float* A, const float* B, const float* C, int M, int N, int K) {
   const int rc = check_args(A, B, C, M, N, K);
   if (rc != FGR_OK) return rc;
-  return select_path(A, B, C, M, N, K);
+  return select_path(A, B, C, M, N, K, kDefaultCus);
 }
 
 int fgr_select_tile(int M, int K, int num_cus) {

@@ -39,15 +39,18 @@
  *   Any 4-byte-aligned pointers are accepted. When N % 4 == 0, K % 4 == 0
  *   and A, B, C are 16-byte aligned the 128-bit load path is used; otherwise
  *   a path with 32-bit loads (the role of the scalar fallback of the LeetGPU
- *   write-up, section "V2: Vectorized float4 Transfers"). M == 1 takes the
- *   bandwidth-bound matrix-vector path.
+ *   write-up, section "V2: Vectorized float4 Transfers"). Problems made of
+ *   whole 256 x 256 tiles (M % 256 == 0, K % 256 == 0, N % 64 == 0, and
+ *   enough tiles to fill the device) copy A and B straight from global memory
+ *   into LDS (the role of the cp.async pipeline of the write-up's section
+ *   "V4"). M == 1 takes the bandwidth-bound matrix-vector path.
  *
  * Errors
  *   Every entry point returns 0 (FGR_OK) on success or a negative FGR_ERR_*
  *   code. Argument errors are detected on the host before any HIP call, and
- *   nothing is enqueued then. FGR_ERR_LAUNCH reports a HIP error right after
- *   the launch (from hipGetLastError); errors raised later, while the kernel
- *   runs, surface at the caller's next synchronisation.
+ *   nothing is enqueued then. FGR_ERR_LAUNCH reports an error returned by the
+ *   kernel launch itself (hipLaunchKernel); errors raised later, while the
+ *   kernel runs, surface at the caller's next synchronisation.
  *
  * Limits
  *   The problem statement guarantees 1 <= M, N, K <= 8192 (LeetGPU
@@ -77,6 +80,9 @@ extern "C" {
 #define FGR_PATH_MFMA_SCALAR 2 /* FP32 MFMA, 32-bit loads; any shape and 4-B alignment */
 #define FGR_PATH_GEMV_VEC 3    /* matrix-vector (M == 1), 128-bit loads of B; needs K%4 == 0 and 16-B aligned B, C */
 #define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector (M == 1), 32-bit loads */
+#define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, whole 256x256 tiles fed by direct global->LDS copies;
+                                  needs the MFMA_VEC conditions and M % 256 == 0, K % 256 == 0,
+                                  N % 64 == 0 (tile 256 only) */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0
@@ -109,15 +115,16 @@ int fgr_solve_default(const float *A, const float *B, float *C, int M, int N, in
  * "Controlled Comparison", build each variant separately). path is an
  * FGR_PATH_* value, tile an FGR_TILE_* value (ignored by the GEMV paths).
  * Returns FGR_ERR_BAD_PATH if that path or tile cannot handle these arguments
- * (e.g. a VEC path with N % 4 != 0, a GEMV path with M != 1, an unknown value).
+ * (e.g. a VEC path with N % 4 != 0, a GEMV path with M != 1, the DMA path
+ * with a tile other than 256 or a partial tile, an unknown value).
  */
 int fgr_solve_path(const float *A, const float *B, float *C, int M, int N, int K, void *stream,
                    int path, int tile);
 
 /*
  * fgr_select_path - the FGR_PATH_* value solve() would take for these
- * arguments, or a negative FGR_ERR_* code for invalid arguments. Host only:
- * makes no HIP call.
+ * arguments on a 256-CU device, or a negative FGR_ERR_* code for invalid
+ * arguments. Host only: makes no HIP call.
  */
 int fgr_select_path(const float *A, const float *B, const float *C, int M, int N, int K);
 

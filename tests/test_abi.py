@@ -105,6 +105,12 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_SCALAR) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 1, 8, 6, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
+    # the direct-copy path needs whole 256x256 tiles, N % 64 == 0 and tile 256
+    assert call(lib, A0, B0, C0, 512, 96, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 500, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 500, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA, 128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     # unknown path or tile values
     assert call(lib, A0, B0, C0, 8, 8, 8, 99) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 8, 8, 8, fgr.PATH_MFMA_VEC, 100) == fgr.ERR_BAD_PATH
@@ -112,7 +118,11 @@ def test_forced_path_rejections(lib):
 
 def test_path_selection_rules():
     sp = fgr.select_path
-    assert sp(A0, B0, C0, 8192, 6144, 4096) == fgr.PATH_MFMA_VEC
+    assert sp(A0, B0, C0, 8192, 6144, 4096) == fgr.PATH_MFMA_DMA
+    assert sp(A0, B0, C0, 4096, 4096, 4096) == fgr.PATH_MFMA_DMA
+    assert sp(A0, B0, C0, 4096, 4064, 4096) == fgr.PATH_MFMA_VEC  # N % 64 != 0
+    assert sp(A0, B0, C0, 4000, 4096, 4096) == fgr.PATH_MFMA_VEC  # partial row tile
+    assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_VEC  # too few 256x256 tiles
     assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_SCALAR
     assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_MFMA_SCALAR
     assert sp(A0 + 4, B0, C0, 8, 8, 8) == fgr.PATH_MFMA_SCALAR

@@ -88,6 +88,8 @@ def paths_for(M, N, K):
         out.append((fgr.PATH_MFMA_SCALAR, tile))
         if N % 4 == 0 and K % 4 == 0:
             out.append((fgr.PATH_MFMA_VEC, tile))
+    if M % 256 == 0 and K % 256 == 0 and N % 64 == 0:
+        out.append((fgr.PATH_MFMA_DMA, fgr.TILE_256))
     if M == 1:
         out.append((fgr.PATH_GEMV_SCALAR, 0))
         if K % 4 == 0:
@@ -117,6 +119,8 @@ EXACT_SHAPES = [
     (70, 70, 1), (70, 70, 3), (70, 70, 4), (70, 70, 5),
     (1, 8, 4), (1, 1000, 999), (1, 4097, 1028), (1, 17, 33),
     (513, 600, 515), (300, 2050, 260),
+    # whole 256x256 tiles: the direct global->LDS copy path
+    (256, 64, 256), (256, 128, 512), (512, 192, 256), (768, 320, 512),
 ]
 
 
@@ -163,6 +167,7 @@ def test_cube256_integer_bit_exact():
     assert_exact(gpu_gemm(A, B), Cref, "cube256 integer auto")
     for tile in ALL_TILES:
         assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_VEC, tile), Cref, f"cube256 integer tile={tile}")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256), Cref, "cube256 integer direct-copy path")
 
 
 @pytest.mark.parametrize("name", ["cube256", "ragged1023"])
