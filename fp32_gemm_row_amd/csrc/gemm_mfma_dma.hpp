@@ -1,15 +1,23 @@
 // FP32 MFMA GEMM for whole tiles, fed by direct global->LDS loads.
 //
-// Same product, tiling, operand layout and reduction order as gemm_mfma.hpp,
-// for problems whose every tile and every reduction chunk is full (M % BM,
-// K % BN and N % (2 BK) all zero, 16-byte aligned rows): no element needs zero
-// padding, so each chunk of A and B can be copied from global memory straight
-// into LDS with global_load_lds_dwordx4 (16 bytes per lane, written to LDS at
-// the M0 base + 16 * lane), the gfx950 counterpart of the cp.async copies of
-// the LeetGPU write-up's section "V4: Hardware-Asynchronous cp.async
-// Pipeline". The data never passes through VGPRs, so the loads do not compete
-// with the MFMAs for register-file bandwidth, and no LDS write instructions
-// are issued.
+// Same product, tiling and operand layout as gemm_mfma.hpp, for rows that are
+// 16-byte aligned (N % 4 == 0, K % 4 == 0, aligned bases) and N >= 64. Every
+// reduction chunk but the first is copied from global memory straight into
+// LDS with global_load_lds_dwordx4 (16 bytes per lane, written to LDS at the
+// M0 base + 16 * lane), the gfx950 counterpart of the cp.async copies of the
+// LeetGPU write-up's section "V4: Hardware-Asynchronous cp.async Pipeline".
+// That data never passes through VGPRs, so the copies do not compete with the
+// MFMAs for register-file bandwidth, and no LDS write instructions are issued.
+//
+// Ragged edges. Rows of A beyond M and columns of B beyond K only feed
+// outputs that are never stored, so their copies read a clamped in-bounds
+// address (the last row / last column quad) and the epilogue guards the
+// stores. Reduction indices beyond N would feed real outputs and must be
+// zero: the chunks are aligned to the END of the reduction (chunk c covers
+// n in [N - BK*(T - c), N - BK*(T - c) + BK), T = ceil(N / BK)), so that only
+// chunk 0 can reach below n = 0; chunk 0 is loaded through registers with
+// every element outside [0, N) set to zero (the zero padding of the study
+// notes' section 4) and written to LDS in the same layout.
 //
 // LDS layout (two stages, each a separate LDS object so that the compiler can
 // tell reads of one stage from copies into the other):
@@ -87,25 +95,30 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
 
   // Copy sources for this lane. A copy j of this wave fills rows
   // [R, R + 8), R = 8 * (wave * kACopies + j): lane L lands in row R + L / 8
-  // at stored position L % 8, which holds quad (L % 8) ^ swz(row).
+  // at stored position L % 8, which holds quad (L % 8) ^ swz(row). Rows past
+  // M read row M - 1 instead (their outputs are not stored).
   const float* a_src[T::kACopies];
   int a_dst[T::kACopies];  // LDS float offset of the copy's 1 KiB block
+  int a_quad[T::kACopies];
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
     const int blk = wave * T::kACopies + j;
     const int r = blk * T::kRowsPerCopy + lane / T::kQuads;
     const int q = (lane % T::kQuads) ^ a_swizzle(r);
-    a_src[j] = A + (int64_t)(m0 + r) * N + 4 * q;
+    const int row = m0 + r < M ? m0 + r : M - 1;
+    a_src[j] = A + (int64_t)row * N + 4 * q;
     a_dst[j] = blk * 256;
+    a_quad[j] = q;
   }
   // B copy j of this wave fills chunk row wave * kBCopies + j; lane L copies
-  // columns 4L .. 4L + 3.
+  // columns 4L .. 4L + 3 (past K: the last quad instead, not stored).
   const float* b_src[T::kBCopies];
   int b_dst[T::kBCopies];
+  const int b_col = k0 + 4 * lane < K ? k0 + 4 * lane : K - 4;
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
     const int r = wave * T::kBCopies + j;
-    b_src[j] = B + (int64_t)r * K + k0 + 4 * lane;
+    b_src[j] = B + (int64_t)r * K + b_col;
     b_dst[j] = r * T::BN;
   }
 
@@ -116,6 +129,32 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j)
       copy16_to_lds(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+  };
+  // The first chunk (n0 <= 0): the same placement through registers, with
+  // every element whose n lies outside [0, N) replaced by zero. N % 4 == 0 and
+  // n0 % 4 == 0, so a quad is wholly inside or wholly outside.
+  auto load_first_chunk = [&](int n0, float* As, float* Bs) {
+    float4 va[T::kACopies], vb[T::kBCopies];
+    bool oka[T::kACopies], okb[T::kBCopies];
+#pragma unroll
+    for (int j = 0; j < T::kACopies; ++j) {
+      const int n = n0 + 4 * a_quad[j];
+      oka[j] = n >= 0 && n < N;
+      va[j] = *reinterpret_cast<const float4*>(oka[j] ? a_src[j] + n0 : A);
+    }
+#pragma unroll
+    for (int j = 0; j < T::kBCopies; ++j) {
+      const int n = n0 + wave * T::kBCopies + j;
+      okb[j] = n >= 0 && n < N;
+      vb[j] = *reinterpret_cast<const float4*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
+    }
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < T::kACopies; ++j)
+      *reinterpret_cast<float4*>(As + a_dst[j] + 4 * lane) = oka[j] ? va[j] : zero;
+#pragma unroll
+    for (int j = 0; j < T::kBCopies; ++j)
+      *reinterpret_cast<float4*>(Bs + b_dst[j] + 4 * lane) = okb[j] ? vb[j] : zero;
   };
 
   struct Frag {
@@ -182,9 +221,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // a chunk followed by another: copy the next one first, then compute
-  auto chunk_more = [&](int c, const float* As, const float* Bs, float* Asn, float* Bsn) {
-    copy_chunk((c + 1) * BK, Asn, Bsn);
+  // a chunk followed by another (at n_next): copy that one first, then compute
+  auto chunk_more = [&](int n_next, const float* As, const float* Bs, float* Asn, float* Bsn) {
+    copy_chunk(n_next, Asn, Bsn);
     steps(As, Bs);
     __syncthreads();
     read_frag(f[H & 1], Asn, Bsn, 0);
@@ -197,30 +236,46 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     mma(f[(H - 1) & 1]);
   };
 
-  // N is a multiple of 2 * BK: chunks come in pairs, stage 0 then stage 1.
-  const int nchunks = N / BK;
-  copy_chunk(0, As0, Bs0);
-  __syncthreads();
-  read_frag(f[0], As0, Bs0, 0);
-  for (int c = 0; c + 2 < nchunks; c += 2) {
-    chunk_more(c, As0, Bs0, As1, Bs1);
-    chunk_more(c + 1, As1, Bs1, As0, Bs0);
+  // nchunks >= 2 chunks, aligned to the end of the reduction; chunk 0 may
+  // reach below n = 0. The loop takes chunks in pairs (stage 0, then stage
+  // 1) and ends with the pair (nchunks - 2, nchunks - 1); with an odd count,
+  // chunk 0 goes to stage 1 and is computed ahead of the pairs.
+  const int nchunks = (N + BK - 1) / BK;
+  const int n_first = N - BK * nchunks;  // in (-BK, 0]
+  int c = 0;
+  if (nchunks & 1) {
+    load_first_chunk(n_first, As1, Bs1);
+    __syncthreads();
+    read_frag(f[0], As1, Bs1, 0);
+    chunk_more(n_first + BK, As1, Bs1, As0, Bs0);
+    c = 1;
+  } else {
+    load_first_chunk(n_first, As0, Bs0);
+    __syncthreads();
+    read_frag(f[0], As0, Bs0, 0);
   }
-  chunk_more(nchunks - 2, As0, Bs0, As1, Bs1);
+  for (; c + 2 < nchunks; c += 2) {
+    chunk_more(n_first + BK * (c + 1), As0, Bs0, As1, Bs1);
+    chunk_more(n_first + BK * (c + 2), As1, Bs1, As0, Bs0);
+  }
+  chunk_more(N - BK, As0, Bs0, As1, Bs1);
   chunk_last(As1, Bs1);
 
-  // Epilogue (whole tiles: no guards). Offsets are 32-bit from the tile's
-  // corner, a wave-uniform base, which keeps the address arithmetic small.
+  // Epilogue. Offsets are 32-bit from the tile's corner, a wave-uniform base,
+  // which keeps the address arithmetic small. K % 4 == 0 and the column pair
+  // starts at an even column, so a pair is wholly inside or outside.
   float* const Ct = C + (int64_t)m0 * K + k0;
-  const uint32_t col = wn * T::kWaveN + T::kCB * li;
+  const int col = wn * T::kWaveN + T::kCB * li;
+  const bool col_ok = k0 + col < K;
 #pragma unroll
   for (int i = 0; i < T::kRB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const uint32_t row = wm * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-      *reinterpret_cast<float2*>(Ct + row * (uint32_t)K + col) = make_float2(acc[i][0][r], acc[i][1][r]);
+      const int row = wm * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+      if (col_ok && m0 + row < M)
+        *reinterpret_cast<float2*>(Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col) =
+            make_float2(acc[i][0][r], acc[i][1][r]);
     }
-  (void)M;
 }
 
 }  // namespace fgr

@@ -73,9 +73,10 @@ bool mfma_vec_ok(const float* A, const float* B, const float* C, int N, int K) {
 
 bool gemv_vec_ok(const float* B, int K) { return K % 4 == 0 && aligned(B, 16); }
 
-// Whole 256 x 256 tiles and an even number of 32-deep chunks: no padding.
-bool mfma_dma_ok(const float* A, const float* B, const float* C, int M, int N, int K) {
-  return mfma_vec_ok(A, B, C, N, K) && M % 256 == 0 && K % 256 == 0 && N % 64 == 0;
+// Direct global->LDS copies need 16-byte aligned rows, and at least two
+// 32-deep reduction chunks.
+bool mfma_dma_ok(const float* A, const float* B, const float* C, int N, int K) {
+  return mfma_vec_ok(A, B, C, N, K) && N >= 64;
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -89,7 +90,7 @@ int select_tile(int M, int K, int cus) {
 
 int select_path(const float* A, const float* B, const float* C, int M, int N, int K, int cus) {
   if (M == 1) return gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR;
-  if (mfma_dma_ok(A, B, C, M, N, K) && select_tile(M, K, cus) == FGR_TILE_256) return FGR_PATH_MFMA_DMA;
+  if (mfma_dma_ok(A, B, C, N, K) && select_tile(M, K, cus) == FGR_TILE_256) return FGR_PATH_MFMA_DMA;
   return mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
 }
 
@@ -114,8 +115,8 @@ using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
 using TileDma = fgr::DmaConfig<256, 256, 32, 2, 4>;
 
 int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
-  int tiles_m = M / TileDma::BM;
-  int tiles_n = K / TileDma::BN;
+  int tiles_m = (int)cdiv(M, TileDma::BM);
+  int tiles_n = (int)cdiv(K, TileDma::BN);
   int group = kTileGroup;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDma>),
@@ -153,7 +154,7 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       if (!mfma_vec_ok(A, B, C, N, K)) return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_DMA:
-      if (!mfma_dma_ok(A, B, C, M, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256))
+      if (!mfma_dma_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256))
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SCALAR: break;

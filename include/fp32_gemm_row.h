@@ -39,11 +39,11 @@
  *   Any 4-byte-aligned pointers are accepted. When N % 4 == 0, K % 4 == 0
  *   and A, B, C are 16-byte aligned the 128-bit load path is used; otherwise
  *   a path with 32-bit loads (the role of the scalar fallback of the LeetGPU
- *   write-up, section "V2: Vectorized float4 Transfers"). Problems made of
- *   whole 256 x 256 tiles (M % 256 == 0, K % 256 == 0, N % 64 == 0, and
- *   enough tiles to fill the device) copy A and B straight from global memory
- *   into LDS (the role of the cp.async pipeline of the write-up's section
- *   "V4"). M == 1 takes the bandwidth-bound matrix-vector path.
+ *   write-up, section "V2: Vectorized float4 Transfers"). With 128-bit rows,
+ *   N >= 64 and enough 256 x 256 output tiles to fill the device, A and B are
+ *   copied straight from global memory into LDS (the role of the cp.async
+ *   pipeline of the write-up's section "V4"). M == 1 takes the
+ *   bandwidth-bound matrix-vector path.
  *
  * Errors
  *   Every entry point returns 0 (FGR_OK) on success or a negative FGR_ERR_*
@@ -80,9 +80,8 @@ extern "C" {
 #define FGR_PATH_MFMA_SCALAR 2 /* FP32 MFMA, 32-bit loads; any shape and 4-B alignment */
 #define FGR_PATH_GEMV_VEC 3    /* matrix-vector (M == 1), 128-bit loads of B; needs K%4 == 0 and 16-B aligned B, C */
 #define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector (M == 1), 32-bit loads */
-#define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, whole 256x256 tiles fed by direct global->LDS copies;
-                                  needs the MFMA_VEC conditions and M % 256 == 0, K % 256 == 0,
-                                  N % 64 == 0 (tile 256 only) */
+#define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, 256x256 tiles fed by direct global->LDS copies;
+                                  needs the MFMA_VEC conditions and N >= 64 (tile 256 only) */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0
@@ -116,7 +115,7 @@ int fgr_solve_default(const float *A, const float *B, float *C, int M, int N, in
  * FGR_PATH_* value, tile an FGR_TILE_* value (ignored by the GEMV paths).
  * Returns FGR_ERR_BAD_PATH if that path or tile cannot handle these arguments
  * (e.g. a VEC path with N % 4 != 0, a GEMV path with M != 1, the DMA path
- * with a tile other than 256 or a partial tile, an unknown value).
+ * with a tile other than 256 or N < 64, an unknown value).
  */
 int fgr_solve_path(const float *A, const float *B, float *C, int M, int N, int K, void *stream,
                    int path, int tile);

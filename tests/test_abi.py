@@ -105,10 +105,10 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_SCALAR) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 1, 8, 6, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
-    # the direct-copy path needs whole 256x256 tiles, N % 64 == 0 and tile 256
-    assert call(lib, A0, B0, C0, 512, 96, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 500, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 128, 500, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    # the direct-copy path needs 128-bit rows, N >= 64 and tile 256
+    assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 130, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     # unknown path or tile values
@@ -120,8 +120,9 @@ def test_path_selection_rules():
     sp = fgr.select_path
     assert sp(A0, B0, C0, 8192, 6144, 4096) == fgr.PATH_MFMA_DMA
     assert sp(A0, B0, C0, 4096, 4096, 4096) == fgr.PATH_MFMA_DMA
-    assert sp(A0, B0, C0, 4096, 4064, 4096) == fgr.PATH_MFMA_VEC  # N % 64 != 0
-    assert sp(A0, B0, C0, 4000, 4096, 4096) == fgr.PATH_MFMA_VEC  # partial row tile
+    assert sp(A0, B0, C0, 4096, 4060, 4096) == fgr.PATH_MFMA_DMA  # ragged reduction
+    assert sp(A0, B0, C0, 4000, 4096, 4004) == fgr.PATH_MFMA_DMA  # partial tiles
+    assert sp(A0, B0, C0, 4096, 60, 4096) == fgr.PATH_MFMA_VEC  # N < 64
     assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_VEC  # too few 256x256 tiles
     assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_SCALAR
     assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_MFMA_SCALAR

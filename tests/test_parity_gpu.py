@@ -88,7 +88,7 @@ def paths_for(M, N, K):
         out.append((fgr.PATH_MFMA_SCALAR, tile))
         if N % 4 == 0 and K % 4 == 0:
             out.append((fgr.PATH_MFMA_VEC, tile))
-    if M % 256 == 0 and K % 256 == 0 and N % 64 == 0:
+    if N % 4 == 0 and K % 4 == 0 and N >= 64:
         out.append((fgr.PATH_MFMA_DMA, fgr.TILE_256))
     if M == 1:
         out.append((fgr.PATH_GEMV_SCALAR, 0))
@@ -119,8 +119,10 @@ EXACT_SHAPES = [
     (70, 70, 1), (70, 70, 3), (70, 70, 4), (70, 70, 5),
     (1, 8, 4), (1, 1000, 999), (1, 4097, 1028), (1, 17, 33),
     (513, 600, 515), (300, 2050, 260),
-    # whole 256x256 tiles: the direct global->LDS copy path
-    (256, 64, 256), (256, 128, 512), (512, 192, 256), (768, 320, 512),
+    # direct global->LDS copy path: whole tiles, odd and even chunk counts,
+    # ragged reduction (first chunk partly below n = 0), partial tiles
+    (256, 64, 256), (256, 128, 512), (512, 96, 256), (768, 320, 512),
+    (300, 68, 260), (257, 100, 516), (520, 132, 300), (255, 1028, 257),
 ]
 
 
