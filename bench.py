@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X: 256 CU x 256 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 METRIC = "FP32 GEMM TFLOP/s at M=8192,N=6144,K=4096; % of MI355X FP32 MFMA peak"
-KERNEL_SOURCES = ["gemm_mfma.hpp", "gemm_mfma_dma.hpp", "gemv.hpp", "solve.hip"]
+KERNEL_SOURCES = ["gemm_mfma.hpp", "gemm_mfma_dma.hpp", "gemm_mfma_split.hpp", "gemv.hpp", "solve.hip"]
 COPY_BYTES = 512 << 20
 
 
@@ -249,9 +249,10 @@ def main() -> int:
     dC = torch.empty(w.M * w.K, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    path = args.path or fgr.select_path(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), w.M, w.N, w.K)
-    tile = args.tile or (fgr.select_tile(w.M, w.K)
-                         if path in (fgr.PATH_MFMA_VEC, fgr.PATH_MFMA_SCALAR, fgr.PATH_MFMA_DMA) else 0)
+    auto_path = fgr.select_path(dA, dB, dC, w.M, w.N, w.K)
+    auto_tile = fgr.select_tile(dA, dB, dC, w.M, w.N, w.K)
+    path = args.path or auto_path
+    tile = args.tile or (auto_tile if path == auto_path else 0)
     stream = torch.cuda.current_stream()
 
     def step(i):

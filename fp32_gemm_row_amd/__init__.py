@@ -36,7 +36,9 @@ PATH_MFMA_SCALAR = 2
 PATH_GEMV_VEC = 3
 PATH_GEMV_SCALAR = 4
 PATH_MFMA_DMA = 5
+PATH_MFMA_SPLIT = 6
 PATH_NAMES = {
+    PATH_MFMA_SPLIT: "mfma_split",
     PATH_MFMA_DMA: "mfma_dma",
     PATH_MFMA_VEC: "mfma_vec",
     PATH_MFMA_SCALAR: "mfma_scalar",
@@ -48,6 +50,7 @@ TILE_AUTO = 0
 TILE_256 = 256
 TILE_128 = 128
 TILE_64 = 64
+TILE_32 = 32
 
 # Every symbol the header declares.
 EXPORTS = (
@@ -90,7 +93,7 @@ def load_library(path: str = LIB_PATH):
     lib.fgr_solve_path.restype = ci
     lib.fgr_select_path.argtypes = [vp, vp, vp, ci, ci, ci]
     lib.fgr_select_path.restype = ci
-    lib.fgr_select_tile.argtypes = [ci, ci, ci]
+    lib.fgr_select_tile.argtypes = [vp, vp, vp, ci, ci, ci]
     lib.fgr_select_tile.restype = ci
     lib.fgr_status_string.argtypes = [ci]
     lib.fgr_status_string.restype = ctypes.c_char_p
@@ -166,17 +169,18 @@ def solve_path(A, B, C, M: int, N: int, K: int, path: int, tile: int = TILE_AUTO
     _check(lib.fgr_solve_path(a, b, c, M, N, K, _stream_handle(stream), int(path), int(tile)))
 
 
+def _raw(x) -> int:
+    return x if isinstance(x, int) else x.data_ptr()
+
+
 def select_path(A, B, C, M: int, N: int, K: int) -> int:
-    """The FGR path solve() would take (host-only decision; negative = error code)."""
-    lib = load_library()
-    a = A if isinstance(A, int) else A.data_ptr()
-    b = B if isinstance(B, int) else B.data_ptr()
-    c = C if isinstance(C, int) else C.data_ptr()
-    return int(lib.fgr_select_path(a, b, c, int(M), int(N), int(K)))
+    """The FGR path solve() would take on a 256-CU device (host-only; negative = error code)."""
+    return int(load_library().fgr_select_path(_raw(A), _raw(B), _raw(C), int(M), int(N), int(K)))
 
 
-def select_tile(M: int, K: int, num_cus: int = 0) -> int:
-    return int(load_library().fgr_select_tile(int(M), int(K), int(num_cus)))
+def select_tile(A, B, C, M: int, N: int, K: int) -> int:
+    """The output tile solve() would use with that path (host-only; negative = error code)."""
+    return int(load_library().fgr_select_tile(_raw(A), _raw(B), _raw(C), int(M), int(N), int(K)))
 
 
 def version() -> int:

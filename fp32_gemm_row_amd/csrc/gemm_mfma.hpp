@@ -233,24 +233,80 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
   }
 
   // Registers staging the next chunk: slots 0 .. kAPerThread-1 are A's, the
-  // rest B's.
+  // rest B's. On the 128-bit path a slot is one float4 (a quad of a row). On
+  // the 32-bit path a slot holds four single elements, placed so that
+  // consecutive threads take consecutive columns: element (s, e) of a thread
+  // is row r0 + (4 s + e) * row_step, column c of the chunk, c = tid % width.
+  // Each 32-bit load instruction then reads whole row segments.
   constexpr int kSlots = T::kAPerThread + T::kBPerThread;
+  constexpr int kARowStep = T::kThreads / BK;  // element rows between a thread's A elements
+  constexpr int kBRowStep = T::kThreads / BN;
+  static_assert(T::kThreads % BK == 0 && T::kThreads % BN == 0, "element slots keep one column");
+  const int ea_r0 = tid / BK, ea_c = tid % BK;
+  const int eb_r0 = tid / BN, eb_c = tid % BN;
+  const float* const ea_base = A + (int64_t)(m0 + ea_r0 < M ? m0 + ea_r0 : 0) * N + ea_c;
+  const float* const eb_base = B + (int64_t)eb_r0 * K + k0 + eb_c;
+  unsigned ea_rows = 0;  // bit 4 s + e: that A element's row is inside M
+#pragma unroll
+  for (int i = 0; i < 4 * T::kAPerThread; ++i) ea_rows |= (m0 + ea_r0 + i * kARowStep < M) ? 1u << i : 0u;
+
   float4 stage[kSlots];
   unsigned stage_ok[kSlots];
   auto load_slot = [&](int s, int n0) {
-    if (s < T::kAPerThread)
-      stage[s] = load_quad<VEC>(a_ptr[s] + n0, A, a_row_ok[s], n0 + a_col[s], N, stage_ok[s]);
-    else {
-      const int i = s - T::kAPerThread;
-      stage[s] = load_quad<VEC>(b_ptr[i] + (int64_t)n0 * K, B, n0 + b_row[i] < N, b_col, K, stage_ok[s]);
+    if constexpr (VEC) {
+      if (s < T::kAPerThread)
+        stage[s] = load_quad<VEC>(a_ptr[s] + n0, A, a_row_ok[s], n0 + a_col[s], N, stage_ok[s]);
+      else {
+        const int i = s - T::kAPerThread;
+        stage[s] = load_quad<VEC>(b_ptr[i] + (int64_t)n0 * K, B, n0 + b_row[i] < N, b_col, K, stage_ok[s]);
+      }
+    } else {
+      float x[4];
+      unsigned ok = 0;
+      if (s < T::kAPerThread) {
+        const bool col_in = n0 + ea_c < N;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * s + e;
+          const bool in = col_in && (ea_rows >> i & 1u);
+          ok |= in ? 1u << e : 0u;
+          x[e] = *(in ? ea_base + (int64_t)i * kARowStep * N + n0 : A);
+        }
+      } else {
+        const int sb = s - T::kAPerThread;
+        const bool col_in = k0 + eb_c < K;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * sb + e;
+          const bool in = col_in && n0 + eb_r0 + i * kBRowStep < N;
+          ok |= in ? 1u << e : 0u;
+          x[e] = *(in ? eb_base + ((int64_t)n0 + i * kBRowStep) * K : B);
+        }
+      }
+      stage[s] = make_float4(x[0], x[1], x[2], x[3]);
+      stage_ok[s] = ok;
     }
   };
   auto store_slot = [&](int s, int buf) {
     const float4 v = mask_quad(stage[s], stage_ok[s]);
-    if (s < T::kAPerThread)
-      *reinterpret_cast<float4*>(As0 + buf * BM * T::kLdA + a_lds[s]) = v;
-    else
-      *reinterpret_cast<float4*>(Bs0 + buf * BK * T::kLdB + b_lds[s - T::kAPerThread]) = v;
+    if constexpr (VEC) {
+      if (s < T::kAPerThread)
+        *reinterpret_cast<float4*>(As0 + buf * BM * T::kLdA + a_lds[s]) = v;
+      else
+        *reinterpret_cast<float4*>(Bs0 + buf * BK * T::kLdB + b_lds[s - T::kAPerThread]) = v;
+    } else {
+      const float x[4] = {v.x, v.y, v.z, v.w};
+      if (s < T::kAPerThread) {
+        float* As = As0 + buf * BM * T::kLdA + ea_r0 * T::kLdA + ea_c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[(4 * s + e) * kARowStep * T::kLdA] = x[e];
+      } else {
+        const int sb = s - T::kAPerThread;
+        float* Bs = Bs0 + buf * BK * T::kLdB + eb_r0 * T::kLdB + eb_c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[(4 * sb + e) * kBRowStep * T::kLdB] = x[e];
+      }
+    }
   };
 
   // MFMA operands of one half-step (8 reduction indices): per 32-row block a
@@ -293,6 +349,7 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
   constexpr int kMfmas = T::kRB * T::kCB * 4;  // per wave and half-step
   constexpr int kReads = T::kRB + 2 * T::kCB;  // b128 A reads, paired 32-bit B reads
   constexpr int kLoadInsts = VEC ? 1 : 4;      // global loads per slot
+  constexpr int kStoreInsts = VEC ? 1 : 4;     // LDS writes per slot
 
   // Software pipeline. Chunk c is consumed from LDS buffer c % 2 in H = BK/8
   // half-steps; the operands of half-step h + 1 are read from LDS while the
@@ -337,7 +394,7 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
       }
       read_frag(f[(h + 1) & 1], buf, h + 1);
       mma(f[h & 1]);
-      sched_interleave<kMfmas, n_slots * kLoadInsts, writes ? kSlots : 0, kReads>();
+      sched_interleave<kMfmas, n_slots * kLoadInsts, writes ? kSlots * kStoreInsts : 0, kReads>();
       __builtin_amdgcn_sched_barrier(0);
     });
     if (kLoadSteps == 0) {

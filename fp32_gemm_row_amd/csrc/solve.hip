@@ -12,6 +12,7 @@
 #include "fp32_gemm_row.h"
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_dma.hpp"
+#include "gemm_mfma_split.hpp"
 #include "gemv.hpp"
 
 namespace {
@@ -81,17 +82,47 @@ bool mfma_dma_ok(const float* A, const float* B, const float* C, int N, int K) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int select_tile(int M, int K, int cus) {
+struct Choice {
+  int path;
+  int tile;
+};
+
+// Kernel choice by the number of output tiles the shape makes at each tile
+// size, relative to the CU count (measured on MI355X; see the design notes):
+// whole-device 256x256 tiles take the direct-copy kernel; shapes with few
+// tiles split each tile's reduction across a workgroup's waves.
+Choice choose(const float* A, const float* B, const float* C, int M, int N, int K, int cus) {
   if (cus <= 0) cus = kDefaultCus;
-  if (cdiv(M, 256) * cdiv(K, 256) >= cus) return FGR_TILE_256;
-  if (cdiv(M, 128) * cdiv(K, 128) >= cus) return FGR_TILE_128;
-  return FGR_TILE_64;
+  if (M == 1) return {gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR, FGR_TILE_AUTO};
+  const int64_t t256 = cdiv(M, 256) * cdiv(K, 256);
+  const int64_t t128 = cdiv(M, 128) * cdiv(K, 128);
+  const int64_t t64 = cdiv(M, 64) * cdiv(K, 64);
+  if (mfma_vec_ok(A, B, C, N, K)) {
+    if (t256 >= cus) return {mfma_dma_ok(A, B, C, N, K) ? FGR_PATH_MFMA_DMA : FGR_PATH_MFMA_VEC, FGR_TILE_256};
+    if (t64 < cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
+    if (t64 < 2 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_64};
+    if (t64 < 4 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
+    if (N >= 1024) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_64};
+    return {FGR_PATH_MFMA_VEC, FGR_TILE_64};
+  }
+  if (t128 >= 4 * cus) return {FGR_PATH_MFMA_SCALAR, FGR_TILE_128};
+  if (t64 >= 2 * cus) return {FGR_PATH_MFMA_SCALAR, FGR_TILE_64};
+  return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
 }
 
-int select_path(const float* A, const float* B, const float* C, int M, int N, int K, int cus) {
-  if (M == 1) return gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR;
-  if (mfma_dma_ok(A, B, C, N, K) && select_tile(M, K, cus) == FGR_TILE_256) return FGR_PATH_MFMA_DMA;
-  return mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
+// Tile for a forced path when the caller left it open.
+int default_tile(int path, const Choice& auto_choice, int M, int K, int cus) {
+  if (path == auto_choice.path) return auto_choice.tile;
+  switch (path) {
+    case FGR_PATH_MFMA_DMA: return FGR_TILE_256;
+    case FGR_PATH_MFMA_SPLIT: return cdiv(M, 64) * cdiv(K, 64) < cus ? FGR_TILE_32 : FGR_TILE_64;
+    case FGR_PATH_MFMA_VEC:
+    case FGR_PATH_MFMA_SCALAR:
+      if (cdiv(M, 256) * cdiv(K, 256) >= cus) return FGR_TILE_256;
+      if (cdiv(M, 128) * cdiv(K, 128) >= cus) return FGR_TILE_128;
+      return FGR_TILE_64;
+    default: return FGR_TILE_AUTO;
+  }
 }
 
 int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStream_t stream) {
@@ -136,6 +167,30 @@ int launch_mfma_tile(int tile, const float* A, const float* B, float* C, int M, 
   }
 }
 
+template <class Cfg, bool VEC>
+int launch_split(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  int tiles_m = (int)cdiv(M, Cfg::BM);
+  int tiles_n = (int)cdiv(K, Cfg::BN);
+  int group = kTileGroup;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_split_kernel<Cfg, VEC>),
+                (int64_t)tiles_m * tiles_n, Cfg::kThreads, args, s);
+}
+
+using Split32 = fgr::SplitConfig<32, 32, 16, 4>;
+using Split64x4 = fgr::SplitConfig<64, 64, 16, 4>;
+using Split64x8 = fgr::SplitConfig<64, 64, 16, 8>;
+
+template <bool VEC>
+int launch_split_tile(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
+                      hipStream_t s) {
+  if (tile == FGR_TILE_32) return launch_split<Split32, VEC>(A, B, C, M, N, K, s);
+  // 64x64 tiles: eight waves per tile while the tiles alone would fill fewer
+  // than two waves of workgroups, four otherwise
+  if (cdiv(M, 64) * cdiv(K, 64) < 2 * cus) return launch_split<Split64x8, VEC>(A, B, C, M, N, K, s);
+  return launch_split<Split64x4, VEC>(A, B, C, M, N, K, s);
+}
+
 template <int VW>
 int launch_gemv(const float* A, const float* B, float* C, int N, int K, hipStream_t s) {
   constexpr int NT = 1024;  // 16 waves: 1024 rows of B in flight per workgroup
@@ -158,6 +213,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SCALAR: break;
+    case FGR_PATH_MFMA_SPLIT:
+      if (tile != FGR_TILE_AUTO && tile != FGR_TILE_32 && tile != FGR_TILE_64) return FGR_ERR_BAD_PATH;
+      break;
     case FGR_PATH_GEMV_VEC:
       if (M != 1 || !gemv_vec_ok(B, K)) return FGR_ERR_BAD_PATH;
       break;
@@ -166,24 +224,39 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     default: return FGR_ERR_BAD_PATH;
   }
-  if (tile != FGR_TILE_AUTO && tile != FGR_TILE_256 && tile != FGR_TILE_128 && tile != FGR_TILE_64)
+  if (tile != FGR_TILE_AUTO && tile != FGR_TILE_256 && tile != FGR_TILE_128 && tile != FGR_TILE_64 &&
+      tile != FGR_TILE_32)
     return FGR_ERR_BAD_PATH;
+  if (tile == FGR_TILE_32 && path != FGR_PATH_MFMA_SPLIT && path != FGR_PATH_AUTO) return FGR_ERR_BAD_PATH;
 
   int cus = 0;
   rc = current_device(&cus);
   if (rc != FGR_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Choice best = choose(A, B, C, M, N, K, cus);
   if (path == FGR_PATH_AUTO) {
-    path = select_path(A, B, C, M, N, K, cus);
-    // a forced smaller tile keeps the register-staged kernel
-    if (path == FGR_PATH_MFMA_DMA && tile != FGR_TILE_AUTO && tile != FGR_TILE_256) path = FGR_PATH_MFMA_VEC;
+    if (tile == FGR_TILE_AUTO) {
+      path = best.path;
+      tile = best.tile;
+    } else if (M == 1) {
+      path = best.path;
+    } else if (tile == FGR_TILE_32) {
+      path = FGR_PATH_MFMA_SPLIT;  // the only kernel with 32x32 tiles
+    } else if (tile == FGR_TILE_256 && best.path == FGR_PATH_MFMA_DMA) {
+      path = FGR_PATH_MFMA_DMA;
+    } else {
+      path = mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
+    }
   }
-  if (tile == FGR_TILE_AUTO) tile = select_tile(M, K, cus);
+  if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, K, cus);
 
   switch (path) {
     case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
+    case FGR_PATH_MFMA_SPLIT:
+      return mfma_vec_ok(A, B, C, N, K) ? launch_split_tile<true>(tile, A, B, C, M, N, K, cus, s)
+                                        : launch_split_tile<false>(tile, A, B, C, M, N, K, cus, s);
     case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, N, K, s);
     case FGR_PATH_GEMV_SCALAR: return launch_gemv<1>(A, B, C, N, K, s);
   }
@@ -210,12 +283,13 @@ int fgr_solve_path(const float* A, const float* B, float* C, int M, int N, int K
 int fgr_select_path(const float* A, const float* B, const float* C, int M, int N, int K) {
   const int rc = check_args(A, B, C, M, N, K);
   if (rc != FGR_OK) return rc;
-  return select_path(A, B, C, M, N, K, kDefaultCus);
+  return choose(A, B, C, M, N, K, kDefaultCus).path;
 }
 
-int fgr_select_tile(int M, int K, int num_cus) {
-  if (M < 1 || K < 1) return FGR_ERR_BAD_DIMS;
-  return select_tile(M, K, num_cus);
+int fgr_select_tile(const float* A, const float* B, const float* C, int M, int N, int K) {
+  const int rc = check_args(A, B, C, M, N, K);
+  if (rc != FGR_OK) return rc;
+  return choose(A, B, C, M, N, K, kDefaultCus).tile;
 }
 
 const char* fgr_status_string(int status) {

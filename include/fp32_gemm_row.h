@@ -42,8 +42,9 @@
  *   write-up, section "V2: Vectorized float4 Transfers"). With 128-bit rows,
  *   N >= 64 and enough 256 x 256 output tiles to fill the device, A and B are
  *   copied straight from global memory into LDS (the role of the cp.async
- *   pipeline of the write-up's section "V4"). M == 1 takes the
- *   bandwidth-bound matrix-vector path.
+ *   pipeline of the write-up's section "V4"). Shapes with too few output tiles
+ *   for the device split each tile's reduction over the waves of a workgroup.
+ *   M == 1 takes the bandwidth-bound matrix-vector path.
  *
  * Errors
  *   Every entry point returns 0 (FGR_OK) on success or a negative FGR_ERR_*
@@ -82,12 +83,16 @@ extern "C" {
 #define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector (M == 1), 32-bit loads */
 #define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, 256x256 tiles fed by direct global->LDS copies;
                                   needs the MFMA_VEC conditions and N >= 64 (tile 256 only) */
+#define FGR_PATH_MFMA_SPLIT 6  /* FP32 MFMA, small tiles (32 or 64) whose reduction is split over
+                                  the waves of a workgroup; any shape (128-bit loads when the
+                                  MFMA_VEC conditions hold, else 32-bit) */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0
 #define FGR_TILE_256 256
 #define FGR_TILE_128 128
 #define FGR_TILE_64 64
+#define FGR_TILE_32 32 /* split path only */
 
 /*
  * solve - C = A x B on `stream`.
@@ -128,11 +133,11 @@ int fgr_solve_path(const float *A, const float *B, float *C, int M, int N, int K
 int fgr_select_path(const float *A, const float *B, const float *C, int M, int N, int K);
 
 /*
- * fgr_select_tile - the FGR_TILE_* output tile solve() would use on the MFMA
- * paths for an M x K output on a device with `num_cus` compute units (<= 0:
- * the 256 of MI355X). Host only.
+ * fgr_select_tile - the FGR_TILE_* output tile solve() would use with the path
+ * fgr_select_path() reports, on a 256-CU device (FGR_TILE_AUTO for the
+ * matrix-vector paths), or a negative FGR_ERR_* code. Host only.
  */
-int fgr_select_tile(int M, int K, int num_cus);
+int fgr_select_tile(const float *A, const float *B, const float *C, int M, int N, int K);
 
 /* fgr_status_string - a static, human-readable name for a status code. */
 const char *fgr_status_string(int status);

@@ -91,9 +91,9 @@ def test_overlap_of_output_rejected(lib):
     # C ends inside B
     assert call(lib, A0, B0, B0 - 4 * (M * K - 1), M, N, K) == fgr.ERR_ALIAS
     # A and B may alias each other
-    assert fgr.select_path(A0, A0, C0, M, N, K) == fgr.PATH_MFMA_VEC
+    assert fgr.select_path(A0, A0, C0, M, N, K) == fgr.PATH_MFMA_SPLIT
     # adjacent, not overlapping
-    assert fgr.select_path(A0, B0, A0 + 4 * M * N, M, N, K) == fgr.PATH_MFMA_VEC
+    assert fgr.select_path(A0, B0, A0 + 4 * M * N, M, N, K) == fgr.PATH_MFMA_SPLIT
 
 
 def test_forced_path_rejections(lib):
@@ -111,6 +111,9 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    # 32x32 tiles exist on the split path only
+    assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_VEC, 32) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_SPLIT, 128) == fgr.ERR_BAD_PATH
     # unknown path or tile values
     assert call(lib, A0, B0, C0, 8, 8, 8, 99) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 8, 8, 8, fgr.PATH_MFMA_VEC, 100) == fgr.ERR_BAD_PATH
@@ -123,11 +126,10 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4096, 4060, 4096) == fgr.PATH_MFMA_DMA  # ragged reduction
     assert sp(A0, B0, C0, 4000, 4096, 4004) == fgr.PATH_MFMA_DMA  # partial tiles
     assert sp(A0, B0, C0, 4096, 60, 4096) == fgr.PATH_MFMA_VEC  # N < 64
-    assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_VEC  # too few 256x256 tiles
-    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_SCALAR
-    assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_MFMA_SCALAR
-    assert sp(A0 + 4, B0, C0, 8, 8, 8) == fgr.PATH_MFMA_SCALAR
-    assert sp(A0, B0, C0 + 8, 8, 8, 8) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_SPLIT  # too few 256x256 tiles
+    assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR  # misaligned A
+    assert sp(A0, B0, C0 + 8, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR
     assert sp(A0, B0, C0, 1, 8192, 8192) == fgr.PATH_GEMV_VEC
     assert sp(A0, B0, C0, 1, 3, 1) == fgr.PATH_GEMV_SCALAR
     assert sp(A0, B0 + 4, C0, 1, 8, 8) == fgr.PATH_GEMV_SCALAR
@@ -136,13 +138,25 @@ def test_path_selection_rules():
 
 def test_tile_selection():
     st = fgr.select_tile
-    assert st(8192, 4096, 256) == 256  # 512 tiles of 256x256
-    assert st(4096, 4096, 256) == 256  # 256 tiles
-    assert st(2048, 2048, 256) == 128  # 64 big tiles, 256 of 128x128
-    assert st(1023, 1027, 256) == 64
-    assert st(256, 256, 256) == 64
-    assert st(0, 4, 256) == fgr.ERR_BAD_DIMS
-    assert st(8192, 4096, 0) == 256  # default CU count
+    assert st(A0, B0, C0, 8192, 6144, 4096) == 256  # 512 tiles of 256x256
+    assert st(A0, B0, C0, 4096, 4096, 4096) == 256  # 256 tiles
+    assert st(A0, B0, C0, 1023, 1025, 1027) == 32  # split, 32x32
+    assert st(A0, B0, C0, 256, 256, 256) == 32
+    assert st(A0, B0, C0, 1024, 1024, 1024) == 64  # split, 64x64
+    assert st(A0, B0, C0, 2048, 512, 2048) == 64  # register-staged, 64x64
+    assert st(A0, B0, C0, 4095, 4097, 4099) == 128  # 32-bit loads, many tiles
+    assert st(A0, B0, C0, 1, 8192, 8192) == 0  # matrix-vector
+    assert st(0, B0, C0, 4, 4, 4) == fgr.ERR_NULL_POINTER
+
+
+def test_split_path_choices():
+    sp = fgr.select_path
+    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 256, 256, 256) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 1024, 8192, 1024) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 2048, 512, 2048) == fgr.PATH_MFMA_VEC
+    assert sp(A0, B0, C0, 2047, 2049, 2051) == fgr.PATH_MFMA_SCALAR
 
 
 def test_python_wrapper_rejects_cpu_tensors():

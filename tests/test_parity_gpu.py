@@ -90,6 +90,8 @@ def paths_for(M, N, K):
             out.append((fgr.PATH_MFMA_VEC, tile))
     if N % 4 == 0 and K % 4 == 0 and N >= 64:
         out.append((fgr.PATH_MFMA_DMA, fgr.TILE_256))
+    out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
+    out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
     if M == 1:
         out.append((fgr.PATH_GEMV_SCALAR, 0))
         if K % 4 == 0:
@@ -204,11 +206,12 @@ def test_large_workloads_sampled(name):
     w = synth.WORKLOADS[name]
     say(f"{name}: generating inputs")
     A, B = synth.workload_inputs(w)
-    say(f"{name}: GPU run (auto path, tile {fgr.select_tile(w.M, w.K)})")
+    tile = fgr.select_tile(1 << 40, 2 << 40, 3 << 40, w.M, w.N, w.K)
+    say(f"{name}: GPU run (auto path, tile {tile})")
     C = gpu_gemm(A, B)
     assert np.isfinite(C).all(), f"{name}: non-finite outputs"
     rng = np.random.default_rng(w.seed)
-    rows, cols = sample_positions(w.M, w.K, fgr.select_tile(w.M, w.K), rng)
+    rows, cols = sample_positions(w.M, w.K, tile, rng)
     say(f"{name}: oracle at {rows.size} positions")
     Cref, S = oracle.gemm_at(A, B, rows, cols)
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{name} sampled")
