@@ -156,6 +156,80 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_
     return out_path
 
 
+def kernel_ms(fn, steps, warmup, stream):
+    """Mean of per-launch HIP-event durations on `stream`."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+
+
+def ablation(w, dA, dBs, dC, copies, steps, warmup, stream):
+    """Every (path, tile) the library accepts for this workload, timed alike."""
+    import fp32_gemm_row_amd as fgr
+
+    variants = [(fgr.PATH_MFMA_DMA, 256)]
+    for tile in (256, 128, 64):
+        variants += [(fgr.PATH_MFMA_VEC, tile), (fgr.PATH_MFMA_SCALAR, tile)]
+    variants += [(fgr.PATH_MFMA_SPLIT, 64), (fgr.PATH_MFMA_SPLIT, 32),
+                 (fgr.PATH_GEMV_VEC, 0), (fgr.PATH_GEMV_SCALAR, 0)]
+    auto = (fgr.select_path(dA, dBs[0], dC, w.M, w.N, w.K), fgr.select_tile(dA, dBs[0], dC, w.M, w.N, w.K))
+    for path, tile in variants:
+        def fn(i, path=path, tile=tile):
+            fgr.solve_path(dA, dBs[i % copies], dC, w.M, w.N, w.K, path, tile, stream=stream)
+
+        try:
+            fn(0)
+        except fgr.GemmError:
+            continue  # this variant cannot run the shape
+        ms = kernel_ms(fn, steps, warmup, stream)
+        print(json.dumps({
+            "workload": w.name, "path": fgr.PATH_NAMES[path], "tile": tile,
+            "auto": (path, tile) == auto, "kernel_ms": round(ms, 5),
+            "tflops": round(w.flops / ms / 1e9, 3), "gbs": round(w.algorithmic_bytes / ms / 1e6, 1),
+        }), flush=True)
+    return 0
+
+
+def roundtrip(w, A, B, dA, dB, dC, dev, iters=10):
+    """Host round trip: pinned A, B -> device, solve, device C -> pinned host."""
+    import torch
+
+    import fp32_gemm_row_amd as fgr
+
+    hA = torch.from_numpy(A.ravel()).pin_memory()
+    hB = torch.from_numpy(B.ravel()).pin_memory()
+    hC = torch.empty(w.M * w.K, dtype=torch.float32).pin_memory()
+
+    def once():
+        dA.copy_(hA, non_blocking=True)
+        dB.copy_(hB, non_blocking=True)
+        fgr.solve(dA, dB, dC, w.M, w.N, w.K)
+        hC.copy_(dC, non_blocking=True)
+        torch.cuda.synchronize()
+
+    once()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        once()
+    ms = (time.perf_counter() - t0) / iters * 1e3
+    return {
+        "ms": round(ms, 4),
+        "tflops": round(w.flops / ms / 1e9, 3),
+        "pcie_bytes": w.algorithmic_bytes,
+        "iterations": iters,
+    }
+
+
 def cpu_baseline(w, A, B, target_s: float):
     """Time the oracle on the first R rows of A (R sized for about target_s)."""
     import oracle
@@ -207,6 +281,13 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run a plain 512 MiB device copy three times "
                          "(the known-size reference for HBM byte counters)")
+    ap.add_argument("--roundtrip", action="store_true",
+                    help="also time the host round trip of the tutorial's section 3 (pinned host A and B "
+                         "copied in, solve, C copied out; 1 warm-up, 10 timed on the host clock) and "
+                         "add it as 'roundtrip' (never the headline value)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time every path/tile the library accepts for the workload, print one JSON line "
+                         "per variant and exit (the controlled comparison of the LeetGPU write-up)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/<workload>_traffic.md from three rocprofv3 output folders and exit")
     ap.add_argument("--command", action="append", default=[],
@@ -257,6 +338,9 @@ def main() -> int:
 
     def step(i):
         fgr.solve_path(dA, dBs[i % copies], dC, w.M, w.N, w.K, path, tile, stream=stream)
+
+    if args.ablation:
+        return ablation(w, dA, dBs, dC, copies, args.steps, args.warmup, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -323,6 +407,8 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.roundtrip:
+        out["roundtrip"] = roundtrip(w, A, B, dA, dB, dC, dev)
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

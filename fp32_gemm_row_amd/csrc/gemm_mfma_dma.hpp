@@ -148,13 +148,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
       okb[j] = n >= 0 && n < N;
       vb[j] = *reinterpret_cast<const float4*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
     }
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
-      *reinterpret_cast<float4*>(As + a_dst[j] + 4 * lane) = oka[j] ? va[j] : zero;
+      *reinterpret_cast<float4*>(As + a_dst[j] + 4 * lane) = mask_quad(va[j], oka[j] ? 0xfu : 0u);
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j)
-      *reinterpret_cast<float4*>(Bs + b_dst[j] + 4 * lane) = okb[j] ? vb[j] : zero;
+      *reinterpret_cast<float4*>(Bs + b_dst[j] + 4 * lane) = mask_quad(vb[j], okb[j] ? 0xfu : 0u);
   };
 
   struct Frag {
