@@ -54,7 +54,7 @@ struct DmaConfig {
 
   static_assert(BN == 256, "one B copy instruction covers a 256-float row");
   static_assert(BK == 32, "the A swizzle is written for 8 quads per row");
-  static_assert(kCB == 2, "B operands are read as pairs (two column blocks per wave)");
+  static_assert(kCB == 2 || kCB == 4, "B operands are read as 2 or 4 adjacent floats");
   static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(BM % (kRowsPerCopy * kWaves) == 0 && BK % kWaves == 0, "copies split evenly over waves");
   static_assert(4 * 2 * (kAStage + kBStage) <= 160 * 1024, "LDS budget of a gfx950 workgroup");
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     b_dst[j] = r * T::BN;
   }
 
-  auto copy_chunk = [&](int n0, float* As, float* Bs) {
+  auto copy_chunk = [&](int n0, float* As, float* Bs) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
       copy16_to_lds(a_src[j] + n0, As + a_dst[j]);
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // The first chunk (n0 <= 0): the same placement through registers, with
   // every element whose n lies outside [0, N) replaced by zero. N % 4 == 0 and
   // n0 % 4 == 0, so a quad is wholly inside or wholly outside.
-  auto load_first_chunk = [&](int n0, float* As, float* Bs) {
+  auto load_first_chunk = [&](int n0, float* As, float* Bs) __attribute__((always_inline)) {
     float4 va[T::kACopies], vb[T::kBCopies];
     bool oka[T::kACopies], okb[T::kBCopies];
 #pragma unroll
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // 64-bit LDS read for two blocks). Every output keeps its own column of B,
   // so the product is unchanged; the epilogue writes with the same mapping.
   const int b_frag = 4 * lg * T::BN + wn * T::kWaveN + T::kCB * li;
-  auto read_frag = [&](Frag& f, const float* As, const float* Bs, int h) {
+  auto read_frag = [&](Frag& f, const float* As, const float* Bs, int h) __attribute__((always_inline)) {
     const int q = (2 * h + lg) ^ a_swz;
 #pragma unroll
     for (int i = 0; i < T::kRB; ++i)
@@ -178,9 +178,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     const float* Bh = Bs + b_frag + 8 * h * T::BN;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float2 v = *reinterpret_cast<const float2*>(Bh + t * T::BN);
-      f.b[0][t] = v.x;
-      f.b[1][t] = v.y;
+      if constexpr (T::kCB == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(Bh + t * T::BN);
+        f.b[0][t] = v.x;
+        f.b[1][t] = v.y;
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(Bh + t * T::BN);
+        f.b[0][t] = v.x;
+        f.b[1][t] = v.y;
+        f.b[2][t] = v.z;
+        f.b[3][t] = v.w;
+      }
     }
   };
 
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
 #pragma unroll
     for (int j = 0; j < T::kCB; ++j) acc[i][j] = f32x16{};
 
-  auto mma = [&](const Frag& f) {
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // __syncthreads), so after it the next chunk is complete in LDS; it also
   // releases (As, Bs) for the copy that the following chunk issues.
   Frag f[2];
-  auto steps = [&](const float* As, const float* Bs) {
+  auto steps = [&](const float* As, const float* Bs) __attribute__((always_inline)) {
     static_for<0, H - 1>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
       read_frag(f[(h + 1) & 1], As, Bs, h + 1);
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     });
   };
   // a chunk followed by another (at n_next): copy that one first, then compute
-  auto chunk_more = [&](int n_next, const float* As, const float* Bs, float* Asn, float* Bsn) {
+  auto chunk_more = [&](int n_next, const float* As, const float* Bs, float* Asn, float* Bsn) __attribute__((always_inline)) {
     copy_chunk(n_next, Asn, Bsn);
     steps(As, Bs);
     __syncthreads();
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     sched_interleave<kMfmas, 0, 0, kReads>();
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto chunk_last = [&](const float* As, const float* Bs) {
+  auto chunk_last = [&](const float* As, const float* Bs) __attribute__((always_inline)) {
     steps(As, Bs);
     mma(f[(H - 1) & 1]);
   };
@@ -261,8 +269,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   chunk_last(As1, Bs1);
 
   // Epilogue. Offsets are 32-bit from the tile's corner, a wave-uniform base,
-  // which keeps the address arithmetic small. K % 4 == 0 and the column pair
-  // starts at an even column, so a pair is wholly inside or outside.
+  // which keeps the address arithmetic small. K % 4 == 0 and a lane's kCB
+  // adjacent columns start at a multiple of kCB, so they are wholly inside or
+  // outside.
   float* const Ct = C + (int64_t)m0 * K + k0;
   const int col = wn * T::kWaveN + T::kCB * li;
   const bool col_ok = k0 + col < K;
@@ -271,9 +280,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wm * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-      if (col_ok && m0 + row < M)
-        *reinterpret_cast<float2*>(Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col) =
-            make_float2(acc[i][0][r], acc[i][1][r]);
+      if (col_ok && m0 + row < M) {
+        float* dst = Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col;
+        if constexpr (T::kCB == 2)
+          *reinterpret_cast<float2*>(dst) = make_float2(acc[i][0][r], acc[i][1][r]);
+        else
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
+      }
     }
 }
 

@@ -143,7 +143,7 @@ int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, h
 }
 
 using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
-using TileDma = fgr::DmaConfig<256, 256, 32, 2, 4>;
+using TileDma = fgr::DmaConfig<256, 256, 32, 2, 2>;  // 4 waves, 128x128 each (accumulators in AGPRs)
 
 int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
   int tiles_m = (int)cdiv(M, TileDma::BM);
