@@ -217,6 +217,21 @@ def test_large_workloads_sampled(name):
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{name} sampled")
 
 
+@pytest.mark.parametrize("shape", [(8000, 6000, 4000), (3072, 3072, 3072), (1024, 8192, 1024), (2047, 2049, 2051)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_large_ragged_sampled(shape):
+    # partial 256x256 tiles with a ragged reduction (direct-copy path), the
+    # split path at 64x64 with eight and four waves, and the 32-bit path
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "uniform", seed=11)
+    say(f"large ragged {shape}: path {fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]}")
+    C = gpu_gemm(A, B)
+    rng = np.random.default_rng(5)
+    rows, cols = sample_positions(M, K, 256, rng, extra=1024)
+    Cref, S = oracle.gemm_at(A, B, rows, cols)
+    assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{shape} sampled")
+
+
 def test_gemv_workload_full_compare():
     w = synth.WORKLOADS["gemv8192"]
     A, B = synth.workload_inputs(w)
@@ -229,12 +244,29 @@ def test_gemv_workload_full_compare():
 # ------------------------------------------------------------- properties
 
 
-def test_repeat_runs_are_bitwise_identical():
-    w = synth.WORKLOADS["ragged1023"]
-    A, B = synth.workload_inputs(w)
-    first = gpu_gemm(A, B)
+@pytest.mark.parametrize("shape,path,tile", [
+    ((1023, 1025, 1027), fgr.PATH_AUTO, 0),
+    ((512, 256, 768), fgr.PATH_MFMA_DMA, 256),
+    ((300, 500, 260), fgr.PATH_MFMA_SPLIT, 64),
+    ((1, 3000, 900), fgr.PATH_GEMV_VEC, 0),
+], ids=["ragged-auto", "dma", "split64", "gemv"])
+def test_repeat_runs_are_bitwise_identical(shape, path, tile):
+    # fixed reduction order and no atomics: identical bits on every run
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "uniform", seed=3)
+    first = gpu_gemm(A, B, path, tile)
     for _ in range(4):
-        assert np.array_equal(gpu_gemm(A, B), first, equal_nan=True)
+        assert np.array_equal(gpu_gemm(A, B, path, tile), first, equal_nan=True)
+
+
+def test_kernels_agree_bitwise_on_integer_data():
+    # every MFMA kernel walks the reduction in the same order (the split kernel
+    # only adds its per-wave partials at the end): on integer data all sums are
+    # exact, so every path must give the oracle's bits
+    A, B = synth.make_inputs(300, 256, 260, "integer", seed=9)
+    Cref, _ = oracle.gemm(A, B)
+    for path, tile in paths_for(300, 256, 260):
+        assert_exact(gpu_gemm(A, B, path, tile), Cref, f"integer path={path} tile={tile}")
 
 
 def test_identity_and_one_hot():
