@@ -74,8 +74,9 @@ bool mfma_vec_ok(const float* A, const float* B, const float* C, int N, int K) {
 
 bool gemv_vec_ok(const float* B, int K) { return K % 4 == 0 && aligned(B, 16); }
 
-// Direct global->LDS copies need 16-byte aligned rows, and at least two
-// 32-deep reduction chunks.
+// Direct global->LDS copies need 16-byte aligned rows, and at least four
+// 16-deep reduction chunks (the copies that run past the last chunk re-read
+// it, and must never reach the zero-padded first chunk).
 bool mfma_dma_ok(const float* A, const float* B, const float* C, int N, int K) {
   return mfma_vec_ok(A, B, C, N, K) && N >= 64;
 }
@@ -143,7 +144,7 @@ int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, h
 }
 
 using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
-using TileDma = fgr::DmaConfig<256, 256, 32, 2, 2>;  // 4 waves, 128x128 each (accumulators in AGPRs)
+using TileDma = fgr::DmaConfig<4>;  // 256x256, 4 waves of 128x128 (accumulators in AGPRs), 4 LDS stages
 
 int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
   int tiles_m = (int)cdiv(M, TileDma::BM);

@@ -121,10 +121,12 @@ EXACT_SHAPES = [
     (70, 70, 1), (70, 70, 3), (70, 70, 4), (70, 70, 5),
     (1, 8, 4), (1, 1000, 999), (1, 4097, 1028), (1, 17, 33),
     (513, 600, 515), (300, 2050, 260),
-    # direct global->LDS copy path: whole tiles, odd and even chunk counts,
-    # ragged reduction (first chunk partly below n = 0), partial tiles
+    # direct global->LDS copy path: whole tiles, every count of 16-deep
+    # chunks mod 3, 4 and 5 (4 to 9 chunks), ragged reduction (first chunk
+    # partly below n = 0), partial tiles
     (256, 64, 256), (256, 128, 512), (512, 96, 256), (768, 320, 512),
     (300, 68, 260), (257, 100, 516), (520, 132, 300), (255, 1028, 257),
+    (264, 84, 260), (256, 116, 264), (300, 1004, 300), (260, 144, 516),
 ]
 
 
