@@ -177,7 +177,7 @@ def ablation(w, dA, dBs, dC, copies, steps, warmup, stream):
     """Every (path, tile) the library accepts for this workload, timed alike."""
     import fp32_gemm_row_amd as fgr
 
-    variants = [(fgr.PATH_MFMA_DMA, 256)]
+    variants = [(fgr.PATH_MFMA_DMA, 256), (fgr.PATH_MFMA_DMA_TAIL, 256)]
     for tile in (256, 128, 64):
         variants += [(fgr.PATH_MFMA_VEC, tile), (fgr.PATH_MFMA_SCALAR, tile)]
     variants += [(fgr.PATH_MFMA_SPLIT, 64), (fgr.PATH_MFMA_SPLIT, 32),

@@ -37,7 +37,9 @@ PATH_GEMV_VEC = 3
 PATH_GEMV_SCALAR = 4
 PATH_MFMA_DMA = 5
 PATH_MFMA_SPLIT = 6
+PATH_MFMA_DMA_TAIL = 7
 PATH_NAMES = {
+    PATH_MFMA_DMA_TAIL: "mfma_dma_tail",
     PATH_MFMA_SPLIT: "mfma_split",
     PATH_MFMA_DMA: "mfma_dma",
     PATH_MFMA_VEC: "mfma_vec",

@@ -18,6 +18,12 @@
 // reduction belongs to one thread or tile) kept at workgroup level, with the
 // reduction of each tile shared by the workgroup's waves.
 //
+// Tail mode (sub > 0): the workgroups cover big square tiles of sub*BM, the
+// logical big tiles [first, first + gridDim.x / sub^2) of a tiles_m x tiles_n
+// grid walked in the grouped order, each cut into sub x sub tiles of BM x BN.
+// This spreads the few 256 x 256 tiles of a last, partial wave of the
+// direct-copy kernel over every CU.
+//
 // Within a wave: the same MFMA operand layout, zero padding and LDS pitch as
 // gemm_mfma.hpp (v_mfma_f32_32x32x2_f32, reduction index 8h + 4g + t of a
 // chunk for half-wave g at step (h, t)); output columns are interleaved across
@@ -78,8 +84,9 @@ __device__ __forceinline__ float vec_get(float4 v, int i) {
 template <class T, bool VEC>
 __global__ __launch_bounds__(T::kThreads) void gemm_mfma_split_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
-    int K, int tiles_m, int tiles_n, int group) {
+    int K, int tiles_m, int tiles_n, int group, int first, int sub) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, S = T::S;
+  static_assert(BM == BN, "tail mode cuts square big tiles");
   constexpr int H = BK / 8;
   __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
 
@@ -89,10 +96,20 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_split_kernel(
   const int li = lane & 31;
   const int lg = lane >> 5;
 
-  int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group, tm, tn);
-  const int m0 = tm * BM;
-  const int k0 = tn * BN;
+  int tm, tn, m0, k0;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  if (sub == 0) {
+    grouped_tile(logical, tiles_m, tiles_n, group, tm, tn);
+    m0 = tm * BM;
+    k0 = tn * BN;
+  } else {
+    const int per = sub * sub;
+    grouped_tile(first + logical / per, tiles_m, tiles_n, group, tm, tn);
+    const int w = logical % per;
+    m0 = (tm * sub + w / sub) * BM;
+    k0 = (tn * sub + w % sub) * BN;
+    if (m0 >= M || k0 >= K) return;  // a piece of a partial big tile: no outputs
+  }
 
   // this wave's share of the reduction: chunks [c_begin, c_end)
   const int nchunks = (N + BK - 1) / BK;

@@ -83,6 +83,12 @@ bool mfma_dma_ok(const float* A, const float* B, const float* C, int N, int K) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Largest last partial wave of 256x256 tiles that is cheaper to spread over
+// every CU as small split-reduction tiles than to run as a wave of its own
+// (measured on MI355X, 4096 x 4096 x K: the split tail wins up to 160 tiles
+// left over, 130.6 vs 121.7 TFLOP/s, and loses at 192, 129.0 vs 131.5).
+int64_t tail_tiles(int cus) { return (int64_t)cus * 11 / 16; }
+
 struct Choice {
   int path;
   int tile;
@@ -99,7 +105,13 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
   const int64_t t128 = cdiv(M, 128) * cdiv(K, 128);
   const int64_t t64 = cdiv(M, 64) * cdiv(K, 64);
   if (mfma_vec_ok(A, B, C, N, K)) {
-    if (t256 >= cus) return {mfma_dma_ok(A, B, C, N, K) ? FGR_PATH_MFMA_DMA : FGR_PATH_MFMA_VEC, FGR_TILE_256};
+    if (t256 >= cus) {
+      if (!mfma_dma_ok(A, B, C, N, K)) return {FGR_PATH_MFMA_VEC, FGR_TILE_256};
+      // a last, partial wave of at most tail_tiles(cus) tiles goes to the split kernel
+      const int64_t rem = t256 % cus;
+      if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
+      return {FGR_PATH_MFMA_DMA, FGR_TILE_256};
+    }
     if (t64 < cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
     if (t64 < 2 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_64};
     if (t64 < 4 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
@@ -115,7 +127,8 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
 int default_tile(int path, const Choice& auto_choice, int M, int K, int cus) {
   if (path == auto_choice.path) return auto_choice.tile;
   switch (path) {
-    case FGR_PATH_MFMA_DMA: return FGR_TILE_256;
+    case FGR_PATH_MFMA_DMA:
+    case FGR_PATH_MFMA_DMA_TAIL: return FGR_TILE_256;
     case FGR_PATH_MFMA_SPLIT: return cdiv(M, 64) * cdiv(K, 64) < cus ? FGR_TILE_32 : FGR_TILE_64;
     case FGR_PATH_MFMA_VEC:
     case FGR_PATH_MFMA_SCALAR:
@@ -146,13 +159,16 @@ int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, h
 using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
 using TileDma = fgr::DmaConfig<4>;  // 256x256, 4 waves of 128x128 (accumulators in AGPRs), 4 LDS stages
 
-int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+// The direct-copy kernel over the first `count` tiles of the grouped order
+// (count < 0: all of them).
+int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
+                    hipStream_t s) {
   int tiles_m = (int)cdiv(M, TileDma::BM);
   int tiles_n = (int)cdiv(K, TileDma::BN);
   int group = kTileGroup;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDma>),
-                (int64_t)tiles_m * tiles_n, TileDma::kThreads, args, s);
+                count < 0 ? (int64_t)tiles_m * tiles_n : count, TileDma::kThreads, args, s);
 }
 using Tile128 = fgr::MfmaConfig<128, 128, 16, 2, 2>;
 using Tile64 = fgr::MfmaConfig<64, 64, 16, 2, 2>;
@@ -173,14 +189,47 @@ int launch_split(const float* A, const float* B, float* C, int M, int N, int K, 
   int tiles_m = (int)cdiv(M, Cfg::BM);
   int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
-  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  int first = 0, sub = 0;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &first, &sub};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_split_kernel<Cfg, VEC>),
                 (int64_t)tiles_m * tiles_n, Cfg::kThreads, args, s);
+}
+
+// The split kernel over 256x256 tiles [first, first + count) of the direct-copy
+// kernel's grid (same grouped order), each cut into (256 / BM)^2 tiles.
+template <class Cfg>
+int launch_split_big(const float* A, const float* B, float* C, int M, int N, int K, int first, int count,
+                     hipStream_t s) {
+  int tiles_m = (int)cdiv(M, TileDma::BM);
+  int tiles_n = (int)cdiv(K, TileDma::BN);
+  int group = kTileGroup;
+  int sub = TileDma::BM / Cfg::BM;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &first, &sub};
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_split_kernel<Cfg, true>),
+                (int64_t)count * sub * sub, Cfg::kThreads, args, s);
 }
 
 using Split32 = fgr::SplitConfig<32, 32, 16, 4>;
 using Split64x4 = fgr::SplitConfig<64, 64, 16, 4>;
 using Split64x8 = fgr::SplitConfig<64, 64, 16, 8>;
+
+// Whole waves of 256x256 tiles (one tile per CU) on the direct-copy kernel;
+// the tiles of the last, partial wave on the split kernel, cut into 64x64
+// tiles (32x32 while 64x64 would leave CUs idle), so that the tail occupies
+// every CU instead of a few.
+int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
+  const int64_t tiles = cdiv(M, TileDma::BM) * cdiv(K, TileDma::BN);
+  const int64_t full = tiles / cus * cus;
+  const int64_t rem = tiles - full;
+  if (full > 0) {
+    const int rc = launch_mfma_dma(A, B, C, M, N, K, full, s);
+    if (rc != FGR_OK || rem == 0) return rc;
+  }
+  if (full > INT_MAX || rem > INT_MAX / 64) return FGR_ERR_BAD_DIMS;
+  if (rem * 16 >= 2 * cus) return launch_split_big<Split64x4>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  if (rem * 16 >= cus) return launch_split_big<Split64x8>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  return launch_split_big<Split32>(A, B, C, M, N, K, (int)full, (int)rem, s);
+}
 
 template <bool VEC>
 int launch_split_tile(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
@@ -210,6 +259,7 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       if (!mfma_vec_ok(A, B, C, N, K)) return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_DMA:
+    case FGR_PATH_MFMA_DMA_TAIL:
       if (!mfma_dma_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256))
         return FGR_ERR_BAD_PATH;
       break;
@@ -243,8 +293,8 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       path = best.path;
     } else if (tile == FGR_TILE_32) {
       path = FGR_PATH_MFMA_SPLIT;  // the only kernel with 32x32 tiles
-    } else if (tile == FGR_TILE_256 && best.path == FGR_PATH_MFMA_DMA) {
-      path = FGR_PATH_MFMA_DMA;
+    } else if (tile == FGR_TILE_256 && (best.path == FGR_PATH_MFMA_DMA || best.path == FGR_PATH_MFMA_DMA_TAIL)) {
+      path = best.path;
     } else {
       path = mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
     }
@@ -252,7 +302,8 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, K, cus);
 
   switch (path) {
-    case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, s);
+    case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, -1, s);
+    case FGR_PATH_MFMA_DMA_TAIL: return launch_dma_tail(A, B, C, M, N, K, cus, s);
     case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SPLIT:

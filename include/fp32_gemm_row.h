@@ -86,6 +86,10 @@ extern "C" {
 #define FGR_PATH_MFMA_SPLIT 6  /* FP32 MFMA, small tiles (32 or 64) whose reduction is split over
                                   the waves of a workgroup; any shape (128-bit loads when the
                                   MFMA_VEC conditions hold, else 32-bit) */
+#define FGR_PATH_MFMA_DMA_TAIL 7 /* MFMA_DMA on the whole waves of 256x256 tiles (one per CU), the
+                                    split kernel on the tiles of the last, partial wave, cut into
+                                    64x64 or 32x32 tiles; same conditions as MFMA_DMA. Two
+                                    launches on `stream`. */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0

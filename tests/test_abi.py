@@ -111,6 +111,10 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
+    # the tail-split form of it has the same conditions
+    assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA_TAIL, 64) == fgr.ERR_BAD_PATH
     # 32x32 tiles exist on the split path only
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_VEC, 32) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_SPLIT, 128) == fgr.ERR_BAD_PATH
@@ -126,6 +130,14 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4096, 4060, 4096) == fgr.PATH_MFMA_DMA  # ragged reduction
     assert sp(A0, B0, C0, 4000, 4096, 4004) == fgr.PATH_MFMA_DMA  # partial tiles
     assert sp(A0, B0, C0, 4096, 60, 4096) == fgr.PATH_MFMA_VEC  # N < 64
+    # a last partial wave of at most 176 tiles of 256x256 goes to the split kernel
+    assert sp(A0, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 272 tiles
+    assert sp(A0, B0, C0, 65792, 64, 256) == fgr.PATH_MFMA_DMA_TAIL  # 257 tiles
+    assert sp(A0, B0, C0, 4096, 4096, 6144) == fgr.PATH_MFMA_DMA_TAIL  # 384 tiles
+    assert sp(A0, B0, C0, 4096, 4096, 6656) == fgr.PATH_MFMA_DMA_TAIL  # 416 tiles: 160 left over
+    assert sp(A0, B0, C0, 4096, 4096, 7168) == fgr.PATH_MFMA_DMA  # 448 tiles: 192 left over
+    assert sp(A0, B0, C0, 8192, 6208, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 544 tiles
+    assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_SCALAR
     assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_SPLIT  # too few 256x256 tiles
     assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_MFMA_SPLIT
     assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR  # misaligned A
@@ -140,6 +152,7 @@ def test_tile_selection():
     st = fgr.select_tile
     assert st(A0, B0, C0, 8192, 6144, 4096) == 256  # 512 tiles of 256x256
     assert st(A0, B0, C0, 4096, 4096, 4096) == 256  # 256 tiles
+    assert st(A0, B0, C0, 4096, 4096, 4160) == 256  # whole waves of 256x256, then the tail
     assert st(A0, B0, C0, 1023, 1025, 1027) == 32  # split, 32x32
     assert st(A0, B0, C0, 256, 256, 256) == 32
     assert st(A0, B0, C0, 1024, 1024, 1024) == 64  # split, 64x64

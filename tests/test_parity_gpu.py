@@ -90,6 +90,9 @@ def paths_for(M, N, K):
             out.append((fgr.PATH_MFMA_VEC, tile))
     if N % 4 == 0 and K % 4 == 0 and N >= 64:
         out.append((fgr.PATH_MFMA_DMA, fgr.TILE_256))
+        # below one wave of 256x256 tiles every tile is in the tail: the split
+        # kernel's big-tile mode alone, partial big tiles included
+        out.append((fgr.PATH_MFMA_DMA_TAIL, fgr.TILE_256))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
     if M == 1:
@@ -219,7 +222,8 @@ def test_large_workloads_sampled(name):
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{name} sampled")
 
 
-@pytest.mark.parametrize("shape", [(8000, 6000, 4000), (3072, 3072, 3072), (1024, 8192, 1024), (2047, 2049, 2051)],
+@pytest.mark.parametrize("shape", [(8000, 6000, 4000), (3072, 3072, 3072), (1024, 8192, 1024), (2047, 2049, 2051),
+                                   (4096, 1028, 4160), (8192, 2052, 4100), (4300, 1000, 4096)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_large_ragged_sampled(shape):
     # partial 256x256 tiles with a ragged reduction (direct-copy path), the
@@ -229,9 +233,25 @@ def test_large_ragged_sampled(shape):
     say(f"large ragged {shape}: path {fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]}")
     C = gpu_gemm(A, B)
     rng = np.random.default_rng(5)
-    rows, cols = sample_positions(M, K, 256, rng, extra=1024)
+    rows, cols = sample_positions(M, K, 64, rng, extra=1024)
     Cref, S = oracle.gemm_at(A, B, rows, cols)
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{shape} sampled")
+
+
+@pytest.mark.parametrize("shape", [(4352, 64, 4096), (4100, 68, 4100), (2304, 100, 8192), (65792, 64, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_partial_last_wave_exact(shape):
+    # one or more whole waves of 256x256 tiles on the direct-copy kernel, the
+    # last partial wave cut into small tiles for the split kernel: on integer
+    # data every output is exact, whichever kernel computed it
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=4)
+    say(f"partial last wave {shape}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_MFMA_DMA_TAIL
+    say(f"partial last wave {shape}: GPU")
+    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto (tail split)")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256), Cref, f"{shape} direct-copy only")
 
 
 def test_gemv_workload_full_compare():
