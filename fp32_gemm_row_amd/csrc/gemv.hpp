@@ -1,21 +1,25 @@
-// Matrix-vector shaped product (M == 1): C[0,k] = sum_n A[0,n] * B[n,k].
+// Matrix-vector and skinny products (M <= 8): C[m,k] = sum_n A[m,n] * B[n,k].
 //
 // The pages give no kernel for this shape; it is legal (1 <= M in the LeetGPU
-// "Constraints") and the LeetGPU "Example 2" is one. With a single output row
-// there is nothing to reuse from B: each element of B is used once, so the
-// kernel is bound by streaming B (N*K floats) from HBM, at 0.5 FLOP per byte.
+// "Constraints") and the LeetGPU "Example 2" is one. With one (or a few)
+// output rows there is (almost) nothing to reuse from B: each element of B is
+// used M times, so the kernel is bound by streaming B (N*K floats) from HBM,
+// at 0.5 * M FLOP per byte.
 //
 // Design: workgroup w owns the 32 output columns [32w, 32w+32) - one 128-byte
-// segment of every row of B - and the whole reduction for them. Its threads
-// split the rows of B: LPR lanes cover the 32 columns of one row (8 lanes x
-// float4 on the 128-bit path, 32 lanes x float on the 32-bit path) and the
-// RPI = NT / LPR row groups walk rows r, r + RPI, r + 2 RPI, ...; the loop is
-// unrolled so that each lane keeps UNROLL independent loads in flight (with
-// NT = 1024 and UNROLL = 8 a workgroup has 1024 rows = 128 KiB of B in
-// flight). A is staged through LDS in chunks of up to 8192 elements. The row
-// groups' partial sums are first added across the lanes of each wave (lanes
-// that share columns differ by multiples of LPR), then across waves in LDS.
-// No atomics and no workspace: the result is deterministic.
+// segment of every row of B - and the whole reduction for them, for all MR
+// (>= M) rows of A. Its threads split the rows of B: LPR lanes cover the 32
+// columns of one row (8 lanes x float4 on the 128-bit path, 32 lanes x float
+// on the 32-bit path) and the RPI = NT / LPR row groups walk rows r, r + RPI,
+// r + 2 RPI, ...; each lane loads UNROLL rows before it uses them (UNROLL
+// loads in flight per lane). A is staged through LDS, row-major,
+// AF elements at a time (AF / MR reduction indices of every row); rows of A
+// past M are staged as zeros and their outputs are not
+// stored. The row groups' partial sums are first added across the lanes of
+// each wave (lanes that share columns differ by multiples of LPR), then across
+// waves in LDS, in wave order. No atomics and no workspace: the result is
+// deterministic, and for M == 1 the reduction order is that of MR == 1 for
+// every MR.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,21 +27,48 @@
 
 namespace fgr {
 
-constexpr int kGemvCols = 32;       // output columns per workgroup
-constexpr int kGemvAChunk = 8192;   // elements of A staged in LDS at a time
+constexpr int kGemvCols = 32;        // output columns per workgroup
+constexpr int kGemvMaxRows = 8;      // largest M the kernel takes
+constexpr int kGemvAFloats = 16384;  // elements of A staged in LDS at a time (all rows)
 
-template <int VW, int NT, int UNROLL>
+template <int VW>
+__device__ __forceinline__ void load_row(const float* p, float (&v)[VW]) {
+  if constexpr (VW == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
+  } else {
+    v[0] = *p;
+  }
+}
+
+// acc[m][e] += A[m][r] * v[e] for the MR staged rows of A
+template <int VW, int MR, int CHUNK>
+__device__ __forceinline__ void fma_row(float (&acc)[MR][VW], const float* a_s, int r, const float (&v)[VW]) {
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const float a = a_s[m * CHUNK + r];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[m][e] += a * v[e];
+  }
+}
+
+template <int VW, int NT, int UNROLL, int MR, int AF = kGemvAFloats>
 __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
                                                   const float* __restrict__ B,
-                                                  float* __restrict__ C, int N, int K) {
-  constexpr int LPR = kGemvCols / VW;  // lanes per row segment
-  constexpr int RPI = NT / LPR;        // rows in flight per workgroup step
+                                                  float* __restrict__ C, int M, int N, int K) {
+  constexpr int LPR = kGemvCols / VW;     // lanes per row segment
+  constexpr int RPI = NT / LPR;           // rows in flight per workgroup step
   constexpr int WAVES = NT / 64;
+  constexpr int CHUNK = AF / MR;          // reduction indices per staged chunk of A
   static_assert(VW == 1 || VW == 4, "vector width");
   static_assert(NT % 64 == 0 && 64 % LPR == 0, "waves must hold whole row segments");
+  static_assert(MR >= 1 && MR <= kGemvMaxRows && AF % MR == 0 && (AF / MR) % RPI == 0, "rows per workgroup");
 
-  __shared__ float a_s[kGemvAChunk];
-  __shared__ float part[WAVES][kGemvCols];
+  __shared__ float a_s[MR * CHUNK];  // [m][n - nb]
+  __shared__ float part[WAVES][MR][kGemvCols];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -47,29 +78,38 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
   const int col = blockIdx.x * kGemvCols + cl * VW;
   const bool col_ok = col < K;  // VW == 4: K % 4 == 0, so all four columns are in
 
-  float acc[VW];
+  float acc[MR][VW];
 #pragma unroll
-  for (int e = 0; e < VW; ++e) acc[e] = 0.f;
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[m][e] = 0.f;
 
-  for (int nb = 0; nb < N; nb += kGemvAChunk) {
-    const int len = (N - nb) < kGemvAChunk ? (N - nb) : kGemvAChunk;
+  for (int nb = 0; nb < N; nb += CHUNK) {
+    const int len = (N - nb) < CHUNK ? (N - nb) : CHUNK;
     __syncthreads();  // the previous chunk of A has been read by every thread
-    for (int i = tid; i < len; i += NT) a_s[i] = A[nb + i];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const bool row_ok = m < M;
+      const float* ar = A + (int64_t)(row_ok ? m : 0) * N + nb;
+      for (int i = tid; i < len; i += NT) a_s[m * CHUNK + i] = row_ok ? ar[i] : 0.f;
+    }
     __syncthreads();
     if (col_ok) {
       const float* bp = B + (int64_t)nb * K + col;
-#pragma unroll UNROLL
-      for (int r = rl; r < len; r += RPI) {
-        const float a = a_s[r];
-        if constexpr (VW == 4) {
-          const float4 v = *reinterpret_cast<const float4*>(bp + (int64_t)r * K);
-          acc[0] += a * v.x;
-          acc[1] += a * v.y;
-          acc[2] += a * v.z;
-          acc[3] += a * v.w;
-        } else {
-          acc[0] += a * bp[(int64_t)r * K];
-        }
+      // UNROLL rows of B are loaded before any is used, so that each lane
+      // keeps UNROLL loads in flight whatever MR is
+      int r = rl;
+      for (; r + (UNROLL - 1) * RPI < len; r += UNROLL * RPI) {
+        float v[UNROLL][VW];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) load_row<VW>(bp + (int64_t)(r + u * RPI) * K, v[u]);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) fma_row<VW, MR, CHUNK>(acc, a_s, r + u * RPI, v[u]);
+      }
+      for (; r < len; r += RPI) {
+        float v[VW];
+        load_row<VW>(bp + (int64_t)r * K, v);
+        fma_row<VW, MR, CHUNK>(acc, a_s, r, v);
       }
     }
   }
@@ -78,18 +118,24 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < VW; ++e) acc[e] += __shfl_xor(acc[e], off);
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int e = 0; e < VW; ++e) acc[m][e] += __shfl_xor(acc[m][e], off);
   if (lane < LPR) {
 #pragma unroll
-    for (int e = 0; e < VW; ++e) part[wave][cl * VW + e] = acc[e];
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int e = 0; e < VW; ++e) part[wave][m][cl * VW + e] = acc[m][e];
   }
   __syncthreads();
-  if (tid < kGemvCols) {
-    const int c = blockIdx.x * kGemvCols + tid;
+  for (int t = tid; t < MR * kGemvCols; t += NT) {
+    const int m = t / kGemvCols;
+    const int cc = t % kGemvCols;
+    const int c = blockIdx.x * kGemvCols + cc;
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s += part[w][tid];
-    if (c < K) C[c] = s;
+    for (int w = 0; w < WAVES; ++w) s += part[w][m][cc];
+    if (m < M && c < K) C[(int64_t)m * K + c] = s;
   }
 }
 

@@ -43,8 +43,10 @@
  *   N >= 64 and enough 256 x 256 output tiles to fill the device, A and B are
  *   copied straight from global memory into LDS (the role of the cp.async
  *   pipeline of the write-up's section "V4"). Shapes with too few output tiles
- *   for the device split each tile's reduction over the waves of a workgroup.
- *   M == 1 takes the bandwidth-bound matrix-vector path.
+ *   for the device split each tile's reduction over the waves of a workgroup;
+ *   when a last, partial wave of 256 x 256 tiles is left, its tiles are cut
+ *   into small split-reduction tiles. M <= 8 takes the bandwidth-bound
+ *   matrix-vector path, which streams B once for all rows of A.
  *
  * Errors
  *   Every entry point returns 0 (FGR_OK) on success or a negative FGR_ERR_*
@@ -79,8 +81,9 @@ extern "C" {
 #define FGR_PATH_AUTO 0
 #define FGR_PATH_MFMA_VEC 1    /* FP32 MFMA, 128-bit loads; needs N%4 == K%4 == 0 and 16-B aligned pointers */
 #define FGR_PATH_MFMA_SCALAR 2 /* FP32 MFMA, 32-bit loads; any shape and 4-B alignment */
-#define FGR_PATH_GEMV_VEC 3    /* matrix-vector (M == 1), 128-bit loads of B; needs K%4 == 0 and 16-B aligned B, C */
-#define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector (M == 1), 32-bit loads */
+#define FGR_PATH_GEMV_VEC 3    /* matrix-vector and skinny (M <= 8), 128-bit loads of B; needs K%4 == 0
+                                  and 16-B aligned B, C */
+#define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector and skinny (M <= 8), 32-bit loads */
 #define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, 256x256 tiles fed by direct global->LDS copies;
                                   needs the MFMA_VEC conditions and N >= 64 (tile 256 only) */
 #define FGR_PATH_MFMA_SPLIT 6  /* FP32 MFMA, small tiles (32 or 64) whose reduction is split over
@@ -123,7 +126,7 @@ int fgr_solve_default(const float *A, const float *B, float *C, int M, int N, in
  * "Controlled Comparison", build each variant separately). path is an
  * FGR_PATH_* value, tile an FGR_TILE_* value (ignored by the GEMV paths).
  * Returns FGR_ERR_BAD_PATH if that path or tile cannot handle these arguments
- * (e.g. a VEC path with N % 4 != 0, a GEMV path with M != 1, the DMA path
+ * (e.g. a VEC path with N % 4 != 0, a GEMV path with M > 8, the DMA path
  * with a tile other than 256 or N < 64, an unknown value).
  */
 int fgr_solve_path(const float *A, const float *B, float *C, int M, int N, int K, void *stream,

@@ -85,7 +85,7 @@ def test_misaligned_pointers_rejected(lib):
 
 
 def test_overlap_of_output_rejected(lib):
-    M = N = K = 16
+    M, N, K = 16, 16, 16
     # C starts inside A
     assert call(lib, A0, B0, A0 + 4 * (M * N - 1), M, N, K) == fgr.ERR_ALIAS
     # C ends inside B
@@ -101,9 +101,9 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 8, 6, 8, fgr.PATH_MFMA_VEC) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 8, 8, 6, fgr.PATH_MFMA_VEC) == fgr.ERR_BAD_PATH
     assert call(lib, A0 + 4, B0, C0, 8, 8, 8, fgr.PATH_MFMA_VEC) == fgr.ERR_BAD_PATH
-    # matrix-vector paths need M == 1
-    assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 2, 8, 8, fgr.PATH_GEMV_SCALAR) == fgr.ERR_BAD_PATH
+    # matrix-vector paths need M <= 8
+    assert call(lib, A0, B0, C0, 9, 8, 8, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 9, 8, 8, fgr.PATH_GEMV_SCALAR) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 1, 8, 6, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
     # the direct-copy path needs 128-bit rows, N >= 64 and tile 256
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
@@ -139,12 +139,17 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 8192, 6208, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 544 tiles
     assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_SCALAR
     assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_SPLIT  # too few 256x256 tiles
-    assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_GEMV_SCALAR  # skinny, K % 4 != 0
+    assert sp(A0, B0, C0, 40, 8, 6) == fgr.PATH_MFMA_SPLIT
     assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR  # misaligned A
     assert sp(A0, B0, C0 + 8, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR
     assert sp(A0, B0, C0, 1, 8192, 8192) == fgr.PATH_GEMV_VEC
     assert sp(A0, B0, C0, 1, 3, 1) == fgr.PATH_GEMV_SCALAR
     assert sp(A0, B0 + 4, C0, 1, 8, 8) == fgr.PATH_GEMV_SCALAR
+    assert sp(A0, B0, C0, 2, 8192, 8192) == fgr.PATH_GEMV_VEC  # skinny: B streamed once
+    assert sp(A0, B0, C0, 8, 8192, 8192) == fgr.PATH_GEMV_VEC
+    assert sp(A0, B0, C0, 8, 8192, 8190) == fgr.PATH_GEMV_SCALAR
+    assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_SPLIT
     assert sp(0, B0, C0, 1, 8, 8) == fgr.ERR_NULL_POINTER
 
 

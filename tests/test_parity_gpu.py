@@ -95,7 +95,7 @@ def paths_for(M, N, K):
         out.append((fgr.PATH_MFMA_DMA_TAIL, fgr.TILE_256))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
-    if M == 1:
+    if M <= 8:
         out.append((fgr.PATH_GEMV_SCALAR, 0))
         if K % 4 == 0:
             out.append((fgr.PATH_GEMV_VEC, 0))
@@ -124,6 +124,9 @@ EXACT_SHAPES = [
     (70, 70, 1), (70, 70, 3), (70, 70, 4), (70, 70, 5),
     (1, 8, 4), (1, 1000, 999), (1, 4097, 1028), (1, 17, 33),
     (513, 600, 515), (300, 2050, 260),
+    # skinny products (M <= 8, B streamed once): several staged chunks of A
+    # (2048 reduction indices per chunk at M = 8, 8192 at M = 2), ragged K
+    (8, 4100, 96), (5, 4500, 100), (3, 4500, 36), (2, 9000, 40), (8, 2050, 33), (7, 3000, 1),
     # direct global->LDS copy path: whole tiles, every count of 16-deep
     # chunks mod 3, 4 and 5 (4 to 9 chunks), ragged reduction (first chunk
     # partly below n = 0), partial tiles
@@ -252,6 +255,19 @@ def test_partial_last_wave_exact(shape):
     say(f"partial last wave {shape}: GPU")
     assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto (tail split)")
     assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256), Cref, f"{shape} direct-copy only")
+
+
+@pytest.mark.parametrize("M", [2, 3, 5, 8])
+def test_skinny_products_full_compare(M):
+    # M rows of A against a 8192 x 8192 B: one pass over B for all rows
+    N = K = 8192
+    A, B = synth.make_inputs(M, N, K, "uniform", seed=20 + M)
+    say(f"skinny M={M}: oracle")
+    Cref, S = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_GEMV_VEC
+    say(f"skinny M={M}: GPU")
+    assert_within_tolerance(gpu_gemm(A, B), Cref, S, f"skinny M={M} auto")
+    assert_within_tolerance(gpu_gemm(A, B, fgr.PATH_GEMV_SCALAR), Cref, S, f"skinny M={M} scalar")
 
 
 def test_gemv_workload_full_compare():
