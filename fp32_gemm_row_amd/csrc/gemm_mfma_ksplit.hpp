@@ -1,0 +1,351 @@
+// FP32 MFMA GEMM for mid-size shapes: 128x128 output tiles whose reduction is
+// split over the four waves of a workgroup, each wave fed by its own direct
+// global->LDS copies.
+//
+// Between the few-tile shapes of gemm_mfma_split.hpp and the whole-device
+// shapes of gemm_mfma_dma.hpp (at least one 256x256 tile per CU) lie shapes
+// such as 2048^3 or a (1024, 6144, 4096) row shard: 64 tiles of 256x256, 256
+// of 128x128. Here each wave of a workgroup computes the WHOLE 128x128 tile
+// (16 MFMA blocks, 256 accumulators in AGPRs, as a wave of the direct-copy
+// kernel) over its own quarter of the reduction chunks, so a 128x128 tile
+// keeps a CU's four matrix cores as busy as a 256x256 tile does. Each wave
+// copies its own A (128 x BK) and B (BK x 128) chunks with
+// global_load_lds_dwordx4 into its own ring of S LDS stages and waits only on
+// its own copies (s_waitcnt vmcnt): the main loop has no barrier. At the end
+// the four partial tiles are added in wave order (0, 1, 2, 3) through LDS, each
+// wave summing and storing a quarter of the tile: deterministic, no
+// workspace, no atomics.
+//
+// This keeps the output-parallel decomposition of the LeetGPU write-up
+// (section "V0", "Approach": outputs independent, each owned with its whole
+// reduction by one block) at workgroup level; only the waves inside the
+// workgroup share a tile's reduction.
+//
+// Chunks are BK = 8 deep (one MFMA step: reduction index 4g + t of a chunk for
+// half-wave g at MFMA t), aligned to the END of the reduction as in the
+// direct-copy kernel, so that only chunk 0 can reach below n = 0; each wave
+// loads its first chunk through registers with zero fill (only wave 0's first
+// chunk is chunk 0). With N >= 64 every wave owns at least two chunks, so a
+// copy clamped to a wave's last chunk never reads chunk 0.
+//
+// LDS: stage s of every wave is a separate LDS object per operand (so that the
+// compiler can tell a stage's reads from the copies into another), each holding
+// the four waves' 4 KiB pieces. A rows are 8 floats (two quads) stored in the
+// order q ^ swz(r), swz(r) = bit 2 ^ bit 3 of r: the 128-bit operand reads of 8
+// consecutive rows from a multiple of 8 (32 banks), and of 16 from a multiple
+// of 16 (64 banks), hit distinct 16-byte bank groups. B is row-major, 128
+// floats per row, two rows per copy instruction.
+#pragma once
+
+#include "gemm_mfma.hpp"
+#include "gemm_mfma_dma.hpp"
+
+namespace fgr {
+
+template <int S_>
+struct KsplitConfig {
+  static constexpr int BM = 128, BN = 128, BK = 8, S = S_;
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRB = BM / 32, kCB = BN / 32;
+  static constexpr int kACopies = BM * BK / 256;  // per wave per chunk (256 floats per copy)
+  static constexpr int kBCopies = BK * BN / 256;
+  static constexpr int kCopies = kACopies + kBCopies;
+  static constexpr int kPiece = BM * BK;          // floats of one wave's A (or B) stage
+  static constexpr int kStage = kWaves * kPiece;  // floats of one LDS stage object
+
+  static_assert(BM * BK == BK * BN, "A and B pieces have one size");
+  static_assert(kRB == 4 && kCB == 4, "a wave owns the whole tile in 16 MFMA blocks");
+  static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");
+  static_assert(2 * S * kStage * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+  static_assert(kRB * kCB * 16 * 64 <= 4 * kStage, "a partial tile fits in four stage objects");
+};
+
+__device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// copy16_to_lds with the LDS destination passed as an opaque wave-uniform
+// integer. The compiler then cannot attribute the copy to one LDS object and
+// does not pair it with the operand reads (which keep their objects): no wait
+// of its own before those reads. The kernel counts the copies in flight and
+// waits for them itself (s_waitcnt vmcnt), the only way its reads are ordered
+// after the copies they need.
+__device__ __forceinline__ void copy16_to_lds_counted(const float* g, float* lds) {
+  uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)lds);
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 16, 0, 0);
+}
+
+template <class T>
+__global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
+    const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
+    int K, int tiles_m, int tiles_n, int group) {
+  constexpr int S = T::S, BK = T::BK, BN = T::BN;
+  using I0 = std::integral_constant<int, 0>;
+  __shared__ __attribute__((aligned(1024))) float As0[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float As1[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float As2[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float As3[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float Bs0[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float Bs1[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float Bs2[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float Bs3[T::kStage];
+  auto a_stage = [&](auto sc) __attribute__((always_inline)) -> float* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return As0;
+    else if constexpr (s == 1) return As1;
+    else if constexpr (s == 2) return As2;
+    else return As3;
+  };
+  auto b_stage = [&](auto sc) __attribute__((always_inline)) -> float* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return Bs0;
+    else if constexpr (s == 1) return Bs1;
+    else if constexpr (s == 2) return Bs2;
+    else return Bs3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int lg = lane >> 5;
+  const int piece = wave * T::kPiece;  // this wave's offset inside every stage object
+
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group, tm, tn);
+  const int m0 = tm * T::BM;
+  const int k0 = tn * BN;
+
+  // this wave's chunks [c_begin, c_end); N >= 64 gives every wave >= 2
+  const int nchunks = (N + BK - 1) / BK;
+  const int n_first = N - BK * nchunks;  // in (-BK, 0]
+  const int c_begin = nchunks * wave / T::kWaves;
+  const int c_end = nchunks * (wave + 1) / T::kWaves;
+  const int c_last = c_end - 1;
+
+  // A copy j: rows [32j, 32j + 32); lane L -> row 32j + L/2 at stored position
+  // L % 2, which holds quad (L % 2) ^ swz(row). Rows past M read row M - 1.
+  const float* a_src[T::kACopies];
+  int a_dst[T::kACopies], a_quad[T::kACopies];
+#pragma unroll
+  for (int j = 0; j < T::kACopies; ++j) {
+    const int r = 32 * j + lane / 2;
+    const int q = (lane % 2) ^ a_swizzle2(r);
+    const int row = m0 + r < M ? m0 + r : M - 1;
+    a_src[j] = A + (int64_t)row * N + 4 * q;
+    a_dst[j] = piece + 256 * j;
+    a_quad[j] = q;
+  }
+  // B copy j: chunk rows 2j, 2j + 1; lane L -> row 2j + L/32, columns
+  // 4 (L % 32) .. + 3 (past K: the last quad instead, not stored).
+  const float* b_src[T::kBCopies];
+  int b_dst[T::kBCopies];
+  const int b_cq = 4 * (lane % 32);
+  const int b_col = k0 + b_cq < K ? k0 + b_cq : K - 4;
+#pragma unroll
+  for (int j = 0; j < T::kBCopies; ++j) {
+    const int r = 2 * j + lane / 32;
+    b_src[j] = B + (int64_t)r * K + b_col;
+    b_dst[j] = piece + 256 * j;
+  }
+
+  auto copy_chunk = [&](int c, float* As, float* Bs) __attribute__((always_inline)) {
+    const int n0 = n_first + BK * c;
+#pragma unroll
+    for (int j = 0; j < T::kACopies; ++j) copy16_to_lds_counted(a_src[j] + n0, As + a_dst[j]);
+#pragma unroll
+    for (int j = 0; j < T::kBCopies; ++j) copy16_to_lds_counted(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+  };
+
+  struct Frag {
+    float4 a[T::kRB];
+    float b[T::kCB][4];
+  };
+  // Operand read offsets, each one integer from the stage's start: a longer
+  // chain of address steps hides the stage object from the compiler, which
+  // then waits for every copy in flight before the read. A: quad lg of row li
+  // (+ 32 i), stored at position lg ^ swz(li) (the same swizzle for every i).
+  const int a_frag = piece + li * BK + 4 * (lg ^ a_swizzle2(li));
+  // lane column li of MFMA column block j is output column 4 li + j (see the
+  // direct-copy kernel): one 128-bit read gives a lane's B operands of all blocks
+  const int b_frag = piece + 4 * lg * BN + 4 * li;
+  auto read_frag = [&](Frag& f, const float* As, const float* Bs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < T::kRB; ++i)
+      f.a[i] = *reinterpret_cast<const float4*>(As + a_frag + 32 * BK * i);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4 v = *reinterpret_cast<const float4*>(Bs + b_frag + t * BN);
+      f.b[0][t] = v.x;
+      f.b[1][t] = v.y;
+      f.b[2][t] = v.z;
+      f.b[3][t] = v.w;
+    }
+  };
+
+  f32x16 acc[T::kRB][T::kCB];
+#pragma unroll
+  for (int i = 0; i < T::kRB; ++i)
+#pragma unroll
+    for (int j = 0; j < T::kCB; ++j) acc[i][j] = f32x16{};
+  // the MFMAs of reduction offsets t in [t0, t1) of a chunk
+  auto mma = [&](const Frag& f, int t0, int t1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = t0; t < t1; ++t)
+#pragma unroll
+      for (int i = 0; i < T::kRB; ++i)
+#pragma unroll
+        for (int j = 0; j < T::kCB; ++j) {
+          const float av = t == 0 ? f.a[i].x : t == 1 ? f.a[i].y : t == 2 ? f.a[i].z : f.a[i].w;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, f.b[j][t], acc[i][j], 0, 0, 0);
+        }
+  };
+  constexpr int kMfmasT = T::kRB * T::kCB;  // MFMAs per reduction offset t
+  constexpr int kReads = T::kRB + 4;
+
+  Frag f[2];
+  // Ring fill with the wave's first chunk in stage OFF: that chunk through
+  // registers (zero where n < 0), the next S - 2 copied into the stages after it.
+  auto fill = [&](auto offc) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(offc)::value;
+    constexpr int X = OFF & 1;  // operand buffer of the chunk in stage OFF
+    using S0 = std::integral_constant<int, OFF>;
+    const int n0 = n_first + BK * c_begin;
+    float4 va[T::kACopies], vb[T::kBCopies];
+    bool oka[T::kACopies], okb[T::kBCopies];
+#pragma unroll
+    for (int j = 0; j < T::kACopies; ++j) {
+      oka[j] = n0 + 4 * a_quad[j] >= 0;
+      va[j] = *reinterpret_cast<const float4*>(oka[j] ? a_src[j] + n0 : A);
+    }
+#pragma unroll
+    for (int j = 0; j < T::kBCopies; ++j) {
+      okb[j] = n0 + 2 * j + lane / 32 >= 0;
+      vb[j] = *reinterpret_cast<const float4*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
+    }
+    static_for<1, S - 1>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      using Sj = std::integral_constant<int, (OFF + j) % S>;
+      copy_chunk(min(c_begin + j, c_last), a_stage(Sj{}), b_stage(Sj{}));
+    });
+#pragma unroll
+    for (int j = 0; j < T::kACopies; ++j)
+      *reinterpret_cast<float4*>(a_stage(S0{}) + a_dst[j] + 4 * lane) = mask_quad(va[j], oka[j] ? 0xfu : 0u);
+#pragma unroll
+    for (int j = 0; j < T::kBCopies; ++j)
+      *reinterpret_cast<float4*>(b_stage(S0{}) + b_dst[j] + 4 * lane) = mask_quad(vb[j], okb[j] ? 0xfu : 0u);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    __builtin_amdgcn_sched_barrier(0);
+    read_frag(f[X], a_stage(S0{}), b_stage(S0{}));
+  };
+
+  // Chunk c in stage s, one MFMA step; f[X] holds its operands on entry, and
+  // f[X ^ 1] receives chunk c + 1's. The copy of chunk c + S - 1 (clamped to
+  // the wave's last chunk) goes to the stage chunk c - 1 used; chunk c + 1's
+  // copies were issued S - 2 chunks ago.
+  auto chunk = [&](auto sc, auto xc, int c) __attribute__((always_inline)) {
+    constexpr int s = decltype(sc)::value, X = decltype(xc)::value;
+    using Sn = std::integral_constant<int, (s + 1) % S>;
+    using Sp = std::integral_constant<int, (s + S - 1) % S>;
+    // t = 0: the copies among its 16 MFMAs
+    copy_chunk(min(c + S - 1, c_last), a_stage(Sp{}), b_stage(Sp{}));
+    mma(f[X], 0, 1);
+    sched_pairs<kSchedVmemRead, kMfmasT / T::kCopies, T::kCopies>();
+    __builtin_amdgcn_sched_barrier(0);
+    // chunk c + 1 has landed in LDS: its operand reads among the 48 MFMAs of t = 1..3
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(T::kCopies * (S - 2)));
+    __builtin_amdgcn_sched_barrier(0);
+    read_frag(f[X ^ 1], a_stage(Sn{}), b_stage(Sn{}));
+    mma(f[X], 1, 4);
+    sched_interleave<3 * kMfmasT, 0, 0, kReads>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Chunk k of a group of S uses stage k and operand buffer k & 1 (S is
+  // even, so a group always starts with buffer 0). The wave's (count mod S)
+  // leading chunks run in stages S - r .. S - 1 so that the loop below starts
+  // at stage 0 with whole groups; one loop, so the accumulators stay in place.
+  const int nmine = c_end - c_begin;
+  const int lead = nmine % S;
+  static_for<0, S>([&](auto rc) {
+    constexpr int R = decltype(rc)::value;
+    if (lead == R) {
+      fill(std::integral_constant<int, (S - R) % S>{});
+      static_for<0, R>([&](auto kc) {
+        constexpr int k = S - R + decltype(kc)::value;
+        chunk(std::integral_constant<int, k>{}, std::integral_constant<int, k & 1>{}, c_begin + k - (S - R));
+      });
+    }
+  });
+  for (int c = c_begin + lead; c < c_end; c += S)
+    static_for<0, S>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      chunk(std::integral_constant<int, k>{}, std::integral_constant<int, k & 1>{}, c + k);
+    });
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // stray copies past the wave's last chunk
+
+  // The four partial tiles are added in wave order, ((p0 + p1) + p2) + p3,
+  // through LDS (the staging is free once every wave is past the first
+  // barrier), two partials at a time: wave w sums and stores block row w of the
+  // tile (MFMA blocks i = w, j = 0..3). Register group g of a partial (blocks
+  // i = g) lives in stage object g of A (waves 0 and 2) or of B (waves 1 and
+  // 3), lane-major as float4: consecutive lanes write consecutive 16 bytes.
+  auto put = [&](bool use_b) __attribute__((always_inline)) {
+    static_for<0, T::kRB>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      float* p = use_b ? b_stage(gc) : a_stage(gc);
+#pragma unroll
+      for (int j = 0; j < T::kCB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(p + ((j * 4 + q) * 64 + lane) * 4) =
+              make_float4(acc[g][j][4 * q], acc[g][j][4 * q + 1], acc[g][j][4 * q + 2], acc[g][j][4 * q + 3]);
+    });
+  };
+  float sum[T::kCB][16];
+  // sum (+)= group `wave` of the partial in the A (use_b false) or B objects
+  auto take = [&](bool use_b, bool first) __attribute__((always_inline)) {
+    static_for<0, T::kRB>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if (wave != g) return;
+      const float* p = use_b ? b_stage(gc) : a_stage(gc);
+#pragma unroll
+      for (int j = 0; j < T::kCB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(p + ((j * 4 + q) * 64 + lane) * 4);
+          const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sum[j][4 * q + k] = first ? e[k] : sum[j][4 * q + k] + e[k];
+        }
+    });
+  };
+  __syncthreads();
+  if (wave == 0) put(false);
+  if (wave == 1) put(true);
+  __syncthreads();
+  take(false, true);
+  take(true, false);
+  __syncthreads();
+  if (wave == 2) put(false);
+  if (wave == 3) put(true);
+  __syncthreads();
+  take(false, false);
+  take(true, false);
+
+  // Block row `wave` of the tile, 4 adjacent columns per lane and row.
+  float* const Ct = C + (int64_t)m0 * K + k0;
+  const int col = 4 * li;
+  const bool col_ok = k0 + col < K;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int row = wave * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
+    if (col_ok && m0 + row < M) {
+      float* dst = Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col;
+      *reinterpret_cast<float4*>(dst) = make_float4(sum[0][rr], sum[1][rr], sum[2][rr], sum[3][rr]);
+    }
+  }
+}
+
+}  // namespace fgr

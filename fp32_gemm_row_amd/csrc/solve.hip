@@ -12,6 +12,7 @@
 #include "fp32_gemm_row.h"
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_dma.hpp"
+#include "gemm_mfma_ksplit.hpp"
 #include "gemm_mfma_split.hpp"
 #include "gemv.hpp"
 
@@ -89,6 +90,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // left over, 130.6 vs 121.7 TFLOP/s, and loses at 192, 129.0 vs 131.5).
 int64_t tail_tiles(int cus) { return (int64_t)cus * 11 / 16; }
 
+// The same for 128x128 tiles of the k-split kernel (measured: 2560^3, 144 of
+// 256 left over, 105.4 TFLOP/s with the split tail, 108.4 without; 3072^3, 64
+// left over, 131.1 vs 104.7).
+int64_t ksplit_tail_tiles(int cus) { return cus / 2; }
+
 struct Choice {
   int path;
   int tile;
@@ -112,6 +118,12 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
       if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
       return {FGR_PATH_MFMA_DMA, FGR_TILE_256};
     }
+    if (t128 >= cus && mfma_dma_ok(A, B, C, N, K)) {
+      // 128x128 tiles with the reduction split over a workgroup's waves
+      const int64_t rem = t128 % cus;
+      if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
+      return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
+    }
     if (t64 < cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
     if (t64 < 2 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_64};
     if (t64 < 4 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
@@ -129,6 +141,8 @@ int default_tile(int path, const Choice& auto_choice, int M, int K, int cus) {
   switch (path) {
     case FGR_PATH_MFMA_DMA:
     case FGR_PATH_MFMA_DMA_TAIL: return FGR_TILE_256;
+    case FGR_PATH_MFMA_KSPLIT:
+    case FGR_PATH_MFMA_KSPLIT_TAIL: return FGR_TILE_128;
     case FGR_PATH_MFMA_SPLIT: return cdiv(M, 64) * cdiv(K, 64) < cus ? FGR_TILE_32 : FGR_TILE_64;
     case FGR_PATH_MFMA_VEC:
     case FGR_PATH_MFMA_SCALAR:
@@ -195,15 +209,16 @@ int launch_split(const float* A, const float* B, float* C, int M, int N, int K, 
                 (int64_t)tiles_m * tiles_n, Cfg::kThreads, args, s);
 }
 
-// The split kernel over 256x256 tiles [first, first + count) of the direct-copy
-// kernel's grid (same grouped order), each cut into (256 / BM)^2 tiles.
-template <class Cfg>
+// The split kernel over big tiles [first, first + count) of a BIG x BIG grid
+// (same grouped order as the kernel that ran the others), each cut into
+// (BIG / BM)^2 tiles.
+template <class Cfg, int BIG>
 int launch_split_big(const float* A, const float* B, float* C, int M, int N, int K, int first, int count,
                      hipStream_t s) {
-  int tiles_m = (int)cdiv(M, TileDma::BM);
-  int tiles_n = (int)cdiv(K, TileDma::BN);
+  int tiles_m = (int)cdiv(M, BIG);
+  int tiles_n = (int)cdiv(K, BIG);
   int group = kTileGroup;
-  int sub = TileDma::BM / Cfg::BM;
+  int sub = BIG / Cfg::BM;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &first, &sub};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_split_kernel<Cfg, true>),
                 (int64_t)count * sub * sub, Cfg::kThreads, args, s);
@@ -226,9 +241,38 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
     if (rc != FGR_OK || rem == 0) return rc;
   }
   if (full > INT_MAX || rem > INT_MAX / 64) return FGR_ERR_BAD_DIMS;
-  if (rem * 16 >= 2 * cus) return launch_split_big<Split64x4>(A, B, C, M, N, K, (int)full, (int)rem, s);
-  if (rem * 16 >= cus) return launch_split_big<Split64x8>(A, B, C, M, N, K, (int)full, (int)rem, s);
-  return launch_split_big<Split32>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  if (rem * 16 >= 2 * cus) return launch_split_big<Split64x4, 256>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  if (rem * 16 >= cus) return launch_split_big<Split64x8, 256>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  return launch_split_big<Split32, 256>(A, B, C, M, N, K, (int)full, (int)rem, s);
+}
+
+using TileKsplit = fgr::KsplitConfig<4>;  // 128x128, each of 4 waves a quarter of the reduction
+
+// The k-split kernel over the first `count` 128x128 tiles of the grouped
+// order (count < 0: all of them).
+int launch_ksplit(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s) {
+  int tiles_m = (int)cdiv(M, TileKsplit::BM);
+  int tiles_n = (int)cdiv(K, TileKsplit::BN);
+  int group = kTileGroup;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<TileKsplit>),
+                count < 0 ? (int64_t)tiles_m * tiles_n : count, TileKsplit::kThreads, args, s);
+}
+
+// Whole waves of 128x128 tiles on the k-split kernel, the last partial wave's
+// tiles cut into 64x64 (or 32x32) split-reduction tiles (as launch_dma_tail).
+int launch_ksplit_tail(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
+  const int64_t tiles = cdiv(M, TileKsplit::BM) * cdiv(K, TileKsplit::BN);
+  const int64_t full = tiles / cus * cus;
+  const int64_t rem = tiles - full;
+  if (full > 0) {
+    const int rc = launch_ksplit(A, B, C, M, N, K, full, s);
+    if (rc != FGR_OK || rem == 0) return rc;
+  }
+  if (full > INT_MAX || rem > INT_MAX / 16) return FGR_ERR_BAD_DIMS;
+  if (rem * 4 >= 2 * cus) return launch_split_big<Split64x4, 128>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  if (rem * 4 >= cus) return launch_split_big<Split64x8, 128>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  return launch_split_big<Split32, 128>(A, B, C, M, N, K, (int)full, (int)rem, s);
 }
 
 template <bool VEC>
@@ -271,6 +315,11 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       if (!mfma_dma_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256))
         return FGR_ERR_BAD_PATH;
       break;
+    case FGR_PATH_MFMA_KSPLIT:
+    case FGR_PATH_MFMA_KSPLIT_TAIL:
+      if (!mfma_dma_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_128))
+        return FGR_ERR_BAD_PATH;
+      break;
     case FGR_PATH_MFMA_SCALAR: break;
     case FGR_PATH_MFMA_SPLIT:
       if (tile != FGR_TILE_AUTO && tile != FGR_TILE_32 && tile != FGR_TILE_64) return FGR_ERR_BAD_PATH;
@@ -301,8 +350,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       path = best.path;
     } else if (tile == FGR_TILE_32) {
       path = FGR_PATH_MFMA_SPLIT;  // the only kernel with 32x32 tiles
-    } else if (tile == FGR_TILE_256 && (best.path == FGR_PATH_MFMA_DMA || best.path == FGR_PATH_MFMA_DMA_TAIL)) {
-      path = best.path;
+    } else if (tile == best.tile && (best.path == FGR_PATH_MFMA_DMA || best.path == FGR_PATH_MFMA_DMA_TAIL ||
+                                     best.path == FGR_PATH_MFMA_KSPLIT || best.path == FGR_PATH_MFMA_KSPLIT_TAIL)) {
+      path = best.path;  // the direct-copy or k-split kernel the table picked for this tile
     } else {
       path = mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
     }
@@ -312,6 +362,8 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   switch (path) {
     case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, -1, s);
     case FGR_PATH_MFMA_DMA_TAIL: return launch_dma_tail(A, B, C, M, N, K, cus, s);
+    case FGR_PATH_MFMA_KSPLIT: return launch_ksplit(A, B, C, M, N, K, -1, s);
+    case FGR_PATH_MFMA_KSPLIT_TAIL: return launch_ksplit_tail(A, B, C, M, N, K, cus, s);
     case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SPLIT:

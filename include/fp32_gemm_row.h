@@ -43,7 +43,8 @@
  *   N >= 64 and enough 256 x 256 output tiles to fill the device, A and B are
  *   copied straight from global memory into LDS (the role of the cp.async
  *   pipeline of the write-up's section "V4"). Shapes with too few output tiles
- *   for the device split each tile's reduction over the waves of a workgroup;
+ *   for the device take 128 x 128 tiles whose reduction is split over the
+ *   four waves of a workgroup, or smaller tiles split the same way;
  *   when a last, partial wave of 256 x 256 tiles is left, its tiles are cut
  *   into small split-reduction tiles. M <= 8 takes the bandwidth-bound
  *   matrix-vector path, which streams B once for all rows of A.
@@ -93,6 +94,11 @@ extern "C" {
                                     split kernel on the tiles of the last, partial wave, cut into
                                     64x64 or 32x32 tiles; same conditions as MFMA_DMA. Two
                                     launches on `stream`. */
+#define FGR_PATH_MFMA_KSPLIT 8 /* FP32 MFMA, 128x128 tiles, each of a workgroup's four waves reducing a
+                                  quarter of N into the whole tile from its own direct global->LDS
+                                  copies; same conditions as MFMA_DMA (tile 128 only) */
+#define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT on the whole waves of 128x128 tiles, the split kernel
+                                       on the tiles of the last, partial wave; two launches */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0

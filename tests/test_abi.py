@@ -111,7 +111,10 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
-    # the tail-split form of it has the same conditions
+    # the tail-split form of it, and the k-split paths (tile 128), have the same conditions
+    assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT_TAIL) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 256) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA_TAIL, 64) == fgr.ERR_BAD_PATH
@@ -138,7 +141,12 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4096, 4096, 7168) == fgr.PATH_MFMA_DMA  # 448 tiles: 192 left over
     assert sp(A0, B0, C0, 8192, 6208, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 544 tiles
     assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_SCALAR
-    assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_SPLIT  # too few 256x256 tiles
+    assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_KSPLIT  # 64 tiles of 256, 256 of 128
+    assert sp(A0, B0, C0, 1024, 6144, 4096) == fgr.PATH_MFMA_KSPLIT  # a row shard of the timed shape
+    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT_TAIL  # 576 tiles of 128
+    assert sp(A0, B0, C0, 2000, 3000, 2100) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 tiles of 128
+    assert sp(A0, B0, C0, 2048, 60, 2048) == fgr.PATH_MFMA_VEC  # N < 64: no direct copies
+    assert sp(A0, B0, C0, 2560, 2560, 2560) == fgr.PATH_MFMA_KSPLIT  # 400 tiles of 128: 144 over half a wave
     assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_GEMV_SCALAR  # skinny, K % 4 != 0
     assert sp(A0, B0, C0, 40, 8, 6) == fgr.PATH_MFMA_SPLIT
     assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR  # misaligned A
@@ -161,7 +169,9 @@ def test_tile_selection():
     assert st(A0, B0, C0, 1023, 1025, 1027) == 32  # split, 32x32
     assert st(A0, B0, C0, 256, 256, 256) == 32
     assert st(A0, B0, C0, 1024, 1024, 1024) == 64  # split, 64x64
-    assert st(A0, B0, C0, 2048, 512, 2048) == 64  # register-staged, 64x64
+    assert st(A0, B0, C0, 2048, 512, 2048) == 128  # k-split, 128x128
+    assert st(A0, B0, C0, 2048, 512, 1024) == 32  # 128 tiles of 128: split, 32x32
+    assert st(A0, B0, C0, 2048, 60, 2048) == 64  # no direct copies (N < 64): register-staged 64x64
     assert st(A0, B0, C0, 4095, 4097, 4099) == 128  # 32-bit loads, many tiles
     assert st(A0, B0, C0, 1, 8192, 8192) == 0  # matrix-vector
     assert st(0, B0, C0, 4, 4, 4) == fgr.ERR_NULL_POINTER
@@ -172,8 +182,9 @@ def test_split_path_choices():
     assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_SPLIT
     assert sp(A0, B0, C0, 256, 256, 256) == fgr.PATH_MFMA_SPLIT
     assert sp(A0, B0, C0, 1024, 8192, 1024) == fgr.PATH_MFMA_SPLIT
-    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_SPLIT
-    assert sp(A0, B0, C0, 2048, 512, 2048) == fgr.PATH_MFMA_VEC
+    assert sp(A0, B0, C0, 1536, 4096, 1536) == fgr.PATH_MFMA_SPLIT  # 144 tiles of 128
+    assert sp(A0, B0, C0, 2048, 512, 1024) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 2048, 60, 2048) == fgr.PATH_MFMA_VEC
     assert sp(A0, B0, C0, 2047, 2049, 2051) == fgr.PATH_MFMA_SCALAR
 
 

@@ -93,6 +93,9 @@ def paths_for(M, N, K):
         # below one wave of 256x256 tiles every tile is in the tail: the split
         # kernel's big-tile mode alone, partial big tiles included
         out.append((fgr.PATH_MFMA_DMA_TAIL, fgr.TILE_256))
+        # 128x128 tiles with the reduction split over the waves; and its tail form
+        out.append((fgr.PATH_MFMA_KSPLIT, fgr.TILE_128))
+        out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
     if M <= 8:
@@ -226,7 +229,8 @@ def test_large_workloads_sampled(name):
 
 
 @pytest.mark.parametrize("shape", [(8000, 6000, 4000), (3072, 3072, 3072), (1024, 8192, 1024), (2047, 2049, 2051),
-                                   (4096, 1028, 4160), (8192, 2052, 4100), (4300, 1000, 4096)],
+                                   (4096, 1028, 4160), (8192, 2052, 4100), (4300, 1000, 4096),
+                                   (1024, 6144, 4096), (2000, 3000, 2100)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_large_ragged_sampled(shape):
     # partial 256x256 tiles with a ragged reduction (direct-copy path), the
@@ -239,6 +243,24 @@ def test_large_ragged_sampled(shape):
     rows, cols = sample_positions(M, K, 64, rng, extra=1024)
     Cref, S = oracle.gemm_at(A, B, rows, cols)
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{shape} sampled")
+
+
+@pytest.mark.parametrize("shape,path", [
+    ((2048, 64, 2048), fgr.PATH_MFMA_KSPLIT), ((2040, 1000, 2044), fgr.PATH_MFMA_KSPLIT),
+    ((2176, 72, 2048), fgr.PATH_MFMA_KSPLIT_TAIL), ((3072, 68, 3076), fgr.PATH_MFMA_KSPLIT_TAIL),
+], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else fgr.PATH_NAMES[v])
+def test_ksplit_exact(shape, path):
+    # 128x128 tiles, each wave of a workgroup reducing a quarter of N; with a
+    # partial last wave of them, the rest cut into split-kernel tiles: exact on
+    # integer data whichever kernel computed an output
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=6)
+    say(f"k-split {shape}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == path
+    say(f"k-split {shape}: GPU")
+    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT, fgr.TILE_128), Cref, f"{shape} k-split only")
 
 
 @pytest.mark.parametrize("shape", [(4352, 64, 4096), (4100, 68, 4100), (2304, 100, 8192), (65792, 64, 256)],
@@ -286,8 +308,10 @@ def test_gemv_workload_full_compare():
     ((1023, 1025, 1027), fgr.PATH_AUTO, 0),
     ((512, 256, 768), fgr.PATH_MFMA_DMA, 256),
     ((300, 500, 260), fgr.PATH_MFMA_SPLIT, 64),
+    ((300, 500, 260), fgr.PATH_MFMA_KSPLIT, 128),
     ((1, 3000, 900), fgr.PATH_GEMV_VEC, 0),
-], ids=["ragged-auto", "dma", "split64", "gemv"])
+    ((5, 3000, 900), fgr.PATH_GEMV_VEC, 0),
+], ids=["ragged-auto", "dma", "split64", "ksplit", "gemv", "skinny"])
 def test_repeat_runs_are_bitwise_identical(shape, path, tile):
     # fixed reduction order and no atomics: identical bits on every run
     M, N, K = shape
