@@ -41,7 +41,9 @@ sys.path.insert(0, ROOT)
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X: 256 CU x 256 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 METRIC = "FP32 GEMM TFLOP/s at M=8192,N=6144,K=4096; % of MI355X FP32 MFMA peak"
-KERNEL_SOURCES = ["gemm_mfma.hpp", "gemm_mfma_dma.hpp", "gemm_mfma_split.hpp", "gemv.hpp", "solve.hip"]
+# every source the library is built from (csrc/*.hpp and csrc/*.hip)
+KERNEL_SOURCES = sorted(n for n in os.listdir(os.path.join(ROOT, "fp32_gemm_row_amd", "csrc"))
+                        if n.endswith((".hpp", ".hip")))
 COPY_BYTES = 512 << 20
 
 
