@@ -1,11 +1,13 @@
 // FP32 MFMA GEMM for whole-device shapes, fed by direct global->LDS copies
 // through a ring of S LDS stages.
 //
-// Same product, output tiling and operand layout as gemm_mfma.hpp, for rows
-// that are 16-byte aligned (N % 4 == 0, K % 4 == 0, aligned bases) and
+// Same product, output tiling and operand layout as gemm_mfma.hpp, for
 // N >= 64. Every reduction chunk but the first is copied from global memory
 // straight into LDS with global_load_lds_dwordx4 (16 bytes per lane, written
-// to LDS at the M0 base + 16 * lane), the gfx950 counterpart of the cp.async
+// to LDS at the M0 base + 16 * lane) when rows are 16-byte aligned (N % 4 ==
+// 0, K % 4 == 0, aligned bases), else with global_load_lds_dword (4 bytes per
+// lane, four times as many copies, the same LDS layout), the gfx950
+// counterpart of the cp.async
 // copies of the LeetGPU write-up's section "V4: Hardware-Asynchronous cp.async
 // Pipeline". The data never passes through VGPRs, so the copies take no
 // register-file bandwidth from the MFMAs and no LDS write instructions are
@@ -39,11 +41,14 @@
 // the reads of one stage from the copies into another):
 //   A stage: BM rows x BK floats, unpadded; row r holds its 4 quads in the
 //     order q ^ swz(r), swz(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1). One copy
-//     instruction fills 16 consecutive rows. The MFMA operand read of lane
-//     (i, g) fetches quad 2h + g of row i; over any 8 consecutive rows from a
-//     multiple of 8, and over 16 from a multiple of 16, the swizzle sends these
-//     reads to distinct 16-byte bank groups (32 or 64 banks).
-//   B stage: BK rows x BN floats, row-major; one copy instruction per row.
+//     instruction fills 16 consecutive rows (4 with 4-byte copies: a lane's
+//     source address is free, so the swizzle holds either way). The MFMA
+//     operand read of lane (i, g) fetches quad 2h + g of row i; over any 8
+//     consecutive rows from a multiple of 8, and over 16 from a multiple of
+//     16, the swizzle sends these reads to distinct 16-byte bank groups (32 or
+//     64 banks).
+//   B stage: BK rows x BN floats, row-major; one copy instruction per row (a
+//     quarter row with 4-byte copies).
 #pragma once
 
 #include "gemm_mfma.hpp"
@@ -52,29 +57,34 @@ namespace fgr {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int S_>
+// VEC: 16-byte copies (rows 16-byte aligned); otherwise 4-byte copies, four
+// times as many, into the same LDS layout (any 4-byte alignment).
+template <int S_, bool VEC_ = true>
 struct DmaConfig {
   static constexpr int BM = 256, BN = 256, BK = 16, WM = 2, WN = 2, S = S_;
+  static constexpr bool VEC = VEC_;
+  static constexpr int kCopyFloats = VEC ? 4 : 1;  // floats per lane per copy
+  static constexpr int kBlock = 64 * kCopyFloats;  // LDS floats one copy fills
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM;
   static constexpr int kWaveN = BN / WN;
   static constexpr int kRB = kWaveM / 32;
   static constexpr int kCB = kWaveN / 32;
-  static constexpr int kQuads = BK / 4;                        // quads per A row
-  static constexpr int kRowsPerCopy = 64 / kQuads;             // A rows per copy instruction
-  static constexpr int kACopies = BM / kRowsPerCopy / kWaves;  // per wave per chunk
-  static constexpr int kBCopies = BK / kWaves;                 // B rows per wave per chunk
+  static constexpr int kQuads = BK / 4;                     // quads per A row
+  static constexpr int kStage = BM * BK;                    // floats, A and B stages alike
+  static constexpr int kACopies = kStage / kBlock / kWaves;  // per wave per chunk
+  static constexpr int kBCopies = kStage / kBlock / kWaves;
   static constexpr int kCopies = kACopies + kBCopies;
-  static constexpr int kStage = BM * BK;                       // floats, A and B stages alike
 
-  static_assert(BN == 256, "one B copy instruction covers a 256-float row");
+  static_assert(BN % kBlock == 0, "a B copy stays inside one row");
   static_assert(BM * BK == BK * BN, "A and B stages have one size");
   static_assert(kQuads == 4, "the A swizzle is written for 4 quads per row");
   static_assert(kCB == 4, "B operands are read as 4 adjacent floats");
   static_assert(kRB * kCB * 16 == 256, "the accumulators fill the 256 AGPRs");
-  static_assert(BM % (kRowsPerCopy * kWaves) == 0 && BK % kWaves == 0, "copies split evenly over waves");
+  static_assert(kStage % (kBlock * kWaves) == 0, "copies split evenly over waves");
   static_assert(S >= 3 && S <= 5, "a ring of 3 to 5 stages");
+  static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
   static_assert(S * 2 * kStage * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
@@ -89,6 +99,11 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (((vm >> 
 // wave-uniform). A plain device function: the builtin has no host form.
 __device__ __forceinline__ void copy16_to_lds(const float* g, float* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// 4 bytes per lane, into LDS at lds + 4 * lane.
+__device__ __forceinline__ void copy4_to_lds(const float* g, float* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
 }
 
 template <class T>
@@ -140,43 +155,60 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   const int m0 = tm * T::BM;
   const int k0 = tn * BN;
 
-  // Copy sources for this lane. A copy j of this wave fills rows
-  // [R, R + 16), R = 16 * (wave * kACopies + j): lane L lands in row R + L / 4
-  // at stored position L % 4, which holds quad (L % 4) ^ swz(row). Rows past
-  // M read row M - 1 instead (their outputs are not stored).
+  // Copy sources for this lane. Copy j of this wave fills LDS floats
+  // [blk * kBlock, (blk + 1) * kBlock) of a stage, blk = wave * kACopies + j;
+  // lane L fills the kCopyFloats floats at position p = blk * kBlock +
+  // L * kCopyFloats. In the A stage position p is row p / 16, stored slot
+  // (p % 16) / 4, element p % 4, and the slot holds quad slot ^ swz(row), so
+  // the lane reads that quad's element (the whole quad with 16-byte copies).
+  // Rows past M read row M - 1 instead (their outputs are not stored).
   const float* a_src[T::kACopies];
-  int a_dst[T::kACopies];  // LDS float offset of the copy's 1 KiB block
-  int a_quad[T::kACopies];
+  int a_dst[T::kACopies];  // LDS float offset of the copy's block
+  int a_col[T::kACopies];  // column of the lane's first element inside the chunk
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
     const int blk = wave * T::kACopies + j;
-    const int r = blk * T::kRowsPerCopy + lane / T::kQuads;
-    const int q = (lane % T::kQuads) ^ a_swizzle(r);
+    const int pos = blk * T::kBlock + lane * T::kCopyFloats;
+    const int r = pos / BK;
+    const int q = ((pos % BK) / 4) ^ a_swizzle(r);
+    const int c = 4 * q + pos % 4;
     const int row = m0 + r < M ? m0 + r : M - 1;
-    a_src[j] = A + (int64_t)row * N + 4 * q;
-    a_dst[j] = blk * 256;
-    a_quad[j] = q;
+    a_src[j] = A + (int64_t)row * N + c;
+    a_dst[j] = blk * T::kBlock;
+    a_col[j] = c;
   }
-  // B copy j of this wave fills chunk row wave * kBCopies + j; lane L copies
-  // columns 4L .. 4L + 3 (past K: the last quad instead, not stored).
+  // In the B stage position p is row p / 256, column p % 256 (columns past K
+  // read the last column, or the last quad with 16-byte copies; not stored).
   const float* b_src[T::kBCopies];
   int b_dst[T::kBCopies];
-  const int b_col = k0 + 4 * lane < K ? k0 + 4 * lane : K - 4;
+  int b_row[T::kBCopies];
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
-    const int r = wave * T::kBCopies + j;
-    b_src[j] = B + (int64_t)r * K + b_col;
-    b_dst[j] = r * BN;
+    const int blk = wave * T::kBCopies + j;
+    const int pos = blk * T::kBlock + lane * T::kCopyFloats;
+    const int r = pos / BN;
+    const int c = k0 + pos % BN;
+    const int col = c < K ? c : K - T::kCopyFloats;
+    b_src[j] = B + (int64_t)r * K + col;
+    b_dst[j] = blk * T::kBlock;
+    b_row[j] = r;
   }
 
   // copies [P0, P1) of this wave's kCopies (A first, then B) of the chunk at n0
   auto copy_part = [&](auto p0c, auto p1c, int n0, float* As, float* Bs) __attribute__((always_inline)) {
     static_for<decltype(p0c)::value, decltype(p1c)::value>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (p < T::kACopies)
-        copy16_to_lds(a_src[p] + n0, As + a_dst[p]);
-      else
-        copy16_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
+      if constexpr (T::VEC) {
+        if constexpr (p < T::kACopies)
+          copy16_to_lds(a_src[p] + n0, As + a_dst[p]);
+        else
+          copy16_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
+      } else {
+        if constexpr (p < T::kACopies)
+          copy4_to_lds(a_src[p] + n0, As + a_dst[p]);
+        else
+          copy4_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
+      }
     });
   };
 
@@ -240,29 +272,34 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   auto fill = [&](auto offc) __attribute__((always_inline)) {
     constexpr int OFF = decltype(offc)::value;
     using S0 = std::integral_constant<int, OFF>;
-    float4 va[T::kACopies], vb[T::kBCopies];
+    typedef typename std::conditional<T::VEC, float4, float>::type CopyT;
+    CopyT va[T::kACopies], vb[T::kBCopies];
     bool oka[T::kACopies], okb[T::kBCopies];
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j) {
-      oka[j] = n_first + 4 * a_quad[j] >= 0;
-      va[j] = *reinterpret_cast<const float4*>(oka[j] ? a_src[j] + n_first : A);
+      oka[j] = n_first + a_col[j] >= 0;
+      va[j] = *reinterpret_cast<const CopyT*>(oka[j] ? a_src[j] + n_first : A);
     }
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j) {
-      okb[j] = n_first + wave * T::kBCopies + j >= 0;
-      vb[j] = *reinterpret_cast<const float4*>(okb[j] ? b_src[j] + (int64_t)n_first * K : B);
+      okb[j] = n_first + b_row[j] >= 0;
+      vb[j] = *reinterpret_cast<const CopyT*>(okb[j] ? b_src[j] + (int64_t)n_first * K : B);
     }
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       using Sj = std::integral_constant<int, (OFF + j) % S>;
       copy_part(I0{}, ICopies{}, n_first + BK * min(j, nchunks - 1), a_stage(Sj{}), b_stage(Sj{}));
     });
+    auto zero_out = [](CopyT v, bool ok) __attribute__((always_inline)) -> CopyT {
+      if constexpr (T::VEC) return mask_quad(v, ok ? 0xfu : 0u);
+      else return ok ? v : 0.f;
+    };
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
-      *reinterpret_cast<float4*>(a_stage(S0{}) + a_dst[j] + 4 * lane) = mask_quad(va[j], oka[j] ? 0xfu : 0u);
+      *reinterpret_cast<CopyT*>(a_stage(S0{}) + a_dst[j] + T::kCopyFloats * lane) = zero_out(va[j], oka[j]);
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j)
-      *reinterpret_cast<float4*>(b_stage(S0{}) + b_dst[j] + 4 * lane) = mask_quad(vb[j], okb[j] ? 0xfu : 0u);
+      *reinterpret_cast<CopyT*>(b_stage(S0{}) + b_dst[j] + T::kCopyFloats * lane) = zero_out(vb[j], okb[j]);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -313,9 +350,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   // Epilogue. Offsets are 32-bit from the tile's corner, a wave-uniform base,
-  // which keeps the address arithmetic small. K % 4 == 0 and a lane's 4
-  // adjacent columns start at a multiple of 4, so they are wholly inside or
-  // outside.
+  // which keeps the address arithmetic small. With 16-byte rows (K % 4 == 0)
+  // a lane's 4 adjacent columns start at a multiple of 4, so they are wholly
+  // inside or outside; otherwise each column is guarded and stored alone.
   float* const Ct = C + (int64_t)m0 * K + k0;
   const int col = wn * T::kWaveN + 4 * li;
   const bool col_ok = k0 + col < K;
@@ -326,7 +363,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
       const int row = wm * T::kWaveM + i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
       if (col_ok && m0 + row < M) {
         float* dst = Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0][rr], acc[i][1][rr], acc[i][2][rr], acc[i][3][rr]);
+        if constexpr (T::VEC) {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0][rr], acc[i][1][rr], acc[i][2][rr], acc[i][3][rr]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < T::kCB; ++j)
+            if (k0 + col + j < K) dst[j] = acc[i][j][rr];
+        }
       }
     }
 }

@@ -75,10 +75,12 @@ bool mfma_vec_ok(const float* A, const float* B, const float* C, int N, int K) {
 
 bool gemv_vec_ok(const float* B, int K) { return K % 4 == 0 && aligned(B, 16); }
 
-// Direct global->LDS copies need 16-byte aligned rows, and at least four
-// 16-deep reduction chunks (the copies that run past the last chunk re-read
-// it, and must never reach the zero-padded first chunk).
-bool mfma_dma_ok(const float* A, const float* B, const float* C, int N, int K) {
+// Direct global->LDS copies need at least four 16-deep reduction chunks (the
+// copies that run past the last chunk re-read it, and must never reach the
+// zero-padded first chunk); they are 16 bytes wide for 16-byte aligned rows,
+// 4 bytes otherwise. The k-split kernel copies 16 bytes only.
+bool mfma_dma_ok(int N) { return N >= 64; }
+bool mfma_ksplit_ok(const float* A, const float* B, const float* C, int N, int K) {
   return mfma_vec_ok(A, B, C, N, K) && N >= 64;
 }
 
@@ -110,15 +112,15 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
   const int64_t t256 = cdiv(M, 256) * cdiv(K, 256);
   const int64_t t128 = cdiv(M, 128) * cdiv(K, 128);
   const int64_t t64 = cdiv(M, 64) * cdiv(K, 64);
+  if (t256 >= cus && mfma_dma_ok(N)) {
+    // a last, partial wave of at most tail_tiles(cus) tiles goes to the split kernel
+    const int64_t rem = t256 % cus;
+    if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
+    return {FGR_PATH_MFMA_DMA, FGR_TILE_256};
+  }
   if (mfma_vec_ok(A, B, C, N, K)) {
-    if (t256 >= cus) {
-      if (!mfma_dma_ok(A, B, C, N, K)) return {FGR_PATH_MFMA_VEC, FGR_TILE_256};
-      // a last, partial wave of at most tail_tiles(cus) tiles goes to the split kernel
-      const int64_t rem = t256 % cus;
-      if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
-      return {FGR_PATH_MFMA_DMA, FGR_TILE_256};
-    }
-    if (t128 >= cus && mfma_dma_ok(A, B, C, N, K)) {
+    if (t256 >= cus) return {FGR_PATH_MFMA_VEC, FGR_TILE_256};  // N < 64
+    if (t128 >= cus && mfma_ksplit_ok(A, B, C, N, K)) {
       // 128x128 tiles with the reduction split over a workgroup's waves
       const int64_t rem = t128 % cus;
       if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
@@ -172,6 +174,9 @@ int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, h
 
 using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
 using TileDma = fgr::DmaConfig<4>;  // 256x256, 4 waves of 128x128 (accumulators in AGPRs), 4 LDS stages
+// 4-byte copies for rows that are not 16-byte aligned: four times as many, so
+// 3 stages (the copies in flight must fit the wave's vmcnt counter)
+using TileDmaScalar = fgr::DmaConfig<3, false>;
 
 // The direct-copy kernel over the first `count` tiles of the grouped order
 // (count < 0: all of them).
@@ -181,8 +186,10 @@ int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int 
   int tiles_n = (int)cdiv(K, TileDma::BN);
   int group = kTileGroup;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
-  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDma>),
-                count < 0 ? (int64_t)tiles_m * tiles_n : count, TileDma::kThreads, args, s);
+  const void* kernel = mfma_vec_ok(A, B, C, N, K)
+                           ? reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDma>)
+                           : reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDmaScalar>);
+  return launch(kernel, count < 0 ? (int64_t)tiles_m * tiles_n : count, TileDma::kThreads, args, s);
 }
 using Tile128 = fgr::MfmaConfig<128, 128, 16, 2, 2>;
 using Tile64 = fgr::MfmaConfig<64, 64, 16, 2, 2>;
@@ -212,7 +219,7 @@ int launch_split(const float* A, const float* B, float* C, int M, int N, int K, 
 // The split kernel over big tiles [first, first + count) of a BIG x BIG grid
 // (same grouped order as the kernel that ran the others), each cut into
 // (BIG / BM)^2 tiles.
-template <class Cfg, int BIG>
+template <class Cfg, int BIG, bool VEC>
 int launch_split_big(const float* A, const float* B, float* C, int M, int N, int K, int first, int count,
                      hipStream_t s) {
   int tiles_m = (int)cdiv(M, BIG);
@@ -220,13 +227,25 @@ int launch_split_big(const float* A, const float* B, float* C, int M, int N, int
   int group = kTileGroup;
   int sub = BIG / Cfg::BM;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &first, &sub};
-  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_split_kernel<Cfg, true>),
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_split_kernel<Cfg, VEC>),
                 (int64_t)count * sub * sub, Cfg::kThreads, args, s);
 }
 
 using Split32 = fgr::SplitConfig<32, 32, 16, 4>;
 using Split64x4 = fgr::SplitConfig<64, 64, 16, 4>;
 using Split64x8 = fgr::SplitConfig<64, 64, 16, 8>;
+
+// The split kernel over the BIG x BIG tiles [full, full + rem): 64x64 pieces
+// (eight waves each while there are fewer than two per CU), or 32x32 pieces
+// while 64x64 ones would leave CUs idle.
+template <int BIG, bool VEC>
+int launch_split_tail(const float* A, const float* B, float* C, int M, int N, int K, int64_t full, int64_t rem,
+                      int cus, hipStream_t s) {
+  constexpr int64_t per64 = (BIG / 64) * (BIG / 64);
+  if (rem * per64 >= 2 * cus) return launch_split_big<Split64x4, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  if (rem * per64 >= cus) return launch_split_big<Split64x8, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  return launch_split_big<Split32, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
+}
 
 // Whole waves of 256x256 tiles (one tile per CU) on the direct-copy kernel;
 // the tiles of the last, partial wave on the split kernel, cut into 64x64
@@ -241,9 +260,8 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
     if (rc != FGR_OK || rem == 0) return rc;
   }
   if (full > INT_MAX || rem > INT_MAX / 64) return FGR_ERR_BAD_DIMS;
-  if (rem * 16 >= 2 * cus) return launch_split_big<Split64x4, 256>(A, B, C, M, N, K, (int)full, (int)rem, s);
-  if (rem * 16 >= cus) return launch_split_big<Split64x8, 256>(A, B, C, M, N, K, (int)full, (int)rem, s);
-  return launch_split_big<Split32, 256>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  if (mfma_vec_ok(A, B, C, N, K)) return launch_split_tail<256, true>(A, B, C, M, N, K, full, rem, cus, s);
+  return launch_split_tail<256, false>(A, B, C, M, N, K, full, rem, cus, s);
 }
 
 using TileKsplit = fgr::KsplitConfig<4>;  // 128x128, each of 4 waves a quarter of the reduction
@@ -270,9 +288,7 @@ int launch_ksplit_tail(const float* A, const float* B, float* C, int M, int N, i
     if (rc != FGR_OK || rem == 0) return rc;
   }
   if (full > INT_MAX || rem > INT_MAX / 16) return FGR_ERR_BAD_DIMS;
-  if (rem * 4 >= 2 * cus) return launch_split_big<Split64x4, 128>(A, B, C, M, N, K, (int)full, (int)rem, s);
-  if (rem * 4 >= cus) return launch_split_big<Split64x8, 128>(A, B, C, M, N, K, (int)full, (int)rem, s);
-  return launch_split_big<Split32, 128>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  return launch_split_tail<128, true>(A, B, C, M, N, K, full, rem, cus, s);
 }
 
 template <bool VEC>
@@ -312,12 +328,11 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     case FGR_PATH_MFMA_DMA:
     case FGR_PATH_MFMA_DMA_TAIL:
-      if (!mfma_dma_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256))
-        return FGR_ERR_BAD_PATH;
+      if (!mfma_dma_ok(N) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256)) return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
-      if (!mfma_dma_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_128))
+      if (!mfma_ksplit_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_128))
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SCALAR: break;

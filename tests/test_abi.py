@@ -105,19 +105,21 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 9, 8, 8, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 9, 8, 8, fgr.PATH_GEMV_SCALAR) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 1, 8, 6, fgr.PATH_GEMV_VEC) == fgr.ERR_BAD_PATH
-    # the direct-copy path needs 128-bit rows, N >= 64 and tile 256
+    # the direct-copy paths need N >= 64 and tile 256; rows that are not
+    # 16-byte aligned take 4-byte copies (accepted: without a GPU the call then
+    # stops at the device check)
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 130, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA, 128) == fgr.ERR_BAD_PATH
-    assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
-    # the tail-split form of it, and the k-split paths (tile 128), have the same conditions
+    assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
+    for path in (fgr.PATH_MFMA_DMA, fgr.PATH_MFMA_DMA_TAIL):
+        assert call(lib, A0, B0, C0, 512, 130, 512, path) == fgr.ERR_DEVICE
+        assert call(lib, A0, B0, C0, 512, 128, 502, path) == fgr.ERR_DEVICE
+        assert call(lib, A0 + 4, B0, C0, 512, 128, 512, path) == fgr.ERR_DEVICE
+    # the k-split paths need 128-bit rows, N >= 64 and tile 128
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT_TAIL) == fgr.ERR_BAD_PATH
+    assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 256) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA_TAIL, 64) == fgr.ERR_BAD_PATH
     # 32x32 tiles exist on the split path only
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_VEC, 32) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_SPLIT, 128) == fgr.ERR_BAD_PATH
@@ -140,7 +142,7 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4096, 4096, 6656) == fgr.PATH_MFMA_DMA_TAIL  # 416 tiles: 160 left over
     assert sp(A0, B0, C0, 4096, 4096, 7168) == fgr.PATH_MFMA_DMA  # 448 tiles: 192 left over
     assert sp(A0, B0, C0, 8192, 6208, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 544 tiles
-    assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 4-byte copies
     assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_KSPLIT  # 64 tiles of 256, 256 of 128
     assert sp(A0, B0, C0, 1024, 6144, 4096) == fgr.PATH_MFMA_KSPLIT  # a row shard of the timed shape
     assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT_TAIL  # 576 tiles of 128
@@ -149,8 +151,10 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 2560, 2560, 2560) == fgr.PATH_MFMA_KSPLIT  # 400 tiles of 128: 144 over half a wave
     assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_GEMV_SCALAR  # skinny, K % 4 != 0
     assert sp(A0, B0, C0, 40, 8, 6) == fgr.PATH_MFMA_SPLIT
-    assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR  # misaligned A
-    assert sp(A0, B0, C0 + 8, 8192, 8192, 8192) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_DMA  # misaligned A: 4-byte copies
+    assert sp(A0, B0, C0 + 8, 8192, 8192, 8192) == fgr.PATH_MFMA_DMA
+    assert sp(A0, B0, C0, 8191, 6143, 4095) == fgr.PATH_MFMA_DMA  # ragged rows: 4-byte copies
+    assert sp(A0, B0, C0, 8192, 60, 8190) == fgr.PATH_MFMA_SCALAR  # N < 64
     assert sp(A0, B0, C0, 1, 8192, 8192) == fgr.PATH_GEMV_VEC
     assert sp(A0, B0, C0, 1, 3, 1) == fgr.PATH_GEMV_SCALAR
     assert sp(A0, B0 + 4, C0, 1, 8, 8) == fgr.PATH_GEMV_SCALAR
@@ -172,7 +176,8 @@ def test_tile_selection():
     assert st(A0, B0, C0, 2048, 512, 2048) == 128  # k-split, 128x128
     assert st(A0, B0, C0, 2048, 512, 1024) == 32  # 128 tiles of 128: split, 32x32
     assert st(A0, B0, C0, 2048, 60, 2048) == 64  # no direct copies (N < 64): register-staged 64x64
-    assert st(A0, B0, C0, 4095, 4097, 4099) == 128  # 32-bit loads, many tiles
+    assert st(A0, B0, C0, 4095, 4097, 4099) == 256  # 4-byte direct copies, 256 tiles
+    assert st(A0, B0, C0, 4095, 60, 4099) == 128  # N < 64: 32-bit loads, many tiles
     assert st(A0, B0, C0, 1, 8192, 8192) == 0  # matrix-vector
     assert st(0, B0, C0, 4, 4, 4) == fgr.ERR_NULL_POINTER
 

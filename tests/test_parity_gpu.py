@@ -88,11 +88,13 @@ def paths_for(M, N, K):
         out.append((fgr.PATH_MFMA_SCALAR, tile))
         if N % 4 == 0 and K % 4 == 0:
             out.append((fgr.PATH_MFMA_VEC, tile))
-    if N % 4 == 0 and K % 4 == 0 and N >= 64:
+    if N >= 64:
+        # direct copies: 16 bytes wide for 16-byte rows, 4 bytes otherwise
         out.append((fgr.PATH_MFMA_DMA, fgr.TILE_256))
         # below one wave of 256x256 tiles every tile is in the tail: the split
         # kernel's big-tile mode alone, partial big tiles included
         out.append((fgr.PATH_MFMA_DMA_TAIL, fgr.TILE_256))
+    if N % 4 == 0 and K % 4 == 0 and N >= 64:
         # 128x128 tiles with the reduction split over the waves; and its tail form
         out.append((fgr.PATH_MFMA_KSPLIT, fgr.TILE_128))
         out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128))
@@ -160,6 +162,9 @@ def test_misaligned_pointers_take_scalar_path(shape):
     for offs in [(1, 0, 0), (0, 1, 0), (0, 0, 1), (3, 2, 1)]:
         say(f"misaligned {shape} offsets={offs}")
         assert_exact(gpu_gemm(A, B, offsets=offs), Cref, f"misaligned {shape} {offs}")
+        if N >= 64:  # the direct-copy kernel with 4-byte copies
+            assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256, offsets=offs), Cref,
+                         f"misaligned {shape} {offs} direct copies")
 
 
 def test_vec_path_refuses_misaligned_pointer():
@@ -230,7 +235,7 @@ def test_large_workloads_sampled(name):
 
 @pytest.mark.parametrize("shape", [(8000, 6000, 4000), (3072, 3072, 3072), (1024, 8192, 1024), (2047, 2049, 2051),
                                    (4096, 1028, 4160), (8192, 2052, 4100), (4300, 1000, 4096),
-                                   (1024, 6144, 4096), (2000, 3000, 2100)],
+                                   (1024, 6144, 4096), (2000, 3000, 2100), (8191, 6143, 4095), (4099, 1001, 4351)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_large_ragged_sampled(shape):
     # partial 256x256 tiles with a ragged reduction (direct-copy path), the
@@ -309,9 +314,10 @@ def test_gemv_workload_full_compare():
     ((512, 256, 768), fgr.PATH_MFMA_DMA, 256),
     ((300, 500, 260), fgr.PATH_MFMA_SPLIT, 64),
     ((300, 500, 260), fgr.PATH_MFMA_KSPLIT, 128),
+    ((300, 500, 261), fgr.PATH_MFMA_DMA, 256),
     ((1, 3000, 900), fgr.PATH_GEMV_VEC, 0),
     ((5, 3000, 900), fgr.PATH_GEMV_VEC, 0),
-], ids=["ragged-auto", "dma", "split64", "ksplit", "gemv", "skinny"])
+], ids=["ragged-auto", "dma", "split64", "ksplit", "dma-4byte", "gemv", "skinny"])
 def test_repeat_runs_are_bitwise_identical(shape, path, tile):
     # fixed reduction order and no atomics: identical bits on every run
     M, N, K = shape
