@@ -1,20 +1,21 @@
-// FP32 MFMA GEMM for mid-size shapes: 128x128 output tiles whose reduction is
-// split over the four waves of a workgroup, each wave fed by its own direct
-// global->LDS copies.
+// FP32 MFMA GEMM for mid-size and small shapes: square BM x BM output tiles
+// (BM = 32, 64 or 128) whose reduction is split over the four waves of a
+// workgroup, each wave fed by its own direct global->LDS copies.
 //
-// Between the few-tile shapes of gemm_mfma_split.hpp and the whole-device
-// shapes of gemm_mfma_dma.hpp (at least one 256x256 tile per CU) lie shapes
-// such as 2048^3 or a (1024, 6144, 4096) row shard: 64 tiles of 256x256, 256
-// of 128x128. Here each wave of a workgroup computes the WHOLE 128x128 tile
-// (16 MFMA blocks, 256 accumulators in AGPRs, as a wave of the direct-copy
-// kernel) over its own quarter of the reduction chunks, so a 128x128 tile
-// keeps a CU's four matrix cores as busy as a 256x256 tile does. Each wave
-// copies its own A (128 x BK) and B (BK x 128) chunks with
-// global_load_lds_dwordx4 into its own ring of S LDS stages and waits only on
-// its own copies (s_waitcnt vmcnt): the main loop has no barrier. At the end
-// the four partial tiles are added in wave order (0, 1, 2, 3) through LDS, each
-// wave summing and storing a quarter of the tile: deterministic, no
-// workspace, no atomics.
+// Between the few-tile shapes and the whole-device shapes of gemm_mfma_dma.hpp
+// (at least one 256x256 tile per CU) lie shapes such as 2048^3 or a
+// (1024, 6144, 4096) row shard: 64 tiles of 256x256, 256 of 128x128. Here each
+// wave of a workgroup computes the WHOLE tile (BM = 128: 16 MFMA blocks, 256
+// accumulators in AGPRs, as a wave of the direct-copy kernel) over its own
+// quarter of the reduction chunks, so a 128x128 tile keeps a CU's four matrix
+// cores as busy as a 256x256 tile does; smaller tiles serve shapes with fewer
+// outputs still. Each wave copies its own A (BM x BK) and B (BK x BM) chunks
+// with global_load_lds (16 bytes per lane for 16-byte aligned rows, 4 bytes
+// otherwise) into its own ring of S LDS stages and waits only on its own
+// copies (s_waitcnt vmcnt): the main loop has no barrier. At the end the four
+// partial tiles are added in wave order (0, 1, 2, 3) through LDS, each wave
+// summing and storing its share of the tile: deterministic, no workspace, no
+// atomics.
 //
 // This keeps the output-parallel decomposition of the LeetGPU write-up
 // (section "V0", "Approach": outputs independent, each owned with its whole
@@ -30,35 +31,46 @@
 //
 // LDS: stage s of every wave is a separate LDS object per operand (so that the
 // compiler can tell a stage's reads from the copies into another), each holding
-// the four waves' 4 KiB pieces. A rows are 8 floats (two quads) stored in the
-// order q ^ swz(r), swz(r) = bit 2 ^ bit 3 of r: the 128-bit operand reads of 8
+// the four waves' pieces. A rows are 8 floats (two quads) stored in the order
+// q ^ swz(r), swz(r) = bit 2 ^ bit 3 of r: the 128-bit operand reads of 8
 // consecutive rows from a multiple of 8 (32 banks), and of 16 from a multiple
-// of 16 (64 banks), hit distinct 16-byte bank groups. B is row-major, 128
-// floats per row, two rows per copy instruction.
+// of 16 (64 banks), hit distinct 16-byte bank groups. B is row-major, BM
+// floats per row. A copy fills 64 (4-byte copies) or 256 consecutive floats of
+// a wave's piece; a lane's source address is free, so the layout is the same
+// for both copy widths.
 #pragma once
 
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_dma.hpp"
+#include "gemm_mfma_split.hpp"
 
 namespace fgr {
 
-template <int S_>
+template <int BM_, int S_, bool VEC_>
 struct KsplitConfig {
-  static constexpr int BM = 128, BN = 128, BK = 8, S = S_;
+  static constexpr int BM = BM_, BN = BM_, BK = 8, S = S_;
+  static constexpr bool VEC = VEC_;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRB = BM / 32, kCB = BN / 32;
-  static constexpr int kACopies = BM * BK / 256;  // per wave per chunk (256 floats per copy)
-  static constexpr int kBCopies = BK * BN / 256;
+  static constexpr int kCopyFloats = VEC ? 4 : 1;  // floats per lane per copy
+  static constexpr int kBlock = 64 * kCopyFloats;  // floats one copy fills
+  static constexpr int kPiece = BM * BK;           // floats of one wave's A (or B) stage
+  static constexpr int kACopies = kPiece / kBlock;  // per wave per chunk
+  static constexpr int kBCopies = kPiece / kBlock;
   static constexpr int kCopies = kACopies + kBCopies;
-  static constexpr int kPiece = BM * BK;          // floats of one wave's A (or B) stage
   static constexpr int kStage = kWaves * kPiece;  // floats of one LDS stage object
+  // the reduction: a slice is one MFMA block's 16 accumulators of every lane
+  static constexpr int kSlices = kRB * kCB;
+  static constexpr int kSlicesPerObj = kStage / 1024;
+  static constexpr int kSlicesPerWave = kSlices >= kWaves ? kSlices / kWaves : 1;
 
-  static_assert(BM * BK == BK * BN, "A and B pieces have one size");
-  static_assert(kRB == 4 && kCB == 4, "a wave owns the whole tile in 16 MFMA blocks");
+  static_assert(BM == 32 || BM == 64 || BM == 128, "tile of 32, 64 or 128");
+  static_assert(kPiece % kBlock == 0 && BN % kCopyFloats == 0, "copies cover whole pieces");
   static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");
+  static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
   static_assert(2 * S * kStage * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
-  static_assert(kRB * kCB * 16 * 64 <= 4 * kStage, "a partial tile fits in four stage objects");
+  static_assert(kSlices <= S * kSlicesPerObj, "a partial tile fits in the stage objects of one operand");
 };
 
 __device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
@@ -69,11 +81,25 @@ __device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) 
 // of its own before those reads. The kernel counts the copies in flight and
 // waits for them itself (s_waitcnt vmcnt), the only way its reads are ordered
 // after the copies they need.
-__device__ __forceinline__ void copy16_to_lds_counted(const float* g, float* lds) {
+template <int BYTES>  // 16 or 4
+__device__ __forceinline__ void copy_to_lds_counted(const float* g, float* lds) {
   uint32_t a = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)lds);
   asm volatile("" : "+s"(a));
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 16, 0, 0);
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 4, 0, 0);
+}
+
+// Scheduling hints for NO memory instructions among MFMAS MFMAs, when there
+// are MFMAs enough to interleave them one by one (else the default order).
+template <int MASK, int MFMAS, int NO>
+__device__ __forceinline__ void sched_spread() {
+  if constexpr (NO > 0 && MFMAS >= NO) {
+    sched_pairs<MASK, MFMAS / NO, NO>();
+    if constexpr (MFMAS % NO) __builtin_amdgcn_sched_group_barrier(kSchedMfma, MFMAS % NO, 0);
+  }
 }
 
 template <class T>
@@ -124,38 +150,45 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int c_end = nchunks * (wave + 1) / T::kWaves;
   const int c_last = c_end - 1;
 
-  // A copy j: rows [32j, 32j + 32); lane L -> row 32j + L/2 at stored position
-  // L % 2, which holds quad (L % 2) ^ swz(row). Rows past M read row M - 1.
+  // Copy j of a wave fills floats [j * kBlock, (j + 1) * kBlock) of its piece;
+  // lane L the kCopyFloats floats at position p = j * kBlock + L * kCopyFloats.
+  // In A, p is row p / 8, stored slot (p % 8) / 4, element p % 4, and the slot
+  // holds quad slot ^ swz(row): the lane copies that quad's element (the whole
+  // quad with 16-byte copies). Rows past M read row M - 1 (not stored).
   const float* a_src[T::kACopies];
-  int a_dst[T::kACopies], a_quad[T::kACopies];
+  int a_dst[T::kACopies], a_col[T::kACopies];
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
-    const int r = 32 * j + lane / 2;
-    const int q = (lane % 2) ^ a_swizzle2(r);
+    const int pos = j * T::kBlock + lane * T::kCopyFloats;
+    const int r = pos / BK;
+    const int c = 4 * (((pos % BK) / 4) ^ a_swizzle2(r)) + pos % 4;
     const int row = m0 + r < M ? m0 + r : M - 1;
-    a_src[j] = A + (int64_t)row * N + 4 * q;
-    a_dst[j] = piece + 256 * j;
-    a_quad[j] = q;
+    a_src[j] = A + (int64_t)row * N + c;
+    a_dst[j] = piece + j * T::kBlock;
+    a_col[j] = c;
   }
-  // B copy j: chunk rows 2j, 2j + 1; lane L -> row 2j + L/32, columns
-  // 4 (L % 32) .. + 3 (past K: the last quad instead, not stored).
+  // In B, p is row p / BN, column p % BN (columns past K read the last column,
+  // or the last quad with 16-byte copies; not stored).
   const float* b_src[T::kBCopies];
-  int b_dst[T::kBCopies];
-  const int b_cq = 4 * (lane % 32);
-  const int b_col = k0 + b_cq < K ? k0 + b_cq : K - 4;
+  int b_dst[T::kBCopies], b_row[T::kBCopies];
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
-    const int r = 2 * j + lane / 32;
-    b_src[j] = B + (int64_t)r * K + b_col;
-    b_dst[j] = piece + 256 * j;
+    const int pos = j * T::kBlock + lane * T::kCopyFloats;
+    const int r = pos / BN;
+    const int c = k0 + pos % BN;
+    b_src[j] = B + (int64_t)r * K + (c < K ? c : K - T::kCopyFloats);
+    b_dst[j] = piece + j * T::kBlock;
+    b_row[j] = r;
   }
 
   auto copy_chunk = [&](int c, float* As, float* Bs) __attribute__((always_inline)) {
     const int n0 = n_first + BK * c;
 #pragma unroll
-    for (int j = 0; j < T::kACopies; ++j) copy16_to_lds_counted(a_src[j] + n0, As + a_dst[j]);
+    for (int j = 0; j < T::kACopies; ++j)
+      copy_to_lds_counted<4 * T::kCopyFloats>(a_src[j] + n0, As + a_dst[j]);
 #pragma unroll
-    for (int j = 0; j < T::kBCopies; ++j) copy16_to_lds_counted(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+    for (int j = 0; j < T::kBCopies; ++j)
+      copy_to_lds_counted<4 * T::kCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
   };
 
   struct Frag {
@@ -167,20 +200,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // then waits for every copy in flight before the read. A: quad lg of row li
   // (+ 32 i), stored at position lg ^ swz(li) (the same swizzle for every i).
   const int a_frag = piece + li * BK + 4 * (lg ^ a_swizzle2(li));
-  // lane column li of MFMA column block j is output column 4 li + j (see the
-  // direct-copy kernel): one 128-bit read gives a lane's B operands of all blocks
-  const int b_frag = piece + 4 * lg * BN + 4 * li;
+  // lane column li of MFMA column block j is output column kCB li + j (see the
+  // direct-copy kernel): one read gives a lane's B operands of all blocks
+  const int b_frag = piece + 4 * lg * BN + T::kCB * li;
+  typedef typename FloatVec<T::kCB>::type BVec;
   auto read_frag = [&](Frag& f, const float* As, const float* Bs) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::kRB; ++i)
       f.a[i] = *reinterpret_cast<const float4*>(As + a_frag + 32 * BK * i);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float4 v = *reinterpret_cast<const float4*>(Bs + b_frag + t * BN);
-      f.b[0][t] = v.x;
-      f.b[1][t] = v.y;
-      f.b[2][t] = v.z;
-      f.b[3][t] = v.w;
+      const BVec v = *reinterpret_cast<const BVec*>(Bs + b_frag + t * BN);
+#pragma unroll
+      for (int j = 0; j < T::kCB; ++j) f.b[j][t] = vec_get(v, j);
     }
   };
 
@@ -212,29 +244,34 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     constexpr int X = OFF & 1;  // operand buffer of the chunk in stage OFF
     using S0 = std::integral_constant<int, OFF>;
     const int n0 = n_first + BK * c_begin;
-    float4 va[T::kACopies], vb[T::kBCopies];
+    typedef typename std::conditional<T::VEC, float4, float>::type CopyT;
+    CopyT va[T::kACopies], vb[T::kBCopies];
     bool oka[T::kACopies], okb[T::kBCopies];
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j) {
-      oka[j] = n0 + 4 * a_quad[j] >= 0;
-      va[j] = *reinterpret_cast<const float4*>(oka[j] ? a_src[j] + n0 : A);
+      oka[j] = n0 + a_col[j] >= 0;
+      va[j] = *reinterpret_cast<const CopyT*>(oka[j] ? a_src[j] + n0 : A);
     }
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j) {
-      okb[j] = n0 + 2 * j + lane / 32 >= 0;
-      vb[j] = *reinterpret_cast<const float4*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
+      okb[j] = n0 + b_row[j] >= 0;
+      vb[j] = *reinterpret_cast<const CopyT*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
     }
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       using Sj = std::integral_constant<int, (OFF + j) % S>;
       copy_chunk(min(c_begin + j, c_last), a_stage(Sj{}), b_stage(Sj{}));
     });
+    auto zero_out = [](CopyT v, bool ok) __attribute__((always_inline)) -> CopyT {
+      if constexpr (T::VEC) return mask_quad(v, ok ? 0xfu : 0u);
+      else return ok ? v : 0.f;
+    };
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
-      *reinterpret_cast<float4*>(a_stage(S0{}) + a_dst[j] + 4 * lane) = mask_quad(va[j], oka[j] ? 0xfu : 0u);
+      *reinterpret_cast<CopyT*>(a_stage(S0{}) + a_dst[j] + T::kCopyFloats * lane) = zero_out(va[j], oka[j]);
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j)
-      *reinterpret_cast<float4*>(b_stage(S0{}) + b_dst[j] + 4 * lane) = mask_quad(vb[j], okb[j] ? 0xfu : 0u);
+      *reinterpret_cast<CopyT*>(b_stage(S0{}) + b_dst[j] + T::kCopyFloats * lane) = zero_out(vb[j], okb[j]);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
     __builtin_amdgcn_sched_barrier(0);
     read_frag(f[X], a_stage(S0{}), b_stage(S0{}));
@@ -248,17 +285,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     constexpr int s = decltype(sc)::value, X = decltype(xc)::value;
     using Sn = std::integral_constant<int, (s + 1) % S>;
     using Sp = std::integral_constant<int, (s + S - 1) % S>;
-    // t = 0: the copies among its 16 MFMAs
+    // t = 0: the copies among its MFMAs
     copy_chunk(min(c + S - 1, c_last), a_stage(Sp{}), b_stage(Sp{}));
     mma(f[X], 0, 1);
-    sched_pairs<kSchedVmemRead, kMfmasT / T::kCopies, T::kCopies>();
+    sched_spread<kSchedVmemRead, kMfmasT, T::kCopies>();
     __builtin_amdgcn_sched_barrier(0);
-    // chunk c + 1 has landed in LDS: its operand reads among the 48 MFMAs of t = 1..3
+    // chunk c + 1 has landed in LDS: its operand reads among the MFMAs of t = 1..3
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(T::kCopies * (S - 2)));
     __builtin_amdgcn_sched_barrier(0);
     read_frag(f[X ^ 1], a_stage(Sn{}), b_stage(Sn{}));
     mma(f[X], 1, 4);
-    sched_interleave<3 * kMfmasT, 0, 0, kReads>();
+    sched_spread<kSchedDsRead, 3 * kMfmasT, kReads>();
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -287,38 +324,42 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
 
   // The four partial tiles are added in wave order, ((p0 + p1) + p2) + p3,
   // through LDS (the staging is free once every wave is past the first
-  // barrier), two partials at a time: wave w sums and stores block row w of the
-  // tile (MFMA blocks i = w, j = 0..3). Register group g of a partial (blocks
-  // i = g) lives in stage object g of A (waves 0 and 2) or of B (waves 1 and
-  // 3), lane-major as float4: consecutive lanes write consecutive 16 bytes.
+  // barrier), two partials at a time, in the stage objects of A (waves 0, 2)
+  // or of B (waves 1, 3). Slice t of a partial (MFMA block i = t / kCB,
+  // j = t % kCB: 16 accumulators of every lane) lives in object
+  // t / kSlicesPerObj, lane-major as float4. Wave w sums and stores slices
+  // [w kSlicesPerWave, (w + 1) kSlicesPerWave) (at BM = 128: block row w).
+  constexpr int kSPW = T::kSlicesPerWave;
+  auto slice_ptr = [&](auto tc, bool use_b) __attribute__((always_inline)) -> float* {
+    constexpr int t = decltype(tc)::value;
+    using O = std::integral_constant<int, t / T::kSlicesPerObj>;
+    return (use_b ? b_stage(O{}) : a_stage(O{})) + (t % T::kSlicesPerObj) * 1024 + 4 * lane;
+  };
   auto put = [&](bool use_b) __attribute__((always_inline)) {
-    static_for<0, T::kRB>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      float* p = use_b ? b_stage(gc) : a_stage(gc);
+    static_for<0, T::kSlices>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      float* p = slice_ptr(tc, use_b);
 #pragma unroll
-      for (int j = 0; j < T::kCB; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(p + ((j * 4 + q) * 64 + lane) * 4) =
-              make_float4(acc[g][j][4 * q], acc[g][j][4 * q + 1], acc[g][j][4 * q + 2], acc[g][j][4 * q + 3]);
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(p + 256 * q) =
+            make_float4(acc[t / T::kCB][t % T::kCB][4 * q], acc[t / T::kCB][t % T::kCB][4 * q + 1],
+                        acc[t / T::kCB][t % T::kCB][4 * q + 2], acc[t / T::kCB][t % T::kCB][4 * q + 3]);
     });
   };
-  float sum[T::kCB][16];
-  // sum (+)= group `wave` of the partial in the A (use_b false) or B objects
+  float sum[kSPW][16];
+  // sum (+)= this wave's slices of the partial in the A (use_b false) or B objects
   auto take = [&](bool use_b, bool first) __attribute__((always_inline)) {
-    static_for<0, T::kRB>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      if (wave != g) return;
-      const float* p = use_b ? b_stage(gc) : a_stage(gc);
+    static_for<0, T::kSlices>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      if (wave != t / kSPW) return;
+      const float* p = slice_ptr(tc, use_b);
 #pragma unroll
-      for (int j = 0; j < T::kCB; ++j)
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(p + 256 * q);
+        const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = *reinterpret_cast<const float4*>(p + ((j * 4 + q) * 64 + lane) * 4);
-          const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) sum[j][4 * q + k] = first ? e[k] : sum[j][4 * q + k] + e[k];
-        }
+        for (int k = 0; k < 4; ++k) sum[t % kSPW][4 * q + k] = first ? e[k] : sum[t % kSPW][4 * q + k] + e[k];
+      }
     });
   };
   __syncthreads();
@@ -334,16 +375,31 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   take(false, false);
   take(true, false);
 
-  // Block row `wave` of the tile, 4 adjacent columns per lane and row.
+  if (wave * kSPW >= T::kSlices) return;  // small tiles: fewer slices than waves
   float* const Ct = C + (int64_t)m0 * K + k0;
-  const int col = 4 * li;
-  const bool col_ok = k0 + col < K;
+  if constexpr (T::VEC && kSPW == T::kCB && T::kCB == 4) {
+    // a whole block row: 4 adjacent columns per lane and row
+    const int col = 4 * li;
+    const bool col_ok = k0 + col < K;
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int row = wave * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
-    if (col_ok && m0 + row < M) {
-      float* dst = Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col;
-      *reinterpret_cast<float4*>(dst) = make_float4(sum[0][rr], sum[1][rr], sum[2][rr], sum[3][rr]);
+    for (int rr = 0; rr < 16; ++rr) {
+      const int row = wave * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
+      if (col_ok && m0 + row < M) {
+        float* dst = Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col;
+        *reinterpret_cast<float4*>(dst) = make_float4(sum[0][rr], sum[1][rr], sum[2][rr], sum[3][rr]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kSPW; ++u) {
+      const int t = wave * kSPW + u;
+      const int i = t / T::kCB, j = t % T::kCB;
+      const int col = T::kCB * li + j;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
+        if (k0 + col < K && m0 + row < M) Ct[(uint32_t)row * (uint32_t)K + (uint32_t)col] = sum[u][rr];
+      }
     }
   }
 }

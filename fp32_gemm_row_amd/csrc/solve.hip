@@ -78,11 +78,8 @@ bool gemv_vec_ok(const float* B, int K) { return K % 4 == 0 && aligned(B, 16); }
 // Direct global->LDS copies need at least four 16-deep reduction chunks (the
 // copies that run past the last chunk re-read it, and must never reach the
 // zero-padded first chunk); they are 16 bytes wide for 16-byte aligned rows,
-// 4 bytes otherwise. The k-split kernel copies 16 bytes only.
+// 4 bytes otherwise (the k-split kernel's 128x128 tiles take 16-byte copies only).
 bool mfma_dma_ok(int N) { return N >= 64; }
-bool mfma_ksplit_ok(const float* A, const float* B, const float* C, int N, int K) {
-  return mfma_vec_ok(A, B, C, N, K) && N >= 64;
-}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -118,18 +115,31 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
     return {FGR_PATH_MFMA_DMA, FGR_TILE_256};
   }
-  if (mfma_vec_ok(A, B, C, N, K)) {
-    if (t256 >= cus) return {FGR_PATH_MFMA_VEC, FGR_TILE_256};  // N < 64
-    if (t128 >= cus && mfma_ksplit_ok(A, B, C, N, K)) {
-      // 128x128 tiles with the reduction split over a workgroup's waves
+  const bool vec = mfma_vec_ok(A, B, C, N, K);
+  if (N >= 64) {
+    // Fewer 256x256 tiles than CUs: tiles whose reduction is split over the
+    // four waves of a workgroup (k-split), the largest that still gives every
+    // CU a tile; a last partial wave of up to half the CUs to the split kernel.
+    if (vec && t128 >= cus) {
       const int64_t rem = t128 % cus;
       if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
     }
+    if (t64 >= cus) {
+      const int64_t rem = t64 % cus;
+      if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_64};
+      return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_64};
+    }
+    // fewer 64x64 tiles than CUs: 32x32 k-split tiles (the split kernel's
+    // 32x32 tiles measured as fast or faster with 4-byte loads)
+    return {vec ? FGR_PATH_MFMA_KSPLIT : FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
+  }
+  // N < 64: no direct copies
+  if (vec) {
+    if (t256 >= cus) return {FGR_PATH_MFMA_VEC, FGR_TILE_256};
     if (t64 < cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
     if (t64 < 2 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_64};
     if (t64 < 4 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
-    if (N >= 1024) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_64};
     return {FGR_PATH_MFMA_VEC, FGR_TILE_64};
   }
   if (t128 >= 4 * cus) return {FGR_PATH_MFMA_SCALAR, FGR_TILE_128};
@@ -138,13 +148,16 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
 }
 
 // Tile for a forced path when the caller left it open.
-int default_tile(int path, const Choice& auto_choice, int M, int K, int cus) {
+int default_tile(int path, const Choice& auto_choice, int M, int K, int cus, bool vec_rows) {
   if (path == auto_choice.path) return auto_choice.tile;
   switch (path) {
     case FGR_PATH_MFMA_DMA:
     case FGR_PATH_MFMA_DMA_TAIL: return FGR_TILE_256;
     case FGR_PATH_MFMA_KSPLIT:
-    case FGR_PATH_MFMA_KSPLIT_TAIL: return FGR_TILE_128;
+    case FGR_PATH_MFMA_KSPLIT_TAIL:
+      if (vec_rows && cdiv(M, 128) * cdiv(K, 128) >= cus) return FGR_TILE_128;
+      if (path == FGR_PATH_MFMA_KSPLIT_TAIL || cdiv(M, 64) * cdiv(K, 64) >= cus) return FGR_TILE_64;
+      return FGR_TILE_32;
     case FGR_PATH_MFMA_SPLIT: return cdiv(M, 64) * cdiv(K, 64) < cus ? FGR_TILE_32 : FGR_TILE_64;
     case FGR_PATH_MFMA_VEC:
     case FGR_PATH_MFMA_SCALAR:
@@ -264,31 +277,62 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
   return launch_split_tail<256, false>(A, B, C, M, N, K, full, rem, cus, s);
 }
 
-using TileKsplit = fgr::KsplitConfig<4>;  // 128x128, each of 4 waves a quarter of the reduction
+// k-split tiles: 128x128 (16-byte copies only: 4-byte ones would leave more
+// copies in flight than the wave's vmcnt counter holds), 64x64 and 32x32
+using Ksplit128 = fgr::KsplitConfig<128, 4, true>;
+using Ksplit64 = fgr::KsplitConfig<64, 4, true>;
+using Ksplit64s = fgr::KsplitConfig<64, 4, false>;
+using Ksplit32 = fgr::KsplitConfig<32, 4, true>;
+using Ksplit32s = fgr::KsplitConfig<32, 4, false>;
 
-// The k-split kernel over the first `count` 128x128 tiles of the grouped
-// order (count < 0: all of them).
-int launch_ksplit(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s) {
-  int tiles_m = (int)cdiv(M, TileKsplit::BM);
-  int tiles_n = (int)cdiv(K, TileKsplit::BN);
+template <class Cfg>
+int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s) {
+  int tiles_m = (int)cdiv(M, Cfg::BM);
+  int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
-  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<TileKsplit>),
-                count < 0 ? (int64_t)tiles_m * tiles_n : count, TileKsplit::kThreads, args, s);
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
+                count < 0 ? (int64_t)tiles_m * tiles_n : count, Cfg::kThreads, args, s);
 }
 
-// Whole waves of 128x128 tiles on the k-split kernel, the last partial wave's
-// tiles cut into 64x64 (or 32x32) split-reduction tiles (as launch_dma_tail).
-int launch_ksplit_tail(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
-  const int64_t tiles = cdiv(M, TileKsplit::BM) * cdiv(K, TileKsplit::BN);
+// The k-split kernel with tile x tile tiles over the first `count` tiles of
+// the grouped order (count < 0: all of them); 16-byte copies when the rows
+// allow them.
+int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
+                  hipStream_t s) {
+  const bool vec = mfma_vec_ok(A, B, C, N, K);
+  switch (tile) {
+    case FGR_TILE_128:
+      return vec ? launch_ksplit_cfg<Ksplit128>(A, B, C, M, N, K, count, s) : FGR_ERR_BAD_PATH;
+    case FGR_TILE_64:
+      return vec ? launch_ksplit_cfg<Ksplit64>(A, B, C, M, N, K, count, s)
+                 : launch_ksplit_cfg<Ksplit64s>(A, B, C, M, N, K, count, s);
+    case FGR_TILE_32:
+      return vec ? launch_ksplit_cfg<Ksplit32>(A, B, C, M, N, K, count, s)
+                 : launch_ksplit_cfg<Ksplit32s>(A, B, C, M, N, K, count, s);
+    default: return FGR_ERR_BAD_PATH;
+  }
+}
+
+// Whole waves of tile x tile tiles on the k-split kernel, the last partial
+// wave's tiles cut into smaller split-reduction tiles (as launch_dma_tail).
+int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
+                       hipStream_t s) {
+  const int64_t tiles = cdiv(M, tile) * cdiv(K, tile);
   const int64_t full = tiles / cus * cus;
   const int64_t rem = tiles - full;
   if (full > 0) {
-    const int rc = launch_ksplit(A, B, C, M, N, K, full, s);
+    const int rc = launch_ksplit(tile, A, B, C, M, N, K, full, s);
     if (rc != FGR_OK || rem == 0) return rc;
   }
   if (full > INT_MAX || rem > INT_MAX / 16) return FGR_ERR_BAD_DIMS;
-  return launch_split_tail<128, true>(A, B, C, M, N, K, full, rem, cus, s);
+  const bool vec = mfma_vec_ok(A, B, C, N, K);
+  if (tile == FGR_TILE_128)
+    return vec ? launch_split_tail<128, true>(A, B, C, M, N, K, full, rem, cus, s) : FGR_ERR_BAD_PATH;
+  if (tile == FGR_TILE_64)
+    return vec ? launch_split_tail<64, true>(A, B, C, M, N, K, full, rem, cus, s)
+               : launch_split_tail<64, false>(A, B, C, M, N, K, full, rem, cus, s);
+  return FGR_ERR_BAD_PATH;
 }
 
 template <bool VEC>
@@ -332,7 +376,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
-      if (!mfma_ksplit_ok(A, B, C, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_128))
+      // N >= 64; tiles of 128 (16-byte rows only) or 64, and 32 without the tail form
+      if (N < 64 || (tile == FGR_TILE_128 && !mfma_vec_ok(A, B, C, N, K)) || tile == FGR_TILE_256 ||
+          (tile == FGR_TILE_32 && path == FGR_PATH_MFMA_KSPLIT_TAIL))
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SCALAR: break;
@@ -350,7 +396,8 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   if (tile != FGR_TILE_AUTO && tile != FGR_TILE_256 && tile != FGR_TILE_128 && tile != FGR_TILE_64 &&
       tile != FGR_TILE_32)
     return FGR_ERR_BAD_PATH;
-  if (tile == FGR_TILE_32 && path != FGR_PATH_MFMA_SPLIT && path != FGR_PATH_AUTO) return FGR_ERR_BAD_PATH;
+  if (tile == FGR_TILE_32 && path != FGR_PATH_MFMA_SPLIT && path != FGR_PATH_MFMA_KSPLIT && path != FGR_PATH_AUTO)
+    return FGR_ERR_BAD_PATH;
 
   int cus = 0;
   rc = current_device(&cus);
@@ -372,13 +419,13 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       path = mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
     }
   }
-  if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, K, cus);
+  if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, K, cus, mfma_vec_ok(A, B, C, N, K));
 
   switch (path) {
     case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, -1, s);
     case FGR_PATH_MFMA_DMA_TAIL: return launch_dma_tail(A, B, C, M, N, K, cus, s);
-    case FGR_PATH_MFMA_KSPLIT: return launch_ksplit(A, B, C, M, N, K, -1, s);
-    case FGR_PATH_MFMA_KSPLIT_TAIL: return launch_ksplit_tail(A, B, C, M, N, K, cus, s);
+    case FGR_PATH_MFMA_KSPLIT: return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
+    case FGR_PATH_MFMA_KSPLIT_TAIL: return launch_ksplit_tail(tile, A, B, C, M, N, K, cus, s);
     case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SPLIT:

@@ -94,18 +94,20 @@ extern "C" {
                                     split kernel on the tiles of the last, partial wave, cut into
                                     64x64 or 32x32 tiles; same conditions as MFMA_DMA. Two
                                     launches on `stream`. */
-#define FGR_PATH_MFMA_KSPLIT 8 /* FP32 MFMA, 128x128 tiles, each of a workgroup's four waves reducing a
-                                  quarter of N into the whole tile from its own direct global->LDS
-                                  copies; same conditions as MFMA_DMA (tile 128 only) */
-#define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT on the whole waves of 128x128 tiles, the split kernel
-                                       on the tiles of the last, partial wave; two launches */
+#define FGR_PATH_MFMA_KSPLIT 8 /* FP32 MFMA, 128x128, 64x64 or 32x32 tiles, each of a workgroup's four
+                                  waves reducing a quarter of N into the whole tile from its own
+                                  direct global->LDS copies (4-byte copies for rows that are not
+                                  16-byte aligned; tile 128 needs 16-byte rows); N >= 64 */
+#define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT (tile 128 or 64) on the whole waves of tiles, the
+                                       split kernel on the tiles of the last, partial wave; two
+                                       launches */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0
 #define FGR_TILE_256 256
 #define FGR_TILE_128 128
 #define FGR_TILE_64 64
-#define FGR_TILE_32 32 /* split path only */
+#define FGR_TILE_32 32 /* split and k-split paths only */
 
 /*
  * solve - C = A x B on `stream`.

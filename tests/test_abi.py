@@ -115,12 +115,17 @@ def test_forced_path_rejections(lib):
         assert call(lib, A0, B0, C0, 512, 130, 512, path) == fgr.ERR_DEVICE
         assert call(lib, A0, B0, C0, 512, 128, 502, path) == fgr.ERR_DEVICE
         assert call(lib, A0 + 4, B0, C0, 512, 128, 512, path) == fgr.ERR_DEVICE
-    # the k-split paths need 128-bit rows, N >= 64 and tile 128
+    # the k-split paths need N >= 64; tile 128 needs 128-bit rows, and the
+    # tail form has no 32x32 tiles
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT_TAIL) == fgr.ERR_BAD_PATH
-    assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 256) == fgr.ERR_BAD_PATH
-    # 32x32 tiles exist on the split path only
+    assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 32) == fgr.ERR_BAD_PATH
+    for tile in (0, 64, 32):
+        assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT, tile) == fgr.ERR_DEVICE
+        assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, tile) == fgr.ERR_DEVICE
+    # 32x32 tiles exist on the split and k-split paths only
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_VEC, 32) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_SPLIT, 128) == fgr.ERR_BAD_PATH
     # unknown path or tile values
@@ -161,7 +166,7 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 2, 8192, 8192) == fgr.PATH_GEMV_VEC  # skinny: B streamed once
     assert sp(A0, B0, C0, 8, 8192, 8192) == fgr.PATH_GEMV_VEC
     assert sp(A0, B0, C0, 8, 8192, 8190) == fgr.PATH_GEMV_SCALAR
-    assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_KSPLIT  # 32x32 k-split tiles
     assert sp(0, B0, C0, 1, 8, 8) == fgr.ERR_NULL_POINTER
 
 
@@ -170,11 +175,11 @@ def test_tile_selection():
     assert st(A0, B0, C0, 8192, 6144, 4096) == 256  # 512 tiles of 256x256
     assert st(A0, B0, C0, 4096, 4096, 4096) == 256  # 256 tiles
     assert st(A0, B0, C0, 4096, 4096, 4160) == 256  # whole waves of 256x256, then the tail
-    assert st(A0, B0, C0, 1023, 1025, 1027) == 32  # split, 32x32
-    assert st(A0, B0, C0, 256, 256, 256) == 32
-    assert st(A0, B0, C0, 1024, 1024, 1024) == 64  # split, 64x64
     assert st(A0, B0, C0, 2048, 512, 2048) == 128  # k-split, 128x128
-    assert st(A0, B0, C0, 2048, 512, 1024) == 32  # 128 tiles of 128: split, 32x32
+    assert st(A0, B0, C0, 1024, 1024, 1024) == 64  # k-split, 64x64 (256 of them)
+    assert st(A0, B0, C0, 1023, 1025, 1027) == 64  # k-split 64x64, 4-byte copies, then the tail
+    assert st(A0, B0, C0, 256, 256, 256) == 32  # k-split, 32x32
+    assert st(A0, B0, C0, 2048, 512, 1024) == 64  # 128 tiles of 128, 512 of 64
     assert st(A0, B0, C0, 2048, 60, 2048) == 64  # no direct copies (N < 64): register-staged 64x64
     assert st(A0, B0, C0, 4095, 4097, 4099) == 256  # 4-byte direct copies, 256 tiles
     assert st(A0, B0, C0, 4095, 60, 4099) == 128  # N < 64: 32-bit loads, many tiles
@@ -184,13 +189,19 @@ def test_tile_selection():
 
 def test_split_path_choices():
     sp = fgr.select_path
-    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_SPLIT
-    assert sp(A0, B0, C0, 256, 256, 256) == fgr.PATH_MFMA_SPLIT
-    assert sp(A0, B0, C0, 1024, 8192, 1024) == fgr.PATH_MFMA_SPLIT
-    assert sp(A0, B0, C0, 1536, 4096, 1536) == fgr.PATH_MFMA_SPLIT  # 144 tiles of 128
-    assert sp(A0, B0, C0, 2048, 512, 1024) == fgr.PATH_MFMA_SPLIT
+    # fewer 256x256 tiles than CUs, N >= 64: k-split tiles, the largest that
+    # still give every CU one (then the tail rule), else 32x32
+    assert sp(A0, B0, C0, 1024, 1024, 1024) == fgr.PATH_MFMA_KSPLIT  # 256 tiles of 64
+    assert sp(A0, B0, C0, 1024, 8192, 1024) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 1536, 4096, 1536) == fgr.PATH_MFMA_KSPLIT_TAIL  # 576 of 64: 64 left over
+    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 64, 4-byte copies
+    assert sp(A0, B0, C0, 2047, 2049, 2051) == fgr.PATH_MFMA_KSPLIT_TAIL  # 1056 of 64
+    assert sp(A0, B0, C0, 256, 256, 256) == fgr.PATH_MFMA_KSPLIT  # 32x32
+    assert sp(A0, B0, C0, 300, 500, 261) == fgr.PATH_MFMA_SPLIT  # unaligned, few tiles: split 32
+    # N < 64: the register-staged and split kernels
     assert sp(A0, B0, C0, 2048, 60, 2048) == fgr.PATH_MFMA_VEC
-    assert sp(A0, B0, C0, 2047, 2049, 2051) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0, B0, C0, 1024, 60, 1024) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 2047, 61, 2051) == fgr.PATH_MFMA_SCALAR
 
 
 def test_python_wrapper_rejects_cpu_tensors():

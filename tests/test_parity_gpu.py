@@ -94,8 +94,13 @@ def paths_for(M, N, K):
         # below one wave of 256x256 tiles every tile is in the tail: the split
         # kernel's big-tile mode alone, partial big tiles included
         out.append((fgr.PATH_MFMA_DMA_TAIL, fgr.TILE_256))
+    if N >= 64:
+        # tiles whose reduction is split over the waves (4-byte copies for
+        # unaligned rows; 128x128 tiles need 16-byte rows); and the tail form
+        for tile in (fgr.TILE_64, fgr.TILE_32):
+            out.append((fgr.PATH_MFMA_KSPLIT, tile))
+        out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_64))
     if N % 4 == 0 and K % 4 == 0 and N >= 64:
-        # 128x128 tiles with the reduction split over the waves; and its tail form
         out.append((fgr.PATH_MFMA_KSPLIT, fgr.TILE_128))
         out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
@@ -250,22 +255,27 @@ def test_large_ragged_sampled(shape):
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{shape} sampled")
 
 
-@pytest.mark.parametrize("shape,path", [
-    ((2048, 64, 2048), fgr.PATH_MFMA_KSPLIT), ((2040, 1000, 2044), fgr.PATH_MFMA_KSPLIT),
-    ((2176, 72, 2048), fgr.PATH_MFMA_KSPLIT_TAIL), ((3072, 68, 3076), fgr.PATH_MFMA_KSPLIT_TAIL),
-], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else fgr.PATH_NAMES[v])
-def test_ksplit_exact(shape, path):
-    # 128x128 tiles, each wave of a workgroup reducing a quarter of N; with a
-    # partial last wave of them, the rest cut into split-kernel tiles: exact on
-    # integer data whichever kernel computed an output
+@pytest.mark.parametrize("shape,path,tile", [
+    ((2048, 64, 2048), fgr.PATH_MFMA_KSPLIT, 128), ((2040, 1000, 2044), fgr.PATH_MFMA_KSPLIT, 128),
+    ((2176, 72, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128), ((3072, 68, 3076), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
+    ((1024, 200, 1024), fgr.PATH_MFMA_KSPLIT, 64), ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
+    ((1536, 100, 1540), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((509, 300, 515), fgr.PATH_MFMA_SPLIT, 32),
+    ((512, 128, 512), fgr.PATH_MFMA_KSPLIT, 32),
+], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_ksplit_exact(shape, path, tile):
+    # tiles whose reduction is split over a workgroup's waves (128, 64 or 32
+    # square, 4-byte copies for unaligned rows); with a partial last wave of
+    # them, the rest cut into split-kernel tiles: exact on integer data
+    # whichever kernel computed an output
     M, N, K = shape
     A, B = synth.make_inputs(M, N, K, "integer", seed=6)
     say(f"k-split {shape}: oracle")
     Cref, _ = oracle.gemm(A, B)
     assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == path
+    assert fgr.select_tile(1 << 40, 2 << 40, 3 << 40, M, N, K) == tile
     say(f"k-split {shape}: GPU")
     assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
-    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT, fgr.TILE_128), Cref, f"{shape} k-split only")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT, tile), Cref, f"{shape} k-split only")
 
 
 @pytest.mark.parametrize("shape", [(4352, 64, 4096), (4100, 68, 4100), (2304, 100, 8192), (65792, 64, 256)],
