@@ -247,17 +247,22 @@ int launch_split_big(const float* A, const float* B, float* C, int M, int N, int
 using Split32 = fgr::SplitConfig<32, 32, 16, 4>;
 using Split64x4 = fgr::SplitConfig<64, 64, 16, 4>;
 using Split64x8 = fgr::SplitConfig<64, 64, 16, 8>;
+// 16 waves per 32x32 tile, each a sixteenth of the reduction: for tails of a
+// few tiles, where a wave's chain of dependent chunk loads sets the time
+using Split32x16 = fgr::SplitConfig<32, 32, 16, 16>;
 
 // The split kernel over the BIG x BIG tiles [full, full + rem): 64x64 pieces
 // (eight waves each while there are fewer than two per CU), or 32x32 pieces
-// while 64x64 ones would leave CUs idle.
+// while 64x64 ones would leave CUs idle (sixteen waves each while even those
+// leave CUs idle).
 template <int BIG, bool VEC>
 int launch_split_tail(const float* A, const float* B, float* C, int M, int N, int K, int64_t full, int64_t rem,
                       int cus, hipStream_t s) {
-  constexpr int64_t per64 = (BIG / 64) * (BIG / 64);
+  constexpr int64_t per64 = (BIG / 64) * (BIG / 64), per32 = (BIG / 32) * (BIG / 32);
   if (rem * per64 >= 2 * cus) return launch_split_big<Split64x4, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
   if (rem * per64 >= cus) return launch_split_big<Split64x8, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
-  return launch_split_big<Split32, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  if (rem * per32 >= cus) return launch_split_big<Split32, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
+  return launch_split_big<Split32x16, BIG, VEC>(A, B, C, M, N, K, (int)full, (int)rem, s);
 }
 
 // Whole waves of 256x256 tiles (one tile per CU) on the direct-copy kernel;
