@@ -40,7 +40,9 @@ PATH_MFMA_SPLIT = 6
 PATH_MFMA_DMA_TAIL = 7
 PATH_MFMA_KSPLIT = 8
 PATH_MFMA_KSPLIT_TAIL = 9
+PATH_MFMA_SPLITK = 10
 PATH_NAMES = {
+    PATH_MFMA_SPLITK: "mfma_splitk",
     PATH_MFMA_KSPLIT: "mfma_ksplit",
     PATH_MFMA_KSPLIT_TAIL: "mfma_ksplit_tail",
     PATH_MFMA_DMA_TAIL: "mfma_dma_tail",

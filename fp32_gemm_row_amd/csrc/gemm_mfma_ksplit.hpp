@@ -105,9 +105,8 @@ __device__ __forceinline__ void sched_spread() {
 template <class T>
 __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
-    int K, int tiles_m, int tiles_n, int group) {
+    int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W) {
   constexpr int S = T::S, BK = T::BK, BN = T::BN;
-  using I0 = std::integral_constant<int, 0>;
   __shared__ __attribute__((aligned(1024))) float As0[T::kStage];
   __shared__ __attribute__((aligned(1024))) float As1[T::kStage];
   __shared__ __attribute__((aligned(1024))) float As2[T::kStage];
@@ -143,12 +142,20 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int m0 = tm * T::BM;
   const int k0 = tn * BN;
 
-  // this wave's chunks [c_begin, c_end); N >= 64 gives every wave >= 2
+  // Split across workgroups (parts > 1): workgroup row blockIdx.y = part owns
+  // the chunks [nchunks part / parts, nchunks (part + 1) / parts) and writes
+  // its partial tile to W + part M K (row stride K) instead of C; a second
+  // kernel adds the parts in order. This wave's chunks are [c_begin, c_end)
+  // of the part's; at least 8 chunks per part give every wave >= 2.
   const int nchunks = (N + BK - 1) / BK;
   const int n_first = N - BK * nchunks;  // in (-BK, 0]
-  const int c_begin = nchunks * wave / T::kWaves;
-  const int c_end = nchunks * (wave + 1) / T::kWaves;
+  const int part = blockIdx.y;
+  const int pc0 = (int)((int64_t)nchunks * part / parts);
+  const int pn = (int)((int64_t)nchunks * (part + 1) / parts) - pc0;
+  const int c_begin = pc0 + pn * wave / T::kWaves;
+  const int c_end = pc0 + pn * (wave + 1) / T::kWaves;
   const int c_last = c_end - 1;
+  float* const Out = parts > 1 ? W + (int64_t)part * M * K : C;
 
   // Copy j of a wave fills floats [j * kBlock, (j + 1) * kBlock) of its piece;
   // lane L the kCopyFloats floats at position p = j * kBlock + L * kCopyFloats.
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   take(true, false);
 
   if (wave * kSPW >= T::kSlices) return;  // small tiles: fewer slices than waves
-  float* const Ct = C + (int64_t)m0 * K + k0;
+  float* const Ct = Out + (int64_t)m0 * K + k0;
   if constexpr (T::VEC && kSPW == T::kCB && T::kCB == 4) {
     // a whole block row: 4 adjacent columns per lane and row
     const int col = 4 * li;

@@ -17,9 +17,10 @@
 // past M are staged as zeros and their outputs are not
 // stored. The row groups' partial sums are first added across the lanes of
 // each wave (lanes that share columns differ by multiples of LPR), then across
-// waves in LDS, in wave order. No atomics and no workspace: the result is
-// deterministic, and for M == 1 the reduction order is that of MR == 1 for
-// every MR.
+// waves in LDS, in wave order. No atomics: the result is deterministic, and
+// for M == 1 the reduction order is that of MR == 1 for every MR. When K has
+// too few 32-column blocks to occupy the CUs, the rows of B are also split
+// into parts over a second grid dimension (below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,10 +56,15 @@ __device__ __forceinline__ void fma_row(float (&acc)[MR][VW], const float* a_s, 
   }
 }
 
+// Split across workgroups (parts > 1): workgroup row blockIdx.y = part owns
+// the reduction indices [N part / parts, N (part + 1) / parts) and writes its
+// partial rows to W + part M K instead of C; a second kernel adds the parts in
+// order (for K too small to give every CU its 32 columns).
 template <int VW, int NT, int UNROLL, int MR, int AF = kGemvAFloats>
 __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
                                                   const float* __restrict__ B,
-                                                  float* __restrict__ C, int M, int N, int K) {
+                                                  float* __restrict__ C, int M, int N, int K, int parts,
+                                                  float* __restrict__ W) {
   constexpr int LPR = kGemvCols / VW;     // lanes per row segment
   constexpr int RPI = NT / LPR;           // rows in flight per workgroup step
   constexpr int WAVES = NT / 64;
@@ -84,8 +90,11 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
 #pragma unroll
     for (int e = 0; e < VW; ++e) acc[m][e] = 0.f;
 
-  for (int nb = 0; nb < N; nb += CHUNK) {
-    const int len = (N - nb) < CHUNK ? (N - nb) : CHUNK;
+  const int n_lo = (int)((int64_t)N * blockIdx.y / parts);
+  const int n_hi = (int)((int64_t)N * (blockIdx.y + 1) / parts);
+  float* const Out = parts > 1 ? W + (int64_t)blockIdx.y * M * K : C;
+  for (int nb = n_lo; nb < n_hi; nb += CHUNK) {
+    const int len = (n_hi - nb) < CHUNK ? (n_hi - nb) : CHUNK;
     __syncthreads();  // the previous chunk of A has been read by every thread
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) s += part[w][m][cc];
-    if (m < M && c < K) C[(int64_t)m * K + c] = s;
+    if (m < M && c < K) Out[(int64_t)m * K + c] = s;
   }
 }
 

@@ -4,7 +4,9 @@
 // of gemm_mfma.hpp and gemv.hpp; this file only decides and enqueues.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -15,6 +17,7 @@
 #include "gemm_mfma_ksplit.hpp"
 #include "gemm_mfma_split.hpp"
 #include "gemv.hpp"
+#include "reduce_parts.hpp"
 
 namespace {
 
@@ -94,6 +97,83 @@ int64_t tail_tiles(int cus) { return (int64_t)cus * 11 / 16; }
 // left over, 131.1 vs 104.7).
 int64_t ksplit_tail_tiles(int cus) { return cus / 2; }
 
+// Parts for splitting a matrix-vector reduction across workgroups when its
+// `wgs` workgroups would fill at most half the CUs: enough parts to give every
+// CU one workgroup, each part at least kGemvPartLen rows of B long (measured
+// on MI355X: shorter parts, or two workgroups per CU, were slower).
+constexpr int kGemvPartLen = 8192;
+int gemv_parts(int64_t wgs, int N, int cus) {
+  if (wgs * 2 > cus) return 1;
+  const int64_t p = std::min<int64_t>(cus / wgs, N / kGemvPartLen);
+  return p >= 2 ? (int)p : 1;
+}
+
+struct SplitPlan {
+  int tile;
+  int parts;
+};
+
+// Estimated time (seconds) of k-split tiles of size t whose reduction is split
+// into p parts, on `cus` CUs at 2.4 GHz: the larger of the MFMA time (a t x t
+// tile over L reduction indices is t^2 L / 128 cycles of its four SIMDs, at
+// 60% of peak) and the HBM time (A and B panels of every tile, half of them
+// served by L2, at 5 TB/s), plus 0.5 us per round of workgroups and, for a
+// split, 10 us for the workspace and the second kernel and its traffic. The
+// constants are fitted to MI355X measurements of 19 shapes with few output
+// tiles (the chosen plan within 3% of the best measured one on all with
+// M N K >= 2^30).
+double splitk_time(int t, int p, int M, int N, int K, int cus) {
+  const double tiles = (double)cdiv(M, t) * (double)cdiv(K, t);
+  const double rounds = std::ceil(tiles * p / cus);
+  const double t_mfma = rounds * ((double)t * t * ((double)N / p) / 128.0) / (2.4e9 * 0.6);
+  const double t_hbm = 4.0 * N * tiles * 2.0 * t * 0.5 / 5e12;
+  double t_fixed = rounds * 0.5e-6;
+  if (p > 1) t_fixed += 10e-6 + (double)p * M * K * 8.0 / 5e12;
+  return std::max(t_mfma, t_hbm) + t_fixed;
+}
+
+// Parts to try: powers of two, each part at least 256 reduction indices long
+// (32 chunks, 8 per wave), at most four workgroups per CU.
+constexpr int kSplitkMinPart = 256;
+template <class F>
+void for_each_parts(int t, int M, int N, int K, int cus, F&& f) {
+  const int64_t tiles = cdiv(M, t) * cdiv(K, t);
+  for (int p = 2; N / p >= kSplitkMinPart && tiles * p <= 4 * (int64_t)cus; p *= 2) f(p);
+}
+
+// Best parts (>= 2) for k-split tiles of size t, by the estimate above.
+SplitPlan splitk_plan_tile(int t, int M, int N, int K, int cus) {
+  SplitPlan best{t, 2};
+  double best_time = 0;
+  for_each_parts(t, M, N, K, cus, [&](int p) {
+    const double e = splitk_time(t, p, M, N, K, cus);
+    if (best_time == 0 || e < best_time) {
+      best = {t, p};
+      best_time = e;
+    }
+  });
+  return best;
+}
+
+// For a shape with fewer 64x64 tiles than CUs: the k-split tile size (64 or
+// 32) and parts (1: no split) with the smallest estimated time.
+SplitPlan splitk_plan(int M, int N, int K, int cus) {
+  SplitPlan best{FGR_TILE_32, 1};
+  double best_time = splitk_time(FGR_TILE_32, 1, M, N, K, cus);
+  for (int t : {FGR_TILE_64, FGR_TILE_32}) {
+    auto consider = [&](int p) {
+      const double e = splitk_time(t, p, M, N, K, cus);
+      if (e < best_time) {
+        best = {t, p};
+        best_time = e;
+      }
+    };
+    consider(1);
+    for_each_parts(t, M, N, K, cus, consider);
+  }
+  return best;
+}
+
 struct Choice {
   int path;
   int tile;
@@ -130,8 +210,13 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
       if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_64};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_64};
     }
-    // fewer 64x64 tiles than CUs: 32x32 k-split tiles (the split kernel's
-    // 32x32 tiles measured as fast or faster with 4-byte loads)
+    // fewer 64x64 tiles than CUs: 64x64 or 32x32 k-split tiles, with the
+    // reduction also split across workgroups where that is estimated faster
+    // (unsplit 32x32 tiles of rows that are not 16-byte aligned go to the
+    // split kernel, measured as fast or faster with 4-byte loads)
+    const SplitPlan sp = splitk_plan(M, N, K, cus);
+    if (sp.parts >= 2) return {FGR_PATH_MFMA_SPLITK, sp.tile};
+    if (sp.tile == FGR_TILE_64) return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_64};
     return {vec ? FGR_PATH_MFMA_KSPLIT : FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
   }
   // N < 64: no direct copies
@@ -148,7 +233,7 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
 }
 
 // Tile for a forced path when the caller left it open.
-int default_tile(int path, const Choice& auto_choice, int M, int K, int cus, bool vec_rows) {
+int default_tile(int path, const Choice& auto_choice, int M, int N, int K, int cus, bool vec_rows) {
   if (path == auto_choice.path) return auto_choice.tile;
   switch (path) {
     case FGR_PATH_MFMA_DMA:
@@ -158,6 +243,9 @@ int default_tile(int path, const Choice& auto_choice, int M, int K, int cus, boo
       if (vec_rows && cdiv(M, 128) * cdiv(K, 128) >= cus) return FGR_TILE_128;
       if (path == FGR_PATH_MFMA_KSPLIT_TAIL || cdiv(M, 64) * cdiv(K, 64) >= cus) return FGR_TILE_64;
       return FGR_TILE_32;
+    case FGR_PATH_MFMA_SPLITK:
+      if (cdiv(M, 64) * cdiv(K, 64) < cus) return splitk_plan(M, N, K, cus).tile;
+      return vec_rows && cdiv(M, 128) * cdiv(K, 128) < cus ? FGR_TILE_128 : FGR_TILE_64;
     case FGR_PATH_MFMA_SPLIT: return cdiv(M, 64) * cdiv(K, 64) < cus ? FGR_TILE_32 : FGR_TILE_64;
     case FGR_PATH_MFMA_VEC:
     case FGR_PATH_MFMA_SCALAR:
@@ -168,11 +256,39 @@ int default_tile(int path, const Choice& auto_choice, int M, int K, int cus, boo
   }
 }
 
-int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStream_t stream) {
-  if (blocks < 1 || blocks > INT_MAX) return FGR_ERR_BAD_DIMS;
+int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStream_t stream, int rows = 1) {
+  if (blocks < 1 || blocks > INT_MAX || rows < 1 || rows > 65535) return FGR_ERR_BAD_DIMS;
   const hipError_t e =
-      hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
+      hipLaunchKernel(kernel, dim3((unsigned)blocks, (unsigned)rows), dim3(threads), args, 0, stream);
   return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
+}
+
+// Work for a reduction split across workgroups: a stream-ordered workspace of
+// parts x M x K floats (hipMallocAsync / hipFreeAsync on the caller's stream,
+// so calls on different streams never share one), the partial products into
+// it, then the parts added in order into C.
+struct PartsWorkspace {
+  float* w = nullptr;
+  hipStream_t s = nullptr;
+  ~PartsWorkspace() {
+    if (w) (void)hipFreeAsync(w, s);
+  }
+};
+
+int alloc_parts(PartsWorkspace& ws, int parts, int M, int K, hipStream_t s) {
+  ws.s = s;
+  const size_t bytes = (size_t)parts * (size_t)M * (size_t)K * sizeof(float);
+  return hipMallocAsync(reinterpret_cast<void**>(&ws.w), bytes, s) == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
+}
+
+int launch_reduce_parts(const float* W, float* C, int M, int K, int parts, bool vec, hipStream_t s) {
+  int64_t n = (int64_t)M * K;
+  const int64_t items = vec ? n / 4 : n;
+  const int64_t blocks = std::min<int64_t>(cdiv(items, fgr::kReduceThreads), 4096);
+  void* args[] = {&W, &C, &n, &parts};
+  return launch(vec ? reinterpret_cast<const void*>(&fgr::reduce_parts_kernel<4>)
+                    : reinterpret_cast<const void*>(&fgr::reduce_parts_kernel<1>),
+                blocks, fgr::kReduceThreads, args, s);
 }
 
 template <class Cfg, bool VEC>
@@ -291,32 +407,50 @@ using Ksplit32 = fgr::KsplitConfig<32, 4, true>;
 using Ksplit32s = fgr::KsplitConfig<32, 4, false>;
 
 template <class Cfg>
-int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s) {
+int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
+                      int parts, float* W) {
   int tiles_m = (int)cdiv(M, Cfg::BM);
   int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
-  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &parts, &W};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
-                count < 0 ? (int64_t)tiles_m * tiles_n : count, Cfg::kThreads, args, s);
+                count < 0 ? (int64_t)tiles_m * tiles_n : count, Cfg::kThreads, args, s, parts);
 }
 
 // The k-split kernel with tile x tile tiles over the first `count` tiles of
 // the grouped order (count < 0: all of them); 16-byte copies when the rows
-// allow them.
+// allow them. parts > 1: each tile's reduction also split over `parts`
+// workgroups writing partial tiles to W.
 int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
-                  hipStream_t s) {
+                  hipStream_t s, int parts = 1, float* W = nullptr) {
   const bool vec = mfma_vec_ok(A, B, C, N, K);
   switch (tile) {
     case FGR_TILE_128:
-      return vec ? launch_ksplit_cfg<Ksplit128>(A, B, C, M, N, K, count, s) : FGR_ERR_BAD_PATH;
+      return vec ? launch_ksplit_cfg<Ksplit128>(A, B, C, M, N, K, count, s, parts, W) : FGR_ERR_BAD_PATH;
     case FGR_TILE_64:
-      return vec ? launch_ksplit_cfg<Ksplit64>(A, B, C, M, N, K, count, s)
-                 : launch_ksplit_cfg<Ksplit64s>(A, B, C, M, N, K, count, s);
+      return vec ? launch_ksplit_cfg<Ksplit64>(A, B, C, M, N, K, count, s, parts, W)
+                 : launch_ksplit_cfg<Ksplit64s>(A, B, C, M, N, K, count, s, parts, W);
     case FGR_TILE_32:
-      return vec ? launch_ksplit_cfg<Ksplit32>(A, B, C, M, N, K, count, s)
-                 : launch_ksplit_cfg<Ksplit32s>(A, B, C, M, N, K, count, s);
+      return vec ? launch_ksplit_cfg<Ksplit32>(A, B, C, M, N, K, count, s, parts, W)
+                 : launch_ksplit_cfg<Ksplit32s>(A, B, C, M, N, K, count, s, parts, W);
     default: return FGR_ERR_BAD_PATH;
   }
+}
+
+bool vec4_rows(const float* C, int M, int K) { return ((int64_t)M * K) % 4 == 0 && aligned(C, 16); }
+
+// k-split tiles with the reduction also split across workgroups: the partial
+// tiles into a stream-ordered workspace, then added in part order (two parts
+// where no longer parts fit the estimate's limits). Without a
+// workspace (allocation failed) the tiles keep their whole reduction.
+int launch_ksplit_parts(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
+                        hipStream_t s) {
+  const int parts = splitk_plan_tile(tile, M, N, K, cus).parts;  // >= 2; N >= 128 gives 8 chunks per part
+  PartsWorkspace ws;
+  if (alloc_parts(ws, parts, M, K, s) != FGR_OK) return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
+  const int rc = launch_ksplit(tile, A, B, C, M, N, K, -1, s, parts, ws.w);
+  if (rc != FGR_OK) return rc;
+  return launch_reduce_parts(ws.w, C, M, K, parts, vec4_rows(C, M, K), s);
 }
 
 // Whole waves of tile x tile tiles on the k-split kernel, the last partial
@@ -355,15 +489,30 @@ int launch_split_tile(int tile, const float* A, const float* B, float* C, int M,
 // flight (two at 8 rows): with 16 waves per CU that saturates HBM, and more
 // loads in flight measured slower (M = 1: 5.79 TB/s with one, 4.82 with four).
 template <int VW>
-int launch_gemv(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
-  void* args[] = {&A, &B, &C, &M, &N, &K};
+int launch_gemv_parts(const float* A, const float* B, float* C, int M, int N, int K, int parts, float* W,
+                      hipStream_t s) {
+  void* args[] = {&A, &B, &C, &M, &N, &K, &parts, &W};
   const int64_t blocks = cdiv(K, fgr::kGemvCols);
   const void* kernel;
   if (M <= 1) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 1>);
   else if (M <= 2) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 2>);
   else if (M <= 4) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 4>);
   else kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 2, 8>);
-  return launch(kernel, blocks, 1024, args, s);
+  return launch(kernel, blocks, 1024, args, s, parts);
+}
+
+// The matrix-vector kernel; when K gives fewer than half the CUs a workgroup
+// (32 columns each) and N is long, the reduction is also split across
+// workgroups through a stream-ordered workspace (then added in part order).
+template <int VW>
+int launch_gemv(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
+  const int parts = gemv_parts(cdiv(K, fgr::kGemvCols), N, cus);
+  PartsWorkspace ws;
+  if (parts < 2 || alloc_parts(ws, parts, M, K, s) != FGR_OK)
+    return launch_gemv_parts<VW>(A, B, C, M, N, K, 1, nullptr, s);
+  const int rc = launch_gemv_parts<VW>(A, B, C, M, N, K, parts, ws.w, s);
+  if (rc != FGR_OK) return rc;
+  return launch_reduce_parts(ws.w, C, M, K, parts, vec4_rows(C, M, K), s);
 }
 
 int run(const float* A, const float* B, float* C, int M, int N, int K, void* stream, int path,
@@ -386,6 +535,11 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
           (tile == FGR_TILE_32 && path == FGR_PATH_MFMA_KSPLIT_TAIL))
         return FGR_ERR_BAD_PATH;
       break;
+    case FGR_PATH_MFMA_SPLITK:
+      // N >= 128 (two parts of at least 8 chunks); tiles of 128 (16-byte rows only), 64 or 32
+      if (N < 128 || (tile == FGR_TILE_128 && !mfma_vec_ok(A, B, C, N, K)) || tile == FGR_TILE_256)
+        return FGR_ERR_BAD_PATH;
+      break;
     case FGR_PATH_MFMA_SCALAR: break;
     case FGR_PATH_MFMA_SPLIT:
       if (tile != FGR_TILE_AUTO && tile != FGR_TILE_32 && tile != FGR_TILE_64) return FGR_ERR_BAD_PATH;
@@ -401,7 +555,8 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   if (tile != FGR_TILE_AUTO && tile != FGR_TILE_256 && tile != FGR_TILE_128 && tile != FGR_TILE_64 &&
       tile != FGR_TILE_32)
     return FGR_ERR_BAD_PATH;
-  if (tile == FGR_TILE_32 && path != FGR_PATH_MFMA_SPLIT && path != FGR_PATH_MFMA_KSPLIT && path != FGR_PATH_AUTO)
+  if (tile == FGR_TILE_32 && path != FGR_PATH_MFMA_SPLIT && path != FGR_PATH_MFMA_KSPLIT &&
+      path != FGR_PATH_MFMA_SPLITK && path != FGR_PATH_AUTO)
     return FGR_ERR_BAD_PATH;
 
   int cus = 0;
@@ -415,16 +570,17 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       tile = best.tile;
     } else if (M <= fgr::kGemvMaxRows) {
       path = best.path;
-    } else if (tile == FGR_TILE_32) {
-      path = FGR_PATH_MFMA_SPLIT;  // the only kernel with 32x32 tiles
     } else if (tile == best.tile && (best.path == FGR_PATH_MFMA_DMA || best.path == FGR_PATH_MFMA_DMA_TAIL ||
-                                     best.path == FGR_PATH_MFMA_KSPLIT || best.path == FGR_PATH_MFMA_KSPLIT_TAIL)) {
-      path = best.path;  // the direct-copy or k-split kernel the table picked for this tile
+                                     best.path == FGR_PATH_MFMA_KSPLIT || best.path == FGR_PATH_MFMA_KSPLIT_TAIL ||
+                                     best.path == FGR_PATH_MFMA_SPLITK || best.path == FGR_PATH_MFMA_SPLIT)) {
+      path = best.path;  // the kernel the table picked for this tile
+    } else if (tile == FGR_TILE_32) {
+      path = FGR_PATH_MFMA_SPLIT;  // 32x32 tiles for any shape
     } else {
       path = mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
     }
   }
-  if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, K, cus, mfma_vec_ok(A, B, C, N, K));
+  if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, N, K, cus, mfma_vec_ok(A, B, C, N, K));
 
   switch (path) {
     case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, -1, s);
@@ -436,8 +592,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     case FGR_PATH_MFMA_SPLIT:
       return mfma_vec_ok(A, B, C, N, K) ? launch_split_tile<true>(tile, A, B, C, M, N, K, cus, s)
                                         : launch_split_tile<false>(tile, A, B, C, M, N, K, cus, s);
-    case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, M, N, K, s);
-    case FGR_PATH_GEMV_SCALAR: return launch_gemv<1>(A, B, C, M, N, K, s);
+    case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, M, N, K, cus, s);
+    case FGR_PATH_GEMV_SCALAR: return launch_gemv<1>(A, B, C, M, N, K, cus, s);
+    case FGR_PATH_MFMA_SPLITK: return launch_ksplit_parts(tile, A, B, C, M, N, K, cus, s);
   }
   return FGR_ERR_BAD_PATH;
 }

@@ -101,6 +101,11 @@ extern "C" {
 #define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT (tile 128 or 64) on the whole waves of tiles, the
                                        split kernel on the tiles of the last, partial wave; two
                                        launches */
+#define FGR_PATH_MFMA_SPLITK 10 /* MFMA_KSPLIT (tile 128, 64 or 32) with each tile's reduction also
+                                   split into P parts over P workgroups, which write partial tiles
+                                   to a workspace of P*M*K floats; a second kernel adds the parts
+                                   in part order into C. For few output tiles and a long N
+                                   (N >= 128). P is chosen from the shape; two launches. */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0
@@ -117,6 +122,16 @@ extern "C" {
  *   M,N,K  dimensions, each >= 1; N is the reduction length
  *   stream hipStream_t as void*, NULL for the null stream
  * Returns FGR_OK or an FGR_ERR_* code (see above). Asynchronous.
+ * Workspace: when the output has too few tiles (or, for M <= 8, too few
+ * 32-column blocks) to give every CU a workgroup and N is long, the reduction
+ * is split into P parts across workgroups (paths MFMA_SPLITK and GEMV_*): the
+ * library then takes a workspace of P*M*K floats with hipMallocAsync on
+ * `stream` (at most 16 MiB on a 256-CU device when solve() picks the split;
+ * a forced MFMA_SPLITK on a large output takes P = 2, i.e. 2*M*K floats) and
+ * releases it with hipFreeAsync on `stream` after its last kernel, so calls
+ * on different streams never share one. If that allocation fails the unsplit
+ * kernel runs instead (same result up to rounding order). Results are
+ * deterministic: the parts are added in a fixed order.
  * The LeetGPU signature (section "Problem Description", and every "Solution"
  * of the write-up) is solve(A, B, C, M, N, K) returning void; this form adds
  * the stream and a status.

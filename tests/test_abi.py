@@ -204,6 +204,29 @@ def test_split_path_choices():
     assert sp(A0, B0, C0, 2047, 61, 2051) == fgr.PATH_MFMA_SCALAR
 
 
+def test_split_reduction_choices():
+    sp, st = fgr.select_path, fgr.select_tile
+    A0, B0, C0 = 1 << 40, 2 << 40, 3 << 40  # room for the long operands
+    # few output tiles and a long reduction: the reduction is also split
+    # across workgroups; 64x64 tiles for tall outputs, 32x32 for skinny ones
+    # (less padding), by the time estimate
+    for shape, tile in [((256, 65536, 256), 64), ((128, 262144, 128), 64), ((64, 65536, 1024), 64),
+                        ((512, 65536, 512), 64), ((16, 1048576, 64), 32), ((24, 65536, 1024), 32),
+                        ((16, 16384, 4096), 32), ((130, 20000, 66), 32)]:
+        assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
+        assert st(A0, B0, C0, *shape) == tile, shape
+        assert sp(A0 + 4, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape  # 4-byte copies too
+    # enough 32x32 tiles for every CU, or too short a reduction: no split
+    assert sp(A0, B0, C0, 512, 8192, 512) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 200, 2048, 200) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 64, 100, 64) == fgr.PATH_MFMA_KSPLIT
+    # tiles enough for every CU: the whole-device kernels, never a split
+    assert sp(A0, B0, C0, 1024, 32768, 1024) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 8192, 65536, 8192) == fgr.PATH_MFMA_DMA
+
+
 def test_python_wrapper_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     a = torch.zeros(4, dtype=torch.float32)

@@ -103,6 +103,12 @@ def paths_for(M, N, K):
     if N % 4 == 0 and K % 4 == 0 and N >= 64:
         out.append((fgr.PATH_MFMA_KSPLIT, fgr.TILE_128))
         out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128))
+    if N >= 128:
+        # the reduction also split across workgroups (two parts at least)
+        for tile in (fgr.TILE_64, fgr.TILE_32):
+            out.append((fgr.PATH_MFMA_SPLITK, tile))
+        if N % 4 == 0 and K % 4 == 0:
+            out.append((fgr.PATH_MFMA_SPLITK, fgr.TILE_128))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
     if M <= 8:
@@ -278,6 +284,58 @@ def test_ksplit_exact(shape, path, tile):
     assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT, tile), Cref, f"{shape} k-split only")
 
 
+@pytest.mark.parametrize("shape,tile", [
+    ((256, 16384, 256), 64), ((100, 30000, 300), 32), ((16, 65536, 64), 32), ((130, 20000, 66), 32),
+    ((96, 50001, 97), 32), ((64, 16384, 64), 32)], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_split_reduction_exact(shape, tile):
+    # few output tiles, long reduction: each tile's reduction split into parts
+    # over workgroups, partial tiles added in part order by a second kernel;
+    # on integer data every sum is exact (|sum| <= 16 N < 2^24), so the result
+    # must be the oracle's bits whatever the split (and for forced tiles too)
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=12)
+    say(f"split reduction {shape}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_MFMA_SPLITK
+    assert fgr.select_tile(1 << 40, 2 << 40, 3 << 40, M, N, K) == tile
+    say(f"split reduction {shape}: GPU")
+    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
+    tiles = [fgr.TILE_64, fgr.TILE_32] + ([fgr.TILE_128] if N % 4 == 0 and K % 4 == 0 else [])
+    for t in tiles:
+        assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_SPLITK, t), Cref, f"{shape} split tile {t}")
+    assert_exact(gpu_gemm(A, B, offsets=(1, 1, 1)), Cref, f"{shape} 4-byte aligned")
+
+
+@pytest.mark.parametrize("shape", [(1, 262144, 64), (8, 131072, 256), (5, 100003, 33), (3, 65536, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_split_matrix_vector_exact(shape):
+    # matrix-vector and skinny products with few 32-column blocks: rows of B
+    # split into parts over workgroups; exact on integer data
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=13)
+    say(f"split matrix-vector {shape}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    say(f"split matrix-vector {shape}: GPU")
+    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_GEMV_SCALAR), Cref, f"{shape} scalar")
+    assert_exact(gpu_gemm(A, B, offsets=(1, 1, 1)), Cref, f"{shape} 4-byte aligned")
+
+
+@pytest.mark.parametrize("shape", [(128, 262144, 128), (16, 1048576, 64), (1, 4194304, 16), (512, 65536, 512)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_split_reduction_long_sampled(shape):
+    # long reductions at full size on uniform data: sampled outputs within
+    # the tolerance (every tile and part boundary crossed by the samples)
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "uniform", seed=14)
+    say(f"long reduction {shape}: path {fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]}")
+    C = gpu_gemm(A, B)
+    rng = np.random.default_rng(7)
+    rows, cols = sample_positions(M, K, 32, rng, extra=256)
+    Cref, S = oracle.gemm_at(A, B, rows, cols)
+    assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{shape} sampled")
+
+
 @pytest.mark.parametrize("shape", [(4352, 64, 4096), (4100, 68, 4100), (2304, 100, 8192), (65792, 64, 256)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_partial_last_wave_exact(shape):
@@ -327,7 +385,9 @@ def test_gemv_workload_full_compare():
     ((300, 500, 261), fgr.PATH_MFMA_DMA, 256),
     ((1, 3000, 900), fgr.PATH_GEMV_VEC, 0),
     ((5, 3000, 900), fgr.PATH_GEMV_VEC, 0),
-], ids=["ragged-auto", "dma", "split64", "ksplit", "dma-4byte", "gemv", "skinny"])
+    ((256, 16384, 256), fgr.PATH_MFMA_SPLITK, 64),
+    ((1, 262144, 64), fgr.PATH_GEMV_VEC, 0),
+], ids=["ragged-auto", "dma", "split64", "ksplit", "dma-4byte", "gemv", "skinny", "splitk", "gemv-parts"])
 def test_repeat_runs_are_bitwise_identical(shape, path, tile):
     # fixed reduction order and no atomics: identical bits on every run
     M, N, K = shape
