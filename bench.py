@@ -22,7 +22,10 @@ clock. Prints ONE JSON line:
 
 Workloads (seeded synthetic inputs, synth/): leetgpu8192 (default, the
 LeetGPU timed shape M=8192, N=6144, K=4096, normal entries / sqrt(N)),
-cube4096, ragged1023, cube256, gemv8192.
+cube4096, ragged1023, cube256, gemv8192, longn128 (128 x 262144 x 128: few
+output tiles, long reduction). For shapes whose reduction is split across
+workgroups one step is two kernels (partial tiles, then their sum); the
+roofline's launch duration covers both.
 """
 
 from __future__ import annotations
@@ -182,7 +185,10 @@ def ablation(w, dA, dBs, dC, copies, steps, warmup, stream):
     variants = [(fgr.PATH_MFMA_DMA, 256), (fgr.PATH_MFMA_DMA_TAIL, 256)]
     for tile in (256, 128, 64):
         variants += [(fgr.PATH_MFMA_VEC, tile), (fgr.PATH_MFMA_SCALAR, tile)]
-    variants += [(fgr.PATH_MFMA_SPLIT, 64), (fgr.PATH_MFMA_SPLIT, 32),
+    for tile in (128, 64, 32):
+        variants += [(fgr.PATH_MFMA_KSPLIT, tile), (fgr.PATH_MFMA_SPLITK, tile)]
+    variants += [(fgr.PATH_MFMA_KSPLIT_TAIL, 128), (fgr.PATH_MFMA_KSPLIT_TAIL, 64),
+                 (fgr.PATH_MFMA_SPLIT, 64), (fgr.PATH_MFMA_SPLIT, 32),
                  (fgr.PATH_GEMV_VEC, 0), (fgr.PATH_GEMV_SCALAR, 0)]
     auto = (fgr.select_path(dA, dBs[0], dC, w.M, w.N, w.K), fgr.select_tile(dA, dBs[0], dC, w.M, w.N, w.K))
     for path, tile in variants:

@@ -137,19 +137,24 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int lg = lane >> 5;
   const int piece = wave * T::kPiece;  // this wave's offset inside every stage object
 
+  // Split across workgroups (parts > 1): the grid holds parts x (tiles)
+  // workgroups; logical id = part * tiles + tile, so that after the XCD
+  // renumbering the tiles of one part, which read the same reduction range of
+  // A and B, run on the same XCD and share its L2. Part p owns the chunks
+  // [nchunks p / parts, nchunks (p + 1) / parts) and writes its partial tile
+  // to W + p M K (row stride K) instead of C; a second kernel adds the parts.
+  // This wave's chunks are [c_begin, c_end) of the part's; at least 8 chunks
+  // per part give every wave >= 2.
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int ntiles = gridDim.x / parts;
+  const int part = logical / ntiles;
   int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group, tm, tn);
+  grouped_tile(logical - part * ntiles, tiles_m, tiles_n, group, tm, tn);
   const int m0 = tm * T::BM;
   const int k0 = tn * BN;
 
-  // Split across workgroups (parts > 1): workgroup row blockIdx.y = part owns
-  // the chunks [nchunks part / parts, nchunks (part + 1) / parts) and writes
-  // its partial tile to W + part M K (row stride K) instead of C; a second
-  // kernel adds the parts in order. This wave's chunks are [c_begin, c_end)
-  // of the part's; at least 8 chunks per part give every wave >= 2.
   const int nchunks = (N + BK - 1) / BK;
   const int n_first = N - BK * nchunks;  // in (-BK, 0]
-  const int part = blockIdx.y;
   const int pc0 = (int)((int64_t)nchunks * part / parts);
   const int pn = (int)((int64_t)nchunks * (part + 1) / parts) - pc0;
   const int c_begin = pc0 + pn * wave / T::kWaves;

@@ -116,19 +116,22 @@ struct SplitPlan {
 // Estimated time (seconds) of k-split tiles of size t whose reduction is split
 // into p parts, on `cus` CUs at 2.4 GHz: the larger of the MFMA time (a t x t
 // tile over L reduction indices is t^2 L / 128 cycles of its four SIMDs, at
-// 60% of peak) and the HBM time (A and B panels of every tile, half of them
-// served by L2, at 5 TB/s), plus 0.5 us per round of workgroups and, for a
-// split, 10 us for the workspace and the second kernel and its traffic. The
-// constants are fitted to MI355X measurements of 19 shapes with few output
-// tiles (the chosen plan within 3% of the best measured one on all with
-// M N K >= 2^30).
+// 70% of peak, 10% less time when two or more workgroups share a CU) and the
+// HBM time (A and B panels of every tile, 35% of them from HBM and the rest
+// from L2, at 5 TB/s), plus 2 us per round of workgroups and, for a split,
+// 20 us (workspace, second launch, the host's extra calls) and its P M K 8
+// bytes. The constants are fitted to MI355X measurements of 19 shapes with
+// few output tiles, tiles 64 and 32, P = 1 .. 128 (the chosen plan within 6%
+// of the best measured one on every shape, small ones included).
 double splitk_time(int t, int p, int M, int N, int K, int cus) {
   const double tiles = (double)cdiv(M, t) * (double)cdiv(K, t);
   const double rounds = std::ceil(tiles * p / cus);
-  const double t_mfma = rounds * ((double)t * t * ((double)N / p) / 128.0) / (2.4e9 * 0.6);
-  const double t_hbm = 4.0 * N * tiles * 2.0 * t * 0.5 / 5e12;
-  double t_fixed = rounds * 0.5e-6;
-  if (p > 1) t_fixed += 10e-6 + (double)p * M * K * 8.0 / 5e12;
+  const int resident = t >= 128 ? 1 : t >= 64 ? 2 : 4;  // workgroups per CU (LDS)
+  const double shared = std::min<double>(rounds, resident) >= 2 ? 0.9 : 1.0;
+  const double t_mfma = shared * rounds * ((double)t * t * ((double)N / p) / 128.0) / (2.4e9 * 0.7);
+  const double t_hbm = 4.0 * N * tiles * 2.0 * t * 0.35 / 5e12;
+  double t_fixed = rounds * 2e-6;
+  if (p > 1) t_fixed += 20e-6 + (double)p * M * K * 8.0 / 5e12;
   return std::max(t_mfma, t_hbm) + t_fixed;
 }
 
@@ -281,11 +284,16 @@ int alloc_parts(PartsWorkspace& ws, int parts, int M, int K, hipStream_t s) {
   return hipMallocAsync(reinterpret_cast<void**>(&ws.w), bytes, s) == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
 }
 
+// The parts' sum into C: `slices` (a power of two <= min(parts, 16)) threads
+// per output, each adding a contiguous run of parts, so that few outputs
+// still give many loads in flight.
 int launch_reduce_parts(const float* W, float* C, int M, int K, int parts, bool vec, hipStream_t s) {
   int64_t n = (int64_t)M * K;
   const int64_t items = vec ? n / 4 : n;
-  const int64_t blocks = std::min<int64_t>(cdiv(items, fgr::kReduceThreads), 4096);
-  void* args[] = {&W, &C, &n, &parts};
+  int slices = 1;
+  while (slices * 2 <= std::min(parts, fgr::kReduceMaxSlices)) slices *= 2;
+  const int64_t blocks = cdiv(items, fgr::kReduceThreads / slices);
+  void* args[] = {&W, &C, &n, &parts, &slices};
   return launch(vec ? reinterpret_cast<const void*>(&fgr::reduce_parts_kernel<4>)
                     : reinterpret_cast<const void*>(&fgr::reduce_parts_kernel<1>),
                 blocks, fgr::kReduceThreads, args, s);
@@ -414,7 +422,7 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
   int group = kTileGroup;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &parts, &W};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
-                count < 0 ? (int64_t)tiles_m * tiles_n : count, Cfg::kThreads, args, s, parts);
+                (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts, Cfg::kThreads, args, s);
 }
 
 // The k-split kernel with tile x tile tiles over the first `count` tiles of

@@ -107,9 +107,10 @@ class Workload:
         return 4 * (self.M * self.N + self.N * self.K + self.M * self.K)
 
 
-# The five workloads: small cube (plus its integer twin for bit-exact checks),
-# ragged odd sizes, large cube, the timed shape of the LeetGPU problem and the
-# single-row (matrix-vector shaped) case.
+# The workloads: small cube (plus its integer twin for bit-exact checks),
+# ragged odd sizes, large cube, the timed shape of the LeetGPU problem, the
+# single-row (matrix-vector shaped) case, and a few-tile output over a long
+# reduction (the shape class whose reduction is split across workgroups).
 WORKLOADS = {
     "cube256": Workload("cube256", 256, 256, 256, "uniform", 0),
     "cube256_int": Workload("cube256_int", 256, 256, 256, "integer", 0),
@@ -117,6 +118,7 @@ WORKLOADS = {
     "cube4096": Workload("cube4096", 4096, 4096, 4096, "uniform", 2),
     "leetgpu8192": Workload("leetgpu8192", 8192, 6144, 4096, "normal", 3),
     "gemv8192": Workload("gemv8192", 1, 8192, 8192, "uniform", 4),
+    "longn128": Workload("longn128", 128, 262144, 128, "uniform", 5),
 }
 
 

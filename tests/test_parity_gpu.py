@@ -228,7 +228,7 @@ def sample_positions(M, K, tile, rng, extra=2048):
     return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["cube4096", "leetgpu8192"])
+@pytest.mark.parametrize("name", ["cube4096", "leetgpu8192", "longn128"])
 def test_large_workloads_sampled(name):
     w = synth.WORKLOADS[name]
     say(f"{name}: generating inputs")
@@ -285,7 +285,8 @@ def test_ksplit_exact(shape, path, tile):
 
 
 @pytest.mark.parametrize("shape,tile", [
-    ((256, 16384, 256), 64), ((100, 30000, 300), 32), ((16, 65536, 64), 32), ((130, 20000, 66), 32),
+    ((128, 262144, 128), 64), ((256, 16384, 256), 32), ((100, 30000, 300), 32), ((16, 65536, 64), 32),
+    ((130, 20000, 66), 32),
     ((96, 50001, 97), 32), ((64, 16384, 64), 32)], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_split_reduction_exact(shape, tile):
     # few output tiles, long reduction: each tile's reduction split into parts
