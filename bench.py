@@ -188,7 +188,7 @@ def ablation(w, dA, dBs, dC, copies, steps, warmup, stream):
     for tile in (128, 64, 32):
         variants += [(fgr.PATH_MFMA_KSPLIT, tile), (fgr.PATH_MFMA_SPLITK, tile)]
     variants += [(fgr.PATH_MFMA_KSPLIT_TAIL, 128), (fgr.PATH_MFMA_KSPLIT_TAIL, 64),
-                 (fgr.PATH_MFMA_SPLIT, 64), (fgr.PATH_MFMA_SPLIT, 32),
+                 (fgr.PATH_MFMA_SPLIT, 64), (fgr.PATH_MFMA_SPLIT, 32), (fgr.PATH_VALU, 128),
                  (fgr.PATH_GEMV_VEC, 0), (fgr.PATH_GEMV_SCALAR, 0)]
     auto = (fgr.select_path(dA, dBs[0], dC, w.M, w.N, w.K), fgr.select_tile(dA, dBs[0], dC, w.M, w.N, w.K))
     for path, tile in variants:

@@ -41,7 +41,9 @@ PATH_MFMA_DMA_TAIL = 7
 PATH_MFMA_KSPLIT = 8
 PATH_MFMA_KSPLIT_TAIL = 9
 PATH_MFMA_SPLITK = 10
+PATH_VALU = 11
 PATH_NAMES = {
+    PATH_VALU: "valu",
     PATH_MFMA_SPLITK: "mfma_splitk",
     PATH_MFMA_KSPLIT: "mfma_ksplit",
     PATH_MFMA_KSPLIT_TAIL: "mfma_ksplit_tail",

@@ -1,7 +1,8 @@
 // C-ABI entry points of the row-major FP32 GEMM library (declared, with the
 // full contract, in include/fp32_gemm_row.h): argument checks, path and tile
 // selection, and the launches. Every step of the product runs in the kernels
-// of gemm_mfma.hpp and gemv.hpp; this file only decides and enqueues.
+// (gemm_mfma*.hpp, gemm_valu.hpp, gemv.hpp, reduce_parts.hpp); this file only
+// decides, takes the split-reduction workspace, and enqueues.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -16,6 +17,7 @@
 #include "gemm_mfma_dma.hpp"
 #include "gemm_mfma_ksplit.hpp"
 #include "gemm_mfma_split.hpp"
+#include "gemm_valu.hpp"
 #include "gemv.hpp"
 #include "reduce_parts.hpp"
 
@@ -250,6 +252,7 @@ int default_tile(int path, const Choice& auto_choice, int M, int N, int K, int c
       if (cdiv(M, 64) * cdiv(K, 64) < cus) return splitk_plan(M, N, K, cus).tile;
       return vec_rows && cdiv(M, 128) * cdiv(K, 128) < cus ? FGR_TILE_128 : FGR_TILE_64;
     case FGR_PATH_MFMA_SPLIT: return cdiv(M, 64) * cdiv(K, 64) < cus ? FGR_TILE_32 : FGR_TILE_64;
+    case FGR_PATH_VALU: return FGR_TILE_128;
     case FGR_PATH_MFMA_VEC:
     case FGR_PATH_MFMA_SCALAR:
       if (cdiv(M, 256) * cdiv(K, 256) >= cus) return FGR_TILE_256;
@@ -492,6 +495,19 @@ int launch_split_tile(int tile, const float* A, const float* B, float* C, int M,
   return launch_split<Split64x4, VEC>(A, B, C, M, N, K, s);
 }
 
+// The vector-ALU kernel (128x128 tiles, 8-deep reduction chunks: 16-deep
+// ones made the compiler hold the whole chunk's operands and exceed 256 VGPRs).
+template <bool VEC>
+int launch_valu(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  using Cfg = fgr::ValuConfig<8, VEC>;
+  int tiles_m = (int)cdiv(M, Cfg::BM);
+  int tiles_n = (int)cdiv(K, Cfg::BN);
+  int group = kTileGroup;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  return launch(reinterpret_cast<const void*>(&fgr::gemm_valu_kernel<Cfg>), (int64_t)tiles_m * tiles_n,
+                fgr::kValuThreads, args, s);
+}
+
 // Rows of A per matrix-vector workgroup: the smallest of 1, 2, 4, 8 that holds
 // all M rows (B is streamed once). Each lane keeps one row of B in
 // flight (two at 8 rows): with 16 waves per CU that saturates HBM, and more
@@ -548,6 +564,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       if (N < 128 || (tile == FGR_TILE_128 && !mfma_vec_ok(A, B, C, N, K)) || tile == FGR_TILE_256)
         return FGR_ERR_BAD_PATH;
       break;
+    case FGR_PATH_VALU:
+      if (tile != FGR_TILE_AUTO && tile != FGR_TILE_128) return FGR_ERR_BAD_PATH;
+      break;
     case FGR_PATH_MFMA_SCALAR: break;
     case FGR_PATH_MFMA_SPLIT:
       if (tile != FGR_TILE_AUTO && tile != FGR_TILE_32 && tile != FGR_TILE_64) return FGR_ERR_BAD_PATH;
@@ -603,6 +622,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, M, N, K, cus, s);
     case FGR_PATH_GEMV_SCALAR: return launch_gemv<1>(A, B, C, M, N, K, cus, s);
     case FGR_PATH_MFMA_SPLITK: return launch_ksplit_parts(tile, A, B, C, M, N, K, cus, s);
+    case FGR_PATH_VALU:
+      return mfma_vec_ok(A, B, C, N, K) ? launch_valu<true>(A, B, C, M, N, K, s)
+                                        : launch_valu<false>(A, B, C, M, N, K, s);
   }
   return FGR_ERR_BAD_PATH;
 }

@@ -106,6 +106,12 @@ extern "C" {
                                    to a workspace of P*M*K floats; a second kernel adds the parts
                                    in part order into C. For few output tiles and a long N
                                    (N >= 128). P is chosen from the shape; two launches. */
+#define FGR_PATH_VALU 11 /* FP32 FMAs on the vector ALUs, no matrix cores: 128x128 tiles, an 8x8
+                            register micro-tile per thread, two LDS buffers (128-bit loads when the
+                            MFMA_VEC conditions hold, else 32-bit); any shape. A reference for the
+                            register-tiled CUDA-core line of the LeetGPU write-up (sections "V1:
+                            Two-Dimensional Thread Tiling" to "V3"); never chosen by solve(). Tile
+                            AUTO or 128 only. */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0

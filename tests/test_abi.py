@@ -125,6 +125,17 @@ def test_forced_path_rejections(lib):
     for tile in (0, 64, 32):
         assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT, tile) == fgr.ERR_DEVICE
         assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, tile) == fgr.ERR_DEVICE
+    # the cross-workgroup split needs N >= 128 (two parts of 8 chunks); tile
+    # 128 needs 128-bit rows; no 256 tiles
+    assert call(lib, A0, B0, C0, 512, 120, 512, fgr.PATH_MFMA_SPLITK) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_SPLITK, 128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, 256) == fgr.ERR_BAD_PATH
+    for tile in (0, 128, 64, 32):
+        assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, tile) == fgr.ERR_DEVICE
+    # the vector-ALU path takes any shape, tile 128 only
+    assert call(lib, A0 + 4, B0, C0, 7, 5, 3, fgr.PATH_VALU) == fgr.ERR_DEVICE
+    assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_VALU, 128) == fgr.ERR_DEVICE
+    assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_VALU, 64) == fgr.ERR_BAD_PATH
     # 32x32 tiles exist on the split and k-split paths only
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_VEC, 32) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_MFMA_SPLIT, 128) == fgr.ERR_BAD_PATH

@@ -111,6 +111,7 @@ def paths_for(M, N, K):
             out.append((fgr.PATH_MFMA_SPLITK, fgr.TILE_128))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
+    out.append((fgr.PATH_VALU, fgr.TILE_AUTO))  # vector ALUs, any shape
     if M <= 8:
         out.append((fgr.PATH_GEMV_SCALAR, 0))
         if K % 4 == 0:
@@ -335,6 +336,31 @@ def test_split_reduction_long_sampled(shape):
     rows, cols = sample_positions(M, K, 32, rng, extra=256)
     Cref, S = oracle.gemm_at(A, B, rows, cols)
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{shape} sampled")
+
+
+@pytest.mark.parametrize("shape", [(1023, 1025, 1027), (1024, 1024, 1024), (300, 2000, 260), (1, 3, 1), (129, 17, 5)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_vector_alu_path_exact(shape):
+    # the register-tiled vector-ALU kernel: ragged tiles, ragged reduction,
+    # 32-bit loads for unaligned rows; exact on integer data
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=15)
+    say(f"vector ALU {shape}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    say(f"vector ALU {shape}: GPU")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_VALU), Cref, f"{shape} vector ALU")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_VALU, offsets=(1, 2, 3)), Cref, f"{shape} vector ALU, 4-byte aligned")
+
+
+def test_vector_alu_path_timed_shape_sampled():
+    w = synth.WORKLOADS["leetgpu8192"]
+    A, B = synth.workload_inputs(w)
+    say("vector ALU at the timed shape: GPU")
+    C = gpu_gemm(A, B, fgr.PATH_VALU)
+    rng = np.random.default_rng(8)
+    rows, cols = sample_positions(w.M, w.K, 128, rng)
+    Cref, S = oracle.gemm_at(A, B, rows, cols)
+    assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], "vector ALU sampled")
 
 
 @pytest.mark.parametrize("shape", [(4352, 64, 4096), (4100, 68, 4100), (2304, 100, 8192), (65792, 64, 256)],
