@@ -257,10 +257,10 @@ def cpu_baseline(w, A, B, target_s: float):
         t0 = time.perf_counter()
         oracle.gemm(A[:R], B, threads=threads)
         elapsed = time.perf_counter() - t0
-    # a whole product shorter than the target: repeat it (at most 1000 times)
+    # a whole product shorter than the target: repeat it
     reps = 1
     if R == w.M and elapsed < target_s / 2:
-        reps = max(1, min(1000, int(target_s / max(elapsed, 1e-6))))
+        reps = max(1, min(100000, int(target_s / max(elapsed, 1e-6))))
         t0 = time.perf_counter()
         for _ in range(reps):
             oracle.gemm(A, B, threads=threads)
@@ -296,7 +296,7 @@ def main() -> int:
                     help="cycle through this many copies of B (0 = 4 for the matrix-vector workload, "
                          "whose 256 MiB B would otherwise partly stay in the 256 MB last-level cache; 1 otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run a plain 512 MiB device copy three times "
                          "(the known-size reference for HBM byte counters)")

@@ -447,6 +447,34 @@ def test_identity_and_one_hot():
     assert_exact(gpu_gemm(A, B), exp, "one-hot rows")
 
 
+@pytest.mark.parametrize("shape", [(300, 500, 260), (1023, 1025, 1027), (64, 20000, 96), (4, 3000, 50)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_algebraic_invariants(shape):
+    # properties of the product that hold exactly on integer data whichever
+    # kernel runs each call: A = 0 gives C = 0; scaling A by a power of two
+    # scales C exactly (on any finite data); (A B)^T = B^T A^T; column and row
+    # blocks of C are the products of the matching blocks of A and B
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=16)
+    C = gpu_gemm(A, B)
+    Cref, _ = oracle.gemm(A, B)
+    assert_exact(C, Cref, f"{shape} product")
+    assert_exact(gpu_gemm(np.zeros_like(A), B), np.zeros((M, K)), f"{shape} zero A")
+    Au, Bu = synth.make_inputs(M, N, K, "uniform", seed=17)
+    Cu = gpu_gemm(Au, Bu).astype(np.float64)
+    assert_exact(gpu_gemm(Au * np.float32(2.0), Bu), 2.0 * Cu, f"{shape} 2A")
+    assert_exact(gpu_gemm(Au, Bu * np.float32(0.25)), 0.25 * Cu, f"{shape} B/4")
+    At = np.ascontiguousarray(A.T)
+    Bt = np.ascontiguousarray(B.T)
+    assert_exact(gpu_gemm(Bt, At), Cref.T, f"{shape} transpose")
+    k1 = K // 3 + 1
+    assert_exact(gpu_gemm(A, np.ascontiguousarray(B[:, :k1])), Cref[:, :k1], f"{shape} columns [0, {k1})")
+    if k1 < K:
+        assert_exact(gpu_gemm(A, np.ascontiguousarray(B[:, k1:])), Cref[:, k1:], f"{shape} columns [{k1}, K)")
+    m1 = M // 2 + 1
+    assert_exact(gpu_gemm(np.ascontiguousarray(A[:m1]), B), Cref[:m1], f"{shape} rows [0, {m1})")
+
+
 def test_single_product_reduction_is_exact():
     # N = 1: C[m,k] = a * b, one product (the padding adds exact zeros)
     rng = np.random.default_rng(1)
