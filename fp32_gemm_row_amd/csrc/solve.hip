@@ -32,6 +32,8 @@ struct DeviceInfo {
   bool probed = false;
   bool ok = false;
   int cus = 0;
+  bool pool_tried = false;
+  hipMemPool_t pool = nullptr;  // the split-reduction workspace pool, made on first use
 };
 
 std::mutex g_dev_mu;
@@ -270,9 +272,9 @@ int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStre
 }
 
 // Work for a reduction split across workgroups: a stream-ordered workspace of
-// parts x M x K floats (hipMallocAsync / hipFreeAsync on the caller's stream,
-// so calls on different streams never share one), the partial products into
-// it, then the parts added in order into C.
+// parts x M x K floats (taken from a per-device pool on the caller's stream and
+// given back with hipFreeAsync on it, so calls on different streams never
+// share one), the partial products into it, then the parts added into C.
 struct PartsWorkspace {
   float* w = nullptr;
   hipStream_t s = nullptr;
@@ -281,10 +283,51 @@ struct PartsWorkspace {
   }
 };
 
+// Freed workspace a device's pool keeps for reuse instead of returning it at
+// each synchronisation (measured on MI355X, 128 x 262144 x 128 with a
+// synchronisation after every call: 158 us per call from the device's default
+// pool, 118 from this one; 16 MiB workspace).
+constexpr uint64_t kPoolKeepBytes = 64ull << 20;
+
+// The current device's workspace pool (created on first use; null if that
+// failed, and then the device's default pool serves).
+hipMemPool_t workspace_pool() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.pool_tried) {
+    d.pool_tried = true;
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+      uint64_t keep = kPoolKeepBytes;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+      d.pool = pool;
+    } else {
+      (void)hipGetLastError();  // clear the failed call's error
+    }
+  }
+  return d.pool;
+}
+
 int alloc_parts(PartsWorkspace& ws, int parts, int M, int K, hipStream_t s) {
   ws.s = s;
   const size_t bytes = (size_t)parts * (size_t)M * (size_t)K * sizeof(float);
-  return hipMallocAsync(reinterpret_cast<void**>(&ws.w), bytes, s) == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
+  hipMemPool_t pool = workspace_pool();
+  const hipError_t e = pool ? hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws.w), bytes, pool, s)
+                            : hipMallocAsync(reinterpret_cast<void**>(&ws.w), bytes, s);
+  if (e != hipSuccess) {
+    ws.w = nullptr;
+    (void)hipGetLastError();  // the caller runs the unsplit kernel instead
+    return FGR_ERR_LAUNCH;
+  }
+  return FGR_OK;
 }
 
 // The parts' sum into C: `slices` (a power of two <= min(parts, 16)) threads

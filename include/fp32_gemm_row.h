@@ -131,13 +131,17 @@ extern "C" {
  * Workspace: when the output has too few tiles (or, for M <= 8, too few
  * 32-column blocks) to give every CU a workgroup and N is long, the reduction
  * is split into P parts across workgroups (paths MFMA_SPLITK and GEMV_*): the
- * library then takes a workspace of P*M*K floats with hipMallocAsync on
- * `stream` (at most 16 MiB on a 256-CU device when solve() picks the split;
- * a forced MFMA_SPLITK on a large output takes P = 2, i.e. 2*M*K floats) and
- * releases it with hipFreeAsync on `stream` after its last kernel, so calls
- * on different streams never share one. If that allocation fails the unsplit
- * kernel runs instead (same result up to rounding order). Results are
- * deterministic: the parts are added in a fixed order.
+ * library then takes a workspace of P*M*K floats, stream-ordered on `stream`
+ * (at most 16 MiB on a 256-CU device when solve() picks the split; a forced
+ * MFMA_SPLITK on a large output takes P = 2, i.e. 2*M*K floats), and releases
+ * it with hipFreeAsync on `stream` after its last kernel, so calls on
+ * different streams never share one. The workspace comes from a memory pool
+ * the library creates per device on first use (hipMemPoolCreate; it keeps up
+ * to 64 MiB of freed workspace for reuse and lives until the process ends),
+ * or from the device's default pool if that creation failed. If the
+ * allocation fails the unsplit kernel runs instead (same result up to
+ * rounding order). Results are deterministic: the parts are added in a fixed
+ * order.
  * The LeetGPU signature (section "Problem Description", and every "Solution"
  * of the write-up) is solve(A, B, C, M, N, K) returning void; this form adds
  * the stream and a status.
