@@ -504,6 +504,46 @@ def test_runs_on_a_side_stream():
     assert_exact(gpu_gemm(A, B, stream=s), Cref, "side stream")
 
 
+def test_concurrent_calls_on_separate_streams():
+    # four host threads, each on its own stream, calling the library at once
+    # (ctypes releases the GIL): the per-device probe and workspace pool are
+    # shared, each split call's workspace is its own; exact on integer data
+    import threading
+
+    shapes = [(128, 65536, 64), (4, 100000, 96), (300, 500, 260), (16, 65536, 64)]
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = synth.make_inputs(M, N, K, "integer", seed=30 + i)
+        Cref, _ = oracle.gemm(A, B)
+        cases.append((M, N, K, torch.from_numpy(A.ravel()).to(DEV), torch.from_numpy(B.ravel()).to(DEV), Cref))
+    torch.cuda.synchronize()
+    results, errors = [None] * len(cases), []
+
+    def work(i):
+        try:
+            M, N, K, dA, dB, _ = cases[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [torch.full((M * K,), float("nan"), device=DEV) for _ in range(8)]
+                for dC in outs:
+                    fgr.solve(dA, dB, dC, M, N, K, stream=s)
+            s.synchronize()
+            results[i] = [o.cpu().numpy().reshape(M, K) for o in outs]
+        except Exception as e:  # reported below, in the main thread
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i, (M, N, K, _, _, Cref) in enumerate(cases):
+        say(f"concurrent {M}x{N}x{K}: {fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]}")
+        for j, C in enumerate(results[i]):
+            assert_exact(C, Cref, f"{M}x{N}x{K} call {j}")
+
+
 def test_six_argument_form_uses_null_stream():
     A, B = synth.make_inputs(33, 40, 36, "eighths")
     Cref, _ = oracle.gemm(A, B)
