@@ -186,6 +186,10 @@ struct Choice {
   int tile;
 };
 
+// Reductions shorter than this (with at least one 64x64 tile per CU) take
+// register-staged 64x64 tiles (128x128 for unaligned rows with many tiles).
+constexpr int kShortReduction = 104;
+
 // Kernel choice by the number of output tiles the shape makes at each tile
 // size, relative to the CU count (measured on MI355X; see the design notes):
 // whole-device 256x256 tiles take the direct-copy kernel; shapes with few
@@ -196,13 +200,22 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
   const int64_t t256 = cdiv(M, 256) * cdiv(K, 256);
   const int64_t t128 = cdiv(M, 128) * cdiv(K, 128);
   const int64_t t64 = cdiv(M, 64) * cdiv(K, 64);
+  const bool vec = mfma_vec_ok(A, B, C, N, K);
+  if (N < kShortReduction && t64 >= cus && (vec || N < 64)) {
+    // A short reduction over many tiles: the time goes to writing C. Small
+    // register-staged tiles keep several workgroups per CU, so that one's
+    // stores overlap another's loads and MFMAs (measured, 8192 x N x 8192:
+    // 64x64 tiles 46 us at N = 16 vs 77 us with 256x256; 100 vs 112 us with
+    // the direct-copy kernel at N = 64; equal at N = 96; 4% slower at N = 112).
+    if (vec) return {FGR_PATH_MFMA_VEC, FGR_TILE_64};
+    return {FGR_PATH_MFMA_SCALAR, t128 >= 4 * cus ? FGR_TILE_128 : FGR_TILE_64};
+  }
   if (t256 >= cus && mfma_dma_ok(N)) {
     // a last, partial wave of at most tail_tiles(cus) tiles goes to the split kernel
     const int64_t rem = t256 % cus;
     if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
     return {FGR_PATH_MFMA_DMA, FGR_TILE_256};
   }
-  const bool vec = mfma_vec_ok(A, B, C, N, K);
   if (N >= 64) {
     // Fewer 256x256 tiles than CUs: tiles whose reduction is split over the
     // four waves of a workgroup (k-split), the largest that still gives every
@@ -226,16 +239,7 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     if (sp.tile == FGR_TILE_64) return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_64};
     return {vec ? FGR_PATH_MFMA_KSPLIT : FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
   }
-  // N < 64: no direct copies
-  if (vec) {
-    if (t256 >= cus) return {FGR_PATH_MFMA_VEC, FGR_TILE_256};
-    if (t64 < cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
-    if (t64 < 2 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_64};
-    if (t64 < 4 * cus) return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
-    return {FGR_PATH_MFMA_VEC, FGR_TILE_64};
-  }
-  if (t128 >= 4 * cus) return {FGR_PATH_MFMA_SCALAR, FGR_TILE_128};
-  if (t64 >= 2 * cus) return {FGR_PATH_MFMA_SCALAR, FGR_TILE_64};
+  // N < 64 with fewer 64x64 tiles than CUs: the split kernel's 32x32 tiles
   return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
 }
 

@@ -153,7 +153,7 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4096, 60, 4096) == fgr.PATH_MFMA_VEC  # N < 64
     # a last partial wave of at most 176 tiles of 256x256 goes to the split kernel
     assert sp(A0, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 272 tiles
-    assert sp(A0, B0, C0, 65792, 64, 256) == fgr.PATH_MFMA_DMA_TAIL  # 257 tiles
+    assert sp(A0, B0, C0, 65792, 128, 256) == fgr.PATH_MFMA_DMA_TAIL  # 257 tiles
     assert sp(A0, B0, C0, 4096, 4096, 6144) == fgr.PATH_MFMA_DMA_TAIL  # 384 tiles
     assert sp(A0, B0, C0, 4096, 4096, 6656) == fgr.PATH_MFMA_DMA_TAIL  # 416 tiles: 160 left over
     assert sp(A0, B0, C0, 4096, 4096, 7168) == fgr.PATH_MFMA_DMA  # 448 tiles: 192 left over
@@ -211,8 +211,25 @@ def test_split_path_choices():
     assert sp(A0, B0, C0, 300, 500, 261) == fgr.PATH_MFMA_SPLIT  # unaligned, few tiles: split 32
     # N < 64: the register-staged and split kernels
     assert sp(A0, B0, C0, 2048, 60, 2048) == fgr.PATH_MFMA_VEC
-    assert sp(A0, B0, C0, 1024, 60, 1024) == fgr.PATH_MFMA_SPLIT
+    assert sp(A0, B0, C0, 1024, 60, 1024) == fgr.PATH_MFMA_VEC  # 256 tiles of 64
+    assert sp(A0, B0, C0, 512, 60, 512) == fgr.PATH_MFMA_SPLIT  # 64 tiles of 64
     assert sp(A0, B0, C0, 2047, 61, 2051) == fgr.PATH_MFMA_SCALAR
+
+
+def test_short_reduction_choices():
+    sp, st = fgr.select_path, fgr.select_tile
+    # N < 104 with a 64x64 tile per CU: register-staged 64x64 tiles (the
+    # work is writing C), even where 256x256 tiles would fill the device
+    for shape in [(8192, 16, 8192), (8192, 64, 8192), (4096, 100, 4096), (65792, 64, 256), (1024, 8, 1024)]:
+        assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_VEC, shape
+        assert st(A0, B0, C0, *shape) == 64, shape
+    assert sp(A0, B0, C0, 8192, 104, 8192) == fgr.PATH_MFMA_DMA
+    # unaligned rows: 32-bit loads, 128x128 tiles when there are many
+    assert sp(A0, B0, C0, 8191, 17, 8191) == fgr.PATH_MFMA_SCALAR
+    assert st(A0, B0, C0, 8191, 17, 8191) == 128
+    assert st(A0, B0, C0, 1023, 33, 1025) == 64
+    # unaligned rows with N >= 64 keep the direct-copy kernel (4-byte copies)
+    assert sp(A0, B0, C0, 8191, 65, 8191) == fgr.PATH_MFMA_DMA
 
 
 def test_split_reduction_choices():

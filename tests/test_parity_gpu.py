@@ -263,10 +263,10 @@ def test_large_ragged_sampled(shape):
 
 
 @pytest.mark.parametrize("shape,path,tile", [
-    ((2048, 64, 2048), fgr.PATH_MFMA_KSPLIT, 128), ((2040, 1000, 2044), fgr.PATH_MFMA_KSPLIT, 128),
-    ((2176, 72, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128), ((3072, 68, 3076), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
+    ((2048, 128, 2048), fgr.PATH_MFMA_KSPLIT, 128), ((2040, 1000, 2044), fgr.PATH_MFMA_KSPLIT, 128),
+    ((2176, 136, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128), ((3072, 132, 3076), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
     ((1024, 200, 1024), fgr.PATH_MFMA_KSPLIT, 64), ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
-    ((1536, 100, 1540), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((509, 300, 515), fgr.PATH_MFMA_SPLIT, 32),
+    ((1536, 104, 1540), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((509, 300, 515), fgr.PATH_MFMA_SPLIT, 32),
     ((512, 128, 512), fgr.PATH_MFMA_KSPLIT, 32),
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_ksplit_exact(shape, path, tile):
@@ -363,7 +363,7 @@ def test_vector_alu_path_timed_shape_sampled():
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], "vector ALU sampled")
 
 
-@pytest.mark.parametrize("shape", [(4352, 64, 4096), (4100, 68, 4100), (2304, 100, 8192), (65792, 64, 256)],
+@pytest.mark.parametrize("shape", [(4352, 112, 4096), (4100, 104, 4100), (2304, 108, 8192), (65792, 128, 256)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_partial_last_wave_exact(shape):
     # one or more whole waves of 256x256 tiles on the direct-copy kernel, the
@@ -377,6 +377,28 @@ def test_partial_last_wave_exact(shape):
     say(f"partial last wave {shape}: GPU")
     assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto (tail split)")
     assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256), Cref, f"{shape} direct-copy only")
+
+
+@pytest.mark.parametrize("shape,path,tile", [
+    ((4352, 64, 4096), fgr.PATH_MFMA_VEC, 64), ((4100, 68, 4100), fgr.PATH_MFMA_VEC, 64),
+    ((2304, 100, 8192), fgr.PATH_MFMA_VEC, 64), ((8191, 17, 8191), fgr.PATH_MFMA_SCALAR, 128),
+    ((1023, 33, 1025), fgr.PATH_MFMA_SCALAR, 64), ((4096, 4, 4096), fgr.PATH_MFMA_VEC, 64),
+    ((4096, 1, 4096), fgr.PATH_MFMA_SCALAR, 128)],
+    ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_short_reduction_exact(shape, path, tile):
+    # short reductions over many tiles take register-staged 64x64 (or, for
+    # unaligned rows, 128x128) tiles; exact on integer data, and the same bits
+    # as the direct-copy kernel where that can run
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=18)
+    say(f"short reduction {shape}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == path
+    assert fgr.select_tile(1 << 40, 2 << 40, 3 << 40, M, N, K) == tile
+    say(f"short reduction {shape}: GPU")
+    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
+    if N >= 64:
+        assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256), Cref, f"{shape} direct copies")
 
 
 @pytest.mark.parametrize("M", [2, 3, 5, 8])
