@@ -105,7 +105,7 @@ __device__ __forceinline__ void sched_spread() {
 template <class T>
 __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
-    int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W) {
+    int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact) {
   constexpr int S = T::S, BK = T::BK, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) float As0[T::kStage];
   __shared__ __attribute__((aligned(1024))) float As1[T::kStage];
@@ -137,19 +137,23 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int lg = lane >> 5;
   const int piece = wave * T::kPiece;  // this wave's offset inside every stage object
 
-  // Split across workgroups (parts > 1): the grid holds parts x (tiles)
-  // workgroups; logical id = part * tiles + tile, so that after the XCD
+  // The launch covers tiles [first, first + ntiles) of the grouped order.
+  // Split across workgroups (parts > 1): the grid holds parts x ntiles
+  // workgroups; logical id = part * ntiles + tile, so that after the XCD
   // renumbering the tiles of one part, which read the same reduction range of
   // A and B, run on the same XCD and share its L2. Part p owns the chunks
   // [nchunks p / parts, nchunks (p + 1) / parts) and writes its partial tile
-  // to W + p M K (row stride K) instead of C; a second kernel adds the parts.
-  // This wave's chunks are [c_begin, c_end) of the part's; at least 8 chunks
-  // per part give every wave >= 2.
+  // to the workspace W instead of C: at its place in a copy of C (W + p M K,
+  // row stride K) or, compact, to slot p ntiles + tile (BM x BN floats, row
+  // stride BN); a second kernel adds the parts. This wave's chunks are
+  // [c_begin, c_end) of the part's; at least 8 chunks per part give every
+  // wave >= 2.
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int ntiles = gridDim.x / parts;
   const int part = logical / ntiles;
+  const int tl = logical - part * ntiles;
   int tm, tn;
-  grouped_tile(logical - part * ntiles, tiles_m, tiles_n, group, tm, tn);
+  grouped_tile(first + tl, tiles_m, tiles_n, group, tm, tn);
   const int m0 = tm * T::BM;
   const int k0 = tn * BN;
 
@@ -160,7 +164,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int c_begin = pc0 + pn * wave / T::kWaves;
   const int c_end = pc0 + pn * (wave + 1) / T::kWaves;
   const int c_last = c_end - 1;
-  float* const Out = parts > 1 ? W + (int64_t)part * M * K : C;
 
   // Copy j of a wave fills floats [j * kBlock, (j + 1) * kBlock) of its piece;
   // lane L the kCopyFloats floats at position p = j * kBlock + L * kCopyFloats.
@@ -388,7 +391,18 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   take(true, false);
 
   if (wave * kSPW >= T::kSlices) return;  // small tiles: fewer slices than waves
-  float* const Ct = Out + (int64_t)m0 * K + k0;
+  float* Ct;
+  uint32_t ldc;
+  if (parts == 1) {
+    Ct = C + (int64_t)m0 * K + k0;
+    ldc = (uint32_t)K;
+  } else if (compact) {
+    Ct = W + ((int64_t)part * ntiles + tl) * (T::BM * BN);
+    ldc = BN;
+  } else {
+    Ct = W + (int64_t)part * M * K + (int64_t)m0 * K + k0;
+    ldc = (uint32_t)K;
+  }
   if constexpr (T::VEC && kSPW == T::kCB && T::kCB == 4) {
     // a whole block row: 4 adjacent columns per lane and row
     const int col = 4 * li;
@@ -397,7 +411,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     for (int rr = 0; rr < 16; ++rr) {
       const int row = wave * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
       if (col_ok && m0 + row < M) {
-        float* dst = Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col;
+        float* dst = Ct + (uint32_t)row * ldc + (uint32_t)col;
         *reinterpret_cast<float4*>(dst) = make_float4(sum[0][rr], sum[1][rr], sum[2][rr], sum[3][rr]);
       }
     }
@@ -410,7 +424,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int row = i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
-        if (k0 + col < K && m0 + row < M) Ct[(uint32_t)row * (uint32_t)K + (uint32_t)col] = sum[u][rr];
+        if (k0 + col < K && m0 + row < M) Ct[(uint32_t)row * ldc + (uint32_t)col] = sum[u][rr];
       }
     }
   }

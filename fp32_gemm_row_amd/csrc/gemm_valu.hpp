@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kValuThreads) void gemm_valu_kernel(const float* __
       const int n = n0 + a_n[j];
       if constexpr (T::VEC) {
         // N % 4 == 0: the four indices are all inside or all outside
-        ra[j] = a_row_ok[j] && n < N ? *reinterpret_cast<const float4*>(a_src[j] + n0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ra[j] = a_row_ok[j] && n < N ? *reinterpret_cast<const float4*>(a_src[j] + n0)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
       } else {
         const float* p = a_src[j] + n0;
         ra[j].x = a_row_ok[j] && n < N ? p[0] : 0.f;

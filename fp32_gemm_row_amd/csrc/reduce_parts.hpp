@@ -15,6 +15,8 @@
 
 #include <type_traits>
 
+#include "gemm_mfma.hpp"  // grouped_tile
+
 namespace fgr {
 
 constexpr int kReduceThreads = 256;
@@ -62,6 +64,36 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_parts_kernel(const floa
     for (int q = 1; q < slices; ++q) r = add_vec(r, run_sum[q * opw + o]);
     c[i] = r;
   }
+}
+
+// The same for partial tiles in compact slots: tiles [first, first + count)
+// of a tiles_m x tiles_n grid of BT x BT tiles in the grouped order, part p of
+// tile t in slot p count + t (BT x BT floats, row stride BT). Block (x, t)
+// covers 256 elements of tile t; each thread adds the parts of one element
+// in part order, four loads in flight, and stores it if it lies in C.
+template <int BT>
+__global__ __launch_bounds__(kReduceThreads) void reduce_tiles_kernel(const float* __restrict__ W,
+                                                                      float* __restrict__ C, int M, int K,
+                                                                      int parts, int tiles_m, int tiles_n,
+                                                                      int group, int first, int count) {
+  static_assert(BT * BT % kReduceThreads == 0, "whole blocks per tile");
+  const int t = blockIdx.y;
+  const int e = blockIdx.x * kReduceThreads + threadIdx.x;
+  int tm, tn;
+  grouped_tile(first + t, tiles_m, tiles_n, group, tm, tn);
+  const int row = tm * BT + e / BT;
+  const int col = tn * BT + e % BT;
+  if (row >= M || col >= K) return;
+  const int64_t stride = (int64_t)count * BT * BT;
+  const float* w = W + (int64_t)t * BT * BT + e;
+  float acc = w[0];
+  int p = 1;
+  for (; p + 4 <= parts; p += 4) {
+    const float a = w[p * stride], b = w[(p + 1) * stride], d = w[(p + 2) * stride], f = w[(p + 3) * stride];
+    acc = (((acc + a) + b) + d) + f;
+  }
+  for (; p < parts; ++p) acc += w[p * stride];
+  C[(int64_t)row * K + col] = acc;
 }
 
 }  // namespace fgr

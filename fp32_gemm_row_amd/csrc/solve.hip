@@ -320,9 +320,9 @@ hipMemPool_t workspace_pool() {
   return d.pool;
 }
 
-int alloc_parts(PartsWorkspace& ws, int parts, int M, int K, hipStream_t s) {
+int alloc_floats(PartsWorkspace& ws, size_t floats, hipStream_t s) {
   ws.s = s;
-  const size_t bytes = (size_t)parts * (size_t)M * (size_t)K * sizeof(float);
+  const size_t bytes = floats * sizeof(float);
   hipMemPool_t pool = workspace_pool();
   const hipError_t e = pool ? hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws.w), bytes, pool, s)
                             : hipMallocAsync(reinterpret_cast<void**>(&ws.w), bytes, s);
@@ -466,31 +466,53 @@ using Ksplit32s = fgr::KsplitConfig<32, 4, false>;
 
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
-                      int parts, float* W) {
+                      int parts, float* W, int first, int compact) {
   int tiles_m = (int)cdiv(M, Cfg::BM);
   int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
-  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &parts, &W};
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &parts, &W, &first, &compact};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
                 (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts, Cfg::kThreads, args, s);
 }
 
-// The k-split kernel with tile x tile tiles over the first `count` tiles of
-// the grouped order (count < 0: all of them); 16-byte copies when the rows
+// The k-split kernel with tile x tile tiles over tiles [first, first + count)
+// of the grouped order (count < 0: all of them); 16-byte copies when the rows
 // allow them. parts > 1: each tile's reduction also split over `parts`
-// workgroups writing partial tiles to W.
+// workgroups writing partial tiles to W (at their place in copies of C, or in
+// compact per-tile slots).
 int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
-                  hipStream_t s, int parts = 1, float* W = nullptr) {
+                  hipStream_t s, int parts = 1, float* W = nullptr, int first = 0, int compact = 0) {
   const bool vec = mfma_vec_ok(A, B, C, N, K);
   switch (tile) {
     case FGR_TILE_128:
-      return vec ? launch_ksplit_cfg<Ksplit128>(A, B, C, M, N, K, count, s, parts, W) : FGR_ERR_BAD_PATH;
+      return vec ? launch_ksplit_cfg<Ksplit128>(A, B, C, M, N, K, count, s, parts, W, first, compact)
+                 : FGR_ERR_BAD_PATH;
     case FGR_TILE_64:
-      return vec ? launch_ksplit_cfg<Ksplit64>(A, B, C, M, N, K, count, s, parts, W)
-                 : launch_ksplit_cfg<Ksplit64s>(A, B, C, M, N, K, count, s, parts, W);
+      return vec ? launch_ksplit_cfg<Ksplit64>(A, B, C, M, N, K, count, s, parts, W, first, compact)
+                 : launch_ksplit_cfg<Ksplit64s>(A, B, C, M, N, K, count, s, parts, W, first, compact);
     case FGR_TILE_32:
-      return vec ? launch_ksplit_cfg<Ksplit32>(A, B, C, M, N, K, count, s, parts, W)
-                 : launch_ksplit_cfg<Ksplit32s>(A, B, C, M, N, K, count, s, parts, W);
+      return vec ? launch_ksplit_cfg<Ksplit32>(A, B, C, M, N, K, count, s, parts, W, first, compact)
+                 : launch_ksplit_cfg<Ksplit32s>(A, B, C, M, N, K, count, s, parts, W, first, compact);
+    default: return FGR_ERR_BAD_PATH;
+  }
+}
+
+// Sum of compact partial tiles (tiles [first, first + count) of the grouped
+// order, tile x tile each) into C.
+int launch_reduce_tiles(const float* W, float* C, int M, int K, int tile, int parts, int first, int count,
+                        hipStream_t s) {
+  int tiles_m = (int)cdiv(M, tile);
+  int tiles_n = (int)cdiv(K, tile);
+  int group = kTileGroup;
+  void* args[] = {&W, &C, &M, &K, &parts, &tiles_m, &tiles_n, &group, &first, &count};
+  const int64_t blocks = (int64_t)tile * tile / fgr::kReduceThreads;
+  switch (tile) {
+    case FGR_TILE_128:
+      return launch(reinterpret_cast<const void*>(&fgr::reduce_tiles_kernel<128>), blocks, fgr::kReduceThreads,
+                    args, s, count);
+    case FGR_TILE_64:
+      return launch(reinterpret_cast<const void*>(&fgr::reduce_tiles_kernel<64>), blocks, fgr::kReduceThreads,
+                    args, s, count);
     default: return FGR_ERR_BAD_PATH;
   }
 }
@@ -505,14 +527,18 @@ int launch_ksplit_parts(int tile, const float* A, const float* B, float* C, int 
                         hipStream_t s) {
   const int parts = splitk_plan_tile(tile, M, N, K, cus).parts;  // >= 2; N >= 128 gives 8 chunks per part
   PartsWorkspace ws;
-  if (alloc_parts(ws, parts, M, K, s) != FGR_OK) return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
+  if (alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) != FGR_OK)
+    return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
   const int rc = launch_ksplit(tile, A, B, C, M, N, K, -1, s, parts, ws.w);
   if (rc != FGR_OK) return rc;
   return launch_reduce_parts(ws.w, C, M, K, parts, vec4_rows(C, M, K), s);
 }
 
+constexpr int kTailSplitMinN = 4096;
+
 // Whole waves of tile x tile tiles on the k-split kernel, the last partial
-// wave's tiles cut into smaller split-reduction tiles (as launch_dma_tail).
+// wave's tiles cut into smaller split-reduction tiles (as launch_dma_tail) or,
+// for long reductions, their reduction split across workgroups.
 int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
                        hipStream_t s) {
   const int64_t tiles = cdiv(M, tile) * cdiv(K, tile);
@@ -523,6 +549,22 @@ int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M
     if (rc != FGR_OK || rem == 0) return rc;
   }
   if (full > INT_MAX || rem > INT_MAX / 16) return FGR_ERR_BAD_DIMS;
+  // With a long reduction the tail tiles' reduction is split over up to
+  // CUs / rem parts (so every CU gets a workgroup), through compact per-tile
+  // slots; otherwise, or without a workspace, the tail is cut into smaller
+  // tiles of the split kernel. Measured on MI355X (us per call, split kernel
+  // tail vs split reduction): 1023 x 4097 x 1027 132 vs 114, 1536 x 16384 x
+  // 1536 680 vs 630; but 2047^3 equal, 3072^3 446 vs 456, 1023 x 1025 x 1027
+  // 45 vs 48 (three launches and the workspace cost more than they save).
+  const int parts = N >= kTailSplitMinN ? (int)std::min<int64_t>(cus / rem, cdiv(N, 8) / 8) : 1;
+  if (parts >= 2 && rem <= 65535) {
+    PartsWorkspace ws;
+    if (alloc_floats(ws, (size_t)parts * (size_t)rem * tile * tile, s) == FGR_OK) {
+      const int rc = launch_ksplit(tile, A, B, C, M, N, K, rem, s, parts, ws.w, (int)full, 1);
+      if (rc != FGR_OK) return rc;
+      return launch_reduce_tiles(ws.w, C, M, K, tile, parts, (int)full, (int)rem, s);
+    }
+  }
   const bool vec = mfma_vec_ok(A, B, C, N, K);
   if (tile == FGR_TILE_128)
     return vec ? launch_split_tail<128, true>(A, B, C, M, N, K, full, rem, cus, s) : FGR_ERR_BAD_PATH;
@@ -579,7 +621,7 @@ template <int VW>
 int launch_gemv(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
   const int parts = gemv_parts(cdiv(K, fgr::kGemvCols), N, cus);
   PartsWorkspace ws;
-  if (parts < 2 || alloc_parts(ws, parts, M, K, s) != FGR_OK)
+  if (parts < 2 || alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) != FGR_OK)
     return launch_gemv_parts<VW>(A, B, C, M, N, K, 1, nullptr, s);
   const int rc = launch_gemv_parts<VW>(A, B, C, M, N, K, parts, ws.w, s);
   if (rc != FGR_OK) return rc;

@@ -268,6 +268,9 @@ def test_large_ragged_sampled(shape):
     ((1024, 200, 1024), fgr.PATH_MFMA_KSPLIT, 64), ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
     ((1536, 104, 1540), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((509, 300, 515), fgr.PATH_MFMA_SPLIT, 32),
     ((512, 128, 512), fgr.PATH_MFMA_KSPLIT, 32),
+    # long reductions: the tail tiles' reduction split across workgroups
+    ((1023, 4097, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((2176, 4096, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
+    ((1088, 4100, 1024), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_ksplit_exact(shape, path, tile):
     # tiles whose reduction is split over a workgroup's waves (128, 64 or 32
