@@ -349,10 +349,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
-  // Epilogue. Offsets are 32-bit from the tile's corner, a wave-uniform base,
-  // which keeps the address arithmetic small. With 16-byte rows (K % 4 == 0)
-  // a lane's 4 adjacent columns start at a multiple of 4, so they are wholly
-  // inside or outside; otherwise each column is guarded and stored alone.
+  // Epilogue. Offsets from the tile's corner (a wave-uniform base) are
+  // row * K + col, 64-bit: 256 rows of a K beyond 2^24 already pass 2^32.
+  // With 16-byte rows (K % 4 == 0) a lane's 4 adjacent columns start at a
+  // multiple of 4, so they are wholly inside or outside; otherwise each column
+  // is guarded and stored alone.
   float* const Ct = C + (int64_t)m0 * K + k0;
   const int col = wn * T::kWaveN + 4 * li;
   const bool col_ok = k0 + col < K;
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     for (int rr = 0; rr < 16; ++rr) {
       const int row = wm * T::kWaveM + i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
       if (col_ok && m0 + row < M) {
-        float* dst = Ct + (uint32_t)row * (uint32_t)K + (uint32_t)col;
+        float* dst = Ct + (uint64_t)row * (uint32_t)K + (uint32_t)col;
         if constexpr (T::VEC) {
           *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0][rr], acc[i][1][rr], acc[i][2][rr], acc[i][3][rr]);
         } else {

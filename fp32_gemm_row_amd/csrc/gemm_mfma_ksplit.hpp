@@ -392,7 +392,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
 
   if (wave * kSPW >= T::kSlices) return;  // small tiles: fewer slices than waves
   float* Ct;
-  uint32_t ldc;
+  uint32_t ldc;  // row stride; row * ldc is formed in 64 bits (K may pass 2^25)
   if (parts == 1) {
     Ct = C + (int64_t)m0 * K + k0;
     ldc = (uint32_t)K;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     for (int rr = 0; rr < 16; ++rr) {
       const int row = wave * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
       if (col_ok && m0 + row < M) {
-        float* dst = Ct + (uint32_t)row * ldc + (uint32_t)col;
+        float* dst = Ct + (uint64_t)row * ldc + (uint32_t)col;
         *reinterpret_cast<float4*>(dst) = make_float4(sum[0][rr], sum[1][rr], sum[2][rr], sum[3][rr]);
       }
     }
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int row = i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
-        if (k0 + col < K && m0 + row < M) Ct[(uint32_t)row * ldc + (uint32_t)col] = sum[u][rr];
+        if (k0 + col < K && m0 + row < M) Ct[(uint64_t)row * ldc + (uint32_t)col] = sum[u][rr];
       }
     }
   }

@@ -500,6 +500,33 @@ def test_algebraic_invariants(shape):
     assert_exact(gpu_gemm(np.ascontiguousarray(A[:m1]), B), Cref[:m1], f"{shape} rows [0, {m1})")
 
 
+def test_output_offsets_past_32_bits():
+    # 256 rows of a 17,000,004-column C: row * K passes 2^32 inside a tile, so
+    # the store offsets must be 64-bit (C alone is 17.4 GB, B 8.7 GB); integer
+    # inputs, exact at sampled outputs (the last rows and columns included)
+    M, N, K = 256, 128, 17_000_004
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(21)
+    say("offsets past 2^32: inputs")
+    dA = torch.randint(-4, 5, (M * N,), device=DEV, generator=gen).float()
+    dB = torch.randint(-4, 5, (N * K,), device=DEV, generator=gen).float()
+    dC = torch.full((M * K,), float("nan"), device=DEV)
+    torch.cuda.synchronize()
+    say(f"offsets past 2^32: GPU ({fgr.PATH_NAMES[fgr.select_path(dA, dB, dC, M, N, K)]})")
+    fgr.solve(dA, dB, dC, M, N, K)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(22)
+    rows = np.concatenate([np.array([255, 255, 254, 0, 128, 255]), rng.integers(0, M, 2000)])
+    cols = np.concatenate([np.array([K - 1, K - 4, K - 1, K - 1, 16_777_217, 0]), rng.integers(0, K, 2000)])
+    got = dC.view(M, K)[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].cpu().numpy()
+    del dC
+    say("offsets past 2^32: oracle at sampled outputs")
+    A = dA.cpu().numpy().reshape(M, N)
+    B = dB.cpu().numpy().reshape(N, K)
+    Cref, _ = oracle.gemm_at(A, B, rows, cols)
+    assert_exact(got[None, :], Cref[None, :], "K = 17,000,004 sampled")
+
+
 def test_single_product_reduction_is_exact():
     # N = 1: C[m,k] = a * b, one product (the padding adds exact zeros)
     rng = np.random.default_rng(1)
