@@ -61,6 +61,7 @@ TILE_256 = 256
 TILE_128 = 128
 TILE_64 = 64
 TILE_32 = 32
+TILE_32X128 = 32128
 
 # Every symbol the header declares.
 EXPORTS = (

@@ -46,31 +46,39 @@
 
 namespace fgr {
 
-template <int BM_, int S_, bool VEC_>
+// BM x BN tiles (BN defaults to BM; BM = 32 with BN = 128 is the skinny
+// tile: few output rows, wide column blocks of B per workgroup).
+template <int BM_, int S_, bool VEC_, int BN_ = BM_>
 struct KsplitConfig {
-  static constexpr int BM = BM_, BN = BM_, BK = 8, S = S_;
+  static constexpr int BM = BM_, BN = BN_, BK = 8, S = S_;
   static constexpr bool VEC = VEC_;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRB = BM / 32, kCB = BN / 32;
   static constexpr int kCopyFloats = VEC ? 4 : 1;  // floats per lane per copy
   static constexpr int kBlock = 64 * kCopyFloats;  // floats one copy fills
-  static constexpr int kPiece = BM * BK;           // floats of one wave's A (or B) stage
-  static constexpr int kACopies = kPiece / kBlock;  // per wave per chunk
-  static constexpr int kBCopies = kPiece / kBlock;
+  static constexpr int kPieceA = BM * BK;          // floats of one wave's A stage
+  static constexpr int kPieceB = BK * BN;          // floats of one wave's B stage
+  static constexpr int kACopies = kPieceA / kBlock;  // per wave per chunk
+  static constexpr int kBCopies = kPieceB / kBlock;
   static constexpr int kCopies = kACopies + kBCopies;
-  static constexpr int kStage = kWaves * kPiece;  // floats of one LDS stage object
+  static constexpr int kStageA = kWaves * kPieceA;  // floats of one LDS stage object of A
+  static constexpr int kStageB = kWaves * kPieceB;
   // the reduction: a slice is one MFMA block's 16 accumulators of every lane
   static constexpr int kSlices = kRB * kCB;
-  static constexpr int kSlicesPerObj = kStage / 1024;
+  static constexpr int kSlicesPerObjA = kStageA / 1024;
+  static constexpr int kSlicesPerObjB = kStageB / 1024;
   static constexpr int kSlicesPerWave = kSlices >= kWaves ? kSlices / kWaves : 1;
 
-  static_assert(BM == 32 || BM == 64 || BM == 128, "tile of 32, 64 or 128");
-  static_assert(kPiece % kBlock == 0 && BN % kCopyFloats == 0, "copies cover whole pieces");
+  static_assert((BM == BN && (BM == 32 || BM == 64 || BM == 128)) || (BM == 32 && BN == 128),
+                "square tiles of 32, 64 or 128, or 32 x 128");
+  static_assert(kPieceA % kBlock == 0 && kPieceB % kBlock == 0 && BN % kCopyFloats == 0,
+                "copies cover whole pieces");
   static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");
   static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
-  static_assert(2 * S * kStage * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
-  static_assert(kSlices <= S * kSlicesPerObj, "a partial tile fits in the stage objects of one operand");
+  static_assert(S * (kStageA + kStageB) * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+  static_assert(kSlices <= S * kSlicesPerObjA && kSlices <= S * kSlicesPerObjB,
+                "a partial tile fits in the stage objects of either operand");
 };
 
 __device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
@@ -107,14 +115,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
     int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact) {
   constexpr int S = T::S, BK = T::BK, BN = T::BN;
-  __shared__ __attribute__((aligned(1024))) float As0[T::kStage];
-  __shared__ __attribute__((aligned(1024))) float As1[T::kStage];
-  __shared__ __attribute__((aligned(1024))) float As2[T::kStage];
-  __shared__ __attribute__((aligned(1024))) float As3[T::kStage];
-  __shared__ __attribute__((aligned(1024))) float Bs0[T::kStage];
-  __shared__ __attribute__((aligned(1024))) float Bs1[T::kStage];
-  __shared__ __attribute__((aligned(1024))) float Bs2[T::kStage];
-  __shared__ __attribute__((aligned(1024))) float Bs3[T::kStage];
+  __shared__ __attribute__((aligned(1024))) float As0[T::kStageA];
+  __shared__ __attribute__((aligned(1024))) float As1[T::kStageA];
+  __shared__ __attribute__((aligned(1024))) float As2[T::kStageA];
+  __shared__ __attribute__((aligned(1024))) float As3[T::kStageA];
+  __shared__ __attribute__((aligned(1024))) float Bs0[T::kStageB];
+  __shared__ __attribute__((aligned(1024))) float Bs1[T::kStageB];
+  __shared__ __attribute__((aligned(1024))) float Bs2[T::kStageB];
+  __shared__ __attribute__((aligned(1024))) float Bs3[T::kStageB];
   auto a_stage = [&](auto sc) __attribute__((always_inline)) -> float* {
     constexpr int s = decltype(sc)::value;
     if constexpr (s == 0) return As0;
@@ -135,7 +143,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;
   const int lg = lane >> 5;
-  const int piece = wave * T::kPiece;  // this wave's offset inside every stage object
+  const int piece_a = wave * T::kPieceA;  // this wave's offset inside every A stage object
+  const int piece_b = wave * T::kPieceB;  // and B stage object
 
   // The launch covers tiles [first, first + ntiles) of the grouped order.
   // Split across workgroups (parts > 1): the grid holds parts x ntiles
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const int c = 4 * (((pos % BK) / 4) ^ a_swizzle2(r)) + pos % 4;
     const int row = m0 + r < M ? m0 + r : M - 1;
     a_src[j] = A + (int64_t)row * N + c;
-    a_dst[j] = piece + j * T::kBlock;
+    a_dst[j] = piece_a + j * T::kBlock;
     a_col[j] = c;
   }
   // In B, p is row p / BN, column p % BN (columns past K read the last column,
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const int r = pos / BN;
     const int c = k0 + pos % BN;
     b_src[j] = B + (int64_t)r * K + (c < K ? c : K - T::kCopyFloats);
-    b_dst[j] = piece + j * T::kBlock;
+    b_dst[j] = piece_b + j * T::kBlock;
     b_row[j] = r;
   }
 
@@ -214,10 +223,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // chain of address steps hides the stage object from the compiler, which
   // then waits for every copy in flight before the read. A: quad lg of row li
   // (+ 32 i), stored at position lg ^ swz(li) (the same swizzle for every i).
-  const int a_frag = piece + li * BK + 4 * (lg ^ a_swizzle2(li));
+  const int a_frag = piece_a + li * BK + 4 * (lg ^ a_swizzle2(li));
   // lane column li of MFMA column block j is output column kCB li + j (see the
   // direct-copy kernel): one read gives a lane's B operands of all blocks
-  const int b_frag = piece + 4 * lg * BN + T::kCB * li;
+  const int b_frag = piece_b + 4 * lg * BN + T::kCB * li;
   typedef typename FloatVec<T::kCB>::type BVec;
   auto read_frag = [&](Frag& f, const float* As, const float* Bs) __attribute__((always_inline)) {
 #pragma unroll
@@ -342,13 +351,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // barrier), two partials at a time, in the stage objects of A (waves 0, 2)
   // or of B (waves 1, 3). Slice t of a partial (MFMA block i = t / kCB,
   // j = t % kCB: 16 accumulators of every lane) lives in object
-  // t / kSlicesPerObj, lane-major as float4. Wave w sums and stores slices
+  // t / kSlicesPerObjA (or B), lane-major as float4. Wave w sums and stores slices
   // [w kSlicesPerWave, (w + 1) kSlicesPerWave) (at BM = 128: block row w).
   constexpr int kSPW = T::kSlicesPerWave;
   auto slice_ptr = [&](auto tc, bool use_b) __attribute__((always_inline)) -> float* {
     constexpr int t = decltype(tc)::value;
-    using O = std::integral_constant<int, t / T::kSlicesPerObj>;
-    return (use_b ? b_stage(O{}) : a_stage(O{})) + (t % T::kSlicesPerObj) * 1024 + 4 * lane;
+    using OA = std::integral_constant<int, t / T::kSlicesPerObjA>;
+    using OB = std::integral_constant<int, t / T::kSlicesPerObjB>;
+    return (use_b ? b_stage(OB{}) + (t % T::kSlicesPerObjB) * 1024 : a_stage(OA{}) + (t % T::kSlicesPerObjA) * 1024) +
+           4 * lane;
   };
   auto put = [&](bool use_b) __attribute__((always_inline)) {
     static_for<0, T::kSlices>([&](auto tc) {

@@ -181,6 +181,26 @@ SplitPlan splitk_plan(int M, int N, int K, int cus) {
   return best;
 }
 
+// Skinny outputs (kSkinnyMinM <= M <= 32, K >= 128, B of at least 32 MiB):
+// 32x128 k-split tiles, each reduction split into the largest power-of-two number of
+// parts that keeps tiles x parts within the CU count and parts at least 512
+// long. The work is streaming B once; wide column blocks and one workgroup
+// per CU measured best (MI355X, TB/s of algorithmic bytes, 32x128 tiles vs
+// the previous choice: 16 x 8192 x 28672 5.61 vs 3.43, 32 x 11008 x 4096 4.21
+// vs 2.56, 32 x 8192 x 8192 4.90 vs 3.25, 16 x 4096 x 4096 2.70 vs 1.99; and
+// at M = 5..8 against the matrix-vector kernel: 8 x 8192 x 28672 5.68 vs 3.61,
+// 8 x 65536 x 256 2.50 vs 1.10). With K < 128 half of a 128-column tile would
+// be padding (16 x 1048576 x 64: 3.57 vs 4.01 with 32x32 tiles).
+constexpr int kSkinnyMinM = 5;  // fewer rows: the matrix-vector kernel
+constexpr int kSkinnyMaxM = 32;
+constexpr int64_t kSkinnyMinB = int64_t(8) << 20;  // elements of B
+int skinny_parts(int M, int N, int K, int cus) {
+  const int64_t tiles = cdiv(M, 32) * cdiv(K, 128);
+  int p = 1;
+  while (tiles * p * 2 <= cus && N / (p * 2) >= 512) p *= 2;
+  return p;
+}
+
 struct Choice {
   int path;
   int tile;
@@ -196,7 +216,13 @@ constexpr int kShortReduction = 104;
 // tiles split each tile's reduction across a workgroup's waves.
 Choice choose(const float* A, const float* B, const float* C, int M, int N, int K, int cus) {
   if (cus <= 0) cus = kDefaultCus;
-  if (M <= fgr::kGemvMaxRows) return {gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR, FGR_TILE_AUTO};
+  const bool skinny = M >= kSkinnyMinM && M <= kSkinnyMaxM && N >= 64 && K >= 128 && (int64_t)N * K >= kSkinnyMinB;
+  if (M <= fgr::kGemvMaxRows && !skinny)
+    return {gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR, FGR_TILE_AUTO};
+  if (skinny) {
+    // skinny: stream B once in 32x128 tiles (see skinny_parts)
+    return {skinny_parts(M, N, K, cus) >= 2 ? FGR_PATH_MFMA_SPLITK : FGR_PATH_MFMA_KSPLIT, FGR_TILE_32X128};
+  }
   const int64_t t256 = cdiv(M, 256) * cdiv(K, 256);
   const int64_t t128 = cdiv(M, 128) * cdiv(K, 128);
   const int64_t t64 = cdiv(M, 64) * cdiv(K, 64);
@@ -463,6 +489,10 @@ using Ksplit64 = fgr::KsplitConfig<64, 4, true>;
 using Ksplit64s = fgr::KsplitConfig<64, 4, false>;
 using Ksplit32 = fgr::KsplitConfig<32, 4, true>;
 using Ksplit32s = fgr::KsplitConfig<32, 4, false>;
+// skinny outputs: 32 rows x 128 columns, so that each workgroup streams a
+// 512-byte-wide column block of B and A's rows are re-read a quarter as often
+using Ksplit32x128 = fgr::KsplitConfig<32, 4, true, 128>;
+using Ksplit32x128s = fgr::KsplitConfig<32, 4, false, 128>;
 
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
@@ -493,6 +523,9 @@ int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int
     case FGR_TILE_32:
       return vec ? launch_ksplit_cfg<Ksplit32>(A, B, C, M, N, K, count, s, parts, W, first, compact)
                  : launch_ksplit_cfg<Ksplit32s>(A, B, C, M, N, K, count, s, parts, W, first, compact);
+    case FGR_TILE_32X128:
+      return vec ? launch_ksplit_cfg<Ksplit32x128>(A, B, C, M, N, K, count, s, parts, W, first, compact)
+                 : launch_ksplit_cfg<Ksplit32x128s>(A, B, C, M, N, K, count, s, parts, W, first, compact);
     default: return FGR_ERR_BAD_PATH;
   }
 }
@@ -525,7 +558,8 @@ bool vec4_rows(const float* C, int M, int K) { return ((int64_t)M * K) % 4 == 0 
 // workspace (allocation failed) the tiles keep their whole reduction.
 int launch_ksplit_parts(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
                         hipStream_t s) {
-  const int parts = splitk_plan_tile(tile, M, N, K, cus).parts;  // >= 2; N >= 128 gives 8 chunks per part
+  int parts = tile == FGR_TILE_32X128 ? skinny_parts(M, N, K, cus) : splitk_plan_tile(tile, M, N, K, cus).parts;
+  if (parts < 2) parts = 2;  // N >= 128 gives 8 chunks per part
   PartsWorkspace ws;
   if (alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) != FGR_OK)
     return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
@@ -643,9 +677,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
-      // N >= 64; tiles of 128 (16-byte rows only) or 64, and 32 without the tail form
+      // N >= 64; tiles of 128 (16-byte rows only) or 64, and 32 or 32x128 without the tail form
       if (N < 64 || (tile == FGR_TILE_128 && !mfma_vec_ok(A, B, C, N, K)) || tile == FGR_TILE_256 ||
-          (tile == FGR_TILE_32 && path == FGR_PATH_MFMA_KSPLIT_TAIL))
+          ((tile == FGR_TILE_32 || tile == FGR_TILE_32X128) && path == FGR_PATH_MFMA_KSPLIT_TAIL))
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SPLITK:
@@ -669,8 +703,11 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     default: return FGR_ERR_BAD_PATH;
   }
   if (tile != FGR_TILE_AUTO && tile != FGR_TILE_256 && tile != FGR_TILE_128 && tile != FGR_TILE_64 &&
-      tile != FGR_TILE_32)
+      tile != FGR_TILE_32 && tile != FGR_TILE_32X128)
     return FGR_ERR_BAD_PATH;
+  if (tile == FGR_TILE_32X128 &&
+      (N < 64 || (path != FGR_PATH_MFMA_KSPLIT && path != FGR_PATH_MFMA_SPLITK && path != FGR_PATH_AUTO)))
+    return FGR_ERR_BAD_PATH;  // direct copies need N >= 64
   if (tile == FGR_TILE_32 && path != FGR_PATH_MFMA_SPLIT && path != FGR_PATH_MFMA_KSPLIT &&
       path != FGR_PATH_MFMA_SPLITK && path != FGR_PATH_AUTO)
     return FGR_ERR_BAD_PATH;
@@ -684,14 +721,16 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     if (tile == FGR_TILE_AUTO) {
       path = best.path;
       tile = best.tile;
-    } else if (M <= fgr::kGemvMaxRows) {
-      path = best.path;
+    } else if (best.path == FGR_PATH_GEMV_VEC || best.path == FGR_PATH_GEMV_SCALAR) {
+      path = best.path;  // the matrix-vector kernel has no tiles
     } else if (tile == best.tile && (best.path == FGR_PATH_MFMA_DMA || best.path == FGR_PATH_MFMA_DMA_TAIL ||
                                      best.path == FGR_PATH_MFMA_KSPLIT || best.path == FGR_PATH_MFMA_KSPLIT_TAIL ||
                                      best.path == FGR_PATH_MFMA_SPLITK || best.path == FGR_PATH_MFMA_SPLIT)) {
       path = best.path;  // the kernel the table picked for this tile
     } else if (tile == FGR_TILE_32) {
       path = FGR_PATH_MFMA_SPLIT;  // 32x32 tiles for any shape
+    } else if (tile == FGR_TILE_32X128) {
+      path = FGR_PATH_MFMA_KSPLIT;  // the only kernel with 32x128 tiles (N >= 64 checked above)
     } else {
       path = mfma_vec_ok(A, B, C, N, K) ? FGR_PATH_MFMA_VEC : FGR_PATH_MFMA_SCALAR;
     }

@@ -119,6 +119,8 @@ extern "C" {
 #define FGR_TILE_128 128
 #define FGR_TILE_64 64
 #define FGR_TILE_32 32 /* split and k-split paths only */
+#define FGR_TILE_32X128 32128 /* 32 rows x 128 columns: k-split paths only (MFMA_KSPLIT, MFMA_SPLITK);
+                                 the tile for skinny outputs (M <= 32) */
 
 /*
  * solve - C = A x B on `stream`.

@@ -132,6 +132,13 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, 256) == fgr.ERR_BAD_PATH
     for tile in (0, 128, 64, 32):
         assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, tile) == fgr.ERR_DEVICE
+    # 32x128 tiles exist on the k-split paths (not their tail form) only
+    assert call(lib, A0, B0, C0, 64, 128, 512, fgr.PATH_MFMA_KSPLIT, fgr.TILE_32X128) == fgr.ERR_DEVICE
+    assert call(lib, A0, B0, C0, 64, 128, 512, fgr.PATH_MFMA_SPLITK, fgr.TILE_32X128) == fgr.ERR_DEVICE
+    assert call(lib, A0, B0, C0, 64, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_32X128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 64, 128, 512, fgr.PATH_MFMA_VEC, fgr.TILE_32X128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 64, 60, 512, fgr.PATH_MFMA_KSPLIT, fgr.TILE_32X128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 64, 60, 512, 0, fgr.TILE_32X128) == fgr.ERR_BAD_PATH
     # the vector-ALU path takes any shape, tile 128 only
     assert call(lib, A0 + 4, B0, C0, 7, 5, 3, fgr.PATH_VALU) == fgr.ERR_DEVICE
     assert call(lib, A0, B0, C0, 64, 64, 64, fgr.PATH_VALU, 128) == fgr.ERR_DEVICE
@@ -175,9 +182,12 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 1, 3, 1) == fgr.PATH_GEMV_SCALAR
     assert sp(A0, B0 + 4, C0, 1, 8, 8) == fgr.PATH_GEMV_SCALAR
     assert sp(A0, B0, C0, 2, 8192, 8192) == fgr.PATH_GEMV_VEC  # skinny: B streamed once
-    assert sp(A0, B0, C0, 8, 8192, 8192) == fgr.PATH_GEMV_VEC
-    assert sp(A0, B0, C0, 8, 8192, 8190) == fgr.PATH_GEMV_SCALAR
-    assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_KSPLIT  # 32x32 k-split tiles
+    assert sp(A0, B0, C0, 4, 8192, 8192) == fgr.PATH_GEMV_VEC
+    assert sp(A0, B0, C0, 4, 8192, 8190) == fgr.PATH_GEMV_SCALAR
+    assert sp(A0, B0, C0, 8, 8192, 64) == fgr.PATH_GEMV_VEC  # K < 128: no 32x128 tiles
+    assert sp(A0, B0, C0, 8, 2048, 2048) == fgr.PATH_GEMV_VEC  # B under 32 MiB
+    assert sp(A0, B0, C0, 8, 8192, 8192) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles
+    assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_SPLITK
     assert sp(0, B0, C0, 1, 8, 8) == fgr.ERR_NULL_POINTER
 
 
@@ -232,6 +242,22 @@ def test_short_reduction_choices():
     assert sp(A0, B0, C0, 8191, 65, 8191) == fgr.PATH_MFMA_DMA
 
 
+def test_skinny_choices():
+    sp, st = fgr.select_path, fgr.select_tile
+    A0, B0, C0 = 1 << 40, 2 << 40, 3 << 40
+    # 5 <= M <= 32 with K >= 128 and B of at least 32 MiB: 32x128 tiles, the
+    # reduction split into the largest power of two of parts that keeps
+    # tiles x parts <= CUs and parts >= 512 long (none: the k-split path)
+    for shape, path in [((16, 4096, 4096), fgr.PATH_MFMA_SPLITK), ((32, 11008, 4096), fgr.PATH_MFMA_SPLITK),
+                        ((5, 65536, 256), fgr.PATH_MFMA_SPLITK), ((8, 8192, 28672), fgr.PATH_MFMA_KSPLIT),
+                        ((32, 4097, 4099), fgr.PATH_MFMA_SPLITK), ((16, 512, 65536), fgr.PATH_MFMA_KSPLIT)]:
+        assert sp(A0, B0, C0, *shape) == path, shape
+        assert st(A0, B0, C0, *shape) == fgr.TILE_32X128, shape
+    assert sp(A0, B0, C0, 4, 8192, 8192) == fgr.PATH_GEMV_VEC  # M < 5: the matrix-vector kernel
+    assert st(A0, B0, C0, 33, 8192, 8192) == 32  # M > 32: the few-tile rules
+    assert st(A0, B0, C0, 16, 1048576, 64) == 32  # K < 128
+
+
 def test_split_reduction_choices():
     sp, st = fgr.select_path, fgr.select_tile
     A0, B0, C0 = 1 << 40, 2 << 40, 3 << 40  # room for the long operands
@@ -239,8 +265,8 @@ def test_split_reduction_choices():
     # across workgroups; 64x64 tiles for tall outputs, 32x32 for skinny ones
     # (less padding), by the time estimate
     for shape, tile in [((256, 65536, 256), 64), ((128, 262144, 128), 64), ((64, 65536, 1024), 64),
-                        ((512, 65536, 512), 64), ((16, 1048576, 64), 32), ((24, 65536, 1024), 32),
-                        ((16, 16384, 4096), 32), ((130, 20000, 66), 32)]:
+                        ((512, 65536, 512), 64), ((16, 1048576, 64), 32), ((130, 20000, 66), 32),
+                        ((24, 65536, 1024), fgr.TILE_32X128), ((16, 16384, 4096), fgr.TILE_32X128)]:
         assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
         assert st(A0, B0, C0, *shape) == tile, shape
         assert sp(A0 + 4, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape  # 4-byte copies too
@@ -248,7 +274,7 @@ def test_split_reduction_choices():
     assert sp(A0, B0, C0, 512, 8192, 512) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 200, 2048, 200) == fgr.PATH_MFMA_KSPLIT
-    assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 33, 8192, 8192) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 100, 64) == fgr.PATH_MFMA_KSPLIT
     # tiles enough for every CU: the whole-device kernels, never a split
     assert sp(A0, B0, C0, 1024, 32768, 1024) == fgr.PATH_MFMA_KSPLIT

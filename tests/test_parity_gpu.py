@@ -103,9 +103,11 @@ def paths_for(M, N, K):
     if N % 4 == 0 and K % 4 == 0 and N >= 64:
         out.append((fgr.PATH_MFMA_KSPLIT, fgr.TILE_128))
         out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128))
+    if N >= 64:
+        out.append((fgr.PATH_MFMA_KSPLIT, fgr.TILE_32X128))
     if N >= 128:
         # the reduction also split across workgroups (two parts at least)
-        for tile in (fgr.TILE_64, fgr.TILE_32):
+        for tile in (fgr.TILE_64, fgr.TILE_32, fgr.TILE_32X128):
             out.append((fgr.PATH_MFMA_SPLITK, tile))
         if N % 4 == 0 and K % 4 == 0:
             out.append((fgr.PATH_MFMA_SPLITK, fgr.TILE_128))
@@ -311,7 +313,7 @@ def test_split_reduction_exact(shape, tile):
     assert_exact(gpu_gemm(A, B, offsets=(1, 1, 1)), Cref, f"{shape} 4-byte aligned")
 
 
-@pytest.mark.parametrize("shape", [(1, 262144, 64), (8, 131072, 256), (5, 100003, 33), (3, 65536, 1000)],
+@pytest.mark.parametrize("shape", [(1, 262144, 64), (4, 131072, 256), (5, 100003, 33), (3, 65536, 1000)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_split_matrix_vector_exact(shape):
     # matrix-vector and skinny products with few 32-column blocks: rows of B
@@ -404,17 +406,44 @@ def test_short_reduction_exact(shape, path, tile):
         assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256), Cref, f"{shape} direct copies")
 
 
-@pytest.mark.parametrize("M", [2, 3, 5, 8])
+@pytest.mark.parametrize("M", [2, 3, 5, 8, 16, 32])
 def test_skinny_products_full_compare(M):
-    # M rows of A against a 8192 x 8192 B: one pass over B for all rows
+    # M rows of A against a 8192 x 8192 B: one pass over B for all rows (the
+    # matrix-vector kernel for M <= 4, 32x128 k-split tiles from M = 5)
     N = K = 8192
     A, B = synth.make_inputs(M, N, K, "uniform", seed=20 + M)
     say(f"skinny M={M}: oracle")
     Cref, S = oracle.gemm(A, B)
-    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_GEMV_VEC
+    expect = fgr.PATH_GEMV_VEC if M < 5 else fgr.PATH_MFMA_SPLITK
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == expect
     say(f"skinny M={M}: GPU")
     assert_within_tolerance(gpu_gemm(A, B), Cref, S, f"skinny M={M} auto")
-    assert_within_tolerance(gpu_gemm(A, B, fgr.PATH_GEMV_SCALAR), Cref, S, f"skinny M={M} scalar")
+    if M <= 8:
+        assert_within_tolerance(gpu_gemm(A, B, fgr.PATH_GEMV_SCALAR), Cref, S, f"skinny M={M} scalar")
+    assert_within_tolerance(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT, fgr.TILE_32X128), Cref, S,
+                            f"skinny M={M} 32x128 unsplit")
+
+
+@pytest.mark.parametrize("shape,path", [
+    ((16, 8192, 4096), fgr.PATH_MFMA_SPLITK), ((24, 65536, 1024), fgr.PATH_MFMA_SPLITK),
+    ((5, 65536, 256), fgr.PATH_MFMA_SPLITK), ((8, 8192, 28672), fgr.PATH_MFMA_KSPLIT),
+    ((32, 4097, 4099), fgr.PATH_MFMA_SPLITK), ((31, 16384, 1000), fgr.PATH_MFMA_SPLITK)],
+    ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_skinny_tiles_exact(shape, path):
+    # 32x128 tiles for skinny outputs: rows past M and columns past K padded,
+    # 4-byte copies for unaligned rows, the reduction split across workgroups
+    # or not; exact on integer data, forced unsplit and split alike
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=19)
+    say(f"skinny tiles {shape}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == path
+    assert fgr.select_tile(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.TILE_32X128
+    say(f"skinny tiles {shape}: GPU")
+    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT, fgr.TILE_32X128), Cref, f"{shape} 32x128 unsplit")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_SPLITK, fgr.TILE_32X128), Cref, f"{shape} 32x128 split")
+    assert_exact(gpu_gemm(A, B, offsets=(1, 1, 1)), Cref, f"{shape} 4-byte aligned")
 
 
 def test_gemv_workload_full_compare():
