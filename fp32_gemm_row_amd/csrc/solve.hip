@@ -181,7 +181,7 @@ SplitPlan splitk_plan(int M, int N, int K, int cus) {
   return best;
 }
 
-// Skinny outputs (kSkinnyMinM <= M <= 32, K >= 128, B of at least 32 MiB):
+// Skinny outputs (kSkinnyMinM <= M <= 64, K >= 128, B of at least 32 MiB):
 // 32x128 k-split tiles, each reduction split into the largest power-of-two number of
 // parts that keeps tiles x parts within the CU count and parts at least 512
 // long. The work is streaming B once; wide column blocks and one workgroup
@@ -190,9 +190,11 @@ SplitPlan splitk_plan(int M, int N, int K, int cus) {
 // vs 2.56, 32 x 8192 x 8192 4.90 vs 3.25, 16 x 4096 x 4096 2.70 vs 1.99; and
 // at M = 5..8 against the matrix-vector kernel: 8 x 8192 x 28672 5.68 vs 3.61,
 // 8 x 65536 x 256 2.50 vs 1.10). With K < 128 half of a 128-column tile would
-// be padding (16 x 1048576 x 64: 3.57 vs 4.01 with 32x32 tiles).
+// be padding (16 x 1048576 x 64: 3.57 vs 4.01 with 32x32 tiles). Up to M = 64
+// two rows of these tiles still beat the square ones (48 x 8192 x 8192 3.01
+// vs 2.18, 64 x 8192 x 28672 3.15 vs 2.87, 64 x 11008 x 4096 2.87 vs 1.72).
 constexpr int kSkinnyMinM = 5;  // fewer rows: the matrix-vector kernel
-constexpr int kSkinnyMaxM = 32;
+constexpr int kSkinnyMaxM = 64;  // two rows of 32x128 tiles at most
 constexpr int64_t kSkinnyMinB = int64_t(8) << 20;  // elements of B
 int skinny_parts(int M, int N, int K, int cus) {
   const int64_t tiles = cdiv(M, 32) * cdiv(K, 128);

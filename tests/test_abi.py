@@ -254,7 +254,8 @@ def test_skinny_choices():
         assert sp(A0, B0, C0, *shape) == path, shape
         assert st(A0, B0, C0, *shape) == fgr.TILE_32X128, shape
     assert sp(A0, B0, C0, 4, 8192, 8192) == fgr.PATH_GEMV_VEC  # M < 5: the matrix-vector kernel
-    assert st(A0, B0, C0, 33, 8192, 8192) == 32  # M > 32: the few-tile rules
+    assert st(A0, B0, C0, 64, 8192, 8192) == fgr.TILE_32X128  # two rows of tiles
+    assert st(A0, B0, C0, 65, 8192, 8192) == 64  # M > 64: the tile-count rules
     assert st(A0, B0, C0, 16, 1048576, 64) == 32  # K < 128
 
 
@@ -264,7 +265,7 @@ def test_split_reduction_choices():
     # few output tiles and a long reduction: the reduction is also split
     # across workgroups; 64x64 tiles for tall outputs, 32x32 for skinny ones
     # (less padding), by the time estimate
-    for shape, tile in [((256, 65536, 256), 64), ((128, 262144, 128), 64), ((64, 65536, 1024), 64),
+    for shape, tile in [((256, 65536, 256), 64), ((128, 262144, 128), 64), ((64, 65536, 1024), fgr.TILE_32X128),
                         ((512, 65536, 512), 64), ((16, 1048576, 64), 32), ((130, 20000, 66), 32),
                         ((24, 65536, 1024), fgr.TILE_32X128), ((16, 16384, 4096), fgr.TILE_32X128)]:
         assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
@@ -272,9 +273,10 @@ def test_split_reduction_choices():
         assert sp(A0 + 4, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape  # 4-byte copies too
     # enough 32x32 tiles for every CU, or too short a reduction: no split
     assert sp(A0, B0, C0, 512, 8192, 512) == fgr.PATH_MFMA_KSPLIT
-    assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles
+    assert sp(A0, B0, C0, 96, 8192, 4096) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 200, 2048, 200) == fgr.PATH_MFMA_KSPLIT
-    assert sp(A0, B0, C0, 33, 8192, 8192) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 65, 8192, 8192) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 100, 64) == fgr.PATH_MFMA_KSPLIT
     # tiles enough for every CU: the whole-device kernels, never a split
     assert sp(A0, B0, C0, 1024, 32768, 1024) == fgr.PATH_MFMA_KSPLIT
