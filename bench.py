@@ -185,7 +185,7 @@ def ablation(w, dA, dBs, dC, copies, steps, warmup, stream):
     variants = [(fgr.PATH_MFMA_DMA, 256), (fgr.PATH_MFMA_DMA_TAIL, 256)]
     for tile in (256, 128, 64):
         variants += [(fgr.PATH_MFMA_VEC, tile), (fgr.PATH_MFMA_SCALAR, tile)]
-    for tile in (128, 64, 32):
+    for tile in (128, 64, 32, fgr.TILE_32X128):
         variants += [(fgr.PATH_MFMA_KSPLIT, tile), (fgr.PATH_MFMA_SPLITK, tile)]
     variants += [(fgr.PATH_MFMA_KSPLIT_TAIL, 128), (fgr.PATH_MFMA_KSPLIT_TAIL, 64),
                  (fgr.PATH_MFMA_SPLIT, 64), (fgr.PATH_MFMA_SPLIT, 32), (fgr.PATH_VALU, 128),
