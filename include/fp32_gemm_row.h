@@ -143,7 +143,8 @@ extern "C" {
  * or from the device's default pool if that creation failed. If the
  * allocation fails the unsplit kernel runs instead (same result up to
  * rounding order). Results are deterministic: the parts are added in a fixed
- * order.
+ * order. solve() can be captured into a HIP graph (stream capture on
+ * `stream`); the split paths' workspace then becomes a graph allocation.
  * The LeetGPU signature (section "Problem Description", and every "Solution"
  * of the write-up) is solve(A, B, C, M, N, K) returning void; this form adds
  * the stream and a status.

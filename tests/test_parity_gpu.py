@@ -628,6 +628,38 @@ def test_concurrent_calls_on_separate_streams():
             assert_exact(C, Cref, f"{M}x{N}x{K} call {j}")
 
 
+@pytest.mark.parametrize("shape", [(512, 512, 512), (1023, 1025, 1027), (100, 30000, 300), (1, 262144, 64),
+                                   (16, 8192, 4096)], ids=lambda s: "x".join(map(str, s)))
+def test_graph_capture_replays(shape):
+    # solve() captured into a HIP graph (torch.cuda.graph) and replayed three
+    # times with eager work in between: one-kernel paths, the two-launch tail,
+    # and the split paths whose stream-ordered workspace becomes a graph
+    # allocation; every replay exact on integer data
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=40)
+    Cref, _ = oracle.gemm(A, B)
+    dA = torch.from_numpy(A.ravel()).to(DEV)
+    dB = torch.from_numpy(B.ravel()).to(DEV)
+    dC = torch.full((M * K,), float("nan"), device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fgr.solve(dA, dB, dC, M, N, K)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say(f"graph capture {shape}: {fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fgr.solve(dA, dB, dC, M, N, K)
+    for r in range(3):
+        dC.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_exact(dC.cpu().numpy().reshape(M, K), Cref, f"{shape} replay {r}")
+        torch.randn(1000, device=DEV).sum().item()  # eager work between replays
+
+
 def test_six_argument_form_uses_null_stream():
     A, B = synth.make_inputs(33, 40, 36, "eighths")
     Cref, _ = oracle.gemm(A, B)
