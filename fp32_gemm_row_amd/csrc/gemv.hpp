@@ -7,7 +7,8 @@
 // at 0.5 * M FLOP per byte.
 //
 // Design: workgroup w owns the 32 output columns [32w, 32w+32) - one 128-byte
-// segment of every row of B - and the whole reduction for them, for all MR
+// segment of every row of B (16 columns, 64 bytes, where K is too small to
+// give every CU a 32-column block) - and the whole reduction for them, for all MR
 // (>= M) rows of A. Its threads split the rows of B: LPR lanes cover the 32
 // columns of one row (8 lanes x float4 on the 128-bit path, 32 lanes x float
 // on the 32-bit path) and the RPI = NT / LPR row groups walk rows r, r + RPI,
@@ -25,6 +26,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "gemm_mfma.hpp"  // xcd_remap
 
 namespace fgr {
 
@@ -60,12 +63,12 @@ __device__ __forceinline__ void fma_row(float (&acc)[MR][VW], const float* a_s, 
 // the reduction indices [N part / parts, N (part + 1) / parts) and writes its
 // partial rows to W + part M K instead of C; a second kernel adds the parts in
 // order (for K too small to give every CU its 32 columns).
-template <int VW, int NT, int UNROLL, int MR, int AF = kGemvAFloats>
+template <int VW, int NT, int UNROLL, int MR, int AF = kGemvAFloats, int COLS = kGemvCols>
 __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
                                                   const float* __restrict__ B,
                                                   float* __restrict__ C, int M, int N, int K, int parts,
                                                   float* __restrict__ W) {
-  constexpr int LPR = kGemvCols / VW;     // lanes per row segment
+  constexpr int LPR = COLS / VW;          // lanes per row segment
   constexpr int RPI = NT / LPR;           // rows in flight per workgroup step
   constexpr int WAVES = NT / 64;
   constexpr int CHUNK = AF / MR;          // reduction indices per staged chunk of A
@@ -74,14 +77,17 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
   static_assert(MR >= 1 && MR <= kGemvMaxRows && AF % MR == 0 && (AF / MR) % RPI == 0, "rows per workgroup");
 
   __shared__ float a_s[MR * CHUNK];  // [m][n - nb]
-  __shared__ float part[WAVES][MR][kGemvCols];
+  __shared__ float part[WAVES][MR][COLS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int cl = tid % LPR;  // column lane
   const int rl = tid / LPR;  // row group
-  const int col = blockIdx.x * kGemvCols + cl * VW;
+  // column block: consecutive blocks on one XCD (with 16-column blocks two
+  // of them share each 128-byte line of B, which its L2 then fetches once)
+  const int cb = xcd_remap(blockIdx.x, gridDim.x);
+  const int col = cb * COLS + cl * VW;
   const bool col_ok = col < K;  // VW == 4: K % 4 == 0, so all four columns are in
 
   float acc[MR][VW];
@@ -137,10 +143,10 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
       for (int e = 0; e < VW; ++e) part[wave][m][cl * VW + e] = acc[m][e];
   }
   __syncthreads();
-  for (int t = tid; t < MR * kGemvCols; t += NT) {
-    const int m = t / kGemvCols;
-    const int cc = t % kGemvCols;
-    const int c = blockIdx.x * kGemvCols + cc;
+  for (int t = tid; t < MR * COLS; t += NT) {
+    const int m = t / COLS;
+    const int cc = t % COLS;
+    const int c = cb * COLS + cc;
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) s += part[w][m][cc];

@@ -637,31 +637,42 @@ int launch_valu(const float* A, const float* B, float* C, int M, int N, int K, h
 // all M rows (B is streamed once). Each lane keeps one row of B in
 // flight (two at 8 rows): with 16 waves per CU that saturates HBM, and more
 // loads in flight measured slower (M = 1: 5.79 TB/s with one, 4.82 with four).
-template <int VW>
+template <int VW, int COLS>
 int launch_gemv_parts(const float* A, const float* B, float* C, int M, int N, int K, int parts, float* W,
                       hipStream_t s) {
   void* args[] = {&A, &B, &C, &M, &N, &K, &parts, &W};
-  const int64_t blocks = cdiv(K, fgr::kGemvCols);
+  const int64_t blocks = cdiv(K, COLS);
   const void* kernel;
-  if (M <= 1) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 1>);
-  else if (M <= 2) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 2>);
-  else if (M <= 4) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 4>);
-  else kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 2, 8>);
+  if (M <= 1) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 1, fgr::kGemvAFloats, COLS>);
+  else if (M <= 2) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 2, fgr::kGemvAFloats, COLS>);
+  else if (M <= 4) kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 1, 4, fgr::kGemvAFloats, COLS>);
+  else kernel = reinterpret_cast<const void*>(&fgr::gemv_kernel<VW, 1024, 2, 8, fgr::kGemvAFloats, COLS>);
   return launch(kernel, blocks, 1024, args, s, parts);
 }
 
-// The matrix-vector kernel; when K gives fewer than half the CUs a workgroup
-// (32 columns each) and N is long, the reduction is also split across
-// workgroups through a stream-ordered workspace (then added in part order).
+// The matrix-vector kernel on 32-column blocks; when those fill at most half
+// the CUs and N is long, the reduction is also split across workgroups
+// through a stream-ordered workspace (then added in part order). When they
+// fill at most half the CUs and N is too short to split, 16-column blocks
+// instead, so that twice the CUs stream B in one launch (measured on MI355X,
+// TB/s, 32 vs 16 columns: 1 x 4096 x 4096 3.09 vs 3.43, 4 x 11008 x 4096 2.69
+// vs 3.30, 1 x 8192 x 2048 1.70 vs 2.02; with more blocks, or with a split,
+// the narrower 64-byte row segments stream worse: 1 x 4096 x 6144 4.31 vs
+// 2.85, 1 x 65536 x 1024 5.13 vs 3.59).
 template <int VW>
 int launch_gemv(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
-  const int parts = gemv_parts(cdiv(K, fgr::kGemvCols), N, cus);
+  const int64_t wide_blocks = cdiv(K, fgr::kGemvCols);
+  const int wide_parts = gemv_parts(wide_blocks, N, cus);
+  const bool narrow = wide_blocks * 2 <= cus && wide_parts < 2;
+  const int parts = narrow ? 1 : wide_parts;
   PartsWorkspace ws;
-  if (parts < 2 || alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) != FGR_OK)
-    return launch_gemv_parts<VW>(A, B, C, M, N, K, 1, nullptr, s);
-  const int rc = launch_gemv_parts<VW>(A, B, C, M, N, K, parts, ws.w, s);
-  if (rc != FGR_OK) return rc;
-  return launch_reduce_parts(ws.w, C, M, K, parts, vec4_rows(C, M, K), s);
+  float* W = nullptr;
+  if (parts >= 2 && alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) == FGR_OK) W = ws.w;
+  const int p = W ? parts : 1;
+  const int rc = narrow ? launch_gemv_parts<VW, fgr::kGemvCols / 2>(A, B, C, M, N, K, p, W, s)
+                        : launch_gemv_parts<VW, fgr::kGemvCols>(A, B, C, M, N, K, p, W, s);
+  if (rc != FGR_OK || !W) return rc;
+  return launch_reduce_parts(W, C, M, K, parts, vec4_rows(C, M, K), s);
 }
 
 int run(const float* A, const float* B, float* C, int M, int N, int K, void* stream, int path,
