@@ -57,32 +57,37 @@ namespace fgr {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// VEC: 16-byte copies (rows 16-byte aligned); otherwise 4-byte copies, four
-// times as many, into the same LDS layout (any 4-byte alignment).
-template <int S_, bool VEC_ = true>
+// VA / VB: 16-byte copies of A / B (rows 16-byte aligned: N % 4 == 0 and an
+// aligned A; K % 4 == 0 and an aligned B), otherwise 4-byte copies, four
+// times as many, into the same LDS layout (any 4-byte alignment). VC:
+// 128-bit stores of C (K % 4 == 0, aligned C). VEC: all three.
+template <int S_, bool VA_ = true, bool VB_ = VA_, bool VC_ = VB_>
 struct DmaConfig {
   static constexpr int BM = 256, BN = 256, BK = 16, WM = 2, WN = 2, S = S_;
-  static constexpr bool VEC = VEC_;
-  static constexpr int kCopyFloats = VEC ? 4 : 1;  // floats per lane per copy
-  static constexpr int kBlock = 64 * kCopyFloats;  // LDS floats one copy fills
+  static constexpr bool VA = VA_, VB = VB_, VC = VC_, VEC = VA_ && VB_ && VC_;
+  static constexpr int kACopyFloats = VA ? 4 : 1;  // floats per lane per copy
+  static constexpr int kBCopyFloats = VB ? 4 : 1;
+  static constexpr int kABlock = 64 * kACopyFloats;  // LDS floats one copy fills
+  static constexpr int kBBlock = 64 * kBCopyFloats;
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM;
   static constexpr int kWaveN = BN / WN;
   static constexpr int kRB = kWaveM / 32;
   static constexpr int kCB = kWaveN / 32;
-  static constexpr int kQuads = BK / 4;                     // quads per A row
-  static constexpr int kStage = BM * BK;                    // floats, A and B stages alike
-  static constexpr int kACopies = kStage / kBlock / kWaves;  // per wave per chunk
-  static constexpr int kBCopies = kStage / kBlock / kWaves;
+  static constexpr int kQuads = BK / 4;                      // quads per A row
+  static constexpr int kStage = BM * BK;                     // floats, A and B stages alike
+  static constexpr int kACopies = kStage / kABlock / kWaves;  // per wave per chunk
+  static constexpr int kBCopies = kStage / kBBlock / kWaves;
   static constexpr int kCopies = kACopies + kBCopies;
 
-  static_assert(BN % kBlock == 0, "a B copy stays inside one row");
+  static_assert(BN % kBBlock == 0, "a B copy stays inside one row");
   static_assert(BM * BK == BK * BN, "A and B stages have one size");
   static_assert(kQuads == 4, "the A swizzle is written for 4 quads per row");
   static_assert(kCB == 4, "B operands are read as 4 adjacent floats");
   static_assert(kRB * kCB * 16 == 256, "the accumulators fill the 256 AGPRs");
-  static_assert(kStage % (kBlock * kWaves) == 0, "copies split evenly over waves");
+  static_assert(kStage % (kABlock * kWaves) == 0 && kStage % (kBBlock * kWaves) == 0,
+                "copies split evenly over waves");
   static_assert(S >= 3 && S <= 5, "a ring of 3 to 5 stages");
   static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
   static_assert(S * 2 * kStage * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
@@ -156,9 +161,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   const int k0 = tn * BN;
 
   // Copy sources for this lane. Copy j of this wave fills LDS floats
-  // [blk * kBlock, (blk + 1) * kBlock) of a stage, blk = wave * kACopies + j;
-  // lane L fills the kCopyFloats floats at position p = blk * kBlock +
-  // L * kCopyFloats. In the A stage position p is row p / 16, stored slot
+  // [blk * kABlock, (blk + 1) * kABlock) of an A stage, blk = wave * kACopies
+  // + j; lane L fills the kACopyFloats floats at position p = blk * kABlock +
+  // L * kACopyFloats (likewise for B). In the A stage position p is row p / 16, stored slot
   // (p % 16) / 4, element p % 4, and the slot holds quad slot ^ swz(row), so
   // the lane reads that quad's element (the whole quad with 16-byte copies).
   // Rows past M read row M - 1 instead (their outputs are not stored).
@@ -168,13 +173,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
     const int blk = wave * T::kACopies + j;
-    const int pos = blk * T::kBlock + lane * T::kCopyFloats;
+    const int pos = blk * T::kABlock + lane * T::kACopyFloats;
     const int r = pos / BK;
     const int q = ((pos % BK) / 4) ^ a_swizzle(r);
     const int c = 4 * q + pos % 4;
     const int row = m0 + r < M ? m0 + r : M - 1;
     a_src[j] = A + (int64_t)row * N + c;
-    a_dst[j] = blk * T::kBlock;
+    a_dst[j] = blk * T::kABlock;
     a_col[j] = c;
   }
   // In the B stage position p is row p / 256, column p % 256 (columns past K
@@ -185,12 +190,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
     const int blk = wave * T::kBCopies + j;
-    const int pos = blk * T::kBlock + lane * T::kCopyFloats;
+    const int pos = blk * T::kBBlock + lane * T::kBCopyFloats;
     const int r = pos / BN;
     const int c = k0 + pos % BN;
-    const int col = c < K ? c : K - T::kCopyFloats;
+    const int col = c < K ? c : K - T::kBCopyFloats;
     b_src[j] = B + (int64_t)r * K + col;
-    b_dst[j] = blk * T::kBlock;
+    b_dst[j] = blk * T::kBBlock;
     b_row[j] = r;
   }
 
@@ -198,16 +203,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   auto copy_part = [&](auto p0c, auto p1c, int n0, float* As, float* Bs) __attribute__((always_inline)) {
     static_for<decltype(p0c)::value, decltype(p1c)::value>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (T::VEC) {
-        if constexpr (p < T::kACopies)
-          copy16_to_lds(a_src[p] + n0, As + a_dst[p]);
-        else
-          copy16_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
+      if constexpr (p < T::kACopies) {
+        if constexpr (T::VA) copy16_to_lds(a_src[p] + n0, As + a_dst[p]);
+        else copy4_to_lds(a_src[p] + n0, As + a_dst[p]);
       } else {
-        if constexpr (p < T::kACopies)
-          copy4_to_lds(a_src[p] + n0, As + a_dst[p]);
-        else
-          copy4_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
+        if constexpr (T::VB) copy16_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
+        else copy4_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
       }
     });
   };
@@ -268,38 +269,41 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
 
   // Pipeline fill with chunk 0 in stage OFF: chunk 0 through registers (zero
   // outside [0, N)), chunks 1 .. S - 2 copied into the stages after it.
-  // N % 4 == 0 and n_first % 4 == 0, so a quad is wholly inside or outside.
+  // With 16-byte copies of A, N % 4 == 0 and n_first % 4 == 0, so a quad is
+  // wholly inside or outside.
   auto fill = [&](auto offc) __attribute__((always_inline)) {
     constexpr int OFF = decltype(offc)::value;
     using S0 = std::integral_constant<int, OFF>;
-    typedef typename std::conditional<T::VEC, float4, float>::type CopyT;
-    CopyT va[T::kACopies], vb[T::kBCopies];
+    typedef typename std::conditional<T::VA, float4, float>::type CopyTA;
+    typedef typename std::conditional<T::VB, float4, float>::type CopyTB;
+    CopyTA va[T::kACopies];
+    CopyTB vb[T::kBCopies];
     bool oka[T::kACopies], okb[T::kBCopies];
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j) {
       oka[j] = n_first + a_col[j] >= 0;
-      va[j] = *reinterpret_cast<const CopyT*>(oka[j] ? a_src[j] + n_first : A);
+      va[j] = *reinterpret_cast<const CopyTA*>(oka[j] ? a_src[j] + n_first : A);
     }
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j) {
       okb[j] = n_first + b_row[j] >= 0;
-      vb[j] = *reinterpret_cast<const CopyT*>(okb[j] ? b_src[j] + (int64_t)n_first * K : B);
+      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? b_src[j] + (int64_t)n_first * K : B);
     }
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       using Sj = std::integral_constant<int, (OFF + j) % S>;
       copy_part(I0{}, ICopies{}, n_first + BK * min(j, nchunks - 1), a_stage(Sj{}), b_stage(Sj{}));
     });
-    auto zero_out = [](CopyT v, bool ok) __attribute__((always_inline)) -> CopyT {
-      if constexpr (T::VEC) return mask_quad(v, ok ? 0xfu : 0u);
+    auto zero_out = [](auto v, bool ok) __attribute__((always_inline)) {
+      if constexpr (std::is_same<decltype(v), float4>::value) return mask_quad(v, ok ? 0xfu : 0u);
       else return ok ? v : 0.f;
     };
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
-      *reinterpret_cast<CopyT*>(a_stage(S0{}) + a_dst[j] + T::kCopyFloats * lane) = zero_out(va[j], oka[j]);
+      *reinterpret_cast<CopyTA*>(a_stage(S0{}) + a_dst[j] + T::kACopyFloats * lane) = zero_out(va[j], oka[j]);
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j)
-      *reinterpret_cast<CopyT*>(b_stage(S0{}) + b_dst[j] + T::kCopyFloats * lane) = zero_out(vb[j], okb[j]);
+      *reinterpret_cast<CopyTB*>(b_stage(S0{}) + b_dst[j] + T::kBCopyFloats * lane) = zero_out(vb[j], okb[j]);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
       const int row = wm * T::kWaveM + i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
       if (col_ok && m0 + row < M) {
         float* dst = Ct + (uint64_t)row * (uint32_t)K + (uint32_t)col;
-        if constexpr (T::VEC) {
+        if constexpr (T::VC) {
           *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0][rr], acc[i][1][rr], acc[i][2][rr], acc[i][3][rr]);
         } else {
 #pragma unroll

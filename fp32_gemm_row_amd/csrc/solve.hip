@@ -393,17 +393,33 @@ using TileDma = fgr::DmaConfig<4>;  // 256x256, 4 waves of 128x128 (accumulators
 // 3 stages (the copies in flight must fit the wave's vmcnt counter)
 using TileDmaScalar = fgr::DmaConfig<3, false>;
 
+template <class Cfg>
+const void* dma_kernel() {
+  return reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<Cfg>);
+}
+
 // The direct-copy kernel over the first `count` tiles of the grouped order
-// (count < 0: all of them).
+// (count < 0: all of them). Each operand takes 16-byte copies when its rows
+// are 16-byte aligned; with one operand so, 4 + 16 copies per wave and chunk
+// still fit 4 stages (measured on MI355X, TFLOP/s, 4-byte copies of both vs
+// of the unaligned one only: 8192 x 6143 x 4096 and 8192 x 6144 x 4095, see
+// the design notes).
 int launch_mfma_dma(const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
                     hipStream_t s) {
   int tiles_m = (int)cdiv(M, TileDma::BM);
   int tiles_n = (int)cdiv(K, TileDma::BN);
   int group = kTileGroup;
   void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
-  const void* kernel = mfma_vec_ok(A, B, C, N, K)
-                           ? reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDma>)
-                           : reinterpret_cast<const void*>(&fgr::gemm_mfma_dma_kernel<TileDmaScalar>);
+  const bool va = N % 4 == 0 && aligned(A, 16);
+  const bool vb = K % 4 == 0 && aligned(B, 16);
+  const bool vc = K % 4 == 0 && aligned(C, 16);
+  const void* kernel;
+  if (va && vb) kernel = vc ? dma_kernel<TileDma>() : dma_kernel<fgr::DmaConfig<4, true, true, false>>();
+  else if (va) kernel = vc ? dma_kernel<fgr::DmaConfig<4, true, false, true>>()
+                           : dma_kernel<fgr::DmaConfig<4, true, false, false>>();
+  else if (vb) kernel = vc ? dma_kernel<fgr::DmaConfig<4, false, true, true>>()
+                           : dma_kernel<fgr::DmaConfig<4, false, true, false>>();
+  else kernel = dma_kernel<TileDmaScalar>();
   return launch(kernel, count < 0 ? (int64_t)tiles_m * tiles_n : count, TileDma::kThreads, args, s);
 }
 using Tile128 = fgr::MfmaConfig<128, 128, 16, 2, 2>;

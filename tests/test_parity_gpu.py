@@ -343,6 +343,26 @@ def test_split_reduction_long_sampled(shape):
     assert_within_tolerance(C[rows, cols][None, :], Cref[None, :], S[None, :], f"{shape} sampled")
 
 
+@pytest.mark.parametrize("shape,offsets", [
+    ((520, 1023, 516), (0, 0, 0)),   # A rows unaligned: 4-byte copies of A, 16-byte of B, 128-bit stores
+    ((520, 1024, 515), (0, 0, 0)),   # B and C rows unaligned
+    ((520, 1024, 516), (0, 0, 1)),   # only C misaligned: 32-bit stores
+    ((520, 1024, 516), (1, 0, 0)),   # only A misaligned
+    ((520, 1024, 516), (0, 3, 0)),   # only B misaligned
+    ((520, 1023, 515), (0, 0, 0)),   # nothing aligned: 4-byte copies of both, 3 stages
+], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_direct_copy_operand_alignments_exact(shape, offsets):
+    # the direct-copy kernel picks 16- or 4-byte copies per operand and 128-
+    # or 32-bit stores for C; every combination exact on integer data
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=23)
+    Cref, _ = oracle.gemm(A, B)
+    say(f"direct copies {shape} offsets {offsets}")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA, fgr.TILE_256, offsets=offsets), Cref, f"{shape} {offsets}")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_DMA_TAIL, fgr.TILE_256, offsets=offsets), Cref,
+                 f"{shape} {offsets} tail form")
+
+
 @pytest.mark.parametrize("shape", [(1023, 1025, 1027), (1024, 1024, 1024), (300, 2000, 260), (1, 3, 1), (129, 17, 5)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_vector_alu_path_exact(shape):
