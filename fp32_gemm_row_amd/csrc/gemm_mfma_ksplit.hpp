@@ -47,20 +47,24 @@
 namespace fgr {
 
 // BM x BN tiles (BN defaults to BM; BM = 32 with BN = 128 is the skinny
-// tile: few output rows, wide column blocks of B per workgroup).
-template <int BM_, int S_, bool VEC_, int BN_ = BM_>
+// tile: few output rows, wide column blocks of B per workgroup). VA / VB:
+// 16-byte copies of A / B (their rows 16-byte aligned), else 4-byte copies;
+// VC: 128-bit stores of C (used by the 128 x 128 tile).
+template <int BM_, int S_, bool VA_, int BN_ = BM_, bool VB_ = VA_, bool VC_ = VB_>
 struct KsplitConfig {
   static constexpr int BM = BM_, BN = BN_, BK = 8, S = S_;
-  static constexpr bool VEC = VEC_;
+  static constexpr bool VA = VA_, VB = VB_, VC = VC_, VEC = VA_ && VB_ && VC_;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRB = BM / 32, kCB = BN / 32;
-  static constexpr int kCopyFloats = VEC ? 4 : 1;  // floats per lane per copy
-  static constexpr int kBlock = 64 * kCopyFloats;  // floats one copy fills
+  static constexpr int kACopyFloats = VA ? 4 : 1;  // floats per lane per copy
+  static constexpr int kBCopyFloats = VB ? 4 : 1;
+  static constexpr int kABlock = 64 * kACopyFloats;  // floats one copy fills
+  static constexpr int kBBlock = 64 * kBCopyFloats;
   static constexpr int kPieceA = BM * BK;          // floats of one wave's A stage
   static constexpr int kPieceB = BK * BN;          // floats of one wave's B stage
-  static constexpr int kACopies = kPieceA / kBlock;  // per wave per chunk
-  static constexpr int kBCopies = kPieceB / kBlock;
+  static constexpr int kACopies = kPieceA / kABlock;  // per wave per chunk
+  static constexpr int kBCopies = kPieceB / kBBlock;
   static constexpr int kCopies = kACopies + kBCopies;
   static constexpr int kStageA = kWaves * kPieceA;  // floats of one LDS stage object of A
   static constexpr int kStageB = kWaves * kPieceB;
@@ -72,7 +76,7 @@ struct KsplitConfig {
 
   static_assert((BM == BN && (BM == 32 || BM == 64 || BM == 128)) || (BM == 32 && BN == 128),
                 "square tiles of 32, 64 or 128, or 32 x 128");
-  static_assert(kPieceA % kBlock == 0 && kPieceB % kBlock == 0 && BN % kCopyFloats == 0,
+  static_assert(kPieceA % kABlock == 0 && kPieceB % kBBlock == 0 && BN % kBCopyFloats == 0,
                 "copies cover whole pieces");
   static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");
   static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
@@ -174,8 +178,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int c_end = pc0 + pn * (wave + 1) / T::kWaves;
   const int c_last = c_end - 1;
 
-  // Copy j of a wave fills floats [j * kBlock, (j + 1) * kBlock) of its piece;
-  // lane L the kCopyFloats floats at position p = j * kBlock + L * kCopyFloats.
+  // Copy j of a wave fills floats [j * kABlock, (j + 1) * kABlock) of its A
+  // piece; lane L the kACopyFloats floats at position p = j * kABlock + L *
+  // kACopyFloats (likewise for B).
   // In A, p is row p / 8, stored slot (p % 8) / 4, element p % 4, and the slot
   // holds quad slot ^ swz(row): the lane copies that quad's element (the whole
   // quad with 16-byte copies). Rows past M read row M - 1 (not stored).
@@ -183,12 +188,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   int a_dst[T::kACopies], a_col[T::kACopies];
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
-    const int pos = j * T::kBlock + lane * T::kCopyFloats;
+    const int pos = j * T::kABlock + lane * T::kACopyFloats;
     const int r = pos / BK;
     const int c = 4 * (((pos % BK) / 4) ^ a_swizzle2(r)) + pos % 4;
     const int row = m0 + r < M ? m0 + r : M - 1;
     a_src[j] = A + (int64_t)row * N + c;
-    a_dst[j] = piece_a + j * T::kBlock;
+    a_dst[j] = piece_a + j * T::kABlock;
     a_col[j] = c;
   }
   // In B, p is row p / BN, column p % BN (columns past K read the last column,
@@ -197,11 +202,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   int b_dst[T::kBCopies], b_row[T::kBCopies];
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
-    const int pos = j * T::kBlock + lane * T::kCopyFloats;
+    const int pos = j * T::kBBlock + lane * T::kBCopyFloats;
     const int r = pos / BN;
     const int c = k0 + pos % BN;
-    b_src[j] = B + (int64_t)r * K + (c < K ? c : K - T::kCopyFloats);
-    b_dst[j] = piece_b + j * T::kBlock;
+    b_src[j] = B + (int64_t)r * K + (c < K ? c : K - T::kBCopyFloats);
+    b_dst[j] = piece_b + j * T::kBBlock;
     b_row[j] = r;
   }
 
@@ -209,10 +214,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const int n0 = n_first + BK * c;
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
-      copy_to_lds_counted<4 * T::kCopyFloats>(a_src[j] + n0, As + a_dst[j]);
+      copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j)
-      copy_to_lds_counted<4 * T::kCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+      copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
   };
 
   struct Frag {
@@ -268,34 +273,36 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     constexpr int X = OFF & 1;  // operand buffer of the chunk in stage OFF
     using S0 = std::integral_constant<int, OFF>;
     const int n0 = n_first + BK * c_begin;
-    typedef typename std::conditional<T::VEC, float4, float>::type CopyT;
-    CopyT va[T::kACopies], vb[T::kBCopies];
+    typedef typename std::conditional<T::VA, float4, float>::type CopyTA;
+    typedef typename std::conditional<T::VB, float4, float>::type CopyTB;
+    CopyTA va[T::kACopies];
+    CopyTB vb[T::kBCopies];
     bool oka[T::kACopies], okb[T::kBCopies];
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j) {
       oka[j] = n0 + a_col[j] >= 0;
-      va[j] = *reinterpret_cast<const CopyT*>(oka[j] ? a_src[j] + n0 : A);
+      va[j] = *reinterpret_cast<const CopyTA*>(oka[j] ? a_src[j] + n0 : A);
     }
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j) {
       okb[j] = n0 + b_row[j] >= 0;
-      vb[j] = *reinterpret_cast<const CopyT*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
+      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
     }
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       using Sj = std::integral_constant<int, (OFF + j) % S>;
       copy_chunk(min(c_begin + j, c_last), a_stage(Sj{}), b_stage(Sj{}));
     });
-    auto zero_out = [](CopyT v, bool ok) __attribute__((always_inline)) -> CopyT {
-      if constexpr (T::VEC) return mask_quad(v, ok ? 0xfu : 0u);
+    auto zero_out = [](auto v, bool ok) __attribute__((always_inline)) {
+      if constexpr (std::is_same<decltype(v), float4>::value) return mask_quad(v, ok ? 0xfu : 0u);
       else return ok ? v : 0.f;
     };
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
-      *reinterpret_cast<CopyT*>(a_stage(S0{}) + a_dst[j] + T::kCopyFloats * lane) = zero_out(va[j], oka[j]);
+      *reinterpret_cast<CopyTA*>(a_stage(S0{}) + a_dst[j] + T::kACopyFloats * lane) = zero_out(va[j], oka[j]);
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j)
-      *reinterpret_cast<CopyT*>(b_stage(S0{}) + b_dst[j] + T::kCopyFloats * lane) = zero_out(vb[j], okb[j]);
+      *reinterpret_cast<CopyTB*>(b_stage(S0{}) + b_dst[j] + T::kBCopyFloats * lane) = zero_out(vb[j], okb[j]);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
     __builtin_amdgcn_sched_barrier(0);
     read_frag(f[X], a_stage(S0{}), b_stage(S0{}));
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     Ct = W + (int64_t)part * M * K + (int64_t)m0 * K + k0;
     ldc = (uint32_t)K;
   }
-  if constexpr (T::VEC && kSPW == T::kCB && T::kCB == 4) {
+  if constexpr (T::VC && kSPW == T::kCB && T::kCB == 4) {
     // a whole block row: 4 adjacent columns per lane and row
     const int col = 4 * li;
     const bool col_ok = k0 + col < K;

@@ -82,6 +82,29 @@ bool mfma_vec_ok(const float* A, const float* B, const float* C, int N, int K) {
 
 bool gemv_vec_ok(const float* B, int K) { return K % 4 == 0 && aligned(B, 16); }
 
+// Row alignment of a product, for the k-split configurations: 16-byte copies
+// of A (N % 4 == 0, aligned A) and of B (K % 4 == 0, aligned B) with 128-bit
+// stores (aligned C), of A only, of B only, or of neither. (A product with
+// aligned A and B but not C takes the A-only form.)
+enum class Rows { kAll, kAOnly, kBOnly, kNone };
+Rows rows_of(const float* A, const float* B, const float* C, int N, int K) {
+  const bool va = N % 4 == 0 && aligned(A, 16);
+  const bool vb = K % 4 == 0 && aligned(B, 16);
+  const bool vc = K % 4 == 0 && aligned(C, 16);
+  if (va && vb && vc) return Rows::kAll;
+  if (va) return Rows::kAOnly;
+  if (vb) return Rows::kBOnly;
+  return Rows::kNone;
+}
+
+// 128x128 k-split tiles need 16-byte copies of both operands: with 4-byte
+// copies of either, the copies' addresses push the kernel past 256 VGPRs
+// (27 spilled with 4-byte copies of A).
+bool ksplit128_ok(const float* A, const float* B, const float* C, int N, int K) {
+  return rows_of(A, B, C, N, K) == Rows::kAll;
+}
+
+
 // Direct global->LDS copies need at least four 16-deep reduction chunks (the
 // copies that run past the last chunk re-read it, and must never reach the
 // zero-padded first chunk); they are 16 bytes wide for 16-byte aligned rows,
@@ -248,7 +271,7 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     // Fewer 256x256 tiles than CUs: tiles whose reduction is split over the
     // four waves of a workgroup (k-split), the largest that still gives every
     // CU a tile; a last partial wave of up to half the CUs to the split kernel.
-    if (vec && t128 >= cus) {
+    if (ksplit128_ok(A, B, C, N, K) && t128 >= cus) {
       const int64_t rem = t128 % cus;
       if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
@@ -500,18 +523,6 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
   return launch_split_tail<256, false>(A, B, C, M, N, K, full, rem, cus, s);
 }
 
-// k-split tiles: 128x128 (16-byte copies only: 4-byte ones would leave more
-// copies in flight than the wave's vmcnt counter holds), 64x64 and 32x32
-using Ksplit128 = fgr::KsplitConfig<128, 4, true>;
-using Ksplit64 = fgr::KsplitConfig<64, 4, true>;
-using Ksplit64s = fgr::KsplitConfig<64, 4, false>;
-using Ksplit32 = fgr::KsplitConfig<32, 4, true>;
-using Ksplit32s = fgr::KsplitConfig<32, 4, false>;
-// skinny outputs: 32 rows x 128 columns, so that each workgroup streams a
-// 512-byte-wide column block of B and A's rows are re-read a quarter as often
-using Ksplit32x128 = fgr::KsplitConfig<32, 4, true, 128>;
-using Ksplit32x128s = fgr::KsplitConfig<32, 4, false, 128>;
-
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
                       int parts, float* W, int first, int compact) {
@@ -523,27 +534,46 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
                 (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts, Cfg::kThreads, args, s);
 }
 
+// k-split configurations by the row alignment of the product: 16-byte copies
+// of A and B with 128-bit stores, of one operand (the other 4-byte), or
+// 4-byte copies of both; 128x128 tiles only in the first form (ksplit128_ok).
+template <int BM, int BN = BM>
+int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
+                       hipStream_t s, int parts, float* W, int first, int compact) {
+  switch (rows) {
+    case Rows::kAll:
+      return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
+                                                                    compact);
+    default:
+      if constexpr (BM == 128) {
+        return FGR_ERR_BAD_PATH;
+      } else if (rows == Rows::kAOnly) {
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(A, B, C, M, N, K, count, s,
+                                                                                    parts, W, first, compact);
+      } else if (rows == Rows::kBOnly) {
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true, false>>(A, B, C, M, N, K, count, s,
+                                                                                    parts, W, first, compact);
+      } else {
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
+                                                                       compact);
+      }
+  }
+}
+
 // The k-split kernel with tile x tile tiles over tiles [first, first + count)
-// of the grouped order (count < 0: all of them); 16-byte copies when the rows
-// allow them. parts > 1: each tile's reduction also split over `parts`
-// workgroups writing partial tiles to W (at their place in copies of C, or in
-// compact per-tile slots).
+// of the grouped order (count < 0: all of them); 16-byte copies of each
+// operand whose rows allow them. parts > 1: each tile's reduction also split
+// over `parts` workgroups writing partial tiles to W (at their place in
+// copies of C, or in compact per-tile slots).
 int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
                   hipStream_t s, int parts = 1, float* W = nullptr, int first = 0, int compact = 0) {
-  const bool vec = mfma_vec_ok(A, B, C, N, K);
+  const Rows rows = rows_of(A, B, C, N, K);
   switch (tile) {
-    case FGR_TILE_128:
-      return vec ? launch_ksplit_cfg<Ksplit128>(A, B, C, M, N, K, count, s, parts, W, first, compact)
-                 : FGR_ERR_BAD_PATH;
-    case FGR_TILE_64:
-      return vec ? launch_ksplit_cfg<Ksplit64>(A, B, C, M, N, K, count, s, parts, W, first, compact)
-                 : launch_ksplit_cfg<Ksplit64s>(A, B, C, M, N, K, count, s, parts, W, first, compact);
-    case FGR_TILE_32:
-      return vec ? launch_ksplit_cfg<Ksplit32>(A, B, C, M, N, K, count, s, parts, W, first, compact)
-                 : launch_ksplit_cfg<Ksplit32s>(A, B, C, M, N, K, count, s, parts, W, first, compact);
+    case FGR_TILE_128: return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
+    case FGR_TILE_64: return launch_ksplit_rows<64>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
+    case FGR_TILE_32: return launch_ksplit_rows<32>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
     case FGR_TILE_32X128:
-      return vec ? launch_ksplit_cfg<Ksplit32x128>(A, B, C, M, N, K, count, s, parts, W, first, compact)
-                 : launch_ksplit_cfg<Ksplit32x128s>(A, B, C, M, N, K, count, s, parts, W, first, compact);
+      return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
     default: return FGR_ERR_BAD_PATH;
   }
 }
@@ -619,7 +649,8 @@ int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M
   }
   const bool vec = mfma_vec_ok(A, B, C, N, K);
   if (tile == FGR_TILE_128)
-    return vec ? launch_split_tail<128, true>(A, B, C, M, N, K, full, rem, cus, s) : FGR_ERR_BAD_PATH;
+    return vec ? launch_split_tail<128, true>(A, B, C, M, N, K, full, rem, cus, s)
+               : launch_split_tail<128, false>(A, B, C, M, N, K, full, rem, cus, s);
   if (tile == FGR_TILE_64)
     return vec ? launch_split_tail<64, true>(A, B, C, M, N, K, full, rem, cus, s)
                : launch_split_tail<64, false>(A, B, C, M, N, K, full, rem, cus, s);
@@ -706,14 +737,14 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
-      // N >= 64; tiles of 128 (16-byte rows only) or 64, and 32 or 32x128 without the tail form
-      if (N < 64 || (tile == FGR_TILE_128 && !mfma_vec_ok(A, B, C, N, K)) || tile == FGR_TILE_256 ||
+      // N >= 64; tiles of 128 (16-byte rows of A or B) or 64, and 32 or 32x128 without the tail form
+      if (N < 64 || (tile == FGR_TILE_128 && !ksplit128_ok(A, B, C, N, K)) || tile == FGR_TILE_256 ||
           ((tile == FGR_TILE_32 || tile == FGR_TILE_32X128) && path == FGR_PATH_MFMA_KSPLIT_TAIL))
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SPLITK:
-      // N >= 128 (two parts of at least 8 chunks); tiles of 128 (16-byte rows only), 64 or 32
-      if (N < 128 || (tile == FGR_TILE_128 && !mfma_vec_ok(A, B, C, N, K)) || tile == FGR_TILE_256)
+      // N >= 128 (two parts of at least 8 chunks); tiles of 128 (16-byte rows of A or B), 64 or 32
+      if (N < 128 || (tile == FGR_TILE_128 && !ksplit128_ok(A, B, C, N, K)) || tile == FGR_TILE_256)
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_VALU:

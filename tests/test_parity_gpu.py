@@ -363,6 +363,23 @@ def test_direct_copy_operand_alignments_exact(shape, offsets):
                  f"{shape} {offsets} tail form")
 
 
+@pytest.mark.parametrize("shape,offsets", [
+    ((300, 1023, 260), (0, 0, 0)), ((300, 1024, 259), (0, 0, 0)), ((300, 1024, 260), (0, 0, 1)),
+    ((300, 1024, 260), (1, 0, 0)), ((300, 1024, 260), (0, 2, 0)), ((300, 1023, 259), (0, 0, 0)),
+], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_ksplit_operand_alignments_exact(shape, offsets):
+    # the k-split kernel likewise picks 16- or 4-byte copies per operand, at
+    # every tile size, split across workgroups or not; exact on integer data
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=24)
+    Cref, _ = oracle.gemm(A, B)
+    say(f"k-split copies {shape} offsets {offsets}")
+    for path, tile in [(fgr.PATH_MFMA_KSPLIT, 64), (fgr.PATH_MFMA_KSPLIT, 32), (fgr.PATH_MFMA_KSPLIT, fgr.TILE_32X128),
+                       (fgr.PATH_MFMA_SPLITK, 64), (fgr.PATH_MFMA_SPLITK, fgr.TILE_32X128),
+                       (fgr.PATH_MFMA_KSPLIT_TAIL, 64)]:
+        assert_exact(gpu_gemm(A, B, path, tile, offsets=offsets), Cref, f"{shape} {offsets} path={path} tile={tile}")
+
+
 @pytest.mark.parametrize("shape", [(1023, 1025, 1027), (1024, 1024, 1024), (300, 2000, 260), (1, 3, 1), (129, 17, 5)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_vector_alu_path_exact(shape):
