@@ -283,12 +283,12 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     }
     // fewer 64x64 tiles than CUs: 64x64 or 32x32 k-split tiles, with the
     // reduction also split across workgroups where that is estimated faster
-    // (unsplit 32x32 tiles of rows that are not 16-byte aligned go to the
-    // split kernel, measured as fast or faster with 4-byte loads)
+    // (the k-split 32x32 tiles measured faster than the split kernel's also
+    // with 4-byte copies: 400 x 1000 x 401 10.0 vs 14.8 us, 512 x 4095 x 512
+    // 30.8 vs 50.9)
     const SplitPlan sp = splitk_plan(M, N, K, cus);
     if (sp.parts >= 2) return {FGR_PATH_MFMA_SPLITK, sp.tile};
-    if (sp.tile == FGR_TILE_64) return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_64};
-    return {vec ? FGR_PATH_MFMA_KSPLIT : FGR_PATH_MFMA_SPLIT, FGR_TILE_32};
+    return {FGR_PATH_MFMA_KSPLIT, sp.tile};
   }
   // N < 64 with fewer 64x64 tiles than CUs: the split kernel's 32x32 tiles
   return {FGR_PATH_MFMA_SPLIT, FGR_TILE_32};

@@ -268,7 +268,7 @@ def test_large_ragged_sampled(shape):
     ((2048, 128, 2048), fgr.PATH_MFMA_KSPLIT, 128), ((2040, 1000, 2044), fgr.PATH_MFMA_KSPLIT, 128),
     ((2176, 136, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128), ((3072, 132, 3076), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
     ((1024, 200, 1024), fgr.PATH_MFMA_KSPLIT, 64), ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
-    ((1536, 104, 1540), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((509, 300, 515), fgr.PATH_MFMA_SPLIT, 32),
+    ((1536, 104, 1540), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((509, 300, 515), fgr.PATH_MFMA_KSPLIT, 32),
     ((512, 128, 512), fgr.PATH_MFMA_KSPLIT, 32),
     # long reductions: the tail tiles' reduction split across workgroups
     ((1023, 4097, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((2176, 4096, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
