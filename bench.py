@@ -16,7 +16,10 @@ clock. Prints ONE JSON line:
                FLOP (or bytes) per launch over that duration, against the
                MI355X peak; `traffic` = HBM bytes per launch from rocprofv3
                FETCH_SIZE / WRITE_SIZE counters (profiles/), or null if the
-               kernel sources changed since those counters were taken
+               kernel sources changed since those counters were taken;
+               `counters` = the dominant kernel's matrix-core busy fraction,
+               LDS busy fraction, LDS bank conflicts per access and MFMA
+               FLOP / 2MNK from a rocprofv3 --pmc run (same file, same rule)
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
                (leading rows of A), on this host's cores
 
@@ -71,6 +74,24 @@ def recorded_traffic(workload: str):
     return int(val.group(1))
 
 
+def recorded_counters(workload: str):
+    """Matrix-core and LDS counters of the dominant kernel from
+    profiles/<workload>_traffic.md, if current (same kernel sources)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    src = re.search(r"kernel-source-sha256:\s*([0-9a-f]+)", text)
+    if not src or src.group(1) != kernel_source_hash():
+        return None
+    out = {}
+    for key in ("mfma-busy", "lds-bank-conflicts-per-access", "lds-busy", "mfma-flop-per-2mnk"):
+        m = re.search(rf"{key}:\s*([0-9.eE+-]+)", text)
+        if m:
+            out[key.replace("-", "_")] = float(m.group(1))
+    return out or None
+
+
 def _csv_rows(path):
     import csv
 
@@ -86,13 +107,20 @@ def _find(directory, suffix):
     raise FileNotFoundError(f"no *{suffix} under {directory}")
 
 
-def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_path, warmup=5):
+SQ_COUNTERS = ("MfmaUtil", "LdsUtil", "LdsBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_F32")
+
+
+def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_path, warmup=5, sq_dir=None):
     """Write the rocprofv3 summary of one workload's dominant kernel.
 
     trace_dir: a --kernel-trace --stats run; fetch_dir / write_dir: --pmc
     FETCH_SIZE / WRITE_SIZE runs of bench.py --calibrate-copy. Each counter
     is scaled by (known bytes of the plain 512 MiB device copy) / (what the
-    same counter reads for that copy)."""
+    same counter reads for that copy). sq_dir (optional): a --pmc run of
+    rocprofv3's derived MfmaUtil (matrix-core busy cycles over GPU-active
+    cycles times SIMDs, percent), LdsUtil (percent), LdsBankConflict (bank
+    conflict cycles per conflict-free LDS cycle) and the raw
+    SQ_INSTS_VALU_MFMA_MOPS_F32 (FP32 MFMA multiply-or-add operations / 512)."""
     stats = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
     stats.sort(key=lambda r: float(r["TotalDurationNs"]), reverse=True)
     top = stats[0]
@@ -153,9 +181,44 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_
         "",
         f"hbm-bytes-per-launch: {total}",
         f"ratio to algorithmic bytes: {total / w.algorithmic_bytes:.2f}",
-        f"kernel-source-sha256: {kernel_source_hash()}",
         "",
     ]
+    if sq_dir is not None:
+        rows = _csv_rows(_find(sq_dir, "counter_collection.csv"))
+        kernels = []
+        for r in rows:
+            if "copyBuffer" not in r["Kernel_Name"] and r["Kernel_Name"] not in kernels:
+                kernels.append(r["Kernel_Name"])
+
+        def avg(kernel, counter):
+            v = [float(r["Counter_Value"]) for r in rows
+                 if r["Kernel_Name"] == kernel and r["Counter_Name"] == counter]
+            return (sum(v) / len(v), len(v)) if v else (float("nan"), 0)
+
+        lines += [
+            "## Matrix cores and LDS (--pmc " + " ".join(SQ_COUNTERS) + ", averages per dispatch)",
+            "",
+            "MFMA busy = MfmaUtil (percent of GPU-active cycles x SIMDs with the matrix unit busy); "
+            "MFMA FLOP = 512 x SQ_INSTS_VALU_MFMA_MOPS_F32 (zero-padded edge tiles count too); "
+            "LDS bank conflicts = conflict cycles per conflict-free LDS cycle.",
+            "",
+            "| kernel | dispatches | MFMA busy % | MFMA FLOP / dispatch | LDS busy % | LDS bank conflicts |",
+            "|---|---|---|---|---|---|",
+        ]
+        for k in kernels:
+            mu, n = avg(k, "MfmaUtil")
+            lines.append(f"| {k} | {n} | {mu:.1f} | {avg(k, 'SQ_INSTS_VALU_MFMA_MOPS_F32')[0] * 512:.4g} "
+                         f"| {avg(k, 'LdsUtil')[0]:.2f} | {avg(k, 'LdsBankConflict')[0]:.4f} |")
+        mops = avg(top["Name"], "SQ_INSTS_VALU_MFMA_MOPS_F32")[0]
+        lines += [
+            "",
+            f"Dominant kernel: mfma-busy: {avg(top['Name'], 'MfmaUtil')[0] / 100:.4f}",
+            f"lds-busy: {avg(top['Name'], 'LdsUtil')[0] / 100:.4f}",
+            f"lds-bank-conflicts-per-access: {avg(top['Name'], 'LdsBankConflict')[0]:.4f}",
+            f"mfma-flop-per-2mnk: {mops * 512 / w.flops:.4f}",
+            "",
+        ]
+    lines += [f"kernel-source-sha256: {kernel_source_hash()}", ""]
     with open(out_path, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines))
     return out_path
@@ -309,13 +372,16 @@ def main() -> int:
                          "per variant and exit (the controlled comparison of the LeetGPU write-up)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/<workload>_traffic.md from three rocprofv3 output folders and exit")
+    ap.add_argument("--summarize-sq", metavar="SQ_DIR", default=None,
+                    help="(with --summarize) a rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " run to add")
     ap.add_argument("--command", action="append", default=[],
                     help="(with --summarize) a command that produced the folders, recorded in the summary")
     args = ap.parse_args()
 
     if args.summarize:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_traffic.md")
-        print(summarize_profiles(args.workload, *args.summarize, args.command, out, args.warmup))
+        print(summarize_profiles(args.workload, *args.summarize, args.command, out, args.warmup,
+                                 sq_dir=args.summarize_sq))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -393,6 +459,7 @@ def main() -> int:
         metric = METRIC if args.workload == "leetgpu8192" else f"FP32 GEMM TFLOP/s at M={w.M},N={w.N},K={w.K}"
     roof["frac"] = round(achieved / roof["peak"], 4)
     roof["traffic"] = recorded_traffic(args.workload)
+    roof["counters"] = recorded_counters(args.workload)
     roof["launch_ms"] = {
         "mean": round(avg_launch_s * 1e3, 4),
         "min": round(min(launch_ms), 4),

@@ -140,26 +140,33 @@ struct SplitPlan {
   int parts;
 };
 
-// Estimated time (seconds) of k-split tiles of size t whose reduction is split
-// into p parts, on `cus` CUs at 2.4 GHz: the larger of the MFMA time (a t x t
-// tile over L reduction indices is t^2 L / 128 cycles of its four SIMDs, at
-// 70% of peak, 10% less time when two or more workgroups share a CU) and the
-// HBM time (A and B panels of every tile, 35% of them from HBM and the rest
-// from L2, at 5 TB/s), plus 2 us per round of workgroups and, for a split,
-// 20 us (workspace, second launch, the host's extra calls) and its P M K 8
-// bytes. The constants are fitted to MI355X measurements of 19 shapes with
-// few output tiles, tiles 64 and 32, P = 1 .. 128 (the chosen plan within 6%
-// of the best measured one on every shape, small ones included).
+// Estimated time (seconds) of one call with k-split tiles of size t whose
+// reduction is split into p parts, on `cus` CUs at 2.4 GHz. GPU side: the
+// larger of the MFMA time of the busiest CU (its workgroups, each a t x t tile
+// over N / p reduction indices, t^2 N / (128 p) cycles of its four SIMDs, at
+// an efficiency of 0.9 for 64x64 and 0.7 for 32x32 tiles, 10% more when two
+// or more of them share the CU) and the HBM time (A and B panels of every
+// tile, 35% of them from HBM and the rest from L2, at 5 TB/s), plus 6 us and
+// 1 us per workgroup of the busiest CU and, for a split, 6 us and the P M K 8
+// bytes of partial tiles written and read back. Host side: 9 us per call, 30
+// us with a split (workspace allocation and free, second launch); the two
+// overlap, so the call takes the longer. Ties go to the smaller GPU time.
+// The constants are fitted to MI355X measurements of 24 shapes with few output
+// tiles (M, K from 96 to 1024, N from 1024 to 262144; 64x64 and 32x32 tiles,
+// P = 1 .. 256; the chosen plan within 6% of the best measured one on every
+// shape, where the previous estimate, which added the host cost to the GPU
+// time, lost up to 35%: 1024 x 32768 x 512 387 us against 286).
 double splitk_time(int t, int p, int M, int N, int K, int cus) {
   const double tiles = (double)cdiv(M, t) * (double)cdiv(K, t);
-  const double rounds = std::ceil(tiles * p / cus);
+  const double per_cu = std::ceil(tiles * p / cus);  // workgroups on the busiest CU
   const int resident = t >= 128 ? 1 : t >= 64 ? 2 : 4;  // workgroups per CU (LDS)
-  const double shared = std::min<double>(rounds, resident) >= 2 ? 0.9 : 1.0;
-  const double t_mfma = shared * rounds * ((double)t * t * ((double)N / p) / 128.0) / (2.4e9 * 0.7);
+  const double eff = (t >= 64 ? 0.9 : 0.7) * (std::min<double>(per_cu, resident) >= 2 ? 1.1 : 1.0);
+  const double t_mfma = per_cu * ((double)t * t * ((double)N / p) / 128.0) / (2.4e9 * eff);
   const double t_hbm = 4.0 * N * tiles * 2.0 * t * 0.35 / 5e12;
-  double t_fixed = rounds * 2e-6;
-  if (p > 1) t_fixed += 20e-6 + (double)p * M * K * 8.0 / 5e12;
-  return std::max(t_mfma, t_hbm) + t_fixed;
+  double gpu = std::max(t_mfma, t_hbm) + 6e-6 + per_cu * 1e-6;
+  if (p > 1) gpu += 6e-6 + (double)p * M * K * 8.0 / 5e12;
+  const double host = p > 1 ? 30e-6 : 9e-6;
+  return std::max(host, gpu) + 1e-3 * gpu;  // the small second term breaks ties
 }
 
 // Parts to try: powers of two, each part at least 256 reduction indices long

@@ -291,9 +291,9 @@ def test_ksplit_exact(shape, path, tile):
 
 
 @pytest.mark.parametrize("shape,tile", [
-    ((128, 262144, 128), 64), ((256, 16384, 256), 32), ((100, 30000, 300), 32), ((16, 65536, 64), 32),
+    ((128, 262144, 128), 64), ((256, 16384, 256), 64), ((100, 30000, 300), 64), ((16, 65536, 64), 32),
     ((130, 20000, 66), 32),
-    ((96, 50001, 97), 32), ((64, 16384, 64), 32)], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+    ((96, 50001, 97), 64), ((64, 16384, 64), 32), ((512, 8192, 512), 64)], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_split_reduction_exact(shape, tile):
     # few output tiles, long reduction: each tile's reduction split into parts
     # over workgroups, partial tiles added in part order by a second kernel;
