@@ -148,14 +148,15 @@ struct SplitPlan {
 // or more of them share the CU) and the HBM time (A and B panels of every
 // tile, 35% of them from HBM and the rest from L2, at 5 TB/s), plus 6 us and
 // 1 us per workgroup of the busiest CU and, for a split, 6 us and the P M K 8
-// bytes of partial tiles written and read back. Host side: 9 us per call, 30
-// us with a split (workspace allocation and free, second launch); the two
-// overlap, so the call takes the longer. Ties go to the smaller GPU time.
+// bytes of partial tiles written and read back. Host side (measured): 9 us per
+// call, 15 us with a split (second launch, workspace lookup and event); the
+// two overlap, so the call takes the longer. Ties go to the smaller GPU time.
 // The constants are fitted to MI355X measurements of 24 shapes with few output
 // tiles (M, K from 96 to 1024, N from 1024 to 262144; 64x64 and 32x32 tiles,
-// P = 1 .. 256; the chosen plan within 6% of the best measured one on every
-// shape, where the previous estimate, which added the host cost to the GPU
-// time, lost up to 35%: 1024 x 32768 x 512 387 us against 286).
+// P = 1 .. 256): the chosen plan is within 5% of the best measured one on each
+// of them and within 7% on 18 others, where the previous estimate, which added
+// the host cost to the GPU time, lost up to 35% (1024 x 32768 x 512: 387 us
+// against 286).
 double splitk_time(int t, int p, int M, int N, int K, int cus) {
   const double tiles = (double)cdiv(M, t) * (double)cdiv(K, t);
   const double per_cu = std::ceil(tiles * p / cus);  // workgroups on the busiest CU
@@ -165,7 +166,7 @@ double splitk_time(int t, int p, int M, int N, int K, int cus) {
   const double t_hbm = 4.0 * N * tiles * 2.0 * t * 0.35 / 5e12;
   double gpu = std::max(t_mfma, t_hbm) + 6e-6 + per_cu * 1e-6;
   if (p > 1) gpu += 6e-6 + (double)p * M * K * 8.0 / 5e12;
-  const double host = p > 1 ? 30e-6 : 9e-6;
+  const double host = p > 1 ? 15e-6 : 9e-6;
   return std::max(host, gpu) + 1e-3 * gpu;  // the small second term breaks ties
 }
 
@@ -333,16 +334,22 @@ int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStre
   return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
 }
 
-// Work for a reduction split across workgroups: a stream-ordered workspace of
-// parts x M x K floats (taken from a per-device pool on the caller's stream and
-// given back with hipFreeAsync on it, so calls on different streams never
-// share one), the partial products into it, then the parts added into C.
+// Work for a reduction split across workgroups: a workspace of parts x M x K
+// floats, the partial products into it, then the parts added into C. The
+// workspace is either the caller's stream's cached one (below), borrowed with
+// the cache lock held until the call's last kernel is enqueued, or a
+// stream-ordered allocation from a per-device pool on the caller's stream,
+// given back with hipFreeAsync on it. Either way calls on different streams
+// never share one.
+struct CachedWorkspace;
+
 struct PartsWorkspace {
   float* w = nullptr;
   hipStream_t s = nullptr;
-  ~PartsWorkspace() {
-    if (w) (void)hipFreeAsync(w, s);
-  }
+  bool owned = false;                 // allocated for this call
+  CachedWorkspace* cached = nullptr;  // or borrowed from the stream's cache entry
+  std::unique_lock<std::mutex> cache_lock;
+  ~PartsWorkspace();
 };
 
 // Freed workspace a device's pool keeps for reuse instead of returning it at
@@ -378,17 +385,109 @@ hipMemPool_t workspace_pool() {
   return d.pool;
 }
 
-int alloc_floats(PartsWorkspace& ws, size_t floats, hipStream_t s) {
-  ws.s = s;
-  const size_t bytes = floats * sizeof(float);
+hipError_t pool_alloc(float** w, size_t bytes, hipStream_t s) {
   hipMemPool_t pool = workspace_pool();
-  const hipError_t e = pool ? hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws.w), bytes, pool, s)
-                            : hipMallocAsync(reinterpret_cast<void**>(&ws.w), bytes, s);
-  if (e != hipSuccess) {
+  return pool ? hipMallocFromPoolAsync(reinterpret_cast<void**>(w), bytes, pool, s)
+              : hipMallocAsync(reinterpret_cast<void**>(w), bytes, s);
+}
+
+// Workspace kept between calls, one per stream handle (up to kCachedStreams
+// per process, each up to kCachedMaxBytes): a stream-ordered allocation and
+// free cost about 9 us of host time per call (measured on MI355X; a split
+// call took 30 us of host time against 9 us unsplit). Each entry has an
+// event recorded behind the last kernel that used its buffer, and every call
+// that borrows the buffer first makes its stream wait for that event: on the
+// same stream the wait is already satisfied by stream order, and a new stream
+// that happens to reuse a destroyed one's handle still waits for the old
+// stream's work. The lock, held from the lookup until the call's last kernel
+// and the event are enqueued, keeps two threads' calls on one stream from
+// interleaving their kernels. A buffer too small for a call is freed with
+// hipFreeAsync on the stream, behind that wait, and replaced. Buffers are
+// never returned otherwise (the process holds at most kCachedStreams x
+// kCachedMaxBytes); a full table, hipStreamPerThread (one handle for many
+// streams), stream capture (the workspace then becomes a graph allocation)
+// and larger workspaces take the per-call allocation.
+constexpr int kCachedStreams = 16;
+constexpr size_t kCachedMaxBytes = size_t(64) << 20;
+constexpr size_t kCachedGrain = size_t(1) << 20;
+
+struct CachedWorkspace {
+  hipStream_t stream = nullptr;
+  int dev = -1;
+  hipEvent_t done = nullptr;  // recorded behind the buffer's last use
+  bool recorded = false;
+  float* w = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_ws_mu;
+CachedWorkspace g_ws[kCachedStreams];
+int g_ws_used = 0;
+
+PartsWorkspace::~PartsWorkspace() {
+  if (cached) {
+    cached->recorded = hipEventRecord(cached->done, s) == hipSuccess;
+    if (!cached->recorded) (void)hipGetLastError();
+  } else if (w && owned) {
+    (void)hipFreeAsync(w, s);
+  }
+}  // cache_lock, if held, is released after the event is enqueued
+
+bool cached_workspace(PartsWorkspace& ws, size_t bytes, hipStream_t s) {
+  if (bytes > kCachedMaxBytes || s == hipStreamPerThread) return false;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  int dev = -1;
+  if (hipStreamIsCapturing(s, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone ||
+      hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  std::unique_lock<std::mutex> lock(g_ws_mu);
+  CachedWorkspace* e = nullptr;
+  for (int i = 0; i < g_ws_used && !e; ++i)
+    if (g_ws[i].stream == s && g_ws[i].dev == dev) e = &g_ws[i];
+  if (!e) {
+    if (g_ws_used == kCachedStreams) return false;
+    hipEvent_t ev = nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    e = &g_ws[g_ws_used++];
+    *e = CachedWorkspace{s, dev, ev, false, nullptr, 0};
+  }
+  if (e->recorded && hipStreamWaitEvent(s, e->done, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (e->bytes < bytes) {
+    const size_t grown = (bytes + kCachedGrain - 1) / kCachedGrain * kCachedGrain;
+    float* w = nullptr;
+    if (pool_alloc(&w, grown, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    if (e->w) (void)hipFreeAsync(e->w, s);
+    e->w = w;
+    e->bytes = grown;
+  }
+  ws.w = e->w;
+  ws.s = s;
+  ws.cached = e;
+  ws.cache_lock = std::move(lock);
+  return true;
+}
+
+int alloc_floats(PartsWorkspace& ws, size_t floats, hipStream_t s) {
+  const size_t bytes = floats * sizeof(float);
+  if (cached_workspace(ws, bytes, s)) return FGR_OK;
+  ws.s = s;
+  if (pool_alloc(&ws.w, bytes, s) != hipSuccess) {
     ws.w = nullptr;
     (void)hipGetLastError();  // the caller runs the unsplit kernel instead
     return FGR_ERR_LAUNCH;
   }
+  ws.owned = true;
   return FGR_OK;
 }
 

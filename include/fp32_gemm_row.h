@@ -22,8 +22,9 @@
  *
  * Memory and ownership
  *   A, B and C are DEVICE pointers owned by the caller. The library never
- *   allocates, frees or synchronises; it keeps no workspace and no state
- *   besides a per-device cache of device properties. C is overwritten
+ *   synchronises. It keeps a per-device cache of device properties and, for
+ *   the paths that split a reduction across workgroups, a workspace (see
+ *   solve() below); nothing else is allocated. C is overwritten
  *   (every one of its M*K elements is written once; its prior contents,
  *   even NaN, are ignored - the write-back rule of the CUDA study notes,
  *   section 3, and "the result must be stored in C" of the LeetGPU
@@ -133,14 +134,21 @@ extern "C" {
  * Workspace: when the output has too few tiles (or, for M <= 8, too few
  * 32-column blocks) to give every CU a workgroup and N is long, the reduction
  * is split into P parts across workgroups (paths MFMA_SPLITK and GEMV_*): the
- * library then takes a workspace of P*M*K floats, stream-ordered on `stream`
- * (at most 16 MiB on a 256-CU device when solve() picks the split; a forced
- * MFMA_SPLITK on a large output takes P = 2, i.e. 2*M*K floats), and releases
- * it with hipFreeAsync on `stream` after its last kernel, so calls on
- * different streams never share one. The workspace comes from a memory pool
- * the library creates per device on first use (hipMemPoolCreate; it keeps up
- * to 64 MiB of freed workspace for reuse and lives until the process ends),
- * or from the device's default pool if that creation failed. If the
+ * library then needs a workspace of P*M*K floats (at most 16 MiB on a
+ * 256-CU device when solve() picks the split; a forced MFMA_SPLITK on a large
+ * output takes P = 2, i.e. 2*M*K floats). Calls on different streams never
+ * share one. Each stream (up to 16 per process, identified by handle and
+ * stream id) keeps its workspace between calls, up to 64 MiB: it is
+ * allocated stream-ordered on `stream` at the stream's first split call,
+ * replaced (the old one freed with hipFreeAsync on `stream`) when a call
+ * needs more, and otherwise held until the process ends. Calls from several
+ * host threads on one stream are serialised while they enqueue. Otherwise
+ * (more streams, larger workspaces, hipStreamPerThread, or `stream` under
+ * capture) the call allocates its workspace stream-ordered on `stream` and
+ * frees it with hipFreeAsync after its last kernel. Allocations come from a
+ * memory pool the library creates per device on first use (hipMemPoolCreate;
+ * it keeps up to 64 MiB of freed memory for reuse and lives until the process
+ * ends), or from the device's default pool if that creation failed. If the
  * allocation fails the unsplit kernel runs instead (same result up to
  * rounding order). Results are deterministic: the parts are added in a fixed
  * order. solve() can be captured into a HIP graph (stream capture on

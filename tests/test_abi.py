@@ -277,7 +277,7 @@ def test_split_reduction_choices():
     assert sp(A0, B0, C0, 512, 4096, 512) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles
     assert sp(A0, B0, C0, 96, 4096, 4096) == fgr.PATH_MFMA_KSPLIT
-    assert sp(A0, B0, C0, 200, 2048, 200) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 640, 2048, 640) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 65, 8192, 8192) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 100, 64) == fgr.PATH_MFMA_KSPLIT
     # tiles enough for every CU: the whole-device kernels, never a split

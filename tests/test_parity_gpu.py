@@ -665,6 +665,45 @@ def test_concurrent_calls_on_separate_streams():
             assert_exact(C, Cref, f"{M}x{N}x{K} call {j}")
 
 
+def test_split_workspace_reuse_between_calls():
+    # split calls back to back without synchronising: each stream's cached
+    # workspace is reused by every call on it, and replaced by a larger one
+    # mid-sequence (the old one freed in stream order); two streams
+    # interleave their calls, each with its own workspace; then the
+    # per-thread default stream (handle 2), which takes a workspace per call.
+    # Exact on integer data.
+    shapes = [(128, 16384, 128), (256, 65536, 256), (4, 100000, 96), (128, 16384, 128), (16, 65536, 64),
+              (512, 8192, 512)]
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = synth.make_inputs(M, N, K, "integer", seed=40 + i)
+        Cref, _ = oracle.gemm(A, B)
+        assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) in (fgr.PATH_MFMA_SPLITK, fgr.PATH_GEMV_VEC)
+        cases.append((M, N, K, torch.from_numpy(A.ravel()).to(DEV), torch.from_numpy(B.ravel()).to(DEV), Cref))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(2):
+        for i, (M, N, K, dA, dB, _) in enumerate(cases):
+            for j, st in enumerate(streams):
+                dC = torch.full((M * K,), float("nan"), device=DEV)
+                st.wait_stream(torch.cuda.current_stream())  # dC's fill
+                fgr.solve(dA, dB, dC, M, N, K, stream=st)
+                dC.record_stream(st)
+                outs.append((i, f"stream {j} round {rep}", dC))
+    per_thread = 2  # hipStreamPerThread
+    for i, (M, N, K, dA, dB, _) in enumerate(cases):
+        dC = torch.full((M * K,), float("nan"), device=DEV)
+        torch.cuda.synchronize()
+        fgr.solve(dA, dB, dC, M, N, K, stream=per_thread)
+        outs.append((i, "per-thread stream", dC))
+    torch.cuda.synchronize()
+    for i, label, dC in outs:
+        M, N, K, _, _, Cref = cases[i]
+        say(f"workspace reuse {M}x{N}x{K} {label}")
+        assert_exact(dC.cpu().numpy().reshape(M, K), Cref, f"{M}x{N}x{K} {label}")
+
+
 @pytest.mark.parametrize("shape", [(512, 512, 512), (1023, 1025, 1027), (100, 30000, 300), (1, 262144, 64),
                                    (16, 8192, 4096)], ids=lambda s: "x".join(map(str, s)))
 def test_graph_capture_replays(shape):
