@@ -118,17 +118,28 @@ def status_string(code: int) -> str:
     return load_library().fgr_status_string(int(code)).decode()
 
 
+_torch = None
+
+
+def _torch_module():
+    global _torch
+    if _torch is None:
+        import torch
+
+        _torch = torch
+    return _torch
+
+
 def _address(x, need: int, name: str) -> int:
     """Device address of a float32 GPU tensor (checked) or a raw int address."""
     if isinstance(x, int):
         return x
-    import torch
-
+    torch = _torch_module()
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor or an int address")
     if x.dtype != torch.float32:
         raise TypeError(f"{name} must be float32, got {x.dtype}")
-    if x.device.type != "cuda":
+    if not x.is_cuda:
         raise ValueError(f"{name} must live on the GPU, got {x.device}")
     if not x.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -137,11 +148,21 @@ def _address(x, need: int, name: str) -> int:
     return x.data_ptr()
 
 
+def _current_stream_handle() -> int:
+    """torch's current stream on the current device, as a raw handle. The
+    raw accessor costs about 0.1 us per call against 2.8 us for
+    torch.cuda.current_stream().cuda_stream (which builds a Stream object);
+    the public form serves where the accessor is absent."""
+    torch = _torch_module()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
+
+
 def _stream_handle(stream) -> int:
     if stream is None:
-        import torch
-
-        return torch.cuda.current_stream().cuda_stream
+        return _current_stream_handle()
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream

@@ -665,6 +665,17 @@ def test_concurrent_calls_on_separate_streams():
             assert_exact(C, Cref, f"{M}x{N}x{K} call {j}")
 
 
+def test_default_stream_is_torchs_current_stream():
+    # solve() without a stream argument enqueues on torch's current stream
+    # (the binding reads its raw handle); inside `with torch.cuda.stream(s)`
+    # that is s
+    assert fgr._current_stream_handle() == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert fgr._current_stream_handle() == side.cuda_stream == torch.cuda.current_stream().cuda_stream
+    assert fgr._current_stream_handle() == torch.cuda.current_stream().cuda_stream
+
+
 def test_split_workspace_reuse_between_calls():
     # split calls back to back without synchronising: each stream's cached
     # workspace is reused by every call on it, and replaced by a larger one
