@@ -117,7 +117,8 @@ __device__ __forceinline__ void sched_spread() {
 template <class T>
 __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
-    int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact) {
+    int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact,
+    int nfull) {
   constexpr int S = T::S, BK = T::BK, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) float As0[T::kStageA];
   __shared__ __attribute__((aligned(1024))) float As1[T::kStageA];
@@ -150,30 +151,37 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int piece_a = wave * T::kPieceA;  // this wave's offset inside every A stage object
   const int piece_b = wave * T::kPieceB;  // and B stage object
 
-  // The launch covers tiles [first, first + ntiles) of the grouped order.
-  // Split across workgroups (parts > 1): the grid holds parts x ntiles
-  // workgroups; logical id = part * ntiles + tile, so that after the XCD
-  // renumbering the tiles of one part, which read the same reduction range of
-  // A and B, run on the same XCD and share its L2. Part p owns the chunks
-  // [nchunks p / parts, nchunks (p + 1) / parts) and writes its partial tile
-  // to the workspace W instead of C: at its place in a copy of C (W + p M K,
-  // row stride K) or, compact, to slot p ntiles + tile (BM x BN floats, row
-  // stride BN); a second kernel adds the parts. This wave's chunks are
-  // [c_begin, c_end) of the part's; at least 8 chunks per part give every
-  // wave >= 2.
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int ntiles = gridDim.x / parts;
+  // The launch covers tiles [first, first + nfull + ntiles) of the grouped
+  // order. The first nfull workgroups take whole tiles [first, first + nfull)
+  // (their whole reduction, results to C). The other gridDim.x - nfull take
+  // the ntiles tiles after them, each split across workgroups when parts > 1:
+  // parts x ntiles workgroups, logical id = part * ntiles + tile, so that
+  // after the XCD renumbering the tiles of one part, which read the same
+  // reduction range of A and B, run on the same XCD and share its L2. Part p
+  // owns the chunks [nchunks p / parts, nchunks (p + 1) / parts) and writes
+  // its partial tile to the workspace W instead of C: at its place in a copy
+  // of C (W + p M K, row stride K) or, compact, to slot p ntiles + tile (BM x
+  // BN floats, row stride BN); a second kernel adds the parts. Whole and split
+  // tiles in one grid run side by side (two workgroups fit a CU): a last
+  // partial wave of tiles then spreads over every CU next to the full wave
+  // instead of running after it. This wave's chunks are [c_begin, c_end) of
+  // the part's; at least 8 chunks per part give every wave >= 2.
+  const bool whole = (int)blockIdx.x < nfull;
+  const int grid = whole ? nfull : (int)gridDim.x - nfull;
+  const int logical = xcd_remap(whole ? (int)blockIdx.x : (int)blockIdx.x - nfull, grid);
+  const int kparts = whole ? 1 : parts;
+  const int ntiles = grid / kparts;
   const int part = logical / ntiles;
   const int tl = logical - part * ntiles;
   int tm, tn;
-  grouped_tile(first + tl, tiles_m, tiles_n, group, tm, tn);
+  grouped_tile(first + (whole ? 0 : nfull) + tl, tiles_m, tiles_n, group, tm, tn);
   const int m0 = tm * T::BM;
   const int k0 = tn * BN;
 
   const int nchunks = (N + BK - 1) / BK;
   const int n_first = N - BK * nchunks;  // in (-BK, 0]
-  const int pc0 = (int)((int64_t)nchunks * part / parts);
-  const int pn = (int)((int64_t)nchunks * (part + 1) / parts) - pc0;
+  const int pc0 = (int)((int64_t)nchunks * part / kparts);
+  const int pn = (int)((int64_t)nchunks * (part + 1) / kparts) - pc0;
   const int c_begin = pc0 + pn * wave / T::kWaves;
   const int c_end = pc0 + pn * (wave + 1) / T::kWaves;
   const int c_last = c_end - 1;
@@ -411,7 +419,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   if (wave * kSPW >= T::kSlices) return;  // small tiles: fewer slices than waves
   float* Ct;
   uint32_t ldc;  // row stride; row * ldc is formed in 64 bits (K may pass 2^25)
-  if (parts == 1) {
+  if (kparts == 1) {
     Ct = C + (int64_t)m0 * K + k0;
     ldc = (uint32_t)K;
   } else if (compact) {

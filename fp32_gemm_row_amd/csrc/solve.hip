@@ -631,13 +631,13 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
 
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
-                      int parts, float* W, int first, int compact) {
+                      int parts, float* W, int first, int compact, int nfull) {
   int tiles_m = (int)cdiv(M, Cfg::BM);
   int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
-  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &parts, &W, &first, &compact};
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &parts, &W, &first, &compact, &nfull};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
-                (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts, Cfg::kThreads, args, s);
+                nfull + (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts, Cfg::kThreads, args, s);
 }
 
 // k-split configurations by the row alignment of the product: 16-byte copies
@@ -645,23 +645,23 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
 // 4-byte copies of both; 128x128 tiles only in the first form (ksplit128_ok).
 template <int BM, int BN = BM>
 int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
-                       hipStream_t s, int parts, float* W, int first, int compact) {
+                       hipStream_t s, int parts, float* W, int first, int compact, int nfull) {
   switch (rows) {
     case Rows::kAll:
       return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                    compact);
+                                                                    compact, nfull);
     default:
       if constexpr (BM == 128) {
         return FGR_ERR_BAD_PATH;
       } else if (rows == Rows::kAOnly) {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(A, B, C, M, N, K, count, s,
-                                                                                    parts, W, first, compact);
+                                                                                    parts, W, first, compact, nfull);
       } else if (rows == Rows::kBOnly) {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true, false>>(A, B, C, M, N, K, count, s,
-                                                                                    parts, W, first, compact);
+                                                                                    parts, W, first, compact, nfull);
       } else {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                       compact);
+                                                                       compact, nfull);
       }
   }
 }
@@ -670,16 +670,22 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
 // of the grouped order (count < 0: all of them); 16-byte copies of each
 // operand whose rows allow them. parts > 1: each tile's reduction also split
 // over `parts` workgroups writing partial tiles to W (at their place in
-// copies of C, or in compact per-tile slots).
+// copies of C, or in compact per-tile slots). nfull > 0: the same grid first
+// runs whole tiles [first, first + nfull) into C, and the count split tiles
+// follow them.
 int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
-                  hipStream_t s, int parts = 1, float* W = nullptr, int first = 0, int compact = 0) {
+                  hipStream_t s, int parts = 1, float* W = nullptr, int first = 0, int compact = 0,
+                  int nfull = 0) {
   const Rows rows = rows_of(A, B, C, N, K);
   switch (tile) {
-    case FGR_TILE_128: return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
-    case FGR_TILE_64: return launch_ksplit_rows<64>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
-    case FGR_TILE_32: return launch_ksplit_rows<32>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
+    case FGR_TILE_128:
+      return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+    case FGR_TILE_64:
+      return launch_ksplit_rows<64>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+    case FGR_TILE_32:
+      return launch_ksplit_rows<32>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
     case FGR_TILE_32X128:
-      return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact);
+      return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
     default: return FGR_ERR_BAD_PATH;
   }
 }
@@ -723,6 +729,7 @@ int launch_ksplit_parts(int tile, const float* A, const float* B, float* C, int 
 }
 
 constexpr int kTailSplitMinN = 4096;
+constexpr int kMixedTailMinN = 1024;
 
 // Whole waves of tile x tile tiles on the k-split kernel, the last partial
 // wave's tiles cut into smaller split-reduction tiles (as launch_dma_tail) or,
@@ -732,11 +739,29 @@ int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M
   const int64_t tiles = cdiv(M, tile) * cdiv(K, tile);
   const int64_t full = tiles / cus * cus;
   const int64_t rem = tiles - full;
+  if (full > INT_MAX || rem > INT_MAX / 16) return FGR_ERR_BAD_DIMS;
+  // 64x64 tiles (two workgroups fit a CU) and N >= kMixedTailMinN: the tail
+  // tiles' reduction split over CUs / rem parts in the same grid as the whole
+  // tiles, so that they run next to the full wave on every CU, then their
+  // parts added. Measured on MI355X (us per call, separate tail launch vs one
+  // grid): 1023 x 1025 x 1027 41.0 vs 37.9, 2047 x 2049 x 2051 211 vs 203,
+  // 1536^3 75.0 vs 71.8, 1023 x 4097 x 1027 114.6 vs 109.1, 1040 x 2048 x
+  // 1040 53.9 vs 51.5; with short reductions the adding launch costs more
+  // than the overlap gives (1030 x 128 x 1030 13.9 vs 15.6, 1088 x 512 x 1024
+  // 19.4 vs 21.7).
+  const int mixed_parts = (int)std::min<int64_t>(cus / std::max<int64_t>(rem, 1), cdiv(N, 8) / 8);
+  if (tile == FGR_TILE_64 && N >= kMixedTailMinN && full > 0 && rem > 0 && mixed_parts >= 2) {
+    PartsWorkspace ws;
+    if (alloc_floats(ws, (size_t)mixed_parts * (size_t)rem * tile * tile, s) == FGR_OK) {
+      const int rc = launch_ksplit(tile, A, B, C, M, N, K, rem, s, mixed_parts, ws.w, 0, 1, (int)full);
+      if (rc != FGR_OK) return rc;
+      return launch_reduce_tiles(ws.w, C, M, K, tile, mixed_parts, (int)full, (int)rem, s);
+    }
+  }
   if (full > 0) {
     const int rc = launch_ksplit(tile, A, B, C, M, N, K, full, s);
     if (rc != FGR_OK || rem == 0) return rc;
   }
-  if (full > INT_MAX || rem > INT_MAX / 16) return FGR_ERR_BAD_DIMS;
   // With a long reduction the tail tiles' reduction is split over up to
   // CUs / rem parts (so every CU gets a workgroup), through compact per-tile
   // slots; otherwise, or without a workspace, the tail is cut into smaller

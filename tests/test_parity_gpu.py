@@ -273,6 +273,10 @@ def test_large_ragged_sampled(shape):
     # long reductions: the tail tiles' reduction split across workgroups
     ((1023, 4097, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((2176, 4096, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
     ((1088, 4100, 1024), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
+    # tails of 64x64 tiles with N >= 1024: whole and split tiles in one grid
+    # (16-byte copies of both operands, of B only, of A only)
+    ((1040, 2048, 1040), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((1024, 1025, 1088), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
+    ((1088, 1028, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((1536, 1536, 1536), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_ksplit_exact(shape, path, tile):
     # tiles whose reduction is split over a workgroup's waves (128, 64 or 32
