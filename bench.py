@@ -224,6 +224,66 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_
     return out_path
 
 
+def variant_kernel(name: str) -> str:
+    """The kernel (as the resource report and rocprofv3 name it) behind a
+    controlled-comparison variant name."""
+    parts = name.split()
+    if parts[0] == "direct":
+        ring = int(parts[1][len("ring"):])
+        return f"fgr::gemm_mfma_dma_kernel<fgr::DmaConfig<{ring}, true, true, true> >"
+    bufs = 1 if parts[1] == "single" else 2
+    bm, bn = (int(x) for x in parts[2].split("x"))
+    bk = int(parts[3][len("bk"):])
+    wn = 4 if bn == 256 else 2
+    return f"fgr::gemm_mfma_kernel<fgr::MfmaConfig<{bm}, {bn}, {bk}, 2, {wn}, 1, {bufs}>, true>"
+
+
+def summarize_ablation(workload, jsonl, sq_dir, resources, commands, out_path):
+    """profiles/<workload>_controlled_comparison.md: each variant's time
+    (bench.py --ablation), the compiler's resource report for its kernel, and
+    rocprofv3 counters (--pmc MfmaUtil LdsUtil LdsBankConflict) for it."""
+    rows = [json.loads(line) for line in open(jsonl) if line.startswith("{") and '"variant"' in line]
+    res = {}
+    for line in open(resources, encoding="utf-8"):
+        m = re.match(r"\| `void (.*?)` \| (.*) \|$", line.strip())
+        if m:
+            res[m.group(1)] = [c.strip() for c in m.group(2).split("|")]
+    counters = _csv_rows(_find(sq_dir, "counter_collection.csv"))
+
+    def avg(kernel, counter):
+        v = [float(r["Counter_Value"]) for r in counters
+             if r["Counter_Name"] == counter and r["Kernel_Name"].startswith("void " + kernel + "(")]
+        return sum(v) / len(v) if v else float("nan")
+
+    import synth
+
+    w = synth.WORKLOADS[workload]
+    lines = [
+        f"# Controlled comparison on {workload} (M={w.M}, N={w.N}, K={w.K})",
+        "",
+        "One variable at a time: LDS buffering (register-staged kernel with one LDS buffer, or two with",
+        "register prefetch; direct-copy kernel with an LDS ring of 3, 4 or 5 stages), output tile and",
+        "reduction chunk. Time: mean of per-launch HIP events. Resources: hipcc",
+        "-Rpass-analysis=kernel-resource-usage. Counters: rocprofv3 --pmc, averages per dispatch.",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):",
+        "",
+        *[f"    {c}" for c in commands],
+        "",
+        "| variant | ms | TFLOP/s | VGPRs | AGPRs | waves/SIMD | LDS bytes | spills | MFMA busy % | LDS busy % | LDS bank conflicts |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        k = variant_kernel(r["variant"])
+        vg, ag, occ, lds, spill, _ = (res.get(k) or ["?"] * 6)[:6]
+        lines.append(f"| {r['variant']} | {r['kernel_ms']:.3f} | {r['tflops']:.1f} | {vg} | {ag} | {occ} | {lds} | "
+                     f"{spill} | {avg(k, 'MfmaUtil'):.1f} | {avg(k, 'LdsUtil'):.2f} | {avg(k, 'LdsBankConflict'):.4f} |")
+    lines += ["", f"kernel-source-sha256: {kernel_source_hash()}", ""]
+    with open(out_path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    return out_path
+
+
 def kernel_ms(fn, steps, warmup, stream):
     """Mean of per-launch HIP-event durations on `stream`."""
     import torch
@@ -242,7 +302,9 @@ def kernel_ms(fn, steps, warmup, stream):
 
 
 def ablation(w, dA, dBs, dC, copies, steps, warmup, stream):
-    """Every (path, tile) the library accepts for this workload, timed alike."""
+    """Every (path, tile) the library accepts for this workload, then every
+    controlled-comparison kernel variant (LDS buffering x output tile x
+    reduction chunk), timed alike."""
     import fp32_gemm_row_amd as fgr
 
     variants = [(fgr.PATH_MFMA_DMA, 256), (fgr.PATH_MFMA_DMA_TAIL, 256)]
@@ -267,6 +329,20 @@ def ablation(w, dA, dBs, dC, copies, steps, warmup, stream):
             "workload": w.name, "path": fgr.PATH_NAMES[path], "tile": tile,
             "auto": (path, tile) == auto, "kernel_ms": round(ms, 5),
             "tflops": round(w.flops / ms / 1e9, 3), "gbs": round(w.algorithmic_bytes / ms / 1e6, 1),
+        }), flush=True)
+    # the controlled comparison: one kernel variant per buffering x tile x chunk
+    for v, name in enumerate(fgr.variant_names()):
+        def fn(i, v=v):
+            fgr.solve_variant(dA, dBs[i % copies], dC, w.M, w.N, w.K, v, stream=stream)
+
+        try:
+            fn(0)
+        except fgr.GemmError:
+            continue
+        ms = kernel_ms(fn, steps, warmup, stream)
+        print(json.dumps({
+            "workload": w.name, "variant": name, "kernel_ms": round(ms, 5),
+            "tflops": round(w.flops / ms / 1e9, 3),
         }), flush=True)
     return 0
 
@@ -374,10 +450,18 @@ def main() -> int:
                     help="write profiles/<workload>_traffic.md from three rocprofv3 output folders and exit")
     ap.add_argument("--summarize-sq", metavar="SQ_DIR", default=None,
                     help="(with --summarize) a rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " run to add")
+    ap.add_argument("--summarize-ablation", nargs=3, metavar=("ABLATION_JSONL", "SQ_DIR", "RESOURCES_MD"),
+                    help="write profiles/<workload>_controlled_comparison.md from a bench.py --ablation "
+                         "output, a rocprofv3 --pmc MfmaUtil LdsUtil LdsBankConflict run of it and the "
+                         "resource report, and exit")
     ap.add_argument("--command", action="append", default=[],
                     help="(with --summarize) a command that produced the folders, recorded in the summary")
     args = ap.parse_args()
 
+    if args.summarize_ablation:
+        out = os.path.join(ROOT, "profiles", f"{args.workload}_controlled_comparison.md")
+        print(summarize_ablation(args.workload, *args.summarize_ablation, args.command, out))
+        return 0
     if args.summarize:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_traffic.md")
         print(summarize_profiles(args.workload, *args.summarize, args.command, out, args.warmup,

@@ -72,6 +72,9 @@ EXPORTS = (
     "fgr_select_tile",
     "fgr_status_string",
     "fgr_version",
+    "fgr_variant_count",
+    "fgr_variant_name",
+    "fgr_solve_variant",
 )
 
 
@@ -110,6 +113,12 @@ def load_library(path: str = LIB_PATH):
     lib.fgr_status_string.restype = ctypes.c_char_p
     lib.fgr_version.argtypes = []
     lib.fgr_version.restype = ci
+    lib.fgr_variant_count.argtypes = []
+    lib.fgr_variant_count.restype = ci
+    lib.fgr_variant_name.argtypes = [ci]
+    lib.fgr_variant_name.restype = ctypes.c_char_p
+    lib.fgr_solve_variant.argtypes = [vp, vp, vp, ci, ci, ci, vp, ci]
+    lib.fgr_solve_variant.restype = ci
     _lib = lib
     return lib
 
@@ -217,3 +226,19 @@ def select_tile(A, B, C, M: int, N: int, K: int) -> int:
 
 def version() -> int:
     return int(load_library().fgr_version())
+
+
+def variant_names() -> list:
+    """Names of the controlled-comparison kernel variants, in index order."""
+    lib = load_library()
+    return [lib.fgr_variant_name(i).decode() for i in range(lib.fgr_variant_count())]
+
+
+def solve_variant(A, B, C, M: int, N: int, K: int, variant: int, stream=None) -> None:
+    """solve() with one controlled-comparison kernel variant alone."""
+    lib = load_library()
+    M, N, K, na, nb, nc = _dims(M, N, K)
+    a = _address(A, na, "A")
+    b = _address(B, nb, "B")
+    c = _address(C, nc, "C")
+    _check(lib.fgr_solve_variant(a, b, c, M, N, K, _stream_handle(stream), int(variant)))

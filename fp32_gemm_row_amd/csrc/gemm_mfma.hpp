@@ -78,10 +78,14 @@ __device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles
 //   BM x BN   output tile of a workgroup;  BK  reduction chunk per LDS stage
 //   WM x WN   waves per workgroup (each owns a (BM/WM) x (BN/WN) sub-tile)
 //   MINB      workgroups per CU the register budget must allow
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int MINB_ = 1>
+//   BUFS      LDS buffers: 2 = double buffer with register prefetch (the
+//             pipeline below), 1 = one buffer, loads and MFMAs in turn (the
+//             single-buffer control of the controlled comparison)
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MINB_ = 1, int BUFS_ = 2>
 struct MfmaConfig {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   static constexpr int kMinBlocks = MINB_;
+  static constexpr int kBufs = BUFS_;
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kWaveM = BM / WM;  // rows of C per wave
   static constexpr int kWaveN = BN / WN;  // columns of C per wave
@@ -93,7 +97,7 @@ struct MfmaConfig {
   static constexpr int kBQuads = BN / 4;   // float4 per B chunk row
   static constexpr int kAPerThread = BM * BK / 4 / kThreads;
   static constexpr int kBPerThread = BK * BN / 4 / kThreads;
-  static constexpr int kLdsFloats = 2 * (BM * kLdA + BK * kLdB);
+  static constexpr int kLdsFloats = kBufs * (BM * kLdA + BK * kLdB);
 
   static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(BK % 16 == 0, "BK must be a multiple of 16 (an even number of half-steps)");
@@ -102,6 +106,7 @@ struct MfmaConfig {
   static_assert(kThreads % kAQuads == 0 && kThreads % kBQuads == 0,
                 "a thread must keep the same column quad in every load slot");
   static_assert(kLdsFloats * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+  static_assert(kBufs == 1 || kBufs == 2, "one or two LDS buffers");
 };
 
 // One float4 slot of a chunk, loaded branch-free: an element outside the
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
   constexpr int H = BK / 8;  // half-steps per chunk
   __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
   float* const As0 = lds;
-  float* const Bs0 = lds + 2 * BM * T::kLdA;
+  float* const Bs0 = lds + T::kBufs * BM * T::kLdA;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -365,6 +370,30 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
   constexpr int kLoadSteps = H >= 3 ? H - 2 : 0;
   const int nchunks = (N + BK - 1) / BK;
   Frag f[2];
+  if constexpr (T::kBufs == 1) {
+    // One LDS buffer: each chunk is loaded into registers, written to LDS
+    // once every wave is done reading the previous chunk, and consumed after
+    // a second barrier; loads, LDS writes and MFMAs of a workgroup take turns
+    // (other workgroups on the CU are what overlaps them). Operand reads one
+    // half-step ahead as above.
+    for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) load_slot(s, c * BK);
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) store_slot(s, 0);
+      __syncthreads();
+      read_frag(f[0], 0, 0);
+      static_for<0, H - 1>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        read_frag(f[(h + 1) & 1], 0, h + 1);
+        mma(f[h & 1]);
+        sched_interleave<kMfmas, 0, 0, kReads>();
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      mma(f[(H - 1) & 1]);
+    }
+  } else {
 #pragma unroll
   for (int s = 0; s < kSlots; ++s) load_slot(s, 0);
 #pragma unroll
@@ -417,6 +446,7 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
     mma(f[(H - 1) & 1]);
+  }
   }
 
   // Epilogue: element r of lane l in block (i, j) is row 8*(r/4) + 4*lg + r%4,

@@ -948,6 +948,62 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   return FGR_ERR_BAD_PATH;
 }
 
+// The controlled comparison (buffering x output tile x reduction chunk, each
+// variant a kernel of its own, timed alike): the register-staged kernel with
+// one LDS buffer or two (with register prefetch), 256x256 / 256x128 / 128x128
+// tiles and 16- or 32-deep chunks, and the direct-copy kernel with LDS rings
+// of 3, 4 and 5 stages (256x256 tiles, 16-deep chunks). 16-byte rows only.
+struct Variant {
+  const char* name;
+  int (*run)(const float*, const float*, float*, int, int, int, hipStream_t);
+  bool dma;
+};
+
+template <int BM, int BN, int BK, int WN, int BUFS>
+int run_regs_variant(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  return launch_mfma<fgr::MfmaConfig<BM, BN, BK, 2, WN, 1, BUFS>, true>(A, B, C, M, N, K, s);
+}
+
+template <int S>
+int run_dma_variant(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  int tiles_m = (int)cdiv(M, 256);
+  int tiles_n = (int)cdiv(K, 256);
+  int group = kTileGroup;
+  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group};
+  return launch(dma_kernel<fgr::DmaConfig<S>>(), (int64_t)tiles_m * tiles_n, fgr::DmaConfig<S>::kThreads, args, s);
+}
+
+constexpr Variant kVariants[] = {
+    {"regs single 256x256 bk16", &run_regs_variant<256, 256, 16, 4, 1>, false},
+    {"regs single 256x256 bk32", &run_regs_variant<256, 256, 32, 4, 1>, false},
+    {"regs single 256x128 bk16", &run_regs_variant<256, 128, 16, 2, 1>, false},
+    {"regs single 256x128 bk32", &run_regs_variant<256, 128, 32, 2, 1>, false},
+    {"regs single 128x128 bk16", &run_regs_variant<128, 128, 16, 2, 1>, false},
+    {"regs single 128x128 bk32", &run_regs_variant<128, 128, 32, 2, 1>, false},
+    {"regs double 256x256 bk16", &run_regs_variant<256, 256, 16, 4, 2>, false},
+    {"regs double 256x256 bk32", &run_regs_variant<256, 256, 32, 4, 2>, false},
+    {"regs double 256x128 bk16", &run_regs_variant<256, 128, 16, 2, 2>, false},
+    {"regs double 256x128 bk32", &run_regs_variant<256, 128, 32, 2, 2>, false},
+    {"regs double 128x128 bk16", &run_regs_variant<128, 128, 16, 2, 2>, false},
+    {"regs double 128x128 bk32", &run_regs_variant<128, 128, 32, 2, 2>, false},
+    {"direct ring3 256x256 bk16", &run_dma_variant<3>, true},
+    {"direct ring4 256x256 bk16", &run_dma_variant<4>, true},
+    {"direct ring5 256x256 bk16", &run_dma_variant<5>, true},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+int run_variant(const float* A, const float* B, float* C, int M, int N, int K, void* stream, int variant) {
+  int rc = check_args(A, B, C, M, N, K);
+  if (rc != FGR_OK) return rc;
+  if (variant < 0 || variant >= kNumVariants || !mfma_vec_ok(A, B, C, N, K) ||
+      (kVariants[variant].dma && !mfma_dma_ok(N)))
+    return FGR_ERR_BAD_PATH;
+  int cus = 0;
+  rc = current_device(&cus);
+  if (rc != FGR_OK) return rc;
+  return kVariants[variant].run(A, B, C, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -992,5 +1048,15 @@ const char* fgr_status_string(int status) {
 }
 
 int fgr_version(void) { return kVersion; }
+
+int fgr_variant_count(void) { return kNumVariants; }
+
+const char* fgr_variant_name(int variant) {
+  return variant >= 0 && variant < kNumVariants ? kVariants[variant].name : nullptr;
+}
+
+int fgr_solve_variant(const float* A, const float* B, float* C, int M, int N, int K, void* stream, int variant) {
+  return run_variant(A, B, C, M, N, K, stream, variant);
+}
 
 }  // extern "C"

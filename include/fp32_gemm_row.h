@@ -196,6 +196,33 @@ const char *fgr_status_string(int status);
 /* fgr_version - library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int fgr_version(void);
 
+/*
+ * The controlled comparison (the LeetGPU write-up, section "Controlled
+ * Comparison": one variable changed at a time, every variant built and timed
+ * alike, with the compiler's resource report beside it). The library holds a
+ * fixed list of kernel variants along three axes: LDS buffering (the
+ * register-staged MFMA kernel with one buffer, or two with register
+ * prefetch; the direct-copy kernel with rings of 3, 4 or 5 stages), output
+ * tile (256x256, 256x128, 128x128) and reduction chunk (16 or 32 deep).
+ * None of them is a product path: solve() uses the tuned kernels.
+ *
+ * fgr_variant_count - the number of variants, V.
+ * fgr_variant_name  - a static name for variant 0 <= v < V ("regs double
+ *                     256x256 bk32", "direct ring4 256x256 bk16", ...), or
+ *                     NULL outside that range.
+ * fgr_solve_variant - C = A x B on `stream` with variant v alone, same
+ *                     arguments, layout, ownership and asynchrony as solve().
+ *                     Returns FGR_ERR_BAD_PATH for v outside [0, V), rows that
+ *                     are not 16-byte aligned (N % 4, K % 4 or a pointer), or
+ *                     a direct-copy variant with N < 64; the other FGR_ERR_*
+ *                     codes as solve(). Host only until the launch; allocates
+ *                     nothing.
+ */
+int fgr_variant_count(void);
+const char *fgr_variant_name(int variant);
+int fgr_solve_variant(const float *A, const float *B, float *C, int M, int N, int K, void *stream,
+                      int variant);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,26 @@ def test_python_constants_match_header():
             assert getattr(fgr, key) == value, key
 
 
+def test_controlled_comparison_variants(lib):
+    # host-only: the variant list along buffering x tile x chunk, names
+    # unique, out-of-range indices rejected before any HIP call
+    names = fgr.variant_names()
+    assert len(names) == 15 and len(set(names)) == 15
+    for buf in ("single", "double"):
+        for tile in ("256x256", "256x128", "128x128"):
+            for bk in ("bk16", "bk32"):
+                assert f"regs {buf} {tile} {bk}" in names
+    for ring in (3, 4, 5):
+        assert f"direct ring{ring} 256x256 bk16" in names
+    assert lib.fgr_variant_name(-1) is None and lib.fgr_variant_name(len(names)) is None
+    assert lib.fgr_solve_variant(A0, B0, C0, 64, 64, 64, None, len(names)) == fgr.ERR_BAD_PATH
+    assert lib.fgr_solve_variant(A0, B0, C0, 64, 64, 64, None, -1) == fgr.ERR_BAD_PATH
+    assert lib.fgr_solve_variant(A0, B0, C0, 64, 63, 64, None, 0) == fgr.ERR_BAD_PATH  # N % 4
+    assert lib.fgr_solve_variant(A0 + 4, B0, C0, 64, 64, 64, None, 0) == fgr.ERR_BAD_PATH  # 4-byte aligned A
+    assert lib.fgr_solve_variant(A0, B0, C0, 64, 60, 64, None, 12) == fgr.ERR_BAD_PATH  # direct copies, N < 64
+    assert lib.fgr_solve_variant(A0, B0, C0, 0, 64, 64, None, 0) == fgr.ERR_BAD_DIMS
+
+
 def test_version_and_status_strings(lib):
     assert fgr.version() == 100
     assert fgr.status_string(fgr.OK) == "ok"

@@ -669,6 +669,25 @@ def test_concurrent_calls_on_separate_streams():
             assert_exact(C, Cref, f"{M}x{N}x{K} call {j}")
 
 
+@pytest.mark.parametrize("shape", [(264, 200, 520), (512, 96, 256), (300, 1028, 260)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_controlled_comparison_variants_exact(shape):
+    # every controlled-comparison variant (LDS buffering x output tile x
+    # reduction chunk) alone over the whole product: ragged M and K tails and
+    # a reduction tail, exact on integer data
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=50)
+    Cref, _ = oracle.gemm(A, B)
+    dA = torch.from_numpy(A.ravel()).to(DEV)
+    dB = torch.from_numpy(B.ravel()).to(DEV)
+    for v, name in enumerate(fgr.variant_names()):
+        say(f"variant {name} {shape}")
+        dC = torch.full((M * K,), float("nan"), device=DEV)
+        fgr.solve_variant(dA, dB, dC, M, N, K, v)
+        torch.cuda.synchronize()
+        assert_exact(dC.cpu().numpy().reshape(M, K), Cref, f"{shape} {name}")
+
+
 def test_default_stream_is_torchs_current_stream():
     # solve() without a stream argument enqueues on torch's current stream
     # (the binding reads its raw handle); inside `with torch.cuda.stream(s)`
