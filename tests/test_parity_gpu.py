@@ -622,6 +622,31 @@ def test_nan_in_a_row_poisons_only_that_row():
     assert_exact(C[mask], Cref, "rows without NaN")
 
 
+@pytest.mark.parametrize("shape", [(1023, 1025, 1027), (128, 16384, 128), (4, 100000, 96), (16, 65536, 64),
+                                   (300, 500, 261), (4100, 104, 4100)], ids=lambda s: "x".join(map(str, s)))
+def test_special_values_stay_in_their_row_and_column(shape):
+    # a NaN in A poisons exactly its row of C and an infinity in B exactly its
+    # column (with a sign mix, NaN or +-inf there), on the paths that pad,
+    # clamp or split: the k-split tail in one grid, the split reduction
+    # through the workspace, the split matrix-vector kernel, 32x32 tiles with
+    # 4-byte copies, short reductions. Padding only ever multiplies zeros by
+    # zeros, and clamped copies feed only outputs that are not stored.
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=60)
+    A, B = A.copy(), B.copy()
+    rm, cn = M // 2, K - 1
+    A[rm, N // 3] = np.nan
+    B[N - 1, cn] = np.inf
+    say(f"special values {shape}: {fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]}")
+    C = gpu_gemm(A, B)
+    assert np.isnan(C[rm]).all()
+    col = np.delete(C[:, cn], rm)
+    assert (~np.isfinite(col)).all()
+    rows = np.delete(np.arange(M), rm)
+    Cref, _ = oracle.gemm(np.delete(A, rm, axis=0), np.delete(B, cn, axis=1))
+    assert_exact(np.delete(C[rows], cn, axis=1), Cref, f"{shape} outside the poisoned row and column")
+
+
 def test_runs_on_a_side_stream():
     A, B = synth.make_inputs(257, 129, 193, "eighths")
     Cref, _ = oracle.gemm(A, B)
