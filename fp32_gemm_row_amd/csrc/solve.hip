@@ -41,9 +41,10 @@ DeviceInfo g_dev[kMaxDevices];
 
 // Current device, checked once: it must be a gfx950 (the FP32 MFMA layouts and
 // the LDS budget used here are gfx950's).
-int current_device(int* cus) {
+int current_device(int* cus, int* dev_out = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FGR_ERR_DEVICE;
+  if (dev_out) *dev_out = dev;
   std::lock_guard<std::mutex> lock(g_dev_mu);
   DeviceInfo& d = g_dev[dev];
   if (!d.probed) {
@@ -56,6 +57,25 @@ int current_device(int* cus) {
   }
   if (!d.ok) return FGR_ERR_DEVICE;
   *cus = d.cus;
+  return FGR_OK;
+}
+
+// The current device's CU count, after checking that it is a gfx950 and
+// that `stream` (other than the null and per-thread streams, which follow
+// the current device) belongs to it: the kernels run on the stream's device,
+// while the CU count and the split workspace come from the current one.
+int device_for(hipStream_t stream, int* cus) {
+  int dev = -1;
+  const int rc = current_device(cus, &dev);
+  if (rc != FGR_OK) return rc;
+  if (stream && stream != hipStreamPerThread) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FGR_ERR_DEVICE;
+    }
+    if (sdev != dev) return FGR_ERR_DEVICE;
+  }
   return FGR_OK;
 }
 
@@ -146,27 +166,27 @@ struct SplitPlan {
 // over N / p reduction indices, t^2 N / (128 p) cycles of its four SIMDs, at
 // an efficiency of 0.9 for 64x64 and 0.7 for 32x32 tiles, 10% more when two
 // or more of them share the CU) and the HBM time (A and B panels of every
-// tile, 35% of them from HBM and the rest from L2, at 5 TB/s), plus 6 us and
-// 1 us per workgroup of the busiest CU and, for a split, 6 us and the P M K 8
-// bytes of partial tiles written and read back. Host side (measured): 9 us per
-// call, 15 us with a split (second launch, workspace lookup and event); the
-// two overlap, so the call takes the longer. Ties go to the smaller GPU time.
-// The constants are fitted to MI355X measurements of 24 shapes with few output
-// tiles (M, K from 96 to 1024, N from 1024 to 262144; 64x64 and 32x32 tiles,
-// P = 1 .. 256): the chosen plan is within 5% of the best measured one on each
-// of them and within 7% on 18 others, where the previous estimate, which added
-// the host cost to the GPU time, lost up to 35% (1024 x 32768 x 512: 387 us
-// against 286).
+// tile, 25% of them from HBM and the rest from L2, at 5 TB/s), plus 3 us and
+// 1 us per workgroup of the busiest CU and, for a split, 3 us and the P M K 8
+// bytes of partial tiles written and read back. Host side (measured from
+// Python): 6 us per call, 10 us with a split (second launch, workspace lookup
+// and event); the two overlap, so the call takes the longer. Ties go to the
+// smaller GPU time. The constants are fitted to MI355X measurements of 24
+// shapes with few output tiles (M, K from 96 to 1024, N from 1024 to 262144;
+// 64x64 and 32x32 tiles, P = 1 .. 256): the chosen plan is within 5% of the
+// best measured one on each of them and within 7% on 18 others, where the
+// first estimate, which added the host cost to the GPU time, lost up to 35%
+// (1024 x 32768 x 512: 387 us against 286).
 double splitk_time(int t, int p, int M, int N, int K, int cus) {
   const double tiles = (double)cdiv(M, t) * (double)cdiv(K, t);
   const double per_cu = std::ceil(tiles * p / cus);  // workgroups on the busiest CU
   const int resident = t >= 128 ? 1 : t >= 64 ? 2 : 4;  // workgroups per CU (LDS)
   const double eff = (t >= 64 ? 0.9 : 0.7) * (std::min<double>(per_cu, resident) >= 2 ? 1.1 : 1.0);
   const double t_mfma = per_cu * ((double)t * t * ((double)N / p) / 128.0) / (2.4e9 * eff);
-  const double t_hbm = 4.0 * N * tiles * 2.0 * t * 0.35 / 5e12;
-  double gpu = std::max(t_mfma, t_hbm) + 6e-6 + per_cu * 1e-6;
-  if (p > 1) gpu += 6e-6 + (double)p * M * K * 8.0 / 5e12;
-  const double host = p > 1 ? 15e-6 : 9e-6;
+  const double t_hbm = 4.0 * N * tiles * 2.0 * t * 0.25 / 5e12;
+  double gpu = std::max(t_mfma, t_hbm) + 3e-6 + per_cu * 1e-6;
+  if (p > 1) gpu += 3e-6 + (double)p * M * K * 8.0 / 5e12;
+  const double host = p > 1 ? 10e-6 : 6e-6;
   return std::max(host, gpu) + 1e-3 * gpu;  // the small second term breaks ties
 }
 
@@ -904,9 +924,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     return FGR_ERR_BAD_PATH;
 
   int cus = 0;
-  rc = current_device(&cus);
-  if (rc != FGR_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  rc = device_for(s, &cus);
+  if (rc != FGR_OK) return rc;
   const Choice best = choose(A, B, C, M, N, K, cus);
   if (path == FGR_PATH_AUTO) {
     if (tile == FGR_TILE_AUTO) {
@@ -999,7 +1019,7 @@ int run_variant(const float* A, const float* B, float* C, int M, int N, int K, v
       (kVariants[variant].dma && !mfma_dma_ok(N)))
     return FGR_ERR_BAD_PATH;
   int cus = 0;
-  rc = current_device(&cus);
+  rc = device_for(reinterpret_cast<hipStream_t>(stream), &cus);
   if (rc != FGR_OK) return rc;
   return kVariants[variant].run(A, B, C, M, N, K, reinterpret_cast<hipStream_t>(stream));
 }

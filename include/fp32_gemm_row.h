@@ -33,8 +33,11 @@
  *
  * Streams
  *   `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
- *   is enqueued on it and the call returns without waiting for it. The
- *   LeetGPU form below uses the null stream.
+ *   is enqueued on it and the call returns without waiting for it. It must
+ *   belong to the current device (FGR_ERR_DEVICE otherwise), where A, B and C
+ *   must live too. The LeetGPU form below uses the null stream. The library
+ *   holds device memory and events (the split workspace, below) for the life
+ *   of the process; it must not be called after hipDeviceReset.
  *
  * Alignment and paths
  *   Any 4-byte-aligned pointers are accepted. When N % 4 == 0, K % 4 == 0
@@ -76,7 +79,8 @@ extern "C" {
 #define FGR_ERR_MISALIGNED (-3)   /* a pointer is not 4-byte aligned */
 #define FGR_ERR_ALIAS (-4)        /* C overlaps A or B */
 #define FGR_ERR_BAD_PATH (-5)     /* forced path/tile cannot run this shape */
-#define FGR_ERR_DEVICE (-6)       /* no HIP device, or the current one is not gfx950 */
+#define FGR_ERR_DEVICE (-6)       /* no HIP device, the current one is not gfx950, or the
+                                     stream belongs to another device */
 #define FGR_ERR_LAUNCH (-7)       /* HIP reported an error at launch */
 
 /* Paths (fgr_select_path / fgr_solve_path). */

@@ -289,14 +289,14 @@ def test_split_reduction_choices():
     for shape, tile in [((256, 65536, 256), 64), ((128, 262144, 128), 64), ((64, 65536, 1024), fgr.TILE_32X128),
                         ((512, 65536, 512), 64), ((16, 1048576, 64), 32), ((130, 20000, 66), 32),
                         ((24, 65536, 1024), fgr.TILE_32X128), ((16, 16384, 4096), fgr.TILE_32X128),
-                        ((512, 8192, 512), 64), ((1024, 32768, 512), 64), ((96, 8192, 4096), 64)]:
+                        ((512, 8192, 512), 64), ((1024, 32768, 512), 64), ((96, 8192, 4096), 32)]:
         assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
         assert st(A0, B0, C0, *shape) == tile, shape
         assert sp(A0 + 4, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape  # 4-byte copies too
     # enough 32x32 tiles for every CU, or too short a reduction: no split
     assert sp(A0, B0, C0, 512, 4096, 512) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles
-    assert sp(A0, B0, C0, 96, 4096, 4096) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 96, 2048, 4096) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 640, 2048, 640) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 65, 8192, 8192) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 100, 64) == fgr.PATH_MFMA_KSPLIT
