@@ -144,15 +144,56 @@ int64_t tail_tiles(int cus) { return (int64_t)cus * 11 / 16; }
 // left over, 131.1 vs 104.7).
 int64_t ksplit_tail_tiles(int cus) { return cus / 2; }
 
-// Parts for splitting a matrix-vector reduction across workgroups when its
-// `wgs` workgroups would fill at most half the CUs: enough parts to give every
-// CU one workgroup, each part at least kGemvPartLen rows of B long (measured
-// on MI355X: shorter parts, or two workgroups per CU, were slower).
-constexpr int kGemvPartLen = 8192;
-int gemv_parts(int64_t wgs, int N, int cus) {
-  if (wgs * 2 > cus) return 1;
-  const int64_t p = std::min<int64_t>(cus / wgs, N / kGemvPartLen);
-  return p >= 2 ? (int)p : 1;
+// Matrix-vector plan: column block width (32, or 16 when 32-column blocks
+// fill at most half the CUs) and parts of the reduction across workgroups,
+// by an estimate of the call's time. GPU side: streaming B (and A and C) at
+// 40 GB/s per workgroup of 32 columns and 26 GB/s per workgroup of 16, at
+// most 5.5 TB/s for the device, plus 4 us, and for a split 3 us and the P M K
+// 8 bytes of partial rows; host side 6 us, 10 us with a split (as for the
+// k-split plan below); the call takes the longer of the two. Candidates: 16
+// columns unsplit; 32 columns with P = 1, 2, 4, ... while the workgroups fit
+// one per CU and parts keep at least 1024 rows of B. Measured on MI355X (us,
+// previous rule of at least 8192 rows per part -> this plan): 1 x 16384 x
+// 1024 31.3 -> 17.6, 1 x 32768 x 512 30.9 -> 17.8, 4 x 8192 x 1024 27.3 ->
+// 16.2, 2 x 65536 x 256 35.4 -> 23.7 or less, 1 x 8192 x 2048 21.4 -> 18.0;
+// unchanged where no split pays (1 x 2048 x 2048 7.4, 1 x 4096 x 4096 15.0,
+// 1 x 8192 x 8192 45.8, 1 x 65536 x 1024 52.3).
+struct GemvPlan {
+  int cols;
+  int parts;
+};
+
+double gemv_time(int cols, int p, int M, int N, int K, int cus) {
+  (void)cus;
+  const double wgs = (double)cdiv(K, cols) * p;
+  const double bytes = 4.0 * ((double)N * K + (double)M * N + (double)M * K);
+  const double rate = std::min(5.5e12, wgs * (cols == fgr::kGemvCols ? 40e9 : 26e9));
+  double gpu = bytes / rate + 4e-6;
+  if (p > 1) gpu += 3e-6 + (double)p * M * K * 8.0 / 5e12;
+  const double host = p > 1 ? 10e-6 : 6e-6;
+  return std::max(host, gpu) + 1e-3 * gpu;  // the small second term breaks ties
+}
+
+constexpr int kGemvMinPart = 1024;
+GemvPlan gemv_plan(int M, int N, int K, int cus) {
+  const int64_t wide = cdiv(K, fgr::kGemvCols);
+  GemvPlan best{fgr::kGemvCols, 1};
+  double best_time = gemv_time(fgr::kGemvCols, 1, M, N, K, cus);
+  if (wide * 2 <= cus) {
+    const double e = gemv_time(fgr::kGemvCols / 2, 1, M, N, K, cus);
+    if (e < best_time) {
+      best = {fgr::kGemvCols / 2, 1};
+      best_time = e;
+    }
+  }
+  for (int p = 2; wide * p <= cus && N / p >= kGemvMinPart && p <= 65535; p *= 2) {
+    const double e = gemv_time(fgr::kGemvCols, p, M, N, K, cus);
+    if (e < best_time) {
+      best = {fgr::kGemvCols, p};
+      best_time = e;
+    }
+  }
+  return best;
 }
 
 struct SplitPlan {
@@ -848,29 +889,21 @@ int launch_gemv_parts(const float* A, const float* B, float* C, int M, int N, in
   return launch(kernel, blocks, 1024, args, s, parts);
 }
 
-// The matrix-vector kernel on 32-column blocks; when those fill at most half
-// the CUs and N is long, the reduction is also split across workgroups
-// through a stream-ordered workspace (then added in part order). When they
-// fill at most half the CUs and N is too short to split, 16-column blocks
-// instead, so that twice the CUs stream B in one launch (measured on MI355X,
-// TB/s, 32 vs 16 columns: 1 x 4096 x 4096 3.09 vs 3.43, 4 x 11008 x 4096 2.69
-// vs 3.30, 1 x 8192 x 2048 1.70 vs 2.02; with more blocks, or with a split,
-// the narrower 64-byte row segments stream worse: 1 x 4096 x 6144 4.31 vs
-// 2.85, 1 x 65536 x 1024 5.13 vs 3.59).
+// The matrix-vector kernel with the plan above: the partial rows of a split
+// into a workspace, then added in part order (without a workspace the
+// unsplit kernel runs).
 template <int VW>
 int launch_gemv(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
-  const int64_t wide_blocks = cdiv(K, fgr::kGemvCols);
-  const int wide_parts = gemv_parts(wide_blocks, N, cus);
-  const bool narrow = wide_blocks * 2 <= cus && wide_parts < 2;
-  const int parts = narrow ? 1 : wide_parts;
+  const GemvPlan plan = gemv_plan(M, N, K, cus);
   PartsWorkspace ws;
   float* W = nullptr;
-  if (parts >= 2 && alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) == FGR_OK) W = ws.w;
-  const int p = W ? parts : 1;
-  const int rc = narrow ? launch_gemv_parts<VW, fgr::kGemvCols / 2>(A, B, C, M, N, K, p, W, s)
-                        : launch_gemv_parts<VW, fgr::kGemvCols>(A, B, C, M, N, K, p, W, s);
+  if (plan.parts >= 2 && alloc_floats(ws, (size_t)plan.parts * (size_t)M * (size_t)K, s) == FGR_OK) W = ws.w;
+  const int p = W ? plan.parts : 1;
+  const int rc = plan.cols == fgr::kGemvCols
+                     ? launch_gemv_parts<VW, fgr::kGemvCols>(A, B, C, M, N, K, p, W, s)
+                     : launch_gemv_parts<VW, fgr::kGemvCols / 2>(A, B, C, M, N, K, p, W, s);
   if (rc != FGR_OK || !W) return rc;
-  return launch_reduce_parts(W, C, M, K, parts, vec4_rows(C, M, K), s);
+  return launch_reduce_parts(W, C, M, K, p, vec4_rows(C, M, K), s);
 }
 
 int run(const float* A, const float* B, float* C, int M, int N, int K, void* stream, int path,
