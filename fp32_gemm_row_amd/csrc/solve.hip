@@ -273,7 +273,7 @@ SplitPlan splitk_plan(int M, int N, int K, int cus) {
   return best;
 }
 
-// Skinny outputs (kSkinnyMinM <= M <= 64, K >= 128, B of at least 32 MiB):
+// Skinny outputs (kSkinnyMinM <= M <= 64, K >= 128, B as in skinny_b below):
 // 32x128 k-split tiles, each reduction split into the largest power-of-two number of
 // parts that keeps tiles x parts within the CU count and parts at least 512
 // long. The work is streaming B once; wide column blocks and one workgroup
@@ -287,7 +287,18 @@ SplitPlan splitk_plan(int M, int N, int K, int cus) {
 // vs 2.18, 64 x 8192 x 28672 3.15 vs 2.87, 64 x 11008 x 4096 2.87 vs 1.72).
 constexpr int kSkinnyMinM = 5;  // fewer rows: the matrix-vector kernel
 constexpr int kSkinnyMaxM = 64;  // two rows of 32x128 tiles at most
-constexpr int64_t kSkinnyMinB = int64_t(8) << 20;  // elements of B
+// B large enough for the 32x128 tiles: at least 32 Mi elements, or 16 Mi when
+// 32x32 tiles alone would leave CUs idle. Below that the split plan's 32x32
+// tiles measured faster (MI355X, us, 32x128 vs the plan: 16 x 4096 x 2048
+// 18.5 vs 14.8, 32 x 2048 x 4096 19.4 vs 14.9, 16 x 2048 x 8192 20.2 vs 15.7
+// with 256 tiles of 32x32; but 16 x 8192 x 8192 55.3 vs 63.9, 32 x 4096 x
+// 4096 21.7 vs 22.8).
+constexpr int64_t kSkinnyMinB = int64_t(16) << 20;
+constexpr int64_t kSkinnyWideB = int64_t(32) << 20;
+bool skinny_b(int M, int N, int K, int cus) {
+  const int64_t b = (int64_t)N * K;
+  return b >= kSkinnyWideB || (b >= kSkinnyMinB && cdiv(M, 32) * cdiv(K, 32) < cus);
+}
 int skinny_parts(int M, int N, int K, int cus) {
   const int64_t tiles = cdiv(M, 32) * cdiv(K, 128);
   int p = 1;
@@ -310,8 +321,13 @@ constexpr int kShortReduction = 104;
 // tiles split each tile's reduction across a workgroup's waves.
 Choice choose(const float* A, const float* B, const float* C, int M, int N, int K, int cus) {
   if (cus <= 0) cus = kDefaultCus;
-  const bool skinny = M >= kSkinnyMinM && M <= kSkinnyMaxM && N >= 64 && K >= 128 && (int64_t)N * K >= kSkinnyMinB;
-  if (M <= fgr::kGemvMaxRows && !skinny)
+  const bool skinny_shape = M >= kSkinnyMinM && M <= kSkinnyMaxM && N >= 64 && K >= 128;
+  const bool skinny = skinny_shape && skinny_b(M, N, K, cus);
+  // M <= 8: the matrix-vector kernel, except that from 5 rows on the split
+  // plan below wins where the skinny tiles do not apply (measured on MI355X,
+  // us: 5 x 4096 x 1024 16.5 vs 12.4, 8 x 4096 x 256 15.6 vs 10.8, 8 x 2048
+  // x 2048 14.8 vs 12.1; at M <= 4 the two are within 15% either way)
+  if (M <= fgr::kGemvMaxRows && !skinny && !skinny_shape)
     return {gemv_vec_ok(B, K) ? FGR_PATH_GEMV_VEC : FGR_PATH_GEMV_SCALAR, FGR_TILE_AUTO};
   if (skinny) {
     // skinny: stream B once in 32x128 tiles (see skinny_parts)

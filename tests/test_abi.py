@@ -205,7 +205,8 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4, 8192, 8192) == fgr.PATH_GEMV_VEC
     assert sp(A0, B0, C0, 4, 8192, 8190) == fgr.PATH_GEMV_SCALAR
     assert sp(A0, B0, C0, 8, 8192, 64) == fgr.PATH_GEMV_VEC  # K < 128: no 32x128 tiles
-    assert sp(A0, B0, C0, 8, 2048, 2048) == fgr.PATH_GEMV_VEC  # B under 32 MiB
+    assert sp(A0, B0, C0, 8, 2048, 2048) == fgr.PATH_MFMA_SPLITK  # 5 <= M <= 8, small B: the split plan
+    assert sp(A0, B0, C0, 4, 2048, 2048) == fgr.PATH_GEMV_VEC  # M <= 4: the matrix-vector kernel
     assert sp(A0, B0, C0, 8, 8192, 8192) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles
     assert sp(A0, B0, C0, 9, 8192, 8192) == fgr.PATH_MFMA_SPLITK
     assert sp(0, B0, C0, 1, 8, 8) == fgr.ERR_NULL_POINTER

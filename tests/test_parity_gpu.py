@@ -468,10 +468,10 @@ def test_skinny_products_full_compare(M):
 @pytest.mark.parametrize("shape,path", [
     ((16, 8192, 4096), fgr.PATH_MFMA_SPLITK), ((24, 65536, 1024), fgr.PATH_MFMA_SPLITK),
     ((5, 65536, 256), fgr.PATH_MFMA_SPLITK), ((8, 8192, 28672), fgr.PATH_MFMA_KSPLIT),
-    ((32, 4097, 4099), fgr.PATH_MFMA_SPLITK), ((31, 16384, 1000), fgr.PATH_MFMA_SPLITK),
+    ((32, 4097, 4099), fgr.PATH_MFMA_SPLITK), ((31, 32768, 1000), fgr.PATH_MFMA_SPLITK),
     # two rows of 32x128 tiles
     ((48, 8192, 4096), fgr.PATH_MFMA_SPLITK), ((64, 4096, 11008), fgr.PATH_MFMA_KSPLIT),
-    ((33, 4100, 2052), fgr.PATH_MFMA_SPLITK)],
+    ((33, 8200, 2052), fgr.PATH_MFMA_SPLITK)],
     ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_skinny_tiles_exact(shape, path):
     # 32x128 tiles for skinny outputs: rows past M and columns past K padded,
