@@ -124,7 +124,6 @@ bool ksplit128_ok(const float* A, const float* B, const float* C, int N, int K) 
   return rows_of(A, B, C, N, K) == Rows::kAll;
 }
 
-
 // Direct global->LDS copies need at least four 16-deep reduction chunks (the
 // copies that run past the last chunk re-read it, and must never reach the
 // zero-padded first chunk); they are 16 bytes wide for 16-byte aligned rows,
@@ -155,7 +154,7 @@ int64_t ksplit_tail_tiles(int cus) { return cus / 2; }
 // one per CU and parts keep at least 1024 rows of B. Measured on MI355X (us,
 // previous rule of at least 8192 rows per part -> this plan): 1 x 16384 x
 // 1024 31.3 -> 17.6, 1 x 32768 x 512 30.9 -> 17.8, 4 x 8192 x 1024 27.3 ->
-// 16.2, 2 x 65536 x 256 35.4 -> 23.7 or less, 1 x 8192 x 2048 21.4 -> 18.0;
+// 16.0, 2 x 65536 x 256 35.4 -> 19.3, 1 x 8192 x 2048 21.4 -> 17.9;
 // unchanged where no split pays (1 x 2048 x 2048 7.4, 1 x 4096 x 4096 15.0,
 // 1 x 8192 x 8192 45.8, 1 x 65536 x 1024 52.3).
 struct GemvPlan {
@@ -163,8 +162,7 @@ struct GemvPlan {
   int parts;
 };
 
-double gemv_time(int cols, int p, int M, int N, int K, int cus) {
-  (void)cus;
+double gemv_time(int cols, int p, int M, int N, int K) {
   const double wgs = (double)cdiv(K, cols) * p;
   const double bytes = 4.0 * ((double)N * K + (double)M * N + (double)M * K);
   const double rate = std::min(5.5e12, wgs * (cols == fgr::kGemvCols ? 40e9 : 26e9));
@@ -178,16 +176,16 @@ constexpr int kGemvMinPart = 1024;
 GemvPlan gemv_plan(int M, int N, int K, int cus) {
   const int64_t wide = cdiv(K, fgr::kGemvCols);
   GemvPlan best{fgr::kGemvCols, 1};
-  double best_time = gemv_time(fgr::kGemvCols, 1, M, N, K, cus);
+  double best_time = gemv_time(fgr::kGemvCols, 1, M, N, K);
   if (wide * 2 <= cus) {
-    const double e = gemv_time(fgr::kGemvCols / 2, 1, M, N, K, cus);
+    const double e = gemv_time(fgr::kGemvCols / 2, 1, M, N, K);
     if (e < best_time) {
       best = {fgr::kGemvCols / 2, 1};
       best_time = e;
     }
   }
   for (int p = 2; wide * p <= cus && N / p >= kGemvMinPart && p <= 65535; p *= 2) {
-    const double e = gemv_time(fgr::kGemvCols, p, M, N, K, cus);
+    const double e = gemv_time(fgr::kGemvCols, p, M, N, K);
     if (e < best_time) {
       best = {fgr::kGemvCols, p};
       best_time = e;
@@ -355,7 +353,8 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
   if (N >= 64) {
     // Fewer 256x256 tiles than CUs: tiles whose reduction is split over the
     // four waves of a workgroup (k-split), the largest that still gives every
-    // CU a tile; a last partial wave of up to half the CUs to the split kernel.
+    // CU a tile; a last partial wave of up to half the CUs is spread over
+    // every CU (launch_ksplit_tail).
     if (ksplit128_ok(A, B, C, N, K) && t128 >= cus) {
       const int64_t rem = t128 % cus;
       if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
