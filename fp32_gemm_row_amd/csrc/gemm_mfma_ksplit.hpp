@@ -6,10 +6,12 @@
 // (at least one 256x256 tile per CU) lie shapes such as 2048^3 or a
 // (1024, 6144, 4096) row shard: 64 tiles of 256x256, 256 of 128x128. Here each
 // wave of a workgroup computes the WHOLE tile (BM = 128: 16 MFMA blocks, 256
-// accumulators in AGPRs, as a wave of the direct-copy kernel) over its own
-// quarter of the reduction chunks, so a 128x128 tile keeps a CU's four matrix
-// cores as busy as a 256x256 tile does; smaller tiles serve shapes with fewer
-// outputs still. Each wave copies its own A (BM x BK) and B (BK x BM) chunks
+// accumulators in AGPRs, as a wave of the direct-copy kernel) over every
+// fourth reduction chunk (wave w takes chunks w, w + 4, ...: the four waves
+// then copy neighbouring 32-byte pieces of the same 128-byte lines of A at
+// about the same time), so a 128x128 tile keeps a CU's four matrix cores as
+// busy as a 256x256 tile does; smaller tiles serve shapes with fewer outputs
+// still. Each wave copies its own A (BM x BK) and B (BK x BM) chunks
 // with global_load_lds (16 bytes per lane for 16-byte aligned rows, 4 bytes
 // otherwise) into its own ring of S LDS stages and waits only on its own
 // copies (s_waitcnt vmcnt): the main loop has no barrier. At the end the four
@@ -164,8 +166,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // BN floats, row stride BN); a second kernel adds the parts. Whole and split
   // tiles in one grid run side by side (two workgroups fit a CU): a last
   // partial wave of tiles then spreads over every CU next to the full wave
-  // instead of running after it. This wave's chunks are [c_begin, c_end) of
-  // the part's; at least 8 chunks per part give every wave >= 2.
+  // instead of running after it. At least 8 chunks per part give every wave
+  // >= 2 of the part's chunks (dealt as below).
   const bool whole = (int)blockIdx.x < nfull;
   const int grid = whole ? nfull : (int)gridDim.x - nfull;
   const int logical = xcd_remap(whole ? (int)blockIdx.x : (int)blockIdx.x - nfull, grid);
@@ -182,9 +184,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   const int n_first = N - BK * nchunks;  // in (-BK, 0]
   const int pc0 = (int)((int64_t)nchunks * part / kparts);
   const int pn = (int)((int64_t)nchunks * (part + 1) / kparts) - pc0;
-  const int c_begin = pc0 + pn * wave / T::kWaves;
-  const int c_end = pc0 + pn * (wave + 1) / T::kWaves;
-  const int c_last = c_end - 1;
+  // The part's chunks are dealt to the waves in turn: this wave's j-th chunk
+  // is pc0 + wave + kWaves j, so that the four waves copy the four 32-byte
+  // pieces of the same 128-byte lines of A at about the same time (with a
+  // contiguous range per wave each line was fetched four times, chunks apart).
+  const int nmine = pn > wave ? (pn - wave + T::kWaves - 1) / T::kWaves : 0;
+  const int j_last = nmine - 1;
+  auto chunk_n0 = [&](int j) __attribute__((always_inline)) {
+    return n_first + BK * (pc0 + wave + T::kWaves * j);
+  };
 
   // Copy j of a wave fills floats [j * kABlock, (j + 1) * kABlock) of its A
   // piece; lane L the kACopyFloats floats at position p = j * kABlock + L *
@@ -218,8 +226,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     b_row[j] = r;
   }
 
-  auto copy_chunk = [&](int c, float* As, float* Bs) __attribute__((always_inline)) {
-    const int n0 = n_first + BK * c;
+  auto copy_chunk = [&](int j, float* As, float* Bs) __attribute__((always_inline)) {
+    const int n0 = chunk_n0(j);
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j)
       copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     constexpr int OFF = decltype(offc)::value;
     constexpr int X = OFF & 1;  // operand buffer of the chunk in stage OFF
     using S0 = std::integral_constant<int, OFF>;
-    const int n0 = n_first + BK * c_begin;
+    const int n0 = chunk_n0(0);
     typedef typename std::conditional<T::VA, float4, float>::type CopyTA;
     typedef typename std::conditional<T::VB, float4, float>::type CopyTB;
     CopyTA va[T::kACopies];
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       using Sj = std::integral_constant<int, (OFF + j) % S>;
-      copy_chunk(min(c_begin + j, c_last), a_stage(Sj{}), b_stage(Sj{}));
+      copy_chunk(min(j, j_last), a_stage(Sj{}), b_stage(Sj{}));
     });
     auto zero_out = [](auto v, bool ok) __attribute__((always_inline)) {
       if constexpr (std::is_same<decltype(v), float4>::value) return mask_quad(v, ok ? 0xfu : 0u);
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     using Sn = std::integral_constant<int, (s + 1) % S>;
     using Sp = std::integral_constant<int, (s + S - 1) % S>;
     // t = 0: the copies among its MFMAs
-    copy_chunk(min(c + S - 1, c_last), a_stage(Sp{}), b_stage(Sp{}));
+    copy_chunk(min(c + S - 1, j_last), a_stage(Sp{}), b_stage(Sp{}));
     mma(f[X], 0, 1);
     sched_spread<kSchedVmemRead, kMfmasT, T::kCopies>();
     __builtin_amdgcn_sched_barrier(0);
@@ -342,7 +350,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // even, so a group always starts with buffer 0). The wave's (count mod S)
   // leading chunks run in stages S - r .. S - 1 so that the loop below starts
   // at stage 0 with whole groups; one loop, so the accumulators stay in place.
-  const int nmine = c_end - c_begin;
   const int lead = nmine % S;
   static_for<0, S>([&](auto rc) {
     constexpr int R = decltype(rc)::value;
@@ -350,11 +357,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
       fill(std::integral_constant<int, (S - R) % S>{});
       static_for<0, R>([&](auto kc) {
         constexpr int k = S - R + decltype(kc)::value;
-        chunk(std::integral_constant<int, k>{}, std::integral_constant<int, k & 1>{}, c_begin + k - (S - R));
+        chunk(std::integral_constant<int, k>{}, std::integral_constant<int, k & 1>{}, k - (S - R));
       });
     }
   });
-  for (int c = c_begin + lead; c < c_end; c += S)
+  for (int c = lead; c < nmine; c += S)
     static_for<0, S>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       chunk(std::integral_constant<int, k>{}, std::integral_constant<int, k & 1>{}, c + k);
