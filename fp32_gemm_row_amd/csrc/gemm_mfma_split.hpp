@@ -5,8 +5,10 @@
 // problem has 272 tiles of 64 x 64, a 256-cube only 16), a workgroup's waves
 // would each own a 32 x 32 corner of a small tile and spend most of their time
 // at barriers. Here every wave of the workgroup computes the WHOLE BM x BN
-// tile, each over its own contiguous range of the reduction index n (the
-// workgroup's S waves split ceil(N / BK) chunks as evenly as possible). A wave
+// tile, each over its own share of the reduction index n (the ceil(N / BK)
+// chunks dealt to the workgroup's S waves in turn: wave w takes chunks w,
+// w + S, ..., so that the waves load neighbouring pieces of the same rows of A
+// at about the same time). A wave
 // stages its own chunks through its own region of LDS, so the main loop has no
 // barrier at all: LDS operations of one wave complete in order, which is the
 // only ordering its private staging needs. At the end the S partial tiles are
@@ -111,10 +113,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_split_kernel(
     if (m0 >= M || k0 >= K) return;  // a piece of a partial big tile: no outputs
   }
 
-  // this wave's share of the reduction: chunks [c_begin, c_end)
+  // this wave's share of the reduction: chunks wave, wave + S, wave + 2S, ...
+  // (dealt in turn, so that the waves load neighbouring pieces of the same
+  // rows of A at about the same time)
   const int nchunks = (N + BK - 1) / BK;
-  const int c_begin = (int)((int64_t)nchunks * wave / S);
-  const int c_end = (int)((int64_t)nchunks * (wave + 1) / S);
+  const int nmine = nchunks > wave ? (nchunks - wave + S - 1) / S : 0;
 
   float* const stage0 = lds + wave * 2 * T::kStage;
 
@@ -266,21 +269,21 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_split_kernel(
         }
   };
 
-  // Per-wave pipeline over its chunks: chunk c sits in stage (c - c_begin) % 2
-  // of the wave's region; the next chunk is loaded into registers at the top
-  // of the current one and written to the other stage before its last
-  // half-step (the reads of that stage for chunk c - 1 were issued earlier by
+  // Per-wave pipeline over its chunks: the wave's j-th chunk sits in stage
+  // j % 2 of the wave's region; the next chunk is loaded into registers at the
+  // top of the current one and written to the other stage before its last
+  // half-step (the reads of that stage for chunk j - 1 were issued earlier by
   // this same wave, and LDS serves one wave's operations in order).
-  if (c_begin < c_end) {
+  if (nmine > 0) {
     Frag f[2];
-    load_chunk(c_begin);
+    load_chunk(wave);
     store_chunk(stage0);
     read_frag(f[0], stage0, 0);
     int s = 0;
-    for (int c = c_begin; c + 1 < c_end; ++c) {
+    for (int j = 0; j + 1 < nmine; ++j) {
       const float* st = stage0 + s * T::kStage;
       float* nx = stage0 + (s ^ 1) * T::kStage;
-      load_chunk(c + 1);
+      load_chunk(wave + S * (j + 1));
       static_for<0, H - 1>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         read_frag(f[(h + 1) & 1], st, h + 1);
