@@ -51,11 +51,14 @@ namespace fgr {
 // BM x BN tiles (BN defaults to BM; BM = 32 with BN = 128 is the skinny
 // tile: few output rows, wide column blocks of B per workgroup). VA / VB:
 // 16-byte copies of A / B (their rows 16-byte aligned), else 4-byte copies;
-// VC: 128-bit stores of C (used by the 128 x 128 tile).
-template <int BM_, int S_, bool VA_, int BN_ = BM_, bool VB_ = VA_, bool VC_ = VB_>
+// VC: 128-bit stores of C (used by the 128 x 128 tile). BUF: the 4-byte
+// copies go through buffer loads (below), which hold a lane's source as two
+// 32-bit offsets instead of one 64-bit address per copy.
+template <int BM_, int S_, bool VA_, int BN_ = BM_, bool VB_ = VA_, bool VC_ = VB_, bool BUF_ = false>
 struct KsplitConfig {
   static constexpr int BM = BM_, BN = BN_, BK = 8, S = S_;
   static constexpr bool VA = VA_, VB = VB_, VC = VC_, VEC = VA_ && VB_ && VC_;
+  static constexpr bool BUFA = BUF_ && !VA_, BUFB = BUF_ && !VB_;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRB = BM / 32, kCB = BN / 32;
@@ -81,6 +84,7 @@ struct KsplitConfig {
   static_assert(kPieceA % kABlock == 0 && kPieceB % kBBlock == 0 && BN % kBCopyFloats == 0,
                 "copies cover whole pieces");
   static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");
+  static_assert(!BUFB || BN % 64 == 0, "buffer copies of B cover whole 64-column blocks");
   static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
   static_assert(S * (kStageA + kStageB) * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
   static_assert(kSlices <= S * kSlicesPerObjA && kSlices <= S * kSlicesPerObjB,
@@ -104,6 +108,22 @@ __device__ __forceinline__ void copy_to_lds_counted(const float* g, float* lds) 
     __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 16, 0, 0);
   else
     __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 4, 0, 0);
+}
+
+// The same 4-byte copy from a buffer: source = the buffer's base + soff +
+// voff bytes, with loads whose voff lies past the buffer's record count
+// returning zeros (the hardware's range check). Buffer word 3 as for every
+// gfx9-family GPU (raw buffer, 32-bit data).
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+__device__ __forceinline__ void copy4_buffer_to_lds_counted(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                                            float* lds) {
+  uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)lds);
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(uintptr_t)a, 4, voff, soff, 0, 0);
 }
 
 // Scheduling hints for NO memory instructions among MFMAS MFMAs, when there
@@ -200,40 +220,91 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // In A, p is row p / 8, stored slot (p % 8) / 4, element p % 4, and the slot
   // holds quad slot ^ swz(row): the lane copies that quad's element (the whole
   // quad with 16-byte copies). Rows past M read row M - 1 (not stored).
-  const float* a_src[T::kACopies];
-  int a_dst[T::kACopies], a_col[T::kACopies];
+  auto a_row_of = [&](int j) __attribute__((always_inline)) {
+    return (j * T::kABlock + lane * T::kACopyFloats) / BK;
+  };
+  auto a_col_of = [&](int j) __attribute__((always_inline)) {
+    const int pos = j * T::kABlock + lane * T::kACopyFloats;
+    return 4 * (((pos % BK) / 4) ^ a_swizzle2(pos / BK)) + pos % 4;
+  };
+  auto a_ptr_of = [&](int j) __attribute__((always_inline)) {
+    const int r = a_row_of(j);
+    const int row = m0 + r < M ? m0 + r : M - 1;
+    return A + (int64_t)row * N + a_col_of(j);
+  };
+  auto b_row_of = [&](int j) __attribute__((always_inline)) {
+    return (j * T::kBBlock + lane * T::kBCopyFloats) / BN;
+  };
+  auto b_ptr_of = [&](int j) __attribute__((always_inline)) {
+    const int c = k0 + (j * T::kBBlock + lane * T::kBCopyFloats) % BN;
+    return B + (int64_t)b_row_of(j) * K + (c < K ? c : K - T::kBCopyFloats);
+  };
+  const float* a_src[T::BUFA ? 1 : T::kACopies];
+  int a_dst[T::kACopies], a_col[T::BUFA ? 1 : T::kACopies];
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
-    const int pos = j * T::kABlock + lane * T::kACopyFloats;
-    const int r = pos / BK;
-    const int c = 4 * (((pos % BK) / 4) ^ a_swizzle2(r)) + pos % 4;
-    const int row = m0 + r < M ? m0 + r : M - 1;
-    a_src[j] = A + (int64_t)row * N + c;
     a_dst[j] = piece_a + j * T::kABlock;
-    a_col[j] = c;
+    if constexpr (!T::BUFA) {
+      a_src[j] = a_ptr_of(j);
+      a_col[j] = a_col_of(j);
+    }
   }
   // In B, p is row p / BN, column p % BN (columns past K read the last column,
   // or the last quad with 16-byte copies; not stored).
-  const float* b_src[T::kBCopies];
-  int b_dst[T::kBCopies], b_row[T::kBCopies];
+  const float* b_src[T::BUFB ? 1 : T::kBCopies];
+  int b_dst[T::kBCopies];
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
-    const int pos = j * T::kBBlock + lane * T::kBCopyFloats;
-    const int r = pos / BN;
-    const int c = k0 + pos % BN;
-    b_src[j] = B + (int64_t)r * K + (c < K ? c : K - T::kBCopyFloats);
     b_dst[j] = piece_b + j * T::kBBlock;
-    b_row[j] = r;
+    if constexpr (!T::BUFB) b_src[j] = b_ptr_of(j);
+  }
+  // Buffer copies (BUFA, BUFB; 4-byte copies, so that a lane covers one float
+  // per copy). A: one buffer over the tile's rows [m0, min(m0 + BM, M)); copy
+  // j of a lane reads row 8 j + lane / 8 of it at column a_col_of(j), which
+  // depends only on the parity of j: the lane's offset is a_voff[j & 1] + j 8
+  // N 4 bytes, and rows past M lie past the buffer and read as zeros (not
+  // stored). B: a buffer per chunk from row n0 of B; copy j reads row j / (BN
+  // / 64) (a uniform offset) at the lane's column for j % (BN / 64), clamped
+  // to the last column. Both offsets stay below 2^31 for N, K < 2^25 / BM.
+  __amdgpu_buffer_rsrc_t a_rsrc;
+  int a_voff[2] = {0, 0};
+  if constexpr (T::BUFA) {
+    const int rows = M - m0 < T::BM ? M - m0 : T::BM;
+    a_rsrc = make_rsrc(A + (int64_t)m0 * N, (uint32_t)rows * (uint32_t)N * 4u);
+    a_voff[0] = (a_row_of(0) * N + a_col_of(0)) * 4;
+    a_voff[1] = (a_row_of(1) * N + a_col_of(1)) * 4 - 8 * N * 4;
+  }
+  constexpr int kBColBlocks = BN / 64;  // 4-byte copies of B per row of a chunk
+  int b_voff[T::BUFB ? kBColBlocks : 1];
+  if constexpr (T::BUFB) {
+#pragma unroll
+    for (int q = 0; q < kBColBlocks; ++q) {
+      const int c = k0 + 64 * q + lane;
+      b_voff[q] = (c < K ? c : K - 1) * 4;
+    }
   }
 
   auto copy_chunk = [&](int j, float* As, float* Bs) __attribute__((always_inline)) {
     const int n0 = chunk_n0(j);
+    if constexpr (T::BUFA) {
 #pragma unroll
-    for (int j = 0; j < T::kACopies; ++j)
-      copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
+      for (int j = 0; j < T::kACopies; ++j)
+        copy4_buffer_to_lds_counted(a_rsrc, a_voff[j & 1] + j * 8 * N * 4, n0 * 4, As + a_dst[j]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < T::kBCopies; ++j)
-      copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+      for (int j = 0; j < T::kACopies; ++j)
+        copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
+    }
+    if constexpr (T::BUFB) {
+      const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * K, (uint32_t)(BK * K) * 4u);
+#pragma unroll
+      for (int j = 0; j < T::kBCopies; ++j)
+        copy4_buffer_to_lds_counted(b_rsrc, b_voff[j % kBColBlocks], (j / kBColBlocks) * K * 4, Bs + b_dst[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < T::kBCopies; ++j)
+        copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+    }
   };
 
   struct Frag {
@@ -296,13 +367,23 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     bool oka[T::kACopies], okb[T::kBCopies];
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j) {
-      oka[j] = n0 + a_col[j] >= 0;
-      va[j] = *reinterpret_cast<const CopyTA*>(oka[j] ? a_src[j] + n0 : A);
+      const float* src;
+      if constexpr (T::BUFA) {
+        oka[j] = n0 + a_col_of(j) >= 0;
+        src = a_ptr_of(j);
+      } else {
+        oka[j] = n0 + a_col[j] >= 0;
+        src = a_src[j];
+      }
+      va[j] = *reinterpret_cast<const CopyTA*>(oka[j] ? src + n0 : A);
     }
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j) {
-      okb[j] = n0 + b_row[j] >= 0;
-      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
+      okb[j] = n0 + b_row_of(j) >= 0;
+      const float* src;
+      if constexpr (T::BUFB) src = b_ptr_of(j);
+      else src = b_src[j];
+      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? src + (int64_t)n0 * K : B);
     }
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;

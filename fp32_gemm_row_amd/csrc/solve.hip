@@ -117,11 +117,22 @@ Rows rows_of(const float* A, const float* B, const float* C, int N, int K) {
   return Rows::kNone;
 }
 
-// 128x128 k-split tiles need 16-byte copies of both operands: with 4-byte
-// copies of either, the copies' addresses push the kernel past 256 VGPRs
-// (27 spilled with 4-byte copies of A).
+// 128x128 k-split tiles: 16-byte copies of both operands, or of A with B's
+// 4-byte copies through buffer loads (a 64-bit address per 4-byte copy pushed
+// the kernel past 256 VGPRs, 27 spilled; B's buffer offsets stay below 2^31
+// for 8 K 4 bytes). Measured on MI355X against 64x64 tiles (us per call):
+// 2048 x 2048 x 2047 161.9 -> 151.4, 1024 x 6144 x 4095 476.4 -> 426.0, 2048
+// x 4096 x 3071 474.2 -> 449.6; 2176 x 1028 x 2047 97.4 -> 100.0. A's 4-byte
+// copies through buffer loads still spilled 11 VGPRs and ran 3-4% slower than
+// 64x64 tiles (2047 x 2051 x 2048, 2040 x 1025 x 2044), and both operands on
+// 4-byte copies would keep more copies in flight than vmcnt counts.
+constexpr int64_t kBufferOffsetLimit = int64_t(1) << 31;
 bool ksplit128_ok(const float* A, const float* B, const float* C, int N, int K) {
-  return rows_of(A, B, C, N, K) == Rows::kAll;
+  switch (rows_of(A, B, C, N, K)) {
+    case Rows::kAll: return true;
+    case Rows::kAOnly: return int64_t(8) * K * 4 < kBufferOffsetLimit;
+    default: return false;
+  }
 }
 
 // Direct global->LDS copies need at least four 16-deep reduction chunks (the
@@ -728,6 +739,10 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
                                                                     compact, nfull);
     default:
       if constexpr (BM == 128) {
+        // B on 4-byte copies through buffer loads (see ksplit128_ok)
+        if (rows == Rows::kAOnly)
+          return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true, BN, false, false, true>>(
+              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
         return FGR_ERR_BAD_PATH;
       } else if (rows == Rows::kAOnly) {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(A, B, C, M, N, K, count, s,
