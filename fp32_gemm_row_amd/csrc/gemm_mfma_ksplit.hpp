@@ -259,21 +259,26 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     if constexpr (!T::BUFB) b_src[j] = b_ptr_of(j);
   }
   // Buffer copies (BUFA, BUFB; 4-byte copies, so that a lane covers one float
-  // per copy). A: one buffer over the tile's rows [m0, min(m0 + BM, M)); copy
-  // j of a lane reads row 8 j + lane / 8 of it at column a_col_of(j), which
-  // depends only on the parity of j: the lane's offset is a_voff[j & 1] + j 8
-  // N 4 bytes, and rows past M lie past the buffer and read as zeros (not
-  // stored). B: a buffer per chunk from row n0 of B; copy j reads row j / (BN
-  // / 64) (a uniform offset) at the lane's column for j % (BN / 64), clamped
-  // to the last column. Both offsets stay below 2^31 for N, K < 2^25 / BM.
-  __amdgpu_buffer_rsrc_t a_rsrc;
+  // per copy). A: copy j of a lane reads row 8 j + lane / 8 of the tile at
+  // column a_col_of(j), which depends only on the parity of j: a buffer per
+  // copy over the tile's rows [8 j, 8 j + 8) that exist, and the lane's
+  // offset a_voff[j & 1] inside it; rows past M lie past the buffer and read
+  // as zeros (not stored). B: a buffer per chunk from row n0 of B; copy j
+  // reads row j / (BN / 64) (a uniform offset) at the lane's column for
+  // j % (BN / 64), clamped to the last column. Offsets stay below 2^31 for
+  // N, K < 2^26.
   int a_voff[2] = {0, 0};
   if constexpr (T::BUFA) {
-    const int rows = M - m0 < T::BM ? M - m0 : T::BM;
-    a_rsrc = make_rsrc(A + (int64_t)m0 * N, (uint32_t)rows * (uint32_t)N * 4u);
+    // the lane's row in its group of 8 and its column (even or odd copies)
     a_voff[0] = (a_row_of(0) * N + a_col_of(0)) * 4;
-    a_voff[1] = (a_row_of(1) * N + a_col_of(1)) * 4 - 8 * N * 4;
+    a_voff[1] = (a_row_of(0) * N + a_col_of(1)) * 4;
   }
+  // copy j's buffer: rows [m0 + 8 j, min(m0 + 8 j + 8, M)) of A (empty past M)
+  auto a_rsrc_of = [&](int j) __attribute__((always_inline)) {
+    const int first_row = m0 + 8 * j;
+    const int rows = first_row >= M ? 0 : (M - first_row < 8 ? M - first_row : 8);
+    return make_rsrc(A + (int64_t)(first_row < M ? first_row : 0) * N, (uint32_t)rows * (uint32_t)N * 4u);
+  };
   constexpr int kBColBlocks = BN / 64;  // 4-byte copies of B per row of a chunk
   int b_voff[T::BUFB ? kBColBlocks : 1];
   if constexpr (T::BUFB) {
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     if constexpr (T::BUFA) {
 #pragma unroll
       for (int j = 0; j < T::kACopies; ++j)
-        copy4_buffer_to_lds_counted(a_rsrc, a_voff[j & 1] + j * 8 * N * 4, n0 * 4, As + a_dst[j]);
+        copy4_buffer_to_lds_counted(a_rsrc_of(j), a_voff[j & 1], n0 * 4, As + a_dst[j]);
     } else {
 #pragma unroll
       for (int j = 0; j < T::kACopies; ++j)

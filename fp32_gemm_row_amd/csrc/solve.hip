@@ -117,20 +117,22 @@ Rows rows_of(const float* A, const float* B, const float* C, int N, int K) {
   return Rows::kNone;
 }
 
-// 128x128 k-split tiles: 16-byte copies of both operands, or of A with B's
-// 4-byte copies through buffer loads (a 64-bit address per 4-byte copy pushed
-// the kernel past 256 VGPRs, 27 spilled; B's buffer offsets stay below 2^31
-// for 8 K 4 bytes). Measured on MI355X against 64x64 tiles (us per call):
-// 2048 x 2048 x 2047 161.9 -> 151.4, 1024 x 6144 x 4095 476.4 -> 426.0, 2048
-// x 4096 x 3071 474.2 -> 449.6; 2176 x 1028 x 2047 97.4 -> 100.0. A's 4-byte
-// copies through buffer loads still spilled 11 VGPRs and ran 3-4% slower than
-// 64x64 tiles (2047 x 2051 x 2048, 2040 x 1025 x 2044), and both operands on
-// 4-byte copies would keep more copies in flight than vmcnt counts.
+// 128x128 k-split tiles: 16-byte copies of both operands, or of one with the
+// other's 4-byte copies through buffer loads (a 64-bit address per 4-byte copy
+// pushed the kernel past 256 VGPRs, 27 spilled; the buffers' offsets stay
+// below 2^31 for 8 K 4 or 8 N 4 bytes). With A on 4-byte copies C must take
+// 128-bit stores too (the epilogue that fits the registers). Measured on
+// MI355X against 64x64 tiles (us per call): 2048 x 2048 x 2047 161.9 ->
+// 151.4, 1024 x 6144 x 4095 476.4 -> 426.0, 1024 x 6143 x 4096 469.6 ->
+// 423.7, 2047 x 2051 x 2048 162.4 -> 150.5; tails within 2% (2176 x 1028 x
+// 2047 97.4 -> 100.0). Both operands on 4-byte copies would keep more copies
+// in flight than vmcnt counts.
 constexpr int64_t kBufferOffsetLimit = int64_t(1) << 31;
 bool ksplit128_ok(const float* A, const float* B, const float* C, int N, int K) {
   switch (rows_of(A, B, C, N, K)) {
     case Rows::kAll: return true;
     case Rows::kAOnly: return int64_t(8) * K * 4 < kBufferOffsetLimit;
+    case Rows::kBOnly: return int64_t(8) * N * 4 < kBufferOffsetLimit && K % 4 == 0 && aligned(C, 16);
     default: return false;
   }
 }
@@ -739,9 +741,12 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
                                                                     compact, nfull);
     default:
       if constexpr (BM == 128) {
-        // B on 4-byte copies through buffer loads (see ksplit128_ok)
+        // one operand on 4-byte copies through buffer loads (see ksplit128_ok)
         if (rows == Rows::kAOnly)
           return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true, BN, false, false, true>>(
+              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+        if (rows == Rows::kBOnly && K % 4 == 0 && aligned(C, 16))
+          return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, false, BN, true, true, true>>(
               A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
         return FGR_ERR_BAD_PATH;
       } else if (rows == Rows::kAOnly) {

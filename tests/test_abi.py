@@ -135,14 +135,15 @@ def test_forced_path_rejections(lib):
         assert call(lib, A0, B0, C0, 512, 130, 512, path) == fgr.ERR_DEVICE
         assert call(lib, A0, B0, C0, 512, 128, 502, path) == fgr.ERR_DEVICE
         assert call(lib, A0 + 4, B0, C0, 512, 128, 512, path) == fgr.ERR_DEVICE
-    # the k-split paths need N >= 64; tile 128 needs 128-bit rows of A, and
-    # the tail form has no 32x32 tiles
+    # the k-split paths need N >= 64; tile 128 needs 128-bit rows of A, or of
+    # B and C, and the tail form has no 32x32 tiles
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 130, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0 + 4, B0 + 4, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_BAD_PATH
-    assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH  # B rows only
+    assert call(lib, A0 + 4, B0, C0 + 4, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH  # B, not C
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # A rows only
     assert call(lib, A0, B0 + 4, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_DEVICE
+    assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # B and C rows
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 256) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 32) == fgr.ERR_BAD_PATH
     for tile in (0, 64, 32):
