@@ -9,6 +9,7 @@ C is prefilled with NaN before every call, so an element the kernels never
 write fails the finiteness check.
 """
 
+import collections
 import sys
 
 import numpy as np
@@ -727,6 +728,35 @@ def test_controlled_comparison_variants_exact(shape):
         fgr.solve_variant(dA, dB, dC, M, N, K, v)
         torch.cuda.synchronize()
         assert_exact(dC.cpu().numpy().reshape(M, K), Cref, f"{shape} {name}")
+
+
+def random_shapes(count, seed):
+    """Seeded random (M, N, K, offsets): dimensions log-uniform over 1..700
+    (some reductions up to 20000), pointer offsets of 0-3 floats."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        M, N, K = (int(np.exp(rng.uniform(0, np.log(700)))) for _ in range(3))
+        if i % 6 == 5:
+            N = int(rng.integers(2000, 20000))
+        offsets = tuple(int(x) for x in rng.integers(0, 4, size=3)) if i % 3 == 2 else (0, 0, 0)
+        out.append((M, N, K, offsets))
+    return out
+
+
+def test_random_shapes_exact():
+    # 60 seeded random shapes and alignments through solve()'s own choice
+    # (every path the rules reach at these sizes), exact on integer data
+    seen = collections.Counter()
+    for (M, N, K, offsets) in random_shapes(60, seed=70):
+        A, B = synth.make_inputs(M, N, K, "integer", seed=M * 7 + N * 3 + K)
+        Cref, _ = oracle.gemm(A, B)
+        path = fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]
+        seen[path] += 1
+        say(f"random {M}x{N}x{K} offsets {offsets}: {path}")
+        assert_exact(gpu_gemm(A, B, offsets=offsets), Cref, f"{M}x{N}x{K} offsets {offsets}")
+    say(f"paths taken: {dict(seen)}")
+    assert len(seen) >= 4
 
 
 def test_default_stream_is_torchs_current_stream():
