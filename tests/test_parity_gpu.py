@@ -759,6 +759,28 @@ def test_random_shapes_exact():
     assert len(seen) >= 4
 
 
+def test_random_large_shapes_sampled():
+    # 16 seeded random shapes from 700 to 5000 per dimension, with random
+    # alignments: the direct-copy, k-split (128x128 with buffer copies
+    # included), tail and split-reduction paths as solve() picks them; on
+    # integer data the sampled outputs (tile corners of 64x64 tiles and random
+    # positions) must equal the oracle's exactly
+    rng = np.random.default_rng(80)
+    seen = collections.Counter()
+    for i in range(16):
+        M, N, K = (int(np.exp(rng.uniform(np.log(700), np.log(5000)))) for _ in range(3))
+        offsets = tuple(int(x) for x in rng.integers(0, 4, size=3)) if i % 2 else (0, 0, 0)
+        path = fgr.PATH_NAMES[fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K)]
+        say(f"random large {M}x{N}x{K} offsets {offsets}: {path}")
+        A, B = synth.make_inputs(M, N, K, "integer", seed=i + 90)
+        C = gpu_gemm(A, B, offsets=offsets)
+        rows, cols = sample_positions(M, K, 64, np.random.default_rng(i), extra=512)
+        Cref, _ = oracle.gemm_at(A, B, rows, cols)
+        assert_exact(C[rows, cols][None, :], Cref[None, :], f"{M}x{N}x{K} offsets {offsets} sampled")
+        seen[path] += 1
+    say(f"paths taken: {dict(seen)}")
+
+
 def test_default_stream_is_torchs_current_stream():
     # solve() without a stream argument enqueues on torch's current stream
     # (the binding reads its raw handle); inside `with torch.cuda.stream(s)`
