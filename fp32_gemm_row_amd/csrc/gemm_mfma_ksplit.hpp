@@ -31,6 +31,12 @@
 // chunk is chunk 0). With N >= 64 every wave owns at least two chunks, so a
 // copy clamped to a wave's last chunk never reads chunk 0.
 //
+// lda is A's row stride (N, or more for a copy of A whose rows were padded
+// to 16-byte multiples) and pad the number of zero columns such a copy has in
+// front of each row: reduction index n of the kernel is then row n - pad of
+// B, and B's rows before 0 (all in chunk 0, read through registers) are taken
+// as zeros and never read.
+//
 // LDS: stage s of every wave is a separate LDS object per operand (so that the
 // compiler can tell a stage's reads from the copies into another), each holding
 // the four waves' pieces. A rows are 8 floats (two quads) stored in the order
@@ -140,7 +146,7 @@ template <class T>
 __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
     int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact,
-    int nfull) {
+    int nfull, int lda, int pad) {
   constexpr int S = T::S, BK = T::BK, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) float As0[T::kStageA];
   __shared__ __attribute__((aligned(1024))) float As1[T::kStageA];
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   auto a_ptr_of = [&](int j) __attribute__((always_inline)) {
     const int r = a_row_of(j);
     const int row = m0 + r < M ? m0 + r : M - 1;
-    return A + (int64_t)row * N + a_col_of(j);
+    return A + (int64_t)row * lda + a_col_of(j);
   };
   auto b_row_of = [&](int j) __attribute__((always_inline)) {
     return (j * T::kBBlock + lane * T::kBCopyFloats) / BN;
@@ -270,14 +276,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   int a_voff[2] = {0, 0};
   if constexpr (T::BUFA) {
     // the lane's row in its group of 8 and its column (even or odd copies)
-    a_voff[0] = (a_row_of(0) * N + a_col_of(0)) * 4;
-    a_voff[1] = (a_row_of(0) * N + a_col_of(1)) * 4;
+    a_voff[0] = (a_row_of(0) * lda + a_col_of(0)) * 4;
+    a_voff[1] = (a_row_of(0) * lda + a_col_of(1)) * 4;
   }
   // copy j's buffer: rows [m0 + 8 j, min(m0 + 8 j + 8, M)) of A (empty past M)
   auto a_rsrc_of = [&](int j) __attribute__((always_inline)) {
     const int first_row = m0 + 8 * j;
     const int rows = first_row >= M ? 0 : (M - first_row < 8 ? M - first_row : 8);
-    return make_rsrc(A + (int64_t)(first_row < M ? first_row : 0) * N, (uint32_t)rows * (uint32_t)N * 4u);
+    return make_rsrc(A + (int64_t)(first_row < M ? first_row : 0) * lda, (uint32_t)rows * (uint32_t)lda * 4u);
   };
   constexpr int kBColBlocks = BN / 64;  // 4-byte copies of B per row of a chunk
   int b_voff[T::BUFB ? kBColBlocks : 1];
@@ -301,14 +307,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
         copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
     }
     if constexpr (T::BUFB) {
-      const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * K, (uint32_t)(BK * K) * 4u);
+      const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + (int64_t)(n0 - pad) * K, (uint32_t)(BK * K) * 4u);
 #pragma unroll
       for (int j = 0; j < T::kBCopies; ++j)
         copy4_buffer_to_lds_counted(b_rsrc, b_voff[j % kBColBlocks], (j / kBColBlocks) * K * 4, Bs + b_dst[j]);
     } else {
 #pragma unroll
       for (int j = 0; j < T::kBCopies; ++j)
-        copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+        copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)(n0 - pad) * K, Bs + b_dst[j]);
     }
   };
 
@@ -384,11 +390,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     }
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j) {
-      okb[j] = n0 + b_row_of(j) >= 0;
+      okb[j] = n0 + b_row_of(j) >= pad;
       const float* src;
       if constexpr (T::BUFB) src = b_ptr_of(j);
       else src = b_src[j];
-      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? src + (int64_t)n0 * K : B);
+      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? src + (int64_t)(n0 - pad) * K : B);
     }
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;

@@ -133,8 +133,9 @@ bool ksplit128_ok(const float* A, const float* B, const float* C, int N, int K) 
     case Rows::kAll: return true;
     case Rows::kAOnly: return int64_t(8) * K * 4 < kBufferOffsetLimit;
     case Rows::kBOnly: return int64_t(8) * N * 4 < kBufferOffsetLimit && K % 4 == 0 && aligned(C, 16);
-    default: return false;
+    case Rows::kNone: return int64_t(8) * K * 4 < kBufferOffsetLimit && N < INT_MAX - 3;  // A packed first
   }
+  return false;
 }
 
 // Direct global->LDS copies need at least four 16-deep reduction chunks (the
@@ -368,9 +369,15 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     // four waves of a workgroup (k-split), the largest that still gives every
     // CU a tile; a last partial wave of up to half the CUs is spread over
     // every CU (launch_ksplit_tail).
-    if (ksplit128_ok(A, B, C, N, K) && t128 >= cus) {
-      const int64_t rem = t128 % cus;
-      if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
+    // (With A to be packed first, 128x128 tiles only where their last wave
+    // is full or a tail of at most half the CUs: measured on MI355X, us per
+    // call, 64x64 tiles -> packed 128x128: 2047 x 8191 x 2047 712 -> 586,
+    // 3001^3 591 -> 536, 4095 x 2049 x 2051 383 -> 354, 2047^3 199 -> 190;
+    // but 2500^3, 400 tiles of 128, 355 -> 373.)
+    const int64_t rem128 = t128 % cus;
+    const bool packed = rows_of(A, B, C, N, K) == Rows::kNone;
+    if (ksplit128_ok(A, B, C, N, K) && t128 >= cus && (!packed || rem128 <= ksplit_tail_tiles(cus))) {
+      if (rem128 != 0 && rem128 <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
     }
     if (t64 >= cus) {
@@ -720,11 +727,12 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
 
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
-                      int parts, float* W, int first, int compact, int nfull) {
+                      int parts, float* W, int first, int compact, int nfull, int lda, int pad) {
   int tiles_m = (int)cdiv(M, Cfg::BM);
   int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
-  void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &group, &parts, &W, &first, &compact, &nfull};
+  void* args[] = {&A,     &B,    &C,     &M,       &N,     &K,     &tiles_m, &tiles_n, &group,
+                  &parts, &W,    &first, &compact, &nfull, &lda,   &pad};
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
                 nfull + (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts, Cfg::kThreads, args, s);
 }
@@ -734,32 +742,60 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
 // 4-byte copies of both; 128x128 tiles only in the first form (ksplit128_ok).
 template <int BM, int BN = BM>
 int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
-                       hipStream_t s, int parts, float* W, int first, int compact, int nfull) {
+                       hipStream_t s, int parts, float* W, int first, int compact, int nfull, int lda,
+                       int pad) {
   switch (rows) {
     case Rows::kAll:
       return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                    compact, nfull);
+                                                                    compact, nfull, lda, pad);
     default:
       if constexpr (BM == 128) {
         // one operand on 4-byte copies through buffer loads (see ksplit128_ok)
         if (rows == Rows::kAOnly)
           return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true, BN, false, false, true>>(
-              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
         if (rows == Rows::kBOnly && K % 4 == 0 && aligned(C, 16))
           return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, false, BN, true, true, true>>(
-              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
         return FGR_ERR_BAD_PATH;
       } else if (rows == Rows::kAOnly) {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(A, B, C, M, N, K, count, s,
-                                                                                    parts, W, first, compact, nfull);
+                                                                                    parts, W, first, compact, nfull, lda, pad);
       } else if (rows == Rows::kBOnly) {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true, false>>(A, B, C, M, N, K, count, s,
-                                                                                    parts, W, first, compact, nfull);
+                                                                                    parts, W, first, compact, nfull, lda, pad);
       } else {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                       compact, nfull);
+                                                                       compact, nfull, lda, pad);
       }
   }
+}
+
+// 128x128 k-split tiles when neither A's nor B's rows are 16-byte aligned: A
+// is first copied into rows of N rounded up to a multiple of 4, zeros in
+// front (pack_rows_kernel), into a stream-ordered allocation of its own on
+// `s`; the aligned-A form then runs over the padded reduction (B's rows
+// before the padding are taken as zeros, not read). Fails with
+// FGR_ERR_LAUNCH if the allocation fails (the caller's rules then never
+// chose this form: see ksplit128_ok).
+int launch_ksplit128_packed(const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
+                            hipStream_t s, int parts, float* W, int first, int compact, int nfull) {
+  int lda = (N + 3) & ~3;
+  const int pad = lda - N;
+  float* Ap = nullptr;
+  if (pool_alloc(&Ap, (size_t)M * (size_t)lda * sizeof(float), s) != hipSuccess) {
+    (void)hipGetLastError();
+    return FGR_ERR_LAUNCH;
+  }
+  int m = M, n = N;
+  void* args[] = {&A, &Ap, &m, &n, &lda};
+  int rc = launch(reinterpret_cast<const void*>(&fgr::pack_rows_kernel), cdiv((int64_t)M * (lda / 4), 256), 256,
+                  args, s);
+  if (rc == FGR_OK)
+    rc = launch_ksplit_rows<128>(Rows::kAOnly, Ap, B, C, M, lda, K, count, s, parts, W, first, compact, nfull, lda,
+                                 pad);
+  (void)hipFreeAsync(Ap, s);
+  return rc;
 }
 
 // The k-split kernel with tile x tile tiles over tiles [first, first + count)
@@ -771,17 +807,20 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
 // follow them.
 int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
                   hipStream_t s, int parts = 1, float* W = nullptr, int first = 0, int compact = 0,
-                  int nfull = 0) {
-  const Rows rows = rows_of(A, B, C, N, K);
+                  int nfull = 0, int lda = -1, int pad = 0) {
+  if (lda < 0) lda = N;
+  const Rows rows = rows_of(A, B, C, lda, K);
+  if (tile == FGR_TILE_128 && rows == Rows::kNone) return launch_ksplit128_packed(A, B, C, M, N, K, count, s, parts,
+                                                                                   W, first, compact, nfull);
   switch (tile) {
     case FGR_TILE_128:
-      return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+      return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
     case FGR_TILE_64:
-      return launch_ksplit_rows<64>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+      return launch_ksplit_rows<64>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
     case FGR_TILE_32:
-      return launch_ksplit_rows<32>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+      return launch_ksplit_rows<32>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
     case FGR_TILE_32X128:
-      return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
+      return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
     default: return FGR_ERR_BAD_PATH;
   }
 }

@@ -135,11 +135,12 @@ def test_forced_path_rejections(lib):
         assert call(lib, A0, B0, C0, 512, 130, 512, path) == fgr.ERR_DEVICE
         assert call(lib, A0, B0, C0, 512, 128, 502, path) == fgr.ERR_DEVICE
         assert call(lib, A0 + 4, B0, C0, 512, 128, 512, path) == fgr.ERR_DEVICE
-    # the k-split paths need N >= 64; tile 128 needs 128-bit rows of A, or of
-    # B and C, and the tail form has no 32x32 tiles
+    # the k-split paths need N >= 64; tile 128 takes any rows but those of B
+    # and not C aligned with A's not (A is packed only when B's are not
+    # aligned either), and the tail form has no 32x32 tiles
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 130, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH
-    assert call(lib, A0 + 4, B0 + 4, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0, B0, C0, 512, 130, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # A packed first
+    assert call(lib, A0 + 4, B0 + 4, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_DEVICE
     assert call(lib, A0 + 4, B0, C0 + 4, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH  # B, not C
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # A rows only
     assert call(lib, A0, B0 + 4, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_DEVICE
@@ -152,7 +153,7 @@ def test_forced_path_rejections(lib):
     # the cross-workgroup split needs N >= 128 (two parts of 8 chunks); tile
     # 128 needs 128-bit rows; no 256 tiles
     assert call(lib, A0, B0, C0, 512, 120, 512, fgr.PATH_MFMA_SPLITK) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 130, 502, fgr.PATH_MFMA_SPLITK, 128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0 + 4, B0, C0 + 4, 512, 128, 512, fgr.PATH_MFMA_SPLITK, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, 256) == fgr.ERR_BAD_PATH
     for tile in (0, 128, 64, 32):
         assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, tile) == fgr.ERR_DEVICE

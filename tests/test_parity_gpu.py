@@ -279,6 +279,10 @@ def test_large_ragged_sampled(shape):
     ((2048, 2048, 2047), fgr.PATH_MFMA_KSPLIT, 128), ((2000, 1028, 2045), fgr.PATH_MFMA_KSPLIT, 128),
     ((2176, 1028, 2047), fgr.PATH_MFMA_KSPLIT_TAIL, 128), ((2047, 2051, 2048), fgr.PATH_MFMA_KSPLIT, 128),
     ((2040, 1025, 2044), fgr.PATH_MFMA_KSPLIT, 128), ((2176, 1025, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
+    # neither operand's rows aligned: A packed into padded rows first (1, 2
+    # and 3 padding columns)
+    ((2040, 2047, 2043), fgr.PATH_MFMA_KSPLIT, 128), ((2000, 2046, 2045), fgr.PATH_MFMA_KSPLIT, 128),
+    ((2047, 2049, 2051), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
     # tails of 64x64 tiles with N >= 1024: whole and split tiles in one grid
     # (16-byte copies of both operands, of B only, of A only)
     ((1040, 2048, 1040), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((1024, 1025, 1088), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
@@ -388,17 +392,10 @@ def test_ksplit_operand_alignments_exact(shape, offsets):
                        (fgr.PATH_MFMA_SPLITK, 64), (fgr.PATH_MFMA_SPLITK, fgr.TILE_32X128),
                        (fgr.PATH_MFMA_KSPLIT_TAIL, 64)]:
         assert_exact(gpu_gemm(A, B, path, tile, offsets=offsets), Cref, f"{shape} {offsets} path={path} tile={tile}")
-    # 128x128 tiles: one operand's 4-byte copies through buffer loads
-    # (refused when neither A's rows nor B's and C's are 16-byte aligned)
-    a_rows = N % 4 == 0 and offsets[0] % 4 == 0
-    bc_rows = K % 4 == 0 and offsets[1] % 4 == 0 and offsets[2] % 4 == 0
-    ok128 = a_rows or bc_rows
+    # 128x128 tiles: one operand's 4-byte copies through buffer loads, or,
+    # with neither A's rows nor B's aligned, A first copied into padded rows
     for path in (fgr.PATH_MFMA_KSPLIT, fgr.PATH_MFMA_SPLITK, fgr.PATH_MFMA_KSPLIT_TAIL):
-        if ok128:
-            assert_exact(gpu_gemm(A, B, path, 128, offsets=offsets), Cref, f"{shape} {offsets} path={path} tile=128")
-        else:
-            with pytest.raises(fgr.GemmError):
-                gpu_gemm(A, B, path, 128, offsets=offsets)
+        assert_exact(gpu_gemm(A, B, path, 128, offsets=offsets), Cref, f"{shape} {offsets} path={path} tile=128")
 
 
 @pytest.mark.parametrize("shape", [(1023, 1025, 1027), (1024, 1024, 1024), (300, 2000, 260), (1, 3, 1), (129, 17, 5)],
