@@ -65,6 +65,9 @@ struct KsplitConfig {
   static constexpr int BM = BM_, BN = BN_, BK = 8, S = S_;
   static constexpr bool VA = VA_, VB = VB_, VC = VC_, VEC = VA_ && VB_ && VC_;
   static constexpr bool BUFA = BUF_ && !VA_, BUFB = BUF_ && !VB_;
+  // only the form with aligned A and B through buffer loads reads a padded
+  // copy of A; every other form takes lda = N and pad = 0 as constants
+  static constexpr bool kPaddedA = VA_ && BUFB;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRB = BM / 32, kCB = BN / 32;
@@ -148,6 +151,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact,
     int nfull, int lda, int pad) {
   constexpr int S = T::S, BK = T::BK, BN = T::BN;
+  if constexpr (!T::kPaddedA) {
+    lda = N;
+    pad = 0;
+  }
   __shared__ __attribute__((aligned(1024))) float As0[T::kStageA];
   __shared__ __attribute__((aligned(1024))) float As1[T::kStageA];
   __shared__ __attribute__((aligned(1024))) float As2[T::kStageA];

@@ -728,6 +728,7 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
                       int parts, float* W, int first, int compact, int nfull, int lda, int pad) {
+  if (!Cfg::kPaddedA && (lda != N || pad != 0)) return FGR_ERR_BAD_PATH;
   int tiles_m = (int)cdiv(M, Cfg::BM);
   int tiles_n = (int)cdiv(K, Cfg::BN);
   int group = kTileGroup;
