@@ -252,6 +252,21 @@ void for_each_parts(int t, int M, int N, int K, int cus, F&& f) {
   for (int p = 2; N / p >= kSplitkMinPart && tiles * p <= 4 * (int64_t)cus; p *= 2) f(p);
 }
 
+// Split plans with 128x128 tiles: taken over the estimate's 64x64 or 32x32
+// choice when they pad the output no more than 64x64 tiles do and their parts
+// are at least this long. Each operand element is then read by fewer tiles,
+// and the long parts amortise the 128x128 tile's start and its 64 KiB
+// partial write; the estimate does not model either. MI355X, us per call,
+// 64x64 plan vs 128x128 plan (128x128 parts): 128 x 2097152 x 128 980 vs 788
+// (8192), 512 x 131072 x 512 572 vs 513 (8192), 128 x 1048576 x 128 503 vs
+// 418 (4096), 256 x 262144 x 256 364 vs 307 (4096), 512 x 65536 x 512 273 vs
+// 258 (4096), 128 x 524288 x 128 253 vs 222 (2048), 128 x 262144 x 256 170
+// vs 148 (2048), 256 x 131072 x 256 146 vs 140 (2048). With parts of 1024 or
+// less it lost (128 x 262144 x 128 83 vs 86, 384 x 32768 x 384 114 vs 126),
+// and so it did where it pads more (192 x 262144 x 192 230 vs 260, 320 x
+// 200000 x 320 412 vs 572).
+constexpr int kSplitk128MinPart = 2048;
+
 // Best parts (>= 2) for k-split tiles of size t, by the estimate above.
 SplitPlan splitk_plan_tile(int t, int M, int N, int K, int cus) {
   SplitPlan best{t, 2};
@@ -391,7 +406,13 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     // with 4-byte copies: 400 x 1000 x 401 10.0 vs 14.8 us, 512 x 4095 x 512
     // 30.8 vs 50.9)
     const SplitPlan sp = splitk_plan(M, N, K, cus);
-    if (sp.parts >= 2) return {FGR_PATH_MFMA_SPLITK, sp.tile};
+    if (sp.parts >= 2) {
+      if (rows_of(A, B, C, N, K) != Rows::kNone && ksplit128_ok(A, B, C, N, K) &&
+          4 * cdiv(M, 128) * cdiv(K, 128) == t64 &&
+          N / splitk_plan_tile(FGR_TILE_128, M, N, K, cus).parts >= kSplitk128MinPart)
+        return {FGR_PATH_MFMA_SPLITK, FGR_TILE_128};
+      return {FGR_PATH_MFMA_SPLITK, sp.tile};
+    }
     return {FGR_PATH_MFMA_KSPLIT, sp.tile};
   }
   // N < 64 with fewer 64x64 tiles than CUs: the split kernel's 32x32 tiles

@@ -293,12 +293,20 @@ def test_split_reduction_choices():
     # across workgroups; 64x64 tiles for tall outputs, 32x32 for skinny ones
     # (less padding), by the time estimate
     for shape, tile in [((256, 65536, 256), 64), ((128, 262144, 128), 64), ((64, 65536, 1024), fgr.TILE_32X128),
-                        ((512, 65536, 512), 64), ((16, 1048576, 64), 32), ((130, 20000, 66), 32),
+                        ((512, 65536, 512), 128), ((16, 1048576, 64), 32), ((130, 20000, 66), 32),
                         ((24, 65536, 1024), fgr.TILE_32X128), ((16, 16384, 4096), fgr.TILE_32X128),
-                        ((512, 8192, 512), 64), ((1024, 32768, 512), 64), ((96, 8192, 4096), 32)]:
+                        ((512, 8192, 512), 64), ((1024, 32768, 512), 128), ((96, 8192, 4096), 32)]:
         assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
         assert st(A0, B0, C0, *shape) == tile, shape
         assert sp(A0 + 4, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape  # 4-byte copies too
+    # 128x128 split tiles: parts of at least 2048 and no more padding than
+    # 64x64 tiles; both operands' rows unaligned, or shorter parts: 64x64
+    for shape, tile in [((128, 524288, 128), 128), ((640, 65536, 640), 128), ((192, 262144, 192), 64),
+                        ((320, 200000, 320), 64), ((256, 100000, 256), 64), ((128, 262144, 128), 64)]:
+        assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
+        assert st(A0, B0, C0, *shape) == tile, shape
+    assert st(A0 + 4, B0, C0, 128, 524288, 128) == 128  # A's rows through buffer loads
+    assert st(A0 + 4, B0 + 4, C0, 128, 524288, 128) == 64
     # enough 32x32 tiles for every CU, or too short a reduction: no split
     assert sp(A0, B0, C0, 512, 4096, 512) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles

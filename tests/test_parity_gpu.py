@@ -778,6 +778,22 @@ def test_random_large_shapes_sampled():
     say(f"paths taken: {dict(seen)}")
 
 
+def test_long_reduction_128_split_exact():
+    # few output tiles over a long reduction, where solve() splits the
+    # reduction over 128x128 tiles (parts of 2048 or more): aligned, and with
+    # A's rows through buffer loads; exact on integer data at sampled outputs
+    # (every |partial sum| stays below 4 * 4 * 524288 < 2^24)
+    for (M, N, K), offsets in [((128, 524288, 128), (0, 0, 0)), ((128, 524288, 128), (1, 0, 0)),
+                               ((512, 65536, 512), (0, 0, 0))]:
+        assert fgr.select_tile((1 << 40) + 4 * offsets[0], 2 << 40, 3 << 40, M, N, K) == 128
+        say(f"128x128 split {M}x{N}x{K} offsets {offsets}")
+        A, B = synth.make_inputs(M, N, K, "integer", seed=M + 7)
+        C = gpu_gemm(A, B, offsets=offsets)
+        rows, cols = sample_positions(M, K, 128, np.random.default_rng(M), extra=256)
+        Cref, _ = oracle.gemm_at(A, B, rows, cols)
+        assert_exact(C[rows, cols][None, :], Cref[None, :], f"{M}x{N}x{K} offsets {offsets} sampled")
+
+
 def test_default_stream_is_torchs_current_stream():
     # solve() without a stream argument enqueues on torch's current stream
     # (the binding reads its raw handle); inside `with torch.cuda.stream(s)`
