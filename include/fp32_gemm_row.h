@@ -138,8 +138,9 @@ extern "C" {
  * Workspace: when the output has too few tiles (or, for M <= 8, too few
  * 32-column blocks) to give every CU a workgroup and N is long, the reduction
  * is split into P parts across workgroups (paths MFMA_SPLITK and GEMV_*): the
- * library then needs a workspace of P*M*K floats (at most 16 MiB on a
- * 256-CU device when solve() picks the split; a forced MFMA_SPLITK on a large
+ * library then needs a workspace of P*M*K floats (when solve() picks the
+ * split, P * tiles <= 4 * CUs: on a 256-CU device at most 16 MiB with 64 x 64
+ * or smaller tiles, 64 MiB with 128 x 128 tiles; a forced MFMA_SPLITK on a large
  * output takes P = 2, i.e. 2*M*K floats). Calls on different streams never
  * share one. Each stream (up to 16 per process, identified by handle and
  * stream id) keeps its workspace between calls, up to 64 MiB: it is
