@@ -21,7 +21,12 @@ clock. Prints ONE JSON line:
                LDS busy fraction, LDS bank conflicts per access and MFMA
                FLOP / 2MNK from a rocprofv3 --pmc run (same file, same rule)
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
-               (leading rows of A), on this host's cores
+               (leading rows of A, or the whole product repeated), on this
+               host's cores
+  parity       the timed run's C against the oracle product that the
+               cpu_baseline leg computed (every element of the rows it
+               covers: all of them when it ran the whole product): the
+               largest |C - C_oracle| / (1e-5 S + 1e-6) and pass / fail
 
 Workloads (seeded synthetic inputs, synth/): leetgpu8192 (default, the
 LeetGPU timed shape M=8192, N=6144, K=4096, normal entries / sqrt(N)),
@@ -377,15 +382,20 @@ def roundtrip(w, A, B, dA, dB, dC, dev, iters=10):
     }
 
 
-def cpu_baseline(w, A, B, target_s: float):
-    """Time the oracle on the first R rows of A (R sized for about target_s)."""
+def cpu_baseline(w, A, B, target_s: float, threads: int = 0):
+    """Time the oracle on the first R rows of A (R sized for about target_s).
+
+    Returns (record, (R, C, S)): the JSON record, and the oracle's fp64
+    product and |a||b| sums of rows 0..R-1 from its first timed run (the whole
+    product when R == M), which the parity check compares the GPU's output
+    with. threads <= 0: every host thread."""
     import oracle
 
-    threads = oracle.max_threads()
+    threads = threads if threads > 0 else oracle.max_threads()
     rows = min(8, w.M)
     while True:  # probe until a timing is long enough to extrapolate from
         t0 = time.perf_counter()
-        oracle.gemm(A[:rows], B, threads=threads)
+        first = oracle.gemm(A[:rows], B, threads=threads)
         probe = time.perf_counter() - t0
         if probe >= 0.5 or rows >= w.M:
             break
@@ -394,7 +404,7 @@ def cpu_baseline(w, A, B, target_s: float):
     elapsed = probe
     if R > rows:
         t0 = time.perf_counter()
-        oracle.gemm(A[:R], B, threads=threads)
+        first = oracle.gemm(A[:R], B, threads=threads)
         elapsed = time.perf_counter() - t0
     # a whole product shorter than the target: repeat it
     reps = 1
@@ -414,13 +424,81 @@ def cpu_baseline(w, A, B, target_s: float):
     what = f"rows 0..{R - 1} of A against all of B ({R}x{w.N}x{w.K}, fp64 with |a||b| sums)"
     if reps > 1:
         what = f"the whole product ({w.M}x{w.N}x{w.K}, fp64 with |a||b| sums) {reps} times"
-    return {
+    record = {
         "value": round(value, 6),
         "unit": unit,
         "cores": threads,
         "kind": "oracle",
         "sample": f"{what}, {elapsed:.2f} s",
     }
+    return record, (R, first[0], first[1])
+
+
+def parity_record(C, reference):
+    """Every output of rows 0..R-1 of the GPU's C (numpy float32, M x K)
+    against the oracle's product of those rows: finite, and |C - Cref| <=
+    1e-5 S + 1e-6 element by element."""
+    import numpy as np
+
+    R, Cref, S = reference
+    got = C[:R].astype(np.float64)
+    finite = bool(np.isfinite(got).all())
+    ratio = float(np.max(np.abs(got - Cref) / (1e-5 * S + 1e-6))) if finite else float("inf")
+    return {
+        "elements": int(got.size),
+        "rows": int(R),
+        "max_err_over_tol": round(ratio, 6),
+        "finite": finite,
+        "pass": finite and ratio <= 1.0,
+        "bar": "|C - C_oracle| <= 1e-5 * sum_n |A[m,n]||B[n,k]| + 1e-6 per element (fp64 oracle)",
+    }
+
+
+def batched_ms(fn, launches, stream):
+    """Mean time per launch of `launches` back-to-back launches between two HIP
+    events on `stream` (no per-launch events: for kernels shorter than an
+    event pair's own cost, as the tutorial's section 3 times its kernels)."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(launches):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / launches
+
+
+READ_BYTES = 1 << 30  # the streaming-read buffer: 4x the 256 MB last-level cache
+
+
+def read_ceiling(dev, stream, cus, steps=20, warmup=5):
+    """The device's streaming-read rate: fgr_stream_read over a 1 GiB buffer
+    (each float read once, 128-bit loads), per-launch HIP events, for a few
+    grid sizes; the best one is the measured read ceiling."""
+    import torch
+
+    import fp32_gemm_row_amd as fgr
+
+    n = READ_BYTES // 4
+    X = torch.ones(n, dtype=torch.float32, device=dev)
+    sweep = []
+    for per_cu in (2, 4, 8, 16):
+        blocks = cus * per_cu
+        out = torch.empty(blocks, dtype=torch.float32, device=dev)
+
+        def fn(i, out=out, blocks=blocks):
+            fgr.stream_read(X, n, out, blocks, stream=stream)
+
+        ms = kernel_ms(fn, steps, warmup, stream)
+        if not torch.isfinite(out).all():
+            raise RuntimeError("stream_read produced non-finite sums")
+        sweep.append({"blocks": blocks, "ms": round(ms, 5), "gbs": round(READ_BYTES / ms / 1e6, 1)})
+    best = max(sweep, key=lambda r: r["gbs"])
+    del X
+    return {"bytes": READ_BYTES, "gbs": best["gbs"], "blocks": best["blocks"], "sweep": sweep}
 
 
 def main() -> int:
@@ -526,6 +604,9 @@ def main() -> int:
     wall = time.perf_counter() - t0
 
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    # the same launches back to back between two events only
+    batch_launches = max(50, args.steps)
+    batch_ms = batched_ms(step, batch_launches, stream)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     ms_per_step = wall / args.steps * 1e3
     gemv = w.M == 1
@@ -544,6 +625,16 @@ def main() -> int:
     roof["frac"] = round(achieved / roof["peak"], 4)
     roof["traffic"] = recorded_traffic(args.workload)
     roof["counters"] = recorded_counters(args.workload)
+    roof["batched"] = {
+        "launches": batch_launches,
+        "ms_per_launch": round(batch_ms, 5),
+        "achieved": round(w.algorithmic_bytes / batch_ms / 1e6, 2) if gemv else round(w.flops / batch_ms / 1e9, 3),
+    }
+    if gemv:
+        # the measured streaming-read ceiling beside the datasheet peak
+        ceiling = read_ceiling(dev, stream, torch.cuda.get_device_properties(dev).multi_processor_count)
+        ceiling["frac"] = round(achieved / ceiling["gbs"], 4)
+        roof["read_ceiling"] = ceiling
     roof["launch_ms"] = {
         "mean": round(avg_launch_s * 1e3, 4),
         "min": round(min(launch_ms), 4),
@@ -587,7 +678,16 @@ def main() -> int:
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = COPY_BYTES
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+        # the oracle's product from the baseline's first timed run also checks
+        # the timed run's output, element by element
+        C_gpu = dC.cpu().numpy().reshape(w.M, w.K)
+        out["cpu_baseline"], reference = cpu_baseline(w, A, B, args.cpu_seconds)
+        out["parity"] = parity_record(C_gpu, reference)
+        del reference
+        if w.flops < 1e10:
+            # small workloads: the oracle on one host thread as well
+            single, _ = cpu_baseline(w, A, B, min(args.cpu_seconds, 10.0), threads=1)
+            out["cpu_baseline"]["single_thread"] = single
     print(json.dumps(out), flush=True)
     return 0
 

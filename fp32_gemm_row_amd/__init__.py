@@ -75,6 +75,8 @@ EXPORTS = (
     "fgr_variant_count",
     "fgr_variant_name",
     "fgr_solve_variant",
+    "fgr_set_workspace_limit",
+    "fgr_stream_read",
 )
 
 
@@ -119,6 +121,10 @@ def load_library(path: str = LIB_PATH):
     lib.fgr_variant_name.restype = ctypes.c_char_p
     lib.fgr_solve_variant.argtypes = [vp, vp, vp, ci, ci, ci, vp, ci]
     lib.fgr_solve_variant.restype = ci
+    lib.fgr_set_workspace_limit.argtypes = [ctypes.c_longlong]
+    lib.fgr_set_workspace_limit.restype = ctypes.c_longlong
+    lib.fgr_stream_read.argtypes = [vp, ctypes.c_longlong, vp, ci, vp]
+    lib.fgr_stream_read.restype = ci
     _lib = lib
     return lib
 
@@ -242,3 +248,19 @@ def solve_variant(A, B, C, M: int, N: int, K: int, variant: int, stream=None) ->
     b = _address(B, nb, "B")
     c = _address(C, nc, "C")
     _check(lib.fgr_solve_variant(a, b, c, M, N, K, _stream_handle(stream), int(variant)))
+
+
+def set_workspace_limit(nbytes: int) -> int:
+    """Largest workspace one request may take from now on (negative: no
+    limit); plans that would need more run their no-workspace form. Returns
+    the previous limit."""
+    return int(load_library().fgr_set_workspace_limit(int(nbytes)))
+
+
+def stream_read(X, n: int, out, blocks: int, stream=None) -> None:
+    """Measurement hook: read n floats of X once (128-bit loads) on `blocks`
+    workgroups, each writing its sum to out[b]; asynchronous."""
+    lib = load_library()
+    x = _address(X, int(n), "X")
+    o = _address(out, int(blocks), "out")
+    _check(lib.fgr_stream_read(x, int(n), o, int(blocks), _stream_handle(stream)))

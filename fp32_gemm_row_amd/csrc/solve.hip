@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "fp32_gemm_row.h"
@@ -20,10 +21,11 @@
 #include "gemm_valu.hpp"
 #include "gemv.hpp"
 #include "reduce_parts.hpp"
+#include "stream_read.hpp"
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultCus = 256;  // MI355X
 constexpr int kTileGroup = 4;     // tile-rows per group in the workgroup order
@@ -126,7 +128,8 @@ Rows rows_of(const float* A, const float* B, const float* C, int N, int K) {
 // 151.4, 1024 x 6144 x 4095 476.4 -> 426.0, 1024 x 6143 x 4096 469.6 ->
 // 423.7, 2047 x 2051 x 2048 162.4 -> 150.5; tails within 2% (2176 x 1028 x
 // 2047 97.4 -> 100.0). Both operands on 4-byte copies would keep more copies
-// in flight than vmcnt counts.
+// in flight than vmcnt counts, so with neither operand's rows aligned A is
+// first copied into padded rows (pack_a), a workspace of M x lda floats.
 constexpr int64_t kBufferOffsetLimit = int64_t(1) << 31;
 bool ksplit128_ok(const float* A, const float* B, const float* C, int N, int K) {
   switch (rows_of(A, B, C, N, K)) {
@@ -451,23 +454,31 @@ int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStre
   return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
 }
 
-// Work for a reduction split across workgroups: a workspace of parts x M x K
-// floats, the partial products into it, then the parts added into C. The
-// workspace is either the caller's stream's cached one (below), borrowed with
-// the cache lock held until the call's last kernel is enqueued, or a
-// stream-ordered allocation from a per-device pool on the caller's stream,
-// given back with hipFreeAsync on it. Either way calls on different streams
-// never share one.
+// Workspace: device memory a call needs beyond A, B and C. Two kinds: the
+// partial tiles (or rows) of a reduction split across workgroups (parts x M x
+// K floats, or parts x tiles x tile^2 in compact slots), and the padded copy
+// of A of the 128x128 k-split tiles when neither A's nor B's rows are 16-byte
+// aligned (M x lda floats, see pack_a). A workspace is either the caller's
+// stream's cached one (below), borrowed with the cache lock held until the
+// call's last kernel is enqueued, or a stream-ordered allocation from a
+// per-device pool on the caller's stream, given back with hipFreeAsync on it
+// behind the call's last kernel. Either way calls on different streams never
+// share one. A call that cannot get its workspace runs its plan's form
+// without one (same result up to rounding order).
 struct CachedWorkspace;
 
-struct PartsWorkspace {
+struct Workspace {
   float* w = nullptr;
   hipStream_t s = nullptr;
   bool owned = false;                 // allocated for this call
   CachedWorkspace* cached = nullptr;  // or borrowed from the stream's cache entry
   std::unique_lock<std::mutex> cache_lock;
-  ~PartsWorkspace();
+  ~Workspace();
 };
+
+// Largest workspace one request may take, in bytes (fgr_set_workspace_limit;
+// negative: no limit). A larger request fails as a failed allocation does.
+std::atomic<long long> g_ws_limit{-1};
 
 // Freed workspace a device's pool keeps for reuse instead of returning it at
 // each synchronisation (measured on MI355X, 128 x 262144 x 128 with a
@@ -541,7 +552,7 @@ std::mutex g_ws_mu;
 CachedWorkspace g_ws[kCachedStreams];
 int g_ws_used = 0;
 
-PartsWorkspace::~PartsWorkspace() {
+Workspace::~Workspace() {
   if (cached) {
     cached->recorded = hipEventRecord(cached->done, s) == hipSuccess;
     if (!cached->recorded) (void)hipGetLastError();
@@ -550,7 +561,7 @@ PartsWorkspace::~PartsWorkspace() {
   }
 }  // cache_lock, if held, is released after the event is enqueued
 
-bool cached_workspace(PartsWorkspace& ws, size_t bytes, hipStream_t s) {
+bool cached_workspace(Workspace& ws, size_t bytes, hipStream_t s) {
   if (bytes > kCachedMaxBytes || s == hipStreamPerThread) return false;
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   int dev = -1;
@@ -595,9 +606,16 @@ bool cached_workspace(PartsWorkspace& ws, size_t bytes, hipStream_t s) {
   return true;
 }
 
-int alloc_floats(PartsWorkspace& ws, size_t floats, hipStream_t s) {
+// A workspace of `floats` floats for this call on `s`: the stream's cached one
+// when `cacheable` (one per call at a time: the cache lock is held while it is
+// borrowed), else a stream-ordered allocation freed after the call's last
+// kernel. A's padded copy is never cached, so that a call may hold it and a
+// split workspace together.
+int alloc_floats(Workspace& ws, size_t floats, hipStream_t s, bool cacheable = true) {
   const size_t bytes = floats * sizeof(float);
-  if (cached_workspace(ws, bytes, s)) return FGR_OK;
+  const long long limit = g_ws_limit.load(std::memory_order_relaxed);
+  if (limit >= 0 && bytes > (unsigned long long)limit) return FGR_ERR_LAUNCH;  // as a failed allocation
+  if (cacheable && cached_workspace(ws, bytes, s)) return FGR_OK;
   ws.s = s;
   if (pool_alloc(&ws.w, bytes, s) != hipSuccess) {
     ws.w = nullptr;
@@ -761,7 +779,7 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
 
 // k-split configurations by the row alignment of the product: 16-byte copies
 // of A and B with 128-bit stores, of one operand (the other 4-byte), or
-// 4-byte copies of both; 128x128 tiles only in the first form (ksplit128_ok).
+// 4-byte copies of both; 128x128 tiles in the first two forms (ksplit128_ok).
 template <int BM, int BN = BM>
 int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
                        hipStream_t s, int parts, float* W, int first, int compact, int nfull, int lda,
@@ -793,47 +811,54 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
   }
 }
 
-// 128x128 k-split tiles when neither A's nor B's rows are 16-byte aligned: A
-// is first copied into rows of N rounded up to a multiple of 4, zeros in
-// front (pack_rows_kernel), into a stream-ordered allocation of its own on
-// `s`; the aligned-A form then runs over the padded reduction (B's rows
-// before the padding are taken as zeros, not read). Fails with
-// FGR_ERR_LAUNCH if the allocation fails (the caller's rules then never
-// chose this form: see ksplit128_ok).
-int launch_ksplit128_packed(const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
-                            hipStream_t s, int parts, float* W, int first, int compact, int nfull) {
+// A as the k-split kernels read it: the caller's rows (lda = N, pad = 0), or
+// a copy whose rows are N rounded up to a multiple of 4 floats with pad = lda
+// - N zeros in front of each (pack_a). The kernels then run over lda
+// reduction indices; index n is row n - pad of B, and B's rows before 0 (all
+// in the first chunk, which is read through registers) count as zeros and are
+// never read.
+struct AOperand {
+  const float* p;
+  int lda;
+  int pad;
+};
+
+constexpr int kNoWorkspace = 1;  // pack_a: the copy's workspace could not be had
+
+// 128x128 k-split tiles need 16-byte rows of A or of B (ksplit128_ok). When
+// neither has them, A is copied once per call into padded rows
+// (pack_rows_kernel) held in `ws` (M x lda floats) until the call's last
+// kernel is enqueued; the aligned-A form with B's 4-byte copies through buffer
+// loads then reads the copy. Returns FGR_OK with `a` set, kNoWorkspace with
+// nothing enqueued when the workspace cannot be had (the caller then takes
+// 64x64 tiles, which need no copy), or a launch error.
+int pack_a(Workspace& ws, AOperand& a, const float* A, int M, int N, hipStream_t s) {
   int lda = (N + 3) & ~3;
-  const int pad = lda - N;
-  float* Ap = nullptr;
-  if (pool_alloc(&Ap, (size_t)M * (size_t)lda * sizeof(float), s) != hipSuccess) {
-    (void)hipGetLastError();
-    return FGR_ERR_LAUNCH;
-  }
+  if (alloc_floats(ws, (size_t)M * (size_t)lda, s, /*cacheable=*/false) != FGR_OK) return kNoWorkspace;
+  float* Ap = ws.w;
   int m = M, n = N;
   void* args[] = {&A, &Ap, &m, &n, &lda};
-  int rc = launch(reinterpret_cast<const void*>(&fgr::pack_rows_kernel), cdiv((int64_t)M * (lda / 4), 256), 256,
-                  args, s);
-  if (rc == FGR_OK)
-    rc = launch_ksplit_rows<128>(Rows::kAOnly, Ap, B, C, M, lda, K, count, s, parts, W, first, compact, nfull, lda,
-                                 pad);
-  (void)hipFreeAsync(Ap, s);
-  return rc;
+  const int rc = launch(reinterpret_cast<const void*>(&fgr::pack_rows_kernel), cdiv((int64_t)M * (lda / 4), 256),
+                        256, args, s);
+  if (rc != FGR_OK) return rc;
+  a = {Ap, lda, lda - N};
+  return FGR_OK;
 }
 
 // The k-split kernel with tile x tile tiles over tiles [first, first + count)
-// of the grouped order (count < 0: all of them); 16-byte copies of each
-// operand whose rows allow them. parts > 1: each tile's reduction also split
-// over `parts` workgroups writing partial tiles to W (at their place in
-// copies of C, or in compact per-tile slots). nfull > 0: the same grid first
-// runs whole tiles [first, first + nfull) into C, and the count split tiles
-// follow them.
-int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
+// of the grouped order (count < 0: all of them), reading A as `a` (its lda
+// reduction indices); 16-byte copies of each operand whose rows allow them.
+// parts > 1: each tile's reduction also split over `parts` workgroups writing
+// partial tiles to W (at their place in copies of C, or in compact per-tile
+// slots). nfull > 0: the same grid first runs whole tiles [first, first +
+// nfull) into C, and the count split tiles follow them.
+int launch_ksplit(int tile, const AOperand& a, const float* B, float* C, int M, int K, int64_t count,
                   hipStream_t s, int parts = 1, float* W = nullptr, int first = 0, int compact = 0,
-                  int nfull = 0, int lda = -1, int pad = 0) {
-  if (lda < 0) lda = N;
-  const Rows rows = rows_of(A, B, C, lda, K);
-  if (tile == FGR_TILE_128 && rows == Rows::kNone) return launch_ksplit128_packed(A, B, C, M, N, K, count, s, parts,
-                                                                                   W, first, compact, nfull);
+                  int nfull = 0) {
+  const Rows rows = rows_of(a.p, B, C, a.lda, K);
+  const float* A = a.p;
+  const int N = a.lda, lda = a.lda, pad = a.pad;
+  if (tile == FGR_TILE_128 && rows == Rows::kNone) return FGR_ERR_BAD_PATH;  // pack_a first
   switch (tile) {
     case FGR_TILE_128:
       return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
@@ -873,14 +898,14 @@ bool vec4_rows(const float* C, int M, int K) { return ((int64_t)M * K) % 4 == 0 
 // tiles into a stream-ordered workspace, then added in part order (two parts
 // where no longer parts fit the estimate's limits). Without a
 // workspace (allocation failed) the tiles keep their whole reduction.
-int launch_ksplit_parts(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
+int launch_ksplit_parts(int tile, const AOperand& a, const float* B, float* C, int M, int N, int K, int cus,
                         hipStream_t s) {
   int parts = tile == FGR_TILE_32X128 ? skinny_parts(M, N, K, cus) : splitk_plan_tile(tile, M, N, K, cus).parts;
   if (parts < 2) parts = 2;  // N >= 128 gives 8 chunks per part
-  PartsWorkspace ws;
+  Workspace ws;
   if (alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) != FGR_OK)
-    return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
-  const int rc = launch_ksplit(tile, A, B, C, M, N, K, -1, s, parts, ws.w);
+    return launch_ksplit(tile, a, B, C, M, K, -1, s);
+  const int rc = launch_ksplit(tile, a, B, C, M, K, -1, s, parts, ws.w);
   if (rc != FGR_OK) return rc;
   return launch_reduce_parts(ws.w, C, M, K, parts, vec4_rows(C, M, K), s);
 }
@@ -891,8 +916,8 @@ constexpr int kMixedTailMinN = 1024;
 // Whole waves of tile x tile tiles on the k-split kernel, the last partial
 // wave's tiles cut into smaller split-reduction tiles (as launch_dma_tail) or,
 // for long reductions, their reduction split across workgroups.
-int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
-                       hipStream_t s) {
+int launch_ksplit_tail(int tile, const float* A, const AOperand& a, const float* B, float* C, int M, int N, int K,
+                       int cus, hipStream_t s) {
   const int64_t tiles = cdiv(M, tile) * cdiv(K, tile);
   const int64_t full = tiles / cus * cus;
   const int64_t rem = tiles - full;
@@ -908,15 +933,15 @@ int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M
   // 19.4 vs 21.7).
   const int mixed_parts = (int)std::min<int64_t>(cus / std::max<int64_t>(rem, 1), cdiv(N, 8) / 8);
   if (tile == FGR_TILE_64 && N >= kMixedTailMinN && full > 0 && rem > 0 && mixed_parts >= 2) {
-    PartsWorkspace ws;
+    Workspace ws;
     if (alloc_floats(ws, (size_t)mixed_parts * (size_t)rem * tile * tile, s) == FGR_OK) {
-      const int rc = launch_ksplit(tile, A, B, C, M, N, K, rem, s, mixed_parts, ws.w, 0, 1, (int)full);
+      const int rc = launch_ksplit(tile, a, B, C, M, K, rem, s, mixed_parts, ws.w, 0, 1, (int)full);
       if (rc != FGR_OK) return rc;
       return launch_reduce_tiles(ws.w, C, M, K, tile, mixed_parts, (int)full, (int)rem, s);
     }
   }
   if (full > 0) {
-    const int rc = launch_ksplit(tile, A, B, C, M, N, K, full, s);
+    const int rc = launch_ksplit(tile, a, B, C, M, K, full, s);
     if (rc != FGR_OK || rem == 0) return rc;
   }
   // With a long reduction the tail tiles' reduction is split over up to
@@ -928,9 +953,9 @@ int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M
   // 45 vs 48 (three launches and the workspace cost more than they save).
   const int parts = N >= kTailSplitMinN ? (int)std::min<int64_t>(cus / rem, cdiv(N, 8) / 8) : 1;
   if (parts >= 2 && rem <= 65535) {
-    PartsWorkspace ws;
+    Workspace ws;
     if (alloc_floats(ws, (size_t)parts * (size_t)rem * tile * tile, s) == FGR_OK) {
-      const int rc = launch_ksplit(tile, A, B, C, M, N, K, rem, s, parts, ws.w, (int)full, 1);
+      const int rc = launch_ksplit(tile, a, B, C, M, K, rem, s, parts, ws.w, (int)full, 1);
       if (rc != FGR_OK) return rc;
       return launch_reduce_tiles(ws.w, C, M, K, tile, parts, (int)full, (int)rem, s);
     }
@@ -991,7 +1016,7 @@ int launch_gemv_parts(const float* A, const float* B, float* C, int M, int N, in
 template <int VW>
 int launch_gemv(const float* A, const float* B, float* C, int M, int N, int K, int cus, hipStream_t s) {
   const GemvPlan plan = gemv_plan(M, N, K, cus);
-  PartsWorkspace ws;
+  Workspace ws;
   float* W = nullptr;
   if (plan.parts >= 2 && alloc_floats(ws, (size_t)plan.parts * (size_t)M * (size_t)K, s) == FGR_OK) W = ws.w;
   const int p = W ? plan.parts : 1;
@@ -1017,13 +1042,15 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
-      // N >= 64; tiles of 128 (16-byte rows of A or B) or 64, and 32 or 32x128 without the tail form
+      // N >= 64; tiles of 128 (with neither A's nor B's rows 16-byte aligned, A is first copied
+      // into padded rows: pack_a) or 64, and 32 or 32x128 without the tail form
       if (N < 64 || (tile == FGR_TILE_128 && !ksplit128_ok(A, B, C, N, K)) || tile == FGR_TILE_256 ||
           ((tile == FGR_TILE_32 || tile == FGR_TILE_32X128) && path == FGR_PATH_MFMA_KSPLIT_TAIL))
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SPLITK:
-      // N >= 128 (two parts of at least 8 chunks); tiles of 128 (16-byte rows of A or B), 64 or 32
+      // N >= 128 (two parts of at least 8 chunks); tiles of 128 (A copied as above when needed), 64
+      // or 32
       if (N < 128 || (tile == FGR_TILE_128 && !ksplit128_ok(A, B, C, N, K)) || tile == FGR_TILE_256)
         return FGR_ERR_BAD_PATH;
       break;
@@ -1080,8 +1107,20 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   switch (path) {
     case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, -1, s);
     case FGR_PATH_MFMA_DMA_TAIL: return launch_dma_tail(A, B, C, M, N, K, cus, s);
-    case FGR_PATH_MFMA_KSPLIT: return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
-    case FGR_PATH_MFMA_KSPLIT_TAIL: return launch_ksplit_tail(tile, A, B, C, M, N, K, cus, s);
+    case FGR_PATH_MFMA_KSPLIT:
+    case FGR_PATH_MFMA_KSPLIT_TAIL:
+    case FGR_PATH_MFMA_SPLITK: {
+      AOperand a{A, N, 0};
+      Workspace packed;  // A's padded copy, when 128x128 tiles need one
+      if (tile == FGR_TILE_128 && rows_of(A, B, C, N, K) == Rows::kNone) {
+        const int prc = pack_a(packed, a, A, M, N, s);
+        if (prc == kNoWorkspace) tile = FGR_TILE_64;  // no copy: 64x64 tiles with 4-byte copies
+        else if (prc != FGR_OK) return prc;
+      }
+      if (path == FGR_PATH_MFMA_KSPLIT) return launch_ksplit(tile, a, B, C, M, K, -1, s);
+      if (path == FGR_PATH_MFMA_KSPLIT_TAIL) return launch_ksplit_tail(tile, A, a, B, C, M, N, K, cus, s);
+      return launch_ksplit_parts(tile, a, B, C, M, N, K, cus, s);
+    }
     case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SPLIT:
@@ -1089,7 +1128,6 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
                                         : launch_split_tile<false>(tile, A, B, C, M, N, K, cus, s);
     case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, M, N, K, cus, s);
     case FGR_PATH_GEMV_SCALAR: return launch_gemv<1>(A, B, C, M, N, K, cus, s);
-    case FGR_PATH_MFMA_SPLITK: return launch_ksplit_parts(tile, A, B, C, M, N, K, cus, s);
     case FGR_PATH_VALU:
       return mfma_vec_ok(A, B, C, N, K) ? launch_valu<true>(A, B, C, M, N, K, s)
                                         : launch_valu<false>(A, B, C, M, N, K, s);
@@ -1197,6 +1235,25 @@ const char* fgr_status_string(int status) {
 }
 
 int fgr_version(void) { return kVersion; }
+
+int fgr_stream_read(const float* X, long long n, float* out, int blocks, void* stream) {
+  if (!X || !out) return FGR_ERR_NULL_POINTER;
+  if (n < 4 || n % 4 != 0 || blocks < 1) return FGR_ERR_BAD_DIMS;
+  if (!aligned(X, 16) || !aligned(out, 4)) return FGR_ERR_MISALIGNED;
+  if (overlaps(out, blocks, X, n)) return FGR_ERR_ALIAS;
+  int cus = 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int rc = device_for(s, &cus);
+  if (rc != FGR_OK) return rc;
+  const float4* X4 = reinterpret_cast<const float4*>(X);
+  int64_t n4 = n / 4;
+  void* args[] = {&X4, &n4, &out};
+  return launch(reinterpret_cast<const void*>(&fgr::stream_read_kernel), blocks, fgr::kStreamThreads, args, s);
+}
+
+long long fgr_set_workspace_limit(long long bytes) {
+  return g_ws_limit.exchange(bytes < 0 ? -1 : bytes, std::memory_order_relaxed);
+}
 
 int fgr_variant_count(void) { return kNumVariants; }
 

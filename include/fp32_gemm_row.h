@@ -22,14 +22,17 @@
  *
  * Memory and ownership
  *   A, B and C are DEVICE pointers owned by the caller. The library never
- *   synchronises. It keeps a per-device cache of device properties and, for
- *   the paths that split a reduction across workgroups, a workspace (see
- *   solve() below); nothing else is allocated. C is overwritten
- *   (every one of its M*K elements is written once; its prior contents,
- *   even NaN, are ignored - the write-back rule of the CUDA study notes,
- *   section 3, and "the result must be stored in C" of the LeetGPU
- *   requirements). A and B are only read and may alias each other; C must
- *   not overlap A or B.
+ *   synchronises. It keeps a per-device cache of device properties, and some
+ *   plans need device memory beyond A, B and C, called workspace here (see
+ *   solve() below for sizes and where it comes from): the partial results of
+ *   a reduction split across workgroups (paths MFMA_SPLITK, MFMA_KSPLIT_TAIL
+ *   and the matrix-vector paths), and, for 128 x 128 k-split tiles when
+ *   neither A's nor B's rows are 16-byte aligned, a copy of A with padded
+ *   rows. Nothing else is allocated. C is overwritten (every one of its M*K
+ *   elements is written once; its prior contents, even NaN, are ignored: the
+ *   output goes to C, as the LeetGPU problem's "Implementation Requirements"
+ *   and the write-back rule of the CUDA study notes, section 3, have it). A
+ *   and B are only read and may alias each other; C must not overlap A or B.
  *
  * Streams
  *   `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
@@ -50,8 +53,10 @@
  *   for the device take 128 x 128 tiles whose reduction is split over the
  *   four waves of a workgroup, or smaller tiles split the same way;
  *   when a last, partial wave of 256 x 256 tiles is left, its tiles are cut
- *   into small split-reduction tiles. M <= 8 takes the bandwidth-bound
- *   matrix-vector path, which streams B once for all rows of A.
+ *   into small split-reduction tiles. M <= 4 takes the bandwidth-bound
+ *   matrix-vector path, which streams B once for all rows of A, and so do
+ *   5 <= M <= 8 unless N >= 64 and K >= 128 (then 32 x 128 k-split tiles or
+ *   the split plans of few-tile shapes serve them).
  *
  * Errors
  *   Every entry point returns 0 (FGR_OK) on success or a negative FGR_ERR_*
@@ -88,7 +93,7 @@ extern "C" {
 #define FGR_PATH_MFMA_VEC 1    /* FP32 MFMA, 128-bit loads; needs N%4 == K%4 == 0 and 16-B aligned pointers */
 #define FGR_PATH_MFMA_SCALAR 2 /* FP32 MFMA, 32-bit loads; any shape and 4-B alignment */
 #define FGR_PATH_GEMV_VEC 3    /* matrix-vector and skinny (M <= 8), 128-bit loads of B; needs K%4 == 0
-                                  and 16-B aligned B, C */
+                                  and a 16-B aligned B */
 #define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector and skinny (M <= 8), 32-bit loads */
 #define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, 256x256 tiles fed by direct global->LDS copies;
                                   needs the MFMA_VEC conditions and N >= 64 (tile 256 only) */
@@ -102,10 +107,16 @@ extern "C" {
 #define FGR_PATH_MFMA_KSPLIT 8 /* FP32 MFMA, 128x128, 64x64 or 32x32 tiles, each of a workgroup's four
                                   waves reducing a quarter of N into the whole tile from its own
                                   direct global->LDS copies (4-byte copies for rows that are not
-                                  16-byte aligned; tile 128 needs 16-byte rows); N >= 64 */
-#define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT (tile 128 or 64) on the whole waves of tiles, the
-                                       split kernel on the tiles of the last, partial wave; two
-                                       launches */
+                                  16-byte aligned; tile 128 with neither A's nor B's rows 16-byte
+                                  aligned first copies A into padded rows, a workspace of its
+                                  own, and takes tile 64 if that cannot be had); N >= 64 */
+#define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT (tile 128 or 64) on the whole waves of tiles; the
+                                       tiles of the last, partial wave either with their reduction
+                                       split over workgroups through a workspace (N >= 4096, or
+                                       N >= 1024 at tile 64, which then runs in the same grid as
+                                       the whole tiles) and a second kernel adding the parts, or
+                                       cut into tiles of the split kernel (also when the workspace
+                                       cannot be had); two or three launches */
 #define FGR_PATH_MFMA_SPLITK 10 /* MFMA_KSPLIT (tile 128, 64 or 32) with each tile's reduction also
                                    split into P parts over P workgroups, which write partial tiles
                                    to a workspace of P*M*K floats; a second kernel adds the parts
@@ -135,29 +146,38 @@ extern "C" {
  *   M,N,K  dimensions, each >= 1; N is the reduction length
  *   stream hipStream_t as void*, NULL for the null stream
  * Returns FGR_OK or an FGR_ERR_* code (see above). Asynchronous.
- * Workspace: when the output has too few tiles (or, for M <= 8, too few
- * 32-column blocks) to give every CU a workgroup and N is long, the reduction
- * is split into P parts across workgroups (paths MFMA_SPLITK and GEMV_*): the
- * library then needs a workspace of P*M*K floats (when solve() picks the
- * split, P * tiles <= 4 * CUs: on a 256-CU device at most 16 MiB with 64 x 64
- * or smaller tiles, 64 MiB with 128 x 128 tiles; a forced MFMA_SPLITK on a large
- * output takes P = 2, i.e. 2*M*K floats). Calls on different streams never
- * share one. Each stream (up to 16 per process, identified by handle and
- * stream id) keeps its workspace between calls, up to 64 MiB: it is
- * allocated stream-ordered on `stream` at the stream's first split call,
- * replaced (the old one freed with hipFreeAsync on `stream`) when a call
- * needs more, and otherwise held until the process ends. Calls from several
- * host threads on one stream are serialised while they enqueue. Otherwise
- * (more streams, larger workspaces, hipStreamPerThread, or `stream` under
- * capture) the call allocates its workspace stream-ordered on `stream` and
- * frees it with hipFreeAsync after its last kernel. Allocations come from a
- * memory pool the library creates per device on first use (hipMemPoolCreate;
- * it keeps up to 64 MiB of freed memory for reuse and lives until the process
- * ends), or from the device's default pool if that creation failed. If the
- * allocation fails the unsplit kernel runs instead (same result up to
- * rounding order). Results are deterministic: the parts are added in a fixed
- * order. solve() can be captured into a HIP graph (stream capture on
- * `stream`); the split paths' workspace then becomes a graph allocation.
+ * Workspace (device memory beyond A, B and C), by plan:
+ *   - a reduction split into P parts across workgroups (MFMA_SPLITK: P*M*K
+ *     floats; the matrix-vector paths when their plan splits: P*M*K floats;
+ *     the last partial wave of MFMA_KSPLIT_TAIL: P*tiles*tile^2 floats). When
+ *     solve() picks the split, P * tiles <= 4 * CUs: on a 256-CU device at most
+ *     16 MiB with 64 x 64 or smaller tiles, 64 MiB with 128 x 128 tiles. A
+ *     forced MFMA_SPLITK on a large output takes P = 2, i.e. 2*M*K floats.
+ *   - 128 x 128 k-split tiles (MFMA_KSPLIT, MFMA_KSPLIT_TAIL, MFMA_SPLITK)
+ *     when neither A's nor B's rows are 16-byte aligned: a copy of A with rows
+ *     of N rounded up to a multiple of 4, M * that floats (e.g. 4095 x 8191 x
+ *     2047: 134 MB), made by a first kernel once per call.
+ * Each stream (up to 16 per process, identified by its handle and device)
+ * keeps one split workspace between calls, up to 64 MiB: it is allocated
+ * stream-ordered on `stream` at the stream's first split call, replaced (the
+ * old one freed with hipFreeAsync on `stream`) when a call needs more, and
+ * otherwise held until the process ends; a stream created after another was
+ * destroyed may inherit its handle and so its entry, whose buffer it uses only
+ * after the old stream's last use of it. Calls from several host threads on one
+ * stream are serialised while they enqueue. Every other workspace (A's copy,
+ * more streams, larger workspaces, hipStreamPerThread, or `stream` under
+ * capture) is allocated stream-ordered on `stream` for the call and freed
+ * with hipFreeAsync after its last kernel. Allocations come from a memory
+ * pool the library creates per device on first use (hipMemPoolCreate; it
+ * keeps up to 64 MiB of freed memory for reuse and lives until the process
+ * ends), or from the device's default pool if that creation failed. If an
+ * allocation fails, or would exceed fgr_set_workspace_limit(), the plan runs
+ * without that workspace: the unsplit kernel instead of a split, the split
+ * kernel for a last partial wave, 64 x 64 tiles instead of 128 x 128 ones
+ * over A's copy (same result up to rounding order); no error is returned for
+ * it. Results are deterministic: the parts are added in a fixed order.
+ * solve() can be captured into a HIP graph (stream capture on `stream`); the
+ * workspace then becomes a graph allocation.
  * The LeetGPU signature (section "Problem Description", and every "Solution"
  * of the write-up) is solve(A, B, C, M, N, K) returning void; this form adds
  * the stream and a status.
@@ -200,6 +220,33 @@ const char *fgr_status_string(int status);
 
 /* fgr_version - library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int fgr_version(void);
+
+/*
+ * fgr_set_workspace_limit - the largest workspace, in bytes, that one request
+ * of a call may take from now on (process-wide; negative: no limit, the
+ * default). A plan whose workspace would exceed it runs without that
+ * workspace, as when an allocation fails (see solve()). For callers short of
+ * device memory, and for tests of those no-workspace forms (a limit of 0
+ * takes every one of them). Returns the previous limit. Host only; calls
+ * already enqueued are not affected.
+ */
+long long fgr_set_workspace_limit(long long bytes);
+
+/*
+ * fgr_stream_read - a measurement hook, not part of the product: reads every
+ * float of X (n floats, device memory, 16-byte aligned, n a multiple of 4,
+ * n >= 4) once with 128-bit loads on `blocks` workgroups of 256 threads
+ * (grid-stride), and writes each workgroup's sum to out[0 .. blocks-1]
+ * (device memory, caller-owned, overwritten; must not overlap X). Timed over a
+ * buffer several times the last-level cache, it gives the device's practical
+ * streaming-read rate, the ceiling the matrix-vector path is judged against
+ * beside the datasheet's HBM peak (the byte bound of the study notes "CUDA 学习笔记
+ * Matrix Multiplication", section 2). Errors as solve(): FGR_ERR_NULL_POINTER,
+ * FGR_ERR_BAD_DIMS (n or blocks out of range), FGR_ERR_MISALIGNED,
+ * FGR_ERR_ALIAS, FGR_ERR_DEVICE, FGR_ERR_LAUNCH. Asynchronous; allocates
+ * nothing.
+ */
+int fgr_stream_read(const float *X, long long n, float *out, int blocks, void *stream);
 
 /*
  * The controlled comparison (the LeetGPU write-up, section "Controlled

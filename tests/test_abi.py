@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "fp32_gemm_row.h")
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?(?:\w+[\s*]+)+(\w+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
@@ -67,7 +67,7 @@ def test_controlled_comparison_variants(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fgr.version() == 100
+    assert fgr.version() == 200
     assert fgr.status_string(fgr.OK) == "ok"
     for code in range(-7, 0):
         s = fgr.status_string(code)
@@ -332,3 +332,28 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(fgr, "_lib", None)
     with pytest.raises(ImportError):
         fgr.load_library(str(tmp_path / "nope.so"))
+
+
+def test_matrix_vector_rows_as_documented():
+    # the header's rule: M <= 4 always takes the matrix-vector path; 5 <= M <= 8
+    # too, unless N >= 64 and K >= 128 (then the k-split or split plans)
+    sp = fgr.select_path
+    a, b, c = 1 << 40, 2 << 40, 3 << 40
+    gemv = (fgr.PATH_GEMV_VEC, fgr.PATH_GEMV_SCALAR)
+    for M in range(1, 9):
+        for N in (1, 17, 63, 64, 1000, 8192, 65536):
+            for K in (1, 7, 64, 127, 128, 1000, 8192):
+                p = sp(a, b, c, M, N, K)
+                if M <= 4 or N < 64 or K < 128:
+                    assert p in gemv, (M, N, K, p)
+                else:
+                    assert p not in gemv, (M, N, K, p)
+    assert sp(a, b, c, 9, 8192, 64) not in gemv
+
+
+def test_workspace_limit_round_trip(lib):
+    # host only: the previous limit comes back; negative values mean no limit
+    assert fgr.set_workspace_limit(0) == -1
+    assert fgr.set_workspace_limit(1 << 20) == 0
+    assert fgr.set_workspace_limit(-5) == 1 << 20
+    assert fgr.set_workspace_limit(-1) == -1
