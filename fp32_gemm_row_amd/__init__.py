@@ -29,6 +29,7 @@ ERR_ALIAS = -4
 ERR_BAD_PATH = -5
 ERR_DEVICE = -6
 ERR_LAUNCH = -7
+ERR_SCRATCH = -8
 
 PATH_AUTO = 0
 PATH_MFMA_VEC = 1
@@ -77,6 +78,7 @@ EXPORTS = (
     "fgr_solve_variant",
     "fgr_set_workspace_limit",
     "fgr_stream_read",
+    "fgr_solve_noalloc",
 )
 
 
@@ -125,6 +127,8 @@ def load_library(path: str = LIB_PATH):
     lib.fgr_set_workspace_limit.restype = ctypes.c_longlong
     lib.fgr_stream_read.argtypes = [vp, ctypes.c_longlong, vp, ci, vp]
     lib.fgr_stream_read.restype = ci
+    lib.fgr_solve_noalloc.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+    lib.fgr_solve_noalloc.restype = ci
     _lib = lib
     return lib
 
@@ -204,6 +208,18 @@ def solve(A, B, C, M: int, N: int, K: int, stream=None) -> None:
     b = _address(B, nb, "B")
     c = _address(C, nc, "C")
     _check(lib.solve(a, b, c, M, N, K, _stream_handle(stream)))
+
+
+def solve_noalloc(A, B, C, M: int, N: int, K: int, stream=None) -> None:
+    """solve() with any workspace taken from the library's static 64 MiB device
+    scratch (no allocation); raises GemmError(ERR_SCRATCH) if the plan needs
+    more. Calls that overlap on one GPU race on that scratch."""
+    lib = load_library()
+    M, N, K, na, nb, nc = _dims(M, N, K)
+    a = _address(A, na, "A")
+    b = _address(B, nb, "B")
+    c = _address(C, nc, "C")
+    _check(lib.fgr_solve_noalloc(a, b, c, M, N, K, _stream_handle(stream)))
 
 
 def solve_path(A, B, C, M: int, N: int, K: int, path: int, tile: int = TILE_AUTO, stream=None) -> None:

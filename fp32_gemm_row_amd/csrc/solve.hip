@@ -36,6 +36,8 @@ struct DeviceInfo {
   int cus = 0;
   bool pool_tried = false;
   hipMemPool_t pool = nullptr;  // the split-reduction workspace pool, made on first use
+  bool scratch_tried = false;
+  char* scratch = nullptr;  // device address of this device's copy of `scratch` (fgr_solve_noalloc)
 };
 
 std::mutex g_dev_mu;
@@ -66,9 +68,10 @@ int current_device(int* cus, int* dev_out = nullptr) {
 // that `stream` (other than the null and per-thread streams, which follow
 // the current device) belongs to it: the kernels run on the stream's device,
 // while the CU count and the split workspace come from the current one.
-int device_for(hipStream_t stream, int* cus) {
+int device_for(hipStream_t stream, int* cus, int* dev_out = nullptr) {
   int dev = -1;
   const int rc = current_device(cus, &dev);
+  if (dev_out) *dev_out = dev;
   if (rc != FGR_OK) return rc;
   if (stream && stream != hipStreamPerThread) {
     int sdev = -1;
@@ -447,8 +450,49 @@ int default_tile(int path, const Choice& auto_choice, int M, int N, int K, int c
   }
 }
 
+// Scratch of fgr_solve_noalloc, for callers that cannot allocate: every
+// workspace of such a call is carved from this array instead (256-byte aligned
+// pieces). Each device holds its own copy, at its own address, until the
+// process ends. In host code the name is a host-side stand-in, never a device
+// address: the device address comes from hipGetSymbolAddress, once per device
+// with that device current (scratch_of), and only that address is passed to
+// kernels. Nothing in it needs to start at zero: every piece is written in full
+// by one kernel of the call before another reads it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's `scratch` (dev is current).
+int scratch_of(int dev, char** out) {
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.scratch_tried) {
+    d.scratch_tried = true;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p) d.scratch = static_cast<char*>(p);
+    else (void)hipGetLastError();
+  }
+  if (!d.scratch) return FGR_ERR_DEVICE;
+  *out = d.scratch;
+  return FGR_OK;
+}
+
+// One fgr_solve_noalloc call, on the calling thread (t_scratch points at it
+// for the call's duration). Its launch sequence runs twice: a dry pass that
+// launches nothing and makes no HIP call, only adding up the workspace the
+// plan takes, then, if that fits the array, the real pass over the same plan.
+struct ScratchCall {
+  bool dry = true;
+  char* base = nullptr;  // the device's array (real pass)
+  size_t used = 0;       // bytes handed out so far
+};
+thread_local ScratchCall* t_scratch = nullptr;
+// Stand-in base of the dry pass's pieces: never dereferenced (nothing is
+// launched), 256-byte aligned like the array so that alignment tests agree.
+constexpr uintptr_t kDryBase = uintptr_t(1) << 32;
+
 int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStream_t stream, int rows = 1) {
   if (blocks < 1 || blocks > INT_MAX || rows < 1 || rows > 65535) return FGR_ERR_BAD_DIMS;
+  if (t_scratch && t_scratch->dry) return FGR_OK;  // counting a scratch call's workspace
   const hipError_t e =
       hipLaunchKernel(kernel, dim3((unsigned)blocks, (unsigned)rows), dim3(threads), args, 0, stream);
   return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
@@ -613,6 +657,15 @@ bool cached_workspace(Workspace& ws, size_t bytes, hipStream_t s) {
 // split workspace together.
 int alloc_floats(Workspace& ws, size_t floats, hipStream_t s, bool cacheable = true) {
   const size_t bytes = floats * sizeof(float);
+  if (t_scratch) {  // fgr_solve_noalloc: a piece of the scratch array
+    ScratchCall& sc = *t_scratch;
+    const size_t off = (sc.used + 255) & ~size_t(255);
+    if (!sc.dry && off + bytes > kScratchBytes) return FGR_ERR_SCRATCH;  // the dry pass rules this out
+    sc.used = off + bytes;
+    ws.w = reinterpret_cast<float*>(sc.dry ? kDryBase + off : reinterpret_cast<uintptr_t>(sc.base) + off);
+    ws.s = s;
+    return FGR_OK;
+  }
   const long long limit = g_ws_limit.load(std::memory_order_relaxed);
   if (limit >= 0 && bytes > (unsigned long long)limit) return FGR_ERR_LAUNCH;  // as a failed allocation
   if (cacheable && cached_workspace(ws, bytes, s)) return FGR_OK;
@@ -1027,8 +1080,11 @@ int launch_gemv(const float* A, const float* B, float* C, int M, int N, int K, i
   return launch_reduce_parts(W, C, M, K, p, vec4_rows(C, M, K), s);
 }
 
+int dispatch(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s, int cus, int path,
+             int tile);
+
 int run(const float* A, const float* B, float* C, int M, int N, int K, void* stream, int path,
-        int tile) {
+        int tile, bool noalloc = false) {
   int rc = check_args(A, B, C, M, N, K);
   if (rc != FGR_OK) return rc;
   switch (path) {
@@ -1079,9 +1135,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       path != FGR_PATH_MFMA_SPLITK && path != FGR_PATH_AUTO)
     return FGR_ERR_BAD_PATH;
 
-  int cus = 0;
+  int cus = 0, dev = -1;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  rc = device_for(s, &cus);
+  rc = device_for(s, &cus, &dev);
   if (rc != FGR_OK) return rc;
   const Choice best = choose(A, B, C, M, N, K, cus);
   if (path == FGR_PATH_AUTO) {
@@ -1103,7 +1159,27 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     }
   }
   if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, N, K, cus, mfma_vec_ok(A, B, C, N, K));
+  if (!noalloc) return dispatch(A, B, C, M, N, K, s, cus, path, tile);
 
+  // fgr_solve_noalloc: the same plan, its workspace from the scratch array
+  char* base = nullptr;
+  rc = scratch_of(dev, &base);
+  if (rc != FGR_OK) return rc;
+  ScratchCall call;
+  struct Reset {
+    ~Reset() { t_scratch = nullptr; }
+  } reset;
+  t_scratch = &call;
+  rc = dispatch(A, B, C, M, N, K, s, cus, path, tile);  // dry: count the bytes
+  if (rc != FGR_OK) return rc;
+  if (call.used > kScratchBytes) return FGR_ERR_SCRATCH;  // nothing enqueued
+  call = ScratchCall{false, base, 0};
+  return dispatch(A, B, C, M, N, K, s, cus, path, tile);
+}
+
+// The launches of one call's plan (path and tile resolved).
+int dispatch(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s, int cus, int path,
+             int tile) {
   switch (path) {
     case FGR_PATH_MFMA_DMA: return launch_mfma_dma(A, B, C, M, N, K, -1, s);
     case FGR_PATH_MFMA_DMA_TAIL: return launch_dma_tail(A, B, C, M, N, K, cus, s);
@@ -1199,6 +1275,10 @@ int solve(const float* A, const float* B, float* C, int M, int N, int K, void* s
   return run(A, B, C, M, N, K, stream, FGR_PATH_AUTO, FGR_TILE_AUTO);
 }
 
+int fgr_solve_noalloc(const float* A, const float* B, float* C, int M, int N, int K, void* stream) {
+  return run(A, B, C, M, N, K, stream, FGR_PATH_AUTO, FGR_TILE_AUTO, /*noalloc=*/true);
+}
+
 int fgr_solve_default(const float* A, const float* B, float* C, int M, int N, int K) {
   return run(A, B, C, M, N, K, nullptr, FGR_PATH_AUTO, FGR_TILE_AUTO);
 }
@@ -1230,6 +1310,7 @@ const char* fgr_status_string(int status) {
     case FGR_ERR_BAD_PATH: return "forced path or tile cannot run these arguments";
     case FGR_ERR_DEVICE: return "no gfx950 HIP device is current";
     case FGR_ERR_LAUNCH: return "HIP kernel launch failed";
+    case FGR_ERR_SCRATCH: return "the plan needs more workspace than fgr_solve_noalloc's 64 MiB scratch holds";
     default: return "unknown status";
   }
 }

@@ -87,6 +87,8 @@ extern "C" {
 #define FGR_ERR_DEVICE (-6)       /* no HIP device, the current one is not gfx950, or the
                                      stream belongs to another device */
 #define FGR_ERR_LAUNCH (-7)       /* HIP reported an error at launch */
+#define FGR_ERR_SCRATCH (-8)      /* fgr_solve_noalloc: the plan needs more workspace than its
+                                     scratch array holds; nothing was enqueued */
 
 /* Paths (fgr_select_path / fgr_solve_path). */
 #define FGR_PATH_AUTO 0
@@ -183,6 +185,26 @@ extern "C" {
  * the stream and a status.
  */
 int solve(const float *A, const float *B, float *C, int M, int N, int K, void *stream);
+
+/*
+ * fgr_solve_noalloc - solve() for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, plan, kernels, result (bit for bit), layout and
+ * asynchrony as solve(); the caller still owns A, B and C. Where solve()'s plan
+ * takes a workspace (see solve() above), this call takes it instead from a
+ * static device array of 64 MiB (67108864 bytes) that the library holds on
+ * each GPU it runs on until the process ends, and it calls no allocating
+ * routine (no hipMalloc, hipMallocAsync, hipFree or pool call). If the plan
+ * needs more than 64 MiB of workspace (on a 256-CU device only A's padded
+ * copy can: M * (N rounded up to a multiple of 4) * 4 bytes, for 128 x 128
+ * k-split tiles when neither A's nor B's rows are 16-byte aligned), it returns
+ * FGR_ERR_SCRATCH and enqueues nothing. The array keeps what the last call
+ * left in it; nothing in it needs to start at zero. All such calls on one GPU
+ * share its array: calls that overlap on one GPU (other streams or threads,
+ * before the previous one's kernels have finished) race, so the caller must
+ * order them (for instance on one stream). Other errors as solve().
+ */
+int fgr_solve_noalloc(const float *A, const float *B, float *C, int M, int N, int K, void *stream);
 
 /*
  * fgr_solve_default - the six-argument LeetGPU form: solve(A, B, C, M, N, K, NULL).
