@@ -507,6 +507,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="leetgpu8192")
+    ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"), default=None,
+                    help="time this shape instead of a named workload (uniform [-1,1) inputs, --seed)")
+    ap.add_argument("--seed", type=int, default=9, help="input seed for --shape")
     ap.add_argument("--path", type=int, default=0, help="force an FGR path (0 = auto)")
     ap.add_argument("--tile", type=int, default=0, help="force an MFMA output tile (0 = auto)")
     ap.add_argument("--rotate", type=int, default=0,
@@ -567,7 +570,11 @@ def main() -> int:
         return 2
     fgr.load_library()
 
-    w = synth.WORKLOADS[args.workload]
+    if args.shape:
+        M, N, K = args.shape
+        w = synth.Workload(f"shape{M}x{N}x{K}", M, N, K, "uniform", args.seed)
+    else:
+        w = synth.WORKLOADS[args.workload]
     A, B = synth.workload_inputs(w)
     dev = torch.device("cuda:0")
     dA = torch.from_numpy(A.ravel()).to(dev)
@@ -621,10 +628,10 @@ def main() -> int:
         unit = "TFLOP/s"
         achieved = w.flops / avg_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
-        metric = METRIC if args.workload == "leetgpu8192" else f"FP32 GEMM TFLOP/s at M={w.M},N={w.N},K={w.K}"
+        metric = METRIC if w.name == "leetgpu8192" else f"FP32 GEMM TFLOP/s at M={w.M},N={w.N},K={w.K}"
     roof["frac"] = round(achieved / roof["peak"], 4)
-    roof["traffic"] = recorded_traffic(args.workload)
-    roof["counters"] = recorded_counters(args.workload)
+    roof["traffic"] = recorded_traffic(w.name)
+    roof["counters"] = recorded_counters(w.name)
     roof["batched"] = {
         "launches": batch_launches,
         "ms_per_launch": round(batch_ms, 5),

@@ -51,7 +51,7 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 
 // Workgroups are dispatched round-robin over the XCDs (id % 8). Renumber them
 // so that consecutive logical ids run on the same XCD and share its L2.
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+__host__ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   const int xcd = wg % kNumXcd;
   const int local = wg / kNumXcd;
   const int per = nwg / kNumXcd;
@@ -62,7 +62,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 // Grouped order (the program-id regrouping of the Triton section of the
 // LeetGPU write-up): walk `group` tile-rows at a time, row index fastest, so
 // that neighbouring logical ids share rows of A and columns of B.
-__device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles_n, int group,
+__host__ __device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles_n, int group,
                                              int& tm, int& tn) {
   const int per_group = group * tiles_n;
   const int g = logical / per_group;

@@ -93,7 +93,20 @@ struct DmaConfig {
   static_assert(S * 2 * kStage * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
-__device__ __forceinline__ int a_swizzle(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__host__ __device__ __forceinline__ int a_swizzle(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// Column (inside the 16-deep chunk) of the A element a copy puts at float
+// position pos of an A stage: row pos / 16, stored slot (pos % 16) / 4, which
+// holds quad slot ^ a_swizzle(row).
+__host__ __device__ __forceinline__ int dma_a_col(int pos) {
+  return 4 * (((pos % 16) / 4) ^ a_swizzle(pos / 16)) + pos % 4;
+}
+
+// Float offset, in an A stage, of quad q of row row0 + 32 i (row0's swizzle
+// serves every i: 32 i leaves bits 1-3 of the row unchanged).
+__host__ __device__ __forceinline__ int dma_a_read(int row0, int i, int q) {
+  return (row0 + 32 * i) * 16 + 4 * (q ^ a_swizzle(row0));
+}
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8) that waits until at most `vm` vector-memory operations are
@@ -175,8 +188,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     const int blk = wave * T::kACopies + j;
     const int pos = blk * T::kABlock + lane * T::kACopyFloats;
     const int r = pos / BK;
-    const int q = ((pos % BK) / 4) ^ a_swizzle(r);
-    const int c = 4 * q + pos % 4;
+    const int c = dma_a_col(pos);
     const int row = m0 + r < M ? m0 + r : M - 1;
     a_src[j] = A + (int64_t)row * N + c;
     a_dst[j] = blk * T::kABlock;
@@ -220,7 +232,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // Row of A block i read by this lane, and its swizzle (the same for every
   // block: blocks start at multiples of 32 and the swizzle reads bits 1-3).
   const int a_row0 = wm * T::kWaveM + li;
-  const int a_swz = a_swizzle(a_row0);
   // Output columns inside the wave tile are interleaved across the MFMA
   // column blocks: lane column li of block j is column 4 * li + j, so one
   // lane's B operands for all four blocks are 4 consecutive floats of a row
@@ -228,10 +239,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // product is unchanged; the epilogue writes with the same mapping.
   const int b_frag = 4 * lg * BN + wn * T::kWaveN + 4 * li;
   auto read_frag = [&](Frag& f, const float* As, const float* Bs, int h) __attribute__((always_inline)) {
-    const int q = (2 * h + lg) ^ a_swz;
 #pragma unroll
     for (int i = 0; i < T::kRB; ++i)
-      f.a[i] = *reinterpret_cast<const float4*>(As + (a_row0 + 32 * i) * BK + 4 * q);
+      f.a[i] = *reinterpret_cast<const float4*>(As + dma_a_read(a_row0, i, 2 * h + lg));
     const float* Bh = Bs + b_frag + 8 * h * BN;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {

@@ -100,7 +100,18 @@ struct KsplitConfig {
                 "a partial tile fits in the stage objects of either operand");
 };
 
-__device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+__host__ __device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// Column (inside the 8-deep chunk) of the A element a copy puts at float
+// position pos of a wave's A piece: row pos / 8, stored slot (pos % 8) / 4,
+// which holds quad slot ^ a_swizzle2(row).
+__host__ __device__ __forceinline__ int ksplit_a_col(int pos) {
+  return 4 * (((pos % 8) / 4) ^ a_swizzle2(pos / 8)) + pos % 4;
+}
+
+// Float offset, in a wave's A piece, of quad g of row li (li < 32; rows li +
+// 32 i sit 32 * 8 * i floats further on with the same swizzle).
+__host__ __device__ __forceinline__ int ksplit_a_read(int li, int g) { return li * 8 + 4 * (g ^ a_swizzle2(li)); }
 
 // copy16_to_lds with the LDS destination passed as an opaque wave-uniform
 // integer. The compiler then cannot attribute the copy to one LDS object and
@@ -236,9 +247,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   auto a_row_of = [&](int j) __attribute__((always_inline)) {
     return (j * T::kABlock + lane * T::kACopyFloats) / BK;
   };
+  static_assert(BK == 8, "ksplit_a_col and ksplit_a_read are written for 8-deep chunks");
   auto a_col_of = [&](int j) __attribute__((always_inline)) {
-    const int pos = j * T::kABlock + lane * T::kACopyFloats;
-    return 4 * (((pos % BK) / 4) ^ a_swizzle2(pos / BK)) + pos % 4;
+    return ksplit_a_col(j * T::kABlock + lane * T::kACopyFloats);
   };
   auto a_ptr_of = [&](int j) __attribute__((always_inline)) {
     const int r = a_row_of(j);
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // chain of address steps hides the stage object from the compiler, which
   // then waits for every copy in flight before the read. A: quad lg of row li
   // (+ 32 i), stored at position lg ^ swz(li) (the same swizzle for every i).
-  const int a_frag = piece_a + li * BK + 4 * (lg ^ a_swizzle2(li));
+  const int a_frag = piece_a + ksplit_a_read(li, lg);
   // lane column li of MFMA column block j is output column kCB li + j (see the
   // direct-copy kernel): one read gives a lane's B operands of all blocks
   const int b_frag = piece_b + 4 * lg * BN + T::kCB * li;
