@@ -43,7 +43,9 @@ PATH_MFMA_KSPLIT = 8
 PATH_MFMA_KSPLIT_TAIL = 9
 PATH_MFMA_SPLITK = 10
 PATH_VALU = 11
+PATH_MFMA_STRIP = 12
 PATH_NAMES = {
+    PATH_MFMA_STRIP: "mfma_strip",
     PATH_VALU: "valu",
     PATH_MFMA_SPLITK: "mfma_splitk",
     PATH_MFMA_KSPLIT: "mfma_ksplit",

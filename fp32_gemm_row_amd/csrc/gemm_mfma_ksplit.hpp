@@ -51,6 +51,7 @@
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_dma.hpp"
 #include "gemm_mfma_split.hpp"
+#include "strip.hpp"
 
 namespace fgr {
 
@@ -59,10 +60,14 @@ namespace fgr {
 // 16-byte copies of A / B (their rows 16-byte aligned), else 4-byte copies;
 // VC: 128-bit stores of C (used by the 128 x 128 tile). BUF: the 4-byte
 // copies go through buffer loads (below), which hold a lane's source as two
-// 32-bit offsets instead of one 64-bit address per copy.
-template <int BM_, int S_, bool VA_, int BN_ = BM_, bool VB_ = VA_, bool VC_ = VB_, bool BUF_ = false>
+// 32-bit offsets instead of one 64-bit address per copy. STRIP: the launch
+// also holds, after the tiles' workgroups, workgroups that compute the narrow
+// column strip [tiles_n * BN, K) of C on the vector ALUs (strip.hpp).
+template <int BM_, int S_, bool VA_, int BN_ = BM_, bool VB_ = VA_, bool VC_ = VB_, bool BUF_ = false,
+          bool STRIP_ = false>
 struct KsplitConfig {
   static constexpr int BM = BM_, BN = BN_, BK = 8, S = S_;
+  static constexpr bool kStrip = STRIP_;
   static constexpr bool VA = VA_, VB = VB_, VC = VC_, VEC = VA_ && VB_ && VC_;
   static constexpr bool BUFA = BUF_ && !VA_, BUFB = BUF_ && !VB_;
   // only the form with aligned A and B through buffer loads reads a padded
@@ -94,6 +99,7 @@ struct KsplitConfig {
                 "copies cover whole pieces");
   static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");
   static_assert(!BUFB || BN % 64 == 0, "buffer copies of B cover whole 64-column blocks");
+  static_assert(!STRIP_ || (BM == 64 && BN == 64 && !BUF_), "the strip goes with 64x64 tiles");
   static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
   static_assert(S * (kStageA + kStageB) * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
   static_assert(kSlices <= S * kSlicesPerObjA && kSlices <= S * kSlicesPerObjB,
@@ -189,6 +195,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     else return Bs3;
   };
 
+  // workgroups past the tiles (STRIP): four rows of the column strip each,
+  // staging B's strip in the first A stage object
+  const int gx = T::kStrip ? tiles_m * tiles_n : (int)gridDim.x;
+  if constexpr (T::kStrip) {
+    if ((int)blockIdx.x >= gx) {
+      strip_rows(A, B, C, M, N, K, tiles_n * BN, (int)blockIdx.x - gx, As0, T::kStageA);
+      return;
+    }
+  }
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -213,7 +229,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // instead of running after it. At least 8 chunks per part give every wave
   // >= 2 of the part's chunks (dealt as below).
   const bool whole = (int)blockIdx.x < nfull;
-  const int grid = whole ? nfull : (int)gridDim.x - nfull;
+  const int grid = whole ? nfull : gx - nfull;
   const int logical = xcd_remap(whole ? (int)blockIdx.x : (int)blockIdx.x - nfull, grid);
   const int kparts = whole ? 1 : parts;
   const int ntiles = grid / kparts;

@@ -21,6 +21,7 @@
 #include "gemm_valu.hpp"
 #include "gemv.hpp"
 #include "reduce_parts.hpp"
+#include "strip.hpp"
 #include "stream_read.hpp"
 
 namespace {
@@ -344,6 +345,14 @@ struct Choice {
   int tile;
 };
 
+// The strip plan (launch_strip) applies when K = 64 q + w, 1 <= w <=
+// kStripMax, N >= 64, and the q whole column blocks of 64x64 tiles fit one
+// tile per CU while the w columns would add a partial second wave.
+bool strip_shape(int M, int N, int K) { return N >= 64 && K > 64 && K % 64 >= 1 && K % 64 <= fgr::kStripMax; }
+bool strip_plan_ok(int M, int N, int K, int cus) {
+  return strip_shape(M, N, K) && cdiv(M, 64) * (K / 64) <= cus && cdiv(M, 64) * cdiv(K, 64) > cus;
+}
+
 // Reductions shorter than this (with at least one 64x64 tile per CU) take
 // register-staged 64x64 tiles (128x128 for unaligned rows with many tiles).
 constexpr int kShortReduction = 104;
@@ -402,6 +411,9 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
     }
     if (t64 >= cus) {
+      // a few columns past whole 64-column blocks that give every CU at most
+      // one tile: those columns on the vector ALUs, not a wave of tiles
+      if (strip_plan_ok(M, N, K, cus)) return {FGR_PATH_MFMA_STRIP, FGR_TILE_64};
       const int64_t rem = t64 % cus;
       if (rem != 0 && rem <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_64};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_64};
@@ -441,6 +453,7 @@ int default_tile(int path, const Choice& auto_choice, int M, int N, int K, int c
       return vec_rows && cdiv(M, 128) * cdiv(K, 128) < cus ? FGR_TILE_128 : FGR_TILE_64;
     case FGR_PATH_MFMA_SPLIT: return cdiv(M, 64) * cdiv(K, 64) < cus ? FGR_TILE_32 : FGR_TILE_64;
     case FGR_PATH_VALU: return FGR_TILE_128;
+    case FGR_PATH_MFMA_STRIP: return FGR_TILE_64;
     case FGR_PATH_MFMA_VEC:
     case FGR_PATH_MFMA_SCALAR:
       if (cdiv(M, 256) * cdiv(K, 256) >= cus) return FGR_TILE_256;
@@ -817,17 +830,21 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
   return launch_split_tail<256, false>(A, B, C, M, N, K, full, rem, cus, s);
 }
 
+// Configurations with kStrip cover columns [0, 64 q) with tiles and add the
+// strip's workgroups (four rows of A each) after them.
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
                       int parts, float* W, int first, int compact, int nfull, int lda, int pad) {
   if (!Cfg::kPaddedA && (lda != N || pad != 0)) return FGR_ERR_BAD_PATH;
   int tiles_m = (int)cdiv(M, Cfg::BM);
-  int tiles_n = (int)cdiv(K, Cfg::BN);
+  int tiles_n = (int)cdiv(Cfg::kStrip ? K / Cfg::BN * Cfg::BN : K, Cfg::BN);
   int group = kTileGroup;
   void* args[] = {&A,     &B,    &C,     &M,       &N,     &K,     &tiles_m, &tiles_n, &group,
                   &parts, &W,    &first, &compact, &nfull, &lda,   &pad};
+  const int64_t strip_blocks = Cfg::kStrip ? cdiv(M, fgr::kStripRows) : 0;
   return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
-                nfull + (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts, Cfg::kThreads, args, s);
+                nfull + (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts + strip_blocks, Cfg::kThreads,
+                args, s);
 }
 
 // k-split configurations by the row alignment of the product: 16-byte copies
@@ -852,11 +869,11 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
               A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
         return FGR_ERR_BAD_PATH;
       } else if (rows == Rows::kAOnly) {
-        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(A, B, C, M, N, K, count, s,
-                                                                                    parts, W, first, compact, nfull, lda, pad);
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(
+            A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
       } else if (rows == Rows::kBOnly) {
-        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true, false>>(A, B, C, M, N, K, count, s,
-                                                                                    parts, W, first, compact, nfull, lda, pad);
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true, false>>(
+            A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
       } else {
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
                                                                        compact, nfull, lda, pad);
@@ -923,6 +940,26 @@ int launch_ksplit(int tile, const AOperand& a, const float* B, float* C, int M, 
       return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
     default: return FGR_ERR_BAD_PATH;
   }
+}
+
+// The strip plan: K = 64 q + w with 1 <= w <= kStripMax. One launch of the
+// k-split kernel: its 64x64 tiles cover columns [0, 64 q) and, after them,
+// workgroups of four rows of A each compute C's last w columns on the vector
+// ALUs (strip.hpp). No workspace.
+template <bool VA, bool VB>
+int launch_strip_cfg(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  using Cfg = fgr::KsplitConfig<64, 4, VA, 64, VB, false, false, true>;
+  return launch_ksplit_cfg<Cfg>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0, N, 0);
+}
+
+int launch_strip(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
+  switch (rows_of(A, B, C, N, K)) {
+    case Rows::kAll: return launch_strip_cfg<true, true>(A, B, C, M, N, K, s);
+    case Rows::kAOnly: return launch_strip_cfg<true, false>(A, B, C, M, N, K, s);
+    case Rows::kBOnly: return launch_strip_cfg<false, true>(A, B, C, M, N, K, s);
+    case Rows::kNone: return launch_strip_cfg<false, false>(A, B, C, M, N, K, s);
+  }
+  return FGR_ERR_BAD_PATH;
 }
 
 // Sum of compact partial tiles (tiles [first, first + count) of the grouped
@@ -1113,6 +1150,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     case FGR_PATH_VALU:
       if (tile != FGR_TILE_AUTO && tile != FGR_TILE_128) return FGR_ERR_BAD_PATH;
       break;
+    case FGR_PATH_MFMA_STRIP:
+      if (!strip_shape(M, N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_64)) return FGR_ERR_BAD_PATH;
+      break;
     case FGR_PATH_MFMA_SCALAR: break;
     case FGR_PATH_MFMA_SPLIT:
       if (tile != FGR_TILE_AUTO && tile != FGR_TILE_32 && tile != FGR_TILE_64) return FGR_ERR_BAD_PATH;
@@ -1148,7 +1188,8 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       path = best.path;  // the matrix-vector kernel has no tiles
     } else if (tile == best.tile && (best.path == FGR_PATH_MFMA_DMA || best.path == FGR_PATH_MFMA_DMA_TAIL ||
                                      best.path == FGR_PATH_MFMA_KSPLIT || best.path == FGR_PATH_MFMA_KSPLIT_TAIL ||
-                                     best.path == FGR_PATH_MFMA_SPLITK || best.path == FGR_PATH_MFMA_SPLIT)) {
+                                     best.path == FGR_PATH_MFMA_SPLITK || best.path == FGR_PATH_MFMA_SPLIT ||
+                                     best.path == FGR_PATH_MFMA_STRIP)) {
       path = best.path;  // the kernel the table picked for this tile
     } else if (tile == FGR_TILE_32) {
       path = FGR_PATH_MFMA_SPLIT;  // 32x32 tiles for any shape
@@ -1202,6 +1243,7 @@ int dispatch(const float* A, const float* B, float* C, int M, int N, int K, hipS
     case FGR_PATH_MFMA_SPLIT:
       return mfma_vec_ok(A, B, C, N, K) ? launch_split_tile<true>(tile, A, B, C, M, N, K, cus, s)
                                         : launch_split_tile<false>(tile, A, B, C, M, N, K, cus, s);
+    case FGR_PATH_MFMA_STRIP: return launch_strip(A, B, C, M, N, K, s);
     case FGR_PATH_GEMV_VEC: return launch_gemv<4>(A, B, C, M, N, K, cus, s);
     case FGR_PATH_GEMV_SCALAR: return launch_gemv<1>(A, B, C, M, N, K, cus, s);
     case FGR_PATH_VALU:

@@ -1,0 +1,102 @@
+// The narrow column strip of a product, on the vector ALUs.
+//
+// When K is a few columns past a multiple of 64 (K = 64 q + w, 1 <= w <= 8)
+// and the q full column blocks of 64 x 64 tiles give every CU at most one
+// tile, the last w columns would otherwise cost a whole extra column of
+// mostly-padding tiles, i.e. a second partial wave of tiles. Instead the
+// k-split kernel's launch holds, after its tiles' workgroups, workgroups that
+// run strip_rows: C[m, c0 + j] = sum over n of A[m,n] B[n, c0 + j], c0 = 64
+// q, j < w, each a plain FP32 dot product (the per-output loop of the LeetGPU
+// write-up's naive kernel, section "V0", spread over a wave's lanes). Two
+// workgroups fit a CU, so these run beside the tiles, whose matrix cores they
+// leave alone.
+//
+// A workgroup takes four rows of A, one per wave. It stages B's strip (rows
+// nb .. nb + len - 1, columns c0 .. K - 1, w floats per row, row-major) in the
+// LDS it is given, read once for its four rows; lane l then takes reduction
+// indices n = nb + l, nb + l + 64, ... of its row, keeping w partial sums. The
+// lanes' sums are added across the wave (xor shuffles: every lane ends with
+// the same bits) and lane j stores column c0 + j. Every loop issues its loads
+// (kStripLoads per thread, or more) before it uses any of them: one at a time,
+// each use would wait out a full memory round trip before the next load.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgr {
+
+constexpr int kStripMax = 8;    // widest strip (columns)
+constexpr int kStripRows = 4;   // rows of A per workgroup (one per wave of 256 threads)
+constexpr int kStripLoads = 8;  // loads each thread keeps in flight
+
+// Rows kStripRows b .. kStripRows b + 3 of the strip (rows past M idle but
+// take part in the barriers). stage: lds_floats floats of LDS (at least
+// kStripMax), overwritten.
+__device__ __forceinline__ void strip_rows(const float* __restrict__ A, const float* __restrict__ B,
+                                           float* __restrict__ C, int M, int N, int K, int c0, int b, float* stage,
+                                           int lds_floats) {
+  const int tid = threadIdx.x;
+  const int m = b * kStripRows + (tid >> 6);
+  const int lane = tid & 63;
+  const bool row_ok = m < M;
+  const int w = K - c0;  // 1 .. kStripMax
+  const int chunk = lds_floats / w;  // rows of B's strip staged at a time
+  const float* a = A + (int64_t)(row_ok ? m : 0) * N;
+  float acc[kStripMax];
+#pragma unroll
+  for (int j = 0; j < kStripMax; ++j) acc[j] = 0.f;
+  constexpr int kRowLoads = 2 * kStripLoads;  // elements of A per lane per round
+  for (int nb = 0; nb < N; nb += chunk) {
+    const int len = N - nb < chunk ? N - nb : chunk;
+    __syncthreads();  // the previous chunk has been read by every wave
+    const int total = len * w;
+    for (int i0 = tid; i0 < total; i0 += 64 * kStripRows * kStripLoads) {
+      float v[kStripLoads];
+#pragma unroll
+      for (int u = 0; u < kStripLoads; ++u) {
+        const int i = i0 + u * 64 * kStripRows;
+        const int n = i / w;
+        v[u] = i < total ? B[(int64_t)(nb + n) * K + c0 + (i - n * w)] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kStripLoads; ++u) {
+        const int i = i0 + u * 64 * kStripRows;
+        if (i < total) stage[i] = v[u];
+      }
+    }
+    __syncthreads();
+    if (row_ok) {
+      for (int n0 = nb + lane; n0 < nb + len; n0 += 64 * kRowLoads) {
+        float v[kRowLoads];
+#pragma unroll
+        for (int u = 0; u < kRowLoads; ++u) {
+          const int n = n0 + 64 * u;
+          v[u] = n < nb + len ? a[n] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kRowLoads; ++u) {
+          const int n = n0 + 64 * u;
+          if (n < nb + len) {
+            const float* bn = stage + (n - nb) * w;
+#pragma unroll
+            for (int j = 0; j < kStripMax; ++j)
+              if (j < w) acc[j] += v[u] * bn[j];
+          }
+        }
+      }
+    }
+  }
+  if (!row_ok) return;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+    for (int j = 0; j < kStripMax; ++j) acc[j] += __shfl_xor(acc[j], off);
+  float mine = 0.f;
+#pragma unroll
+  for (int j = 0; j < kStripMax; ++j)
+    if (lane == j) mine = acc[j];
+  if (lane < w) C[(int64_t)m * K + c0 + lane] = mine;
+}
+
+}  // namespace fgr

@@ -131,6 +131,14 @@ extern "C" {
                             Two-Dimensional Thread Tiling" to "V3"); never chosen by solve(). Tile
                             AUTO or 128 only. */
 
+#define FGR_PATH_MFMA_STRIP 12 /* K = 64 q + w with 1 <= w <= 8, N >= 64, K > 64: one launch of the
+                                  MFMA_KSPLIT kernel whose 64x64 tiles cover columns [0, 64 q),
+                                  with workgroups after them that compute C's last w columns
+                                  on the vector ALUs (4-byte or 16-byte copies as for
+                                  MFMA_KSPLIT; no workspace). Chosen when those tiles fit one
+                                  per CU and the w columns would add a partial second wave of
+                                  tiles. Tile AUTO or 64. */
+
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0
 #define FGR_TILE_256 256

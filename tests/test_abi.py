@@ -224,7 +224,7 @@ def test_tile_selection():
     assert st(A0, B0, C0, 4096, 4096, 4160) == 256  # whole waves of 256x256, then the tail
     assert st(A0, B0, C0, 2048, 512, 2048) == 128  # k-split, 128x128
     assert st(A0, B0, C0, 1024, 1024, 1024) == 64  # k-split, 64x64 (256 of them)
-    assert st(A0, B0, C0, 1023, 1025, 1027) == 64  # k-split 64x64, 4-byte copies, then the tail
+    assert st(A0, B0, C0, 1023, 1025, 1027) == 64  # k-split 64x64 and a column strip
     assert st(A0, B0, C0, 256, 256, 256) == 32  # k-split, 32x32
     assert st(A0, B0, C0, 2048, 512, 1024) == 64  # 128 tiles of 128, 512 of 64
     assert st(A0, B0, C0, 2048, 60, 2048) == 64  # no direct copies (N < 64): register-staged 64x64
@@ -241,7 +241,8 @@ def test_split_path_choices():
     assert sp(A0, B0, C0, 1024, 1024, 1024) == fgr.PATH_MFMA_KSPLIT  # 256 tiles of 64
     assert sp(A0, B0, C0, 1024, 8192, 1024) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 1536, 4096, 1536) == fgr.PATH_MFMA_KSPLIT_TAIL  # 576 of 64: 64 left over
-    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 64, 4-byte copies
+    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_STRIP  # 256 of 64 and a 3-column strip
+    assert sp(A0, B0, C0, 1023, 1025, 1036) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 64: a 12-column strip
     assert sp(A0, B0, C0, 2047, 2049, 2051) == fgr.PATH_MFMA_KSPLIT_TAIL  # 1056 of 64
     assert sp(A0, B0, C0, 256, 256, 256) == fgr.PATH_MFMA_KSPLIT  # 32x32
     assert sp(A0, B0, C0, 300, 500, 261) == fgr.PATH_MFMA_KSPLIT  # unaligned, few tiles: 32x32, 4-byte copies
@@ -357,3 +358,26 @@ def test_workspace_limit_round_trip(lib):
     assert fgr.set_workspace_limit(1 << 20) == 0
     assert fgr.set_workspace_limit(-5) == 1 << 20
     assert fgr.set_workspace_limit(-1) == -1
+
+
+def test_strip_choices():
+    sp, st = fgr.select_path, fgr.select_tile
+    a, b, c = 1 << 40, 2 << 40, 3 << 40
+    # K = 64 q + w, 1 <= w <= 8: when the q column blocks of 64x64 tiles fit
+    # one per CU and the w columns would add a partial second wave
+    for shape in [(1023, 1025, 1027), (1024, 1024, 1028), (1023, 1024, 1027), (16384, 512, 67),
+                  (1000, 2049, 1030), (1023, 1025, 1032), (4096, 1025, 257)]:
+        assert sp(a, b, c, *shape) == fgr.PATH_MFMA_STRIP, shape
+        assert st(a, b, c, *shape) == 64, shape
+    assert sp(a, b, c, 1023, 1025, 1033) != fgr.PATH_MFMA_STRIP  # w = 9
+    assert sp(a, b, c, 960, 1025, 1027) == fgr.PATH_MFMA_KSPLIT  # 255 tiles: one wave already
+    assert sp(a, b, c, 1088, 1025, 1027) != fgr.PATH_MFMA_STRIP  # 17 x 16 whole tiles > 256
+    # forced: any shape with such a K, N >= 64; tile AUTO or 64
+    assert call(lib_handle(), A0, B0, C0, 100, 63, 70, fgr.PATH_MFMA_STRIP) == fgr.ERR_BAD_PATH  # N < 64
+    assert call(lib_handle(), A0, B0, C0, 100, 64, 73, fgr.PATH_MFMA_STRIP) == fgr.ERR_BAD_PATH  # w = 9
+    assert call(lib_handle(), A0, B0, C0, 100, 64, 64, fgr.PATH_MFMA_STRIP) == fgr.ERR_BAD_PATH  # w = 0
+    assert call(lib_handle(), A0, B0, C0, 100, 64, 65, fgr.PATH_MFMA_STRIP, 128) == fgr.ERR_BAD_PATH
+
+
+def lib_handle():
+    return fgr.load_library()

@@ -114,6 +114,8 @@ def paths_for(M, N, K):
             out.append((fgr.PATH_MFMA_SPLITK, fgr.TILE_128))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
+    if N >= 64 and K > 64 and 1 <= K % 64 <= 8:
+        out.append((fgr.PATH_MFMA_STRIP, fgr.TILE_64))  # the last K % 64 columns on the vector ALUs
     out.append((fgr.PATH_VALU, fgr.TILE_AUTO))  # vector ALUs, any shape
     if M <= 8:
         out.append((fgr.PATH_GEMV_SCALAR, 0))
@@ -271,11 +273,11 @@ def test_large_ragged_sampled(shape):
 @pytest.mark.parametrize("shape,path,tile", [
     ((2048, 128, 2048), fgr.PATH_MFMA_KSPLIT, 128), ((2040, 1000, 2044), fgr.PATH_MFMA_KSPLIT, 128),
     ((2176, 136, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128), ((3072, 132, 3076), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
-    ((1024, 200, 1024), fgr.PATH_MFMA_KSPLIT, 64), ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
+    ((1024, 200, 1024), fgr.PATH_MFMA_KSPLIT, 64), ((1023, 1025, 1039), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
     ((1536, 104, 1540), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((509, 300, 515), fgr.PATH_MFMA_KSPLIT, 32),
     ((512, 128, 512), fgr.PATH_MFMA_KSPLIT, 32),
     # long reductions: the tail tiles' reduction split across workgroups
-    ((1023, 4097, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((2176, 4096, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
+    ((1023, 4097, 1039), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((2176, 4096, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
     ((1088, 4100, 1024), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
     # 128x128 tiles with one operand on 4-byte copies (buffer loads): B's, then
     # A's; ragged M and K, a partial last wave
@@ -345,6 +347,42 @@ def test_split_matrix_vector_exact(shape):
     assert_exact(gpu_gemm(A, B, offsets=(1, 1, 1)), Cref, f"{shape} 4-byte aligned")
 
 
+@pytest.mark.parametrize("shape,offsets", [
+    ((1023, 1025, 1027), (0, 0, 0)),   # neither operand aligned: A packed, w = 3
+    ((1023, 1025, 1027), (1, 2, 3)),
+    ((1023, 1024, 1027), (0, 0, 0)),   # A aligned, B not: no copy
+    ((1024, 1024, 1028), (0, 0, 0)),   # all aligned, w = 4
+    ((1024, 1024, 1028), (0, 0, 1)),   # C misaligned
+    ((1000, 2049, 1030), (0, 0, 0)),   # w = 6, ragged rows
+    ((1023, 1025, 1032), (3, 0, 0)),   # w = 8, A misaligned, B aligned
+    ((16384, 512, 67), (0, 0, 0)),     # one column block, many rows
+    ((4096, 1025, 257), (0, 0, 0)),    # four column blocks, w = 1
+], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_strip_plan_exact(shape, offsets):
+    # the last K % 64 columns on the vector ALUs (with A's padded copy when
+    # neither operand's rows are aligned), 64x64 k-split tiles on the rest:
+    # exact on integer data, auto and forced
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=16)
+    say(f"strip plan {shape} offsets {offsets}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_MFMA_STRIP
+    say(f"strip plan {shape} offsets {offsets}: GPU")
+    assert_exact(gpu_gemm(A, B, offsets=offsets), Cref, f"{shape} auto {offsets}")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_STRIP, 64, offsets=offsets), Cref, f"{shape} forced {offsets}")
+
+
+@pytest.mark.parametrize("shape", [(100, 300, 70), (37, 64, 65), (5, 128, 72), (300, 4097, 129), (64, 64, 136)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_strip_plan_forced_small_exact(shape):
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=17)
+    Cref, _ = oracle.gemm(A, B)
+    for offsets in [(0, 0, 0), (1, 1, 1)]:
+        say(f"strip plan forced {shape} offsets {offsets}")
+        assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_STRIP, 64, offsets=offsets), Cref, f"{shape} {offsets}")
+
+
 def test_packed_a_with_split_tail_exact():
     # neither operand's rows 16-byte aligned (N, K odd), 128x128 tiles forced
     # with the tail form: 9 tiles, none in a whole wave, so all of them are
@@ -363,7 +401,8 @@ def test_packed_a_with_split_tail_exact():
     ((2040, 2047, 2043), fgr.PATH_MFMA_KSPLIT, 128),        # A's padded copy -> 64x64 tiles
     ((300, 4097, 259), fgr.PATH_MFMA_KSPLIT_TAIL, 128),     # A's copy and the split tail
     ((2047, 2049, 2051), fgr.PATH_AUTO, 0),                 # the same, picked by solve()
-    ((1023, 1025, 1027), fgr.PATH_AUTO, 0),                 # tail split in the whole tiles' grid
+    ((1023, 1025, 1027), fgr.PATH_AUTO, 0),                 # strip plan without A's copy
+    ((1023, 1025, 1036), fgr.PATH_AUTO, 0),                 # tail split in the whole tiles' grid
     ((1023, 4097, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64),    # tail split after the whole tiles
     ((128, 262144, 128), fgr.PATH_AUTO, 0),                 # split reduction -> unsplit tiles
     ((301, 8191, 127), fgr.PATH_MFMA_SPLITK, 128),          # forced split over A's copy
@@ -679,8 +718,9 @@ def test_nan_in_a_row_poisons_only_that_row():
     assert_exact(C[mask], Cref, "rows without NaN")
 
 
-@pytest.mark.parametrize("shape", [(1023, 1025, 1027), (128, 16384, 128), (4, 100000, 96), (16, 65536, 64),
-                                   (300, 500, 261), (4100, 104, 4100)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(1023, 1025, 1027), (1023, 1025, 1039), (128, 16384, 128), (4, 100000, 96),
+                                   (16, 65536, 64), (300, 500, 261), (4100, 104, 4100)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_special_values_stay_in_their_row_and_column(shape):
     # a NaN in A poisons exactly its row of C and an infinity in B exactly its
     # column (with a sign mix, NaN or +-inf there), on the paths that pad,
