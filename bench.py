@@ -23,6 +23,16 @@ clock. Prints ONE JSON line:
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
                (leading rows of A, or the whole product repeated), on this
                host's cores
+  batched      the same launches back to back between two events only
+               (and, for calls under 0.2 ms, captured in one HIP graph and
+               replayed, which takes the host's launch cost out)
+  clock        cycles per launch (profiles/<workload>_clock.md, GPU-active
+               clocks from rocprofv3) over this run's launch time: the clock
+               the timed launches ran at, the FP32 matrix peak at that clock,
+               and the cycle efficiency 2MNK / (256 FLOP x 256 CUs x cycles)
+  read_ceiling (matrix-vector workload) the measured streaming-read rate of
+               a plain 1 GiB read (fgr_stream_read), and the kernel's
+               fraction of it
   parity       the timed run's C against the oracle product that the
                cpu_baseline leg computed (every element of the rows it
                covers: all of them when it ran the whole product): the
@@ -77,6 +87,122 @@ def recorded_traffic(workload: str):
     if not src or not val or src.group(1) != kernel_source_hash():
         return None
     return int(val.group(1))
+
+
+CU_COUNT = 256
+FP32_FLOP_PER_CU_CLK = 256  # v_mfma_f32_32x32x2_f32: 4096 FLOP in 64 cycles, 4 SIMDs per CU
+NUM_XCC = 8
+
+
+def recorded_clock(workload: str):
+    """The dominant kernel's cycles per launch from profiles/<workload>_clock.md,
+    if current (same kernel sources)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_clock.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    src = re.search(r"kernel-source-sha256:\s*([0-9a-f]+)", text)
+    cyc = re.search(r"cycles-per-launch:\s*([0-9.]+)", text)
+    if not src or not cyc or src.group(1) != kernel_source_hash():
+        return None
+    return float(cyc.group(1))
+
+
+def summarize_clock(workload, pmc_dir, commands, out_path, warmup=2):
+    """profiles/<workload>_clock.md from a rocprofv3 --pmc GRBM_GUI_ACTIVE
+    SQ_BUSY_CYCLES SQ_CYCLES --kernel-trace run: per dispatch of the dominant
+    kernel, GPU-active cycles (GRBM_GUI_ACTIVE summed over the XCDs, divided
+    by their number), the dispatch's duration and the clock they imply; the
+    kernel's cycles per launch set against the cycles its 2MNK FLOP take at
+    the matrix cores' rate (256 FLOP per CU per clock), a clock-independent
+    efficiency."""
+    rows = _csv_rows(_find(pmc_dir, "counter_collection.csv"))
+    trace = {r["Dispatch_Id"]: r for r in _csv_rows(_find(pmc_dir, "kernel_trace.csv"))}
+    per = {}
+    for r in rows:
+        if "copyBuffer" in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"kernel": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    names = {}
+    for d in per.values():
+        names[d["kernel"]] = names.get(d["kernel"], 0) + d.get("GRBM_GUI_ACTIVE", 0)
+    top = max(names, key=names.get)
+    disp = sorted((int(k), v) for k, v in per.items() if v["kernel"] == top)[warmup:]
+    import synth
+
+    w = synth.WORKLOADS[workload]
+    ideal = w.flops / (CU_COUNT * FP32_FLOP_PER_CU_CLK)
+    lines = [
+        f"# Clock and cycles: {top.split('(')[0]} on {workload} (M={w.M}, N={w.N}, K={w.K})",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):",
+        "",
+        *[f"    {c}" for c in commands],
+        "",
+        f"GRBM_GUI_ACTIVE counts GPU-active clocks; rocprofv3 sums it over the {NUM_XCC} XCDs, so cycles = "
+        f"GRBM_GUI_ACTIVE / {NUM_XCC}. SQ_CYCLES (summed over the 32 shader engines) and SQ_BUSY_CYCLES are shown "
+        "beside it. Clock = cycles / dispatch duration (kernel trace of the same run; the profiler serialises "
+        "dispatches, so the clock here ramps over the first ones). Ideal cycles = 2MNK / (256 CUs x 256 FLOP "
+        f"per clock) = {ideal:.0f}.",
+        "",
+        "| dispatch | duration ns | GRBM_GUI_ACTIVE / 8 | SQ_CYCLES / 32 | SQ_BUSY_CYCLES / 32 | clock GHz |",
+        "|---|---|---|---|---|---|",
+    ]
+    cycles = []
+    for did, d in disp:
+        t = trace.get(str(did))
+        ns = int(t["End_Timestamp"]) - int(t["Start_Timestamp"]) if t else 0
+        cyc = d.get("GRBM_GUI_ACTIVE", 0) / NUM_XCC
+        cycles.append(cyc)
+        lines.append(f"| {did} | {ns} | {cyc:.0f} | {d.get('SQ_CYCLES', 0) / 32:.0f} | "
+                     f"{d.get('SQ_BUSY_CYCLES', 0) / 32:.0f} | {cyc / ns if ns else 0:.3f} |")
+    avg = sum(cycles) / len(cycles)
+    lines += [
+        "",
+        f"cycles-per-launch: {avg:.0f}",
+        f"ideal-mfma-cycles: {ideal:.0f}",
+        f"cycle-efficiency: {ideal / avg:.4f}",
+        "",
+        f"kernel-source-sha256: {kernel_source_hash()}",
+        "",
+    ]
+    with open(out_path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    return out_path
+
+
+def summarize_read(trace_dir, commands, out_path, warmup=5):
+    """profiles/stream_read_1gib.md from a rocprofv3 --kernel-trace --stats run
+    of bench.py --read-ceiling: each grid size's launches (in launch order,
+    warm-ups dropped) and their read rate over the 1 GiB buffer."""
+    trace = [r for r in _csv_rows(_find(trace_dir, "kernel_trace.csv")) if "stream_read" in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    groups = {}
+    for r in trace:
+        blocks = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0) // 256
+        groups.setdefault(blocks, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = [
+        "# Streaming-read ceiling: fgr_stream_read over 1 GiB (each float read once, 128-bit loads)",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):",
+        "",
+        *[f"    {c}" for c in commands],
+        "",
+        "| workgroups | timed launches | average ns | min ns | GB/s at the average |",
+        "|---|---|---|---|---|",
+    ]
+    best = 0.0
+    for blocks, d in sorted(groups.items()):
+        t = d[warmup:] or d
+        avg = sum(t) / len(t)
+        gbs = READ_BYTES / avg
+        best = max(best, gbs)
+        lines.append(f"| {blocks} | {len(t)} | {avg:.0f} | {min(t)} | {gbs:.1f} |")
+    lines += ["", f"read-ceiling-gbs: {best:.1f}", "", f"kernel-source-sha256: {kernel_source_hash()}", ""]
+    with open(out_path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    return out_path
 
 
 def recorded_counters(workload: str):
@@ -471,6 +597,36 @@ def batched_ms(fn, launches, stream):
     return start.elapsed_time(end) / launches
 
 
+def graph_ms(fn, launches, stream):
+    """Mean time per launch of `launches` launches captured in one HIP graph,
+    replayed between two events (after a first replay). The graph holds only
+    the library's kernel launches (and, for split paths, its stream-ordered
+    workspace allocation)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(launches):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / launches
+    del graph
+    return ms
+
+
 READ_BYTES = 1 << 30  # the streaming-read buffer: 4x the 256 MB last-level cache
 
 
@@ -485,7 +641,7 @@ def read_ceiling(dev, stream, cus, steps=20, warmup=5):
     n = READ_BYTES // 4
     X = torch.ones(n, dtype=torch.float32, device=dev)
     sweep = []
-    for per_cu in (2, 4, 8, 16):
+    for per_cu in (1, 2, 4, 8, 16):
         blocks = cus * per_cu
         out = torch.empty(blocks, dtype=torch.float32, device=dev)
 
@@ -529,6 +685,14 @@ def main() -> int:
                          "per variant and exit (the controlled comparison of the LeetGPU write-up)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/<workload>_traffic.md from three rocprofv3 output folders and exit")
+    ap.add_argument("--summarize-clock", metavar="PMC_DIR", default=None,
+                    help="write profiles/<workload>_clock.md from a rocprofv3 --pmc GRBM_GUI_ACTIVE "
+                         "SQ_BUSY_CYCLES SQ_CYCLES --kernel-trace run and exit")
+    ap.add_argument("--summarize-read", metavar="TRACE_DIR", default=None,
+                    help="write profiles/stream_read_1gib.md from a rocprofv3 --kernel-trace --stats run of "
+                         "bench.py --read-ceiling and exit")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the streaming-read ceiling (fgr_stream_read over 1 GiB) and print it")
     ap.add_argument("--summarize-sq", metavar="SQ_DIR", default=None,
                     help="(with --summarize) a rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " run to add")
     ap.add_argument("--summarize-ablation", nargs=3, metavar=("ABLATION_JSONL", "SQ_DIR", "RESOURCES_MD"),
@@ -542,6 +706,14 @@ def main() -> int:
     if args.summarize_ablation:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_controlled_comparison.md")
         print(summarize_ablation(args.workload, *args.summarize_ablation, args.command, out))
+        return 0
+    if args.summarize_read:
+        out = os.path.join(ROOT, "profiles", "stream_read_1gib.md")
+        print(summarize_read(args.summarize_read, args.command, out, args.warmup))
+        return 0
+    if args.summarize_clock:
+        out = os.path.join(ROOT, "profiles", f"{args.workload}_clock.md")
+        print(summarize_clock(args.workload, args.summarize_clock, args.command, out))
         return 0
     if args.summarize:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_traffic.md")
@@ -569,6 +741,12 @@ def main() -> int:
         print("bench.py needs a GPU (no CPU fallback)", file=sys.stderr)
         return 2
     fgr.load_library()
+    if args.read_ceiling:
+        dev = torch.device("cuda:0")
+        res = read_ceiling(dev, torch.cuda.current_stream(), torch.cuda.get_device_properties(dev).multi_processor_count,
+                           steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"metric": "streaming read GB/s (fgr_stream_read, 1 GiB)", **res}), flush=True)
+        return 0
 
     if args.shape:
         M, N, K = args.shape
@@ -592,6 +770,9 @@ def main() -> int:
 
     def step(i):
         fgr.solve_path(dA, dBs[i % copies], dC, w.M, w.N, w.K, path, tile, stream=stream)
+
+    def step_current(i):  # on torch's current stream (a graph capture's, when capturing)
+        fgr.solve_path(dA, dBs[i % copies], dC, w.M, w.N, w.K, path, tile)
 
     if args.ablation:
         return ablation(w, dA, dBs, dC, copies, args.steps, args.warmup, stream)
@@ -637,6 +818,26 @@ def main() -> int:
         "ms_per_launch": round(batch_ms, 5),
         "achieved": round(w.algorithmic_bytes / batch_ms / 1e6, 2) if gemv else round(w.flops / batch_ms / 1e9, 3),
     }
+    if batch_ms < 0.2:
+        # short calls: the same launches captured in one HIP graph and replayed
+        # between two events, so that the host's launch cost drops out
+        g_ms = graph_ms(step_current, batch_launches, stream)
+        roof["batched"]["graph_ms_per_launch"] = round(g_ms, 5)
+        roof["batched"]["graph_achieved"] = (round(w.algorithmic_bytes / g_ms / 1e6, 2) if gemv
+                                             else round(w.flops / g_ms / 1e9, 3))
+    cycles = recorded_clock(w.name)
+    if cycles and not gemv:
+        # cycles per launch (profiles/<workload>_clock.md) over this run's launch
+        # time: the clock the timed launches ran at, and the peak at that clock
+        ghz = cycles / (avg_launch_s * 1e9)
+        peak_at_clock = CU_COUNT * FP32_FLOP_PER_CU_CLK * ghz / 1e3
+        roof["clock"] = {
+            "cycles_per_launch": round(cycles),
+            "ghz": round(ghz, 3),
+            "peak_at_clock": round(peak_at_clock, 1),
+            "frac_at_clock": round(achieved / peak_at_clock, 4),
+            "cycle_efficiency": round(w.flops / (CU_COUNT * FP32_FLOP_PER_CU_CLK) / cycles, 4),
+        }
     if gemv:
         # the measured streaming-read ceiling beside the datasheet peak
         ceiling = read_ceiling(dev, stream, torch.cuda.get_device_properties(dev).multi_processor_count)
