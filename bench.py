@@ -254,7 +254,8 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_
     SQ_INSTS_VALU_MFMA_MOPS_F32 (FP32 MFMA multiply-or-add operations / 512)."""
     stats = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
     stats.sort(key=lambda r: float(r["TotalDurationNs"]), reverse=True)
-    top = stats[0]
+    # the product's kernels only: not the read-ceiling measurement or torch's own
+    top = [r for r in stats if "fgr::" in r["Name"] and "stream_read" not in r["Name"]][0]
     # the dispatches of the timed steps: drop the warm-up launches
     trace = [r for r in _csv_rows(_find(trace_dir, "kernel_trace.csv")) if r["Kernel_Name"] == top["Name"]]
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
@@ -265,8 +266,11 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_
         rows = _csv_rows(_find(directory, "counter_collection.csv"))
         kern = [float(r["Counter_Value"]) for r in rows
                 if r["Counter_Name"] == counter and r["Kernel_Name"] == top["Name"]]
-        copy = [float(r["Counter_Value"]) for r in rows
-                if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+        # the 512 MiB calibration copies: the copy dispatches with the largest
+        # grid (small device-to-host copies use the same kernel)
+        copies = [r for r in rows if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+        big = max((int(r["Grid_Size"]) for r in copies), default=0)
+        copy = [float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == big]
         if not kern or not copy:
             raise ValueError(f"{counter}: kernel or copy dispatches missing in {directory}")
         k_kib = sum(kern) / len(kern)
