@@ -381,3 +381,15 @@ def test_strip_choices():
 
 def lib_handle():
     return fgr.load_library()
+
+
+def test_stream_read_rejects_bad_arguments(lib):
+    # host-only checks of the measurement hook, before any HIP call
+    sr = lib.fgr_stream_read
+    assert sr(0, 1024, C0, 4, None) == fgr.ERR_NULL_POINTER
+    assert sr(A0, 1024, 0, 4, None) == fgr.ERR_NULL_POINTER
+    assert sr(A0, 1022, C0, 4, None) == fgr.ERR_BAD_DIMS  # n % 4
+    assert sr(A0, 0, C0, 4, None) == fgr.ERR_BAD_DIMS
+    assert sr(A0, 1024, C0, 0, None) == fgr.ERR_BAD_DIMS
+    assert sr(A0 + 4, 1024, C0, 4, None) == fgr.ERR_MISALIGNED
+    assert sr(A0, 1024, A0 + 16, 4, None) == fgr.ERR_ALIAS

@@ -383,6 +383,19 @@ def test_strip_plan_forced_small_exact(shape):
         assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_STRIP, 64, offsets=offsets), Cref, f"{shape} {offsets}")
 
 
+@pytest.mark.parametrize("n,blocks", [(4, 1), (1 << 20, 256), ((1 << 20) + 36, 1000), (64, 512)])
+def test_stream_read_sums(n, blocks):
+    # the read-ceiling hook reads every float once: with small integers every
+    # workgroup's sum is exact and the sums add up to the whole buffer's
+    x = torch.from_numpy((np.arange(n) % 7).astype(np.float32)).to(DEV)
+    out = torch.full((blocks,), float("nan"), device=DEV)
+    fgr.stream_read(x, n, out, blocks)
+    torch.cuda.synchronize()
+    sums = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(sums).all()
+    assert sums.sum() == float((np.arange(n) % 7).sum())
+
+
 def test_packed_a_with_split_tail_exact():
     # neither operand's rows 16-byte aligned (N, K odd), 128x128 tiles forced
     # with the tail form: 9 tiles, none in a whole wave, so all of them are
