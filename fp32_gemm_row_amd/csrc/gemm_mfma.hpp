@@ -140,6 +140,22 @@ __device__ __forceinline__ float4 mask_quad(float4 v, unsigned ok) {
   return make_float4(ok & 1u ? v.x : 0.f, ok & 2u ? v.y : 0.f, ok & 4u ? v.z : 0.f, ok & 8u ? v.w : 0.f);
 }
 
+// V (float2 or float4) consecutive floats at an address that is only 4-byte
+// aligned, and the store of such a vector. On gfx9-family GPUs global loads and
+// stores of two or more dwords need only dword alignment; the compiler emits
+// one global_load_dwordx2 / x4 (store) for these.
+template <class V>
+__device__ __forceinline__ V load_dwords(const float* p) {
+  V v;
+  __builtin_memcpy(&v, p, sizeof(V));
+  return v;
+}
+
+template <class V>
+__device__ __forceinline__ void store_dwords(float* p, V v) {
+  __builtin_memcpy(p, &v, sizeof(V));
+}
+
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;

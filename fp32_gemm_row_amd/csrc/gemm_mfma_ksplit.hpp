@@ -19,6 +19,11 @@
 // summing and storing its share of the tile: deterministic, no workspace, no
 // atomics.
 //
+// Here the 4-byte copies serve the 128x128 and 32x128 tiles only: 64x64 tiles
+// whose rows are not all 16-byte aligned, and every 32x32 tile, load their
+// operands straight into registers instead (gemm_mfma_kreg.hpp), which was
+// measured faster there.
+//
 // This keeps the output-parallel decomposition of the LeetGPU write-up
 // (section "V0", "Approach": outputs independent, each owned with its whole
 // reduction by one block) at workgroup level; only the waves inside the
@@ -73,6 +78,7 @@ struct KsplitConfig {
   // only the form with aligned A and B through buffer loads reads a padded
   // copy of A; every other form takes lda = N and pad = 0 as constants
   static constexpr bool kPaddedA = VA_ && BUFB;
+  static constexpr bool kReg = false;  // operands through LDS (gemm_mfma_kreg.hpp: through registers)
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRB = BM / 32, kCB = BN / 32;

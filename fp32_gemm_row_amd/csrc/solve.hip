@@ -17,6 +17,7 @@
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_dma.hpp"
 #include "gemm_mfma_ksplit.hpp"
+#include "gemm_mfma_kreg.hpp"
 #include "gemm_mfma_split.hpp"
 #include "gemm_valu.hpp"
 #include "gemv.hpp"
@@ -420,9 +421,9 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     }
     // fewer 64x64 tiles than CUs: 64x64 or 32x32 k-split tiles, with the
     // reduction also split across workgroups where that is estimated faster
-    // (the k-split 32x32 tiles measured faster than the split kernel's also
-    // with 4-byte copies: 400 x 1000 x 401 10.0 vs 14.8 us, 512 x 4095 x 512
-    // 30.8 vs 50.9)
+    // (the k-split 32x32 tiles measured faster than the split kernel's on
+    // unaligned rows even when they still took 4-byte copies through LDS:
+    // 400 x 1000 x 401 10.0 vs 14.8 us, 512 x 4095 x 512 30.8 vs 50.9)
     const SplitPlan sp = splitk_plan(M, N, K, cus);
     if (sp.parts >= 2) {
       if (rows_of(A, B, C, N, K) != Rows::kNone && ksplit128_ok(A, B, C, N, K) &&
@@ -842,42 +843,64 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
   void* args[] = {&A,     &B,    &C,     &M,       &N,     &K,     &tiles_m, &tiles_n, &group,
                   &parts, &W,    &first, &compact, &nfull, &lda,   &pad};
   const int64_t strip_blocks = Cfg::kStrip ? cdiv(M, fgr::kStripRows) : 0;
-  return launch(reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>),
+  const void* kernel;
+  if constexpr (Cfg::kReg) kernel = reinterpret_cast<const void*>(&fgr::gemm_mfma_kreg_kernel<Cfg>);
+  else kernel = reinterpret_cast<const void*>(&fgr::gemm_mfma_ksplit_kernel<Cfg>);
+  return launch(kernel,
                 nfull + (count < 0 ? (int64_t)tiles_m * tiles_n : count) * parts + strip_blocks, Cfg::kThreads,
                 args, s);
 }
 
-// k-split configurations by the row alignment of the product: 16-byte copies
-// of A and B with 128-bit stores, of one operand (the other 4-byte), or
-// 4-byte copies of both; 128x128 tiles in the first two forms (ksplit128_ok).
+// k-split configurations by tile and by the row alignment of the product.
+// 64x64 tiles with 16-byte rows of A, B and C: direct 16-byte copies through
+// LDS (KsplitConfig); other 64x64 and all 32x32 tiles: operands loaded
+// straight into registers at any 4-byte alignment (KregConfig; 64x64 needs K
+// >= 2, so K = 1 takes 32x32). 128x128 and 32x128 tiles: 16-byte copies of
+// each operand whose rows allow them, 4-byte copies of the other (128x128:
+// through buffer loads, and one operand at least aligned: ksplit128_ok).
+constexpr int kKregDepth = 2;  // chunks of operands in registers: deeper rings measured slower
+
 template <int BM, int BN = BM>
 int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
                        hipStream_t s, int parts, float* W, int first, int compact, int nfull, int lda,
                        int pad) {
-  switch (rows) {
-    case Rows::kAll:
-      return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                    compact, nfull, lda, pad);
-    default:
-      if constexpr (BM == 128) {
-        // one operand on 4-byte copies through buffer loads (see ksplit128_ok)
-        if (rows == Rows::kAOnly)
-          return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true, BN, false, false, true>>(
-              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
-        if (rows == Rows::kBOnly && K % 4 == 0 && aligned(C, 16))
-          return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, false, BN, true, true, true>>(
+  if constexpr (BM == BN && BM <= 64) {
+    if (BM == 64 && rows == Rows::kAll)
+      return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true>>(A, B, C, M, N, K, count, s, parts, W, first,
+                                                               compact, nfull, lda, pad);
+    if (K < BM / 32) return FGR_ERR_BAD_PATH;  // run() maps K = 1 to 32x32 tiles
+    return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth>>(A, B, C, M, N, K, count, s, parts, W, first,
+                                                             compact, nfull, lda, pad);
+  } else if constexpr (BM == 128) {
+    switch (rows) {
+      case Rows::kAll:
+        return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true>>(A, B, C, M, N, K, count, s, parts, W, first,
+                                                                  compact, nfull, lda, pad);
+      case Rows::kAOnly:
+        return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true, 128, false, false, true>>(
+            A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
+      case Rows::kBOnly:
+        if (K % 4 == 0 && aligned(C, 16))
+          return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, false, 128, true, true, true>>(
               A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
         return FGR_ERR_BAD_PATH;
-      } else if (rows == Rows::kAOnly) {
+      default: return FGR_ERR_BAD_PATH;  // pack_a first
+    }
+  } else {
+    switch (rows) {
+      case Rows::kAll:
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
+                                                                      compact, nfull, lda, pad);
+      case Rows::kAOnly:
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(
             A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
-      } else if (rows == Rows::kBOnly) {
+      case Rows::kBOnly:
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true, false>>(
             A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
-      } else {
+      default:
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
                                                                        compact, nfull, lda, pad);
-      }
+    }
   }
 }
 
@@ -942,24 +965,17 @@ int launch_ksplit(int tile, const AOperand& a, const float* B, float* C, int M, 
   }
 }
 
-// The strip plan: K = 64 q + w with 1 <= w <= kStripMax. One launch of the
+// The strip plan: K = 64 q + w with 1 <= w <= kStripMax. One launch of a
 // k-split kernel: its 64x64 tiles cover columns [0, 64 q) and, after them,
 // workgroups of four rows of A each compute C's last w columns on the vector
-// ALUs (strip.hpp). No workspace.
-template <bool VA, bool VB>
-int launch_strip_cfg(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
-  using Cfg = fgr::KsplitConfig<64, 4, VA, 64, VB, false, false, true>;
-  return launch_ksplit_cfg<Cfg>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0, N, 0);
-}
-
+// ALUs (strip.hpp). No workspace. Direct 16-byte copies when the rows of A, B
+// and C allow them, else operands straight into registers.
 int launch_strip(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
-  switch (rows_of(A, B, C, N, K)) {
-    case Rows::kAll: return launch_strip_cfg<true, true>(A, B, C, M, N, K, s);
-    case Rows::kAOnly: return launch_strip_cfg<true, false>(A, B, C, M, N, K, s);
-    case Rows::kBOnly: return launch_strip_cfg<false, true>(A, B, C, M, N, K, s);
-    case Rows::kNone: return launch_strip_cfg<false, false>(A, B, C, M, N, K, s);
-  }
-  return FGR_ERR_BAD_PATH;
+  if (rows_of(A, B, C, N, K) == Rows::kAll)
+    return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true, 64, true, false, false, true>>(
+        A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0, N, 0);
+  return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0,
+                                                                  N, 0);
 }
 
 // Sum of compact partial tiles (tiles [first, first + count) of the grouped
@@ -1200,6 +1216,13 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
     }
   }
   if (tile == FGR_TILE_AUTO) tile = default_tile(path, best, M, N, K, cus, mfma_vec_ok(A, B, C, N, K));
+  if (tile == FGR_TILE_64 && K < 2 &&
+      (path == FGR_PATH_MFMA_KSPLIT || path == FGR_PATH_MFMA_KSPLIT_TAIL || path == FGR_PATH_MFMA_SPLITK)) {
+    // the register-fed 64x64 tiles load B two columns at a time: one column
+    // takes 32x32 tiles (which have no tail form)
+    tile = FGR_TILE_32;
+    if (path == FGR_PATH_MFMA_KSPLIT_TAIL) path = FGR_PATH_MFMA_KSPLIT;
+  }
   if (!noalloc) return dispatch(A, B, C, M, N, K, s, cus, path, tile);
 
   // fgr_solve_noalloc: the same plan, its workspace from the scratch array
@@ -1231,7 +1254,7 @@ int dispatch(const float* A, const float* B, float* C, int M, int N, int K, hipS
       Workspace packed;  // A's padded copy, when 128x128 tiles need one
       if (tile == FGR_TILE_128 && rows_of(A, B, C, N, K) == Rows::kNone) {
         const int prc = pack_a(packed, a, A, M, N, s);
-        if (prc == kNoWorkspace) tile = FGR_TILE_64;  // no copy: 64x64 tiles with 4-byte copies
+        if (prc == kNoWorkspace) tile = FGR_TILE_64;  // no copy: 64x64 tiles, operands into registers
         else if (prc != FGR_OK) return prc;
       }
       if (path == FGR_PATH_MFMA_KSPLIT) return launch_ksplit(tile, a, B, C, M, K, -1, s);

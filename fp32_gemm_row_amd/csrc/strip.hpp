@@ -14,7 +14,8 @@
 // A workgroup takes four rows of A, one per wave. It stages B's strip (rows
 // nb .. nb + len - 1, columns c0 .. K - 1, w floats per row, row-major) in the
 // LDS it is given, read once for its four rows; lane l then takes reduction
-// indices n = nb + l, nb + l + 64, ... of its row, keeping w partial sums. The
+// indices nb + 4 l + 256 u .. + 3 of its row (one 16-byte load each, for
+// which 4-byte alignment suffices), keeping w partial sums. The
 // lanes' sums are added across the wave (xor shuffles: every lane ends with
 // the same bits) and lane j stores column c0 + j. Every loop issues its loads
 // (kStripLoads per thread, or more) before it uses any of them: one at a time,
@@ -23,6 +24,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "gemm_mfma.hpp"
 
 namespace fgr {
 
@@ -46,7 +49,7 @@ __device__ __forceinline__ void strip_rows(const float* __restrict__ A, const fl
   float acc[kStripMax];
 #pragma unroll
   for (int j = 0; j < kStripMax; ++j) acc[j] = 0.f;
-  constexpr int kRowLoads = 2 * kStripLoads;  // elements of A per lane per round
+  constexpr int kRowQuads = kStripLoads / 2;  // 16-byte loads of A per lane per round
   for (int nb = 0; nb < N; nb += chunk) {
     const int len = N - nb < chunk ? N - nb : chunk;
     __syncthreads();  // the previous chunk has been read by every wave
@@ -67,21 +70,34 @@ __device__ __forceinline__ void strip_rows(const float* __restrict__ A, const fl
     }
     __syncthreads();
     if (row_ok) {
-      for (int n0 = nb + lane; n0 < nb + len; n0 += 64 * kRowLoads) {
-        float v[kRowLoads];
+      // lane l: elements n = nb + 4 l + 256 u .. n + 3 of its row, one 16-byte
+      // load each (4-byte alignment suffices), element by element at the end
+      for (int n0 = nb + 4 * lane; n0 < nb + len; n0 += 256 * kRowQuads) {
+        float4 v[kRowQuads];
 #pragma unroll
-        for (int u = 0; u < kRowLoads; ++u) {
-          const int n = n0 + 64 * u;
-          v[u] = n < nb + len ? a[n] : 0.f;
+        for (int u = 0; u < kRowQuads; ++u) {
+          const int n = n0 + 256 * u;
+          if (n + 3 < nb + len) {
+            v[u] = load_dwords<float4>(a + n);
+          } else {
+            float e[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) e[q] = n + q < nb + len ? a[n + q] : 0.f;
+            v[u] = make_float4(e[0], e[1], e[2], e[3]);
+          }
         }
 #pragma unroll
-        for (int u = 0; u < kRowLoads; ++u) {
-          const int n = n0 + 64 * u;
-          if (n < nb + len) {
-            const float* bn = stage + (n - nb) * w;
+        for (int u = 0; u < kRowQuads; ++u) {
+          const int n = n0 + 256 * u;
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-            for (int j = 0; j < kStripMax; ++j)
-              if (j < w) acc[j] += v[u] * bn[j];
+          for (int q = 0; q < 4; ++q) {
+            if (n + q < nb + len) {
+              const float* bn = stage + (n + q - nb) * w;
+#pragma unroll
+              for (int j = 0; j < kStripMax; ++j)
+                if (j < w) acc[j] += e[q] * bn[j];
+            }
           }
         }
       }

@@ -106,12 +106,17 @@ extern "C" {
                                     split kernel on the tiles of the last, partial wave, cut into
                                     64x64 or 32x32 tiles; same conditions as MFMA_DMA. Two
                                     launches on `stream`. */
-#define FGR_PATH_MFMA_KSPLIT 8 /* FP32 MFMA, 128x128, 64x64 or 32x32 tiles, each of a workgroup's four
-                                  waves reducing a quarter of N into the whole tile from its own
-                                  direct global->LDS copies (4-byte copies for rows that are not
+#define FGR_PATH_MFMA_KSPLIT 8 /* FP32 MFMA, 128x128, 64x64, 32x32 or 32x128 tiles, each of a
+                                  workgroup's four waves reducing a quarter of N into the whole
+                                  tile. Operands: 64x64 tiles with 16-byte aligned rows of A, B
+                                  and C, and 128x128 / 32x128 tiles, through direct
+                                  global->LDS copies (4-byte copies for rows that are not
                                   16-byte aligned; tile 128 with neither A's nor B's rows 16-byte
                                   aligned first copies A into padded rows, a workspace of its
-                                  own, and takes tile 64 if that cannot be had); N >= 64 */
+                                  own, and takes tile 64 if that cannot be had); other 64x64 and
+                                  all 32x32 tiles load them straight into registers (16- and
+                                  8-byte loads at any 4-byte alignment; 64x64 with K = 1 runs
+                                  as 32x32). N >= 64 */
 #define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT (tile 128 or 64) on the whole waves of tiles; the
                                        tiles of the last, partial wave either with their reduction
                                        split over workgroups through a workspace (N >= 4096, or
@@ -134,10 +139,10 @@ extern "C" {
 #define FGR_PATH_MFMA_STRIP 12 /* K = 64 q + w with 1 <= w <= 8, N >= 64, K > 64: one launch of the
                                   MFMA_KSPLIT kernel whose 64x64 tiles cover columns [0, 64 q),
                                   with workgroups after them that compute C's last w columns
-                                  on the vector ALUs (4-byte or 16-byte copies as for
-                                  MFMA_KSPLIT; no workspace). Chosen when those tiles fit one
-                                  per CU and the w columns would add a partial second wave of
-                                  tiles. Tile AUTO or 64. */
+                                  on the vector ALUs (operands as for MFMA_KSPLIT's 64x64
+                                  tiles; no workspace). Chosen when those tiles fit one per CU
+                                  and the w columns would add a partial second wave of tiles.
+                                  Tile AUTO or 64. */
 
 /* Output tile of the MFMA paths (rows x columns of C per workgroup). */
 #define FGR_TILE_AUTO 0

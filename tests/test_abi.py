@@ -245,7 +245,7 @@ def test_split_path_choices():
     assert sp(A0, B0, C0, 1023, 1025, 1036) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 64: a 12-column strip
     assert sp(A0, B0, C0, 2047, 2049, 2051) == fgr.PATH_MFMA_KSPLIT_TAIL  # 1056 of 64
     assert sp(A0, B0, C0, 256, 256, 256) == fgr.PATH_MFMA_KSPLIT  # 32x32
-    assert sp(A0, B0, C0, 300, 500, 261) == fgr.PATH_MFMA_KSPLIT  # unaligned, few tiles: 32x32, 4-byte copies
+    assert sp(A0, B0, C0, 300, 500, 261) == fgr.PATH_MFMA_KSPLIT  # unaligned, few tiles: 32x32, operands into registers
     assert sp(A0 + 4, B0 + 4, C0, 512, 4096, 512) == fgr.PATH_MFMA_KSPLIT  # misaligned A and B
     # N < 64: the register-staged and split kernels
     assert sp(A0, B0, C0, 2048, 60, 2048) == fgr.PATH_MFMA_VEC

@@ -96,8 +96,9 @@ def paths_for(M, N, K):
         # kernel's big-tile mode alone, partial big tiles included
         out.append((fgr.PATH_MFMA_DMA_TAIL, fgr.TILE_256))
     if N >= 64:
-        # tiles whose reduction is split over the waves (4-byte copies for
-        # unaligned rows; 128x128 tiles need 16-byte rows); and the tail form
+        # tiles whose reduction is split over the waves (operands into
+        # registers for unaligned rows; 128x128 tiles need 16-byte rows); and
+        # the tail form
         for tile in (fgr.TILE_64, fgr.TILE_32):
             out.append((fgr.PATH_MFMA_KSPLIT, tile))
         out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_64))
@@ -381,6 +382,47 @@ def test_strip_plan_forced_small_exact(shape):
     for offsets in [(0, 0, 0), (1, 1, 1)]:
         say(f"strip plan forced {shape} offsets {offsets}")
         assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_STRIP, 64, offsets=offsets), Cref, f"{shape} {offsets}")
+
+
+# The register-fed k-split tiles: 32x32 tiles, and 64x64 tiles whenever a
+# row of A, B or C is not 16-byte aligned, load their operands straight into
+# registers (16- and 8-byte loads at 4-byte alignment). Cases: one, two and
+# three columns (64x64 tiles take B two columns at a time; one column runs on
+# 32x32 tiles; with three the last lane's pair is shifted back by one), N not
+# a multiple of 8 (chunk 0 reaches below n = 0 and is zero-filled), partial
+# row and column tiles, split parts written to copies of C and to compact
+# slots (the tail tiles beside whole ones), the strip, and each operand's
+# pointer 4 bytes past a 16-byte boundary.
+KREG_CASES = [
+    ((64, 64, 2), fgr.PATH_MFMA_KSPLIT, 64, (0, 0, 0)),
+    ((65, 67, 3), fgr.PATH_MFMA_KSPLIT, 64, (0, 0, 0)),
+    ((100, 71, 1), fgr.PATH_MFMA_KSPLIT, 64, (0, 0, 0)),
+    ((100, 71, 1), fgr.PATH_MFMA_KSPLIT_TAIL, 64, (0, 0, 0)),
+    ((130, 1025, 129), fgr.PATH_MFMA_KSPLIT, 64, (0, 0, 0)),
+    ((130, 1025, 129), fgr.PATH_MFMA_SPLITK, 64, (0, 0, 0)),
+    ((130, 1025, 129), fgr.PATH_MFMA_SPLITK, 32, (0, 0, 0)),
+    ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64, (0, 0, 0)),
+    ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT, 64, (0, 0, 0)),
+    ((1023, 1025, 1027), fgr.PATH_MFMA_STRIP, 64, (0, 0, 0)),
+    ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 64, (1, 1, 1)),
+    ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 64, (1, 0, 0)),
+    ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 64, (0, 3, 0)),
+    ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 64, (0, 0, 2)),
+    ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 32, (0, 0, 0)),
+    ((96, 333, 97), fgr.PATH_MFMA_KSPLIT, 32, (0, 0, 0)),
+    ((96, 8192, 96), fgr.PATH_MFMA_SPLITK, 32, (1, 2, 3)),
+]
+
+
+@pytest.mark.parametrize("shape,path,tile,offsets", KREG_CASES,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_register_fed_ksplit_exact(shape, path, tile, offsets):
+    M, N, K = shape
+    A, B = synth.make_inputs(M, N, K, "integer", seed=23)
+    say(f"register-fed k-split {shape} path {path} tile {tile} offsets {offsets}: oracle")
+    Cref, _ = oracle.gemm(A, B)
+    say(f"register-fed k-split {shape} path {path} tile {tile} offsets {offsets}: GPU")
+    assert_exact(gpu_gemm(A, B, path, tile, offsets=offsets), Cref, f"{shape} path={path} tile={tile} {offsets}")
 
 
 @pytest.mark.parametrize("n,blocks", [(4, 1), (1 << 20, 256), ((1 << 20) + 36, 1000), (64, 512)])
