@@ -38,31 +38,51 @@
 
 namespace fgr {
 
-// BM x BM tiles (32 or 64); D chunks of operands in registers; STRIP as in
-// KsplitConfig (the column strip on the vector ALUs in the same launch).
+// BM x BM tiles (32, 64 or 128); D chunks of operands in registers; STRIP as
+// in KsplitConfig (the column strip on the vector ALUs in the same launch).
+// The four partial tiles pass through LDS four at a time, or two at a time at
+// BM = 128 (four would need 256 KB).
 template <int BM_, int D_, bool STRIP_ = false>
 struct KregConfig {
   static constexpr int BM = BM_, BN = BM_, BK = 8, D = D_;
   static constexpr bool kStrip = STRIP_;
-  static constexpr bool kPaddedA = false;  // reads the caller's A: lda = N, pad = 0
   static constexpr bool kReg = true;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRB = BM / 32, kCB = BN / 32;
   static constexpr int kSlices = kRB * kCB;  // MFMA blocks of a tile
   static constexpr int kPartial = BM * BN;   // floats of one wave's partial tile
-  static constexpr int kLds = kWaves * kPartial;
-  static_assert(BM == 32 || BM == 64, "32x32 or 64x64 tiles (four 128x128 partials exceed the LDS)");
+  static constexpr int kAtOnce = BM == 128 ? 2 : 4;  // partials in LDS at a time
+  static constexpr int kLds = kAtOnce * kPartial;
+  // a wave's share of the reduced tile: kPairs (MFMA block, accumulator group) pairs
+  static constexpr int kPairs = kSlices * 4 / kWaves;
+  static_assert(BM == 32 || BM == 64 || BM == 128, "32x32, 64x64 or 128x128 tiles");
   static_assert(D >= 2 && D <= 4, "two to four chunks in registers");
   static_assert(!STRIP_ || BM == 64, "the strip goes with 64x64 tiles");
   static_assert(kLds * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
+// The B columns of lane column li in the tile that starts at column k0, kcb
+// adjacent columns per lane (K >= kcb): the lane loads (and computes)
+// columns first .. first + kcb - 1, where first is its own first column k0 +
+// kcb li, or K - kcb where that would run past K; it stores those from its own
+// first column on, i.e. the last kcb - skip of them (none when all of its own
+// columns lie past K). The stored columns of the tile's lanes are then each
+// column of [k0, min(k0 + 32 kcb, K)) exactly once, and no load leaves [0, K).
+struct KregCols {
+  int first;
+  int skip;
+};
+__host__ __device__ __forceinline__ KregCols kreg_cols(int k0, int li, int K, int kcb) {
+  const int own = k0 + kcb * li;
+  const int first = own + kcb <= K ? own : K - kcb;
+  return {first, own - first};
+}
+
 template <class T>
 __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N, int K,
-    int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact, int nfull,
-    int /*lda*/, int /*pad*/) {
+    int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact, int nfull) {
   constexpr int BK = T::BK, BN = T::BN, D = T::D, kRB = T::kRB, kCB = T::kCB;
   __shared__ __attribute__((aligned(1024))) float red[T::kLds];
 
@@ -113,18 +133,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
     const int r = m0 + li + 32 * i;
     pa[i] = A + (int64_t)(r < M ? r : M - 1) * N + 4 * lg;
   }
-  // B: the lane's kCB columns from bc, read from bce = bc clamped so that
-  // the load stays inside the row (K >= kCB); a lane whose first column is
-  // the row's last (bc = K - 1 with kCB = 2) takes it from the load's second
-  // element. Columns past K are read but never stored.
-  const int bc = k0 + kCB * li;
-  const int bce = bc + kCB <= K ? bc : K - kCB;
-  const bool shifted = bc != bce;
+  // B: the lane's kCB adjacent columns (kreg_cols: at the right edge the kCB
+  // columns ending at K, of which it stores only its own)
+  const KregCols cols = kreg_cols(k0, li, K, kCB);
+  const int bce = cols.first;
+  const int shift = cols.skip;  // 0 but at the right edge
   const float* pb = B + (int64_t)(4 * lg) * K + bce;
   typedef typename FloatVec<kCB>::type BVec;
 
-  // a chunk's operands as loaded: B's stay raw vectors until the MFMAs take
-  // them (choosing the shifted element at load time would wait for the load)
+  // a chunk's operands, in the registers the MFMAs read
   struct Frag {
     float4 a[kRB];
     BVec b[4];
@@ -158,10 +175,25 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
       f.b[t] = ok ? v : BVec{};
     }
   };
-  // operand of column block j at reduction offset t
+  // Operand of column block j at reduction offset t. At 64x64, block 0's
+  // operand is passed through a VALU move first: with the MFMAs reading both
+  // B operands straight from the registers the loads wrote, two waves per
+  // SIMD ran about 30% slower (measured on MI355X, 2047^3: 183 against 141 us
+  // with the move; moving both operands: 142; reordering the MFMAs instead:
+  // 183). The same move cost 3-8% at 32x32 and 4% at 128x128 (one wave per
+  // SIMD), which go without it. The asm keeps the compiler from folding the
+  // move away.
   auto b_of = [&](const Frag& f, int j, int t) __attribute__((always_inline)) {
-    if constexpr (kCB == 2) return j == 0 ? (shifted ? f.b[t].y : f.b[t].x) : f.b[t].y;
-    else return f.b[t];
+    float v;
+    if constexpr (kCB == 1) {
+      v = f.b[t];
+    } else if constexpr (kCB == 2) {
+      v = j == 0 ? f.b[t].x : f.b[t].y;
+      if (j == 0) asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(v));
+    } else {
+      v = j == 0 ? f.b[t].x : j == 1 ? f.b[t].y : j == 2 ? f.b[t].z : f.b[t].w;
+    }
+    return v;
   };
 
   f32x16 acc[kRB][kCB];
@@ -181,12 +213,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
         }
   };
 
-  // The ring: chunk j's operands in f[j % D]. Chunks 0 .. D - 2 first; then
-  // each step issues chunk j + D - 1's loads and runs chunk j's MFMAs. Loads
-  // past the wave's last chunk repeat it (never used), so that every step
-  // issues the same loads and the compiler's wait counts stay exact (a load
-  // issued on some paths only makes it wait for every load in flight); the
-  // last nmine % D chunks, already loaded, run after the whole groups of D.
+  // The ring: the wave's chunk j has its operands in f[(j + D - lead) % D],
+  // lead = nmine % D. Chunks 0 .. D - 2 are loaded first; then each step
+  // issues chunk j + D - 1's loads and runs chunk j's MFMAs. The lead chunks
+  // run before the loop, so that the loop runs whole groups of D from f[0]:
+  // one loop and no chunk under a condition, so the accumulators stay in
+  // place. Loads past the wave's last chunk repeat it (never used), so that
+  // every step issues the same loads and the compiler's wait counts stay exact
+  // (a load issued on some paths only makes it wait for every load in flight).
   Frag f[D];
   const int j_last = nmine - 1;
   if (nmine > 0) {
@@ -196,46 +230,81 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
       const int n0 = chunk_n0(j < j_last ? j : j_last);
       return n0 > 0 ? n0 : 0;
     };
-    if (chunk_n0(0) < 0) load_first(f[0], chunk_n0(0));
-    else load(f[0], chunk_n0(0));
-    static_for<1, D - 1>([&](auto dc) { load(f[decltype(dc)::value], n0_of(decltype(dc)::value)); });
-    const int whole_end = nmine - nmine % D;
-    for (int c = 0; c < whole_end; c += D) {
-      static_for<0, D>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        load(f[(k + D - 1) % D], n0_of(c + k + D - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        mma(f[k]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    }
-    // the last nmine - whole_end < D chunks, nested so that every path
-    // updates the accumulators in place
-    auto rest = [&](auto kc, auto& self) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value;
-      if constexpr (k < D - 1) {
-        if (whole_end + k < nmine) {
-          mma(f[k]);
-          self(std::integral_constant<int, k + 1>{}, self);
-        }
-      }
+    auto step = [&](auto kc, int j) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;  // slot of chunk j
+      load(f[(k + D - 1) % D], n0_of(j + D - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f[k]);
+      __builtin_amdgcn_sched_barrier(0);
     };
-    rest(std::integral_constant<int, 0>{}, rest);
+    const int lead = nmine % D;
+    static_for<0, D>([&](auto rc) {
+      constexpr int R = decltype(rc)::value;
+      if (lead == R) {
+        constexpr int s0 = (D - R) % D;  // slot of chunk 0
+        if (chunk_n0(0) < 0) load_first(f[s0], chunk_n0(0));
+        else load(f[s0], chunk_n0(0));
+        static_for<1, D - 1>([&](auto dc) {
+          constexpr int d = decltype(dc)::value;
+          load(f[(s0 + d) % D], n0_of(d));
+        });
+        static_for<0, R>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          step(std::integral_constant<int, (s0 + k) % D>{}, k);
+        });
+      }
+    });
+    for (int c = lead; c < nmine; c += D)
+      static_for<0, D>([&](auto kc) { step(kc, c + decltype(kc)::value); });
   }
 
-  // The four partial tiles through LDS, each wave's at red + wave kPartial:
-  // slice s (MFMA block i = s / kCB, j = s % kCB, 16 accumulators of every
-  // lane) at s * 1024, lane-major as float4. Then each wave adds its share of
-  // the tile over the partials in wave order, ((p0 + p1) + p2) + p3.
-  float* mine = red + wave * T::kPartial;
+  // The four partial tiles are added in wave order, ((p0 + p1) + p2) + p3,
+  // through LDS: kAtOnce of them at a time, wave w's in slot w % kAtOnce
+  // (slice s = MFMA block i = s / kCB, j = s % kCB: 16 accumulators of every
+  // lane, at s * 1024, lane-major as float4). Each wave adds up its share of
+  // the tile, kPairs (slice, accumulator group q) pairs:
+  //   32x32: group q = w;
+  //   64x64: block row i = w / 2, both column blocks, groups 2 (w % 2) and
+  //          2 (w % 2) + 1 (pair u: j = u % 2, q = 2 (w % 2) + u / 2);
+  //   128x128: block row w, all four column blocks and groups (j = u % 4, q = u / 4).
+  auto pair_of = [&](int u, int& sl, int& q) __attribute__((always_inline)) {
+    if constexpr (T::BM == 32) {
+      sl = 0;
+      q = wave;
+    } else if constexpr (T::BM == 64) {
+      sl = 2 * (wave >> 1) + (u & 1);
+      q = 2 * (wave & 1) + (u >> 1);
+    } else {
+      sl = 4 * wave + (u & 3);
+      q = u >> 2;
+    }
+  };
+  float4 sum[T::kPairs];
 #pragma unroll
-  for (int s = 0; s < T::kSlices; ++s)
+  for (int ph = 0; ph < T::kWaves / T::kAtOnce; ++ph) {
+    if (ph > 0) __syncthreads();  // the last phase's partials have been read
+    if (wave / T::kAtOnce == ph) {
+      float* mine = red + (wave % T::kAtOnce) * T::kPartial;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(mine + s * 1024 + 256 * q + 4 * lane) =
-          make_float4(acc[s / kCB][s % kCB][4 * q], acc[s / kCB][s % kCB][4 * q + 1],
-                      acc[s / kCB][s % kCB][4 * q + 2], acc[s / kCB][s % kCB][4 * q + 3]);
-  __syncthreads();
+      for (int sl = 0; sl < T::kSlices; ++sl)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(mine + sl * 1024 + 256 * q + 4 * lane) =
+              make_float4(acc[sl / kCB][sl % kCB][4 * q], acc[sl / kCB][sl % kCB][4 * q + 1],
+                          acc[sl / kCB][sl % kCB][4 * q + 2], acc[sl / kCB][sl % kCB][4 * q + 3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < T::kPairs; ++u) {
+      int sl, q;
+      pair_of(u, sl, q);
+#pragma unroll
+      for (int p = 0; p < T::kAtOnce; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(red + p * T::kPartial + sl * 1024 + 256 * q + 4 * lane);
+        sum[u] = ph == 0 && p == 0 ? v : make_float4(sum[u].x + v.x, sum[u].y + v.y, sum[u].z + v.z, sum[u].w + v.w);
+      }
+    }
+  }
 
   float* Ct;
   uint32_t ldc;  // row stride; row * ldc is formed in 64 bits (K may pass 2^25)
@@ -249,47 +318,53 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
     Ct = W + (int64_t)part * M * K + (int64_t)m0 * K + k0;
     ldc = (uint32_t)K;
   }
-  // the partial sums of accumulator group q (4 accumulators) of slice s
-  auto sum4 = [&](int s, int q) __attribute__((always_inline)) {
-    float4 v = *reinterpret_cast<const float4*>(red + s * 1024 + 256 * q + 4 * lane);
-#pragma unroll
-    for (int p = 1; p < T::kWaves; ++p) {
-      const float4 w = *reinterpret_cast<const float4*>(red + p * T::kPartial + s * 1024 + 256 * q + 4 * lane);
-      v = make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
-    }
-    return v;
+  // Row r of accumulator group q, element k: 8 q + 4 lg + k of its block
+  // row; the lane's columns are bce .. bce + kCB - 1, of which it stores
+  // those from bc on (all of them, in one store, but at the right edge).
+  auto comp = [](const float4& v, int k) __attribute__((always_inline)) {
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
   };
-  if constexpr (kCB == 2) {
-    // 64x64: wave w takes block row i = w / 2, both column blocks, and
-    // accumulator groups q = 2 (w % 2), 2 (w % 2) + 1 (rows 16 (w % 2) ..
-    // + 15 of the block row's 32 in the MFMA's order): lane column li holds
-    // output columns 2 li and 2 li + 1, stored together
-    const int i = wave >> 1;
-    const int col = 2 * li;
+  const int col = bce - k0;  // negative (down to 1 - kCB) at the right edge
+  const bool whole_cols = shift == 0;
+  auto store_row = [&](int row, const float (&e)[kCB]) __attribute__((always_inline)) {
+    if (m0 + row >= M) return;
+    // signed: with col < 0 only the elements j >= shift, at or past the
+    // row's column 0 of the tile, are written
+    float* dst = Ct + (int64_t)row * (int64_t)ldc + col;
+    if (whole_cols) {
+      if constexpr (kCB == 4) store_dwords<float4>(dst, make_float4(e[0], e[1], e[2], e[3]));
+      else if constexpr (kCB == 2) store_dwords<float2>(dst, make_float2(e[0], e[1]));
+      else *dst = e[0];
+    } else {
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int q = 2 * (wave & 1) + qq;
-      const float4 v0 = sum4(2 * i, q), v1 = sum4(2 * i + 1, q);
-      const float e0[4] = {v0.x, v0.y, v0.z, v0.w}, e1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int row = i * 32 + 8 * q + 4 * lg + k;
-        if (m0 + row >= M) continue;
-        float* dst = Ct + (uint64_t)row * ldc + (uint32_t)col;
-        if (k0 + col + 1 < K) store_dwords<float2>(dst, make_float2(e0[k], e1[k]));
-        else if (k0 + col < K) *dst = e0[k];
-      }
+      for (int j = 0; j < kCB; ++j)
+        if (j >= shift) dst[j] = e[j];
     }
-  } else {
-    // 32x32: one slice; wave w stores accumulator group q = w
-    const int q = wave;
-    const float4 v = sum4(0, q);
-    const float e[4] = {v.x, v.y, v.z, v.w};
+  };
+  if constexpr (T::BM == 32) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int row = 8 * q + 4 * lg + k;
-      if (k0 + li < K && m0 + row < M) Ct[(uint64_t)row * ldc + (uint32_t)li] = e[k];
+      const float e[1] = {comp(sum[0], k)};
+      store_row(8 * wave + 4 * lg + k, e);
     }
+  } else if constexpr (T::BM == 64) {
+    const int i = wave >> 1;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e[2] = {comp(sum[2 * qq], k), comp(sum[2 * qq + 1], k)};
+        store_row(i * 32 + 8 * (2 * (wave & 1) + qq) + 4 * lg + k, e);
+      }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e[4] = {comp(sum[4 * q], k), comp(sum[4 * q + 1], k), comp(sum[4 * q + 2], k),
+                            comp(sum[4 * q + 3], k)};
+        store_row(32 * wave + 8 * q + 4 * lg + k, e);
+      }
   }
 }
 

@@ -1,27 +1,27 @@
-// FP32 MFMA GEMM for mid-size and small shapes: square BM x BM output tiles
-// (BM = 32, 64 or 128) whose reduction is split over the four waves of a
-// workgroup, each wave fed by its own direct global->LDS copies.
+// FP32 MFMA GEMM for mid-size and small shapes: output tiles whose reduction
+// is split over the four waves of a workgroup ("k-split"), each wave fed by
+// its own direct global->LDS copies.
 //
 // Between the few-tile shapes and the whole-device shapes of gemm_mfma_dma.hpp
 // (at least one 256x256 tile per CU) lie shapes such as 2048^3 or a
-// (1024, 6144, 4096) row shard: 64 tiles of 256x256, 256 of 128x128. Here each
-// wave of a workgroup computes the WHOLE tile (BM = 128: 16 MFMA blocks, 256
-// accumulators in AGPRs, as a wave of the direct-copy kernel) over every
-// fourth reduction chunk (wave w takes chunks w, w + 4, ...: the four waves
-// then copy neighbouring 32-byte pieces of the same 128-byte lines of A at
-// about the same time), so a 128x128 tile keeps a CU's four matrix cores as
-// busy as a 256x256 tile does; smaller tiles serve shapes with fewer outputs
-// still. Each wave copies its own A (BM x BK) and B (BK x BM) chunks
-// with global_load_lds (16 bytes per lane for 16-byte aligned rows, 4 bytes
-// otherwise) into its own ring of S LDS stages and waits only on its own
-// copies (s_waitcnt vmcnt): the main loop has no barrier. At the end the four
+// (1024, 6144, 4096) row shard: 64 tiles of 256x256, 256 of 128x128, 1024 of
+// 64x64. Each wave of a workgroup computes the WHOLE tile over every fourth
+// reduction chunk (wave w takes chunks w, w + 4, ...: the four waves then
+// read neighbouring 32-byte pieces of the same 128-byte lines of A at about
+// the same time), so a tile keeps a CU's four matrix cores busy with a
+// quarter of the outputs a whole-device tile needs. At the end the four
 // partial tiles are added in wave order (0, 1, 2, 3) through LDS, each wave
 // summing and storing its share of the tile: deterministic, no workspace, no
 // atomics.
 //
-// Here the 4-byte copies serve the 128x128 and 32x128 tiles only: 64x64 tiles
-// whose rows are not all 16-byte aligned, and every 32x32 tile, load their
-// operands straight into registers instead (gemm_mfma_kreg.hpp), which was
+// This file is the form whose operands go through LDS: each wave copies its
+// own A (BM x BK) and B (BK x BN) chunks with global_load_lds (16 bytes per
+// lane for 16-byte aligned rows, 4 bytes otherwise) into its own ring of S
+// LDS stages and waits only on its own copies (s_waitcnt vmcnt): the main
+// loop has no barrier. It serves 64x64 tiles whose rows of A, B and C are all
+// 16-byte aligned, and the skinny 32x128 tiles. 128x128 tiles, all 32x32
+// tiles and 64x64 tiles with unaligned rows load their operands straight into
+// registers instead (gemm_mfma_kreg.hpp, the same decomposition), which was
 // measured faster there.
 //
 // This keeps the output-parallel decomposition of the LeetGPU write-up
@@ -35,12 +35,6 @@
 // loads its first chunk through registers with zero fill (only wave 0's first
 // chunk is chunk 0). With N >= 64 every wave owns at least two chunks, so a
 // copy clamped to a wave's last chunk never reads chunk 0.
-//
-// lda is A's row stride (N, or more for a copy of A whose rows were padded
-// to 16-byte multiples) and pad the number of zero columns such a copy has in
-// front of each row: reduction index n of the kernel is then row n - pad of
-// B, and B's rows before 0 (all in chunk 0, read through registers) are taken
-// as zeros and never read.
 //
 // LDS: stage s of every wave is a separate LDS object per operand (so that the
 // compiler can tell a stage's reads from the copies into another), each holding
@@ -60,24 +54,16 @@
 
 namespace fgr {
 
-// BM x BN tiles (BN defaults to BM; BM = 32 with BN = 128 is the skinny
-// tile: few output rows, wide column blocks of B per workgroup). VA / VB:
-// 16-byte copies of A / B (their rows 16-byte aligned), else 4-byte copies;
-// VC: 128-bit stores of C (used by the 128 x 128 tile). BUF: the 4-byte
-// copies go through buffer loads (below), which hold a lane's source as two
-// 32-bit offsets instead of one 64-bit address per copy. STRIP: the launch
-// also holds, after the tiles' workgroups, workgroups that compute the narrow
+// BM x BN tiles: 64 x 64, or the skinny 32 x 128 tile (few output rows,
+// wide column blocks of B per workgroup). VA / VB: 16-byte copies of A / B
+// (their rows 16-byte aligned), else 4-byte copies. STRIP: the launch also
+// holds, after the tiles' workgroups, workgroups that compute the narrow
 // column strip [tiles_n * BN, K) of C on the vector ALUs (strip.hpp).
-template <int BM_, int S_, bool VA_, int BN_ = BM_, bool VB_ = VA_, bool VC_ = VB_, bool BUF_ = false,
-          bool STRIP_ = false>
+template <int BM_, int S_, bool VA_, int BN_ = BM_, bool VB_ = VA_, bool STRIP_ = false>
 struct KsplitConfig {
   static constexpr int BM = BM_, BN = BN_, BK = 8, S = S_;
   static constexpr bool kStrip = STRIP_;
-  static constexpr bool VA = VA_, VB = VB_, VC = VC_, VEC = VA_ && VB_ && VC_;
-  static constexpr bool BUFA = BUF_ && !VA_, BUFB = BUF_ && !VB_;
-  // only the form with aligned A and B through buffer loads reads a padded
-  // copy of A; every other form takes lda = N and pad = 0 as constants
-  static constexpr bool kPaddedA = VA_ && BUFB;
+  static constexpr bool VA = VA_, VB = VB_;
   static constexpr bool kReg = false;  // operands through LDS (gemm_mfma_kreg.hpp: through registers)
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
@@ -99,13 +85,11 @@ struct KsplitConfig {
   static constexpr int kSlicesPerObjB = kStageB / 1024;
   static constexpr int kSlicesPerWave = kSlices >= kWaves ? kSlices / kWaves : 1;
 
-  static_assert((BM == BN && (BM == 32 || BM == 64 || BM == 128)) || (BM == 32 && BN == 128),
-                "square tiles of 32, 64 or 128, or 32 x 128");
+  static_assert((BM == 64 && BN == 64) || (BM == 32 && BN == 128), "64 x 64 or 32 x 128 tiles");
   static_assert(kPieceA % kABlock == 0 && kPieceB % kBBlock == 0 && BN % kBCopyFloats == 0,
                 "copies cover whole pieces");
   static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");
-  static_assert(!BUFB || BN % 64 == 0, "buffer copies of B cover whole 64-column blocks");
-  static_assert(!STRIP_ || (BM == 64 && BN == 64 && !BUF_), "the strip goes with 64x64 tiles");
+  static_assert(!STRIP_ || (BM == 64 && BN == 64), "the strip goes with 64x64 tiles");
   static_assert(kCopies * (S - 2) <= 63, "the wait count fits the vmcnt field");
   static_assert(S * (kStageA + kStageB) * 4 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
   static_assert(kSlices <= S * kSlicesPerObjA && kSlices <= S * kSlicesPerObjB,
@@ -142,22 +126,6 @@ __device__ __forceinline__ void copy_to_lds_counted(const float* g, float* lds) 
     __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 4, 0, 0);
 }
 
-// The same 4-byte copy from a buffer: source = the buffer's base + soff +
-// voff bytes, with loads whose voff lies past the buffer's record count
-// returning zeros (the hardware's range check). Buffer word 3 as for every
-// gfx9-family GPU (raw buffer, 32-bit data).
-constexpr int kBufferWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, kBufferWord3);
-}
-__device__ __forceinline__ void copy4_buffer_to_lds_counted(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
-                                                            float* lds) {
-  uint32_t a = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)lds);
-  asm volatile("" : "+s"(a));
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(uintptr_t)a, 4, voff, soff, 0, 0);
-}
-
 // Scheduling hints for NO memory instructions among MFMAS MFMAs, when there
 // are MFMAs enough to interleave them one by one (else the default order).
 template <int MASK, int MFMAS, int NO>
@@ -172,12 +140,8 @@ template <class T>
 __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
     int K, int tiles_m, int tiles_n, int group, int parts, float* __restrict__ W, int first, int compact,
-    int nfull, int lda, int pad) {
+    int nfull) {
   constexpr int S = T::S, BK = T::BK, BN = T::BN;
-  if constexpr (!T::kPaddedA) {
-    lda = N;
-    pad = 0;
-  }
   __shared__ __attribute__((aligned(1024))) float As0[T::kStageA];
   __shared__ __attribute__((aligned(1024))) float As1[T::kStageA];
   __shared__ __attribute__((aligned(1024))) float As2[T::kStageA];
@@ -276,7 +240,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   auto a_ptr_of = [&](int j) __attribute__((always_inline)) {
     const int r = a_row_of(j);
     const int row = m0 + r < M ? m0 + r : M - 1;
-    return A + (int64_t)row * lda + a_col_of(j);
+    return A + (int64_t)row * N + a_col_of(j);
   };
   auto b_row_of = [&](int j) __attribute__((always_inline)) {
     return (j * T::kBBlock + lane * T::kBCopyFloats) / BN;
@@ -285,77 +249,31 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const int c = k0 + (j * T::kBBlock + lane * T::kBCopyFloats) % BN;
     return B + (int64_t)b_row_of(j) * K + (c < K ? c : K - T::kBCopyFloats);
   };
-  const float* a_src[T::BUFA ? 1 : T::kACopies];
-  int a_dst[T::kACopies], a_col[T::BUFA ? 1 : T::kACopies];
+  const float* a_src[T::kACopies];
+  int a_dst[T::kACopies], a_col[T::kACopies];
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
     a_dst[j] = piece_a + j * T::kABlock;
-    if constexpr (!T::BUFA) {
-      a_src[j] = a_ptr_of(j);
-      a_col[j] = a_col_of(j);
-    }
+    a_src[j] = a_ptr_of(j);
+    a_col[j] = a_col_of(j);
   }
   // In B, p is row p / BN, column p % BN (columns past K read the last column,
   // or the last quad with 16-byte copies; not stored).
-  const float* b_src[T::BUFB ? 1 : T::kBCopies];
+  const float* b_src[T::kBCopies];
   int b_dst[T::kBCopies];
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
     b_dst[j] = piece_b + j * T::kBBlock;
-    if constexpr (!T::BUFB) b_src[j] = b_ptr_of(j);
-  }
-  // Buffer copies (BUFA, BUFB; 4-byte copies, so that a lane covers one float
-  // per copy). A: copy j of a lane reads row 8 j + lane / 8 of the tile at
-  // column a_col_of(j), which depends only on the parity of j: a buffer per
-  // copy over the tile's rows [8 j, 8 j + 8) that exist, and the lane's
-  // offset a_voff[j & 1] inside it; rows past M lie past the buffer and read
-  // as zeros (not stored). B: a buffer per chunk from row n0 of B; copy j
-  // reads row j / (BN / 64) (a uniform offset) at the lane's column for
-  // j % (BN / 64), clamped to the last column. Offsets stay below 2^31 for
-  // N, K < 2^26.
-  int a_voff[2] = {0, 0};
-  if constexpr (T::BUFA) {
-    // the lane's row in its group of 8 and its column (even or odd copies)
-    a_voff[0] = (a_row_of(0) * lda + a_col_of(0)) * 4;
-    a_voff[1] = (a_row_of(0) * lda + a_col_of(1)) * 4;
-  }
-  // copy j's buffer: rows [m0 + 8 j, min(m0 + 8 j + 8, M)) of A (empty past M)
-  auto a_rsrc_of = [&](int j) __attribute__((always_inline)) {
-    const int first_row = m0 + 8 * j;
-    const int rows = first_row >= M ? 0 : (M - first_row < 8 ? M - first_row : 8);
-    return make_rsrc(A + (int64_t)(first_row < M ? first_row : 0) * lda, (uint32_t)rows * (uint32_t)lda * 4u);
-  };
-  constexpr int kBColBlocks = BN / 64;  // 4-byte copies of B per row of a chunk
-  int b_voff[T::BUFB ? kBColBlocks : 1];
-  if constexpr (T::BUFB) {
-#pragma unroll
-    for (int q = 0; q < kBColBlocks; ++q) {
-      const int c = k0 + 64 * q + lane;
-      b_voff[q] = (c < K ? c : K - 1) * 4;
-    }
+    b_src[j] = b_ptr_of(j);
   }
 
   auto copy_chunk = [&](int j, float* As, float* Bs) __attribute__((always_inline)) {
     const int n0 = chunk_n0(j);
-    if constexpr (T::BUFA) {
 #pragma unroll
-      for (int j = 0; j < T::kACopies; ++j)
-        copy4_buffer_to_lds_counted(a_rsrc_of(j), a_voff[j & 1], n0 * 4, As + a_dst[j]);
-    } else {
+    for (int j = 0; j < T::kACopies; ++j) copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
 #pragma unroll
-      for (int j = 0; j < T::kACopies; ++j)
-        copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
-    }
-    if constexpr (T::BUFB) {
-      const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + (int64_t)(n0 - pad) * K, (uint32_t)(BK * K) * 4u);
-#pragma unroll
-      for (int j = 0; j < T::kBCopies; ++j)
-        copy4_buffer_to_lds_counted(b_rsrc, b_voff[j % kBColBlocks], (j / kBColBlocks) * K * 4, Bs + b_dst[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < T::kBCopies; ++j)
-        copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)(n0 - pad) * K, Bs + b_dst[j]);
-    }
+    for (int j = 0; j < T::kBCopies; ++j)
+      copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
   };
 
   struct Frag {
@@ -418,23 +336,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     bool oka[T::kACopies], okb[T::kBCopies];
 #pragma unroll
     for (int j = 0; j < T::kACopies; ++j) {
-      const float* src;
-      if constexpr (T::BUFA) {
-        oka[j] = n0 + a_col_of(j) >= 0;
-        src = a_ptr_of(j);
-      } else {
-        oka[j] = n0 + a_col[j] >= 0;
-        src = a_src[j];
-      }
-      va[j] = *reinterpret_cast<const CopyTA*>(oka[j] ? src + n0 : A);
+      oka[j] = n0 + a_col[j] >= 0;
+      va[j] = *reinterpret_cast<const CopyTA*>(oka[j] ? a_src[j] + n0 : A);
     }
 #pragma unroll
     for (int j = 0; j < T::kBCopies; ++j) {
-      okb[j] = n0 + b_row_of(j) >= pad;
-      const float* src;
-      if constexpr (T::BUFB) src = b_ptr_of(j);
-      else src = b_src[j];
-      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? src + (int64_t)(n0 - pad) * K : B);
+      okb[j] = n0 + b_row_of(j) >= 0;
+      vb[j] = *reinterpret_cast<const CopyTB*>(okb[j] ? b_src[j] + (int64_t)n0 * K : B);
     }
     static_for<1, S - 1>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
@@ -506,7 +414,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
   // or of B (waves 1, 3). Slice t of a partial (MFMA block i = t / kCB,
   // j = t % kCB: 16 accumulators of every lane) lives in object
   // t / kSlicesPerObjA (or B), lane-major as float4. Wave w sums and stores slices
-  // [w kSlicesPerWave, (w + 1) kSlicesPerWave) (at BM = 128: block row w).
+  // [w kSlicesPerWave, (w + 1) kSlicesPerWave).
   constexpr int kSPW = T::kSlicesPerWave;
   auto slice_ptr = [&](auto tc, bool use_b) __attribute__((always_inline)) -> float* {
     constexpr int t = decltype(tc)::value;
@@ -568,29 +476,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     Ct = W + (int64_t)part * M * K + (int64_t)m0 * K + k0;
     ldc = (uint32_t)K;
   }
-  if constexpr (T::VC && kSPW == T::kCB && T::kCB == 4) {
-    // a whole block row: 4 adjacent columns per lane and row
-    const int col = 4 * li;
-    const bool col_ok = k0 + col < K;
+#pragma unroll
+  for (int u = 0; u < kSPW; ++u) {
+    const int t = wave * kSPW + u;
+    const int i = t / T::kCB, j = t % T::kCB;
+    const int col = T::kCB * li + j;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int row = wave * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
-      if (col_ok && m0 + row < M) {
-        float* dst = Ct + (uint64_t)row * ldc + (uint32_t)col;
-        *reinterpret_cast<float4*>(dst) = make_float4(sum[0][rr], sum[1][rr], sum[2][rr], sum[3][rr]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < kSPW; ++u) {
-      const int t = wave * kSPW + u;
-      const int i = t / T::kCB, j = t % T::kCB;
-      const int col = T::kCB * li + j;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
-        if (k0 + col < K && m0 + row < M) Ct[(uint64_t)row * ldc + (uint32_t)col] = sum[u][rr];
-      }
+      const int row = i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
+      if (k0 + col < K && m0 + row < M) Ct[(uint64_t)row * ldc + (uint32_t)col] = sum[u][rr];
     }
   }
 }

@@ -96,24 +96,4 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_tiles_kernel(const floa
   C[(int64_t)row * K + col] = acc;
 }
 
-// A copy of A (M x N, row-major) in rows of lda floats (lda a multiple of 4,
-// lda - N < 4) with the lda - N padding columns in FRONT: Ap[m][lda - N + n]
-// = A[m][n], Ap[m][c] = 0 for c < lda - N. The k-split kernel's reduction
-// chunks are aligned to the end of the reduction, so with the padding in
-// front every chunk of Ap starts 16 bytes aligned. One float4 of Ap per
-// thread (4-byte reads, 128-bit writes).
-__global__ __launch_bounds__(256) void pack_rows_kernel(const float* __restrict__ A, float* __restrict__ Ap, int M,
-                                                        int N, int lda) {
-  const int qpr = lda / 4;  // float4 per row of Ap
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (q >= (int64_t)M * qpr) return;
-  const int m = (int)(q / qpr);
-  const int c0 = 4 * (int)(q % qpr) - (lda - N);  // column of A for the float4's first element
-  const float* a = A + (int64_t)m * N;
-  float v[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = c0 + e >= 0 ? a[c0 + e] : 0.f;
-  *reinterpret_cast<float4*>(Ap + (int64_t)m * lda + (c0 + lda - N)) = make_float4(v[0], v[1], v[2], v[3]);
-}
-
 }  // namespace fgr

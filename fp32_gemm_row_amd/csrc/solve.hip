@@ -124,27 +124,10 @@ Rows rows_of(const float* A, const float* B, const float* C, int N, int K) {
   return Rows::kNone;
 }
 
-// 128x128 k-split tiles: 16-byte copies of both operands, or of one with the
-// other's 4-byte copies through buffer loads (a 64-bit address per 4-byte copy
-// pushed the kernel past 256 VGPRs, 27 spilled; the buffers' offsets stay
-// below 2^31 for 8 K 4 or 8 N 4 bytes). With A on 4-byte copies C must take
-// 128-bit stores too (the epilogue that fits the registers). Measured on
-// MI355X against 64x64 tiles (us per call): 2048 x 2048 x 2047 161.9 ->
-// 151.4, 1024 x 6144 x 4095 476.4 -> 426.0, 1024 x 6143 x 4096 469.6 ->
-// 423.7, 2047 x 2051 x 2048 162.4 -> 150.5; tails within 2% (2176 x 1028 x
-// 2047 97.4 -> 100.0). Both operands on 4-byte copies would keep more copies
-// in flight than vmcnt counts, so with neither operand's rows aligned A is
-// first copied into padded rows (pack_a), a workspace of M x lda floats.
-constexpr int64_t kBufferOffsetLimit = int64_t(1) << 31;
-bool ksplit128_ok(const float* A, const float* B, const float* C, int N, int K) {
-  switch (rows_of(A, B, C, N, K)) {
-    case Rows::kAll: return true;
-    case Rows::kAOnly: return int64_t(8) * K * 4 < kBufferOffsetLimit;
-    case Rows::kBOnly: return int64_t(8) * N * 4 < kBufferOffsetLimit && K % 4 == 0 && aligned(C, 16);
-    case Rows::kNone: return int64_t(8) * K * 4 < kBufferOffsetLimit && N < INT_MAX - 3;  // A packed first
-  }
-  return false;
-}
+// 128x128 k-split tiles load their operands straight into registers, four
+// columns of B per lane (gemm_mfma_kreg.hpp): they need K >= 4 and no
+// alignment beyond 4 bytes.
+bool ksplit128_ok(int K) { return K >= 4; }
 
 // Direct global->LDS copies need at least four 16-deep reduction chunks (the
 // copies that run past the last chunk re-read it, and must never reach the
@@ -357,6 +340,14 @@ bool strip_plan_ok(int M, int N, int K, int cus) {
 // Reductions shorter than this (with at least one 64x64 tile per CU) take
 // register-staged 64x64 tiles (128x128 for unaligned rows with many tiles).
 constexpr int kShortReduction = 104;
+// With whole-device shapes whose B rows are not 16-byte aligned (the
+// direct-copy kernel would copy B 4 bytes at a time) the register-staged
+// tiles win up to this reduction length.
+constexpr int kShortReductionNarrowB = 384;
+// With neither operand's rows aligned, whole-device shapes from this
+// reduction length on take 128x128 k-split tiles instead of direct copies
+// (8191 x N x 8191, us: N = 511 613 vs 596, 767 842 vs 849, 1023 1069 vs 1092).
+constexpr int kKsplitUnalignedMinN = 768;
 
 // Kernel choice by the number of output tiles the shape makes at each tile
 // size, relative to the CU count (measured on MI355X; see the design notes):
@@ -380,34 +371,50 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
   const int64_t t128 = cdiv(M, 128) * cdiv(K, 128);
   const int64_t t64 = cdiv(M, 64) * cdiv(K, 64);
   const bool vec = mfma_vec_ok(A, B, C, N, K);
-  if (N < kShortReduction && t64 >= cus && (vec || N < 64)) {
+  const Rows rows = rows_of(A, B, C, N, K);
+  const bool narrow_b = rows == Rows::kAOnly || rows == Rows::kNone;
+  if (t64 >= cus && (N < kShortReduction || (narrow_b && t256 >= cus && N < kShortReductionNarrowB))) {
     // A short reduction over many tiles: the time goes to writing C. Small
     // register-staged tiles keep several workgroups per CU, so that one's
     // stores overlap another's loads and MFMAs (measured, 8192 x N x 8192:
     // 64x64 tiles 46 us at N = 16 vs 77 us with 256x256; 100 vs 112 us with
-    // the direct-copy kernel at N = 64; equal at N = 96; 4% slower at N = 112).
+    // the direct-copy kernel at N = 64; equal at N = 96; 4% slower at N =
+    // 112). Unaligned rows take 32-bit loads; against direct copies that move
+    // B 4 bytes at a time they win up to N = 384 (us: 8191 x 65 x 8191 121 vs
+    // 177, 8191 x 255 x 8191 317 vs 346, 8191 x 383 x 8191 463 vs 475, 8191 x
+    // 128 x 8191 170 vs 216; but 8191 x 511 x 8191 611 vs 596; with B's rows
+    // aligned 8192 x 129 x 8192 188 vs 180).
     if (vec) return {FGR_PATH_MFMA_VEC, FGR_TILE_64};
     return {FGR_PATH_MFMA_SCALAR, t128 >= 4 * cus ? FGR_TILE_128 : FGR_TILE_64};
   }
-  if (t256 >= cus && mfma_dma_ok(N)) {
+  // Whole-device shapes take the direct-copy kernel, unless neither operand's
+  // rows are 16-byte aligned and the reduction is long: its 4-byte copies then
+  // lose to the k-split kernel's 128x128 tiles, which load at any alignment
+  // (measured on MI355X, us per call: 8191 x 6143 x 4095 3261 vs 2864, 4095 x
+  // 4097 x 4099 1143 vs 1022, 8191 x 1023 x 8191 1092 vs 1069; but 8191 x 511
+  // x 8191 596 vs 613; with one operand aligned they are within 1%: 4096 x
+  // 4096 x 4095 958 vs 964, 6000 x 1001 x 6000 599 vs 602).
+  if (t256 >= cus && mfma_dma_ok(N) &&
+      (rows != Rows::kNone || N < kKsplitUnalignedMinN || !ksplit128_ok(K))) {
     // a last, partial wave of at most tail_tiles(cus) tiles goes to the split kernel
     const int64_t rem = t256 % cus;
     if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
     return {FGR_PATH_MFMA_DMA, FGR_TILE_256};
   }
   if (N >= 64) {
-    // Fewer 256x256 tiles than CUs: tiles whose reduction is split over the
-    // four waves of a workgroup (k-split), the largest that still gives every
-    // CU a tile; a last partial wave of up to half the CUs is spread over
-    // every CU (launch_ksplit_tail).
-    // (With A to be packed first, 128x128 tiles only where their last wave
-    // is full or a tail of at most half the CUs: measured on MI355X, us per
-    // call, 64x64 tiles -> packed 128x128: 2047 x 8191 x 2047 712 -> 586,
-    // 3001^3 591 -> 536, 4095 x 2049 x 2051 383 -> 354, 2047^3 199 -> 190;
-    // but 2500^3, 400 tiles of 128, 355 -> 373.)
+    // Fewer 256x256 tiles than CUs (or, above, unaligned rows): tiles whose
+    // reduction is split over the four waves of a workgroup (k-split), the
+    // largest that still gives every CU a tile; a last partial wave of up to
+    // half the CUs is spread over every CU (launch_ksplit_tail). 128x128
+    // tiles where they make whole waves, three waves or more, or a last wave
+    // more than three quarters full; else 64x64, whose two workgroups per CU
+    // even out a partial wave better (measured on MI355X, us per call, 128x128
+    // vs 64x64 tiles: 2047^3 128 vs 138, 1024 x 6144 x 4095 358 vs 395,
+    // 3584^3 675 vs 694, 2816^3 336 vs 354; but 2304^3 237 vs 194, 2560^3 305
+    // vs 261, 2303 x 2305 x 2307 269 vs 206, 4095 x 2049 x 2051 296 vs 285,
+    // 3072^3 432 vs 440).
     const int64_t rem128 = t128 % cus;
-    const bool packed = rows_of(A, B, C, N, K) == Rows::kNone;
-    if (ksplit128_ok(A, B, C, N, K) && t128 >= cus && (!packed || rem128 <= ksplit_tail_tiles(cus))) {
+    if (ksplit128_ok(K) && t128 >= cus && (rem128 == 0 || t128 >= 3 * cus || 4 * rem128 > 3 * cus)) {
       if (rem128 != 0 && rem128 <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
     }
@@ -426,8 +433,7 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     // 400 x 1000 x 401 10.0 vs 14.8 us, 512 x 4095 x 512 30.8 vs 50.9)
     const SplitPlan sp = splitk_plan(M, N, K, cus);
     if (sp.parts >= 2) {
-      if (rows_of(A, B, C, N, K) != Rows::kNone && ksplit128_ok(A, B, C, N, K) &&
-          4 * cdiv(M, 128) * cdiv(K, 128) == t64 &&
+      if (ksplit128_ok(K) && 4 * cdiv(M, 128) * cdiv(K, 128) == t64 &&
           N / splitk_plan_tile(FGR_TILE_128, M, N, K, cus).parts >= kSplitk128MinPart)
         return {FGR_PATH_MFMA_SPLITK, FGR_TILE_128};
       return {FGR_PATH_MFMA_SPLITK, sp.tile};
@@ -512,11 +518,9 @@ int launch(const void* kernel, int64_t blocks, int threads, void** args, hipStre
   return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
 }
 
-// Workspace: device memory a call needs beyond A, B and C. Two kinds: the
-// partial tiles (or rows) of a reduction split across workgroups (parts x M x
-// K floats, or parts x tiles x tile^2 in compact slots), and the padded copy
-// of A of the 128x128 k-split tiles when neither A's nor B's rows are 16-byte
-// aligned (M x lda floats, see pack_a). A workspace is either the caller's
+// Workspace: device memory a call needs beyond A, B and C: the partial tiles
+// (or rows) of a reduction split across workgroups (parts x M x K floats, or
+// parts x tiles x tile^2 in compact slots). A workspace is either the caller's
 // stream's cached one (below), borrowed with the cache lock held until the
 // call's last kernel is enqueued, or a stream-ordered allocation from a
 // per-device pool on the caller's stream, given back with hipFreeAsync on it
@@ -665,11 +669,9 @@ bool cached_workspace(Workspace& ws, size_t bytes, hipStream_t s) {
 }
 
 // A workspace of `floats` floats for this call on `s`: the stream's cached one
-// when `cacheable` (one per call at a time: the cache lock is held while it is
-// borrowed), else a stream-ordered allocation freed after the call's last
-// kernel. A's padded copy is never cached, so that a call may hold it and a
-// split workspace together.
-int alloc_floats(Workspace& ws, size_t floats, hipStream_t s, bool cacheable = true) {
+// (one per call at a time: the cache lock is held while it is borrowed), else
+// a stream-ordered allocation freed after the call's last kernel.
+int alloc_floats(Workspace& ws, size_t floats, hipStream_t s) {
   const size_t bytes = floats * sizeof(float);
   if (t_scratch) {  // fgr_solve_noalloc: a piece of the scratch array
     ScratchCall& sc = *t_scratch;
@@ -682,7 +684,7 @@ int alloc_floats(Workspace& ws, size_t floats, hipStream_t s, bool cacheable = t
   }
   const long long limit = g_ws_limit.load(std::memory_order_relaxed);
   if (limit >= 0 && bytes > (unsigned long long)limit) return FGR_ERR_LAUNCH;  // as a failed allocation
-  if (cacheable && cached_workspace(ws, bytes, s)) return FGR_OK;
+  if (cached_workspace(ws, bytes, s)) return FGR_OK;
   ws.s = s;
   if (pool_alloc(&ws.w, bytes, s) != hipSuccess) {
     ws.w = nullptr;
@@ -835,13 +837,12 @@ int launch_dma_tail(const float* A, const float* B, float* C, int M, int N, int 
 // strip's workgroups (four rows of A each) after them.
 template <class Cfg>
 int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, int K, int64_t count, hipStream_t s,
-                      int parts, float* W, int first, int compact, int nfull, int lda, int pad) {
-  if (!Cfg::kPaddedA && (lda != N || pad != 0)) return FGR_ERR_BAD_PATH;
+                      int parts, float* W, int first, int compact, int nfull) {
   int tiles_m = (int)cdiv(M, Cfg::BM);
   int tiles_n = (int)cdiv(Cfg::kStrip ? K / Cfg::BN * Cfg::BN : K, Cfg::BN);
   int group = kTileGroup;
   void* args[] = {&A,     &B,    &C,     &M,       &N,     &K,     &tiles_m, &tiles_n, &group,
-                  &parts, &W,    &first, &compact, &nfull, &lda,   &pad};
+                  &parts, &W,    &first, &compact, &nfull};
   const int64_t strip_blocks = Cfg::kStrip ? cdiv(M, fgr::kStripRows) : 0;
   const void* kernel;
   if constexpr (Cfg::kReg) kernel = reinterpret_cast<const void*>(&fgr::gemm_mfma_kreg_kernel<Cfg>);
@@ -852,115 +853,61 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
 }
 
 // k-split configurations by tile and by the row alignment of the product.
-// 64x64 tiles with 16-byte rows of A, B and C: direct 16-byte copies through
-// LDS (KsplitConfig); other 64x64 and all 32x32 tiles: operands loaded
-// straight into registers at any 4-byte alignment (KregConfig; 64x64 needs K
-// >= 2, so K = 1 takes 32x32). 128x128 and 32x128 tiles: 16-byte copies of
-// each operand whose rows allow them, 4-byte copies of the other (128x128:
-// through buffer loads, and one operand at least aligned: ksplit128_ok).
+// 64x64 tiles with 16-byte rows of A, B and C, and the skinny 32x128 tiles:
+// direct copies through LDS (KsplitConfig; 32x128 with 4-byte copies of an
+// operand whose rows are not 16-byte aligned). All other tiles (128x128,
+// 32x32, 64x64 with unaligned rows): operands loaded straight into registers
+// at any 4-byte alignment (KregConfig; 128x128 needs K >= 4 and 64x64 K >= 2,
+// run() maps K = 1 to 32x32).
 constexpr int kKregDepth = 2;  // chunks of operands in registers: deeper rings measured slower
 
 template <int BM, int BN = BM>
 int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
-                       hipStream_t s, int parts, float* W, int first, int compact, int nfull, int lda,
-                       int pad) {
-  if constexpr (BM == BN && BM <= 64) {
+                       hipStream_t s, int parts, float* W, int first, int compact, int nfull) {
+  if constexpr (BM == BN) {
     if (BM == 64 && rows == Rows::kAll)
       return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                               compact, nfull, lda, pad);
-    if (K < BM / 32) return FGR_ERR_BAD_PATH;  // run() maps K = 1 to 32x32 tiles
-    return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                             compact, nfull, lda, pad);
-  } else if constexpr (BM == 128) {
-    switch (rows) {
-      case Rows::kAll:
-        return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                  compact, nfull, lda, pad);
-      case Rows::kAOnly:
-        return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, true, 128, false, false, true>>(
-            A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
-      case Rows::kBOnly:
-        if (K % 4 == 0 && aligned(C, 16))
-          return launch_ksplit_cfg<fgr::KsplitConfig<128, 4, false, 128, true, true, true>>(
-              A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
-        return FGR_ERR_BAD_PATH;
-      default: return FGR_ERR_BAD_PATH;  // pack_a first
-    }
+                                                               compact, nfull);
+    if (K < BM / 32) return FGR_ERR_BAD_PATH;
+    return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth>>(A, B, C, M, N, K, count, s, parts, W, first, compact,
+                                                             nfull);
   } else {
     switch (rows) {
       case Rows::kAll:
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                      compact, nfull, lda, pad);
+                                                                      compact, nfull);
       case Rows::kAOnly:
-        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false, false>>(
-            A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN, false>>(A, B, C, M, N, K, count, s, parts, W,
+                                                                             first, compact, nfull);
       case Rows::kBOnly:
-        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true, false>>(
-            A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN, true>>(A, B, C, M, N, K, count, s, parts, W,
+                                                                             first, compact, nfull);
       default:
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, false, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                                       compact, nfull, lda, pad);
+                                                                       compact, nfull);
     }
   }
 }
 
-// A as the k-split kernels read it: the caller's rows (lda = N, pad = 0), or
-// a copy whose rows are N rounded up to a multiple of 4 floats with pad = lda
-// - N zeros in front of each (pack_a). The kernels then run over lda
-// reduction indices; index n is row n - pad of B, and B's rows before 0 (all
-// in the first chunk, which is read through registers) count as zeros and are
-// never read.
-struct AOperand {
-  const float* p;
-  int lda;
-  int pad;
-};
-
-constexpr int kNoWorkspace = 1;  // pack_a: the copy's workspace could not be had
-
-// 128x128 k-split tiles need 16-byte rows of A or of B (ksplit128_ok). When
-// neither has them, A is copied once per call into padded rows
-// (pack_rows_kernel) held in `ws` (M x lda floats) until the call's last
-// kernel is enqueued; the aligned-A form with B's 4-byte copies through buffer
-// loads then reads the copy. Returns FGR_OK with `a` set, kNoWorkspace with
-// nothing enqueued when the workspace cannot be had (the caller then takes
-// 64x64 tiles, which need no copy), or a launch error.
-int pack_a(Workspace& ws, AOperand& a, const float* A, int M, int N, hipStream_t s) {
-  int lda = (N + 3) & ~3;
-  if (alloc_floats(ws, (size_t)M * (size_t)lda, s, /*cacheable=*/false) != FGR_OK) return kNoWorkspace;
-  float* Ap = ws.w;
-  int m = M, n = N;
-  void* args[] = {&A, &Ap, &m, &n, &lda};
-  const int rc = launch(reinterpret_cast<const void*>(&fgr::pack_rows_kernel), cdiv((int64_t)M * (lda / 4), 256),
-                        256, args, s);
-  if (rc != FGR_OK) return rc;
-  a = {Ap, lda, lda - N};
-  return FGR_OK;
-}
-
-// The k-split kernel with tile x tile tiles over tiles [first, first + count)
-// of the grouped order (count < 0: all of them), reading A as `a` (its lda
-// reduction indices); 16-byte copies of each operand whose rows allow them.
-// parts > 1: each tile's reduction also split over `parts` workgroups writing
-// partial tiles to W (at their place in copies of C, or in compact per-tile
-// slots). nfull > 0: the same grid first runs whole tiles [first, first +
-// nfull) into C, and the count split tiles follow them.
-int launch_ksplit(int tile, const AOperand& a, const float* B, float* C, int M, int K, int64_t count,
+// The k-split kernels with tile x tile tiles over tiles [first, first + count)
+// of the grouped order (count < 0: all of them). parts > 1: each tile's
+// reduction also split over `parts` workgroups writing partial tiles to W (at
+// their place in copies of C, or in compact per-tile slots). nfull > 0: the
+// same grid first runs whole tiles [first, first + nfull) into C, and the
+// count split tiles follow them.
+int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
                   hipStream_t s, int parts = 1, float* W = nullptr, int first = 0, int compact = 0,
                   int nfull = 0) {
-  const Rows rows = rows_of(a.p, B, C, a.lda, K);
-  const float* A = a.p;
-  const int N = a.lda, lda = a.lda, pad = a.pad;
-  if (tile == FGR_TILE_128 && rows == Rows::kNone) return FGR_ERR_BAD_PATH;  // pack_a first
+  const Rows rows = rows_of(A, B, C, N, K);
   switch (tile) {
     case FGR_TILE_128:
-      return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
+      return launch_ksplit_rows<128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
     case FGR_TILE_64:
-      return launch_ksplit_rows<64>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
+      return launch_ksplit_rows<64>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
     case FGR_TILE_32:
-      return launch_ksplit_rows<32>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
+      return launch_ksplit_rows<32>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
     case FGR_TILE_32X128:
-      return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull, lda, pad);
+      return launch_ksplit_rows<32, 128>(rows, A, B, C, M, N, K, count, s, parts, W, first, compact, nfull);
     default: return FGR_ERR_BAD_PATH;
   }
 }
@@ -972,10 +919,9 @@ int launch_ksplit(int tile, const AOperand& a, const float* B, float* C, int M, 
 // and C allow them, else operands straight into registers.
 int launch_strip(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
   if (rows_of(A, B, C, N, K) == Rows::kAll)
-    return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true, 64, true, false, false, true>>(
-        A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0, N, 0);
-  return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0,
-                                                                  N, 0);
+    return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true, 64, true, true>>(A, B, C, M, N, K, -1, s, 1, nullptr,
+                                                                            0, 0, 0);
+  return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0);
 }
 
 // Sum of compact partial tiles (tiles [first, first + count) of the grouped
@@ -1004,14 +950,14 @@ bool vec4_rows(const float* C, int M, int K) { return ((int64_t)M * K) % 4 == 0 
 // tiles into a stream-ordered workspace, then added in part order (two parts
 // where no longer parts fit the estimate's limits). Without a
 // workspace (allocation failed) the tiles keep their whole reduction.
-int launch_ksplit_parts(int tile, const AOperand& a, const float* B, float* C, int M, int N, int K, int cus,
+int launch_ksplit_parts(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
                         hipStream_t s) {
   int parts = tile == FGR_TILE_32X128 ? skinny_parts(M, N, K, cus) : splitk_plan_tile(tile, M, N, K, cus).parts;
   if (parts < 2) parts = 2;  // N >= 128 gives 8 chunks per part
   Workspace ws;
   if (alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) != FGR_OK)
-    return launch_ksplit(tile, a, B, C, M, K, -1, s);
-  const int rc = launch_ksplit(tile, a, B, C, M, K, -1, s, parts, ws.w);
+    return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
+  const int rc = launch_ksplit(tile, A, B, C, M, N, K, -1, s, parts, ws.w);
   if (rc != FGR_OK) return rc;
   return launch_reduce_parts(ws.w, C, M, K, parts, vec4_rows(C, M, K), s);
 }
@@ -1022,7 +968,7 @@ constexpr int kMixedTailMinN = 1024;
 // Whole waves of tile x tile tiles on the k-split kernel, the last partial
 // wave's tiles cut into smaller split-reduction tiles (as launch_dma_tail) or,
 // for long reductions, their reduction split across workgroups.
-int launch_ksplit_tail(int tile, const float* A, const AOperand& a, const float* B, float* C, int M, int N, int K,
+int launch_ksplit_tail(int tile, const float* A, const float* B, float* C, int M, int N, int K,
                        int cus, hipStream_t s) {
   const int64_t tiles = cdiv(M, tile) * cdiv(K, tile);
   const int64_t full = tiles / cus * cus;
@@ -1041,13 +987,13 @@ int launch_ksplit_tail(int tile, const float* A, const AOperand& a, const float*
   if (tile == FGR_TILE_64 && N >= kMixedTailMinN && full > 0 && rem > 0 && mixed_parts >= 2) {
     Workspace ws;
     if (alloc_floats(ws, (size_t)mixed_parts * (size_t)rem * tile * tile, s) == FGR_OK) {
-      const int rc = launch_ksplit(tile, a, B, C, M, K, rem, s, mixed_parts, ws.w, 0, 1, (int)full);
+      const int rc = launch_ksplit(tile, A, B, C, M, N, K, rem, s, mixed_parts, ws.w, 0, 1, (int)full);
       if (rc != FGR_OK) return rc;
       return launch_reduce_tiles(ws.w, C, M, K, tile, mixed_parts, (int)full, (int)rem, s);
     }
   }
   if (full > 0) {
-    const int rc = launch_ksplit(tile, a, B, C, M, K, full, s);
+    const int rc = launch_ksplit(tile, A, B, C, M, N, K, full, s);
     if (rc != FGR_OK || rem == 0) return rc;
   }
   // With a long reduction the tail tiles' reduction is split over up to
@@ -1061,7 +1007,7 @@ int launch_ksplit_tail(int tile, const float* A, const AOperand& a, const float*
   if (parts >= 2 && rem <= 65535) {
     Workspace ws;
     if (alloc_floats(ws, (size_t)parts * (size_t)rem * tile * tile, s) == FGR_OK) {
-      const int rc = launch_ksplit(tile, a, B, C, M, K, rem, s, parts, ws.w, (int)full, 1);
+      const int rc = launch_ksplit(tile, A, B, C, M, N, K, rem, s, parts, ws.w, (int)full, 1);
       if (rc != FGR_OK) return rc;
       return launch_reduce_tiles(ws.w, C, M, K, tile, parts, (int)full, (int)rem, s);
     }
@@ -1151,16 +1097,14 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
-      // N >= 64; tiles of 128 (with neither A's nor B's rows 16-byte aligned, A is first copied
-      // into padded rows: pack_a) or 64, and 32 or 32x128 without the tail form
-      if (N < 64 || (tile == FGR_TILE_128 && !ksplit128_ok(A, B, C, N, K)) || tile == FGR_TILE_256 ||
+      // N >= 64; tiles of 128 (K >= 4) or 64, and 32 or 32x128 without the tail form
+      if (N < 64 || (tile == FGR_TILE_128 && !ksplit128_ok(K)) || tile == FGR_TILE_256 ||
           ((tile == FGR_TILE_32 || tile == FGR_TILE_32X128) && path == FGR_PATH_MFMA_KSPLIT_TAIL))
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_SPLITK:
-      // N >= 128 (two parts of at least 8 chunks); tiles of 128 (A copied as above when needed), 64
-      // or 32
-      if (N < 128 || (tile == FGR_TILE_128 && !ksplit128_ok(A, B, C, N, K)) || tile == FGR_TILE_256)
+      // N >= 128 (two parts of at least 8 chunks); tiles of 128 (K >= 4), 64 or 32
+      if (N < 128 || (tile == FGR_TILE_128 && !ksplit128_ok(K)) || tile == FGR_TILE_256)
         return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_VALU:
@@ -1236,7 +1180,9 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
   t_scratch = &call;
   rc = dispatch(A, B, C, M, N, K, s, cus, path, tile);  // dry: count the bytes
   if (rc != FGR_OK) return rc;
-  if (call.used > kScratchBytes) return FGR_ERR_SCRATCH;  // nothing enqueued
+  const long long limit = g_ws_limit.load(std::memory_order_relaxed);
+  if (call.used > kScratchBytes || (limit >= 0 && call.used > (unsigned long long)limit))
+    return FGR_ERR_SCRATCH;  // nothing enqueued
   call = ScratchCall{false, base, 0};
   return dispatch(A, B, C, M, N, K, s, cus, path, tile);
 }
@@ -1249,18 +1195,10 @@ int dispatch(const float* A, const float* B, float* C, int M, int N, int K, hipS
     case FGR_PATH_MFMA_DMA_TAIL: return launch_dma_tail(A, B, C, M, N, K, cus, s);
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
-    case FGR_PATH_MFMA_SPLITK: {
-      AOperand a{A, N, 0};
-      Workspace packed;  // A's padded copy, when 128x128 tiles need one
-      if (tile == FGR_TILE_128 && rows_of(A, B, C, N, K) == Rows::kNone) {
-        const int prc = pack_a(packed, a, A, M, N, s);
-        if (prc == kNoWorkspace) tile = FGR_TILE_64;  // no copy: 64x64 tiles, operands into registers
-        else if (prc != FGR_OK) return prc;
-      }
-      if (path == FGR_PATH_MFMA_KSPLIT) return launch_ksplit(tile, a, B, C, M, K, -1, s);
-      if (path == FGR_PATH_MFMA_KSPLIT_TAIL) return launch_ksplit_tail(tile, A, a, B, C, M, N, K, cus, s);
-      return launch_ksplit_parts(tile, a, B, C, M, N, K, cus, s);
-    }
+    case FGR_PATH_MFMA_SPLITK:
+      if (path == FGR_PATH_MFMA_KSPLIT) return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
+      if (path == FGR_PATH_MFMA_KSPLIT_TAIL) return launch_ksplit_tail(tile, A, B, C, M, N, K, cus, s);
+      return launch_ksplit_parts(tile, A, B, C, M, N, K, cus, s);
     case FGR_PATH_MFMA_VEC: return launch_mfma_tile<true>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SCALAR: return launch_mfma_tile<false>(tile, A, B, C, M, N, K, s);
     case FGR_PATH_MFMA_SPLIT:
@@ -1375,7 +1313,8 @@ const char* fgr_status_string(int status) {
     case FGR_ERR_BAD_PATH: return "forced path or tile cannot run these arguments";
     case FGR_ERR_DEVICE: return "no gfx950 HIP device is current";
     case FGR_ERR_LAUNCH: return "HIP kernel launch failed";
-    case FGR_ERR_SCRATCH: return "the plan needs more workspace than fgr_solve_noalloc's 64 MiB scratch holds";
+    case FGR_ERR_SCRATCH:
+      return "the plan needs more workspace than fgr_solve_noalloc's 64 MiB scratch or the workspace limit allows";
     default: return "unknown status";
   }
 }

@@ -37,9 +37,22 @@ RULES = [
      [((4096, 4096, 6656), [("auto (160 left over)", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
       ((4096, 4096, 7168), [("auto (192 left over)", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))])]),
     ("k-split tail", "ksplit_tail_tiles(cus) = cus / 2 (choose, launch_ksplit_tail)",
-     "128x128 k-split tiles: a last partial wave of at most 128 tiles goes to the tail form",
-     [((3072, 3072, 3072), [("auto (64 left over)", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
-      ((2560, 2560, 2560), [("auto (144 left over)", AUTO),
+     "k-split tiles: a last partial wave of at most 128 tiles goes to the tail form",
+     [((3584, 3584, 3584), [("auto (128x128, 16 left over)", AUTO),
+                            ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
+      ((3001, 3001, 3001), [("auto (64x64, 161 left over)", AUTO),
+                            ("MFMA_KSPLIT_TAIL 64", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 64))])]),
+    ("128x128 or 64x64 k-split tiles", "t128 == 0 mod cus, t128 >= 3 cus or a last wave > 3 cus / 4 (choose)",
+     "128x128 tiles in whole waves, from three waves on or with a last wave more than 3/4 full; else 64x64",
+     [((2047, 2047, 2047), [("auto (128x128, one wave)", AUTO),
+                            ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
+      ((2816, 2816, 2816), [("auto (128x128, 484 tiles)", AUTO),
+                            ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
+      ((2304, 2304, 2304), [("auto (64x64; 324 of 128)", AUTO),
+                            ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))]),
+      ((2560, 2560, 2560), [("auto (64x64; 400 of 128)", AUTO),
+                            ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
+      ((3072, 3072, 3072), [("auto (64x64; 576 of 128)", AUTO),
                             ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))])]),
     ("Short reductions", "kShortReduction = 104 (choose)",
      "N < 104 with a 64x64 tile per CU: register-staged 64x64 tiles instead of the direct-copy kernel",
@@ -48,6 +61,14 @@ RULES = [
       ((65792, 96, 256), [("auto", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))]),
       ((4096, 96, 4096), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
       ((8192, 112, 8192), [("auto", AUTO), ("MFMA_VEC 64", forced(fgr.PATH_MFMA_VEC, 64))])]),
+    ("Short reductions, unaligned B", "kShortReduction = 104, kShortReductionNarrowB = 384 (choose)",
+     "unaligned rows: 32-bit register-staged tiles up to N = 104, and up to N = 384 where the direct-copy "
+     "kernel would copy B 4 bytes at a time",
+     [((8191, 65, 8191), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+      ((8191, 255, 8191), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+      ((8191, 128, 8191), [("auto (A aligned)", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+      ((8191, 511, 8191), [("auto", AUTO), ("MFMA_SCALAR 128", forced(fgr.PATH_MFMA_SCALAR, 128))]),
+      ((8192, 129, 8192), [("auto (B aligned)", AUTO), ("MFMA_SCALAR 128", forced(fgr.PATH_MFMA_SCALAR, 128))])]),
     ("Matrix-vector rows", "kSkinnyMinM = 5, kGemvMaxRows = 8 (choose)",
      "M <= 4: the matrix-vector kernel; 5 <= M <= 8 with N >= 64 and K >= 128: the k-split / split plans",
      [((4, 8192, 8192), [("auto", AUTO), ("MFMA_SPLITK 32x128", forced(fgr.PATH_MFMA_SPLITK, fgr.TILE_32X128))]),
@@ -77,11 +98,14 @@ RULES = [
      "a partial last wave of 64x64 tiles with N >= 1024 splits its tiles' reduction in the whole tiles' grid",
      [((1023, 4097, 1039), [("auto", AUTO), ("no split (split-kernel tail)", NOSPLIT)]),
       ((1536, 4096, 1536), [("auto", AUTO), ("no split (split-kernel tail)", NOSPLIT)])]),
-    ("Packed A for 128x128 tiles", "ksplit_tail_tiles with Rows::kNone (choose, pack_a)",
-     "neither operand's rows aligned: 128x128 tiles over A's padded copy where their last wave is whole "
-     "or at most half the CUs",
-     [((2047, 8191, 2047), [("auto", AUTO), ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
-      ((2500, 2501, 2503), [("auto", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))])]),
+    ("Unaligned whole-device shapes", "kKsplitUnalignedMinN = 768 (choose)",
+     "neither operand's rows aligned, enough 256x256 tiles: 128x128 k-split tiles from N = 768 on, "
+     "direct copies below",
+     [((8191, 6143, 4095), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+      ((4095, 4097, 4099), [("auto", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))]),
+      ((8191, 1023, 8191), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+      ((8191, 511, 8191), [("auto", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
+      ((4096, 4096, 4095), [("auto (A aligned)", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))])]),
     ("Column strip", "kStripMax = 8 (strip_plan_ok)",
      "K = 64 q + w, w <= 8: tiles on the q column blocks, the w columns on the vector ALUs, one launch",
      [((1023, 1025, 1027), [("auto", AUTO), ("MFMA_KSPLIT_TAIL 64", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 64))]),

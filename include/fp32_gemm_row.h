@@ -88,7 +88,8 @@ extern "C" {
                                      stream belongs to another device */
 #define FGR_ERR_LAUNCH (-7)       /* HIP reported an error at launch */
 #define FGR_ERR_SCRATCH (-8)      /* fgr_solve_noalloc: the plan needs more workspace than its
-                                     scratch array holds; nothing was enqueued */
+                                     scratch array holds or the workspace limit allows;
+                                     nothing was enqueued */
 
 /* Paths (fgr_select_path / fgr_solve_path). */
 #define FGR_PATH_AUTO 0
@@ -168,10 +169,7 @@ extern "C" {
  *     solve() picks the split, P * tiles <= 4 * CUs: on a 256-CU device at most
  *     16 MiB with 64 x 64 or smaller tiles, 64 MiB with 128 x 128 tiles. A
  *     forced MFMA_SPLITK on a large output takes P = 2, i.e. 2*M*K floats.
- *   - 128 x 128 k-split tiles (MFMA_KSPLIT, MFMA_KSPLIT_TAIL, MFMA_SPLITK)
- *     when neither A's nor B's rows are 16-byte aligned: a copy of A with rows
- *     of N rounded up to a multiple of 4, M * that floats (e.g. 4095 x 8191 x
- *     2047: 134 MB), made by a first kernel once per call.
+ *   No other plan takes a workspace.
  * Each stream (up to 16 per process, identified by its handle and device)
  * keeps one split workspace between calls, up to 64 MiB: it is allocated
  * stream-ordered on `stream` at the stream's first split call, replaced (the
@@ -179,18 +177,17 @@ extern "C" {
  * otherwise held until the process ends; a stream created after another was
  * destroyed may inherit its handle and so its entry, whose buffer it uses only
  * after the old stream's last use of it. Calls from several host threads on one
- * stream are serialised while they enqueue. Every other workspace (A's copy,
- * more streams, larger workspaces, hipStreamPerThread, or `stream` under
- * capture) is allocated stream-ordered on `stream` for the call and freed
+ * stream are serialised while they enqueue. Every other workspace (more
+ * streams, larger workspaces, hipStreamPerThread, or `stream` under capture)
+ * is allocated stream-ordered on `stream` for the call and freed
  * with hipFreeAsync after its last kernel. Allocations come from a memory
  * pool the library creates per device on first use (hipMemPoolCreate; it
  * keeps up to 64 MiB of freed memory for reuse and lives until the process
  * ends), or from the device's default pool if that creation failed. If an
  * allocation fails, or would exceed fgr_set_workspace_limit(), the plan runs
  * without that workspace: the unsplit kernel instead of a split, the split
- * kernel for a last partial wave, 64 x 64 tiles instead of 128 x 128 ones
- * over A's copy (same result up to rounding order); no error is returned for
- * it. Results are deterministic: the parts are added in a fixed order.
+ * kernel for a last partial wave (same result up to rounding order); no error
+ * is returned for it. Results are deterministic: the parts are added in a fixed order.
  * solve() can be captured into a HIP graph (stream capture on `stream`); the
  * workspace then becomes a graph allocation.
  * The LeetGPU signature (section "Problem Description", and every "Solution"
@@ -208,10 +205,10 @@ int solve(const float *A, const float *B, float *C, int M, int N, int K, void *s
  * static device array of 64 MiB (67108864 bytes) that the library holds on
  * each GPU it runs on until the process ends, and it calls no allocating
  * routine (no hipMalloc, hipMallocAsync, hipFree or pool call). If the plan
- * needs more than 64 MiB of workspace (on a 256-CU device only A's padded
- * copy can: M * (N rounded up to a multiple of 4) * 4 bytes, for 128 x 128
- * k-split tiles when neither A's nor B's rows are 16-byte aligned), it returns
- * FGR_ERR_SCRATCH and enqueues nothing. The array keeps what the last call
+ * needs more workspace than the array holds, or than fgr_set_workspace_limit()
+ * allows, it returns FGR_ERR_SCRATCH and enqueues nothing (on a 256-CU device
+ * no plan of solve() needs more than 64 MiB: see the split workspaces above;
+ * one with more CUs can). The array keeps what the last call
  * left in it; nothing in it needs to start at zero. All such calls on one GPU
  * share its array: calls that overlap on one GPU (other streams or threads,
  * before the previous one's kernels have finished) race, so the caller must
@@ -259,11 +256,12 @@ int fgr_version(void);
 /*
  * fgr_set_workspace_limit - the largest workspace, in bytes, that one request
  * of a call may take from now on (process-wide; negative: no limit, the
- * default). A plan whose workspace would exceed it runs without that
- * workspace, as when an allocation fails (see solve()). For callers short of
- * device memory, and for tests of those no-workspace forms (a limit of 0
- * takes every one of them). Returns the previous limit. Host only; calls
- * already enqueued are not affected.
+ * default). A plan of solve() whose workspace would exceed it runs without
+ * that workspace, as when an allocation fails (see solve()); fgr_solve_noalloc
+ * refuses such a plan with FGR_ERR_SCRATCH. For callers short of device
+ * memory, and for tests of those forms (a limit of 0 takes every one of
+ * them). Returns the previous limit. Host only; calls already enqueued are not
+ * affected.
  */
 long long fgr_set_workspace_limit(long long bytes);
 

@@ -6,6 +6,7 @@
 
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_dma.hpp"
+#include "gemm_mfma_kreg.hpp"
 #include "gemm_mfma_ksplit.hpp"
 
 namespace {
@@ -40,6 +41,12 @@ int shim_dma_a_col(int pos) { return fgr::dma_a_col(pos); }
 int shim_dma_a_read(int row0, int i, int q) { return fgr::dma_a_read(row0, i, q); }
 int shim_ksplit_a_col(int pos) { return fgr::ksplit_a_col(pos); }
 int shim_ksplit_a_read(int li, int g) { return fgr::ksplit_a_read(li, g); }
+
+void shim_kreg_cols(int k0, int li, int K, int kcb, int* first, int* skip) {
+  const fgr::KregCols c = fgr::kreg_cols(k0, li, K, kcb);
+  *first = c.first;
+  *skip = c.skip;
+}
 
 // D = A x B through one MFMA (device pointers; one wave). 0 or a HIP error.
 int shim_mfma_probe(const float* A, const float* B, float* D, void* stream) {

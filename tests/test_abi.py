@@ -135,13 +135,15 @@ def test_forced_path_rejections(lib):
         assert call(lib, A0, B0, C0, 512, 130, 512, path) == fgr.ERR_DEVICE
         assert call(lib, A0, B0, C0, 512, 128, 502, path) == fgr.ERR_DEVICE
         assert call(lib, A0 + 4, B0, C0, 512, 128, 512, path) == fgr.ERR_DEVICE
-    # the k-split paths need N >= 64; tile 128 takes any rows but those of B
-    # and not C aligned with A's not (A is packed only when B's are not
-    # aligned either), and the tail form has no 32x32 tiles
+    # the k-split paths need N >= 64; tile 128 takes rows at any alignment
+    # but needs K >= 4 (four columns of B per lane); the tail form has no
+    # 32x32 tiles
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_KSPLIT) == fgr.ERR_BAD_PATH
-    assert call(lib, A0, B0, C0, 512, 130, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # A packed first
+    assert call(lib, A0, B0, C0, 512, 130, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # neither aligned
     assert call(lib, A0 + 4, B0 + 4, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_DEVICE
-    assert call(lib, A0 + 4, B0, C0 + 4, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH  # B, not C
+    assert call(lib, A0 + 4, B0, C0 + 4, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # B, not C
+    assert call(lib, A0, B0, C0, 512, 128, 3, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_BAD_PATH  # K < 4
+    assert call(lib, A0, B0, C0, 512, 128, 4, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE
     assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # A rows only
     assert call(lib, A0, B0 + 4, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT_TAIL, 128) == fgr.ERR_DEVICE
     assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, 128) == fgr.ERR_DEVICE  # B and C rows
@@ -151,9 +153,10 @@ def test_forced_path_rejections(lib):
         assert call(lib, A0, B0, C0, 512, 128, 502, fgr.PATH_MFMA_KSPLIT, tile) == fgr.ERR_DEVICE
         assert call(lib, A0 + 4, B0, C0, 512, 128, 512, fgr.PATH_MFMA_KSPLIT, tile) == fgr.ERR_DEVICE
     # the cross-workgroup split needs N >= 128 (two parts of 8 chunks); tile
-    # 128 needs 128-bit rows; no 256 tiles
+    # 128 needs K >= 4; no 256 tiles
     assert call(lib, A0, B0, C0, 512, 120, 512, fgr.PATH_MFMA_SPLITK) == fgr.ERR_BAD_PATH
-    assert call(lib, A0 + 4, B0, C0 + 4, 512, 128, 512, fgr.PATH_MFMA_SPLITK, 128) == fgr.ERR_BAD_PATH
+    assert call(lib, A0 + 4, B0, C0 + 4, 512, 128, 512, fgr.PATH_MFMA_SPLITK, 128) == fgr.ERR_DEVICE
+    assert call(lib, A0, B0, C0, 512, 128, 2, fgr.PATH_MFMA_SPLITK, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, 256) == fgr.ERR_BAD_PATH
     for tile in (0, 128, 64, 32):
         assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_SPLITK, tile) == fgr.ERR_DEVICE
@@ -177,7 +180,7 @@ def test_forced_path_rejections(lib):
 
 
 def test_path_selection_rules():
-    sp = fgr.select_path
+    sp, st = fgr.select_path, fgr.select_tile
     assert sp(A0, B0, C0, 8192, 6144, 4096) == fgr.PATH_MFMA_DMA
     assert sp(A0, B0, C0, 4096, 4096, 4096) == fgr.PATH_MFMA_DMA
     assert sp(A0, B0, C0, 4096, 4060, 4096) == fgr.PATH_MFMA_DMA  # ragged reduction
@@ -193,15 +196,36 @@ def test_path_selection_rules():
     assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 4-byte copies
     assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_KSPLIT  # 64 tiles of 256, 256 of 128
     assert sp(A0, B0, C0, 1024, 6144, 4096) == fgr.PATH_MFMA_KSPLIT  # a row shard of the timed shape
-    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT_TAIL  # 576 tiles of 128
-    assert sp(A0, B0, C0, 2000, 3000, 2100) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 tiles of 128
+    # 128x128 tiles in whole waves, three waves or more, or a last wave more
+    # than three quarters full; else 64x64 tiles
+    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT  # 576 of 128 (2.25 waves): 2304 of 64
+    assert st(A0, B0, C0, 3072, 3072, 3072) == 64
+    assert sp(A0, B0, C0, 2000, 3000, 2100) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 128: 1056 of 64
+    assert st(A0, B0, C0, 2000, 3000, 2100) == 64
+    assert sp(A0, B0, C0, 2304, 2304, 2304) == fgr.PATH_MFMA_KSPLIT_TAIL  # 324 of 128: 1296 of 64
+    assert st(A0, B0, C0, 2304, 2304, 2304) == 64
+    assert sp(A0, B0, C0, 2816, 2816, 2816) == fgr.PATH_MFMA_KSPLIT  # 484 of 128: 228 in the last wave
+    assert st(A0, B0, C0, 2816, 2816, 2816) == 128
+    assert sp(A0, B0, C0, 3584, 3584, 3584) == fgr.PATH_MFMA_KSPLIT_TAIL  # 784 of 128: three waves and 16
+    assert st(A0, B0, C0, 3584, 3584, 3584) == 128
+    assert sp(A0, B0, C0, 2047, 2047, 2047) == fgr.PATH_MFMA_KSPLIT  # 256 of 128, unaligned rows
+    assert st(A0, B0, C0, 2047, 2047, 2047) == 128
     assert sp(A0, B0, C0, 2048, 60, 2048) == fgr.PATH_MFMA_VEC  # N < 64: no direct copies
-    assert sp(A0, B0, C0, 2560, 2560, 2560) == fgr.PATH_MFMA_KSPLIT  # 400 tiles of 128: 144 over half a wave
+    assert sp(A0, B0, C0, 2560, 2560, 2560) == fgr.PATH_MFMA_KSPLIT_TAIL  # 400 of 128: 1600 of 64, 64 left
     assert sp(A0, B0, C0, 8, 8, 6) == fgr.PATH_GEMV_SCALAR  # skinny, K % 4 != 0
     assert sp(A0, B0, C0, 40, 8, 6) == fgr.PATH_MFMA_SPLIT
     assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_DMA  # misaligned A: 4-byte copies
     assert sp(A0, B0, C0 + 8, 8192, 8192, 8192) == fgr.PATH_MFMA_DMA
-    assert sp(A0, B0, C0, 8191, 6143, 4095) == fgr.PATH_MFMA_DMA  # ragged rows: 4-byte copies
+    # neither operand's rows aligned: 128x128 k-split tiles from N = 768 on,
+    # direct copies below (and the register-staged tiles below N = 384)
+    assert sp(A0, B0, C0, 8191, 6143, 4095) == fgr.PATH_MFMA_KSPLIT
+    assert st(A0, B0, C0, 8191, 6143, 4095) == 128
+    assert sp(A0, B0, C0, 4095, 4097, 4099) == fgr.PATH_MFMA_KSPLIT_TAIL  # 1056 of 128: 32 left over
+    assert sp(A0, B0, C0, 8191, 1023, 8191) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 8191, 769, 8191) == fgr.PATH_MFMA_KSPLIT
+    assert sp(A0, B0, C0, 8191, 767, 8191) == fgr.PATH_MFMA_DMA
+    assert sp(A0, B0, C0, 8191, 511, 8191) == fgr.PATH_MFMA_DMA
+    assert sp(A0 + 4, B0, C0, 4096, 6144, 4096) == fgr.PATH_MFMA_DMA  # one operand aligned
     assert sp(A0, B0, C0, 8192, 60, 8190) == fgr.PATH_MFMA_SCALAR  # N < 64
     assert sp(A0, B0, C0, 1, 8192, 8192) == fgr.PATH_GEMV_VEC
     assert sp(A0, B0, C0, 1, 3, 1) == fgr.PATH_GEMV_SCALAR
@@ -228,7 +252,7 @@ def test_tile_selection():
     assert st(A0, B0, C0, 256, 256, 256) == 32  # k-split, 32x32
     assert st(A0, B0, C0, 2048, 512, 1024) == 64  # 128 tiles of 128, 512 of 64
     assert st(A0, B0, C0, 2048, 60, 2048) == 64  # no direct copies (N < 64): register-staged 64x64
-    assert st(A0, B0, C0, 4095, 4097, 4099) == 256  # 4-byte direct copies, 256 tiles
+    assert st(A0, B0, C0, 4095, 4097, 4099) == 128  # unaligned rows, long reduction: k-split 128x128
     assert st(A0, B0, C0, 4095, 60, 4099) == 128  # N < 64: 32-bit loads, many tiles
     assert st(A0, B0, C0, 1, 8192, 8192) == 0  # matrix-vector
     assert st(0, B0, C0, 4, 4, 4) == fgr.ERR_NULL_POINTER
@@ -266,8 +290,19 @@ def test_short_reduction_choices():
     assert sp(A0, B0, C0, 8191, 17, 8191) == fgr.PATH_MFMA_SCALAR
     assert st(A0, B0, C0, 8191, 17, 8191) == 128
     assert st(A0, B0, C0, 1023, 33, 1025) == 64
-    # unaligned rows with N >= 64 keep the direct-copy kernel (4-byte copies)
-    assert sp(A0, B0, C0, 8191, 65, 8191) == fgr.PATH_MFMA_DMA
+    # unaligned rows up to N = 104, and up to 384 where the direct-copy kernel
+    # would copy B 4 bytes at a time: 32-bit loads; B's rows aligned: direct copies
+    assert sp(A0, B0, C0, 8191, 65, 8191) == fgr.PATH_MFMA_SCALAR
+    assert st(A0, B0, C0, 8191, 65, 8191) == 128
+    assert sp(A0, B0, C0, 8191, 383, 8191) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0, B0, C0, 8191, 385, 8191) == fgr.PATH_MFMA_DMA
+    assert sp(A0, B0, C0, 8191, 128, 8191) == fgr.PATH_MFMA_SCALAR  # A's rows aligned, B's not
+    assert sp(A0, B0, C0, 8191, 384, 8191) == fgr.PATH_MFMA_DMA
+    assert sp(A0, B0, C0, 8192, 129, 8192) == fgr.PATH_MFMA_DMA  # B's rows aligned
+    assert sp(A0, B0, C0, 8192, 101, 8192) == fgr.PATH_MFMA_SCALAR
+    assert sp(A0, B0, C0, 2047, 97, 2049) == fgr.PATH_MFMA_SCALAR  # 1056 tiles of 64
+    assert st(A0, B0, C0, 2047, 97, 2049) == 64
+    assert sp(A0, B0, C0, 2047, 255, 2049) == fgr.PATH_MFMA_KSPLIT_TAIL  # few 256x256 tiles: k-split
 
 
 def test_skinny_choices():
@@ -300,14 +335,14 @@ def test_split_reduction_choices():
         assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
         assert st(A0, B0, C0, *shape) == tile, shape
         assert sp(A0 + 4, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape  # 4-byte copies too
-    # 128x128 split tiles: parts of at least 2048 and no more padding than
-    # 64x64 tiles; both operands' rows unaligned, or shorter parts: 64x64
+    # 128x128 split tiles (any row alignment): parts of at least 2048 and no
+    # more padding than 64x64 tiles; shorter parts: 64x64
     for shape, tile in [((128, 524288, 128), 128), ((640, 65536, 640), 128), ((192, 262144, 192), 64),
                         ((320, 200000, 320), 64), ((256, 100000, 256), 64), ((128, 262144, 128), 64)]:
         assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_SPLITK, shape
         assert st(A0, B0, C0, *shape) == tile, shape
-    assert st(A0 + 4, B0, C0, 128, 524288, 128) == 128  # A's rows through buffer loads
-    assert st(A0 + 4, B0 + 4, C0, 128, 524288, 128) == 64
+    assert st(A0 + 4, B0, C0, 128, 524288, 128) == 128
+    assert st(A0 + 4, B0 + 4, C0, 128, 524288, 128) == 128
     # enough 32x32 tiles for every CU, or too short a reduction: no split
     assert sp(A0, B0, C0, 512, 4096, 512) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles

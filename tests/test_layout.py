@@ -33,6 +33,8 @@ def _load_shim():
         getattr(lib, name).argtypes = [ci]
     lib.shim_dma_a_read.argtypes = [ci, ci, ci]
     lib.shim_ksplit_a_read.argtypes = [ci, ci]
+    lib.shim_kreg_cols.argtypes = [ci, ci, ci, ci, pi, pi]
+    lib.shim_kreg_cols.restype = None
     vp = ctypes.c_void_p
     lib.shim_mfma_probe.argtypes = [vp, vp, vp, vp]
     return lib
@@ -136,6 +138,31 @@ def test_ksplit_a_layout(shim, bm):
             offs.append(off)
         assert bank_groups_distinct(offs, 8, 8), (bm, i)
         assert bank_groups_distinct(offs, 16, 16), (bm, i)
+
+
+@pytest.mark.parametrize("kcb", [1, 2, 4])
+def test_register_fed_columns(shim, kcb):
+    # the register-fed k-split tiles (32 kcb columns, kcb adjacent columns per
+    # lane): every lane's B load stays inside [0, K); the columns the tile's
+    # lanes store cover [k0, min(k0 + 32 kcb, K)) exactly once; no store lies
+    # left of the tile's first column (the store address is formed from
+    # first - k0, which is negative at the right edge)
+    first, skip = ctypes.c_int(), ctypes.c_int()
+    bn = 32 * kcb
+    for K in list(range(kcb, 4 * bn + 9)) + [1023, 1025, 1027, 4097, 6143]:
+        for k0 in range(0, K, bn):
+            stored = []
+            for li in range(32):
+                shim.shim_kreg_cols(k0, li, K, kcb, ctypes.byref(first), ctypes.byref(skip))
+                f, sk = first.value, skip.value
+                assert 0 <= f and f + kcb <= K, (K, k0, li, f)
+                assert sk >= 0, (K, k0, li, sk)
+                if sk == 0:
+                    assert f == k0 + kcb * li
+                cols = [f + j for j in range(sk, kcb)]
+                assert all(c >= k0 for c in cols), (K, k0, li, cols)
+                stored += cols
+            assert sorted(stored) == list(range(k0, min(k0 + bn, K))), (K, k0)
 
 
 def test_swizzles_stay_in_range(shim):

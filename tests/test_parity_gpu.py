@@ -102,7 +102,8 @@ def paths_for(M, N, K):
         for tile in (fgr.TILE_64, fgr.TILE_32):
             out.append((fgr.PATH_MFMA_KSPLIT, tile))
         out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_64))
-    if N % 4 == 0 and K % 4 == 0 and N >= 64:
+    if N >= 64 and K >= 4:
+        # 128x128 tiles, operands into registers at any alignment
         out.append((fgr.PATH_MFMA_KSPLIT, fgr.TILE_128))
         out.append((fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128))
     if N >= 64:
@@ -111,7 +112,7 @@ def paths_for(M, N, K):
         # the reduction also split across workgroups (two parts at least)
         for tile in (fgr.TILE_64, fgr.TILE_32, fgr.TILE_32X128):
             out.append((fgr.PATH_MFMA_SPLITK, tile))
-        if N % 4 == 0 and K % 4 == 0:
+        if K >= 4:
             out.append((fgr.PATH_MFMA_SPLITK, fgr.TILE_128))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_32))
     out.append((fgr.PATH_MFMA_SPLIT, fgr.TILE_64))
@@ -280,13 +281,12 @@ def test_large_ragged_sampled(shape):
     # long reductions: the tail tiles' reduction split across workgroups
     ((1023, 4097, 1039), fgr.PATH_MFMA_KSPLIT_TAIL, 64), ((2176, 4096, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
     ((1088, 4100, 1024), fgr.PATH_MFMA_KSPLIT_TAIL, 64),
-    # 128x128 tiles with one operand on 4-byte copies (buffer loads): B's, then
-    # A's; ragged M and K, a partial last wave
+    # 128x128 tiles with one operand's rows unaligned: B's, then A's; ragged
+    # M and K, a partial last wave
     ((2048, 2048, 2047), fgr.PATH_MFMA_KSPLIT, 128), ((2000, 1028, 2045), fgr.PATH_MFMA_KSPLIT, 128),
     ((2176, 1028, 2047), fgr.PATH_MFMA_KSPLIT_TAIL, 128), ((2047, 2051, 2048), fgr.PATH_MFMA_KSPLIT, 128),
     ((2040, 1025, 2044), fgr.PATH_MFMA_KSPLIT, 128), ((2176, 1025, 2048), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
-    # neither operand's rows aligned: A packed into padded rows first (1, 2
-    # and 3 padding columns)
+    # neither operand's rows aligned (N mod 4 = 3, 2, 1)
     ((2040, 2047, 2043), fgr.PATH_MFMA_KSPLIT, 128), ((2000, 2046, 2045), fgr.PATH_MFMA_KSPLIT, 128),
     ((2047, 2049, 2051), fgr.PATH_MFMA_KSPLIT_TAIL, 128),
     # tails of 64x64 tiles with N >= 1024: whole and split tiles in one grid
@@ -296,18 +296,19 @@ def test_large_ragged_sampled(shape):
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_ksplit_exact(shape, path, tile):
     # tiles whose reduction is split over a workgroup's waves (128, 64 or 32
-    # square, 4-byte copies for unaligned rows); with a partial last wave of
-    # them, the rest cut into split-kernel tiles: exact on integer data
-    # whichever kernel computed an output
+    # square; operands through LDS or straight into registers by tile and
+    # alignment), the listed form forced; with a partial last wave of them, the
+    # rest cut into split-kernel tiles or split across workgroups: exact on
+    # integer data whichever kernel computed an output. The automatic plan of
+    # each shape (whose rules the CPU tests pin) too.
     M, N, K = shape
     A, B = synth.make_inputs(M, N, K, "integer", seed=6)
     say(f"k-split {shape}: oracle")
     Cref, _ = oracle.gemm(A, B)
-    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == path
-    assert fgr.select_tile(1 << 40, 2 << 40, 3 << 40, M, N, K) == tile
-    say(f"k-split {shape}: GPU")
-    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
+    say(f"k-split {shape}: GPU, path {path} tile {tile}")
+    assert_exact(gpu_gemm(A, B, path, tile), Cref, f"{shape} path {path} tile {tile}")
     assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT, tile), Cref, f"{shape} k-split only")
+    assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
 
 
 @pytest.mark.parametrize("shape,tile", [
@@ -349,9 +350,9 @@ def test_split_matrix_vector_exact(shape):
 
 
 @pytest.mark.parametrize("shape,offsets", [
-    ((1023, 1025, 1027), (0, 0, 0)),   # neither operand aligned: A packed, w = 3
+    ((1023, 1025, 1027), (0, 0, 0)),   # neither operand aligned, w = 3
     ((1023, 1025, 1027), (1, 2, 3)),
-    ((1023, 1024, 1027), (0, 0, 0)),   # A aligned, B not: no copy
+    ((1023, 1024, 1027), (0, 0, 0)),   # A aligned, B not
     ((1024, 1024, 1028), (0, 0, 0)),   # all aligned, w = 4
     ((1024, 1024, 1028), (0, 0, 1)),   # C misaligned
     ((1000, 2049, 1030), (0, 0, 0)),   # w = 6, ragged rows
@@ -360,8 +361,8 @@ def test_split_matrix_vector_exact(shape):
     ((4096, 1025, 257), (0, 0, 0)),    # four column blocks, w = 1
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_strip_plan_exact(shape, offsets):
-    # the last K % 64 columns on the vector ALUs (with A's padded copy when
-    # neither operand's rows are aligned), 64x64 k-split tiles on the rest:
+    # the last K % 64 columns on the vector ALUs, 64x64 k-split tiles on the
+    # rest (operands through LDS with every row aligned, else into registers):
     # exact on integer data, auto and forced
     M, N, K = shape
     A, B = synth.make_inputs(M, N, K, "integer", seed=16)
@@ -384,9 +385,9 @@ def test_strip_plan_forced_small_exact(shape):
         assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_STRIP, 64, offsets=offsets), Cref, f"{shape} {offsets}")
 
 
-# The register-fed k-split tiles: 32x32 tiles, and 64x64 tiles whenever a
-# row of A, B or C is not 16-byte aligned, load their operands straight into
-# registers (16- and 8-byte loads at 4-byte alignment). Cases: one, two and
+# The register-fed k-split tiles: 128x128 and 32x32 tiles, and 64x64 tiles
+# whenever a row of A, B or C is not 16-byte aligned, load their operands
+# straight into registers (16-, 8- and 4-byte loads at 4-byte alignment). Cases: one, two and
 # three columns (64x64 tiles take B two columns at a time; one column runs on
 # 32x32 tiles; with three the last lane's pair is shifted back by one), N not
 # a multiple of 8 (chunk 0 reaches below n = 0 and is zero-filled), partial
@@ -411,6 +412,19 @@ KREG_CASES = [
     ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 32, (0, 0, 0)),
     ((96, 333, 97), fgr.PATH_MFMA_KSPLIT, 32, (0, 0, 0)),
     ((96, 8192, 96), fgr.PATH_MFMA_SPLITK, 32, (1, 2, 3)),
+    # 128x128: four columns of B per lane, so the right edge shifts a lane
+    # back by one to three columns; all alignments; split parts and tails
+    ((130, 67, 4), fgr.PATH_MFMA_KSPLIT, 128, (0, 0, 0)),
+    ((130, 67, 5), fgr.PATH_MFMA_KSPLIT, 128, (0, 0, 0)),
+    ((130, 67, 6), fgr.PATH_MFMA_KSPLIT, 128, (1, 1, 1)),
+    ((130, 67, 7), fgr.PATH_MFMA_KSPLIT, 128, (0, 0, 0)),
+    ((257, 1025, 263), fgr.PATH_MFMA_KSPLIT, 128, (0, 0, 0)),
+    ((257, 1025, 265), fgr.PATH_MFMA_KSPLIT, 128, (0, 1, 0)),
+    ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 128, (0, 0, 0)),
+    ((256, 256, 256), fgr.PATH_MFMA_KSPLIT, 128, (1, 0, 2)),
+    ((130, 4097, 131), fgr.PATH_MFMA_SPLITK, 128, (0, 0, 0)),
+    ((1023, 1025, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 128, (0, 0, 0)),
+    ((2047, 2049, 2051), fgr.PATH_MFMA_KSPLIT, 128, (0, 0, 0)),
 ]
 
 
@@ -438,29 +452,28 @@ def test_stream_read_sums(n, blocks):
     assert sums.sum() == float((np.arange(n) % 7).sum())
 
 
-def test_packed_a_with_split_tail_exact():
-    # neither operand's rows 16-byte aligned (N, K odd), 128x128 tiles forced
-    # with the tail form: 9 tiles, none in a whole wave, so all of them are
-    # the tail, whose reduction (N >= 4096) is split over 28 parts through a
-    # workspace, over A's padded copy made once for the call
+def test_unaligned_128_with_split_tail_exact():
+    # neither operand's rows 16-byte aligned (N, K odd), 128x128 register-fed
+    # tiles forced with the tail form: 9 tiles, none in a whole wave, so all
+    # of them are the tail, whose reduction (N >= 4096) is split over 28
+    # parts through a workspace; the last column tile has 3 columns
     M, N, K = 300, 4097, 259
     A, B = synth.make_inputs(M, N, K, "integer", seed=14)
     Cref, _ = oracle.gemm(A, B)
-    say(f"packed A, split tail {M}x{N}x{K}")
-    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128), Cref, "packed A + split tail")
+    say(f"unaligned 128x128, split tail {M}x{N}x{K}")
+    assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128), Cref, "128x128 + split tail")
     assert_exact(gpu_gemm(A, B, fgr.PATH_MFMA_KSPLIT_TAIL, fgr.TILE_128, offsets=(1, 2, 3)), Cref,
-                 "packed A + split tail, 4-byte aligned pointers")
+                 "128x128 + split tail, 4-byte aligned pointers")
 
 
 @pytest.mark.parametrize("shape,path,tile", [
-    ((2040, 2047, 2043), fgr.PATH_MFMA_KSPLIT, 128),        # A's padded copy -> 64x64 tiles
-    ((300, 4097, 259), fgr.PATH_MFMA_KSPLIT_TAIL, 128),     # A's copy and the split tail
-    ((2047, 2049, 2051), fgr.PATH_AUTO, 0),                 # the same, picked by solve()
-    ((1023, 1025, 1027), fgr.PATH_AUTO, 0),                 # strip plan without A's copy
+    ((300, 4097, 259), fgr.PATH_MFMA_KSPLIT_TAIL, 128),     # 128x128 split tail -> split kernel
+    ((2047, 2049, 2051), fgr.PATH_AUTO, 0),                 # 64x64 tail split in the tiles' grid
+    ((1023, 1025, 1027), fgr.PATH_AUTO, 0),                 # strip plan: no workspace anyway
     ((1023, 1025, 1036), fgr.PATH_AUTO, 0),                 # tail split in the whole tiles' grid
     ((1023, 4097, 1027), fgr.PATH_MFMA_KSPLIT_TAIL, 64),    # tail split after the whole tiles
     ((128, 262144, 128), fgr.PATH_AUTO, 0),                 # split reduction -> unsplit tiles
-    ((301, 8191, 127), fgr.PATH_MFMA_SPLITK, 128),          # forced split over A's copy
+    ((301, 8191, 127), fgr.PATH_MFMA_SPLITK, 128),          # forced 128x128 split -> unsplit
     ((1, 262144, 64), fgr.PATH_AUTO, 0),                    # split matrix-vector -> unsplit
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_no_workspace_fallbacks_exact(shape, path, tile):
@@ -529,8 +542,7 @@ def test_ksplit_operand_alignments_exact(shape, offsets):
                        (fgr.PATH_MFMA_SPLITK, 64), (fgr.PATH_MFMA_SPLITK, fgr.TILE_32X128),
                        (fgr.PATH_MFMA_KSPLIT_TAIL, 64)]:
         assert_exact(gpu_gemm(A, B, path, tile, offsets=offsets), Cref, f"{shape} {offsets} path={path} tile={tile}")
-    # 128x128 tiles: one operand's 4-byte copies through buffer loads, or,
-    # with neither A's rows nor B's aligned, A first copied into padded rows
+    # 128x128 tiles, operands straight into registers at any alignment
     for path in (fgr.PATH_MFMA_KSPLIT, fgr.PATH_MFMA_SPLITK, fgr.PATH_MFMA_KSPLIT_TAIL):
         assert_exact(gpu_gemm(A, B, path, 128, offsets=offsets), Cref, f"{shape} {offsets} path={path} tile=128")
 
@@ -919,7 +931,7 @@ def test_random_large_shapes_sampled():
 def test_long_reduction_128_split_exact():
     # few output tiles over a long reduction, where solve() splits the
     # reduction over 128x128 tiles (parts of 2048 or more): aligned, and with
-    # A's rows through buffer loads; exact on integer data at sampled outputs
+    # A's rows unaligned; exact on integer data at sampled outputs
     # (every |partial sum| stays below 4 * 4 * 524288 < 2^24)
     for (M, N, K), offsets in [((128, 524288, 128), (0, 0, 0)), ((128, 524288, 128), (1, 0, 0)),
                                ((512, 65536, 512), (0, 0, 0))]:

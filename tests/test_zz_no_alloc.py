@@ -57,8 +57,8 @@ def check(A, B, dist, label):
 
 # Sequences of calls, each later input smaller than the one before. Plans:
 # 128x128 split reduction (the largest split workspace), 64x64 split
-# reduction, A's padded copy for 128x128 tiles, the tail split in the whole
-# tiles' grid, the split matrix-vector product, and a plan with no workspace.
+# reduction, the tail split in the whole tiles' grid, the split
+# matrix-vector product, and plans with no workspace.
 SEQUENCES = [
     [(512, 65536, 512), (128, 262144, 128), (100, 30000, 300)],
     [(2047, 2049, 2051), (1023, 1025, 1027), (1, 262144, 64)],
@@ -76,23 +76,29 @@ def test_noalloc_matches_solve_on_calls_in_a_row(seq):
         check(A, B, dist, f"{M}x{N}x{K} {dist}")
 
 
-def test_noalloc_refuses_plans_beyond_the_scratch():
-    # 128x128 tiles over A's padded copy of 4095 x 8192 floats (134 MB): more
-    # than the 64 MiB scratch, so the call fails with FGR_ERR_SCRATCH and
-    # leaves C as it was; solve() itself runs the shape
-    M, N, K = 4095, 8191, 2047
-    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_MFMA_KSPLIT
-    assert fgr.select_tile(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.TILE_128
+def test_noalloc_refuses_plans_beyond_the_limit():
+    # a 128x128 split reduction whose partial tiles take 16 MiB, with the
+    # workspace limit at 4 MiB: the call fails with FGR_ERR_SCRATCH and leaves
+    # C as it was; with the limit lifted the same call runs
+    M, N, K = 512, 65536, 512
+    assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_MFMA_SPLITK
     say(f"noalloc refusal {M}x{N}x{K}")
     dA = torch.zeros(M * N, device=DEV)
     dB = torch.zeros(N * K, device=DEV)
     dC = torch.full((M * K,), float("nan"), device=DEV)
     torch.cuda.synchronize()
-    with pytest.raises(fgr.GemmError) as err:
-        fgr.solve_noalloc(dA, dB, dC, M, N, K)
-    assert err.value.code == fgr.ERR_SCRATCH
+    old = fgr.set_workspace_limit(4 << 20)
+    try:
+        with pytest.raises(fgr.GemmError) as err:
+            fgr.solve_noalloc(dA, dB, dC, M, N, K)
+        assert err.value.code == fgr.ERR_SCRATCH
+        torch.cuda.synchronize()
+        assert torch.isnan(dC).all().item(), "a refused call wrote to C"
+    finally:
+        fgr.set_workspace_limit(old)
+    fgr.solve_noalloc(dA, dB, dC, M, N, K)
     torch.cuda.synchronize()
-    assert torch.isnan(dC).all().item(), "a refused call wrote to C"
+    assert (dC == 0).all().item()
     # a small call right after still works
     A, B = synth.make_inputs(200, 3000, 100, "integer", seed=60)
     check(A, B, "integer", "200x3000x100 after a refusal")
