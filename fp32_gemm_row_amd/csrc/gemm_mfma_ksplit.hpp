@@ -18,11 +18,11 @@
 // own A (BM x BK) and B (BK x BN) chunks with global_load_lds (16 bytes per
 // lane for 16-byte aligned rows, 4 bytes otherwise) into its own ring of S
 // LDS stages and waits only on its own copies (s_waitcnt vmcnt): the main
-// loop has no barrier. It serves 64x64 tiles whose rows of A, B and C are all
-// 16-byte aligned, and the skinny 32x128 tiles. 128x128 tiles, all 32x32
-// tiles and 64x64 tiles with unaligned rows load their operands straight into
-// registers instead (gemm_mfma_kreg.hpp, the same decomposition), which was
-// measured faster there.
+// loop has no barrier. It serves 64x64 and 32x32 tiles whose rows of A, B
+// and C are all 16-byte aligned, and the skinny 32x128 tiles. 128x128 tiles,
+// and 64x64 and 32x32 tiles with unaligned rows, load their operands straight
+// into registers instead (gemm_mfma_kreg.hpp, the same decomposition), which
+// was measured faster there.
 //
 // This keeps the output-parallel decomposition of the LeetGPU write-up
 // (section "V0", "Approach": outputs independent, each owned with its whole
@@ -54,8 +54,8 @@
 
 namespace fgr {
 
-// BM x BN tiles: 64 x 64, or the skinny 32 x 128 tile (few output rows,
-// wide column blocks of B per workgroup). VA / VB: 16-byte copies of A / B
+// BM x BN tiles: 64 x 64, 32 x 32, or the skinny 32 x 128 tile (few output
+// rows, wide column blocks of B per workgroup). VA / VB: 16-byte copies of A / B
 // (their rows 16-byte aligned), else 4-byte copies. STRIP: the launch also
 // holds, after the tiles' workgroups, workgroups that compute the narrow
 // column strip [tiles_n * BN, K) of C on the vector ALUs (strip.hpp).
@@ -85,7 +85,7 @@ struct KsplitConfig {
   static constexpr int kSlicesPerObjB = kStageB / 1024;
   static constexpr int kSlicesPerWave = kSlices >= kWaves ? kSlices / kWaves : 1;
 
-  static_assert((BM == 64 && BN == 64) || (BM == 32 && BN == 128), "64 x 64 or 32 x 128 tiles");
+  static_assert((BM == BN && (BM == 32 || BM == 64)) || (BM == 32 && BN == 128), "64x64, 32x32 or 32x128 tiles");
   static_assert(kPieceA % kABlock == 0 && kPieceB % kBBlock == 0 && BN % kBCopyFloats == 0,
                 "copies cover whole pieces");
   static_assert(S == 2 || S == 4, "an even ring depth: stage and operand buffer cycle together");

@@ -407,14 +407,16 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     // largest that still gives every CU a tile; a last partial wave of up to
     // half the CUs is spread over every CU (launch_ksplit_tail). 128x128
     // tiles where they make whole waves, three waves or more, or a last wave
-    // more than three quarters full; else 64x64, whose two workgroups per CU
-    // even out a partial wave better (measured on MI355X, us per call, 128x128
-    // vs 64x64 tiles: 2047^3 128 vs 138, 1024 x 6144 x 4095 358 vs 395,
-    // 3584^3 675 vs 694, 2816^3 336 vs 354; but 2304^3 237 vs 194, 2560^3 305
-    // vs 261, 2303 x 2305 x 2307 269 vs 206, 4095 x 2049 x 2051 296 vs 285,
-    // 3072^3 432 vs 440).
+    // more than three quarters full (with every row aligned, where the 64x64
+    // tiles go through LDS, from two waves on); else 64x64, whose two
+    // workgroups per CU even out a partial wave better (measured on MI355X,
+    // us per call, 128x128 vs 64x64 tiles: 2047^3 128 vs 138, 1024 x 6144 x
+    // 4095 358 vs 395, 3584^3 675 vs 694, 2816^3 336 vs 354, aligned 3072^3
+    // 430 vs 449; but 2304^3 237 vs 194, 2560^3 305 vs 261, 2303 x 2305 x 2307
+    // 269 vs 206, 4095 x 2049 x 2051 296 vs 285, 3001^3 442 vs 438).
     const int64_t rem128 = t128 % cus;
-    if (ksplit128_ok(K) && t128 >= cus && (rem128 == 0 || t128 >= 3 * cus || 4 * rem128 > 3 * cus)) {
+    const int64_t waves128 = rows == Rows::kAll ? 2 : 3;
+    if (ksplit128_ok(K) && t128 >= cus && (rem128 == 0 || t128 >= waves128 * cus || 4 * rem128 > 3 * cus)) {
       if (rem128 != 0 && rem128 <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
     }
@@ -853,21 +855,27 @@ int launch_ksplit_cfg(const float* A, const float* B, float* C, int M, int N, in
 }
 
 // k-split configurations by tile and by the row alignment of the product.
-// 64x64 tiles with 16-byte rows of A, B and C, and the skinny 32x128 tiles:
-// direct copies through LDS (KsplitConfig; 32x128 with 4-byte copies of an
-// operand whose rows are not 16-byte aligned). All other tiles (128x128,
-// 32x32, 64x64 with unaligned rows): operands loaded straight into registers
-// at any 4-byte alignment (KregConfig; 128x128 needs K >= 4 and 64x64 K >= 2,
-// run() maps K = 1 to 32x32).
+// 64x64 and 32x32 tiles with 16-byte rows of A, B and C, and the skinny
+// 32x128 tiles: direct copies through LDS (KsplitConfig; 32x128 with 4-byte
+// copies of an operand whose rows are not 16-byte aligned). All other tiles
+// (128x128; 64x64 and 32x32 with unaligned rows): operands loaded straight
+// into registers at any 4-byte alignment (KregConfig; 128x128 needs K >= 4
+// and 64x64 K >= 2, run() maps K = 1 to 32x32). Measured on MI355X (us per
+// call), aligned rows, LDS vs registers: 64x64 96 x 8192 x 4096 67 vs 84,
+// 2048^3 134 vs 139; 32x32 96 x 8192 x 4096 (split) 81 vs 97; unaligned rows,
+// 4-byte copies vs registers: 64x64 1023 x 1025 x 1023 27.6 vs 21.4, 2047 x
+// 2049 x 2051 227 vs 173; 32x32 250 x 1001 x 250 11.4 vs 7.2.
 constexpr int kKregDepth = 2;  // chunks of operands in registers: deeper rings measured slower
 
 template <int BM, int BN = BM>
 int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int M, int N, int K, int64_t count,
                        hipStream_t s, int parts, float* W, int first, int compact, int nfull) {
   if constexpr (BM == BN) {
-    if (BM == 64 && rows == Rows::kAll)
-      return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true>>(A, B, C, M, N, K, count, s, parts, W, first,
-                                                               compact, nfull);
+    if constexpr (BM <= 64) {
+      if (rows == Rows::kAll)
+        return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true>>(A, B, C, M, N, K, count, s, parts, W, first,
+                                                                 compact, nfull);
+    }
     if (K < BM / 32) return FGR_ERR_BAD_PATH;
     return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth>>(A, B, C, M, N, K, count, s, parts, W, first, compact,
                                                              nfull);

@@ -12,8 +12,8 @@
 // leave alone.
 //
 // A workgroup takes four rows of A, one per wave. It stages B's strip (rows
-// nb .. nb + len - 1, columns c0 .. K - 1, w floats per row, row-major) in the
-// LDS it is given, read once for its four rows; lane l then takes reduction
+// nb .. nb + len - 1, columns c0 .. K - 1, column by column) in the LDS it is
+// given, read once for its four rows; lane l then takes reduction
 // indices nb + 4 l + 256 u .. + 3 of its row (one 16-byte load each, for
 // which 4-byte alignment suffices), keeping w partial sums. The
 // lanes' sums are added across the wave (xor shuffles: every lane ends with
@@ -34,8 +34,8 @@ constexpr int kStripRows = 4;   // rows of A per workgroup (one per wave of 256 
 constexpr int kStripLoads = 8;  // loads each thread keeps in flight
 
 // Rows kStripRows b .. kStripRows b + 3 of the strip (rows past M idle but
-// take part in the barriers). stage: lds_floats floats of LDS (at least
-// kStripMax), overwritten.
+// take part in the barriers). stage: lds_floats floats of LDS, 16-byte
+// aligned, at least 68 kStripMax, overwritten.
 __device__ __forceinline__ void strip_rows(const float* __restrict__ A, const float* __restrict__ B,
                                            float* __restrict__ C, int M, int N, int K, int c0, int b, float* stage,
                                            int lds_floats) {
@@ -44,28 +44,37 @@ __device__ __forceinline__ void strip_rows(const float* __restrict__ A, const fl
   const int lane = tid & 63;
   const bool row_ok = m < M;
   const int w = K - c0;  // 1 .. kStripMax
-  const int chunk = lds_floats / w;  // rows of B's strip staged at a time
+  // B's strip is staged column by column: rows nb .. nb + len - 1 of column
+  // c0 + j at stage[j * pitch + (n - nb)], zeros after them up to a multiple
+  // of 4 rows, so that a lane reads its four consecutive rows of a column
+  // with one 16-byte LDS read, the lanes' reads side by side (no bank
+  // conflicts; row-major staging put the lanes 4 w floats apart, a 32-way
+  // conflict at w = 8). pitch = 4 mod 64 spreads the staging writes of the
+  // columns over the banks.
+  const int pitch = (((lds_floats / w) - 4) & ~63) + 4;  // rows of B's strip staged at a time
   const float* a = A + (int64_t)(row_ok ? m : 0) * N;
   float acc[kStripMax];
 #pragma unroll
   for (int j = 0; j < kStripMax; ++j) acc[j] = 0.f;
   constexpr int kRowQuads = kStripLoads / 2;  // 16-byte loads of A per lane per round
-  for (int nb = 0; nb < N; nb += chunk) {
-    const int len = N - nb < chunk ? N - nb : chunk;
+  for (int nb = 0; nb < N; nb += pitch) {
+    const int len = N - nb < pitch ? N - nb : pitch;
+    const int len4 = (len + 3) & ~3;
     __syncthreads();  // the previous chunk has been read by every wave
-    const int total = len * w;
+    const int total = len4 * w;
     for (int i0 = tid; i0 < total; i0 += 64 * kStripRows * kStripLoads) {
       float v[kStripLoads];
 #pragma unroll
       for (int u = 0; u < kStripLoads; ++u) {
         const int i = i0 + u * 64 * kStripRows;
         const int n = i / w;
-        v[u] = i < total ? B[(int64_t)(nb + n) * K + c0 + (i - n * w)] : 0.f;
+        v[u] = i < total && n < len ? B[(int64_t)(nb + n) * K + c0 + (i - n * w)] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < kStripLoads; ++u) {
         const int i = i0 + u * 64 * kStripRows;
-        if (i < total) stage[i] = v[u];
+        const int n = i / w;
+        if (i < total) stage[(i - n * w) * pitch + n] = v[u];
       }
     }
     __syncthreads();
@@ -88,16 +97,14 @@ __device__ __forceinline__ void strip_rows(const float* __restrict__ A, const fl
         }
 #pragma unroll
         for (int u = 0; u < kRowQuads; ++u) {
-          const int n = n0 + 256 * u;
-          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          const int r = n0 + 256 * u - nb;  // a multiple of 4
+          if (r < len) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (n + q < nb + len) {
-              const float* bn = stage + (n + q - nb) * w;
-#pragma unroll
-              for (int j = 0; j < kStripMax; ++j)
-                if (j < w) acc[j] += e[q] * bn[j];
-            }
+            for (int j = 0; j < kStripMax; ++j)
+              if (j < w) {
+                const float4 bq = *reinterpret_cast<const float4*>(stage + j * pitch + r);
+                acc[j] += ((v[u].x * bq.x + v[u].y * bq.y) + v[u].z * bq.z) + v[u].w * bq.w;
+              }
           }
         }
       }

@@ -42,8 +42,10 @@ RULES = [
                             ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
       ((3001, 3001, 3001), [("auto (64x64, 161 left over)", AUTO),
                             ("MFMA_KSPLIT_TAIL 64", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 64))])]),
-    ("128x128 or 64x64 k-split tiles", "t128 == 0 mod cus, t128 >= 3 cus or a last wave > 3 cus / 4 (choose)",
-     "128x128 tiles in whole waves, from three waves on or with a last wave more than 3/4 full; else 64x64",
+    ("128x128 or 64x64 k-split tiles",
+     "t128 == 0 mod cus, t128 >= 3 cus (2 cus with aligned rows) or a last wave > 3 cus / 4 (choose)",
+     "128x128 tiles in whole waves, from three waves on (two with every row aligned) or with a last wave "
+     "more than 3/4 full; else 64x64",
      [((2047, 2047, 2047), [("auto (128x128, one wave)", AUTO),
                             ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
       ((2816, 2816, 2816), [("auto (128x128, 484 tiles)", AUTO),
@@ -52,7 +54,9 @@ RULES = [
                             ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))]),
       ((2560, 2560, 2560), [("auto (64x64; 400 of 128)", AUTO),
                             ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
-      ((3072, 3072, 3072), [("auto (64x64; 576 of 128)", AUTO),
+      ((3072, 3072, 3072), [("auto (aligned, 128x128; 576 of 128)", AUTO),
+                            ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
+      ((3001, 3001, 3001), [("auto (64x64; 576 of 128)", AUTO),
                             ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))])]),
     ("Short reductions", "kShortReduction = 104 (choose)",
      "N < 104 with a 64x64 tile per CU: register-staged 64x64 tiles instead of the direct-copy kernel",

@@ -196,10 +196,12 @@ def test_path_selection_rules():
     assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 4-byte copies
     assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_KSPLIT  # 64 tiles of 256, 256 of 128
     assert sp(A0, B0, C0, 1024, 6144, 4096) == fgr.PATH_MFMA_KSPLIT  # a row shard of the timed shape
-    # 128x128 tiles in whole waves, three waves or more, or a last wave more
-    # than three quarters full; else 64x64 tiles
-    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT  # 576 of 128 (2.25 waves): 2304 of 64
-    assert st(A0, B0, C0, 3072, 3072, 3072) == 64
+    # 128x128 tiles in whole waves, three waves or more (two with every row
+    # aligned), or a last wave more than three quarters full; else 64x64 tiles
+    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT_TAIL  # 576 of 128 (2.25 waves), aligned
+    assert st(A0, B0, C0, 3072, 3072, 3072) == 128
+    assert sp(A0, B0, C0, 3001, 3001, 3001) == fgr.PATH_MFMA_KSPLIT  # 576 of 128, unaligned: 2209 of 64
+    assert st(A0, B0, C0, 3001, 3001, 3001) == 64
     assert sp(A0, B0, C0, 2000, 3000, 2100) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 128: 1056 of 64
     assert st(A0, B0, C0, 2000, 3000, 2100) == 64
     assert sp(A0, B0, C0, 2304, 2304, 2304) == fgr.PATH_MFMA_KSPLIT_TAIL  # 324 of 128: 1296 of 64
