@@ -40,8 +40,8 @@ namespace fgr {
 
 // BM x BM tiles (32, 64 or 128); D chunks of operands in registers; STRIP as
 // in KsplitConfig (the column strip on the vector ALUs in the same launch).
-// The four partial tiles pass through LDS four at a time, or two at a time at
-// BM = 128 (four would need 256 KB).
+// The four partial tiles pass through LDS all at once, or at BM = 128 half a
+// tile at a time (four whole partials would need 256 KB).
 template <int BM_, int D_, bool STRIP_ = false>
 struct KregConfig {
   static constexpr int BM = BM_, BN = BM_, BK = 8, D = D_;
@@ -52,9 +52,10 @@ struct KregConfig {
   static constexpr int kRB = BM / 32, kCB = BN / 32;
   static constexpr int kSlices = kRB * kCB;  // MFMA blocks of a tile
   static constexpr int kPartial = BM * BN;   // floats of one wave's partial tile
-  static constexpr int kAtOnce = BM == 128 ? 2 : 4;  // partials in LDS at a time
+  static constexpr int kAtOnce = BM == 128 ? 2 : 4;  // whole partials' worth of LDS
   static constexpr int kLds = kAtOnce * kPartial;
-  // a wave's share of the reduced tile: kPairs (MFMA block, accumulator group) pairs
+  // a wave's share of the reduced tile (32x32, 64x64): kPairs (MFMA block,
+  // accumulator group) pairs
   static constexpr int kPairs = kSlices * 4 / kWaves;
   static_assert(BM == 32 || BM == 64 || BM == 128, "32x32, 64x64 or 128x128 tiles");
   static_assert(D >= 2 && D <= 4, "two to four chunks in registers");
@@ -182,14 +183,18 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
   // with the move; moving both operands: 142; reordering the MFMAs instead:
   // 183). The same move cost 3-8% at 32x32 and 4% at 128x128 (one wave per
   // SIMD), which go without it. The asm keeps the compiler from folding the
-  // move away.
+  // move away; since the compiler does not take the asm for a vector-ALU
+  // write, the asm itself carries the two wait states that an MFMA reading a
+  // register needs after such a write (the compiler, counting the asm as one,
+  // would leave a single one, and the MFMA could read the register's
+  // previous value).
   auto b_of = [&](const Frag& f, int j, int t) __attribute__((always_inline)) {
     float v;
     if constexpr (kCB == 1) {
       v = f.b[t];
     } else if constexpr (kCB == 2) {
       v = j == 0 ? f.b[t].x : f.b[t].y;
-      if (j == 0) asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(v));
+      if (j == 0) asm volatile("v_mov_b32 %0, %1\n\ts_nop 1" : "=v"(v) : "v"(v));
     } else {
       v = j == 0 ? f.b[t].x : j == 1 ? f.b[t].y : j == 2 ? f.b[t].z : f.b[t].w;
     }
@@ -265,43 +270,42 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
   // the tile, kPairs (slice, accumulator group q) pairs:
   //   32x32: group q = w;
   //   64x64: block row i = w / 2, both column blocks, groups 2 (w % 2) and
-  //          2 (w % 2) + 1 (pair u: j = u % 2, q = 2 (w % 2) + u / 2);
-  //   128x128: block row w, all four column blocks and groups (j = u % 4, q = u / 4).
+  //          2 (w % 2) + 1 (pair u: j = u % 2, q = 2 (w % 2) + u / 2).
+  // 128x128 tiles reduce half a tile at a time after the store set-up below.
   auto pair_of = [&](int u, int& sl, int& q) __attribute__((always_inline)) {
     if constexpr (T::BM == 32) {
       sl = 0;
       q = wave;
-    } else if constexpr (T::BM == 64) {
+    } else {
       sl = 2 * (wave >> 1) + (u & 1);
       q = 2 * (wave & 1) + (u >> 1);
-    } else {
-      sl = 4 * wave + (u & 3);
-      q = u >> 2;
     }
   };
   float4 sum[T::kPairs];
+  if constexpr (T::kAtOnce == 4) {
 #pragma unroll
-  for (int ph = 0; ph < T::kWaves / T::kAtOnce; ++ph) {
-    if (ph > 0) __syncthreads();  // the last phase's partials have been read
-    if (wave / T::kAtOnce == ph) {
-      float* mine = red + (wave % T::kAtOnce) * T::kPartial;
+    for (int ph = 0; ph < T::kWaves / T::kAtOnce; ++ph) {
+      if (ph > 0) __syncthreads();  // the last phase's partials have been read
+      if (wave / T::kAtOnce == ph) {
+        float* mine = red + (wave % T::kAtOnce) * T::kPartial;
 #pragma unroll
-      for (int sl = 0; sl < T::kSlices; ++sl)
+        for (int sl = 0; sl < T::kSlices; ++sl)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(mine + sl * 1024 + 256 * q + 4 * lane) =
-              make_float4(acc[sl / kCB][sl % kCB][4 * q], acc[sl / kCB][sl % kCB][4 * q + 1],
-                          acc[sl / kCB][sl % kCB][4 * q + 2], acc[sl / kCB][sl % kCB][4 * q + 3]);
-    }
-    __syncthreads();
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(mine + sl * 1024 + 256 * q + 4 * lane) =
+                make_float4(acc[sl / kCB][sl % kCB][4 * q], acc[sl / kCB][sl % kCB][4 * q + 1],
+                            acc[sl / kCB][sl % kCB][4 * q + 2], acc[sl / kCB][sl % kCB][4 * q + 3]);
+      }
+      __syncthreads();
 #pragma unroll
-    for (int u = 0; u < T::kPairs; ++u) {
-      int sl, q;
-      pair_of(u, sl, q);
+      for (int u = 0; u < T::kPairs; ++u) {
+        int sl, q;
+        pair_of(u, sl, q);
 #pragma unroll
-      for (int p = 0; p < T::kAtOnce; ++p) {
-        const float4 v = *reinterpret_cast<const float4*>(red + p * T::kPartial + sl * 1024 + 256 * q + 4 * lane);
-        sum[u] = ph == 0 && p == 0 ? v : make_float4(sum[u].x + v.x, sum[u].y + v.y, sum[u].z + v.z, sum[u].w + v.w);
+        for (int p = 0; p < T::kAtOnce; ++p) {
+          const float4 v = *reinterpret_cast<const float4*>(red + p * T::kPartial + sl * 1024 + 256 * q + 4 * lane);
+          sum[u] = ph == 0 && p == 0 ? v : make_float4(sum[u].x + v.x, sum[u].y + v.y, sum[u].z + v.z, sum[u].w + v.w);
+        }
       }
     }
   }
@@ -341,6 +345,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
         if (j >= shift) dst[j] = e[j];
     }
   };
+
   if constexpr (T::BM == 32) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -357,14 +362,60 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
         store_row(i * 32 + 8 * (2 * (wave & 1) + qq) + 4 * lg + k, e);
       }
   } else {
+    // 128x128: the tile in two halves of 8 MFMA blocks (block rows 2h and
+    // 2h + 1), all four partials of a half at once (4 x 32 KiB). Wave w's
+    // share of half h: block row 2h + w / 2, column blocks 2 (w % 2) and
+    // 2 (w % 2) + 1, every accumulator group; a lane stores its two adjacent
+    // columns of those blocks together. (Two whole partials at a time instead
+    // needed a running sum, or adds into a wave's accumulators, kept across a
+    // barrier: 12 to 16 VGPRs spilled.)
+    constexpr int kHalf = T::kSlices / 2;  // MFMA blocks per half
+    auto half_slot = [&](int p) __attribute__((always_inline)) { return red + p * (kHalf * 1024); };
+    const int j0 = 2 * (wave & 1);  // the share's first column block
+    auto add4 = [](float4 x, float4 y) __attribute__((always_inline)) {
+      return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    };
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int h = 0; h < 2; ++h) {
+      if (h > 0) __syncthreads();  // the first half has been read
+      float* mine = half_slot(wave);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float e[4] = {comp(sum[4 * q], k), comp(sum[4 * q + 1], k), comp(sum[4 * q + 2], k),
-                            comp(sum[4 * q + 3], k)};
-        store_row(32 * wave + 8 * q + 4 * lg + k, e);
+      for (int b = 0; b < kHalf; ++b) {
+        const int sl = kHalf * h + b;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(mine + b * 1024 + 256 * q + 4 * lane) =
+              make_float4(acc[sl / kCB][sl % kCB][4 * q], acc[sl / kCB][sl % kCB][4 * q + 1],
+                          acc[sl / kCB][sl % kCB][4 * q + 2], acc[sl / kCB][sl % kCB][4 * q + 3]);
       }
+      __syncthreads();
+      const int br = 2 * h + (wave >> 1);  // block row
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 v[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int b = 4 * (wave >> 1) + j0 + jj;  // block inside the half
+          auto at = [&](int p) __attribute__((always_inline)) {
+            return *reinterpret_cast<const float4*>(half_slot(p) + b * 1024 + 256 * q + 4 * lane);
+          };
+          v[jj] = add4(add4(add4(at(0), at(1)), at(2)), at(3));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int row = 32 * br + 8 * q + 4 * lg + k;
+          if (m0 + row >= M) continue;
+          float* dst = Ct + (int64_t)row * (int64_t)ldc + col + j0;
+          const float e0 = comp(v[0], k), e1 = comp(v[1], k);
+          if (whole_cols) {
+            store_dwords<float2>(dst, make_float2(e0, e1));
+          } else {
+            if (j0 >= shift) dst[0] = e0;
+            if (j0 + 1 >= shift) dst[1] = e1;
+          }
+        }
+      }
+    }
   }
 }
 
