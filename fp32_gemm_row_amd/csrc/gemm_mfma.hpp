@@ -467,14 +467,26 @@ __global__ __launch_bounds__(T::kThreads, T::kMinBlocks) void gemm_mfma_kernel(
 
   // Epilogue: element r of lane l in block (i, j) is row 8*(r/4) + 4*lg + r%4,
   // column li of that block. Each half-wave stores 32 consecutive floats.
+  // The 32-bit-copy forms, whose loops leave no register to carry the lane's
+  // indices across, take them afresh: the wave from a scalar copy made at the
+  // start, the lane from mbcnt.
+  int ewm = wm, ewn = wn, eli = li, elg = lg;
+  if constexpr (!VEC) {
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    ewm = w / WN;
+    ewn = w % WN;
+    eli = el & 31;
+    elg = el >> 5;
+  }
 #pragma unroll
   for (int i = 0; i < T::kRB; ++i)
 #pragma unroll
     for (int j = 0; j < T::kCB; ++j) {
-      const int col = k0 + wn * T::kWaveN + j * 32 + li;
+      const int col = k0 + ewn * T::kWaveN + j * 32 + eli;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        const int row = m0 + ewm * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * elg + (r % 4);
         if (row < M && col < K) C[(int64_t)row * K + col] = acc[i][j][r];
       }
     }

@@ -368,14 +368,23 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // With 16-byte rows (K % 4 == 0) a lane's 4 adjacent columns start at a
   // multiple of 4, so they are wholly inside or outside; otherwise each column
   // is guarded and stored alone.
+  // The 32-bit-store forms take the lane's index afresh from mbcnt, so that
+  // nothing derived from it has to stay live across the loop (their loops
+  // leave no register for it).
+  int eli = li, elg = lg;
+  if constexpr (!T::VC) {
+    const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    eli = elane & 31;
+    elg = elane >> 5;
+  }
   float* const Ct = C + (int64_t)m0 * K + k0;
-  const int col = wn * T::kWaveN + 4 * li;
+  const int col = wn * T::kWaveN + 4 * eli;
   const bool col_ok = k0 + col < K;
 #pragma unroll
   for (int i = 0; i < T::kRB; ++i)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int row = wm * T::kWaveM + i * 32 + 8 * (rr / 4) + 4 * lg + (rr % 4);
+      const int row = wm * T::kWaveM + i * 32 + 8 * (rr / 4) + 4 * elg + (rr % 4);
       if (col_ok && m0 + row < M) {
         float* dst = Ct + (uint64_t)row * (uint32_t)K + (uint32_t)col;
         if constexpr (T::VC) {

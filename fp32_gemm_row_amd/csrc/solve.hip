@@ -723,6 +723,9 @@ int launch_mfma(const float* A, const float* B, float* C, int M, int N, int K, h
 }
 
 using Tile256 = fgr::MfmaConfig<256, 256, 32, 2, 4>;  // 8 waves, 128x64 each
+// 32-bit loads stage four times as many registers per chunk: 16-deep chunks
+// keep them within the register budget (32-deep ones spilled)
+using Tile256Scalar = fgr::MfmaConfig<256, 256, 16, 2, 4>;
 using TileDma = fgr::DmaConfig<4>;  // 256x256, 4 waves of 128x128 (accumulators in AGPRs), 4 LDS stages
 // 4-byte copies for rows that are not 16-byte aligned: four times as many, so
 // 3 stages (the copies in flight must fit the wave's vmcnt counter)
@@ -764,7 +767,9 @@ template <bool VEC>
 int launch_mfma_tile(int tile, const float* A, const float* B, float* C, int M, int N, int K,
                      hipStream_t s) {
   switch (tile) {
-    case FGR_TILE_256: return launch_mfma<Tile256, VEC>(A, B, C, M, N, K, s);
+    case FGR_TILE_256:
+      if constexpr (VEC) return launch_mfma<Tile256, true>(A, B, C, M, N, K, s);
+      else return launch_mfma<Tile256Scalar, false>(A, B, C, M, N, K, s);
     case FGR_TILE_128: return launch_mfma<Tile128, VEC>(A, B, C, M, N, K, s);
     case FGR_TILE_64: return launch_mfma<Tile64, VEC>(A, B, C, M, N, K, s);
     default: return FGR_ERR_BAD_PATH;
