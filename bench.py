@@ -7,7 +7,9 @@
 One step is one call of the library's solve() on the workload's inputs,
 which are already resident in HBM when the timed region starts. W untimed
 steps, then exactly K steps between two device synchronisations on the host
-clock. Prints ONE JSON line:
+clock. Without --warmup, W is as many steps as take about 0.3 s (at least 5):
+the GPU's clock climbs over the first tens of milliseconds of work, which a
+few launches of a small shape never reach. Prints ONE JSON line:
 
   value        whole-job throughput over the K steps (TFLOP/s = 2MNK / time;
                GB/s of algorithmic bytes for the matrix-vector workload)
@@ -63,6 +65,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X: 256 CU x 256 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+WARMUP_SECONDS = 0.3  # default warm-up: the clock climbs over the first tens of ms of work
 METRIC = "FP32 GEMM TFLOP/s at M=8192,N=6144,K=4096; % of MI355X FP32 MFMA peak"
 # every source the library is built from (csrc/*.hpp and csrc/*.hip)
 KERNEL_SOURCES = sorted(n for n in os.listdir(os.path.join(ROOT, "fp32_gemm_row_amd", "csrc"))
@@ -667,7 +670,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: about 0.3 s of steps, at least 5; 5 for the "
+                         "summaries, the ablation and the read ceiling)")
     ap.add_argument("--workload", default="leetgpu8192")
     ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"), default=None,
                     help="time this shape instead of a named workload (uniform [-1,1) inputs, --seed)")
@@ -708,6 +713,9 @@ def main() -> int:
     ap.add_argument("--command", action="append", default=[],
                     help="(with --summarize) a command that produced the folders, recorded in the summary")
     args = ap.parse_args()
+    auto_warmup = args.warmup is None
+    if auto_warmup:
+        args.warmup = 5
 
     if args.summarize_ablation:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_controlled_comparison.md")
@@ -786,6 +794,13 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if auto_warmup:  # until about 0.3 s of steps have run (the clock has climbed)
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < WARMUP_SECONDS:
+            for _ in range(5):
+                step(args.warmup)
+                args.warmup += 1
+            torch.cuda.synchronize()
 
     # The timed region: K steps back to back, one HIP event pair around them
     # on the launch stream (an event record between steps costs the GPU about
