@@ -73,6 +73,7 @@ EXPORTS = (
     "fgr_solve_path",
     "fgr_select_path",
     "fgr_select_tile",
+    "fgr_select_parts",
     "fgr_status_string",
     "fgr_version",
     "fgr_variant_count",
@@ -115,6 +116,8 @@ def load_library(path: str = LIB_PATH):
     lib.fgr_select_path.restype = ci
     lib.fgr_select_tile.argtypes = [vp, vp, vp, ci, ci, ci]
     lib.fgr_select_tile.restype = ci
+    lib.fgr_select_parts.argtypes = [vp, vp, vp, ci, ci, ci]
+    lib.fgr_select_parts.restype = ci
     lib.fgr_status_string.argtypes = [ci]
     lib.fgr_status_string.restype = ctypes.c_char_p
     lib.fgr_version.argtypes = []
@@ -246,6 +249,11 @@ def select_path(A, B, C, M: int, N: int, K: int) -> int:
 def select_tile(A, B, C, M: int, N: int, K: int) -> int:
     """The output tile solve() would use with that path (host-only; negative = error code)."""
     return int(load_library().fgr_select_tile(_raw(A), _raw(B), _raw(C), int(M), int(N), int(K)))
+
+
+def select_parts(A, B, C, M: int, N: int, K: int) -> int:
+    """Workgroups per tile's reduction on the split path (1 on any other; host-only)."""
+    return int(load_library().fgr_select_parts(_raw(A), _raw(B), _raw(C), int(M), int(N), int(K)))
 
 
 def version() -> int:

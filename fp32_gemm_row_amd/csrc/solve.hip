@@ -234,13 +234,22 @@ double splitk_time(int t, int p, int M, int N, int K, int cus) {
   return std::max(host, gpu) + 1e-3 * gpu;  // the small second term breaks ties
 }
 
-// Parts to try: powers of two, each part at least 256 reduction indices long
-// (32 chunks, 8 per wave), at most four workgroups per CU.
+// Parts to try: powers of two and, with `rounds`, the counts that fill whole
+// rounds of the CUs (k CUs / tiles, k = 1 .. 4: with few tiles a power of two
+// either leaves CUs idle or starts a second round, e.g. nine 128x128 tiles:
+// 16 parts on 144 CUs or 32 in two rounds, against 28); each part at least
+// 256 reduction indices long (32 chunks, 8 per wave), at most four
+// workgroups per CU.
 constexpr int kSplitkMinPart = 256;
 template <class F>
-void for_each_parts(int t, int M, int N, int K, int cus, F&& f) {
+void for_each_parts(int t, int M, int N, int K, int cus, bool rounds, F&& f) {
   const int64_t tiles = cdiv(M, t) * cdiv(K, t);
-  for (int p = 2; N / p >= kSplitkMinPart && tiles * p <= 4 * (int64_t)cus; p *= 2) f(p);
+  auto ok = [&](int64_t p) { return p >= 2 && N / p >= kSplitkMinPart && tiles * p <= 4 * (int64_t)cus; };
+  for (int p = 2; ok(p); p *= 2) f(p);
+  for (int k = 1; rounds && k <= 4; ++k) {
+    const int64_t p = k * (int64_t)cus / tiles;
+    if (ok(p) && (p & (p - 1)) != 0) f((int)p);  // powers of two came above
+  }
 }
 
 // Split plans with 128x128 tiles: taken over the estimate's 64x64 or 32x32
@@ -258,11 +267,16 @@ void for_each_parts(int t, int M, int N, int K, int cus, F&& f) {
 // 200000 x 320 412 vs 572).
 constexpr int kSplitk128MinPart = 2048;
 
-// Best parts (>= 2) for k-split tiles of size t, by the estimate above.
-SplitPlan splitk_plan_tile(int t, int M, int N, int K, int cus) {
+// Best parts (>= 2) for k-split tiles of size t, by the estimate above, over
+// power-of-two parts or (rounds) also the whole-round counts; with rounds,
+// 128x128 tiles take only parts of at least kSplitk128MinPart (two parts
+// where none is that long).
+SplitPlan splitk_plan_tile(int t, int M, int N, int K, int cus, bool rounds) {
   SplitPlan best{t, 2};
   double best_time = 0;
-  for_each_parts(t, M, N, K, cus, [&](int p) {
+  const int min_part = rounds && t == FGR_TILE_128 ? kSplitk128MinPart : kSplitkMinPart;
+  for_each_parts(t, M, N, K, cus, rounds, [&](int p) {
+    if (N / p < min_part) return;
     const double e = splitk_time(t, p, M, N, K, cus);
     if (best_time == 0 || e < best_time) {
       best = {t, p};
@@ -273,7 +287,17 @@ SplitPlan splitk_plan_tile(int t, int M, int N, int K, int cus) {
 }
 
 // For a shape with fewer 64x64 tiles than CUs: the k-split tile size (64 or
-// 32) and parts (1: no split) with the smallest estimated time.
+// 32) and parts (1: no split) with the smallest estimated time, over
+// power-of-two parts. The launch then takes the tile's best parts among the
+// whole-round counts too (splitk_plan_tile with rounds). Choosing the tile
+// over those counts as well was measured on 62 few-tile shapes (MI355X, us
+// per call against power-of-two plans): keeping the tile, worst +1.4% and
+// mean -4.1% (384 x 131072 x 384 385 vs 290, 640 x 65536 x 640 483 vs 392,
+// 384 x 32768 x 384 108 vs 87); re-choosing it gained more on short
+// reductions (mean -10.7%) but lost up to 34% where the estimate misjudges
+// 32x32 tiles (96 x 262144 x 384 226 vs 302), and offering those counts
+// against no split turned short reductions into splits that lost up to 34%
+// (320 x 1024 x 1000 13.2 vs 17.7).
 SplitPlan splitk_plan(int M, int N, int K, int cus) {
   SplitPlan best{FGR_TILE_32, 1};
   double best_time = splitk_time(FGR_TILE_32, 1, M, N, K, cus);
@@ -286,7 +310,7 @@ SplitPlan splitk_plan(int M, int N, int K, int cus) {
       }
     };
     consider(1);
-    for_each_parts(t, M, N, K, cus, consider);
+    for_each_parts(t, M, N, K, cus, false, consider);
   }
   return best;
 }
@@ -436,7 +460,7 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     const SplitPlan sp = splitk_plan(M, N, K, cus);
     if (sp.parts >= 2) {
       if (ksplit128_ok(K) && 4 * cdiv(M, 128) * cdiv(K, 128) == t64 &&
-          N / splitk_plan_tile(FGR_TILE_128, M, N, K, cus).parts >= kSplitk128MinPart)
+          N / splitk_plan_tile(FGR_TILE_128, M, N, K, cus, false).parts >= kSplitk128MinPart)
         return {FGR_PATH_MFMA_SPLITK, FGR_TILE_128};
       return {FGR_PATH_MFMA_SPLITK, sp.tile};
     }
@@ -963,10 +987,15 @@ bool vec4_rows(const float* C, int M, int K) { return ((int64_t)M * K) % 4 == 0 
 // tiles into a stream-ordered workspace, then added in part order (two parts
 // where no longer parts fit the estimate's limits). Without a
 // workspace (allocation failed) the tiles keep their whole reduction.
+int split_parts(int tile, int M, int N, int K, int cus) {
+  const int parts =
+      tile == FGR_TILE_32X128 ? skinny_parts(M, N, K, cus) : splitk_plan_tile(tile, M, N, K, cus, true).parts;
+  return parts < 2 ? 2 : parts;  // N >= 128 gives 8 chunks per part
+}
+
 int launch_ksplit_parts(int tile, const float* A, const float* B, float* C, int M, int N, int K, int cus,
                         hipStream_t s) {
-  int parts = tile == FGR_TILE_32X128 ? skinny_parts(M, N, K, cus) : splitk_plan_tile(tile, M, N, K, cus).parts;
-  if (parts < 2) parts = 2;  // N >= 128 gives 8 chunks per part
+  const int parts = split_parts(tile, M, N, K, cus);
   Workspace ws;
   if (alloc_floats(ws, (size_t)parts * (size_t)M * (size_t)K, s) != FGR_OK)
     return launch_ksplit(tile, A, B, C, M, N, K, -1, s);
@@ -1314,6 +1343,13 @@ int fgr_select_tile(const float* A, const float* B, const float* C, int M, int N
   const int rc = check_args(A, B, C, M, N, K);
   if (rc != FGR_OK) return rc;
   return choose(A, B, C, M, N, K, kDefaultCus).tile;
+}
+
+int fgr_select_parts(const float* A, const float* B, const float* C, int M, int N, int K) {
+  const int rc = check_args(A, B, C, M, N, K);
+  if (rc != FGR_OK) return rc;
+  const Choice c = choose(A, B, C, M, N, K, kDefaultCus);
+  return c.path == FGR_PATH_MFMA_SPLITK ? split_parts(c.tile, M, N, K, kDefaultCus) : 1;
 }
 
 const char* fgr_status_string(int status) {

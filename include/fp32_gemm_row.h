@@ -247,6 +247,15 @@ int fgr_select_path(const float *A, const float *B, const float *C, int M, int N
  */
 int fgr_select_tile(const float *A, const float *B, const float *C, int M, int N, int K);
 
+/*
+ * fgr_select_parts - the number of workgroups each output tile's reduction is
+ * split over when fgr_select_path() reports FGR_PATH_MFMA_SPLITK (1 for every
+ * other path), on a 256-CU device, or a negative FGR_ERR_* code. Powers of
+ * two, or the counts that fill whole rounds of the CUs (k CUs / tiles, k = 1
+ * .. 4), whichever the time estimate prefers. Host only.
+ */
+int fgr_select_parts(const float *A, const float *B, const float *C, int M, int N, int K);
+
 /* fgr_status_string - a static, human-readable name for a status code. */
 const char *fgr_status_string(int status);
 

@@ -345,6 +345,17 @@ def test_split_reduction_choices():
         assert st(A0, B0, C0, *shape) == tile, shape
     assert st(A0 + 4, B0, C0, 128, 524288, 128) == 128
     assert st(A0 + 4, B0 + 4, C0, 128, 524288, 128) == 128
+    # parts per tile: powers of two, or the counts filling whole rounds of
+    # the 256 CUs (nine 128x128 tiles: 28 parts, 252 workgroups; ten 64x64
+    # tiles: 25); 1 off the split path, error codes for bad arguments
+    parts = fgr.select_parts
+    assert parts(A0, B0, C0, 384, 131072, 384) == 28
+    assert parts(A0, B0, C0, 100, 30000, 300) == 25
+    assert parts(A0, B0, C0, 512, 8192, 512) == 8
+    assert parts(A0, B0, C0, 128, 262144, 128) == 128
+    assert parts(A0, B0, C0, 8192, 6144, 4096) == 1
+    assert parts(A0, B0, C0, 512, 4096, 512) == 1
+    assert parts(A0, B0, C0, 0, 4096, 512) < 0
     # enough 32x32 tiles for every CU, or too short a reduction: no split
     assert sp(A0, B0, C0, 512, 4096, 512) == fgr.PATH_MFMA_KSPLIT
     assert sp(A0, B0, C0, 64, 8192, 4096) == fgr.PATH_MFMA_SPLITK  # skinny: 32x128 tiles

@@ -314,7 +314,7 @@ def test_ksplit_exact(shape, path, tile):
 @pytest.mark.parametrize("shape,tile", [
     ((128, 262144, 128), 64), ((256, 16384, 256), 64), ((100, 30000, 300), 64), ((16, 65536, 64), 32),
     ((130, 20000, 66), 32),
-    ((96, 50001, 97), 64), ((64, 16384, 64), 32), ((512, 8192, 512), 64)], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+    ((96, 50001, 97), 64), ((64, 16384, 64), 32), ((512, 8192, 512), 64), ((384, 131072, 384), 128)], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_split_reduction_exact(shape, tile):
     # few output tiles, long reduction: each tile's reduction split into parts
     # over workgroups, partial tiles added in part order by a second kernel;
@@ -326,7 +326,8 @@ def test_split_reduction_exact(shape, tile):
     Cref, _ = oracle.gemm(A, B)
     assert fgr.select_path(1 << 40, 2 << 40, 3 << 40, M, N, K) == fgr.PATH_MFMA_SPLITK
     assert fgr.select_tile(1 << 40, 2 << 40, 3 << 40, M, N, K) == tile
-    say(f"split reduction {shape}: GPU")
+    assert fgr.select_parts(1 << 40, 2 << 40, 3 << 40, M, N, K) >= 2
+    say(f"split reduction {shape}: GPU ({fgr.select_parts(1 << 40, 2 << 40, 3 << 40, M, N, K)} parts)")
     assert_exact(gpu_gemm(A, B), Cref, f"{shape} auto")
     tiles = [fgr.TILE_64, fgr.TILE_32] + ([fgr.TILE_128] if N % 4 == 0 and K % 4 == 0 else [])
     for t in tiles:
