@@ -316,7 +316,7 @@ SplitPlan splitk_plan(int M, int N, int K, int cus) {
 }
 
 // Skinny outputs (kSkinnyMinM <= M <= 64, K >= 128, B as in skinny_b below):
-// 32x128 k-split tiles, each reduction split into the largest power-of-two number of
+// 32x128 k-split tiles, each reduction split into the largest number of
 // parts that keeps tiles x parts within the CU count and parts at least 512
 // long. The work is streaming B once; wide column blocks and one workgroup
 // per CU measured best (MI355X, TB/s of algorithmic bytes, 32x128 tiles vs
@@ -343,9 +343,7 @@ bool skinny_b(int M, int N, int K, int cus) {
 }
 int skinny_parts(int M, int N, int K, int cus) {
   const int64_t tiles = cdiv(M, 32) * cdiv(K, 128);
-  int p = 1;
-  while (tiles * p * 2 <= cus && N / (p * 2) >= 512) p *= 2;
-  return p;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(cus / tiles, N / 512));
 }
 
 struct Choice {

@@ -311,13 +311,18 @@ def test_skinny_choices():
     sp, st = fgr.select_path, fgr.select_tile
     A0, B0, C0 = 1 << 40, 2 << 40, 3 << 40
     # 5 <= M <= 32 with K >= 128 and B of at least 32 MiB: 32x128 tiles, the
-    # reduction split into the largest power of two of parts that keeps
+    # reduction split into the largest number of parts that keeps
     # tiles x parts <= CUs and parts >= 512 long (none: the k-split path)
     for shape, path in [((16, 4096, 4096), fgr.PATH_MFMA_SPLITK), ((32, 11008, 4096), fgr.PATH_MFMA_SPLITK),
                         ((5, 65536, 256), fgr.PATH_MFMA_SPLITK), ((8, 8192, 28672), fgr.PATH_MFMA_KSPLIT),
                         ((32, 4097, 4099), fgr.PATH_MFMA_SPLITK), ((16, 512, 65536), fgr.PATH_MFMA_KSPLIT)]:
         assert sp(A0, B0, C0, *shape) == path, shape
         assert st(A0, B0, C0, *shape) == fgr.TILE_32X128, shape
+    parts = fgr.select_parts
+    assert parts(A0, B0, C0, 33, 8200, 2052) == 7  # 34 tiles: 238 workgroups
+    assert parts(A0, B0, C0, 16, 100000, 640) == 51  # 5 tiles
+    assert parts(A0, B0, C0, 32, 11008, 4096) == 8  # 32 tiles
+    assert parts(A0, B0, C0, 5, 65536, 256) == 128  # 2 tiles
     assert sp(A0, B0, C0, 4, 8192, 8192) == fgr.PATH_GEMV_VEC  # M < 5: the matrix-vector kernel
     assert st(A0, B0, C0, 64, 8192, 8192) == fgr.TILE_32X128  # two rows of tiles
     assert st(A0, B0, C0, 65, 8192, 8192) == 64  # M > 64: the tile-count rules
