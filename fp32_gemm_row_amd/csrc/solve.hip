@@ -268,13 +268,20 @@ void for_each_parts(int t, int M, int N, int K, int cus, bool rounds, F&& f) {
 constexpr int kSplitk128MinPart = 2048;
 
 // Best parts (>= 2) for k-split tiles of size t, by the estimate above, over
-// power-of-two parts or (rounds) also the whole-round counts; with rounds,
-// 128x128 tiles take only parts of at least kSplitk128MinPart (two parts
-// where none is that long).
+// power-of-two parts or (rounds) also the whole-round counts. With rounds,
+// 128x128 tiles whose power-of-two plan has parts of at least
+// kSplitk128MinPart (the plans choose() takes them for) keep parts that long:
+// shorter ones lost there (896 x 16384 x 1024 247 vs 264 us). A forced
+// 128x128 split elsewhere takes the estimate's count (one 128x128 tile of
+// 128 x 262144 x 128: 128 parts of 2048 on half the CUs ran 60.6 TFLOP/s,
+// 256 of 1024 ran 82.9).
 SplitPlan splitk_plan_tile(int t, int M, int N, int K, int cus, bool rounds) {
   SplitPlan best{t, 2};
   double best_time = 0;
-  const int min_part = rounds && t == FGR_TILE_128 ? kSplitk128MinPart : kSplitkMinPart;
+  const int min_part = rounds && t == FGR_TILE_128 &&
+                               N / splitk_plan_tile(t, M, N, K, cus, false).parts >= kSplitk128MinPart
+                           ? kSplitk128MinPart
+                           : kSplitkMinPart;
   for_each_parts(t, M, N, K, cus, rounds, [&](int p) {
     if (N / p < min_part) return;
     const double e = splitk_time(t, p, M, N, K, cus);
