@@ -3,16 +3,26 @@
 //
 // Same product, output tiling and operand layout as gemm_mfma.hpp, for
 // N >= 64. Every reduction chunk but the first is copied from global memory
-// straight into LDS with global_load_lds_dwordx4 (16 bytes per lane, written
-// to LDS at the M0 base + 16 * lane) when rows are 16-byte aligned (N % 4 ==
-// 0, K % 4 == 0, aligned bases), else with global_load_lds_dword (4 bytes per
-// lane, four times as many copies, the same LDS layout), the gfx950
-// counterpart of the cp.async
-// copies of the LeetGPU write-up's section "V4: Hardware-Asynchronous cp.async
-// Pipeline". The data never passes through VGPRs, so the copies take no
-// register-file bandwidth from the MFMAs and no LDS write instructions are
-// issued. The write-up's Triton solution runs a 3-stage software pipeline;
-// here the ring has S stages (3..5) of BK = 16 reduction indices.
+// straight into LDS with buffer_load_dwordx4 ... lds (16 bytes per lane,
+// written to LDS at the M0 base + 16 * lane) when rows are 16-byte aligned
+// (N % 4 == 0, K % 4 == 0, aligned bases), else with buffer_load_dword ...
+// lds (4 bytes per lane, four times as many copies, the same LDS layout), the
+// gfx950 counterpart of the cp.async copies of the LeetGPU write-up's section
+// "V4: Hardware-Asynchronous cp.async Pipeline". The data never passes
+// through VGPRs, so the copies take no register-file bandwidth from the MFMAs
+// and no LDS write instructions are issued. The write-up's Triton solution
+// runs a 3-stage software pipeline; here the ring has S stages (3..5) of
+// BK = 16 reduction indices.
+//
+// Copy addressing. A copy's source is a buffer resource in scalar registers
+// (A: the workgroup's rows of A; B: the chunk's 16 rows of B, rebuilt per
+// chunk), a per-lane 32-bit byte offset fixed for the whole loop, and for A a
+// scalar offset that advances with the chunk. A copy is thus one instruction
+// with no vector address arithmetic; with 64-bit per-lane addresses (one
+// vector add per copy in the loop) the timed shape 8192 x 6144 x 4096 ran
+// 1.6% slower (2743 against 2699 us). The 32-bit offsets bound the shapes this
+// kernel takes: 256 rows of A span at most 2^32 bytes (N <= kDmaMaxN) and 16
+// rows of B too (K <= kDmaMaxK); the host routes larger ones elsewhere.
 //
 // Pipeline. Chunk c lives in stage (c + off) mod S. While chunk c is
 // multiplied, this wave copies chunk c + S - 1 into the stage that chunk c - 1
@@ -113,15 +123,28 @@ __host__ __device__ __forceinline__ int dma_a_read(int row0, int i, int q) {
 // outstanding and every LDS operation is done.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (((vm >> 4) & 3) << 14); }
 
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds is
-// wave-uniform). A plain device function: the builtin has no host form.
-__device__ __forceinline__ void copy16_to_lds(const float* g, float* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+// Largest N and K whose copy offsets fit the buffers' 32-bit byte range:
+// 256 rows of A (BM N floats) and 16 rows of B (BK K floats).
+constexpr int kDmaMaxN = (int)(0xffffffffu / (256u * 4u));
+constexpr int kDmaMaxK = (int)(0xffffffffu / (16u * 4u));
+
+// Raw buffer resource over `bytes` bytes from `base` (word 3 as on every
+// gfx9-family GPU: raw buffer, 32-bit data). A load at an offset at or past
+// `bytes` returns zeros (the hardware's range check); every copy here stays
+// inside.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-// 4 bytes per lane, into LDS at lds + 4 * lane.
-__device__ __forceinline__ void copy4_to_lds(const float* g, float* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
+// BYTES (16 or 4) bytes per lane from the buffer at soff + voff into LDS at
+// lds + BYTES * lane (lds and soff are wave-uniform). A plain device
+// function: the builtin has no host form.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, float* lds) {
+  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte copies");
+  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 4, voff, soff, 0, 0);
 }
 
 template <class T>
@@ -180,9 +203,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
   // (p % 16) / 4, element p % 4, and the slot holds quad slot ^ swz(row), so
   // the lane reads that quad's element (the whole quad with 16-byte copies).
   // Rows past M read row M - 1 instead (their outputs are not stored).
+  // a_src is the lane's source in chunk 0 (loaded through registers); the
+  // copies of later chunks read the A buffer (the tile's rows) at a_off plus
+  // 4 n0 bytes.
+  const int tile_rows = M - m0 < T::BM ? M - m0 : T::BM;
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * N, (uint32_t)tile_rows * (uint32_t)N * 4u);
   const float* a_src[T::kACopies];
-  int a_dst[T::kACopies];  // LDS float offset of the copy's block
-  int a_col[T::kACopies];  // column of the lane's first element inside the chunk
+  uint32_t a_off[T::kACopies];  // byte offset of the lane's source in the A buffer at n0 = 0
+  int a_dst[T::kACopies];       // LDS float offset of the copy's block
+  int a_col[T::kACopies];       // column of the lane's first element inside the chunk
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
     const int blk = wave * T::kACopies + j;
@@ -191,12 +220,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     const int c = dma_a_col(pos);
     const int row = m0 + r < M ? m0 + r : M - 1;
     a_src[j] = A + (int64_t)row * N + c;
+    a_off[j] = (uint32_t)((row - m0) * N + c) * 4u;
     a_dst[j] = blk * T::kABlock;
     a_col[j] = c;
   }
   // In the B stage position p is row p / 256, column p % 256 (columns past K
   // read the last column, or the last quad with 16-byte copies; not stored).
+  // The copies of the chunk at n0 read a buffer over rows [n0, n0 + BK) of B
+  // at b_off.
   const float* b_src[T::kBCopies];
+  uint32_t b_off[T::kBCopies];
   int b_dst[T::kBCopies];
   int b_row[T::kBCopies];
 #pragma unroll
@@ -207,20 +240,20 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     const int c = k0 + pos % BN;
     const int col = c < K ? c : K - T::kBCopyFloats;
     b_src[j] = B + (int64_t)r * K + col;
+    b_off[j] = (uint32_t)(r * K + col) * 4u;
     b_dst[j] = blk * T::kBBlock;
     b_row[j] = r;
   }
 
   // copies [P0, P1) of this wave's kCopies (A first, then B) of the chunk at n0
   auto copy_part = [&](auto p0c, auto p1c, int n0, float* As, float* Bs) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * K, (uint32_t)(BK * K) * 4u);
     static_for<decltype(p0c)::value, decltype(p1c)::value>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       if constexpr (p < T::kACopies) {
-        if constexpr (T::VA) copy16_to_lds(a_src[p] + n0, As + a_dst[p]);
-        else copy4_to_lds(a_src[p] + n0, As + a_dst[p]);
+        copy_to_lds<4 * T::kACopyFloats>(a_rsrc, a_off[p], (uint32_t)n0 * 4u, As + a_dst[p]);
       } else {
-        if constexpr (T::VB) copy16_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
-        else copy4_to_lds(b_src[p - T::kACopies] + (int64_t)n0 * K, Bs + b_dst[p - T::kACopies]);
+        copy_to_lds<4 * T::kBCopyFloats>(b_rsrc, b_off[p - T::kACopies], 0u, Bs + b_dst[p - T::kACopies]);
       }
     });
   };

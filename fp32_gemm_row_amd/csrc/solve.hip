@@ -133,7 +133,9 @@ bool ksplit128_ok(int K) { return K >= 4; }
 // copies that run past the last chunk re-read it, and must never reach the
 // zero-padded first chunk); they are 16 bytes wide for 16-byte aligned rows,
 // 4 bytes otherwise (the k-split kernel's 128x128 tiles take 16-byte copies only).
-bool mfma_dma_ok(int N) { return N >= 64; }
+// The direct-copy kernel: N >= 64 (two chunks at least), and copy offsets
+// inside 32 bits (256 rows of A, 16 rows of B).
+bool mfma_dma_ok(int N, int K) { return N >= 64 && N <= fgr::kDmaMaxN && K <= fgr::kDmaMaxK; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -423,7 +425,7 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
   // 4097 x 4099 1143 vs 1022, 8191 x 1023 x 8191 1092 vs 1069; but 8191 x 511
   // x 8191 596 vs 613; with one operand aligned they are within 1%: 4096 x
   // 4096 x 4095 958 vs 964, 6000 x 1001 x 6000 599 vs 602).
-  if (t256 >= cus && mfma_dma_ok(N) &&
+  if (t256 >= cus && mfma_dma_ok(N, K) &&
       (rows != Rows::kNone || N < kKsplitUnalignedMinN || !ksplit128_ok(K))) {
     // a last, partial wave of at most tail_tiles(cus) tiles goes to the split kernel
     const int64_t rem = t256 % cus;
@@ -1140,7 +1142,7 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       break;
     case FGR_PATH_MFMA_DMA:
     case FGR_PATH_MFMA_DMA_TAIL:
-      if (!mfma_dma_ok(N) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256)) return FGR_ERR_BAD_PATH;
+      if (!mfma_dma_ok(N, K) || (tile != FGR_TILE_AUTO && tile != FGR_TILE_256)) return FGR_ERR_BAD_PATH;
       break;
     case FGR_PATH_MFMA_KSPLIT:
     case FGR_PATH_MFMA_KSPLIT_TAIL:
@@ -1309,7 +1311,7 @@ int run_variant(const float* A, const float* B, float* C, int M, int N, int K, v
   int rc = check_args(A, B, C, M, N, K);
   if (rc != FGR_OK) return rc;
   if (variant < 0 || variant >= kNumVariants || !mfma_vec_ok(A, B, C, N, K) ||
-      (kVariants[variant].dma && !mfma_dma_ok(N)))
+      (kVariants[variant].dma && !mfma_dma_ok(N, K)))
     return FGR_ERR_BAD_PATH;
   int cus = 0;
   rc = device_for(reinterpret_cast<hipStream_t>(stream), &cus);

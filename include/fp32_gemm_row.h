@@ -98,8 +98,11 @@ extern "C" {
 #define FGR_PATH_GEMV_VEC 3    /* matrix-vector and skinny (M <= 8), 128-bit loads of B; needs K%4 == 0
                                   and a 16-B aligned B */
 #define FGR_PATH_GEMV_SCALAR 4 /* matrix-vector and skinny (M <= 8), 32-bit loads */
-#define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, 256x256 tiles fed by direct global->LDS copies;
-                                  needs the MFMA_VEC conditions and N >= 64 (tile 256 only) */
+#define FGR_PATH_MFMA_DMA 5    /* FP32 MFMA, 256x256 tiles fed by direct global->LDS copies
+                                  (16-byte copies of an operand whose rows are 16-byte aligned,
+                                  else 4-byte); needs 64 <= N <= 4194303 and K <= 67108863 (the
+                                  copies use 32-bit byte offsets over 256 rows of A and 16 rows
+                                  of B); tile 256 only */
 #define FGR_PATH_MFMA_SPLIT 6  /* FP32 MFMA, small tiles (32 or 64) whose reduction is split over
                                   the waves of a workgroup; any shape (128-bit loads when the
                                   MFMA_VEC conditions hold, else 32-bit) */

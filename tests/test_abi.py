@@ -131,6 +131,15 @@ def test_forced_path_rejections(lib):
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 128, 512, fgr.PATH_MFMA_DMA, 128) == fgr.ERR_BAD_PATH
     assert call(lib, A0, B0, C0, 512, 60, 512, fgr.PATH_MFMA_DMA_TAIL) == fgr.ERR_BAD_PATH
+    # the copies address 256 rows of A and 16 rows of B with 32-bit byte
+    # offsets: N <= 4194303 (= (2^32 - 1) / 1024), K <= 67108863
+    # (operands far apart, so that these sizes do not overlap)
+    a, b, c = 1 << 40, 2 << 40, 3 << 40
+    for path in (fgr.PATH_MFMA_DMA, fgr.PATH_MFMA_DMA_TAIL):
+        assert call(lib, a, b, c, 512, 4194304, 512, path) == fgr.ERR_BAD_PATH
+        assert call(lib, a, b, c, 512, 4194303, 512, path) == fgr.ERR_DEVICE
+        assert call(lib, a, b, c, 256, 128, 67108864, path) == fgr.ERR_BAD_PATH
+        assert call(lib, a, b, c, 256, 128, 67108863, path) == fgr.ERR_DEVICE
     for path in (fgr.PATH_MFMA_DMA, fgr.PATH_MFMA_DMA_TAIL):
         assert call(lib, A0, B0, C0, 512, 130, 512, path) == fgr.ERR_DEVICE
         assert call(lib, A0, B0, C0, 512, 128, 502, path) == fgr.ERR_DEVICE
@@ -186,6 +195,11 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4096, 4060, 4096) == fgr.PATH_MFMA_DMA  # ragged reduction
     assert sp(A0, B0, C0, 4000, 4096, 4004) == fgr.PATH_MFMA_DMA  # partial tiles
     assert sp(A0, B0, C0, 4096, 60, 4096) == fgr.PATH_MFMA_VEC  # N < 64
+    # past the direct-copy kernel's 32-bit copy offsets: 128x128 k-split tiles
+    a, b, c = 1 << 40, 2 << 40, 3 << 40
+    assert sp(a, b, c, 4096, 4194303, 4096) == fgr.PATH_MFMA_DMA
+    assert sp(a, b, c, 4096, 4194304, 4096) == fgr.PATH_MFMA_KSPLIT
+    assert st(a, b, c, 4096, 4194304, 4096) == fgr.TILE_128
     # a last partial wave of at most 176 tiles of 256x256 goes to the split kernel
     assert sp(A0, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 272 tiles
     assert sp(A0, B0, C0, 65792, 128, 256) == fgr.PATH_MFMA_DMA_TAIL  # 257 tiles
