@@ -96,6 +96,12 @@ struct KsplitConfig {
                 "a partial tile fits in the stage objects of either operand");
 };
 
+// The copies address bm rows of A and the BK = 8 rows of B of a chunk with
+// 32-bit byte offsets: both spans must stay within 2^32 bytes.
+__host__ __device__ constexpr bool ksplit_copies_fit(int bm, int N, int K) {
+  return (uint64_t)bm * (uint64_t)N * 4u <= 0xffffffffu && (uint64_t)K * 32u <= 0xffffffffu;
+}
+
 __host__ __device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 // Column (inside the 8-deep chunk) of the A element a copy puts at float
@@ -115,15 +121,19 @@ __host__ __device__ __forceinline__ int ksplit_a_read(int li, int g) { return li
 // of its own before those reads. The kernel counts the copies in flight and
 // waits for them itself (s_waitcnt vmcnt), the only way its reads are ordered
 // after the copies they need.
+// The source is a buffer resource (scalar registers) at soff + voff bytes, as
+// in the direct-copy kernel: no vector address arithmetic per copy.
 template <int BYTES>  // 16 or 4
-__device__ __forceinline__ void copy_to_lds_counted(const float* g, float* lds) {
+__device__ __forceinline__ void copy_to_lds_counted(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                                    float* lds) {
   uint32_t a = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)lds);
   asm volatile("" : "+s"(a));
+  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte copies");
   if constexpr (BYTES == 16)
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(uintptr_t)a, 16, voff, soff, 0, 0);
   else
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(uintptr_t)a, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(uintptr_t)a, 4, voff, soff, 0, 0);
 }
 
 // Scheduling hints for NO memory instructions among MFMAS MFMAs, when there
@@ -249,31 +259,43 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     const int c = k0 + (j * T::kBBlock + lane * T::kBCopyFloats) % BN;
     return B + (int64_t)b_row_of(j) * K + (c < K ? c : K - T::kBCopyFloats);
   };
+  // a_src / b_src: the lane's sources in the wave's first chunk (loaded
+  // through registers). The copies of later chunks read a buffer over the
+  // tile's rows of A at a_off + 4 n0 bytes, and a buffer over rows [n0, n0 +
+  // BK) of B at b_off (32-bit offsets: BM N and BK K floats at most 2^32
+  // bytes, which the host checks).
+  const int tile_rows = M - m0 < T::BM ? M - m0 : T::BM;
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * N, (uint32_t)tile_rows * (uint32_t)N * 4u);
   const float* a_src[T::kACopies];
+  uint32_t a_off[T::kACopies];
   int a_dst[T::kACopies], a_col[T::kACopies];
 #pragma unroll
   for (int j = 0; j < T::kACopies; ++j) {
     a_dst[j] = piece_a + j * T::kABlock;
     a_src[j] = a_ptr_of(j);
+    a_off[j] = (uint32_t)(a_src[j] - (A + (int64_t)m0 * N)) * 4u;
     a_col[j] = a_col_of(j);
   }
   // In B, p is row p / BN, column p % BN (columns past K read the last column,
   // or the last quad with 16-byte copies; not stored).
   const float* b_src[T::kBCopies];
+  uint32_t b_off[T::kBCopies];
   int b_dst[T::kBCopies];
 #pragma unroll
   for (int j = 0; j < T::kBCopies; ++j) {
     b_dst[j] = piece_b + j * T::kBBlock;
     b_src[j] = b_ptr_of(j);
+    b_off[j] = (uint32_t)(b_src[j] - B) * 4u;
   }
 
   auto copy_chunk = [&](int j, float* As, float* Bs) __attribute__((always_inline)) {
     const int n0 = chunk_n0(j);
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * K, (uint32_t)(BK * K) * 4u);
 #pragma unroll
-    for (int j = 0; j < T::kACopies; ++j) copy_to_lds_counted<4 * T::kACopyFloats>(a_src[j] + n0, As + a_dst[j]);
+    for (int j = 0; j < T::kACopies; ++j)
+      copy_to_lds_counted<4 * T::kACopyFloats>(a_rsrc, a_off[j], (uint32_t)n0 * 4u, As + a_dst[j]);
 #pragma unroll
-    for (int j = 0; j < T::kBCopies; ++j)
-      copy_to_lds_counted<4 * T::kBCopyFloats>(b_src[j] + (int64_t)n0 * K, Bs + b_dst[j]);
+    for (int j = 0; j < T::kBCopies; ++j) copy_to_lds_counted<4 * T::kBCopyFloats>(b_rsrc, b_off[j], 0u, Bs + b_dst[j]);
   };
 
   struct Frag {

@@ -112,15 +112,17 @@ extern "C" {
                                     launches on `stream`. */
 #define FGR_PATH_MFMA_KSPLIT 8 /* FP32 MFMA, 128x128, 64x64, 32x32 or 32x128 tiles, each of a
                                   workgroup's four waves reducing a quarter of N into the whole
-                                  tile. Operands: 64x64 tiles with 16-byte aligned rows of A, B
-                                  and C, and 128x128 / 32x128 tiles, through direct
-                                  global->LDS copies (4-byte copies for rows that are not
-                                  16-byte aligned; tile 128 with neither A's nor B's rows 16-byte
-                                  aligned first copies A into padded rows, a workspace of its
-                                  own, and takes tile 64 if that cannot be had); other 64x64 and
-                                  all 32x32 tiles load them straight into registers (16- and
-                                  8-byte loads at any 4-byte alignment; 64x64 with K = 1 runs
-                                  as 32x32). N >= 64 */
+                                  tile. Operands: 64x64 and 32x32 tiles with 16-byte aligned rows
+                                  of A, B and C, and all 32x128 tiles, through direct
+                                  global->LDS copies (32x128: 4-byte copies of an operand whose
+                                  rows are not 16-byte aligned). The copies use 32-bit byte
+                                  offsets over a tile's rows of A and 8 rows of B: 64x64 needs
+                                  N <= 16777215, 32x32 and 32x128 N <= 33554431, all K <=
+                                  134217727 (past that 64x64 and 32x32 tiles load into
+                                  registers; 32x128 is refused). 128x128 tiles and the other
+                                  64x64 and 32x32 tiles load operands straight into registers
+                                  (16- and 8-byte loads at any 4-byte alignment; 128x128 needs
+                                  K >= 4; 64x64 with K = 1 runs as 32x32). N >= 64 */
 #define FGR_PATH_MFMA_KSPLIT_TAIL 9 /* MFMA_KSPLIT (tile 128 or 64) on the whole waves of tiles; the
                                        tiles of the last, partial wave either with their reduction
                                        split over workgroups through a workspace (N >= 4096, or
@@ -155,7 +157,8 @@ extern "C" {
 #define FGR_TILE_64 64
 #define FGR_TILE_32 32 /* split and k-split paths only */
 #define FGR_TILE_32X128 32128 /* 32 rows x 128 columns: k-split paths only (MFMA_KSPLIT, MFMA_SPLITK);
-                                 the tile for skinny outputs (M <= 32) */
+                                 the tile for skinny outputs (M <= 64); N <= 33554431 and
+                                 K <= 134217727 (see MFMA_KSPLIT) */
 
 /*
  * solve - C = A x B on `stream`.

@@ -134,7 +134,11 @@ def test_forced_path_rejections(lib):
     # the copies address 256 rows of A and 16 rows of B with 32-bit byte
     # offsets: N <= 4194303 (= (2^32 - 1) / 1024), K <= 67108863
     # (operands far apart, so that these sizes do not overlap)
-    a, b, c = 1 << 40, 2 << 40, 3 << 40
+    a, b, c = 1 << 44, 2 << 44, 3 << 44
+    for path in (fgr.PATH_MFMA_KSPLIT, fgr.PATH_MFMA_SPLITK):
+        assert call(lib, a, b, c, 16, 33554432, 128, path, fgr.TILE_32X128) == fgr.ERR_BAD_PATH
+        assert call(lib, a, b, c, 16, 128, 134217728, path, fgr.TILE_32X128) == fgr.ERR_BAD_PATH
+        assert call(lib, a, b, c, 16, 33554431, 128, path, fgr.TILE_32X128) == fgr.ERR_DEVICE
     for path in (fgr.PATH_MFMA_DMA, fgr.PATH_MFMA_DMA_TAIL):
         assert call(lib, a, b, c, 512, 4194304, 512, path) == fgr.ERR_BAD_PATH
         assert call(lib, a, b, c, 512, 4194303, 512, path) == fgr.ERR_DEVICE
@@ -196,10 +200,14 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 4000, 4096, 4004) == fgr.PATH_MFMA_DMA  # partial tiles
     assert sp(A0, B0, C0, 4096, 60, 4096) == fgr.PATH_MFMA_VEC  # N < 64
     # past the direct-copy kernel's 32-bit copy offsets: 128x128 k-split tiles
-    a, b, c = 1 << 40, 2 << 40, 3 << 40
+    a, b, c = 1 << 44, 2 << 44, 3 << 44
     assert sp(a, b, c, 4096, 4194303, 4096) == fgr.PATH_MFMA_DMA
     assert sp(a, b, c, 4096, 4194304, 4096) == fgr.PATH_MFMA_KSPLIT
     assert st(a, b, c, 4096, 4194304, 4096) == fgr.TILE_128
+    # the skinny 32x128 tiles address 32 rows of A with 32-bit offsets: past
+    # N = 33554431 the skinny shape takes the split plan's 32x32 tiles
+    assert st(a, b, c, 16, 33554431, 128) == fgr.TILE_32X128
+    assert st(a, b, c, 16, 33554432, 128) != fgr.TILE_32X128
     # a last partial wave of at most 176 tiles of 256x256 goes to the split kernel
     assert sp(A0, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 272 tiles
     assert sp(A0, B0, C0, 65792, 128, 256) == fgr.PATH_MFMA_DMA_TAIL  # 257 tiles
