@@ -144,6 +144,24 @@ __device__ __forceinline__ float4 mask_quad(float4 v, unsigned ok) {
 // aligned, and the store of such a vector. On gfx9-family GPUs global loads and
 // stores of two or more dwords need only dword alignment; the compiler emits
 // one global_load_dwordx2 / x4 (store) for these.
+// Raw buffer resource over `bytes` bytes from `base` (word 3 as on every
+// gfx9-family GPU: raw buffer, 32-bit data). Loads through it take a 32-bit
+// per-lane offset and a 32-bit scalar offset, so a kernel that keeps its
+// per-lane offsets fixed and moves a scalar one (or the base) per chunk
+// issues its loads with no vector address arithmetic. A load at an offset at
+// or past `bytes` returns zeros (the hardware's range check); the kernels'
+// loads all stay inside.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// The k-split kernels address a tile's rows_a rows of A and a chunk's 8 rows
+// of B with 32-bit byte offsets: both spans must stay within 2^32 bytes.
+__host__ __device__ constexpr bool ksplit_offsets_fit(int rows_a, int N, int K) {
+  return (uint64_t)rows_a * (uint64_t)N * 4u <= 0xffffffffu && (uint64_t)K * 32u <= 0xffffffffu;
+}
+
 template <class V>
 __device__ __forceinline__ V load_dwords(const float* p) {
   V v;

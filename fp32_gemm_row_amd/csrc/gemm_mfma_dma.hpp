@@ -128,15 +128,6 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (((vm >> 
 constexpr int kDmaMaxN = (int)(0xffffffffu / (256u * 4u));
 constexpr int kDmaMaxK = (int)(0xffffffffu / (16u * 4u));
 
-// Raw buffer resource over `bytes` bytes from `base` (word 3 as on every
-// gfx9-family GPU: raw buffer, 32-bit data). A load at an offset at or past
-// `bytes` returns zeros (the hardware's range check); every copy here stays
-// inside.
-constexpr int kBufferWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, kBufferWord3);
-}
-
 // BYTES (16 or 4) bytes per lane from the buffer at soff + voff into LDS at
 // lds + BYTES * lane (lds and soff are wave-uniform). A plain device
 // function: the builtin has no host form.

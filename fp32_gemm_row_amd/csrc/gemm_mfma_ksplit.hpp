@@ -96,12 +96,6 @@ struct KsplitConfig {
                 "a partial tile fits in the stage objects of either operand");
 };
 
-// The copies address bm rows of A and the BK = 8 rows of B of a chunk with
-// 32-bit byte offsets: both spans must stay within 2^32 bytes.
-__host__ __device__ constexpr bool ksplit_copies_fit(int bm, int N, int K) {
-  return (uint64_t)bm * (uint64_t)N * 4u <= 0xffffffffu && (uint64_t)K * 32u <= 0xffffffffu;
-}
-
 __host__ __device__ __forceinline__ int a_swizzle2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 // Column (inside the 8-deep chunk) of the A element a copy puts at float

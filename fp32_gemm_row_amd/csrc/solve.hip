@@ -387,7 +387,7 @@ constexpr int kKsplitUnalignedMinN = 768;
 Choice choose(const float* A, const float* B, const float* C, int M, int N, int K, int cus) {
   if (cus <= 0) cus = kDefaultCus;
   const bool skinny_shape =
-      M >= kSkinnyMinM && M <= kSkinnyMaxM && N >= 64 && K >= 128 && fgr::ksplit_copies_fit(32, N, K);
+      M >= kSkinnyMinM && M <= kSkinnyMaxM && N >= 64 && K >= 128 && fgr::ksplit_offsets_fit(32, N, K);
   const bool skinny = skinny_shape && skinny_b(M, N, K, cus);
   // M <= 8: the matrix-vector kernel, except that from 5 rows on the split
   // plan below wins where the skinny tiles do not apply (measured on MI355X,
@@ -909,15 +909,18 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
                        hipStream_t s, int parts, float* W, int first, int compact, int nfull) {
   if constexpr (BM == BN) {
     if constexpr (BM <= 64) {
-      if (rows == Rows::kAll && fgr::ksplit_copies_fit(BM, N, K))
+      if (rows == Rows::kAll && fgr::ksplit_offsets_fit(BM, N, K))
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true>>(A, B, C, M, N, K, count, s, parts, W, first,
                                                                  compact, nfull);
     }
     if (K < BM / 32) return FGR_ERR_BAD_PATH;
+    if (!fgr::ksplit_offsets_fit(BM, N, K))
+      return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth, false, false>>(A, B, C, M, N, K, count, s, parts, W,
+                                                                            first, compact, nfull);
     return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth>>(A, B, C, M, N, K, count, s, parts, W, first, compact,
                                                              nfull);
   } else {
-    if (!fgr::ksplit_copies_fit(BM, N, K)) return FGR_ERR_BAD_PATH;
+    if (!fgr::ksplit_offsets_fit(BM, N, K)) return FGR_ERR_BAD_PATH;
     switch (rows) {
       case Rows::kAll:
         return launch_ksplit_cfg<fgr::KsplitConfig<BM, 4, true, BN>>(A, B, C, M, N, K, count, s, parts, W, first,
@@ -964,9 +967,12 @@ int launch_ksplit(int tile, const float* A, const float* B, float* C, int M, int
 // ALUs (strip.hpp). No workspace. Direct 16-byte copies when the rows of A, B
 // and C allow them, else operands straight into registers.
 int launch_strip(const float* A, const float* B, float* C, int M, int N, int K, hipStream_t s) {
-  if (rows_of(A, B, C, N, K) == Rows::kAll && fgr::ksplit_copies_fit(64, N, K))
+  if (rows_of(A, B, C, N, K) == Rows::kAll && fgr::ksplit_offsets_fit(64, N, K))
     return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true, 64, true, true>>(A, B, C, M, N, K, -1, s, 1, nullptr,
                                                                             0, 0, 0);
+  if (!fgr::ksplit_offsets_fit(64, N, K))
+    return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true, false>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0,
+                                                                          0);
   return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0);
 }
 
@@ -1180,7 +1186,7 @@ int run(const float* A, const float* B, float* C, int M, int N, int K, void* str
       tile != FGR_TILE_32 && tile != FGR_TILE_32X128)
     return FGR_ERR_BAD_PATH;
   if (tile == FGR_TILE_32X128 &&
-      (N < 64 || !fgr::ksplit_copies_fit(32, N, K) ||
+      (N < 64 || !fgr::ksplit_offsets_fit(32, N, K) ||
        (path != FGR_PATH_MFMA_KSPLIT && path != FGR_PATH_MFMA_SPLITK && path != FGR_PATH_AUTO)))
     return FGR_ERR_BAD_PATH;  // direct copies need N >= 64 and 32-bit copy offsets
   if (tile == FGR_TILE_32 && path != FGR_PATH_MFMA_SPLIT && path != FGR_PATH_MFMA_KSPLIT &&

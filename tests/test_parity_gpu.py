@@ -945,6 +945,23 @@ def test_long_reduction_128_split_exact():
         assert_exact(C[rows, cols][None, :], Cref[None, :], f"{M}x{N}x{K} offsets {offsets} sampled")
 
 
+@pytest.mark.parametrize("N,tile", [(8388612, fgr.TILE_128), (16777220, fgr.TILE_64), (33554436, fgr.TILE_32)],
+                         ids=["128-N8388612", "64-N16777220", "32-N33554436"])
+def test_k_split_tiles_past_32bit_offsets(N, tile):
+    # The k-split kernels address a tile's rows of A with 32-bit byte offsets
+    # where tile * N * 4 < 2^32; past that (these N) they fall back to 64-bit
+    # addresses (the LDS form of 64x64 and 32x32 tiles to the register-fed
+    # one). Two rows, four columns, split over workgroups; within tolerance
+    # against the fp64 oracle.
+    M, K = 2, 4
+    assert tile * N * 4 > 0xFFFFFFFF
+    say(f"k-split tile {tile} past 32-bit offsets: {M}x{N}x{K}")
+    A, B = synth.make_inputs(M, N, K, "uniform", seed=N % 1000)
+    C = gpu_gemm(A, B, fgr.PATH_MFMA_SPLITK, tile)
+    Cref, S = oracle.gemm(A, B)
+    assert_within_tolerance(C, Cref, S, f"{M}x{N}x{K} tile {tile}")
+
+
 def test_default_stream_is_torchs_current_stream():
     # solve() without a stream argument enqueues on torch's current stream
     # (the binding reads its raw handle); inside `with torch.cuda.stream(s)`
