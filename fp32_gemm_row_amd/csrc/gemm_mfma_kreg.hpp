@@ -41,11 +41,15 @@ namespace fgr {
 // BM x BM tiles (32, 64 or 128); D chunks of operands in registers; STRIP as
 // in KsplitConfig (the column strip on the vector ALUs in the same launch).
 // BUF: the chunk loads go through buffer resources with fixed 32-bit lane
-// offsets (measured 1-2% faster than 64-bit addresses, e.g. 1023 x 1025 x
-// 1027 22.8 against 23.2 us), for shapes whose offsets fit 32 bits.
+// offsets, for shapes whose offsets fit 32 bits. Measured on MI355X (us per
+// call, buffer against 64-bit addresses): at 128x128 0.5-1.2% faster on every
+// shape tried (2047^3 126.3 vs 127.4, 8191 x 1023 x 8191 1055 vs 1068, 3501 x
+// 2001 x 3501 393 vs 397); at 64x64 faster on a few (1023 x 1025 x 1027 22.9
+// vs 23.2) but 5-7% slower on others (3001^3 464 vs 440, 3001 x 1001 x 3001
+// 169 vs 158), so only 128x128 tiles take it.
 // The four partial tiles pass through LDS all at once, or at BM = 128 half a
 // tile at a time (four whole partials would need 256 KB).
-template <int BM_, int D_, bool STRIP_ = false, bool BUF_ = true>
+template <int BM_, int D_, bool STRIP_ = false, bool BUF_ = false>
 struct KregConfig {
   static constexpr int BM = BM_, BN = BM_, BK = 8, D = D_;
   static constexpr bool kStrip = STRIP_;

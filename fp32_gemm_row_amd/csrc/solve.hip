@@ -420,14 +420,18 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     return {FGR_PATH_MFMA_SCALAR, t128 >= 4 * cus ? FGR_TILE_128 : FGR_TILE_64};
   }
   // Whole-device shapes take the direct-copy kernel, unless neither operand's
-  // rows are 16-byte aligned and the reduction is long: its 4-byte copies then
-  // lose to the k-split kernel's 128x128 tiles, which load at any alignment
-  // (measured on MI355X, us per call: 8191 x 6143 x 4095 3261 vs 2864, 4095 x
-  // 4097 x 4099 1143 vs 1022, 8191 x 1023 x 8191 1092 vs 1069; but 8191 x 511
-  // x 8191 596 vs 613; with one operand aligned they are within 1%: 4096 x
-  // 4096 x 4095 958 vs 964, 6000 x 1001 x 6000 599 vs 602).
+  // rows are 16-byte aligned, the reduction is long and the 256x256 tiles
+  // leave a partial last wave: the k-split kernel's 128x128 tiles, which load
+  // at any alignment, then even that wave out better than the direct-copy
+  // kernel's 4-byte copies and split tail (measured on MI355X, us per call,
+  // direct copies vs 128x128: partial waves 4095 x 4097 x 4099 1043 vs 1003,
+  // 6143 x 4095 x 6143 2287 vs 2126, 5119 x 3001 x 5119 1401 vs 1141; whole
+  // waves 8191 x 1023 x 8191 1000 vs 1052, 8191 x 2047 x 8191 1901 vs 1963,
+  // 8191 x 4095 x 8191 3692 vs 3773, 8191 x 6143 x 4095 2765 vs 2803; below
+  // N = 768 8191 x 511 x 8191 557 vs 605; with one operand aligned the direct
+  // copies are faster or within 1%: 4096 x 4096 x 4095 927 vs 952).
   if (t256 >= cus && mfma_dma_ok(N, K) &&
-      (rows != Rows::kNone || N < kKsplitUnalignedMinN || !ksplit128_ok(K))) {
+      (rows != Rows::kNone || N < kKsplitUnalignedMinN || !ksplit128_ok(K) || t256 % cus == 0)) {
     // a last, partial wave of at most tail_tiles(cus) tiles goes to the split kernel
     const int64_t rem = t256 % cus;
     if (rem != 0 && rem <= tail_tiles(cus)) return {FGR_PATH_MFMA_DMA_TAIL, FGR_TILE_256};
@@ -439,16 +443,14 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
     // largest that still gives every CU a tile; a last partial wave of up to
     // half the CUs is spread over every CU (launch_ksplit_tail). 128x128
     // tiles where they make whole waves, three waves or more, or a last wave
-    // more than three quarters full (with every row aligned, where the 64x64
-    // tiles go through LDS, from two waves on); else 64x64, whose two
-    // workgroups per CU even out a partial wave better (measured on MI355X,
-    // us per call, 128x128 vs 64x64 tiles: 2047^3 128 vs 138, 1024 x 6144 x
-    // 4095 358 vs 395, 3584^3 675 vs 694, 2816^3 336 vs 354, aligned 3072^3
-    // 430 vs 449; but 2304^3 237 vs 194, 2560^3 305 vs 261, 2303 x 2305 x 2307
-    // 269 vs 206, 4095 x 2049 x 2051 296 vs 285, 3001^3 442 vs 438).
+    // more than three quarters full; else 64x64, whose two workgroups per CU
+    // even out a partial wave better (measured on MI355X, us per call, 128x128
+    // vs 64x64 tiles: 2047^3 128 vs 135, 1024 x 6144 x 4095 358 vs 395, 2048 x
+    // 8192 x 2048 464 vs 470, aligned 2048 x 4096 x 4096 474 vs 478, 3584^3
+    // 669 vs 694; but 2304^3 237 vs 184, 2560^3 302 vs 248, 2303 x 2305 x 2307
+    // 269 vs 206, aligned 3072^3 (2.25 waves) 424 vs 409; 2816^3 334 vs 329).
     const int64_t rem128 = t128 % cus;
-    const int64_t waves128 = rows == Rows::kAll ? 2 : 3;
-    if (ksplit128_ok(K) && t128 >= cus && (rem128 == 0 || t128 >= waves128 * cus || 4 * rem128 > 3 * cus)) {
+    if (ksplit128_ok(K) && t128 >= cus && (rem128 == 0 || t128 >= 3 * cus || 4 * rem128 > 3 * cus)) {
       if (rem128 != 0 && rem128 <= ksplit_tail_tiles(cus)) return {FGR_PATH_MFMA_KSPLIT_TAIL, FGR_TILE_128};
       return {FGR_PATH_MFMA_KSPLIT, FGR_TILE_128};
     }
@@ -914,11 +916,14 @@ int launch_ksplit_rows(Rows rows, const float* A, const float* B, float* C, int 
                                                                  compact, nfull);
     }
     if (K < BM / 32) return FGR_ERR_BAD_PATH;
-    if (!fgr::ksplit_offsets_fit(BM, N, K))
-      return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth, false, false>>(A, B, C, M, N, K, count, s, parts, W,
-                                                                            first, compact, nfull);
-    return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth>>(A, B, C, M, N, K, count, s, parts, W, first, compact,
-                                                             nfull);
+    // buffer loads at 128x128 where their offsets fit (see KregConfig)
+    if constexpr (BM == 128) {
+      if (fgr::ksplit_offsets_fit(BM, N, K))
+        return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth, false, true>>(A, B, C, M, N, K, count, s, parts, W,
+                                                                             first, compact, nfull);
+    }
+    return launch_ksplit_cfg<fgr::KregConfig<BM, kKregDepth, false, false>>(A, B, C, M, N, K, count, s, parts, W,
+                                                                          first, compact, nfull);
   } else {
     if (!fgr::ksplit_offsets_fit(BM, N, K)) return FGR_ERR_BAD_PATH;
     switch (rows) {
@@ -970,10 +975,8 @@ int launch_strip(const float* A, const float* B, float* C, int M, int N, int K, 
   if (rows_of(A, B, C, N, K) == Rows::kAll && fgr::ksplit_offsets_fit(64, N, K))
     return launch_ksplit_cfg<fgr::KsplitConfig<64, 4, true, 64, true, true>>(A, B, C, M, N, K, -1, s, 1, nullptr,
                                                                             0, 0, 0);
-  if (!fgr::ksplit_offsets_fit(64, N, K))
-    return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true, false>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0,
-                                                                          0);
-  return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0, 0);
+  return launch_ksplit_cfg<fgr::KregConfig<64, kKregDepth, true, false>>(A, B, C, M, N, K, -1, s, 1, nullptr, 0, 0,
+                                                                        0);
 }
 
 // Sum of compact partial tiles (tiles [first, first + count) of the grouped

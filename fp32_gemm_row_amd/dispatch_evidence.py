@@ -43,9 +43,8 @@ RULES = [
       ((3001, 3001, 3001), [("auto (64x64, 161 left over)", AUTO),
                             ("MFMA_KSPLIT_TAIL 64", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 64))])]),
     ("128x128 or 64x64 k-split tiles",
-     "t128 == 0 mod cus, t128 >= 3 cus (2 cus with aligned rows) or a last wave > 3 cus / 4 (choose)",
-     "128x128 tiles in whole waves, from three waves on (two with every row aligned) or with a last wave "
-     "more than 3/4 full; else 64x64",
+     "t128 == 0 mod cus, t128 >= 3 cus or a last wave > 3 cus / 4 (choose)",
+     "128x128 tiles in whole waves, from three waves on or with a last wave more than 3/4 full; else 64x64",
      [((2047, 2047, 2047), [("auto (128x128, one wave)", AUTO),
                             ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
       ((2816, 2816, 2816), [("auto (128x128, 484 tiles)", AUTO),
@@ -54,7 +53,9 @@ RULES = [
                             ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))]),
       ((2560, 2560, 2560), [("auto (64x64; 400 of 128)", AUTO),
                             ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
-      ((3072, 3072, 3072), [("auto (aligned, 128x128; 576 of 128)", AUTO),
+      ((3072, 3072, 3072), [("auto (aligned, 64x64; 576 of 128)", AUTO),
+                            ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))]),
+      ((2048, 4096, 4096), [("auto (aligned, 128x128, two whole waves)", AUTO),
                             ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
       ((3001, 3001, 3001), [("auto (64x64; 576 of 128)", AUTO),
                             ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))])]),
@@ -102,12 +103,13 @@ RULES = [
      "a partial last wave of 64x64 tiles with N >= 1024 splits its tiles' reduction in the whole tiles' grid",
      [((1023, 4097, 1039), [("auto", AUTO), ("no split (split-kernel tail)", NOSPLIT)]),
       ((1536, 4096, 1536), [("auto", AUTO), ("no split (split-kernel tail)", NOSPLIT)])]),
-    ("Unaligned whole-device shapes", "kKsplitUnalignedMinN = 768 (choose)",
-     "neither operand's rows aligned, enough 256x256 tiles: 128x128 k-split tiles from N = 768 on, "
-     "direct copies below",
-     [((8191, 6143, 4095), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
-      ((4095, 4097, 4099), [("auto", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))]),
-      ((8191, 1023, 8191), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+    ("Unaligned whole-device shapes", "kKsplitUnalignedMinN = 768, t256 mod cus (choose)",
+     "neither operand's rows aligned, enough 256x256 tiles: direct copies in whole waves of 256x256 tiles "
+     "or below N = 768, else 128x128 k-split tiles",
+     [((8191, 6143, 4095), [("auto (two whole waves)", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
+      ((8191, 1023, 8191), [("auto (four whole waves)", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
+      ((4095, 4097, 4099), [("auto (272 tiles)", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))]),
+      ((6143, 4095, 6143), [("auto (576 tiles)", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))]),
       ((8191, 511, 8191), [("auto", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))]),
       ((4096, 4096, 4095), [("auto (A aligned)", AUTO), ("MFMA_KSPLIT 128", forced(fgr.PATH_MFMA_KSPLIT, 128))])]),
     ("Column strip", "kStripMax = 8 (strip_plan_ok)",

@@ -218,10 +218,12 @@ def test_path_selection_rules():
     assert sp(A0 + 4, B0, C0, 4096, 4096, 4160) == fgr.PATH_MFMA_DMA_TAIL  # 4-byte copies
     assert sp(A0, B0, C0, 2048, 2048, 2048) == fgr.PATH_MFMA_KSPLIT  # 64 tiles of 256, 256 of 128
     assert sp(A0, B0, C0, 1024, 6144, 4096) == fgr.PATH_MFMA_KSPLIT  # a row shard of the timed shape
-    # 128x128 tiles in whole waves, three waves or more (two with every row
-    # aligned), or a last wave more than three quarters full; else 64x64 tiles
-    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT_TAIL  # 576 of 128 (2.25 waves), aligned
-    assert st(A0, B0, C0, 3072, 3072, 3072) == 128
+    # 128x128 tiles in whole waves, three waves or more, or a last wave more
+    # than three quarters full; else 64x64 tiles
+    assert sp(A0, B0, C0, 3072, 3072, 3072) == fgr.PATH_MFMA_KSPLIT  # 576 of 128 (2.25 waves), aligned
+    assert st(A0, B0, C0, 3072, 3072, 3072) == 64  # 2304 of 64: 9 whole waves
+    assert sp(A0, B0, C0, 2048, 4096, 4096) == fgr.PATH_MFMA_KSPLIT  # 512 of 128: two whole waves
+    assert st(A0, B0, C0, 2048, 4096, 4096) == 128
     assert sp(A0, B0, C0, 3001, 3001, 3001) == fgr.PATH_MFMA_KSPLIT  # 576 of 128, unaligned: 2209 of 64
     assert st(A0, B0, C0, 3001, 3001, 3001) == 64
     assert sp(A0, B0, C0, 2000, 3000, 2100) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 128: 1056 of 64
@@ -240,14 +242,18 @@ def test_path_selection_rules():
     assert sp(A0, B0, C0, 40, 8, 6) == fgr.PATH_MFMA_SPLIT
     assert sp(A0 + 4, B0, C0, 8192, 8192, 8192) == fgr.PATH_MFMA_DMA  # misaligned A: 4-byte copies
     assert sp(A0, B0, C0 + 8, 8192, 8192, 8192) == fgr.PATH_MFMA_DMA
-    # neither operand's rows aligned: 128x128 k-split tiles from N = 768 on,
-    # direct copies below (and the register-staged tiles below N = 384)
-    assert sp(A0, B0, C0, 8191, 6143, 4095) == fgr.PATH_MFMA_KSPLIT
-    assert st(A0, B0, C0, 8191, 6143, 4095) == 128
-    assert sp(A0, B0, C0, 4095, 4097, 4099) == fgr.PATH_MFMA_KSPLIT_TAIL  # 1056 of 128: 32 left over
-    assert sp(A0, B0, C0, 8191, 1023, 8191) == fgr.PATH_MFMA_KSPLIT
-    assert sp(A0, B0, C0, 8191, 769, 8191) == fgr.PATH_MFMA_KSPLIT
-    assert sp(A0, B0, C0, 8191, 767, 8191) == fgr.PATH_MFMA_DMA
+    # neither operand's rows aligned: direct copies (4 bytes wide) in whole
+    # waves of 256x256 tiles or below N = 768 (the register-staged tiles below
+    # N = 384); 128x128 k-split tiles where the 256x256 tiles leave a partial
+    # last wave
+    assert sp(A0, B0, C0, 8191, 6143, 4095) == fgr.PATH_MFMA_DMA  # 512 of 256: two whole waves
+    assert sp(A0, B0, C0, 8191, 1023, 8191) == fgr.PATH_MFMA_DMA  # 1024 of 256
+    assert sp(A0, B0, C0, 4095, 4097, 4099) == fgr.PATH_MFMA_KSPLIT_TAIL  # 272 of 256; 1056 of 128: 32 left
+    assert st(A0, B0, C0, 4095, 4097, 4099) == 128
+    assert sp(A0, B0, C0, 6143, 4095, 6143) == fgr.PATH_MFMA_KSPLIT  # 576 of 256; 2304 of 128
+    assert st(A0, B0, C0, 6143, 4095, 6143) == 128
+    assert sp(A0, B0, C0, 7167, 769, 7167) == fgr.PATH_MFMA_KSPLIT_TAIL  # 784 of 256; 3136 of 128: 64 left
+    assert sp(A0, B0, C0, 7167, 767, 7167) == fgr.PATH_MFMA_DMA_TAIL
     assert sp(A0, B0, C0, 8191, 511, 8191) == fgr.PATH_MFMA_DMA
     assert sp(A0 + 4, B0, C0, 4096, 6144, 4096) == fgr.PATH_MFMA_DMA  # one operand aligned
     assert sp(A0, B0, C0, 8192, 60, 8190) == fgr.PATH_MFMA_SCALAR  # N < 64
