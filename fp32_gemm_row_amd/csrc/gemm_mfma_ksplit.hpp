@@ -15,8 +15,8 @@
 // atomics.
 //
 // This file is the form whose operands go through LDS: each wave copies its
-// own A (BM x BK) and B (BK x BN) chunks with global_load_lds (16 bytes per
-// lane for 16-byte aligned rows, 4 bytes otherwise) into its own ring of S
+// own A (BM x BK) and B (BK x BN) chunks with buffer_load ... lds (16 bytes
+// per lane for 16-byte aligned rows, 4 bytes otherwise) into its own ring of S
 // LDS stages and waits only on its own copies (s_waitcnt vmcnt): the main
 // loop has no barrier. It serves 64x64 and 32x32 tiles whose rows of A, B
 // and C are all 16-byte aligned, and the skinny 32x128 tiles. 128x128 tiles,
@@ -109,14 +109,15 @@ __host__ __device__ __forceinline__ int ksplit_a_col(int pos) {
 // 32 i sit 32 * 8 * i floats further on with the same swizzle).
 __host__ __device__ __forceinline__ int ksplit_a_read(int li, int g) { return li * 8 + 4 * (g ^ a_swizzle2(li)); }
 
-// copy16_to_lds with the LDS destination passed as an opaque wave-uniform
-// integer. The compiler then cannot attribute the copy to one LDS object and
-// does not pair it with the operand reads (which keep their objects): no wait
-// of its own before those reads. The kernel counts the copies in flight and
-// waits for them itself (s_waitcnt vmcnt), the only way its reads are ordered
-// after the copies they need.
-// The source is a buffer resource (scalar registers) at soff + voff bytes, as
-// in the direct-copy kernel: no vector address arithmetic per copy.
+// A BYTES-wide copy per lane into LDS at lds + BYTES * lane, from a buffer
+// resource (scalar registers) at soff + voff bytes, as in the direct-copy
+// kernel: no vector address arithmetic per copy. The LDS destination is
+// passed as an opaque wave-uniform integer: the compiler then cannot
+// attribute the copy to one LDS object and does not pair it with the operand
+// reads (which keep their objects), so it inserts no wait of its own before
+// those reads. The kernel counts the copies in flight and waits for them
+// itself (s_waitcnt vmcnt), the only way its reads are ordered after the
+// copies they need.
 template <int BYTES>  // 16 or 4
 __device__ __forceinline__ void copy_to_lds_counted(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
                                                     float* lds) {

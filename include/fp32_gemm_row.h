@@ -26,9 +26,8 @@
  *   plans need device memory beyond A, B and C, called workspace here (see
  *   solve() below for sizes and where it comes from): the partial results of
  *   a reduction split across workgroups (paths MFMA_SPLITK, MFMA_KSPLIT_TAIL
- *   and the matrix-vector paths), and, for 128 x 128 k-split tiles when
- *   neither A's nor B's rows are 16-byte aligned, a copy of A with padded
- *   rows. Nothing else is allocated. C is overwritten (every one of its M*K
+ *   and the matrix-vector paths). Nothing else is allocated. C is
+ *   overwritten (every one of its M*K
  *   elements is written once; its prior contents, even NaN, are ignored: the
  *   output goes to C, as the LeetGPU problem's "Implementation Requirements"
  *   and the write-back rule of the CUDA study notes, section 3, have it). A
@@ -46,12 +45,15 @@
  *   Any 4-byte-aligned pointers are accepted. When N % 4 == 0, K % 4 == 0
  *   and A, B, C are 16-byte aligned the 128-bit load path is used; otherwise
  *   a path with 32-bit loads (the role of the scalar fallback of the LeetGPU
- *   write-up, section "V2: Vectorized float4 Transfers"). With 128-bit rows,
- *   N >= 64 and enough 256 x 256 output tiles to fill the device, A and B are
- *   copied straight from global memory into LDS (the role of the cp.async
- *   pipeline of the write-up's section "V4"). Shapes with too few output tiles
- *   for the device take 128 x 128 tiles whose reduction is split over the
- *   four waves of a workgroup, or smaller tiles split the same way;
+ *   write-up, section "V2: Vectorized float4 Transfers"). With N >= 64 and
+ *   enough 256 x 256 output tiles to fill the device, A and B are copied
+ *   straight from global memory into LDS (the role of the cp.async pipeline
+ *   of the write-up's section "V4"; 16 bytes per lane for an operand with
+ *   16-byte rows, else 4), except where neither operand's rows are 16-byte
+ *   aligned, N >= 768 and the tiles leave a partial last wave. Shapes with too
+ *   few output tiles for the device, and those, take 128 x 128 tiles whose
+ *   reduction is split over the four waves of a workgroup, or smaller tiles
+ *   split the same way;
  *   when a last, partial wave of 256 x 256 tiles is left, its tiles are cut
  *   into small split-reduction tiles. M <= 4 takes the bandwidth-bound
  *   matrix-vector path, which streams B once for all rows of A, and so do
@@ -68,7 +70,12 @@
  * Limits
  *   The problem statement guarantees 1 <= M, N, K <= 8192 (LeetGPU
  *   "Constraints"); that is the tested range. Larger values are accepted:
- *   index and size arithmetic is 64-bit. Values < 1 are rejected.
+ *   index and size arithmetic is 64-bit. Values < 1 are rejected. Some
+ *   kernels address their operands with 32-bit byte offsets from a tile's
+ *   first row (see FGR_PATH_MFMA_DMA and FGR_PATH_MFMA_KSPLIT); shapes past
+ *   those offsets take kernels with 64-bit addresses (solve() chooses them
+ *   itself; a forced path that cannot take the shape returns
+ *   FGR_ERR_BAD_PATH).
  */
 #ifndef FP32_GEMM_ROW_H
 #define FP32_GEMM_ROW_H
