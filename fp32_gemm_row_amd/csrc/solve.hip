@@ -371,6 +371,14 @@ bool strip_plan_ok(int M, int N, int K, int cus) {
 // Reductions shorter than this (with at least one 64x64 tile per CU) take
 // register-staged 64x64 tiles (128x128 for unaligned rows with many tiles).
 constexpr int kShortReduction = 104;
+// With every row aligned and whole waves of 256x256 tiles the direct-copy
+// kernel wins from this length on (measured on MI355X, us per call,
+// register-staged 64x64 vs direct copies: 8192 x N x 8192, N = 64 110.0 vs
+// 109.9, 72 122.8 vs 117.5, 80 124.9 vs 118.1, 96 145.3 vs 133.2; 4096 x 80 x
+// 4096 32.5 vs 31.6); with a partial last wave the short tiles keep the
+// lead (6144 x 80 x 6144 72.3 vs 76.3 with the split tail, 65792 x 96 x 256
+// 40.0 vs 41.3).
+constexpr int kShortReductionWholeWaves = 72;
 // With whole-device shapes whose B rows are not 16-byte aligned (the
 // direct-copy kernel would copy B 4 bytes at a time) the register-staged
 // tiles win up to this reduction length.
@@ -405,7 +413,9 @@ Choice choose(const float* A, const float* B, const float* C, int M, int N, int 
   const bool vec = mfma_vec_ok(A, B, C, N, K);
   const Rows rows = rows_of(A, B, C, N, K);
   const bool narrow_b = rows == Rows::kAOnly || rows == Rows::kNone;
-  if (t64 >= cus && (N < kShortReduction || (narrow_b && t256 >= cus && N < kShortReductionNarrowB))) {
+  const bool whole_waves = rows == Rows::kAll && t256 >= cus && t256 % cus == 0 && mfma_dma_ok(N, K);
+  const int short_n = whole_waves ? kShortReductionWholeWaves : kShortReduction;
+  if (t64 >= cus && (N < short_n || (narrow_b && t256 >= cus && N < kShortReductionNarrowB))) {
     // A short reduction over many tiles: the time goes to writing C. Small
     // register-staged tiles keep several workgroups per CU, so that one's
     // stores overlap another's loads and MFMAs (measured, 8192 x N x 8192:

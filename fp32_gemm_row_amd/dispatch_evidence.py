@@ -59,12 +59,15 @@ RULES = [
                             ("MFMA_KSPLIT 64", forced(fgr.PATH_MFMA_KSPLIT, 64))]),
       ((3001, 3001, 3001), [("auto (64x64; 576 of 128)", AUTO),
                             ("MFMA_KSPLIT_TAIL 128", forced(fgr.PATH_MFMA_KSPLIT_TAIL, 128))])]),
-    ("Short reductions", "kShortReduction = 104 (choose)",
-     "N < 104 with a 64x64 tile per CU: register-staged 64x64 tiles instead of the direct-copy kernel",
+    ("Short reductions", "kShortReduction = 104, kShortReductionWholeWaves = 72 (choose)",
+     "N < 104 (N < 72 with every row aligned and whole waves of 256x256 tiles) with a 64x64 tile per CU: "
+     "register-staged 64x64 tiles instead of the direct-copy kernel",
      [((8192, 64, 8192), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
-      ((8192, 96, 8192), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+      ((8192, 80, 8192), [("auto (whole waves)", AUTO), ("MFMA_VEC 64", forced(fgr.PATH_MFMA_VEC, 64))]),
+      ((8192, 96, 8192), [("auto (whole waves)", AUTO), ("MFMA_VEC 64", forced(fgr.PATH_MFMA_VEC, 64))]),
+      ((6144, 80, 6144), [("auto (partial wave)", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))]),
       ((65792, 96, 256), [("auto", AUTO), ("MFMA_DMA_TAIL", forced(fgr.PATH_MFMA_DMA_TAIL, 256))]),
-      ((4096, 96, 4096), [("auto", AUTO), ("MFMA_DMA", forced(fgr.PATH_MFMA_DMA, 256))]),
+      ((4096, 96, 4096), [("auto (whole waves)", AUTO), ("MFMA_VEC 64", forced(fgr.PATH_MFMA_VEC, 64))]),
       ((8192, 112, 8192), [("auto", AUTO), ("MFMA_VEC 64", forced(fgr.PATH_MFMA_VEC, 64))])]),
     ("Short reductions, unaligned B", "kShortReduction = 104, kShortReductionNarrowB = 384 (choose)",
      "unaligned rows: 32-bit register-staged tiles up to N = 104, and up to N = 384 where the direct-copy "

@@ -311,11 +311,14 @@ def test_split_path_choices():
 def test_short_reduction_choices():
     sp, st = fgr.select_path, fgr.select_tile
     # N < 104 with a 64x64 tile per CU: register-staged 64x64 tiles (the
-    # work is writing C), even where 256x256 tiles would fill the device
-    for shape in [(8192, 16, 8192), (8192, 64, 8192), (4096, 100, 4096), (65792, 64, 256), (1024, 8, 1024)]:
+    # work is writing C), even where 256x256 tiles would fill the device; but
+    # from N = 72 on the direct-copy kernel where those make whole waves
+    for shape in [(8192, 16, 8192), (8192, 64, 8192), (8192, 68, 8192), (6144, 100, 6144), (65792, 96, 256),
+                  (1024, 8, 1024)]:
         assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_VEC, shape
         assert st(A0, B0, C0, *shape) == 64, shape
-    assert sp(A0, B0, C0, 8192, 104, 8192) == fgr.PATH_MFMA_DMA
+    for shape in [(8192, 72, 8192), (4096, 100, 4096), (8192, 104, 8192)]:
+        assert sp(A0, B0, C0, *shape) == fgr.PATH_MFMA_DMA, shape
     # unaligned rows: 32-bit loads, 128x128 tiles when there are many
     assert sp(A0, B0, C0, 8191, 17, 8191) == fgr.PATH_MFMA_SCALAR
     assert st(A0, B0, C0, 8191, 17, 8191) == 128
