@@ -666,6 +666,94 @@ def read_ceiling(dev, stream, cus, steps=20, warmup=5):
     return {"bytes": READ_BYTES, "gbs": best["gbs"], "blocks": best["blocks"], "sweep": sweep}
 
 
+TS_WORDS = 8  # 64-bit words per timestamp record (include/fp32_gemm_row_timestamps.h)
+
+
+def timestamps_summary(w, path_name, tile, parts, launches_records, out_path, command):
+    """profiles/<workload>_timestamps.md from the measurement build's
+    per-workgroup records of several launches: the launch's span, the XCDs'
+    staggered starts, each XCD's shader clock and loop cycles, and the loop
+    cycles against the MFMA cycles the workgroup's work needs."""
+    import numpy as np
+
+    tile_rows = 32 if tile == 32128 else tile
+    tile_cols = 128 if tile == 32128 else tile
+    # MFMA cycles of one wave: a workgroup's tile over its part of N, its work
+    # spread over 4 SIMDs at 64 FLOP per clock each (v_mfma_f32_32x32x2_f32)
+    ideal = None
+    if tile_rows and path_name.startswith("mfma_"):
+        ideal = 2.0 * tile_rows * tile_cols * (w.N / max(1, parts)) / (4 * 64)
+    per_launch = []
+    xcd_rows = {}
+    for rec in launches_records:
+        r = rec[rec[:, 0] != 0]
+        tiles = r[r[:, 6] == 0]
+        if len(tiles) == 0:
+            continue
+        t0 = r[:, 0].min()
+        span_us = (r[:, 2].max() - t0) / 100.0
+        loop_us = (tiles[:, 1] - tiles[:, 0]) / 100.0
+        end_us = (tiles[:, 2] - tiles[:, 1]) / 100.0
+        cycles = (tiles[:, 4] - tiles[:, 3]).astype(np.float64)
+        ghz = cycles / ((tiles[:, 1] - tiles[:, 0]) * 10.0)
+        xcc = (tiles[:, 5] >> 32) & 0xFFFF
+        starts = {}
+        for x in sorted(set(xcc.tolist())):
+            m = xcc == x
+            starts[x] = (tiles[m, 0].min() - t0) / 100.0
+            xcd_rows.setdefault(x, []).append((starts[x], float(np.median(ghz[m])), float(np.median(cycles[m])),
+                                               float(np.median(loop_us[m]))))
+        per_launch.append({
+            "workgroups": len(r), "tiles": len(tiles), "span": span_us,
+            "loop": float(np.median(loop_us)), "end": float(np.median(end_us)),
+            "cycles": float(np.median(cycles)), "stagger": max(starts.values()) - min(starts.values()),
+            "ghz_lo": float(min(np.median(ghz[xcc == x]) for x in starts)),
+            "ghz_hi": float(max(np.median(ghz[xcc == x]) for x in starts)),
+        })
+    if not per_launch:
+        raise RuntimeError("no timestamp records (does the plan's kernel record them?)")
+    med = lambda k: float(np.median([d[k] for d in per_launch]))  # noqa: E731
+    lines = [
+        f"# Per-workgroup timestamps: {w.name} (M={w.M}, N={w.N}, K={w.K}), plan {path_name} {tile}"
+        + (f", {parts} parts" if parts > 1 else ""),
+        "",
+        "Command (repository at /root/repo; the measurement build libfp32_gemm_row_ts.so, the same kernels",
+        "with per-workgroup records of the constant 100 MHz clock and the shader clock):",
+        "",
+        f"    {command}",
+        "",
+        f"{len(per_launch)} launches, each after a synchronisation (so they start from an idle GPU), after",
+        "0.3 s of warm-up launches. A workgroup's loop is its start to the end of its main loop; its end",
+        "phase is the reduction of partial tiles (k-split kernels), the stores, and their completion.",
+        "Medians over the launches (and over each launch's workgroups):",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| workgroups recorded per launch (tiles) | {per_launch[0]['workgroups']} ({per_launch[0]['tiles']}) |",
+        f"| launch span, first start to last end | {med('span'):.2f} us |",
+        f"| last XCD's first start after the first XCD's | {med('stagger'):.2f} us |",
+        f"| a tile workgroup's loop | {med('loop'):.2f} us, {med('cycles'):.0f} shader clocks |",
+        f"| a tile workgroup's end phase | {med('end'):.2f} us |",
+        f"| shader clock, slowest to fastest XCD | {med('ghz_lo'):.3f} - {med('ghz_hi'):.3f} GHz |",
+    ]
+    if ideal:
+        lines.append(f"| MFMA clocks of a wave's share of its tile (2 BM BN N_part / 256) | {ideal:.0f} "
+                     f"(loop at {ideal / med('cycles') * 100:.1f}% of them) |")
+    lines += ["", "Per XCD (medians over launches: first start after the launch's first, the XCD's tiles' clock,",
+              "loop clocks and loop time):", "",
+              "| XCD | first start, us | clock, GHz | loop clocks | loop, us |", "|---|---|---|---|---|"]
+    for x in sorted(xcd_rows):
+        v = np.array(xcd_rows[x])
+        lines.append(f"| {x} | {np.median(v[:, 0]):.2f} | {np.median(v[:, 1]):.3f} | {np.median(v[:, 2]):.0f} | "
+                     f"{np.median(v[:, 3]):.2f} |")
+    lines += ["", f"loop-clocks: {med('cycles'):.0f}", f"launch-span-us: {med('span'):.2f}",
+              f"xcd-start-stagger-us: {med('stagger'):.2f}", "",
+              f"kernel-source-sha256: {kernel_source_hash()}", ""]
+    with open(out_path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    return out_path
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -710,6 +798,9 @@ def main() -> int:
                     help="write profiles/<workload>_controlled_comparison.md from a bench.py --ablation "
                          "output, a rocprofv3 --pmc MfmaUtil LdsUtil LdsBankConflict run of it and the "
                          "resource report, and exit")
+    ap.add_argument("--timestamps", action="store_true",
+                    help="with the measurement build (libfp32_gemm_row_ts.so), record per-workgroup timestamps "
+                         "of --steps launches of the workload, write profiles/<workload>_timestamps.md and exit")
     ap.add_argument("--command", action="append", default=[],
                     help="(with --summarize) a command that produced the folders, recorded in the summary")
     args = ap.parse_args()
@@ -754,7 +845,12 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (no CPU fallback)", file=sys.stderr)
         return 2
-    fgr.load_library()
+    if args.timestamps:
+        from fp32_gemm_row_amd import build as fgr_build
+
+        fgr.load_library(fgr_build.TS_LIB_PATH)
+    else:
+        fgr.load_library()
     if args.read_ceiling:
         dev = torch.device("cuda:0")
         res = read_ceiling(dev, torch.cuda.current_stream(), torch.cuda.get_device_properties(dev).multi_processor_count,
@@ -787,6 +883,36 @@ def main() -> int:
 
     def step_current(i):  # on torch's current stream (a graph capture's, when capturing)
         fgr.solve_path(dA, dBs[i % copies], dC, w.M, w.N, w.K, path, tile)
+
+    if args.timestamps:
+        import ctypes
+
+        import numpy as np
+
+        lib = fgr.load_library()
+        lib.fgr_timestamps_read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        lib.fgr_timestamps_read.restype = ctypes.c_int
+        t_warm = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t_warm < WARMUP_SECONDS:
+            for _ in range(5):
+                step(i)
+                i += 1
+            torch.cuda.synchronize()
+        records = []
+        for i in range(args.steps):
+            step(i)
+            torch.cuda.synchronize()
+            buf = np.zeros((4096, TS_WORDS), dtype=np.uint64)
+            rc = lib.fgr_timestamps_read(buf.ctypes.data, 4096)
+            if rc != 0:
+                raise RuntimeError(f"fgr_timestamps_read: {fgr.status_string(rc)}")
+            records.append(buf.astype(np.int64))
+        parts = fgr.select_parts(dA, dB, dC, w.M, w.N, w.K) if (path, tile) == (auto_path, auto_tile) else 1
+        out = os.path.join(ROOT, "profiles", f"{w.name}_timestamps.md")
+        cmd = " ".join(["python3 /root/repo/bench.py"] + sys.argv[1:])
+        print(timestamps_summary(w, fgr.PATH_NAMES[path], tile, parts, records, out, cmd))
+        return 0
 
     if args.ablation:
         # the clock climbs over the first tens of ms of work: warm up on the

@@ -1,6 +1,9 @@
 """Build the HIP library libfp32_gemm_row.so in-tree with hipcc for gfx950.
 
-    python -m fp32_gemm_row_amd.build [--resource-usage] [--resource-report FILE]
+    python -m fp32_gemm_row_amd.build [--resource-usage] [--resource-report FILE] [--timestamps]
+
+--timestamps builds the measurement library libfp32_gemm_row_ts.so instead
+(FGR_TIMESTAMPS: per-workgroup timestamp records, bench.py --timestamps).
 
 --resource-report writes a markdown table of every kernel's registers, LDS,
 occupancy and spills, as the compiler reports them (-Rpass-analysis=
@@ -25,6 +28,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfp32_gemm_row.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the measurement build: the same library with per-workgroup timestamps
+# (FGR_TIMESTAMPS, csrc/timestamps.hpp, include/fp32_gemm_row_timestamps.h)
+TS_LIB_PATH = os.path.join(PKG, "libfp32_gemm_row_ts.so")
 SOURCES = [os.path.join(CSRC, "solve.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -70,10 +76,13 @@ def resource_table(remarks: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def build(resource_usage: bool = False, verbose: bool = False, report: str = "") -> str:
-    """Compile every source into LIB_PATH (always recompiles)."""
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *SOURCES, "-o", tmp]
+def build(resource_usage: bool = False, verbose: bool = False, report: str = "", timestamps: bool = False) -> str:
+    """Compile every source into LIB_PATH, or with timestamps into
+    TS_LIB_PATH (always recompiles)."""
+    out = TS_LIB_PATH if timestamps else LIB_PATH
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, *(["-DFGR_TIMESTAMPS"] if timestamps else []), f"-I{INCLUDE}", f"-I{CSRC}", *SOURCES,
+           "-o", tmp]
     if resource_usage or report:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     if verbose:
@@ -90,13 +99,13 @@ def build(resource_usage: bool = False, verbose: bool = False, report: str = "")
             fh.write("Command: `python -m fp32_gemm_row_amd.build --resource-report " + os.path.relpath(report, ROOT)
                      + "`\n\n")
             fh.write(resource_table(res.stderr))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     rep = ""
     if "--resource-report" in sys.argv:
         rep = os.path.abspath(sys.argv[sys.argv.index("--resource-report") + 1])
-    build(resource_usage="--resource-usage" in sys.argv, verbose=True, report=rep)
-    print(LIB_PATH)
+    print(build(resource_usage="--resource-usage" in sys.argv, verbose=True, report=rep,
+                timestamps="--timestamps" in sys.argv))

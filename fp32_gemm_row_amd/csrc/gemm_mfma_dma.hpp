@@ -62,6 +62,7 @@
 #pragma once
 
 #include "gemm_mfma.hpp"
+#include "timestamps.hpp"
 
 namespace fgr {
 
@@ -173,6 +174,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     else return Bs4;
   };
 
+  TsMarks ts;  // measurement build only (timestamps.hpp)
+  ts.start();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform (scalar): the LDS destination of a copy goes to M0
@@ -386,6 +389,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
     static_for<0, S>([&](auto sc) { chunk(sc, c + decltype(sc)::value); });
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  ts.loop_done();
 
   // Epilogue. Offsets from the tile's corner (a wave-uniform base) are
   // row * K + col, 64-bit: 256 rows of a K beyond 2^24 already pass 2^32.
@@ -420,6 +424,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_dma_kernel(
         }
       }
     }
+  ts.finish();
 }
 
 }  // namespace fgr

@@ -35,6 +35,7 @@
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_split.hpp"
 #include "strip.hpp"
+#include "timestamps.hpp"
 
 namespace fgr {
 
@@ -95,11 +96,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
   constexpr int BK = T::BK, BN = T::BN, D = T::D, kRB = T::kRB, kCB = T::kCB;
   __shared__ __attribute__((aligned(1024))) float red[T::kLds];
 
+  TsMarks ts;  // measurement build only (timestamps.hpp)
+  ts.start();
   // workgroups past the tiles (STRIP): four rows of the column strip each
   const int gx = T::kStrip ? tiles_m * tiles_n : (int)gridDim.x;
   if constexpr (T::kStrip) {
     if ((int)blockIdx.x >= gx) {
       strip_rows(A, B, C, M, N, K, tiles_n * BN, (int)blockIdx.x - gx, red, T::kLds);
+      ts.loop_done();
+      ts.finish(1);
       return;
     }
   }
@@ -297,6 +302,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
       static_for<0, D>([&](auto kc) { step(kc, c + decltype(kc)::value); });
   }
 
+  ts.loop_done();
   // The four partial tiles are added in wave order, ((p0 + p1) + p2) + p3,
   // through LDS: kAtOnce of them at a time, wave w's in slot w % kAtOnce
   // (slice s = MFMA block i = s / kCB, j = s % kCB: 16 accumulators of every
@@ -451,6 +457,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_kreg_kernel(
       }
     }
   }
+  ts.finish();
 }
 
 }  // namespace fgr

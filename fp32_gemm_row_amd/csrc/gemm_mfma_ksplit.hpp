@@ -170,12 +170,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
     else return Bs3;
   };
 
+  TsMarks ts;  // measurement build only (timestamps.hpp)
+  ts.start();
   // workgroups past the tiles (STRIP): four rows of the column strip each,
   // staging B's strip in the first A stage object
   const int gx = T::kStrip ? tiles_m * tiles_n : (int)gridDim.x;
   if constexpr (T::kStrip) {
     if ((int)blockIdx.x >= gx) {
       strip_rows(A, B, C, M, N, K, tiles_n * BN, (int)blockIdx.x - gx, As0, T::kStageA);
+      ts.loop_done();
+      ts.finish(1);
       return;
     }
   }
@@ -424,6 +428,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
       chunk(std::integral_constant<int, k>{}, std::integral_constant<int, k & 1>{}, c + k);
     });
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // stray copies past the wave's last chunk
+  ts.loop_done();
 
   // The four partial tiles are added in wave order, ((p0 + p1) + p2) + p3,
   // through LDS (the staging is free once every wave is past the first
@@ -504,6 +509,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_mfma_ksplit_kernel(
       if (k0 + col < K && m0 + row < M) Ct[(uint64_t)row * ldc + (uint32_t)col] = sum[u][rr];
     }
   }
+  ts.finish();  // wave 0 always stores, so thread 0 gets here
 }
 
 }  // namespace fgr

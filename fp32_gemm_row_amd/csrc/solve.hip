@@ -14,6 +14,9 @@
 #include <mutex>
 
 #include "fp32_gemm_row.h"
+#ifdef FGR_TIMESTAMPS
+#include "fp32_gemm_row_timestamps.h"
+#endif
 #include "gemm_mfma.hpp"
 #include "gemm_mfma_dma.hpp"
 #include "gemm_mfma_ksplit.hpp"
@@ -1413,6 +1416,18 @@ int fgr_stream_read(const float* X, long long n, float* out, int blocks, void* s
   void* args[] = {&X4, &n4, &out};
   return launch(reinterpret_cast<const void*>(&fgr::stream_read_kernel), blocks, fgr::kStreamThreads, args, s);
 }
+
+#ifdef FGR_TIMESTAMPS
+// The measurement build's per-workgroup records of the last launch (see
+// timestamps.hpp and fp32_gemm_row_timestamps.h).
+int fgr_timestamps_read(void* host, int records) {
+  if (!host) return FGR_ERR_NULL_POINTER;
+  if (records < 1 || records > fgr::kTsRecords) return FGR_ERR_BAD_DIMS;
+  const hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(fgr::fgr_ts_records),
+                                           (size_t)records * sizeof(fgr::TsRecord));
+  return e == hipSuccess ? FGR_OK : FGR_ERR_LAUNCH;
+}
+#endif
 
 long long fgr_set_workspace_limit(long long bytes) {
   return g_ws_limit.exchange(bytes < 0 ? -1 : bytes, std::memory_order_relaxed);
