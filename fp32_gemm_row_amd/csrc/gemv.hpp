@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include "gemm_mfma.hpp"  // xcd_remap
+#include "timestamps.hpp"
 
 namespace fgr {
 
@@ -88,6 +89,8 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
   __shared__ float a_s[MR == 1 ? 1 : MR * CHUNK];  // [m][n - nb] (M > 1: A is staged)
   __shared__ float part[WAVES][MR][COLS];
 
+  TsMarks ts;  // measurement build only (timestamps.hpp)
+  ts.start();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -158,6 +161,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
     }
   }
 
+  ts.loop_done();
   // lanes cl, cl + LPR, cl + 2 LPR, ... of a wave hold the same columns
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1)
@@ -181,6 +185,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const float* __restrict__ A,
     for (int w = 0; w < WAVES; ++w) s += part[w][m][cc];
     if (m < M && c < K) Out[(int64_t)m * K + c] = s;
   }
+  ts.finish();
 }
 
 }  // namespace fgr

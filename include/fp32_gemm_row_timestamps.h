@@ -3,8 +3,9 @@
  *
  * libfp32_gemm_row_ts.so is the library built with FGR_TIMESTAMPS: the same
  * entry points and kernels as libfp32_gemm_row.so (fp32_gemm_row.h), except
- * that the direct-copy, k-split and register-fed k-split kernels each record
- * one timestamp record per workgroup of their last launch. It is for
+ * that the direct-copy, k-split, register-fed k-split and matrix-vector
+ * kernels each record one timestamp record per workgroup of their last
+ * launch. It is for
  * measurement only (bench.py --timestamps); solve() callers use the plain
  * library, which has none of this.
  *
