@@ -244,6 +244,48 @@ def _find(directory, suffix):
 
 
 SQ_COUNTERS = ("MfmaUtil", "LdsUtil", "LdsBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_F32")
+CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_CYCLES")
+ABLATION_COUNTERS = ("MfmaUtil", "LdsUtil", "LdsBankConflict")
+
+
+def profile_commands(kind, workload=None, warmup=5, out="/tmp/prof"):
+    """The recipe behind a summary, written into it when no --command is given:
+    the runs that fill the folders the summary reads (from /tmp with
+    TMPDIR=/tmp, each under its own time limit) and the summarising call (from
+    the repository root). Each --pmc pass is a run of its own."""
+    b = "python3 /root/repo/bench.py"
+    fmt = "--output-format csv --"
+    if kind == "traffic":
+        w, d = f"--workload {workload} --no-cpu-baseline", f"{out}/{workload}"
+        return [
+            f"rocprofv3 --kernel-trace --stats -d {d}/kt -o kt {fmt} {b} {w} --steps 20 --warmup {warmup}",
+            f"rocprofv3 --pmc FETCH_SIZE -d {d}/pmc_fetch -o pmc {fmt} {b} {w} --steps 3 --warmup 1 --calibrate-copy",
+            f"rocprofv3 --pmc WRITE_SIZE -d {d}/pmc_write -o pmc {fmt} {b} {w} --steps 3 --warmup 1 --calibrate-copy",
+            f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {d}/pmc_sq -o pmc {fmt} {b} {w} --steps 3 --warmup 1",
+            f"python3 bench.py --workload {workload} --warmup {warmup} --summarize {d}/kt {d}/pmc_fetch "
+            f"{d}/pmc_write --summarize-sq {d}/pmc_sq",
+        ]
+    if kind == "clock":
+        return [
+            f"rocprofv3 --pmc {' '.join(CLOCK_COUNTERS)} --kernel-trace -d {out}/clk -o clk {fmt} {b} "
+            f"--workload {workload} --no-cpu-baseline --steps 10 --warmup 2",
+            f"python3 bench.py --workload {workload} --summarize-clock {out}/clk",
+        ]
+    if kind == "read":
+        return [
+            f"rocprofv3 --kernel-trace --stats -d {out}/rd -o rd {fmt} {b} --read-ceiling --steps 20 --warmup {warmup}",
+            f"python3 bench.py --summarize-read {out}/rd",
+        ]
+    if kind == "ablation":
+        return [
+            f"{b} --workload {workload} --ablation --steps 20 --warmup 5 > {out}/ablation.jsonl",
+            f"rocprofv3 --pmc {' '.join(ABLATION_COUNTERS)} -d {out}/abl_sq -o pmc {fmt} {b} --workload {workload} "
+            "--ablation --steps 3 --warmup 1",
+            "python3 -m fp32_gemm_row_amd.build --resource-report profiles/kernel_resources.md",
+            f"python3 bench.py --workload {workload} --summarize-ablation {out}/ablation.jsonl {out}/abl_sq "
+            "profiles/kernel_resources.md",
+        ]
+    raise ValueError(kind)
 
 
 def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, commands, out_path, warmup=5, sq_dir=None):
@@ -802,7 +844,8 @@ def main() -> int:
                     help="with the measurement build (libfp32_gemm_row_ts.so), record per-workgroup timestamps "
                          "of --steps launches of the workload, write profiles/<workload>_timestamps.md and exit")
     ap.add_argument("--command", action="append", default=[],
-                    help="(with --summarize) a command that produced the folders, recorded in the summary")
+                    help="(with a --summarize option) a command that produced the folders, recorded in the "
+                         "summary in place of the standard recipe (profile_commands)")
     args = ap.parse_args()
     auto_warmup = args.warmup is None
     if auto_warmup:
@@ -810,19 +853,23 @@ def main() -> int:
 
     if args.summarize_ablation:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_controlled_comparison.md")
-        print(summarize_ablation(args.workload, *args.summarize_ablation, args.command, out))
+        cmds = args.command or profile_commands("ablation", args.workload)
+        print(summarize_ablation(args.workload, *args.summarize_ablation, cmds, out))
         return 0
     if args.summarize_read:
         out = os.path.join(ROOT, "profiles", "stream_read_1gib.md")
-        print(summarize_read(args.summarize_read, args.command, out, args.warmup))
+        cmds = args.command or profile_commands("read", warmup=args.warmup)
+        print(summarize_read(args.summarize_read, cmds, out, args.warmup))
         return 0
     if args.summarize_clock:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_clock.md")
-        print(summarize_clock(args.workload, args.summarize_clock, args.command, out))
+        cmds = args.command or profile_commands("clock", args.workload)
+        print(summarize_clock(args.workload, args.summarize_clock, cmds, out))
         return 0
     if args.summarize:
         out = os.path.join(ROOT, "profiles", f"{args.workload}_traffic.md")
-        print(summarize_profiles(args.workload, *args.summarize, args.command, out, args.warmup,
+        cmds = args.command or profile_commands("traffic", args.workload, args.warmup)
+        print(summarize_profiles(args.workload, *args.summarize, cmds, out, args.warmup,
                                  sq_dir=args.summarize_sq))
         return 0
 
