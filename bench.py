@@ -73,11 +73,26 @@ KERNEL_SOURCES = sorted(n for n in os.listdir(os.path.join(ROOT, "fp32_gemm_row_
 COPY_BYTES = 512 << 20
 
 
+_CXX_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_text(source: str) -> str:
+    """C++/HIP source with its comments removed and each run of blank space
+    made one space: what the compiler sees, so that a profile stays current
+    through edits of comments and layout alone."""
+    text = _CXX_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), source)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """First 16 hex digits of the sha256 of the library's sources (csrc/*.hip,
+    *.hpp, in name order) as code_text gives them. Profile summaries record it;
+    their counters are used only while it still matches."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "fp32_gemm_row_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "fp32_gemm_row_amd", "csrc", name), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
+            h.update(b"\0")
     return h.hexdigest()[:16]
 
 
