@@ -132,12 +132,11 @@ Rows rows_of(const float* A, const float* B, const float* C, int N, int K) {
 // alignment beyond 4 bytes.
 bool ksplit128_ok(int K) { return K >= 4; }
 
-// Direct global->LDS copies need at least four 16-deep reduction chunks (the
-// copies that run past the last chunk re-read it, and must never reach the
-// zero-padded first chunk); they are 16 bytes wide for 16-byte aligned rows,
-// 4 bytes otherwise (the k-split kernel's 128x128 tiles take 16-byte copies only).
-// The direct-copy kernel: N >= 64 (two chunks at least), and copy offsets
-// inside 32 bits (256 rows of A, 16 rows of B).
+// The direct-copy kernel's global->LDS copies need at least four 16-deep
+// reduction chunks, N >= 64 (the copies that run past the last chunk re-read
+// it, and must never reach the zero-padded first chunk), and their byte
+// offsets inside 32 bits (256 rows of A, 16 rows of B). They are 16 bytes wide
+// for 16-byte aligned rows, 4 bytes otherwise.
 bool mfma_dma_ok(int N, int K) { return N >= 64 && N <= fgr::kDmaMaxN && K <= fgr::kDmaMaxK; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -42,23 +42,47 @@
  *   of the process; it must not be called after hipDeviceReset.
  *
  * Alignment and paths
- *   Any 4-byte-aligned pointers are accepted. When N % 4 == 0, K % 4 == 0
- *   and A, B, C are 16-byte aligned the 128-bit load path is used; otherwise
- *   a path with 32-bit loads (the role of the scalar fallback of the LeetGPU
- *   write-up, section "V2: Vectorized float4 Transfers"). With N >= 64 and
- *   enough 256 x 256 output tiles to fill the device, A and B are copied
- *   straight from global memory into LDS (the role of the cp.async pipeline
- *   of the write-up's section "V4"; 16 bytes per lane for an operand with
- *   16-byte rows, else 4), except where neither operand's rows are 16-byte
- *   aligned, N >= 768 and the tiles leave a partial last wave. Shapes with too
- *   few output tiles for the device, and those, take 128 x 128 tiles whose
- *   reduction is split over the four waves of a workgroup, or smaller tiles
- *   split the same way;
- *   when a last, partial wave of 256 x 256 tiles is left, its tiles are cut
- *   into small split-reduction tiles. M <= 4 takes the bandwidth-bound
- *   matrix-vector path, which streams B once for all rows of A, and so do
- *   5 <= M <= 8 unless N >= 64 and K >= 128 (then 32 x 128 k-split tiles or
- *   the split plans of few-tile shapes serve them).
+ *   Any 4-byte-aligned pointers are accepted. An operand's rows are "aligned"
+ *   below when its row length is a multiple of 4 floats and its pointer is
+ *   16-byte aligned; aligned rows move in 16-byte pieces, others in 4-byte or
+ *   8-byte ones (the role of the scalar fallback of the LeetGPU write-up,
+ *   section "V2: Vectorized float4 Transfers"). With T256, T128 and T64 the
+ *   numbers of 256 x 256, 128 x 128 and 64 x 64 output tiles and CUs the
+ *   device's compute units, solve() takes the first of these that applies:
+ *   1. M <= 4, or M <= 8 without rule 2's shape: the bandwidth-bound
+ *      matrix-vector path, which streams B once for all rows of A
+ *      (FGR_PATH_GEMV_VEC when B's rows are aligned, else GEMV_SCALAR).
+ *   2. 5 <= M <= 64, N >= 64 and K >= 128 (within the 32 x 128 tiles'
+ *      offset limits), with B of at least 32 Mi floats, or 16 Mi when 32 x 32
+ *      tiles would not fill the CUs: 32 x 128 k-split tiles, their reduction
+ *      also split across workgroups where that fills the device
+ *      (MFMA_KSPLIT or MFMA_SPLITK, tile 32X128). The same shape with a
+ *      smaller B goes on to the rules below, also at M <= 8.
+ *   3. T64 >= CUs and a short reduction: N < 104 (N < 72 when every row is
+ *      aligned and the 256 x 256 tiles make whole waves), or N < 384 when
+ *      T256 >= CUs and B's rows (or, with A's aligned, C's) are not
+ *      aligned: register-staged 64 x 64 tiles (MFMA_VEC when all rows are
+ *      aligned; else MFMA_SCALAR, tile 128 when T128 >= 4 CUs).
+ *   4. T256 >= CUs within FGR_PATH_MFMA_DMA's limits, unless neither A's nor
+ *      B's rows are aligned, N >= 768 and the tiles leave a partial last
+ *      wave: 256 x 256 tiles whose operands are copied straight from global
+ *      memory into LDS (the role of the cp.async pipeline of the write-up's
+ *      section "V4"), MFMA_DMA; a partial last wave of at most 11/16 of the
+ *      CUs is cut into split-kernel tiles (MFMA_DMA_TAIL).
+ *   5. N >= 64: tiles whose reduction is split over the four waves of a
+ *      workgroup (k-split). 128 x 128 when K >= 4, T128 >= CUs and they
+ *      make whole waves, three waves or more, or a last wave over three
+ *      quarters full;
+ *      else the strip plan where it applies (MFMA_STRIP); else 64 x 64 when
+ *      T64 >= CUs. A partial last wave of at most half the CUs takes
+ *      MFMA_KSPLIT_TAIL, else MFMA_KSPLIT. With T64 < CUs: 64 x 64 or
+ *      32 x 32 tiles, their reduction also split across workgroups where a
+ *      time estimate prefers it (MFMA_SPLITK; 128 x 128 tiles when they pad
+ *      no more and their parts are at least 2048 long).
+ *   6. Otherwise (N < 64, T64 < CUs): the split kernel's 32 x 32 tiles
+ *      (MFMA_SPLIT).
+ *   fgr_select_path() and fgr_select_tile() report the choice for a 256-CU
+ *   device.
  *
  * Errors
  *   Every entry point returns 0 (FGR_OK) on success or a negative FGR_ERR_*

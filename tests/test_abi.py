@@ -477,3 +477,19 @@ def test_stream_read_rejects_bad_arguments(lib):
     assert sr(A0, 1024, C0, 0, None) == fgr.ERR_BAD_DIMS
     assert sr(A0 + 4, 1024, C0, 4, None) == fgr.ERR_MISALIGNED
     assert sr(A0, 1024, A0 + 16, 4, None) == fgr.ERR_ALIAS
+
+
+def test_header_path_rules_in_order():
+    # one shape per numbered rule of the header's "Alignment and paths" list
+    sp, st = fgr.select_path, fgr.select_tile
+    assert sp(A0, B0, C0, 4, 8192, 8192) == fgr.PATH_GEMV_VEC  # 1: M <= 4
+    assert sp(A0, B0, C0, 8, 32, 8192) == fgr.PATH_GEMV_VEC  # 1: M <= 8, N < 64
+    assert st(A0, B0, C0, 16, 8192, 8192) == fgr.TILE_32X128  # 2: B of 64 Mi floats
+    assert sp(A0, B0, C0, 8, 2048, 2048) != fgr.PATH_GEMV_VEC  # 2: the shape, small B: on to 3-6
+    assert (sp(A0, B0, C0, 6144, 100, 6144), st(A0, B0, C0, 6144, 100, 6144)) == (fgr.PATH_MFMA_VEC, 64)  # 3
+    assert sp(A0, B0, C0, 8192, 100, 8192) == fgr.PATH_MFMA_DMA  # 3: N >= 72 with whole waves
+    assert sp(A0, B0, C0, 8192, 6144, 4096) == fgr.PATH_MFMA_DMA  # 4
+    assert (sp(A0, B0, C0, 2048, 2048, 2048), st(A0, B0, C0, 2048, 2048, 2048)) == (fgr.PATH_MFMA_KSPLIT, 128)  # 5
+    assert sp(A0, B0, C0, 1023, 1025, 1027) == fgr.PATH_MFMA_STRIP  # 5: the strip plan
+    assert sp(A0, B0, C0, 128, 262144, 128) == fgr.PATH_MFMA_SPLITK  # 5: few tiles, long N
+    assert (sp(A0, B0, C0, 256, 32, 256), st(A0, B0, C0, 256, 32, 256)) == (fgr.PATH_MFMA_SPLIT, 32)  # 6
