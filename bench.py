@@ -164,25 +164,33 @@ def summarize_clock(workload, pmc_dir, commands, out_path, warmup=2):
         f"GRBM_GUI_ACTIVE / {NUM_XCC}. SQ_CYCLES (summed over the 32 shader engines) and SQ_BUSY_CYCLES are shown "
         "beside it. Clock = cycles / dispatch duration (kernel trace of the same run; the profiler serialises "
         "dispatches, so the clock here ramps over the first ones). Ideal cycles = 2MNK / (256 CUs x 256 FLOP "
-        f"per clock) = {ideal:.0f}.",
+        f"per clock) = {ideal:.0f}. GRBM_GUI_ACTIVE can also count clocks outside a dispatch's trace window: "
+        "for dispatches of tens of microseconds the clock column then reads above the chip's 2.4 GHz, and "
+        "rocprofv3's MfmaUtil, whose denominator it is, reads low. The shader engines' busy cycles "
+        "(SQ_BUSY_CYCLES / 32, the clocks in which an engine had waves) hold the kernel's own span; "
+        "busy-cycle-efficiency sets the ideal cycles against them.",
         "",
         "| dispatch | duration ns | GRBM_GUI_ACTIVE / 8 | SQ_CYCLES / 32 | SQ_BUSY_CYCLES / 32 | clock GHz |",
         "|---|---|---|---|---|---|",
     ]
-    cycles = []
+    cycles, busy = [], []
     for did, d in disp:
         t = trace.get(str(did))
         ns = int(t["End_Timestamp"]) - int(t["Start_Timestamp"]) if t else 0
         cyc = d.get("GRBM_GUI_ACTIVE", 0) / NUM_XCC
         cycles.append(cyc)
+        busy.append(d.get("SQ_BUSY_CYCLES", 0) / 32)
         lines.append(f"| {did} | {ns} | {cyc:.0f} | {d.get('SQ_CYCLES', 0) / 32:.0f} | "
                      f"{d.get('SQ_BUSY_CYCLES', 0) / 32:.0f} | {cyc / ns if ns else 0:.3f} |")
     avg = sum(cycles) / len(cycles)
+    avg_busy = sum(busy) / len(busy)
     lines += [
         "",
         f"cycles-per-launch: {avg:.0f}",
+        f"busy-cycles-per-launch: {avg_busy:.0f}",
         f"ideal-mfma-cycles: {ideal:.0f}",
         f"cycle-efficiency: {ideal / avg:.4f}",
+        f"busy-cycle-efficiency: {ideal / avg_busy:.4f}" if avg_busy else "busy-cycle-efficiency: n/a",
         "",
         f"kernel-source-sha256: {kernel_source_hash()}",
         "",
@@ -263,7 +271,7 @@ CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_CYCLES")
 ABLATION_COUNTERS = ("MfmaUtil", "LdsUtil", "LdsBankConflict")
 
 
-def profile_commands(kind, workload=None, warmup=5, out="/tmp/prof"):
+def profile_commands(kind, workload=None, warmup=5, out="/tmp/prof", summary_out=None):
     """The recipe behind a summary, written into it when no --command is given:
     the runs that fill the folders the summary reads (from /tmp with
     TMPDIR=/tmp, each under its own time limit) and the summarising call (from
@@ -284,7 +292,8 @@ def profile_commands(kind, workload=None, warmup=5, out="/tmp/prof"):
         return [
             f"rocprofv3 --pmc {' '.join(CLOCK_COUNTERS)} --kernel-trace -d {out}/clk -o clk {fmt} {b} "
             f"--workload {workload} --no-cpu-baseline --steps 10 --warmup 2",
-            f"python3 bench.py --workload {workload} --summarize-clock {out}/clk",
+            f"python3 bench.py --workload {workload} --summarize-clock {out}/clk"
+            + (f" --summary-out {summary_out}" if summary_out else ""),
         ]
     if kind == "read":
         return [
@@ -858,6 +867,9 @@ def main() -> int:
     ap.add_argument("--timestamps", action="store_true",
                     help="with the measurement build (libfp32_gemm_row_ts.so), record per-workgroup timestamps "
                          "of --steps launches of the workload, write profiles/<workload>_timestamps.md and exit")
+    ap.add_argument("--summary-out", metavar="PATH", default=None,
+                    help="(with --summarize-clock) write the summary here instead of profiles/<workload>_clock.md, "
+                         "the record bench.py reads the clock from (for kernels too short for that record)")
     ap.add_argument("--command", action="append", default=[],
                     help="(with a --summarize option) a command that produced the folders, recorded in the "
                          "summary in place of the standard recipe (profile_commands)")
@@ -877,8 +889,8 @@ def main() -> int:
         print(summarize_read(args.summarize_read, cmds, out, args.warmup))
         return 0
     if args.summarize_clock:
-        out = os.path.join(ROOT, "profiles", f"{args.workload}_clock.md")
-        cmds = args.command or profile_commands("clock", args.workload)
+        out = args.summary_out or os.path.join(ROOT, "profiles", f"{args.workload}_clock.md")
+        cmds = args.command or profile_commands("clock", args.workload, summary_out=args.summary_out)
         print(summarize_clock(args.workload, args.summarize_clock, cmds, out))
         return 0
     if args.summarize:
