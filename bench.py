@@ -115,17 +115,25 @@ NUM_XCC = 8
 
 
 def recorded_clock(workload: str):
-    """The dominant kernel's cycles per launch from profiles/<workload>_clock.md,
-    if current (same kernel sources)."""
+    """The dominant kernel's GPU-active cycles per launch from
+    profiles/<workload>_clock.md, if current (same kernel sources)."""
+    rec = recorded_cycles(workload)
+    return rec[0] if rec else None
+
+
+def recorded_cycles(workload: str):
+    """(GPU-active cycles, shader-engine busy cycles or None) per launch from
+    profiles/<workload>_clock.md, if current (same kernel sources)."""
     path = os.path.join(ROOT, "profiles", f"{workload}_clock.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
     src = re.search(r"kernel-source-sha256:\s*([0-9a-f]+)", text)
-    cyc = re.search(r"cycles-per-launch:\s*([0-9.]+)", text)
+    cyc = re.search(r"^cycles-per-launch:\s*([0-9.]+)", text, flags=re.M)
+    busy = re.search(r"^busy-cycles-per-launch:\s*([0-9.]+)", text, flags=re.M)
     if not src or not cyc or src.group(1) != kernel_source_hash():
         return None
-    return float(cyc.group(1))
+    return float(cyc.group(1)), float(busy.group(1)) if busy else None
 
 
 def summarize_clock(workload, pmc_dir, commands, out_path, warmup=2):
@@ -1067,7 +1075,8 @@ def main() -> int:
         roof["batched"]["graph_ms_per_launch"] = round(g_ms, 5)
         roof["batched"]["graph_achieved"] = (round(w.algorithmic_bytes / g_ms / 1e6, 2) if gemv
                                              else round(w.flops / g_ms / 1e9, 3))
-    cycles = recorded_clock(w.name)
+    rec = recorded_cycles(w.name)
+    cycles, busy_cycles = rec if rec else (None, None)
     if cycles and not gemv:
         # cycles per launch (profiles/<workload>_clock.md) over this run's launch
         # time: the clock the timed launches ran at, and the peak at that clock
@@ -1080,6 +1089,9 @@ def main() -> int:
             "frac_at_clock": round(achieved / peak_at_clock, 4),
             "cycle_efficiency": round(w.flops / (CU_COUNT * FP32_FLOP_PER_CU_CLK) / cycles, 4),
         }
+        if busy_cycles:
+            # against the clocks in which the shader engines had waves
+            roof["clock"]["busy_cycle_efficiency"] = round(w.flops / (CU_COUNT * FP32_FLOP_PER_CU_CLK) / busy_cycles, 4)
     if gemv:
         # the measured streaming-read ceiling beside the datasheet peak
         ceiling = read_ceiling(dev, stream, torch.cuda.get_device_properties(dev).multi_processor_count)
